@@ -1,0 +1,280 @@
+"""CPU oracle of the KDA / gated delta rule -- TEST INFRASTRUCTURE ONLY.
+
+Only the test-suite, the smoke check and the benchmark's CPU-baseline leg may
+import this package.  The HIP library never loads it, and the two share no
+code: the only common module is the seeded input generator, which holds no
+arithmetic of the method.
+
+Contents
+--------
+``forward``            ctypes front end of the plain C fp64 token recurrence
+                       (``kda_oracle.c``); the oracle proper.
+``recurrence``         the same recurrence in NumPy fp64 (a second, independent
+                       spelling used to cross-check the C code).
+``brute_force``        the recurrence with each transition matrix
+                       M_t = (I - beta_t k_t^T k_t) diag(alpha_t) built
+                       explicitly, a different evaluation order.
+``chunk_reference``    naive chunkwise form (per-chunk WY factors), the bridge
+                       between the recurrence and the chunked GPU kernels.
+``pages_chunk_deltanet`` the pages' printed alpha = 1 chunk algorithm, with its
+                       batched indexing read per chunk.
+``forward_substitution`` the pages' in-place inversion of (I + A).
+``slab_error``         the parity metric.
+
+Every function takes fp64 NumPy arrays for one head unless said otherwise.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+from typing import Optional
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "kda_oracle.c")
+_LIB = os.path.join(_HERE, "libkda_oracle.so")
+
+F32, BF16 = 0, 1
+ALPHA_NONE, ALPHA_HEAD, ALPHA_CHANNEL = 0, 1, 2
+_DT = {"f32": F32, "bf16": BF16}
+_AM = {"none": ALPHA_NONE, "head": ALPHA_HEAD, "channel": ALPHA_CHANNEL}
+
+
+# ---------------------------------------------------------------------------
+# build + load of the C oracle
+# ---------------------------------------------------------------------------
+
+def build(verbose: bool = False) -> str:
+    """Compile kda_oracle.c with gcc (IEEE fp64, no contraction) in place."""
+    cmd = ["gcc", "-O2", "-std=c99", "-ffp-contract=off", "-fno-fast-math",
+           "-fPIC", "-shared", "-pthread", _SRC, "-o", _LIB, "-lm"]
+    if verbose:
+        print(" ".join(cmd))
+    subprocess.run(cmd, check=True)
+    return _LIB
+
+
+_lib = None
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+            build()
+        lib = ctypes.CDLL(_LIB)
+        f = lib.kda_oracle_forward
+        i64, i32, vp = ctypes.c_int64, ctypes.c_int, ctypes.c_void_p
+        f.argtypes = [i64, i64, i64, i64, i64, i32, i32, i32,
+                      vp, vp, vp, vp, vp, vp, i64, i64, i32, vp, vp, i32]
+        f.restype = ctypes.c_int
+        _lib = lib
+    return _lib
+
+
+def _ptr(a: Optional[np.ndarray]):
+    return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
+
+
+def default_threads() -> int:
+    try:
+        return len(os.sched_getaffinity(0))
+    except AttributeError:  # pragma: no cover
+        return os.cpu_count() or 1
+
+
+def forward(q, k, v, log_alpha, beta, S0=None, *, qkv_dtype="f32", gate_dtype="f32",
+            alpha_mode="channel", col0=0, ncols=None, delta=True, want_o=True,
+            threads=None):
+    """Run the C fp64 recurrence on stacked heads.
+
+    q, k: [N, L, dk]; v: [N, L, dv]; log_alpha: [N, L, dk] | [N, L] | None;
+    beta: [N, L]; S0: [N, dk, dv] (any float dtype, widened to fp64) or None.
+    Arrays are in storage type: float32, or uint16 bf16 bits.
+    Returns (o [N, L, ncols] fp64 or None, S_final [N, dk, ncols] fp64).
+    """
+    lib = _load()
+    q = np.ascontiguousarray(q)
+    k = np.ascontiguousarray(k)
+    v = np.ascontiguousarray(v)
+    beta = np.ascontiguousarray(beta)
+    N, L, dk = q.shape
+    dv = v.shape[-1]
+    if ncols is None:
+        ncols = dv - col0
+    la = None if (log_alpha is None or alpha_mode == "none") else np.ascontiguousarray(log_alpha)
+    s0 = None if S0 is None else np.ascontiguousarray(S0, dtype=np.float64)
+    o = np.empty((N, L, ncols), dtype=np.float64) if want_o else None
+    sf = np.empty((N, dk, ncols), dtype=np.float64)
+    rc = lib.kda_oracle_forward(N, 1, L, dk, dv, _DT[qkv_dtype], _DT[gate_dtype],
+                                _AM[alpha_mode], _ptr(q), _ptr(k), _ptr(v), _ptr(la),
+                                _ptr(beta), _ptr(s0), col0, ncols, 1 if delta else 0,
+                                _ptr(o), _ptr(sf),
+                                threads if threads is not None else default_threads())
+    if rc != 0:
+        raise ValueError("kda_oracle_forward rejected its arguments")
+    return o, sf
+
+
+# ---------------------------------------------------------------------------
+# NumPy fp64 spellings (one head each)
+# ---------------------------------------------------------------------------
+
+def _decay(log_alpha, L, dk):
+    """exp(log_alpha) as an [L, dk] array (broadcast in head mode, ones if None)."""
+    if log_alpha is None:
+        return np.ones((L, dk))
+    la = np.asarray(log_alpha, dtype=np.float64)
+    if la.ndim == 1:
+        return np.repeat(np.exp(la)[:, None], dk, axis=1)
+    return np.exp(la)
+
+
+def recurrence(q, k, v, log_alpha, beta, S0=None, delta=True):
+    """Token-by-token recurrence (decay, correct against the decayed state,
+    write, read).  Same passages as kda_oracle.h.  Returns (o [L,dv], S)."""
+    L, dk = q.shape
+    dv = v.shape[1]
+    a = _decay(log_alpha, L, dk)
+    S = np.zeros((dk, dv)) if S0 is None else np.array(S0, dtype=np.float64)
+    o = np.zeros((L, dv))
+    for t in range(L):
+        S = a[t][:, None] * S
+        kS = k[t] @ S if delta else 0.0
+        u = beta[t] * (v[t] - kS)
+        S = S + np.outer(k[t], u)
+        o[t] = q[t] @ S
+    return o, S
+
+
+def brute_force(q, k, v, log_alpha, beta, S0=None):
+    """S_t = M_t S_{t-1} + beta_t k_t^T v_t with M_t = (I - beta_t k_t^T k_t) D_t
+    formed as an explicit d_k x d_k matrix ("Gated DeltaNet adds controlled
+    forgetting", zharfai.com; products of Householder-like transitions,
+    yichencityu.github.io section 6.3)."""
+    L, dk = q.shape
+    dv = v.shape[1]
+    a = _decay(log_alpha, L, dk)
+    S = np.zeros((dk, dv)) if S0 is None else np.array(S0, dtype=np.float64)
+    o = np.zeros((L, dv))
+    eye = np.eye(dk)
+    for t in range(L):
+        M = (eye - beta[t] * np.outer(k[t], k[t])) @ np.diag(a[t])
+        S = M @ S + beta[t] * np.outer(k[t], v[t])
+        o[t] = q[t] @ S
+    return o, S
+
+
+def forward_substitution(A):
+    """(I + A)^{-1} for strictly lower-triangular A (C x C), computed the way
+    section 6.3 of yichencityu.github.io does it: start from -A and complete
+    row i from the finished rows above it, then add the identity."""
+    C = A.shape[0]
+    T = -np.tril(A, -1)
+    for i in range(1, C):
+        T[i, :i] = T[i, :i] + (T[i, :, None] * T[:, :i]).sum(0)
+    return T + np.eye(C)
+
+
+def chunk_reference(q, k, v, log_alpha, beta, S0=None, C=64):
+    """Chunkwise form of the gated delta rule with per-channel decay.
+
+    For a chunk of n tokens entering with state S (g = cumulative sum of
+    log_alpha within the chunk, per key channel):
+        A_rj = beta_r sum_c k_rc k_jc exp(g_rc - g_jc)   (j < r)
+        T    = (I + A)^{-1}                              (forward substitution)
+        W    = T diag(beta) (K * exp(g)),   U = T diag(beta) V
+        P_rj = sum_c q_rc k_jc exp(g_rc - g_jc)          (j <= r)
+        u    = U - W S
+        O    = (Q * exp(g)) S + P u
+        S    <- diag(exp(g_n)) S + (K * exp(g_n - g))^T u
+    At alpha = 1 this is the chunk algorithm of section 6.3 of
+    yichencityu.github.io; the gated form is derived from the recurrence (the
+    pages stop before printing it).  A short last chunk is simply shorter.
+    """
+    L, dk = q.shape
+    dv = v.shape[1]
+    la = np.zeros((L, dk))
+    if log_alpha is not None:
+        x = np.asarray(log_alpha, dtype=np.float64)
+        la = np.repeat(x[:, None], dk, axis=1) if x.ndim == 1 else x
+    S = np.zeros((dk, dv)) if S0 is None else np.array(S0, dtype=np.float64)
+    o = np.zeros((L, dv))
+    for s in range(0, L, C):
+        e = min(s + C, L)
+        Q, K, V, bt = q[s:e], k[s:e], v[s:e], beta[s:e]
+        g = np.cumsum(la[s:e], axis=0)
+        n = e - s
+        causal = np.tril(np.ones((n, n), dtype=bool))[:, :, None]
+        dec = np.exp(np.where(causal, g[:, None, :] - g[None, :, :], -np.inf))  # [r, j, c]
+        KK = np.einsum("rc,jc,rjc->rj", K, K, dec)
+        QK = np.einsum("rc,jc,rjc->rj", Q, K, dec)
+        A = np.tril(bt[:, None] * KK, -1)
+        T = forward_substitution(A)
+        W = T @ (bt[:, None] * K * np.exp(g))
+        U = T @ (bt[:, None] * V)
+        P = np.tril(QK)
+        u = U - W @ S
+        o[s:e] = (Q * np.exp(g)) @ S + P @ u
+        S = np.exp(g[n - 1])[:, None] * S + (K * np.exp(g[n - 1][None, :] - g)).T @ u
+    return o, S
+
+
+def pages_chunk_deltanet(Q, K, V, beta, C):
+    """The alpha = 1 chunk algorithm as printed in section 6.3 of
+    yichencityu.github.io (zero initial state, L a multiple of C), with its
+    batched triangular indexing read per chunk."""
+    L, d = Q.shape
+    dv = V.shape[1]
+    Qc, Kc, Vc = (x.reshape(-1, C, x.shape[1]) for x in (Q, K, V))
+    bc = beta.reshape(-1, C)
+    K_beta = Kc * bc[..., None]
+    V_beta = Vc * bc[..., None]
+    T = -np.tril(K_beta @ Kc.transpose(0, 2, 1), -1)
+    for i in range(1, C):
+        T[:, i, :i] = T[:, i, :i] + (T[:, i, :, None] * T[:, :, :i]).sum(-2)
+    T = T + np.eye(C)
+    W = T @ K_beta
+    U = T @ V_beta
+    S = np.zeros((d, dv))
+    O = np.empty_like(Vc)
+    for i in range(L // C):
+        q_i, k_i, w_i = Qc[i], Kc[i], W[i]
+        u_i = U[i] - w_i @ S
+        o_inter = q_i @ S
+        A_i = np.tril(q_i @ k_i.T)
+        O[i] = A_i @ u_i + o_inter
+        S = S + k_i.T @ u_i
+    return O.reshape(L, dv), S
+
+
+# ---------------------------------------------------------------------------
+# parity metric
+# ---------------------------------------------------------------------------
+
+def slab_error(x, ref, slab_axes=2):
+    """Worst per-slab relative error max|x - ref| / max|ref|.
+
+    The leading ``slab_axes`` axes index slabs (e.g. (b, h)); the metric is
+    taken over each slab and the worst slab is returned.  Any NaN or Inf in
+    x gives inf.  A slab whose reference is all zero is judged by its absolute
+    error.
+    """
+    x = np.asarray(x, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    if x.shape != ref.shape:
+        raise ValueError(f"shape mismatch {x.shape} vs {ref.shape}")
+    if x.size == 0:
+        return 0.0
+    if not np.all(np.isfinite(x)):
+        return float("inf")
+    lead = int(np.prod(x.shape[:slab_axes])) if slab_axes else 1
+    xs = x.reshape(lead, -1)
+    rs = ref.reshape(lead, -1)
+    num = np.max(np.abs(xs - rs), axis=1)
+    den = np.max(np.abs(rs), axis=1)
+    den = np.where(den > 0, den, 1.0)
+    return float(np.max(num / den))
