@@ -1,0 +1,142 @@
+/*
+ * kda.h -- C ABI of the MI355X (gfx950) KDA / gated delta rule library.
+ *
+ * The operation (per batch b and head h; row vectors; S is d_k x d_v):
+ *
+ *     S~  = diag(alpha_t) S             decay, one factor per key channel
+ *     u   = beta_t (v_t - k_t S~)       delta-rule correction
+ *     S   = S~ + k_t^T u                write
+ *     o_t = q_t S                       read (after the write)
+ *
+ * i.e. S_t = (I - beta_t k_t^T k_t) diag(alpha_t) S_(t-1) + beta_t k_t^T v_t,
+ * o_t = q_t S_t.  Sources: "22580: From GPT-2 to Kimi3, Explained"
+ * (zharfai.com), sections "The delta rule turns writing into editing",
+ * "Gated DeltaNet adds controlled forgetting" and "Kimi Delta Attention makes
+ * forgetting finer"; "22,580: From GPT-2 to Kimi K3" (yichencityu.github.io),
+ * sections 5.2 (delta update), 6.1 (token loop: write then read), 6.3 (the
+ * chunkwise WY form) and 9.1 (per-channel alpha).  The decay is applied before
+ * the correction, so a unit key written with beta = 1 reads back its value
+ * exactly for any per-channel alpha.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * - All tensors are dense, row-major, contiguous device buffers owned by the
+ *   caller.  q, k: [B,H,L,dk]; v, o: [B,H,L,dv]; beta: [B,H,L];
+ *   log_alpha: [B,H,L,dk] (KDA_ALPHA_CHANNEL) or [B,H,L] (KDA_ALPHA_HEAD) or
+ *   unused (KDA_ALPHA_NONE, alpha = 1; may be NULL).  States are fp32
+ *   [B,H,dk,dv] with d_v contiguous.  Decode drops the L axis (L must be 1).
+ * - log_alpha holds ln(alpha_t), which must be finite and <= 0.  The GPU
+ *   kernels factor the decay inside a 16-token sub-block and are exact to
+ *   rounding for log_alpha >= -5 per token and channel (alpha >= 0.0067);
+ *   smaller values are not checked and may lose accuracy.  beta should be in
+ *   [0, 1].  Neither is checked; NaN or Inf stays inside its own (b, h).
+ * - q, k, v and o share qkv_dtype; log_alpha and beta share gate_dtype.
+ *   Arithmetic: fp32 inputs are computed entirely in fp32 (fp32 MFMA); bf16
+ *   inputs use bf16 MFMA operands with fp32 accumulation, and the state is
+ *   fp32 throughout.  o is rounded to its dtype with round-to-nearest-even.
+ * - Supported sizes: dk, dv in {64, 128}; B, H, L >= 0 (any L: a ragged last
+ *   chunk is handled in the kernel).  Every pointer must be 16-byte aligned.
+ * - Calls are asynchronous on hip_stream (a hipStream_t; NULL = the null
+ *   stream).  Outputs are valid once that stream has been synchronized.  The
+ *   library allocates no device memory, keeps no per-call state and is safe
+ *   to call from several host threads.
+ * - Return value: KDA_OK (0) or a kda_status code.  Every check except
+ *   KDA_ERR_HIP is made on the host before any HIP call, so a rejected call
+ *   touches neither the device nor any buffer.  A fault inside a kernel is
+ *   reported by the stream, not here.
+ */
+#ifndef KDA_H
+#define KDA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define KDA_ABI_VERSION 1
+
+enum kda_dtype { KDA_F32 = 0, KDA_BF16 = 1 };
+
+enum kda_alpha_mode {
+    KDA_ALPHA_NONE = 0,    /* alpha = 1: DeltaNet                          */
+    KDA_ALPHA_HEAD = 1,    /* one decay per token and head: Gated DeltaNet */
+    KDA_ALPHA_CHANNEL = 2  /* one decay per token, head and key channel: KDA */
+};
+
+enum kda_status {
+    KDA_OK = 0,
+    KDA_ERR_NULL = 1,       /* a required pointer is NULL                     */
+    KDA_ERR_SHAPE = 2,      /* negative size, unsupported dk/dv, size overflow,
+                               or L != 1 for decode                           */
+    KDA_ERR_DTYPE = 3,      /* qkv_dtype or gate_dtype not a kda_dtype        */
+    KDA_ERR_ALPHA_MODE = 4, /* alpha_mode not a kda_alpha_mode                */
+    KDA_ERR_ALIGN = 5,      /* a pointer is not 16-byte aligned               */
+    KDA_ERR_WORKSPACE = 6,  /* workspace smaller than the size query returns  */
+    KDA_ERR_ALIAS = 7,      /* an output overlaps an input, or S_final only
+                               partly overlaps S0                             */
+    KDA_ERR_HIP = 8         /* a HIP launch failed; kda_last_error() has text */
+};
+
+typedef struct kda_shape {
+    int64_t B, H, L, dk, dv; /* L = 1 for decode */
+    int32_t qkv_dtype;       /* enum kda_dtype: q, k, v and o                 */
+    int32_t gate_dtype;      /* enum kda_dtype: log_alpha and beta            */
+    int32_t alpha_mode;      /* enum kda_alpha_mode                           */
+} kda_shape;
+
+/*
+ * Chunkwise-parallel prefill ("22,580: From GPT-2 to Kimi K3", section 6.3:
+ * chunks of C = 64 tokens; inside a chunk the delta corrections are solved at
+ * once through the WY factors T = (I + A)^-1 found by forward substitution,
+ * and one state is carried from chunk to chunk).  Per (b, h) it runs the
+ * recurrence above over all L tokens, starting from S0.
+ *
+ *   S0       [B,H,dk,dv] fp32 initial state, or NULL for a zero state.
+ *   o        [B,H,L,dv] output in qkv_dtype.  Must not overlap any input or
+ *            S_final.
+ *   S_final  [B,H,dk,dv] fp32 final state, or NULL to skip it.  May be the
+ *            same buffer as S0 (in-place update); any other overlap with S0
+ *            or with an input is an error.
+ *   workspace, workspace_bytes: device scratch of at least
+ *            kda_chunk_fwd_workspace_bytes(shape) bytes (may be NULL when that
+ *            is 0).  The library does not keep it after the call's kernels end.
+ */
+int kda_chunk_fwd(const kda_shape* shape, const void* q, const void* k, const void* v,
+                  const void* log_alpha, const void* beta, const float* S0, void* o,
+                  float* S_final, void* workspace, size_t workspace_bytes,
+                  void* hip_stream);
+
+/* Bytes of device workspace kda_chunk_fwd needs for this shape (0 for a
+ * shape the call would reject). */
+size_t kda_chunk_fwd_workspace_bytes(const kda_shape* shape);
+
+/*
+ * One decode step for every (b, h): the recurrence above for a single token,
+ * updating S in place ("22,580: From GPT-2 to Kimi K3", section 5.2 and
+ * section 08's gate; "22580: From GPT-2 to Kimi3, Explained", "Gated DeltaNet
+ * adds controlled forgetting").  shape->L must be 1.
+ *
+ *   q, k     [B,H,dk]; v, o: [B,H,dv]; log_alpha [B,H,dk] | [B,H] | unused;
+ *   beta     [B,H].
+ *   S        [B,H,dk,dv] fp32, read and overwritten with the new state.
+ *   o        must not overlap S or any input.
+ */
+int kda_decode_step(const kda_shape* shape, const void* q, const void* k, const void* v,
+                    const void* log_alpha, const void* beta, float* S, void* o,
+                    void* hip_stream);
+
+/* Static text for a kda_status code. */
+const char* kda_strerror(int status);
+
+/* Text of the last KDA_ERR_HIP seen on the calling thread ("" if none). */
+const char* kda_last_error(void);
+
+/* KDA_ABI_VERSION of the loaded library. */
+int kda_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* KDA_H */

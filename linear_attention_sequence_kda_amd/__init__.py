@@ -1,1 +1,14 @@
-"""MI355X-native KDA / gated delta rule (placeholder; binding added below)."""
+"""MI355X-native KDA / gated delta rule: chunkwise prefill and decode.
+
+The compute path is libkda.so (hand-written HIP for gfx950, C ABI in
+``include/kda.h``); this package only marshals arguments to it:
+
+    o, S_final = chunk_fwd(q, k, v, log_alpha, beta, S0)
+    o          = decode_step(q, k, v, log_alpha, beta, S)   # S updated in place
+
+``inputs`` holds the seeded synthetic workloads.
+"""
+
+from .binding import KdaError, chunk_fwd, decode_step, library  # noqa: F401
+
+__all__ = ["chunk_fwd", "decode_step", "library", "KdaError"]

@@ -1,0 +1,191 @@
+"""ctypes binding of libkda.so -- argument marshalling only.
+
+Every step of the computation runs in the HIP kernels behind the C ABI
+(``include/kda.h``).  PyTorch supplies device memory and the current stream.
+There is no fallback: if the library is missing, or a tensor is not on a
+GPU, the call raises.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+from typing import Optional, Tuple
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG, "libkda.so")
+HEADER = os.path.join(os.path.dirname(PKG), "include", "kda.h")
+
+KDA_F32, KDA_BF16 = 0, 1
+KDA_ALPHA_NONE, KDA_ALPHA_HEAD, KDA_ALPHA_CHANNEL = 0, 1, 2
+STATUS = {0: "KDA_OK", 1: "KDA_ERR_NULL", 2: "KDA_ERR_SHAPE", 3: "KDA_ERR_DTYPE",
+          4: "KDA_ERR_ALPHA_MODE", 5: "KDA_ERR_ALIGN", 6: "KDA_ERR_WORKSPACE",
+          7: "KDA_ERR_ALIAS", 8: "KDA_ERR_HIP"}
+
+
+class KdaShape(ctypes.Structure):
+    _fields_ = [("B", ctypes.c_int64), ("H", ctypes.c_int64), ("L", ctypes.c_int64),
+                ("dk", ctypes.c_int64), ("dv", ctypes.c_int64),
+                ("qkv_dtype", ctypes.c_int32), ("gate_dtype", ctypes.c_int32),
+                ("alpha_mode", ctypes.c_int32)]
+
+
+class KdaError(RuntimeError):
+    def __init__(self, status: int, text: str):
+        super().__init__(f"{STATUS.get(status, status)}: {text}")
+        self.status = status
+
+
+_lib = None
+
+
+def library() -> ctypes.CDLL:
+    """Load libkda.so (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(
+                f"{LIB_PATH} is missing: build it first (python -m "
+                "linear_attention_sequence_kda_amd.build, or __graft_entry__.build())")
+        lib = ctypes.CDLL(LIB_PATH)
+        vp, sz = ctypes.c_void_p, ctypes.c_size_t
+        sp = ctypes.POINTER(KdaShape)
+        lib.kda_chunk_fwd.argtypes = [sp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+        lib.kda_chunk_fwd.restype = ctypes.c_int
+        lib.kda_chunk_fwd_workspace_bytes.argtypes = [sp]
+        lib.kda_chunk_fwd_workspace_bytes.restype = sz
+        lib.kda_decode_step.argtypes = [sp, vp, vp, vp, vp, vp, vp, vp, vp]
+        lib.kda_decode_step.restype = ctypes.c_int
+        lib.kda_strerror.argtypes = [ctypes.c_int]
+        lib.kda_strerror.restype = ctypes.c_char_p
+        lib.kda_last_error.argtypes = []
+        lib.kda_last_error.restype = ctypes.c_char_p
+        lib.kda_abi_version.argtypes = []
+        lib.kda_abi_version.restype = ctypes.c_int
+        _lib = lib
+    return _lib
+
+
+def header_functions():
+    """Names of the functions declared in include/kda.h."""
+    with open(HEADER) as fh:
+        text = fh.read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(kda_[a-z_]+)\s*\(", text)))
+
+
+def _check(rc: int):
+    if rc != 0:
+        lib = library()
+        text = lib.kda_strerror(rc).decode()
+        extra = lib.kda_last_error().decode()
+        raise KdaError(rc, text + (f" ({extra})" if extra else ""))
+
+
+# ---------------------------------------------------------------------------
+# torch front end
+# ---------------------------------------------------------------------------
+
+def _torch():
+    import torch
+    return torch
+
+
+def _dtype_code(t) -> int:
+    torch = _torch()
+    if t.dtype == torch.bfloat16:
+        return KDA_BF16
+    if t.dtype == torch.float32:
+        return KDA_F32
+    raise TypeError(f"unsupported dtype {t.dtype} (bfloat16 or float32)")
+
+
+def _ptr(t) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _require(t, name):
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _stream(t) -> int:
+    torch = _torch()
+    return torch.cuda.current_stream(t.device).cuda_stream
+
+
+def chunk_fwd(q, k, v, log_alpha, beta, S0=None, *, output_final_state: bool = True,
+              o=None, S_final=None) -> Tuple[object, Optional[object]]:
+    """Chunkwise prefill: returns (o [B,H,L,dv], S_final [B,H,dk,dv] fp32 or None).
+
+    q, k: [B,H,L,dk]; v: [B,H,L,dv] (bf16 or fp32, same dtype);
+    log_alpha: None (alpha = 1), [B,H,L] (one decay per head) or [B,H,L,dk]
+    (one per key channel); beta: [B,H,L] (same dtype as log_alpha, or any
+    float dtype when log_alpha is None); S0: [B,H,dk,dv] fp32 or None.
+    ``o`` / ``S_final`` may be given to write into existing buffers
+    (S_final may be S0 itself).
+    """
+    torch = _torch()
+    B, H, L, dk = q.shape
+    dv = v.shape[-1]
+    if log_alpha is None:
+        mode = KDA_ALPHA_NONE
+    elif log_alpha.dim() == 3:
+        mode = KDA_ALPHA_HEAD
+    else:
+        mode = KDA_ALPHA_CHANNEL
+    for name, t in (("q", q), ("k", k), ("v", v), ("beta", beta), ("log_alpha", log_alpha),
+                    ("S0", S0)):
+        if t is not None:
+            _require(t, name)
+    if o is None:
+        o = torch.empty((B, H, L, dv), dtype=v.dtype, device=v.device)
+    if output_final_state and S_final is None:
+        S_final = torch.empty((B, H, dk, dv), dtype=torch.float32, device=v.device)
+    if S0 is not None and S0.dtype != torch.float32:
+        raise TypeError("S0 must be float32")
+    shape = KdaShape(B, H, L, dk, dv, _dtype_code(q),
+                     _dtype_code(log_alpha if log_alpha is not None else beta), mode)
+    lib = library()
+    ws = lib.kda_chunk_fwd_workspace_bytes(ctypes.byref(shape))
+    workspace = torch.empty(ws, dtype=torch.uint8, device=v.device) if ws else None
+    rc = lib.kda_chunk_fwd(ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha),
+                           _ptr(beta), _ptr(S0), _ptr(o),
+                           _ptr(S_final) if output_final_state else None,
+                           _ptr(workspace), ws, _stream(v))
+    _check(rc)
+    return o, (S_final if output_final_state else None)
+
+
+def decode_step(q, k, v, log_alpha, beta, S, *, o=None):
+    """One decode step for every (b, h); S [B,H,dk,dv] fp32 is updated in place.
+
+    q, k: [B,H,dk]; v: [B,H,dv]; log_alpha: None, [B,H] or [B,H,dk];
+    beta: [B,H].  Returns o [B,H,dv].
+    """
+    torch = _torch()
+    B, H, dk = q.shape
+    dv = v.shape[-1]
+    if log_alpha is None:
+        mode = KDA_ALPHA_NONE
+    elif log_alpha.dim() == 2:
+        mode = KDA_ALPHA_HEAD
+    else:
+        mode = KDA_ALPHA_CHANNEL
+    for name, t in (("q", q), ("k", k), ("v", v), ("beta", beta), ("log_alpha", log_alpha),
+                    ("S", S)):
+        if t is not None:
+            _require(t, name)
+    if S.dtype != torch.float32:
+        raise TypeError("S must be float32")
+    if o is None:
+        o = torch.empty((B, H, dv), dtype=v.dtype, device=v.device)
+    shape = KdaShape(B, H, 1, dk, dv, _dtype_code(q),
+                     _dtype_code(log_alpha if log_alpha is not None else beta), mode)
+    rc = library().kda_decode_step(ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(v),
+                                   _ptr(log_alpha), _ptr(beta), _ptr(S), _ptr(o), _stream(v))
+    _check(rc)
+    return o

@@ -1,0 +1,158 @@
+// kda_device.h -- device helpers shared by the gfx950 KDA kernels.
+//
+// MFMA fragment conventions (checked on gfx950):
+//   v_mfma_f32_16x16x32_bf16: lane l supplies A[l%16][8(l/16) .. 8(l/16)+7]
+//     and B[8(l/16) .. +7][l%16]; it receives D[4(l/16)+i][l%16], i = 0..3.
+//   v_mfma_f32_16x16x4_f32:   lane l supplies A[l%16][l/16], B[l/16][l%16],
+//     and receives D[4(l/16)+i][l%16].
+// A "fragment" below is what one lane supplies for KS consecutive k:
+//   bf16: 8 bf16 at k offset 8(l/16) of a 32-wide k step  (one MFMA)
+//   fp32: 4 floats at k offset 4(l/16) of a 16-wide k step (four MFMAs; the
+//         s-th MFMA takes element s, which permutes k consistently for both
+//         operands, so the sum over the four covers all 16 k).
+// Both operands are given "k-contiguous": A as [m][k], B as [n][k].
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace kda {
+
+typedef __bf16 bf16;
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float floatx4 __attribute__((ext_vector_type(4)));
+typedef float floatx2 __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
+
+// ---- scalar conversions ---------------------------------------------------
+__device__ __forceinline__ float to_f32(float x) { return x; }
+__device__ __forceinline__ float to_f32(bf16 x) { return (float)x; }
+template <typename E> __device__ __forceinline__ E from_f32(float x);
+template <> __device__ __forceinline__ float from_f32<float>(float x) { return x; }
+template <> __device__ __forceinline__ bf16 from_f32<bf16>(float x) { return (bf16)x; }
+
+// ---- MFMA fragments -------------------------------------------------------
+template <typename E> struct Frag;
+
+template <> struct Frag<bf16> {
+    typedef bf16x8 T;
+    static constexpr int W = 8;    // k elements per lane
+    static constexpr int KS = 32;  // k per step
+    static __device__ __forceinline__ T load(const bf16* p) { return *(const bf16x8*)p; }
+    // p[0..7] * s[0..7], rounded back to bf16
+    static __device__ __forceinline__ T load_scaled(const bf16* p, const float* s) {
+        bf16x8 v = *(const bf16x8*)p;
+        floatx4 s0 = *(const floatx4*)s;
+        floatx4 s1 = *(const floatx4*)(s + 4);
+        bf16x8 r;
+        r[0] = (bf16)((float)v[0] * s0[0]);
+        r[1] = (bf16)((float)v[1] * s0[1]);
+        r[2] = (bf16)((float)v[2] * s0[2]);
+        r[3] = (bf16)((float)v[3] * s0[3]);
+        r[4] = (bf16)((float)v[4] * s1[0]);
+        r[5] = (bf16)((float)v[5] * s1[1]);
+        r[6] = (bf16)((float)v[6] * s1[2]);
+        r[7] = (bf16)((float)v[7] * s1[3]);
+        return r;
+    }
+    static __device__ __forceinline__ T load_scaled_neg(const bf16* p, const float* s) {
+        bf16x8 v = *(const bf16x8*)p;
+        floatx4 s0 = *(const floatx4*)s;
+        floatx4 s1 = *(const floatx4*)(s + 4);
+        bf16x8 r;
+        r[0] = (bf16)(-(float)v[0] * s0[0]);
+        r[1] = (bf16)(-(float)v[1] * s0[1]);
+        r[2] = (bf16)(-(float)v[2] * s0[2]);
+        r[3] = (bf16)(-(float)v[3] * s0[3]);
+        r[4] = (bf16)(-(float)v[4] * s1[0]);
+        r[5] = (bf16)(-(float)v[5] * s1[1]);
+        r[6] = (bf16)(-(float)v[6] * s1[2]);
+        r[7] = (bf16)(-(float)v[7] * s1[3]);
+        return r;
+    }
+    static __device__ __forceinline__ floatx4 mma(floatx4 acc, T a, T b) {
+        return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, acc, 0, 0, 0);
+    }
+};
+
+template <> struct Frag<float> {
+    typedef floatx4 T;
+    static constexpr int W = 4;
+    static constexpr int KS = 16;
+    static __device__ __forceinline__ T load(const float* p) { return *(const floatx4*)p; }
+    static __device__ __forceinline__ T load_scaled(const float* p, const float* s) {
+        return *(const floatx4*)p * *(const floatx4*)s;
+    }
+    static __device__ __forceinline__ T load_scaled_neg(const float* p, const float* s) {
+        return -(*(const floatx4*)p * *(const floatx4*)s);
+    }
+    static __device__ __forceinline__ floatx4 mma(floatx4 acc, T a, T b) {
+        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[0], b[0], acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[1], b[1], acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[2], b[2], acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[3], b[3], acc, 0, 0, 0);
+        return acc;
+    }
+};
+
+// acc(16x16) += A[16 x K] * B[16 x K]^T; A, B point at row 0 / k 0 of the
+// operand tiles (k-contiguous, pitches lda / ldb in elements).  K % KS == 0.
+template <typename E>
+__device__ __forceinline__ floatx4 mma_block(floatx4 acc, const E* A, int lda, const E* B,
+                                             int ldb, int K) {
+    const int l = lane_id();
+    const int r = l & 15, q = l >> 4;
+    typedef Frag<E> F;
+    const E* pa = A + r * lda + F::W * q;
+    const E* pb = B + r * ldb + F::W * q;
+#pragma unroll
+    for (int kk = 0; kk < K; kk += F::KS)
+        acc = F::mma(acc, F::load(pa + kk), F::load(pb + kk));
+    return acc;
+}
+
+// Same, with the A operand scaled per k by s[k] (s indexed from k = 0).
+template <typename E, bool NEG>
+__device__ __forceinline__ floatx4 mma_block_scaled_a(floatx4 acc, const E* A, int lda,
+                                                      const float* s, const E* B, int ldb,
+                                                      int K) {
+    const int l = lane_id();
+    const int r = l & 15, q = l >> 4;
+    typedef Frag<E> F;
+    const E* pa = A + r * lda + F::W * q;
+    const E* pb = B + r * ldb + F::W * q;
+    const float* ps = s + F::W * q;
+#pragma unroll
+    for (int kk = 0; kk < K; kk += F::KS) {
+        typename F::T a = NEG ? F::load_scaled_neg(pa + kk, ps + kk) : F::load_scaled(pa + kk, ps + kk);
+        acc = F::mma(acc, a, F::load(pb + kk));
+    }
+    return acc;
+}
+
+// Write the four accumulator values of a lane, D[4q+i][r], transposed into a
+// k-contiguous tile: dst[r * ld + 4q + i].
+template <typename E>
+__device__ __forceinline__ void store_acc_transposed(E* dst, int ld, floatx4 acc) {
+    const int l = lane_id();
+    const int r = l & 15, q = l >> 4;
+    E* p = dst + r * ld + 4 * q;
+    if constexpr (sizeof(E) == 2) {
+        bf16x4 v;
+        v[0] = (bf16)acc[0];
+        v[1] = (bf16)acc[1];
+        v[2] = (bf16)acc[2];
+        v[3] = (bf16)acc[3];
+        *(bf16x4*)p = v;
+    } else {
+        *(floatx4*)p = acc;
+    }
+}
+
+// ---- fast exp for decay factors (inputs <= 0) -----------------------------
+__device__ __forceinline__ float exp_neg(float x) { return __expf(x); }
+
+}  // namespace kda

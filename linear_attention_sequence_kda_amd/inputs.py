@@ -92,10 +92,11 @@ WORKLOADS = {
 def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
     """Round fp32 values to bf16 (nearest even) and return the uint16 bits."""
     x = np.ascontiguousarray(x, dtype=np.float32)
-    u = x.view(np.uint32).astype(np.uint64)
-    nan = np.isnan(x)
-    rounded = (u + 0x7FFF + ((u >> 16) & 1)) >> 16
+    u = x.view(np.uint32)
+    # round half to even on the 16 dropped bits; only NaN patterns can wrap
+    rounded = (u + np.uint32(0x7FFF) + ((u >> np.uint32(16)) & np.uint32(1))) >> np.uint32(16)
     out = rounded.astype(np.uint16)
+    nan = np.isnan(x)
     if nan.any():
         out[nan] = 0x7FC0
     return out
@@ -178,14 +179,20 @@ def head_inputs(w: Workload, b: int, h: int) -> dict:
     return out
 
 
-def prefill_inputs(w: Workload, heads=None) -> dict:
+def prefill_inputs(w: Workload, heads=None, threads: int = 8) -> dict:
     """Stack head_inputs over all (b, h) (or the given list of (b, h) pairs).
 
     With ``heads=None`` the arrays are [B, H, ...]; with a list of n pairs they
-    are [n, ...] in the order given.
+    are [n, ...] in the order given.  Heads are drawn on ``threads`` threads
+    (each head has its own generator, so the result does not depend on it).
     """
     pairs = heads if heads is not None else [(b, h) for b in range(w.B) for h in range(w.H)]
-    blocks = [head_inputs(w, b, h) for (b, h) in pairs]
+    if threads > 1 and len(pairs) > 1:
+        from concurrent.futures import ThreadPoolExecutor
+        with ThreadPoolExecutor(min(threads, len(pairs))) as ex:
+            blocks = list(ex.map(lambda bh: head_inputs(w, *bh), pairs))
+    else:
+        blocks = [head_inputs(w, b, h) for (b, h) in pairs]
     out = {}
     for key in ("q", "k", "v", "log_alpha", "beta", "S0"):
         if blocks[0][key] is None:

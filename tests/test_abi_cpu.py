@@ -1,0 +1,136 @@
+"""The C ABI without a GPU: the library loads, exports what kda.h declares, and
+rejects bad arguments on the host before any HIP call.
+
+Pointers here are plain integers that are never dereferenced: every call made
+below fails validation (or is an empty problem) and returns before touching
+the device.
+"""
+
+import ctypes
+
+import pytest
+
+from linear_attention_sequence_kda_amd import binding
+
+BASE = 0x7F0000000000  # 16-byte aligned fake device addresses, never dereferenced
+MB = 1 << 20
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return binding.library()
+
+
+def test_exports_every_declared_function(lib):
+    names = binding.header_functions()
+    assert set(names) >= {"kda_chunk_fwd", "kda_decode_step", "kda_chunk_fwd_workspace_bytes",
+                          "kda_strerror", "kda_last_error", "kda_abi_version"}
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_version_and_strings(lib):
+    assert lib.kda_abi_version() == 1
+    for code in range(9):
+        assert lib.kda_strerror(code)
+    assert lib.kda_strerror(0) == b"ok"
+    assert lib.kda_last_error() == b""
+
+
+def shape(B=2, H=3, L=100, dk=128, dv=128, qd=binding.KDA_BF16, gd=binding.KDA_F32,
+          mode=binding.KDA_ALPHA_CHANNEL):
+    return binding.KdaShape(B, H, L, dk, dv, qd, gd, mode)
+
+
+def bufs():
+    """Disjoint fake buffers, 64 MiB apart."""
+    names = ["q", "k", "v", "la", "beta", "S0", "o", "Sf"]
+    return {n: BASE + i * 64 * MB for i, n in enumerate(names)}
+
+
+def chunk(lib, s, b, ws=None, wsb=0):
+    return lib.kda_chunk_fwd(ctypes.byref(s) if s is not None else None, b["q"], b["k"], b["v"],
+                             b["la"], b["beta"], b["S0"], b["o"], b["Sf"], ws, wsb, None)
+
+
+def decode(lib, s, b):
+    return lib.kda_decode_step(ctypes.byref(s) if s is not None else None, b["q"], b["k"],
+                               b["v"], b["la"], b["beta"], b["S0"], b["o"], None)
+
+
+def test_workspace_query(lib):
+    assert lib.kda_chunk_fwd_workspace_bytes(ctypes.byref(shape())) == 0
+    assert lib.kda_chunk_fwd_workspace_bytes(None) == 0
+
+
+def test_null_shape(lib):
+    assert chunk(lib, None, bufs()) == 1  # KDA_ERR_NULL
+    assert decode(lib, None, bufs()) == 1
+
+
+@pytest.mark.parametrize("field,value,code", [
+    ("qkv_dtype", 7, 3), ("gate_dtype", -1, 3), ("alpha_mode", 3, 4), ("dk", 96, 2),
+    ("dv", 32, 2), ("B", -1, 2), ("L", -5, 2), ("H", 1 << 40, 2)])
+def test_bad_shape_fields(lib, field, value, code):
+    s = shape()
+    setattr(s, field, value)
+    assert chunk(lib, s, bufs()) == code
+
+
+def test_decode_requires_L1(lib):
+    s = shape(L=2)
+    assert decode(lib, s, bufs()) == 2
+    s = shape(L=0)
+    assert decode(lib, s, bufs()) == 2
+
+
+@pytest.mark.parametrize("name", ["q", "k", "v", "beta", "o"])
+def test_null_pointers(lib, name):
+    b = bufs()
+    b[name] = None
+    assert chunk(lib, shape(), b) == 1
+
+
+def test_null_log_alpha_only_allowed_without_decay(lib):
+    b = bufs()
+    b["la"] = None
+    assert chunk(lib, shape(mode=binding.KDA_ALPHA_HEAD), b) == 1
+    # with alpha_mode NONE, log_alpha is ignored; misalign something else to stop
+    # the call before any launch
+    b["q"] += 2
+    assert chunk(lib, shape(mode=binding.KDA_ALPHA_NONE), b) == 5
+
+
+@pytest.mark.parametrize("name", ["q", "k", "v", "la", "beta", "S0", "o", "Sf"])
+def test_misaligned(lib, name):
+    b = bufs()
+    b[name] += 8
+    assert chunk(lib, shape(), b) == 5
+
+
+def test_aliasing(lib):
+    b = bufs()
+    b["o"] = b["q"] + 1024          # o overlaps q
+    assert chunk(lib, shape(), b) == 7
+    b = bufs()
+    b["Sf"] = b["S0"] + 4096        # partial overlap of S_final and S0
+    assert chunk(lib, shape(), b) == 7
+    b = bufs()
+    b["Sf"] = b["v"]                # final state written over an input
+    assert chunk(lib, shape(), b) == 7
+    b = bufs()
+    b["o"] = b["S0"]                # decode: o overlapping S is rejected too
+    assert decode(lib, shape(L=1), b) == 7
+
+
+def test_empty_problem_is_ok_without_buffers(lib):
+    # B*H == 0: nothing to do, no pointer needed, no HIP call made
+    none = {n: None for n in bufs()}
+    assert chunk(lib, shape(B=0), none) == 0
+    assert decode(lib, shape(B=0, L=1), none) == 0
+
+
+def test_header_mentions_every_status():
+    text = open(binding.HEADER).read()
+    for name in binding.STATUS.values():
+        assert name in text

@@ -1,0 +1,118 @@
+"""Parity of kda_decode_step (HIP, through the C ABI) with the fp64 CPU oracle.
+
+T decode steps of one token per sequence are the recurrence over a T-token
+sequence, so the oracle runs once over the stacked steps and is compared with
+every step's o and the final in-place state.
+"""
+
+import numpy as np
+import pytest
+
+import oracle
+from linear_attention_sequence_kda_amd import inputs as gen
+
+from gpu_util import TOL, device_inputs, flat_heads, oracle_prefill, say, to_dev, to_f64
+
+pytestmark = pytest.mark.gpu
+
+
+def _kda():
+    import linear_attention_sequence_kda_amd as kda
+    return kda
+
+
+def run_decode(w: gen.Workload, steps: int, label: str):
+    import torch
+    kda = _kda()
+    S0 = gen.decode_state(w)
+    S = to_dev(S0, gen.F32) if S0 is not None else torch.zeros(
+        (w.B, w.H, w.dk, w.dv), dtype=torch.float32, device="cuda:0")
+    outs, per_step = [], []
+    for t in range(steps):
+        x = gen.decode_inputs(w, t)
+        per_step.append(x)
+        dq = to_dev(x["q"], w.qkv_dtype)
+        dk_ = to_dev(x["k"], w.qkv_dtype)
+        dv_ = to_dev(x["v"], w.qkv_dtype)
+        dla = to_dev(x["log_alpha"], w.gate_dtype)
+        db = to_dev(x["beta"], w.gate_dtype)
+        if t == 0:
+            say(f"{label}: decode B={w.B} H={w.H} dk={w.dk} dv={w.dv} "
+                f"{w.qkv_dtype}/{w.gate_dtype}/{w.alpha_mode} steps={steps}")
+        outs.append(kda.decode_step(dq, dk_, dv_, dla, db, S))
+    torch.cuda.synchronize()
+    N = w.B * w.H
+    stack = lambda key: None if per_step[0][key] is None else np.stack(
+        [p[key] for p in per_step], axis=2).reshape((N, steps) + per_step[0][key].shape[2:])
+    o_ref, S_ref = oracle.forward(stack("q"), stack("k"), stack("v"), stack("log_alpha"),
+                                  stack("beta"),
+                                  None if S0 is None else S0.reshape(N, w.dk, w.dv),
+                                  qkv_dtype=w.qkv_dtype, gate_dtype=w.gate_dtype,
+                                  alpha_mode=w.alpha_mode)
+    og = np.stack([to_f64(o) for o in outs], axis=2).reshape(N, steps, w.dv)
+    e_o = oracle.slab_error(og, o_ref, 1)
+    e_s = oracle.slab_error(to_f64(S).reshape(N, w.dk, w.dv), S_ref, 1)
+    tol = TOL[w.qkv_dtype]
+    say(f"{label}: err o={e_o:.3e} S={e_s:.3e} (tol {tol})")
+    assert e_o <= tol and e_s <= tol
+
+
+DTYPES = [("f32", "f32", "none"), ("f32", "f32", "head"), ("f32", "f32", "channel"),
+          ("bf16", "f32", "channel"), ("bf16", "bf16", "channel"), ("bf16", "f32", "head"),
+          ("bf16", "bf16", "none")]
+
+
+@pytest.mark.parametrize("qd,gd,mode", DTYPES, ids=lambda x: str(x))
+@pytest.mark.parametrize("dk,dv", [(64, 64), (128, 128), (128, 64), (64, 128)], ids=str)
+def test_small_decode(qd, gd, mode, dk, dv):
+    w = gen.Workload("decode_small", 3, 5, 1, dk, dv, qd, gd, mode, -4.0, 0.5, 0.02,
+                     seed=dk + dv, decode_steps=6)
+    run_decode(w, 6, "small")
+
+
+def test_decode_workload_full():
+    w = gen.WORKLOADS[5]
+    run_decode(w, w.decode_steps, "workload5")
+
+
+def test_prefill_then_decode_handoff():
+    """chunk_fwd over L tokens, then decode steps continue the same sequences."""
+    import torch
+    kda = _kda()
+    L, T = 150, 5
+    w = gen.custom(B=2, H=4, L=L + T, dk=128, dv=128, qkv_dtype="bf16", gate_dtype="f32",
+                   alpha_mode="channel", seed=44)
+    x = gen.prefill_inputs(w)
+    d = device_inputs(w, x)
+    pre = {n: d[n][:, :, :L].contiguous() for n in ("q", "k", "v", "log_alpha", "beta")}
+    say("handoff: prefill")
+    o_pre, S = kda.chunk_fwd(pre["q"], pre["k"], pre["v"], pre["log_alpha"], pre["beta"],
+                             d["S0"])
+    outs = []
+    for t in range(L, L + T):
+        step = {n: d[n][:, :, t].contiguous() for n in ("q", "k", "v", "log_alpha", "beta")}
+        outs.append(kda.decode_step(step["q"], step["k"], step["v"], step["log_alpha"],
+                                    step["beta"], S))
+    torch.cuda.synchronize()
+    o_ref, S_ref = oracle_prefill(w, flat_heads(x, 8))
+    og = np.concatenate([to_f64(o_pre), np.stack([to_f64(o) for o in outs], axis=2)],
+                        axis=2).reshape(8, L + T, 128)
+    assert oracle.slab_error(og, o_ref, 1) <= TOL["bf16"]
+    assert oracle.slab_error(to_f64(S).reshape(8, 128, 128), S_ref, 1) <= TOL["bf16"]
+
+
+def test_decode_deterministic():
+    import torch
+    kda = _kda()
+    w = gen.WORKLOADS[5].replace(B=16)
+    x = gen.decode_inputs(w, 0)
+    S0 = to_dev(gen.decode_state(w)[:16], gen.F32)
+    args = [to_dev(x[n], w.qkv_dtype if n in "qkv" else w.gate_dtype)
+            for n in ("q", "k", "v", "log_alpha", "beta")]
+    say("decode determinism")
+    S1 = S0.clone()
+    o1 = kda.decode_step(*args, S1)
+    S2 = S0.clone()
+    o2 = kda.decode_step(*args, S2)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(S1, S2)

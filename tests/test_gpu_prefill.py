@@ -1,0 +1,261 @@
+"""Parity of kda_chunk_fwd (HIP, through the C ABI) with the fp64 CPU oracle.
+
+Metric: per (b, h) slab, max|x - ref| / max|ref|, worst slab; o and S_final
+each.  Bar: 1e-4 for fp32 inputs, 2e-2 for bf16 inputs.
+"""
+
+import numpy as np
+import pytest
+
+import oracle
+from linear_attention_sequence_kda_amd import inputs as gen
+
+from gpu_util import TOL, device_inputs, flat_heads, oracle_prefill, say, to_dev, to_f64
+
+pytestmark = pytest.mark.gpu
+
+
+def _kda():
+    import linear_attention_sequence_kda_amd as kda
+    return kda
+
+
+def run_and_compare(w: gen.Workload, label: str, tol=None):
+    import torch
+    kda = _kda()
+    x = gen.prefill_inputs(w)
+    N = w.B * w.H
+    d = device_inputs(w, x)
+    say(f"{label}: chunk_fwd B={w.B} H={w.H} L={w.L} dk={w.dk} dv={w.dv} "
+        f"{w.qkv_dtype}/{w.gate_dtype}/{w.alpha_mode} seed={w.seed}")
+    o, Sf = kda.chunk_fwd(d["q"], d["k"], d["v"], d["log_alpha"], d["beta"], d["S0"])
+    torch.cuda.synchronize()
+    xf = flat_heads(x, N)
+    o_ref, S_ref = oracle_prefill(w, xf)
+    tol = TOL[w.qkv_dtype] if tol is None else tol
+    e_o = oracle.slab_error(to_f64(o).reshape(N, w.L, w.dv), o_ref, 1)
+    e_s = oracle.slab_error(to_f64(Sf).reshape(N, w.dk, w.dv), S_ref, 1)
+    say(f"{label}: err o={e_o:.3e} S={e_s:.3e} (tol {tol})")
+    assert e_o <= tol, f"o error {e_o}"
+    assert e_s <= tol, f"S_final error {e_s}"
+    return o, Sf
+
+
+DTYPES = [("f32", "f32", "none"), ("f32", "f32", "head"), ("f32", "f32", "channel"),
+          ("bf16", "f32", "head"), ("bf16", "bf16", "channel"), ("bf16", "f32", "channel"),
+          ("bf16", "bf16", "none"), ("f32", "bf16", "channel")]
+DIMS = [(64, 64), (128, 128), (128, 64), (64, 128)]
+
+
+@pytest.mark.parametrize("qd,gd,mode", DTYPES, ids=lambda x: str(x))
+@pytest.mark.parametrize("dk,dv", DIMS, ids=lambda x: str(x))
+@pytest.mark.parametrize("L", [1, 65, 200])
+def test_small_shapes(qd, gd, mode, dk, dv, L):
+    w = gen.custom(B=2, H=2, L=L, dk=dk, dv=dv, qkv_dtype=qd, gate_dtype=gd, alpha_mode=mode,
+                   seed=1000 + L + dk + dv)
+    run_and_compare(w, "small")
+
+
+@pytest.mark.parametrize("L", [63, 64, 127, 128, 129, 640])
+def test_chunk_boundaries(L):
+    w = gen.custom(B=1, H=3, L=L, dk=128, dv=128, qkv_dtype="bf16", gate_dtype="bf16",
+                   alpha_mode="channel", seed=L)
+    run_and_compare(w, "boundary")
+
+
+@pytest.mark.parametrize("B,H,dk,dv,qd", [(2, 32, 128, 128, "bf16"),    # 32-column slices
+                                          (4, 16, 128, 64, "bf16"),     # 32-column slices, dv 64
+                                          (4, 64, 64, 64, "bf16"),      # 64-column slices
+                                          (2, 64, 64, 128, "f32"),      # fp32, 32-column slices
+                                          (2, 64, 128, 128, "f32")])
+def test_slice_widths(B, H, dk, dv, qd):
+    w = gen.custom(B=B, H=H, L=150, dk=dk, dv=dv, qkv_dtype=qd, gate_dtype="f32",
+                   alpha_mode="channel", seed=B * H)
+    run_and_compare(w, "slices")
+
+
+@pytest.mark.parametrize("cfg", [1, 2, 3])
+def test_workload_full(cfg):
+    run_and_compare(gen.WORKLOADS[cfg], f"workload{cfg}")
+
+
+def test_long_context_sampled():
+    """The long-context workload at full size; the oracle computes two heads
+    and a block of state columns (columns of S evolve independently)."""
+    import torch
+    kda = _kda()
+    w = gen.WORKLOADS[4]
+    say("workload4: drawing inputs")
+    x = gen.prefill_inputs(w, threads=16)
+    d = device_inputs(w, x)
+    say("workload4: chunk_fwd full size")
+    o, Sf = kda.chunk_fwd(d["q"], d["k"], d["v"], d["log_alpha"], d["beta"], d["S0"])
+    torch.cuda.synchronize()
+    del d
+    heads = [0, 11]
+    col0, ncols = 40, 24
+    xs = {k: (None if v is None else np.ascontiguousarray(v[0, heads])) for k, v in x.items()}
+    say("workload4: oracle on sampled heads/columns")
+    o_ref, S_ref = oracle.forward(xs["q"], xs["k"], xs["v"], xs["log_alpha"], xs["beta"], None,
+                                  qkv_dtype="bf16", gate_dtype="bf16", alpha_mode="channel",
+                                  col0=col0, ncols=ncols)
+    og = to_f64(o[0, heads, :, col0:col0 + ncols])
+    sg = to_f64(Sf[0, heads, :, col0:col0 + ncols])
+    e_o = oracle.slab_error(og, o_ref, 1)
+    e_s = oracle.slab_error(sg, S_ref, 1)
+    say(f"workload4: err o={e_o:.3e} S={e_s:.3e}")
+    assert e_o <= TOL["bf16"] and e_s <= TOL["bf16"]
+    assert torch.isfinite(o).all() and torch.isfinite(Sf).all()
+
+
+# ---------------------------------------------------------------------------
+# edge cases
+# ---------------------------------------------------------------------------
+
+def test_empty_sequence_returns_initial_state():
+    import torch
+    kda = _kda()
+    w = gen.custom(B=2, H=3, L=0, dk=128, dv=128, qkv_dtype="bf16", gate_dtype="f32")
+    q = torch.empty((2, 3, 0, 128), dtype=torch.bfloat16, device="cuda:0")
+    la = torch.empty((2, 3, 0, 128), dtype=torch.float32, device="cuda:0")
+    beta = torch.empty((2, 3, 0), dtype=torch.float32, device="cuda:0")
+    S0 = torch.randn((2, 3, 128, 128), device="cuda:0")
+    say("empty: L=0")
+    o, Sf = kda.chunk_fwd(q, q, q, la, beta, S0)
+    torch.cuda.synchronize()
+    assert o.shape == (2, 3, 0, 128)
+    assert torch.equal(Sf, S0)
+    o, Sf = kda.chunk_fwd(q, q, q, la, beta, None)
+    torch.cuda.synchronize()
+    assert torch.count_nonzero(Sf) == 0
+
+
+def test_zero_inputs_keep_state_bitwise():
+    import torch
+    kda = _kda()
+    B, H, L, d = 1, 4, 100, 128
+    z = torch.zeros((B, H, L, d), dtype=torch.bfloat16, device="cuda:0")
+    la = torch.zeros((B, H, L, d), dtype=torch.bfloat16, device="cuda:0")
+    beta = torch.rand((B, H, L), device="cuda:0").to(torch.bfloat16)
+    S0 = torch.randn((B, H, d, d), device="cuda:0")
+    say("zeros")
+    o, Sf = kda.chunk_fwd(z, z, z, la, beta, S0)
+    torch.cuda.synchronize()
+    assert torch.count_nonzero(o) == 0
+    assert torch.equal(Sf, S0)
+
+
+def test_exact_replacement_on_gpu():
+    """beta = 1 and q = k (unit keys) must read back each value."""
+    import torch
+    kda = _kda()
+    w = gen.custom(B=1, H=4, L=130, dk=128, dv=128, qkv_dtype="f32", gate_dtype="f32",
+                   alpha_mode="channel", seed=9)
+    x = gen.prefill_inputs(w)
+    d = device_inputs(w, x)
+    ones = torch.ones_like(d["beta"])
+    say("replacement")
+    o, _ = kda.chunk_fwd(d["k"], d["k"], d["v"], d["log_alpha"], ones, d["S0"])
+    torch.cuda.synchronize()
+    v = to_f64(d["v"])
+    err = np.abs(to_f64(o) - v).max() / np.abs(v).max()
+    assert err <= 1e-4
+
+
+def test_in_place_final_state():
+    import torch
+    kda = _kda()
+    w = gen.custom(B=2, H=4, L=100, dk=128, dv=128, qkv_dtype="bf16", gate_dtype="bf16", seed=3)
+    x = gen.prefill_inputs(w)
+    d = device_inputs(w, x)
+    say("in-place S_final = S0")
+    o1, S1 = kda.chunk_fwd(d["q"], d["k"], d["v"], d["log_alpha"], d["beta"], d["S0"])
+    S = d["S0"].clone()
+    o2, S2 = kda.chunk_fwd(d["q"], d["k"], d["v"], d["log_alpha"], d["beta"], S, S_final=S)
+    torch.cuda.synchronize()
+    assert S2.data_ptr() == S.data_ptr()
+    assert torch.equal(o1, o2) and torch.equal(S1, S2)
+
+
+@pytest.mark.parametrize("split", [37, 64, 100])
+def test_split_sequence_state_passing(split):
+    import torch
+    kda = _kda()
+    w = gen.custom(B=1, H=4, L=200, dk=128, dv=128, qkv_dtype="bf16", gate_dtype="bf16",
+                   alpha_mode="channel", seed=21)
+    x = gen.prefill_inputs(w)
+    d = device_inputs(w, x)
+    sl = lambda t, a, b: t[:, :, a:b].contiguous()
+    say(f"split at {split}")
+    o1, Sm = kda.chunk_fwd(*(sl(d[n], 0, split) for n in ("q", "k", "v", "log_alpha", "beta")),
+                           d["S0"])
+    o2, Se = kda.chunk_fwd(*(sl(d[n], split, 200) for n in ("q", "k", "v", "log_alpha", "beta")),
+                           Sm)
+    torch.cuda.synchronize()
+    xf = flat_heads(x, 4)
+    o_ref, S_ref = oracle_prefill(w, xf)
+    og = np.concatenate([to_f64(o1), to_f64(o2)], axis=2).reshape(4, 200, 128)
+    assert oracle.slab_error(og, o_ref, 1) <= TOL["bf16"]
+    assert oracle.slab_error(to_f64(Se).reshape(4, 128, 128), S_ref, 1) <= TOL["bf16"]
+
+
+def test_nan_stays_in_its_head():
+    import torch
+    kda = _kda()
+    w = gen.custom(B=1, H=4, L=130, dk=128, dv=128, qkv_dtype="bf16", gate_dtype="bf16", seed=5)
+    x = gen.prefill_inputs(w)
+    d = device_inputs(w, x)
+    d["v"][0, 2, 70, 5] = float("nan")
+    say("nan confinement")
+    o, Sf = kda.chunk_fwd(d["q"], d["k"], d["v"], d["log_alpha"], d["beta"], d["S0"])
+    torch.cuda.synchronize()
+    for h in (0, 1, 3):
+        assert torch.isfinite(o[0, h]).all() and torch.isfinite(Sf[0, h]).all()
+    assert not torch.isfinite(o[0, 2]).all()
+
+
+def test_deterministic():
+    import torch
+    kda = _kda()
+    w = gen.custom(B=2, H=32, L=300, dk=128, dv=128, qkv_dtype="bf16", gate_dtype="bf16", seed=8)
+    x = gen.prefill_inputs(w)
+    d = device_inputs(w, x)
+    say("determinism")
+    ref = kda.chunk_fwd(d["q"], d["k"], d["v"], d["log_alpha"], d["beta"], d["S0"])
+    for _ in range(5):
+        o, Sf = kda.chunk_fwd(d["q"], d["k"], d["v"], d["log_alpha"], d["beta"], d["S0"])
+        torch.cuda.synchronize()
+        assert torch.equal(o, ref[0]) and torch.equal(Sf, ref[1])
+
+
+def test_strong_decay_documented_range():
+    """ln(alpha) down to -5 per token and channel stays within tolerance."""
+    w = gen.custom(B=1, H=4, L=200, dk=128, dv=128, qkv_dtype="bf16", gate_dtype="f32",
+                   alpha_mode="channel", seed=31, la_mu=1.2, la_sigma=0.3)
+    x = gen.prefill_inputs(w)
+    x["log_alpha"] = np.maximum(x["log_alpha"], -5.0).astype(np.float32)
+    import torch
+    kda = _kda()
+    d = device_inputs(w, x)
+    say("strong decay")
+    o, Sf = kda.chunk_fwd(d["q"], d["k"], d["v"], d["log_alpha"], d["beta"], d["S0"])
+    torch.cuda.synchronize()
+    o_ref, S_ref = oracle_prefill(w, flat_heads(x, 4))
+    assert oracle.slab_error(to_f64(o).reshape(4, 200, 128), o_ref, 1) <= TOL["bf16"]
+    assert oracle.slab_error(to_f64(Sf).reshape(4, 128, 128), S_ref, 1) <= TOL["bf16"]
+
+
+def test_head_gate_equals_broadcast_channel_gate():
+    import torch
+    kda = _kda()
+    w = gen.custom(B=1, H=4, L=150, dk=128, dv=128, qkv_dtype="bf16", gate_dtype="f32",
+                   alpha_mode="head", seed=12)
+    x = gen.prefill_inputs(w)
+    d = device_inputs(w, x)
+    la_c = d["log_alpha"][..., None].expand(1, 4, 150, 128).contiguous()
+    say("head vs channel gate")
+    a = kda.chunk_fwd(d["q"], d["k"], d["v"], d["log_alpha"], d["beta"], d["S0"])
+    b = kda.chunk_fwd(d["q"], d["k"], d["v"], la_c, d["beta"], d["S0"])
+    torch.cuda.synchronize()
+    assert torch.allclose(a[0].float(), b[0].float(), atol=1e-2, rtol=1e-2)
+    assert torch.allclose(a[1], b[1], atol=1e-3, rtol=1e-3)
