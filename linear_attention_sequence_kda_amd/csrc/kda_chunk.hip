@@ -2,11 +2,11 @@
 // for gfx950 (MI355X).
 //
 // Math: "22,580: From GPT-2 to Kimi K3" (yichencityu.github.io) section 6.3 gives
-// the alpha = 1 chunk form; the gated, per-channel form below follows from
-// unrolling the recurrence inside a chunk (the pages stop before printing it,
-// sections 08 and 9.1).  For a chunk of C
-// tokens entering with state S, with g_r = sum_{s<=r} ln(alpha_s) per key
-// channel (inclusive, chunk-relative):
+// the alpha = 1 chunk form; the gated and per-channel forms below follow from
+// unrolling the recurrence inside a chunk (the pages stop before printing them,
+// sections 08 and 9.1).  For a chunk of C tokens entering with state S, with
+// g_r = sum_{s<=r} ln(alpha_s) (chunk-relative, inclusive; per key channel in
+// KDA, per token otherwise):
 //
 //   A_rj = beta_r sum_c k_rc k_jc e^{g_rc - g_jc}   (j < r)       strictly lower
 //   T    = (I + A)^-1                                             forward substitution
@@ -21,32 +21,38 @@
 //
 // One workgroup (4 waves) owns one (b, h) head and one slice of NV state
 // columns; columns of S evolve independently, so slices never talk.  It walks
-// the chunks in order with its fp32 state slice resident in registers.  Per
-// chunk:
-//   G  load q, k, ln(alpha), beta, v; per-channel decay factors in 16-token
-//      sub-blocks; scaled K/Q tiles into LDS
-//   AP A and P, 16x16 blocks, MFMA (k = key channels)
+// the chunks in order with its fp32 state slice resident in registers, and
+// fetches chunk i+1's inputs into registers while chunk i computes.  Per chunk:
+//   G  inputs to LDS (and decay factors)
+//   AP A and P in 16x16 blocks on MFMA (k = key channels)
 //   T  diagonal 16x16 blocks of T by forward substitution (one lane per column),
-//      off-diagonal blocks by the block formula T_RJ = -T_RR sum_M A_RM T_MJ on
-//      fp32 MFMA; T' = T diag(beta) rounded to the operand type
+//      off-diagonal blocks by T_RJ = -T_RR sum_M A_RM T_MJ on fp32 MFMA; each
+//      block is also written as T diag(beta) in operand precision
 //   S  X = V - K~ S;  u = T' X;  o = Q~ S + P u;  S = e^{g_n} S + K^^T u
 //
-// Decay inside A and P, e^{g_r - g_j}, is split at the end of r's 16-token
-// sub-block R (cumulative G_{R+1}): the row operand carries e^{g_r - G_{R+1}}
-// (>= 1, at most e^{16 |ln alpha|}), the column operand e^{G_{J+1} - g_j} (<= 1)
-// and, for J < R, a per-channel pair scale e^{G_{R+1} - G_{J+1}} (<= 1).  A
-// diagonal pair therefore uses both stored operands unscaled (one bf16 rounding
-// each).  The bound on the row factor is why the GPU path asks for
+// Scalar decay (one alpha per token: Gated DeltaNet, or alpha = 1): e^{g_r - g_j}
+// leaves every channel sum, so A, P, K S and Q S take the stored bf16 inputs as
+// MFMA operands unchanged and the decay is applied to the fp32 results.
+//
+// Per-channel decay (KDA): e^{g_rc - g_jc} stays inside the sums and is split
+// at the end of r's 16-token sub-block R (cumulative G_{R+1}): the row operand
+// carries e^{g_r - G_{R+1}} (>= 1, at most e^{16 |ln alpha|}), the column
+// operand e^{G_{J+1} - g_j} (<= 1) and, for J < R, a per-channel pair scale
+// e^{G_{R+1} - G_{J+1}} (<= 1).  A diagonal pair therefore uses both stored
+// operands unscaled.  The bound on the row factor is why the KDA path asks for
 // ln(alpha) >= -5 per token and channel.
+#include <type_traits>
+
 #include "kda_device.h"
 #include "kda_internal.h"
 
 namespace kda {
 
-template <int DK_, int NV_, int C_, typename E_>
+template <int DK_, int NV_, int C_, typename E_, int AMODE_>
 struct ChunkCfg {
     typedef E_ E;
-    static constexpr int DK = DK_, NV = NV_, C = C_;
+    static constexpr int DK = DK_, NV = NV_, C = C_, AMODE = AMODE_;
+    static constexpr bool KDA = AMODE == KDA_ALPHA_CHANNEL;  // per-channel decay
     static constexpr int NB = C / 16;                  // 16-token sub-blocks per chunk
     static constexpr int NPAIR = NB * (NB + 1) / 2;    // (R, J <= R) block pairs
     static constexpr int ESZ = sizeof(E);
@@ -55,15 +61,20 @@ struct ChunkCfg {
     static constexpr int PC = C + PADE;                // pitch of [*][C] tiles
     static constexpr int PV = NV + PADE;               // pitch of [C][NV] tiles
     static constexpr int PA = C + 4;                   // pitch of the fp32 A/T tile
+    static constexpr int PD = 20;                      // pitch of a transposed 16x16 fp32 block
     static constexpr int NCB = DK / 16, NVB = NV / 16; // 16x16 blocks of the state slice
     static constexpr int NTHREADS = 256;
 
-    // LDS byte offsets
+    // LDS byte offsets.  Tiles: K row operand (KDA: k e^{g-G_{R+1}}; scalar: k),
+    // Q row operand, KDA column operand k e^{G_{J+1}-g}, the S-update operand
+    // (K e^{g_n-g})^T (KDA) or K^T (scalar), T', P, v slice, S^T (double
+    // buffered), X^T (then o), u^T, scalar only: (e^{g_n-g} u)^T.
     static constexpr int O_KR = 0;
     static constexpr int O_QR = O_KR + C * PK * ESZ;
     static constexpr int O_KC = O_QR + C * PK * ESZ;
-    static constexpr int O_KHT = O_KC + C * PK * ESZ;
-    static constexpr int O_TB = O_KHT + DK * PC * ESZ;
+    static constexpr int SZ_KC = KDA ? C * PK * ESZ : 0;
+    static constexpr int O_KT = O_KC + SZ_KC;
+    static constexpr int O_TB = O_KT + DK * PC * ESZ;
     static constexpr int O_P = O_TB + C * PC * ESZ;
     static constexpr int O_V = O_P + C * PC * ESZ;
     static constexpr int O_ST0 = O_V + C * PV * ESZ;
@@ -71,35 +82,21 @@ struct ChunkCfg {
     static constexpr int SZ_XT = (NV * PC > C * PV ? NV * PC : C * PV) * ESZ;  // X^T, then o
     static constexpr int O_XT = O_ST1 + NV * PK * ESZ;
     static constexpr int O_UT = O_XT + SZ_XT;
-    static constexpr int O_A = O_UT + NV * PC * ESZ;
-    static constexpr int O_Z = O_A + C * PA * 4;
-    static constexpr int O_E = O_Z + NB * DK * 4;
-    static constexpr int O_Y = O_E + NB * DK * 4;
-    static constexpr int O_GN = O_Y + NPAIR * DK * 4;
-    static constexpr int O_BETA = O_GN + DK * 4;
+    static constexpr int O_UHT = O_UT + NV * PC * ESZ;
+    static constexpr int SZ_UHT = KDA ? 0 : NV * PC * ESZ;
+    static constexpr int O_A = O_UHT + SZ_UHT;
+    static constexpr int O_AD = O_A + C * PA * 4;      // transposed diagonal blocks of A
+    static constexpr int O_GATE = O_AD + NB * 16 * PD * 4;
+    // KDA gate area: Z[NB][DK], E'[NB][DK], Y'[NPAIR][DK], e^{g_n}[DK]
+    // scalar gate area: g[C], e^g[C], e^{g_n-g}[C], e^{g_n} (one float, padded)
+    static constexpr int SZ_GATE = KDA ? (2 * NB + NPAIR + 1) * DK * 4 : (3 * C + 4) * 4;
+    static constexpr int O_BETA = O_GATE + SZ_GATE;
     static constexpr int LDS_BYTES = O_BETA + C * 4;
 
     static_assert(DK % 32 == 0 && NV % 16 == 0 && (C == 32 || C == 64), "tile shape");
     static_assert((NCB * NVB) % 4 == 0, "state blocks split evenly over 4 waves");
     static_assert(LDS_BYTES <= 160 * 1024, "LDS budget of one gfx950 CU");
 };
-
-// ---- global loads of two adjacent elements ---------------------------------
-__device__ __forceinline__ floatx2 ld2(const bf16* p) {
-    bf16x2 v = *(const bf16x2*)p;
-    floatx2 r;
-    r[0] = (float)v[0];
-    r[1] = (float)v[1];
-    return r;
-}
-__device__ __forceinline__ floatx2 ld2(const float* p) { return *(const floatx2*)p; }
-
-__device__ __forceinline__ float ld_gate(const void* p, int64_t i, bool bf) {
-    return bf ? (float)((const bf16*)p)[i] : ((const float*)p)[i];
-}
-__device__ __forceinline__ floatx2 ld_gate2(const void* p, int64_t i, bool bf) {
-    return bf ? ld2((const bf16*)p + i) : ld2((const float*)p + i);
-}
 
 template <typename E>
 __device__ __forceinline__ void st2(E* p, float a, float b) {
@@ -116,6 +113,20 @@ __device__ __forceinline__ void st2(E* p, float a, float b) {
     }
 }
 
+template <typename E>
+__device__ __forceinline__ void st4(E* p, floatx4 v) {
+    if constexpr (sizeof(E) == 2) {
+        bf16x4 t;
+        t[0] = (bf16)v[0];
+        t[1] = (bf16)v[1];
+        t[2] = (bf16)v[2];
+        t[3] = (bf16)v[3];
+        *(bf16x4*)p = t;
+    } else {
+        *(floatx4*)p = v;
+    }
+}
+
 __device__ __forceinline__ void pair_of(int p, int& R, int& J) {
     R = 0;
     while (p >= R + 1) {
@@ -125,21 +136,48 @@ __device__ __forceinline__ void pair_of(int p, int& R, int& J) {
     J = p;
 }
 
-template <class Cfg>
+// Load through a uniform base pointer plus a 32-bit byte offset (saddr form).
+template <typename T>
+__device__ __forceinline__ T ldg(const void* base, uint32_t byte_off) {
+    return *(const T*)((const char*)base + byte_off);
+}
+
+// Transpose a TW x TW tile held as TW rows of 16 bytes (TW = 8 bf16 or 4 fp32).
+__device__ __forceinline__ void transpose_tile(const uint4 (&in)[8], uint4 (&out)[8]) {
+    const uint32_t* r = (const uint32_t*)in;  // r[4*i + d]: row i, dword d
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        const uint32_t sel = (e & 1) ? 0x07060302u : 0x05040100u;
+        uint32_t o[4];
+#pragma unroll
+        for (int m = 0; m < 4; ++m)
+            o[m] = __builtin_amdgcn_perm(r[4 * (2 * m + 1) + (e >> 1)], r[4 * (2 * m) + (e >> 1)], sel);
+        out[e] = make_uint4(o[0], o[1], o[2], o[3]);
+    }
+}
+__device__ __forceinline__ void transpose_tile(const uint4 (&in)[4], uint4 (&out)[4]) {
+    const uint32_t* r = (const uint32_t*)in;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) out[e] = make_uint4(r[e], r[4 + e], r[8 + e], r[12 + e]);
+}
+
+template <class Cfg, bool GBF>
 __global__ void __launch_bounds__(256)
 kda_chunk_kernel(ChunkParams prm) {
     typedef typename Cfg::E E;
     typedef Frag<E> F;
-    constexpr int DK = Cfg::DK, NV = Cfg::NV, C = Cfg::C, NB = Cfg::NB;
-    constexpr int PK = Cfg::PK, PC = Cfg::PC, PV = Cfg::PV, PA = Cfg::PA;
+    constexpr int DK = Cfg::DK, NV = Cfg::NV, C = Cfg::C, NB = Cfg::NB, AMODE = Cfg::AMODE;
+    constexpr bool KDA = Cfg::KDA;
+    constexpr int PK = Cfg::PK, PC = Cfg::PC, PV = Cfg::PV, PA = Cfg::PA, PD = Cfg::PD;
     constexpr int NCB = Cfg::NCB, NVB = Cfg::NVB;
     constexpr int SB_PER_WAVE = NCB * NVB / 4;
+    constexpr int ESZ = Cfg::ESZ;
 
     __shared__ __attribute__((aligned(16))) char smem[Cfg::LDS_BYTES];
     E* sKr = (E*)(smem + Cfg::O_KR);
     E* sQr = (E*)(smem + Cfg::O_QR);
     E* sKc = (E*)(smem + Cfg::O_KC);
-    E* sKhT = (E*)(smem + Cfg::O_KHT);
+    E* sKT = (E*)(smem + Cfg::O_KT);
     E* sTb = (E*)(smem + Cfg::O_TB);
     E* sP = (E*)(smem + Cfg::O_P);
     E* sV = (E*)(smem + Cfg::O_V);
@@ -148,12 +186,21 @@ kda_chunk_kernel(ChunkParams prm) {
     E* sXT = (E*)(smem + Cfg::O_XT);
     E* sO = (E*)(smem + Cfg::O_XT);  // o tile reuses the X^T area after u is formed
     E* sUT = (E*)(smem + Cfg::O_UT);
+    E* sUhT = (E*)(smem + Cfg::O_UHT);
     float* sA = (float*)(smem + Cfg::O_A);
-    float* sZ = (float*)(smem + Cfg::O_Z);
-    float* sE = (float*)(smem + Cfg::O_E);
-    float* sY = (float*)(smem + Cfg::O_Y);
-    float* sGn = (float*)(smem + Cfg::O_GN);
+    float* sAd = (float*)(smem + Cfg::O_AD);
+    float* sGate = (float*)(smem + Cfg::O_GATE);
     float* sBeta = (float*)(smem + Cfg::O_BETA);
+    // KDA gate views
+    float* sZ = sGate;
+    float* sE = sGate + NB * DK;
+    float* sY = sGate + 2 * NB * DK;
+    float* sGnv = sGate + (2 * NB + Cfg::NPAIR) * DK;
+    // scalar gate views
+    float* sG = sGate;
+    float* sEg = sGate + C;
+    float* sEgn = sGate + 2 * C;
+    float* sGn1 = sGate + 3 * C;
 
     const int tid = threadIdx.x;
     const int w = tid >> 6;
@@ -171,14 +218,16 @@ kda_chunk_kernel(ChunkParams prm) {
     const int v0 = slice * NV;
     const int64_t L = prm.L;
     const int DV = prm.DV;
-    const bool gbf = prm.gate_bf16 != 0;
-    const int amode = prm.alpha_mode;
 
-    const E* gq = (const E*)prm.q + (int64_t)bh * L * DK;
-    const E* gk = (const E*)prm.k + (int64_t)bh * L * DK;
-    const E* gv = (const E*)prm.v + (int64_t)bh * L * DV;
-    E* go = (E*)prm.o + (int64_t)bh * L * DV;
-    const int64_t gate_head = (int64_t)bh * L;  // token index base for beta / head-mode gate
+    // per-head base pointers (64-bit, uniform); all offsets below are 32-bit
+    const char* gq = (const char*)prm.q + (int64_t)bh * L * DK * ESZ;
+    const char* gk = (const char*)prm.k + (int64_t)bh * L * DK * ESZ;
+    const char* gv = (const char*)prm.v + (int64_t)bh * L * DV * ESZ + v0 * ESZ;
+    char* go = (char*)prm.o + (int64_t)bh * L * DV * ESZ + v0 * ESZ;
+    constexpr int GSZ = GBF ? 2 : 4;
+    const char* gla = (const char*)prm.log_alpha +
+                      (int64_t)bh * L * (KDA ? DK : 1) * GSZ;
+    const char* gbeta = (const char*)prm.beta + (int64_t)bh * L * GSZ;
 
     // ---- zero the triangular operand tiles once (upper blocks stay zero) ---
     for (int i = tid; i < C * PC; i += Cfg::NTHREADS) {
@@ -188,180 +237,309 @@ kda_chunk_kernel(ChunkParams prm) {
 
     // ---- initial state slice into registers, and its operand copy ----------
     floatx4 Sreg[SB_PER_WAVE];
+    if (prm.S0) {  // uniform branch: all loads issue before the first use
+        const float* s0 = prm.S0 + (int64_t)bh * DK * DV + v0;
+#pragma unroll
+        for (int i = 0; i < SB_PER_WAVE; ++i) {
+            const int item = w + 4 * i;
+            const int cb = item % NCB, vb = item / NCB;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int row = 16 * cb + 4 * lq + e;
+                Sreg[i][e] = s0[row * DV + 16 * vb + lr];
+            }
+        }
+    } else {
+#pragma unroll
+        for (int i = 0; i < SB_PER_WAVE; ++i) Sreg[i] = floatx4{0.f, 0.f, 0.f, 0.f};
+    }
 #pragma unroll
     for (int i = 0; i < SB_PER_WAVE; ++i) {
         const int item = w + 4 * i;
         const int cb = item % NCB, vb = item / NCB;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const int row = 16 * cb + 4 * lq + e;
-            Sreg[i][e] = prm.S0 ? prm.S0[((int64_t)bh * DK + row) * DV + v0 + 16 * vb + lr] : 0.f;
-        }
         store_acc_transposed<E>(sST0 + (16 * vb) * PK + 16 * cb, PK, Sreg[i]);
     }
 
+    // ---- raw registers of the next chunk's inputs ---------------------------
+    // Every load reads a clamped, in-bounds token (the last valid one of a
+    // ragged tail) and is masked when used, so the loads carry no branches and
+    // all stay in flight together while the previous chunk computes.
+    constexpr int VPIECE = 16 / ESZ;              // elements per 16-byte piece
+    constexpr int VPPR = NV / VPIECE;             // pieces per row of the v slice
+    constexpr int VPT = (C * VPPR + 255) / 256;   // pieces per thread
+    uint4 rv[VPT];
+    uint32_t rb = 0, rla = 0;
+
+    // KDA: thread (cp, bg) owns channel pair c0 = 2cp of sub-block R = bg
+    constexpr int NCP = DK / 2;
+    const int cp = tid % NCP, bg = tid / NCP;
+    const int c0 = 2 * cp;
+    const int myR = (bg < NB) ? bg : -1;
+    typedef typename std::conditional<sizeof(E) == 2, bf16x2, floatx2>::type Pair;
+    Pair rq[KDA ? 16 : 1], rk[KDA ? 16 : 1];
+    uint2 rg[KDA ? 16 : 1];  // gate bits: bf16 pair in .x, or two floats
+
+    // scalar decay: k as TW x TW tiles (row-major and transposed copies), q as rows
+    constexpr int TW = VPIECE;                    // 8 bf16 or 4 fp32 per 16 bytes
+    constexpr int NKT = (C / TW) * (DK / TW);     // k tiles
+    constexpr int NQP = C * DK / TW;              // q pieces
+    constexpr int QPT = NQP / 256;
+    static_assert(KDA || (NKT <= 256 && NQP % 256 == 0), "scalar-decay copy split");
+    uint4 rkt[KDA ? 1 : TW];
+    uint4 rqp[KDA ? 1 : QPT];
+    const int kt_r0 = TW * (tid / (DK / TW)), kt_c0 = TW * (tid % (DK / TW));
+
+    auto load_chunk = [&](int64_t ch) {
+        const int64_t t0 = ch * C;
+        const int n = (int)((L - t0) < C ? (L - t0) : C);
+        const uint32_t tb = (uint32_t)t0;  // chunk's first token (fits: checked on the host)
+        if constexpr (KDA) {
+            if (myR >= 0) {
+#pragma unroll
+                for (int s = 0; s < 16; ++s) {
+                    const uint32_t r = (uint32_t)((16 * myR + s) < n ? (16 * myR + s) : (n - 1));
+                    const uint32_t el = (tb + r) * DK + c0;
+                    rq[s] = ldg<Pair>(gq, el * ESZ);
+                    rk[s] = ldg<Pair>(gk, el * ESZ);
+                    if constexpr (GBF) rg[s].x = ldg<uint32_t>(gla, el * 2);
+                    else rg[s] = ldg<uint2>(gla, el * 4);
+                }
+            }
+        } else {
+            if (tid < NKT) {
+#pragma unroll
+                for (int i = 0; i < TW; ++i) {
+                    const int r = (kt_r0 + i) < n ? (kt_r0 + i) : (n - 1);
+                    rkt[i] = ldg<uint4>(gk, ((tb + r) * DK + kt_c0) * ESZ);
+                }
+            }
+#pragma unroll
+            for (int i = 0; i < QPT; ++i) {
+                const int idx = tid + 256 * i;
+                const int r0 = idx / (DK / TW), cc = (idx % (DK / TW)) * TW;
+                const int r = r0 < n ? r0 : n - 1;
+                rqp[i] = ldg<uint4>(gq, ((tb + r) * DK + cc) * ESZ);
+            }
+            if constexpr (AMODE == KDA_ALPHA_HEAD) {
+                if (tid < C) {
+                    const uint32_t r = tid < n ? tid : n - 1;
+                    if constexpr (GBF) rla = ldg<uint16_t>(gla, (tb + r) * 2);
+                    else rla = ldg<uint32_t>(gla, (tb + r) * 4);
+                }
+            }
+        }
+        if (tid < C) {
+            const uint32_t r = tid < n ? tid : n - 1;
+            if constexpr (GBF) rb = ldg<uint16_t>(gbeta, (tb + r) * 2);
+            else rb = ldg<uint32_t>(gbeta, (tb + r) * 4);
+        }
+#pragma unroll
+        for (int i = 0; i < VPT; ++i) {
+            int idx = tid + 256 * i;
+            idx = idx < C * VPPR ? idx : C * VPPR - 1;
+            const int r = idx / VPPR, cc = (idx % VPPR) * VPIECE;
+            const int rr = r < n ? r : n - 1;
+            rv[i] = ldg<uint4>(gv, ((tb + rr) * DV + cc) * ESZ);
+        }
+    };
+
     const int64_t nchunks = (L + C - 1) / C;
+    if (nchunks > 0) load_chunk(0);
     for (int64_t ch = 0; ch < nchunks; ++ch) {
         const int64_t t0 = ch * C;
         const int n = (int)((L - t0) < C ? (L - t0) : C);  // valid tokens in this chunk
         E* sSTc = (ch & 1) ? sST1 : sST0;
         E* sSTn = (ch & 1) ? sST0 : sST1;
 
-        // ================= G1: loads, in-block decay products ================
-        constexpr int NCP = DK / 2;            // channel pairs
-        constexpr int NBG = 256 / NCP;         // block groups
-        const int cp = tid % NCP, bg = tid / NCP;
-        const int c0 = 2 * cp;
-        floatx2 ky[16];  // k * y for the K^ tile, kept across the barrier
-        int myR = (bg < NB) ? bg : -1;
-        static_assert(NBG >= 1, "");
-        if (myR >= 0) {
-            const int R = myR;
-            floatx2 a[16], qv[16], kv[16];
+        // ================= G: inputs into LDS =================================
+        floatx2 ky[KDA ? 16 : 1];  // KDA: k * y for the K^ tile, kept across the barrier
+        if constexpr (KDA) {
+            if (myR >= 0) {
+                const int R = myR;
+                floatx2 a[16], qv[16], kv[16];
 #pragma unroll
-            for (int s = 0; s < 16; ++s) {
-                const int r = 16 * R + s;
-                const bool valid = r < n;
-                const int64_t tok = t0 + r;
-                floatx2 z2 = {0.f, 0.f};
-                qv[s] = valid ? ld2(gq + tok * DK + c0) : z2;
-                kv[s] = valid ? ld2(gk + tok * DK + c0) : z2;
-                if (amode == KDA_ALPHA_CHANNEL) {
-                    a[s] = valid ? ld_gate2(prm.log_alpha, (gate_head + tok) * DK + c0, gbf) : z2;
-                } else if (amode == KDA_ALPHA_HEAD) {
-                    float x = valid ? ld_gate(prm.log_alpha, gate_head + tok, gbf) : 0.f;
-                    a[s][0] = x;
-                    a[s][1] = x;
-                } else {
-                    a[s] = z2;
+                for (int s = 0; s < 16; ++s) {
+                    const bool valid = (16 * R + s) < n;
+                    floatx2 qq, kk2, la;
+                    qq[0] = to_f32(rq[s][0]);
+                    qq[1] = to_f32(rq[s][1]);
+                    kk2[0] = to_f32(rk[s][0]);
+                    kk2[1] = to_f32(rk[s][1]);
+                    if constexpr (GBF) {
+                        la[0] = __uint_as_float(rg[s].x << 16);
+                        la[1] = __uint_as_float(rg[s].x & 0xffff0000u);
+                    } else {
+                        la[0] = __uint_as_float(rg[s].x);
+                        la[1] = __uint_as_float(rg[s].y);
+                    }
+                    const floatx2 z2 = {0.f, 0.f};
+                    qv[s] = valid ? qq : z2;
+                    kv[s] = valid ? kk2 : z2;
+                    a[s] = valid ? la : z2;
                 }
-            }
-            // alpha = exp(ln alpha); x_s = prod_{s'<=s} alpha (within block)
-            floatx2 x[16];
-            floatx2 run = {1.f, 1.f};
+                // alpha = exp(ln alpha); x_s = prod_{s'<=s} alpha (within block)
+                floatx2 x[16];
+                floatx2 run = {1.f, 1.f};
 #pragma unroll
-            for (int s = 0; s < 16; ++s) {
-                if (amode != KDA_ALPHA_NONE) {
+                for (int s = 0; s < 16; ++s) {
                     a[s][0] = exp_neg(a[s][0]);
                     a[s][1] = exp_neg(a[s][1]);
-                } else {
-                    a[s][0] = 1.f;
-                    a[s][1] = 1.f;
+                    run = run * a[s];
+                    x[s] = run;
                 }
-                run = run * a[s];
-                x[s] = run;
-            }
-            // y_s = prod_{s' > s} alpha = e^{G_{R+1} - g_s} (within block, <= 1)
-            floatx2 yrun = {1.f, 1.f};
+                // y_s = prod_{s' > s} alpha = e^{G_{R+1} - g_s} (<= 1)
+                floatx2 yrun = {1.f, 1.f};
 #pragma unroll
-            for (int s = 15; s >= 0; --s) {
-                ky[s] = kv[s] * yrun;
-                yrun = yrun * a[s];
-            }
-            // x'_s = x_s / Z_R = e^{g_s - G_{R+1}} (>= 1): rows are referenced to
-            // the end of their block, so a diagonal block pair needs no rescale
-            floatx2 rz;
-            rz[0] = 1.f / x[15][0];
-            rz[1] = 1.f / x[15][1];
+                for (int s = 15; s >= 0; --s) {
+                    ky[s] = kv[s] * yrun;
+                    yrun = yrun * a[s];
+                }
+                // x'_s = x_s / Z_R = e^{g_s - G_{R+1}} (>= 1)
+                floatx2 rz;
+                rz[0] = 1.f / x[15][0];
+                rz[1] = 1.f / x[15][1];
 #pragma unroll
-            for (int s = 0; s < 16; ++s) {
-                const int r = 16 * R + s;
-                const floatx2 xp = x[s] * rz;
-                st2<E>(sKr + r * PK + c0, kv[s][0] * xp[0], kv[s][1] * xp[1]);
-                st2<E>(sQr + r * PK + c0, qv[s][0] * xp[0], qv[s][1] * xp[1]);
-                st2<E>(sKc + r * PK + c0, ky[s][0], ky[s][1]);
+                for (int s = 0; s < 16; ++s) {
+                    const int r = 16 * R + s;
+                    const floatx2 xp = x[s] * rz;
+                    st2<E>(sKr + r * PK + c0, kv[s][0] * xp[0], kv[s][1] * xp[1]);
+                    st2<E>(sQr + r * PK + c0, qv[s][0] * xp[0], qv[s][1] * xp[1]);
+                    st2<E>(sKc + r * PK + c0, ky[s][0], ky[s][1]);
+                }
+                sZ[R * DK + c0] = x[15][0];
+                sZ[R * DK + c0 + 1] = x[15][1];
             }
-            sZ[R * DK + c0] = x[15][0];
-            sZ[R * DK + c0 + 1] = x[15][1];
+        } else {
+            // k: row-major copy and transposed copy; invalid rows become zero
+            if (tid < NKT) {
+                uint4 tin[TW], tout[TW];
+#pragma unroll
+                for (int i = 0; i < TW; ++i) {
+                    tin[i] = (kt_r0 + i) < n ? rkt[i] : make_uint4(0u, 0u, 0u, 0u);
+                    *(uint4*)(sKr + (kt_r0 + i) * PK + kt_c0) = tin[i];
+                }
+                transpose_tile(tin, tout);
+#pragma unroll
+                for (int e = 0; e < TW; ++e) *(uint4*)(sKT + (kt_c0 + e) * PC + kt_r0) = tout[e];
+            }
+#pragma unroll
+            for (int i = 0; i < QPT; ++i) {
+                const int idx = tid + 256 * i;
+                const int r0 = idx / (DK / TW), cc = (idx % (DK / TW)) * TW;
+                *(uint4*)(sQr + r0 * PK + cc) = r0 < n ? rqp[i] : make_uint4(0u, 0u, 0u, 0u);
+            }
+            // per-token decay: g = inclusive prefix sum of ln(alpha) over the chunk
+            if (w == 0) {
+                float g = 0.f;
+                if constexpr (AMODE == KDA_ALPHA_HEAD) {
+                    const float la = GBF ? __uint_as_float(rla << 16) : __uint_as_float(rla);
+                    g = (l < n) ? la : 0.f;
+#pragma unroll
+                    for (int off = 1; off < 64; off <<= 1) {
+                        const float y = __shfl_up(g, off, 64);
+                        if (l >= off) g += y;
+                    }
+                }
+                const float gn = __shfl(g, C - 1, 64);
+                if (l < C) {
+                    sG[l] = g;
+                    sEg[l] = exp_neg(g);
+                    sEgn[l] = exp_neg(gn - g);
+                }
+                if (l == 0) sGn1[0] = exp_neg(gn);
+            }
         }
         if (tid < C) {
-            const int r = tid;
-            sBeta[r] = (r < n) ? ld_gate(prm.beta, gate_head + t0 + r, gbf) : 0.f;
+            const float b = GBF ? __uint_as_float(rb << 16) : __uint_as_float(rb);
+            sBeta[tid] = (tid < n) ? b : 0.f;
         }
-        {
-            // v slice [C][NV] -> sV, 16-byte pieces
-            constexpr int PIECE = 16 / Cfg::ESZ;           // elements per piece
-            constexpr int PPR = NV / PIECE;                // pieces per row
-            for (int i = tid; i < C * PPR; i += Cfg::NTHREADS) {
-                const int r = i / PPR, cc = (i % PPR) * PIECE;
-                uint4 val = {0u, 0u, 0u, 0u};
-                if (r < n) val = *(const uint4*)(gv + (t0 + r) * DV + v0 + cc);
+#pragma unroll
+        for (int i = 0; i < VPT; ++i) {
+            const int idx = tid + 256 * i;
+            if (idx < C * VPPR) {
+                const int r = idx / VPPR, cc = (idx % VPPR) * VPIECE;
+                uint4 val = rv[i];
+                if (r >= n) val = make_uint4(0u, 0u, 0u, 0u);
                 *(uint4*)(sV + r * PV + cc) = val;
             }
         }
+        // the registers are free again: start fetching the next chunk now, so
+        // its HBM latency hides behind this chunk's work
+        if (ch + 1 < nchunks) load_chunk(ch + 1);
         __syncthreads();
 
-        // ================= G2: cross-block decay factors, K^ tile ============
-        if (myR >= 0) {
-            const int R = myR;
-            floatx2 Zb[NB];
-#pragma unroll
-            for (int b = 0; b < NB; ++b) {
-                Zb[b][0] = sZ[b * DK + c0];
-                Zb[b][1] = sZ[b * DK + c0 + 1];
-            }
-            floatx2 Fr = {1.f, 1.f};  // e^{g_n - G_{R+1}} = prod of later blocks
-#pragma unroll
-            for (int b = 0; b < NB; ++b)
-                if (b > R) Fr = Fr * Zb[b];
-            // K^ = k y F, transposed: [channel][token]
-#pragma unroll
-            for (int s = 0; s < 16; s += Frag<E>::W) {
-#pragma unroll
-                for (int ch2 = 0; ch2 < 2; ++ch2) {
-                    E* dst = sKhT + (c0 + ch2) * PC + 16 * R + s;
-                    if constexpr (sizeof(E) == 2) {
-                        bf16x8 vv;
-#pragma unroll
-                        for (int e = 0; e < 8; ++e) vv[e] = (bf16)(ky[s + e][ch2] * Fr[ch2]);
-                        *(bf16x8*)dst = vv;
-                    } else {
-                        floatx4 vv;
-#pragma unroll
-                        for (int e = 0; e < 4; ++e) vv[e] = ky[s + e][ch2] * Fr[ch2];
-                        *(floatx4*)dst = vv;
-                    }
-                }
-            }
-            if (R == 0) {
-                // block-end factors E'_R = e^{G_{R+1}}, pair scales
-                // Y'_RJ = e^{G_{R+1} - G_{J+1}} (1 on the diagonal), e^{g_n}
-                floatx2 run = {1.f, 1.f};
+        // ================= G2 (KDA): cross-block factors, K^ tile =============
+        if constexpr (KDA) {
+            if (myR >= 0) {
+                const int R = myR;
+                floatx2 Zb[NB];
 #pragma unroll
                 for (int b = 0; b < NB; ++b) {
-                    run = run * Zb[b];
-                    sE[b * DK + c0] = run[0];
-                    sE[b * DK + c0 + 1] = run[1];
+                    Zb[b][0] = sZ[b * DK + c0];
+                    Zb[b][1] = sZ[b * DK + c0 + 1];
                 }
-                sGn[c0] = run[0];
-                sGn[c0 + 1] = run[1];
-                int p = 0;
+                floatx2 Fr = {1.f, 1.f};  // e^{g_n - G_{R+1}} = prod of later blocks
 #pragma unroll
-                for (int rb = 0; rb < NB; ++rb) {
+                for (int b = 0; b < NB; ++b)
+                    if (b > R) Fr = Fr * Zb[b];
+                // K^ = k y F, transposed: [channel][token]
 #pragma unroll
-                    for (int jb = 0; jb <= rb; ++jb, ++p) {
-                        floatx2 y = {1.f, 1.f};
+                for (int s = 0; s < 16; s += F::W) {
 #pragma unroll
-                        for (int m = 0; m < NB; ++m)
-                            if (m > jb && m <= rb) y = y * Zb[m];
-                        sY[p * DK + c0] = y[0];
-                        sY[p * DK + c0 + 1] = y[1];
+                    for (int ch2 = 0; ch2 < 2; ++ch2) {
+                        E* dst = sKT + (c0 + ch2) * PC + 16 * R + s;
+                        if constexpr (sizeof(E) == 2) {
+                            bf16x8 vv;
+#pragma unroll
+                            for (int e = 0; e < 8; ++e) vv[e] = (bf16)(ky[s + e][ch2] * Fr[ch2]);
+                            *(bf16x8*)dst = vv;
+                        } else {
+                            floatx4 vv;
+#pragma unroll
+                            for (int e = 0; e < 4; ++e) vv[e] = ky[s + e][ch2] * Fr[ch2];
+                            *(floatx4*)dst = vv;
+                        }
+                    }
+                }
+                if (R == 0) {
+                    // block-end factors E'_R = e^{G_{R+1}}, pair scales
+                    // Y'_RJ = e^{G_{R+1} - G_{J+1}} (1 on the diagonal), e^{g_n}
+                    floatx2 run = {1.f, 1.f};
+#pragma unroll
+                    for (int b = 0; b < NB; ++b) {
+                        run = run * Zb[b];
+                        sE[b * DK + c0] = run[0];
+                        sE[b * DK + c0 + 1] = run[1];
+                    }
+                    sGnv[c0] = run[0];
+                    sGnv[c0 + 1] = run[1];
+                    int p = 0;
+#pragma unroll
+                    for (int rb2 = 0; rb2 < NB; ++rb2) {
+#pragma unroll
+                        for (int jb = 0; jb <= rb2; ++jb, ++p) {
+                            floatx2 y = {1.f, 1.f};
+#pragma unroll
+                            for (int m = 0; m < NB; ++m)
+                                if (m > jb && m <= rb2) y = y * Zb[m];
+                            sY[p * DK + c0] = y[0];
+                            sY[p * DK + c0 + 1] = y[1];
+                        }
                     }
                 }
             }
+            __syncthreads();
         }
-        __syncthreads();
 
         // ================= AP: A (fp32) and P (operand type) =================
         for (int p = w; p < Cfg::NPAIR; p += 4) {
             int R, J;
             pair_of(p, R, J);
             floatx4 accA = {0.f, 0.f, 0.f, 0.f}, accP = {0.f, 0.f, 0.f, 0.f};
-            const E* pa = sKc + (16 * J + lr) * PK + F::W * lq;
-            const float* ps = sY + p * DK + F::W * lq;
+            const E* pa = (KDA ? sKc : sKr) + (16 * J + lr) * PK + F::W * lq;
             const E* pk = sKr + (16 * R + lr) * PK + F::W * lq;
             const E* pq = sQr + (16 * R + lr) * PK + F::W * lq;
-            if (J == R) {
+            if (!KDA || J == R) {
 #pragma unroll
                 for (int kk = 0; kk < DK; kk += F::KS) {
                     typename F::T af = F::load(pa + kk);
@@ -369,6 +547,7 @@ kda_chunk_kernel(ChunkParams prm) {
                     accP = F::mma(accP, af, F::load(pq + kk));
                 }
             } else {
+                const float* ps = sY + p * DK + F::W * lq;
 #pragma unroll
                 for (int kk = 0; kk < DK; kk += F::KS) {
                     typename F::T af = F::load_scaled(pa + kk, ps + kk);
@@ -379,55 +558,80 @@ kda_chunk_kernel(ChunkParams prm) {
             // lane holds [m = j = 16J + 4lq + e][n = r = 16R + lr]
             const int rr = 16 * R + lr;
             const float br = sBeta[rr];
+            float gr = 0.f;
+            if constexpr (AMODE == KDA_ALPHA_HEAD) gr = sG[rr];
             floatx4 va, vp;
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const int jj = 16 * J + 4 * lq + e;
-                va[e] = (J < R || jj < rr) ? br * accA[e] : 0.f;
-                vp[e] = (J < R || jj <= rr) ? accP[e] : 0.f;
+                float f = 1.f;  // scalar decay e^{g_r - g_j}, applied to the result
+                if constexpr (AMODE == KDA_ALPHA_HEAD) f = exp_neg(gr - sG[jj]);
+                va[e] = (J < R || jj < rr) ? br * accA[e] * f : 0.f;
+                vp[e] = (J < R || jj <= rr) ? accP[e] * f : 0.f;
             }
             *(floatx4*)(sA + rr * PA + 16 * J + 4 * lq) = va;
-            E* dp = sP + rr * PC + 16 * J + 4 * lq;
-            if constexpr (sizeof(E) == 2) {
-                bf16x4 t;
-                t[0] = (bf16)vp[0];
-                t[1] = (bf16)vp[1];
-                t[2] = (bf16)vp[2];
-                t[3] = (bf16)vp[3];
-                *(bf16x4*)dp = t;
-            } else {
-                *(floatx4*)dp = vp;
+            st4<E>(sP + rr * PC + 16 * J + 4 * lq, vp);
+            if (J == R) {
+                // transposed copy of the diagonal block for the column sweep of T1
+#pragma unroll
+                for (int e = 0; e < 4; ++e) sAd[(R * 16 + 4 * lq + e) * PD + lr] = va[e];
             }
         }
         __syncthreads();
 
         // ================= T1: diagonal blocks by forward substitution =======
-        // Lane (R, j) owns column j of T_RR and solves
-        //   t_i = [i == j] - sum_{m < i} A_RR[i][m] t_m,  i = 0..15.
-        // The result is stored transposed in the diagonal block of sA.
-        if (w == 0 && l < 16 * NB) {
-            const int R = l >> 4, j = l & 15;
-            const float* Ab = sA + (16 * R) * PA + 16 * R;
-            float t[16];
+        // Lane (R, j) owns column j of T_RR.  Right-looking sweep: once t_m is
+        // final, every later row takes its A_RR[i][m] t_m term, so the chain of
+        // dependent steps is 16 long.  Results: T_RR^T (fp32) in the diagonal
+        // block of sA, and T_RR diag(beta) in operand precision in sTb.
+        if (w == 0) {
+            if (l < 16 * NB) {
+                const int R = l >> 4, j = l & 15;
+                float acc[16];
 #pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                float s = (i == j) ? 1.f : 0.f;
+                for (int i = 0; i < 16; ++i) acc[i] = (i == j) ? 1.f : 0.f;
+                const float* Ad = sAd + (R * 16) * PD;  // Ad[m * PD + i] = A_RR[i][m]
 #pragma unroll
-                for (int m = 0; m < i; ++m) s -= Ab[i * PA + m] * t[m];
-                t[i] = s;
+                for (int m = 0; m < 15; ++m) {
+                    floatx4 col[4];
+#pragma unroll
+                    for (int q4 = 0; q4 < 4; ++q4) col[q4] = *(const floatx4*)(Ad + m * PD + 4 * q4);
+                    const float tm = acc[m];
+#pragma unroll
+                    for (int i = m + 1; i < 16; ++i) acc[i] -= col[i >> 2][i & 3] * tm;
+                }
+                float* dst = sA + (16 * R + j) * PA + 16 * R;
+#pragma unroll
+                for (int i = 0; i < 16; i += 4) {
+                    floatx4 v4 = {acc[i], acc[i + 1], acc[i + 2], acc[i + 3]};
+                    *(floatx4*)(dst + i) = v4;
+                }
+                const float bj = sBeta[16 * R + j];
+#pragma unroll
+                for (int i = 0; i < 16; ++i) sTb[(16 * R + i) * PC + 16 * R + j] = from_f32<E>(acc[i] * bj);
             }
-            __atomic_signal_fence(__ATOMIC_SEQ_CST);
-            float* dst = sA + (16 * R + j) * PA + 16 * R;
-#pragma unroll
-            for (int i = 0; i < 16; i += 4) {
-                floatx4 v4 = {t[i], t[i + 1], t[i + 2], t[i + 3]};
-                *(floatx4*)(dst + i) = v4;
+        } else if constexpr (KDA) {
+            // waves 1..3: rescale the row operands in place, K~ = k e^{g},
+            // Q~ = q e^{g} (row operand x E'_R), for the state products
+            constexpr int PER_ROW = DK / VPIECE;
+            for (int i = tid - 64; i < 2 * C * PER_ROW; i += 192) {
+                const int which = i / (C * PER_ROW);
+                const int rem = i % (C * PER_ROW);
+                const int r = rem / PER_ROW, cc = (rem % PER_ROW) * VPIECE;
+                E* p = (which ? sQr : sKr) + r * PK + cc;
+                const float* sc = sE + (r >> 4) * DK + cc;
+                if constexpr (sizeof(E) == 2) {
+                    *(bf16x8*)p = Frag<bf16>::load_scaled((const bf16*)p, sc);
+                } else {
+                    *(floatx4*)p = Frag<float>::load_scaled((const float*)p, sc);
+                }
             }
         }
         __syncthreads();
 
         // ================= T2: off-diagonal blocks, by distance ===============
-        // T_RJ = -T_RR sum_{M=J}^{R-1} A_RM T_MJ; T_RJ^T is stored at block (J, R).
+        // T_RJ = -T_RR sum_{M=J}^{R-1} A_RM T_MJ; T_RJ^T is stored at block (J, R)
+        // of sA, and T_RJ diag(beta) in sTb.
 #pragma unroll
         for (int d = 1; d < NB; ++d) {
             const int R = d + w, J = w;
@@ -443,47 +647,28 @@ kda_chunk_kernel(ChunkParams prm) {
 #pragma unroll
                 for (int s = 0; s < 4; ++s) tf[s] = sA[(16 * R + 4 * lq + s) * PA + 16 * R + lr];
                 floatx4 z = {0.f, 0.f, 0.f, 0.f};
-                floatx4 res = Frag<float>::mma(z, tf, acc);
-                *(floatx4*)(sA + (16 * J + lr) * PA + 16 * R + 4 * lq) = -res;
+                floatx4 res = -Frag<float>::mma(z, tf, acc);
+                *(floatx4*)(sA + (16 * J + lr) * PA + 16 * R + 4 * lq) = res;
+                const float bj = sBeta[16 * J + lr];
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    sTb[(16 * R + 4 * lq + e) * PC + 16 * J + lr] = from_f32<E>(res[e] * bj);
             }
             __syncthreads();
         }
 
-        // ================= T': T diag(beta) in operand precision =============
-        {
-            constexpr int NG = 256 / C;
-            const int r = tid % C, grp = tid / C;
-            const int Rr = r >> 4;
-            for (int jc = grp; jc < C / 4; jc += NG) {
-                const int j = 4 * jc;
-                if ((j >> 4) > Rr) continue;
-                float tv[4];
-#pragma unroll
-                for (int e = 0; e < 4; ++e) tv[e] = sA[(j + e) * PA + r] * sBeta[j + e];
-                E* dst = sTb + r * PC + j;
-                if constexpr (sizeof(E) == 2) {
-                    bf16x4 t4;
-                    t4[0] = (bf16)tv[0];
-                    t4[1] = (bf16)tv[1];
-                    t4[2] = (bf16)tv[2];
-                    t4[3] = (bf16)tv[3];
-                    *(bf16x4*)dst = t4;
-                } else {
-                    floatx4 t4 = {tv[0], tv[1], tv[2], tv[3]};
-                    *(floatx4*)dst = t4;
-                }
-            }
-        }
-        __syncthreads();
-
-        // ================= S1: X = V - (K e^g) S ==============================
+        // ================= S1: X = V - K~ S ===================================
         for (int item = w; item < NB * NVB; item += 4) {
             const int R = item % NB, vb = item / NB;
-            floatx4 acc;
+            floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+            acc = mma_block<E>(acc, sKr + (16 * R) * PK, PK, sSTc + (16 * vb) * PK, PK, DK);
 #pragma unroll
-            for (int e = 0; e < 4; ++e) acc[e] = to_f32(sV[(16 * R + 4 * lq + e) * PV + 16 * vb + lr]);
-            acc = mma_block_scaled_a<E, true>(acc, sKr + (16 * R) * PK, PK, sE + R * DK,
-                                              sSTc + (16 * vb) * PK, PK, DK);
+            for (int e = 0; e < 4; ++e) {
+                const int r = 16 * R + 4 * lq + e;
+                float ks = acc[e];
+                if constexpr (AMODE == KDA_ALPHA_HEAD) ks *= sEg[r];
+                acc[e] = to_f32(sV[r * PV + 16 * vb + lr]) - ks;
+            }
             store_acc_transposed<E>(sXT + (16 * vb) * PC + 16 * R, PC, acc);
         }
         __syncthreads();
@@ -496,6 +681,12 @@ kda_chunk_kernel(ChunkParams prm) {
             floatx4 acc = {0.f, 0.f, 0.f, 0.f};
             acc = mma_block<E>(acc, sTb + (16 * R) * PC, PC, sXT + (16 * vb) * PC, PC, K);
             store_acc_transposed<E>(sUT + (16 * vb) * PC + 16 * R, PC, acc);
+            if constexpr (!KDA) {
+                // u scaled by e^{g_n - g} for the state update
+#pragma unroll
+                for (int e = 0; e < 4; ++e) acc[e] *= sEgn[16 * R + 4 * lq + e];
+                store_acc_transposed<E>(sUhT + (16 * vb) * PC + 16 * R, PC, acc);
+            }
         }
         __syncthreads();
 
@@ -505,8 +696,11 @@ kda_chunk_kernel(ChunkParams prm) {
             constexpr int KS = Frag<E>::KS;
             const int K = ((16 * (R + 1) + KS - 1) / KS) * KS;
             floatx4 acc = {0.f, 0.f, 0.f, 0.f};
-            acc = mma_block_scaled_a<E, false>(acc, sQr + (16 * R) * PK, PK, sE + R * DK,
-                                               sSTc + (16 * vb) * PK, PK, DK);
+            acc = mma_block<E>(acc, sQr + (16 * R) * PK, PK, sSTc + (16 * vb) * PK, PK, DK);
+            if constexpr (AMODE == KDA_ALPHA_HEAD) {
+#pragma unroll
+                for (int e = 0; e < 4; ++e) acc[e] *= sEg[16 * R + 4 * lq + e];
+            }
             acc = mma_block<E>(acc, sP + (16 * R) * PC, PC, sUT + (16 * vb) * PC, PC, K);
 #pragma unroll
             for (int e = 0; e < 4; ++e)
@@ -514,32 +708,39 @@ kda_chunk_kernel(ChunkParams prm) {
         }
 
         // ================= S4: S = e^{g_n} S + K^^T u =========================
+        {
+            const E* ub = KDA ? sUT : sUhT;
 #pragma unroll
-        for (int i = 0; i < SB_PER_WAVE; ++i) {
-            const int item = w + 4 * i;
-            const int cb = item % NCB, vb = item / NCB;
-            floatx4 acc = Sreg[i];
+            for (int i = 0; i < SB_PER_WAVE; ++i) {
+                const int item = w + 4 * i;
+                const int cb = item % NCB, vb = item / NCB;
+                floatx4 acc = Sreg[i];
 #pragma unroll
-            for (int e = 0; e < 4; ++e) acc[e] *= sGn[16 * cb + 4 * lq + e];
-            acc = mma_block<E>(acc, sKhT + (16 * cb) * PC, PC, sUT + (16 * vb) * PC, PC, C);
-            Sreg[i] = acc;
-            store_acc_transposed<E>(sSTn + (16 * vb) * PK + 16 * cb, PK, acc);
+                for (int e = 0; e < 4; ++e) {
+                    if constexpr (KDA) acc[e] *= sGnv[16 * cb + 4 * lq + e];
+                    else if constexpr (AMODE == KDA_ALPHA_HEAD) acc[e] *= sGn1[0];
+                }
+                acc = mma_block<E>(acc, sKT + (16 * cb) * PC, PC, ub + (16 * vb) * PC, PC, C);
+                Sreg[i] = acc;
+                store_acc_transposed<E>(sSTn + (16 * vb) * PK + 16 * cb, PK, acc);
+            }
         }
         __syncthreads();
 
         // ================= o tile -> HBM (valid rows only) ====================
         {
-            constexpr int PIECE = 16 / Cfg::ESZ;
-            constexpr int PPR = NV / PIECE;
-            for (int i = tid; i < C * PPR; i += Cfg::NTHREADS) {
-                const int r = i / PPR, cc = (i % PPR) * PIECE;
-                if (r < n) *(uint4*)(go + (t0 + r) * DV + v0 + cc) = *(const uint4*)(sO + r * PV + cc);
+            for (int i = tid; i < C * VPPR; i += Cfg::NTHREADS) {
+                const int r = i / VPPR, cc = (i % VPPR) * VPIECE;
+                if (r < n)
+                    *(uint4*)(go + (((uint32_t)t0 + r) * DV + cc) * ESZ) =
+                        *(const uint4*)(sO + r * PV + cc);
             }
         }
     }
 
     // ---- final state --------------------------------------------------------
     if (prm.S_final) {
+        float* sf = prm.S_final + (int64_t)bh * DK * DV + v0;
 #pragma unroll
         for (int i = 0; i < SB_PER_WAVE; ++i) {
             const int item = w + 4 * i;
@@ -547,7 +748,7 @@ kda_chunk_kernel(ChunkParams prm) {
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const int row = 16 * cb + 4 * lq + e;
-                prm.S_final[((int64_t)bh * DK + row) * DV + v0 + 16 * vb + lr] = Sreg[i][e];
+                sf[row * DV + 16 * vb + lr] = Sreg[i][e];
             }
         }
     }
@@ -555,16 +756,31 @@ kda_chunk_kernel(ChunkParams prm) {
 
 // ---- host-side dispatch -----------------------------------------------------
 
-template <class Cfg>
+template <int DK, int NV, int C, typename E, int AMODE>
 static hipError_t launch_cfg(const ChunkParams& prm, hipStream_t stream) {
+    typedef ChunkCfg<DK, NV, C, E, AMODE> Cfg;
     const int total = prm.BH * prm.n_slices;
-    hipLaunchKernelGGL(kda_chunk_kernel<Cfg>, dim3(total), dim3(Cfg::NTHREADS), 0, stream, prm);
+    if (prm.gate_bf16)
+        hipLaunchKernelGGL((kda_chunk_kernel<Cfg, true>), dim3(total), dim3(Cfg::NTHREADS), 0,
+                           stream, prm);
+    else
+        hipLaunchKernelGGL((kda_chunk_kernel<Cfg, false>), dim3(total), dim3(Cfg::NTHREADS), 0,
+                           stream, prm);
     return hipGetLastError();
 }
 
+template <int DK, int NV, int C, typename E>
+static hipError_t launch_mode(const ChunkParams& prm, hipStream_t stream) {
+    switch (prm.alpha_mode) {
+        case KDA_ALPHA_NONE: return launch_cfg<DK, NV, C, E, KDA_ALPHA_NONE>(prm, stream);
+        case KDA_ALPHA_HEAD: return launch_cfg<DK, NV, C, E, KDA_ALPHA_HEAD>(prm, stream);
+        case KDA_ALPHA_CHANNEL: return launch_cfg<DK, NV, C, E, KDA_ALPHA_CHANNEL>(prm, stream);
+        default: return hipErrorInvalidValue;
+    }
+}
+
 int chunk_slice_width(int dk, int dv, int qkv_bf16, int64_t BH) {
-    (void)qkv_bf16;
-    // Prefer 32-column slices while that still gives >= 256 workgroups; else 16.
+    // Prefer wide slices while that still gives >= 256 workgroups; else 16.
     if (dk == 64 && qkv_bf16 && BH * (dv / 64) >= 256) return 64;
     if (BH * (dv / 32) >= 256) return 32;
     return 16;
@@ -575,7 +791,7 @@ hipError_t launch_chunk(ChunkParams prm, int dk, int qkv_bf16, int nv, hipStream
     prm.n_slices = prm.DV / nv;
 #define KDA_CASE(DK_, NV_, C_, E_)                                             \
     if (dk == DK_ && nv == NV_ && (qkv_bf16 != 0) == (sizeof(E_) == 2))        \
-        return launch_cfg<ChunkCfg<DK_, NV_, C_, E_>>(prm, stream);
+        return launch_mode<DK_, NV_, C_, E_>(prm, stream);
     KDA_CASE(128, 16, 64, bf16)
     KDA_CASE(128, 32, 64, bf16)
     KDA_CASE(64, 16, 64, bf16)

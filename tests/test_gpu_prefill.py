@@ -246,6 +246,9 @@ def test_strong_decay_documented_range():
 
 
 def test_head_gate_equals_broadcast_channel_gate():
+    """A per-head gate and the same gate broadcast over channels are the same
+    recurrence; the two kernel paths (decay on results vs decay in operands)
+    must each meet the bar against the oracle and agree with each other."""
     import torch
     kda = _kda()
     w = gen.custom(B=1, H=4, L=150, dk=128, dv=128, qkv_dtype="bf16", gate_dtype="f32",
@@ -257,5 +260,9 @@ def test_head_gate_equals_broadcast_channel_gate():
     a = kda.chunk_fwd(d["q"], d["k"], d["v"], d["log_alpha"], d["beta"], d["S0"])
     b = kda.chunk_fwd(d["q"], d["k"], d["v"], la_c, d["beta"], d["S0"])
     torch.cuda.synchronize()
-    assert torch.allclose(a[0].float(), b[0].float(), atol=1e-2, rtol=1e-2)
-    assert torch.allclose(a[1], b[1], atol=1e-3, rtol=1e-3)
+    o_ref, S_ref = oracle_prefill(w, flat_heads(x, 4))
+    for o, Sf in (a, b):
+        assert oracle.slab_error(to_f64(o).reshape(4, 150, 128), o_ref, 1) <= TOL["bf16"]
+        assert oracle.slab_error(to_f64(Sf).reshape(4, 128, 128), S_ref, 1) <= TOL["bf16"]
+    assert oracle.slab_error(to_f64(a[0]).reshape(4, 150, 128),
+                             to_f64(b[0]).reshape(4, 150, 128), 1) <= 2 * TOL["bf16"]
