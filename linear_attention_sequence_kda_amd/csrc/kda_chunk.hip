@@ -19,7 +19,7 @@
 // U = T diag(beta) V; merging the two products into T diag(beta)(V - K S) keeps
 // W off chip and out of the per-chunk work.)
 //
-// One workgroup (4 waves) owns one (b, h) head and one slice of NV state
+// One workgroup (8 waves, two per SIMD) owns one (b, h) head and one slice of NV state
 // columns; columns of S evolve independently, so slices never talk.  It walks
 // the chunks in order with its fp32 state slice resident in registers, and
 // fetches chunk i+1's inputs into registers while chunk i computes.  Per chunk:
@@ -62,19 +62,24 @@ struct ChunkCfg {
     static constexpr int PV = NV + PADE;               // pitch of [C][NV] tiles
     static constexpr int PA = C + 4;                   // pitch of the fp32 A/T tile
     static constexpr int PD = 20;                      // pitch of a transposed 16x16 fp32 block
+    static constexpr int PKH = DK + 32 / ESZ;          // pitch of the KDA K^ tile (read transposed)
     static constexpr int NCB = DK / 16, NVB = NV / 16; // 16x16 blocks of the state slice
-    static constexpr int NTHREADS = 256;
+    static constexpr int NW = 8;                       // waves per workgroup (2 per SIMD)
+    static constexpr int NTHREADS = 64 * NW;
+    static constexpr int SBW = (NCB * NVB + NW - 1) / NW;  // state blocks per wave
 
-    // LDS byte offsets.  Tiles: K row operand (KDA: k e^{g-G_{R+1}}; scalar: k),
-    // Q row operand, KDA column operand k e^{G_{J+1}-g}, the S-update operand
-    // (K e^{g_n-g})^T (KDA) or K^T (scalar), T', P, v slice, S^T (double
-    // buffered), X^T (then o), u^T, scalar only: (e^{g_n-g} u)^T.
+    // LDS byte offsets.  Tiles: K row operand (KDA: k e^{g-G_{R+1}}; scalar: k,
+    // also read transposed for the state update), Q row operand, KDA only: the
+    // column operand k e^{G_{J+1}-g} and K^ = k e^{g_n-g} (read transposed);
+    // T', P, v slice, S^T (double buffered), X^T (then o), u^T, scalar only:
+    // (e^{g_n-g} u)^T.
     static constexpr int O_KR = 0;
     static constexpr int O_QR = O_KR + C * PK * ESZ;
     static constexpr int O_KC = O_QR + C * PK * ESZ;
     static constexpr int SZ_KC = KDA ? C * PK * ESZ : 0;
     static constexpr int O_KT = O_KC + SZ_KC;
-    static constexpr int O_TB = O_KT + DK * PC * ESZ;
+    static constexpr int SZ_KT = KDA ? C * PKH * ESZ : 0;
+    static constexpr int O_TB = O_KT + SZ_KT;
     static constexpr int O_P = O_TB + C * PC * ESZ;
     static constexpr int O_V = O_P + C * PC * ESZ;
     static constexpr int O_ST0 = O_V + C * PV * ESZ;
@@ -94,7 +99,6 @@ struct ChunkCfg {
     static constexpr int LDS_BYTES = O_BETA + C * 4;
 
     static_assert(DK % 32 == 0 && NV % 16 == 0 && (C == 32 || C == 64), "tile shape");
-    static_assert((NCB * NVB) % 4 == 0, "state blocks split evenly over 4 waves");
     static_assert(LDS_BYTES <= 160 * 1024, "LDS budget of one gfx950 CU");
 };
 
@@ -136,48 +140,37 @@ __device__ __forceinline__ void pair_of(int p, int& R, int& J) {
     J = p;
 }
 
+// v if keep, else zero (an explicit mask: a select of 16-byte values can be
+// lowered into a select of stack addresses)
+__device__ __forceinline__ uint4 keep_or_zero(uint4 v, bool keep) {
+    const uint32_t m = keep ? 0xffffffffu : 0u;
+    return make_uint4(v.x & m, v.y & m, v.z & m, v.w & m);
+}
+
 // Load through a uniform base pointer plus a 32-bit byte offset (saddr form).
 template <typename T>
 __device__ __forceinline__ T ldg(const void* base, uint32_t byte_off) {
     return *(const T*)((const char*)base + byte_off);
 }
 
-// Transpose a TW x TW tile held as TW rows of 16 bytes (TW = 8 bf16 or 4 fp32).
-__device__ __forceinline__ void transpose_tile(const uint4 (&in)[8], uint4 (&out)[8]) {
-    const uint32_t* r = (const uint32_t*)in;  // r[4*i + d]: row i, dword d
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-        const uint32_t sel = (e & 1) ? 0x07060302u : 0x05040100u;
-        uint32_t o[4];
-#pragma unroll
-        for (int m = 0; m < 4; ++m)
-            o[m] = __builtin_amdgcn_perm(r[4 * (2 * m + 1) + (e >> 1)], r[4 * (2 * m) + (e >> 1)], sel);
-        out[e] = make_uint4(o[0], o[1], o[2], o[3]);
-    }
-}
-__device__ __forceinline__ void transpose_tile(const uint4 (&in)[4], uint4 (&out)[4]) {
-    const uint32_t* r = (const uint32_t*)in;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) out[e] = make_uint4(r[e], r[4 + e], r[8 + e], r[12 + e]);
-}
-
 template <class Cfg, bool GBF>
-__global__ void __launch_bounds__(256)
+__global__ void __launch_bounds__(Cfg::NTHREADS)
 kda_chunk_kernel(ChunkParams prm) {
     typedef typename Cfg::E E;
     typedef Frag<E> F;
     constexpr int DK = Cfg::DK, NV = Cfg::NV, C = Cfg::C, NB = Cfg::NB, AMODE = Cfg::AMODE;
     constexpr bool KDA = Cfg::KDA;
     constexpr int PK = Cfg::PK, PC = Cfg::PC, PV = Cfg::PV, PA = Cfg::PA, PD = Cfg::PD;
-    constexpr int NCB = Cfg::NCB, NVB = Cfg::NVB;
-    constexpr int SB_PER_WAVE = NCB * NVB / 4;
+    constexpr int PKH = Cfg::PKH;
+    constexpr int NCB = Cfg::NCB, NVB = Cfg::NVB, NW = Cfg::NW, NT = Cfg::NTHREADS;
+    constexpr int SBW = Cfg::SBW;
     constexpr int ESZ = Cfg::ESZ;
 
     __shared__ __attribute__((aligned(16))) char smem[Cfg::LDS_BYTES];
     E* sKr = (E*)(smem + Cfg::O_KR);
     E* sQr = (E*)(smem + Cfg::O_QR);
     E* sKc = (E*)(smem + Cfg::O_KC);
-    E* sKT = (E*)(smem + Cfg::O_KT);
+    E* sKh = (E*)(smem + Cfg::O_KT);
     E* sTb = (E*)(smem + Cfg::O_TB);
     E* sP = (E*)(smem + Cfg::O_P);
     E* sV = (E*)(smem + Cfg::O_V);
@@ -203,7 +196,7 @@ kda_chunk_kernel(ChunkParams prm) {
     float* sGn1 = sGate + 3 * C;
 
     const int tid = threadIdx.x;
-    const int w = tid >> 6;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index, uniform
     const int l = tid & 63;
     const int lr = l & 15, lq = l >> 4;
 
@@ -230,34 +223,36 @@ kda_chunk_kernel(ChunkParams prm) {
     const char* gbeta = (const char*)prm.beta + (int64_t)bh * L * GSZ;
 
     // ---- zero the triangular operand tiles once (upper blocks stay zero) ---
-    for (int i = tid; i < C * PC; i += Cfg::NTHREADS) {
+    for (int i = tid; i < C * PC; i += NT) {
         sTb[i] = from_f32<E>(0.f);
         sP[i] = from_f32<E>(0.f);
     }
 
     // ---- initial state slice into registers, and its operand copy ----------
-    floatx4 Sreg[SB_PER_WAVE];
+    // Wave w holds the 16x16 state blocks item = w + NW i (cb = item % NCB,
+    // vb = item / NCB); lane element e is S[16cb + 4lq + e][16vb + lr].
+    floatx4 Sreg[SBW];
+#pragma unroll
+    for (int i = 0; i < SBW; ++i) Sreg[i] = floatx4{0.f, 0.f, 0.f, 0.f};
     if (prm.S0) {  // uniform branch: all loads issue before the first use
         const float* s0 = prm.S0 + (int64_t)bh * DK * DV + v0;
 #pragma unroll
-        for (int i = 0; i < SB_PER_WAVE; ++i) {
-            const int item = w + 4 * i;
-            const int cb = item % NCB, vb = item / NCB;
+        for (int i = 0; i < SBW; ++i) {
+            const int item = w + NW * i;
+            if (item < NCB * NVB) {
+                const int cb = item % NCB, vb = item / NCB;
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int row = 16 * cb + 4 * lq + e;
-                Sreg[i][e] = s0[row * DV + 16 * vb + lr];
+                for (int e = 0; e < 4; ++e) Sreg[i][e] = s0[(16 * cb + 4 * lq + e) * DV + 16 * vb + lr];
             }
         }
-    } else {
-#pragma unroll
-        for (int i = 0; i < SB_PER_WAVE; ++i) Sreg[i] = floatx4{0.f, 0.f, 0.f, 0.f};
     }
 #pragma unroll
-    for (int i = 0; i < SB_PER_WAVE; ++i) {
-        const int item = w + 4 * i;
-        const int cb = item % NCB, vb = item / NCB;
-        store_acc_transposed<E>(sST0 + (16 * vb) * PK + 16 * cb, PK, Sreg[i]);
+    for (int i = 0; i < SBW; ++i) {
+        const int item = w + NW * i;
+        if (item < NCB * NVB) {
+            const int cb = item % NCB, vb = item / NCB;
+            store_acc_transposed<E>(sST0 + (16 * vb) * PK + 16 * cb, PK, Sreg[i]);
+        }
     }
 
     // ---- raw registers of the next chunk's inputs ---------------------------
@@ -266,59 +261,51 @@ kda_chunk_kernel(ChunkParams prm) {
     // all stay in flight together while the previous chunk computes.
     constexpr int VPIECE = 16 / ESZ;              // elements per 16-byte piece
     constexpr int VPPR = NV / VPIECE;             // pieces per row of the v slice
-    constexpr int VPT = (C * VPPR + 255) / 256;   // pieces per thread
+    constexpr int VPT = (C * VPPR + NT - 1) / NT; // pieces per thread
     uint4 rv[VPT];
     uint32_t rb = 0, rla = 0;
 
-    // KDA: thread (cp, bg) owns channel pair c0 = 2cp of sub-block R = bg
-    constexpr int NCP = DK / 2;
-    const int cp = tid % NCP, bg = tid / NCP;
-    const int c0 = 2 * cp;
-    const int myR = (bg < NB) ? bg : -1;
-    typedef typename std::conditional<sizeof(E) == 2, bf16x2, floatx2>::type Pair;
-    Pair rq[KDA ? 16 : 1], rk[KDA ? 16 : 1];
-    uint2 rg[KDA ? 16 : 1];  // gate bits: bf16 pair in .x, or two floats
+    // KDA: thread (c, R) owns key channel c of 16-token sub-block R
+    const int kc = tid % DK, kR = tid / DK;
+    const bool kact = KDA && kR < NB;
+    uint32_t rq[KDA ? 16 : 1], rk[KDA ? 16 : 1], rg[KDA ? 16 : 1];  // raw element bits
 
-    // scalar decay: k as TW x TW tiles (row-major and transposed copies), q as rows
-    constexpr int TW = VPIECE;                    // 8 bf16 or 4 fp32 per 16 bytes
-    constexpr int NKT = (C / TW) * (DK / TW);     // k tiles
-    constexpr int NQP = C * DK / TW;              // q pieces
-    constexpr int QPT = NQP / 256;
-    static_assert(KDA || (NKT <= 256 && NQP % 256 == 0), "scalar-decay copy split");
-    uint4 rkt[KDA ? 1 : TW];
-    uint4 rqp[KDA ? 1 : QPT];
-    const int kt_r0 = TW * (tid / (DK / TW)), kt_c0 = TW * (tid % (DK / TW));
+    // scalar decay: q and k rows as 16-byte pieces
+    constexpr int TW = VPIECE;
+    constexpr int PPR = DK / TW;                  // pieces per q/k row
+    constexpr int QPT = (C * PPR) / NT;           // pieces per thread and tensor
+    static_assert(KDA || (C * PPR) % NT == 0, "scalar-decay copy split");
+    uint4 rqp[KDA ? 1 : QPT], rkp[KDA ? 1 : QPT];
 
     auto load_chunk = [&](int64_t ch) {
         const int64_t t0 = ch * C;
         const int n = (int)((L - t0) < C ? (L - t0) : C);
         const uint32_t tb = (uint32_t)t0;  // chunk's first token (fits: checked on the host)
         if constexpr (KDA) {
-            if (myR >= 0) {
+            if (kact) {
 #pragma unroll
                 for (int s = 0; s < 16; ++s) {
-                    const uint32_t r = (uint32_t)((16 * myR + s) < n ? (16 * myR + s) : (n - 1));
-                    const uint32_t el = (tb + r) * DK + c0;
-                    rq[s] = ldg<Pair>(gq, el * ESZ);
-                    rk[s] = ldg<Pair>(gk, el * ESZ);
-                    if constexpr (GBF) rg[s].x = ldg<uint32_t>(gla, el * 2);
-                    else rg[s] = ldg<uint2>(gla, el * 4);
+                    const uint32_t r = (uint32_t)((16 * kR + s) < n ? (16 * kR + s) : (n - 1));
+                    const uint32_t el = (tb + r) * DK + kc;
+                    if constexpr (ESZ == 2) {
+                        rq[s] = ldg<uint16_t>(gq, el * 2);
+                        rk[s] = ldg<uint16_t>(gk, el * 2);
+                    } else {
+                        rq[s] = ldg<uint32_t>(gq, el * 4);
+                        rk[s] = ldg<uint32_t>(gk, el * 4);
+                    }
+                    if constexpr (GBF) rg[s] = ldg<uint16_t>(gla, el * 2);
+                    else rg[s] = ldg<uint32_t>(gla, el * 4);
                 }
             }
         } else {
-            if (tid < NKT) {
-#pragma unroll
-                for (int i = 0; i < TW; ++i) {
-                    const int r = (kt_r0 + i) < n ? (kt_r0 + i) : (n - 1);
-                    rkt[i] = ldg<uint4>(gk, ((tb + r) * DK + kt_c0) * ESZ);
-                }
-            }
 #pragma unroll
             for (int i = 0; i < QPT; ++i) {
-                const int idx = tid + 256 * i;
-                const int r0 = idx / (DK / TW), cc = (idx % (DK / TW)) * TW;
-                const int r = r0 < n ? r0 : n - 1;
+                const int idx = tid + NT * i;
+                const int r0 = idx / PPR, cc = (idx % PPR) * TW;
+                const uint32_t r = r0 < n ? r0 : n - 1;
                 rqp[i] = ldg<uint4>(gq, ((tb + r) * DK + cc) * ESZ);
+                rkp[i] = ldg<uint4>(gk, ((tb + r) * DK + cc) * ESZ);
             }
             if constexpr (AMODE == KDA_ALPHA_HEAD) {
                 if (tid < C) {
@@ -335,12 +322,16 @@ kda_chunk_kernel(ChunkParams prm) {
         }
 #pragma unroll
         for (int i = 0; i < VPT; ++i) {
-            int idx = tid + 256 * i;
+            int idx = tid + NT * i;
             idx = idx < C * VPPR ? idx : C * VPPR - 1;
             const int r = idx / VPPR, cc = (idx % VPPR) * VPIECE;
             const int rr = r < n ? r : n - 1;
             rv[i] = ldg<uint4>(gv, ((tb + rr) * DV + cc) * ESZ);
         }
+    };
+    // raw element bits -> fp32
+    auto bits_f32 = [](uint32_t u, bool half) -> float {
+        return half ? __uint_as_float(u << 16) : __uint_as_float(u);
     };
 
     const int64_t nchunks = (L + C - 1) / C;
@@ -352,88 +343,63 @@ kda_chunk_kernel(ChunkParams prm) {
         E* sSTn = (ch & 1) ? sST0 : sST1;
 
         // ================= G: inputs into LDS =================================
-        floatx2 ky[KDA ? 16 : 1];  // KDA: k * y for the K^ tile, kept across the barrier
+        float ky[KDA ? 16 : 1];  // KDA: k * y for the K^ tile, kept across the barrier
         if constexpr (KDA) {
-            if (myR >= 0) {
-                const int R = myR;
-                floatx2 a[16], qv[16], kv[16];
+            if (kact) {
+                const int R = kR;
+                float a[16], qv[16], kv[16];
 #pragma unroll
                 for (int s = 0; s < 16; ++s) {
                     const bool valid = (16 * R + s) < n;
-                    floatx2 qq, kk2, la;
-                    qq[0] = to_f32(rq[s][0]);
-                    qq[1] = to_f32(rq[s][1]);
-                    kk2[0] = to_f32(rk[s][0]);
-                    kk2[1] = to_f32(rk[s][1]);
-                    if constexpr (GBF) {
-                        la[0] = __uint_as_float(rg[s].x << 16);
-                        la[1] = __uint_as_float(rg[s].x & 0xffff0000u);
-                    } else {
-                        la[0] = __uint_as_float(rg[s].x);
-                        la[1] = __uint_as_float(rg[s].y);
-                    }
-                    const floatx2 z2 = {0.f, 0.f};
-                    qv[s] = valid ? qq : z2;
-                    kv[s] = valid ? kk2 : z2;
-                    a[s] = valid ? la : z2;
+                    const float qq = bits_f32(rq[s], ESZ == 2);
+                    const float kk2 = bits_f32(rk[s], ESZ == 2);
+                    const float la = bits_f32(rg[s], GBF);
+                    qv[s] = valid ? qq : 0.f;
+                    kv[s] = valid ? kk2 : 0.f;
+                    a[s] = valid ? la : 0.f;
                 }
                 // alpha = exp(ln alpha); x_s = prod_{s'<=s} alpha (within block)
-                floatx2 x[16];
-                floatx2 run = {1.f, 1.f};
+                float x[16];
+                float run = 1.f;
 #pragma unroll
                 for (int s = 0; s < 16; ++s) {
-                    a[s][0] = exp_neg(a[s][0]);
-                    a[s][1] = exp_neg(a[s][1]);
-                    run = run * a[s];
+                    a[s] = exp_neg(a[s]);
+                    run *= a[s];
                     x[s] = run;
                 }
                 // y_s = prod_{s' > s} alpha = e^{G_{R+1} - g_s} (<= 1)
-                floatx2 yrun = {1.f, 1.f};
+                float yrun = 1.f;
 #pragma unroll
                 for (int s = 15; s >= 0; --s) {
                     ky[s] = kv[s] * yrun;
-                    yrun = yrun * a[s];
+                    yrun *= a[s];
                 }
                 // x'_s = x_s / Z_R = e^{g_s - G_{R+1}} (>= 1)
-                floatx2 rz;
-                rz[0] = 1.f / x[15][0];
-                rz[1] = 1.f / x[15][1];
+                const float rz = 1.f / x[15];
 #pragma unroll
                 for (int s = 0; s < 16; ++s) {
                     const int r = 16 * R + s;
-                    const floatx2 xp = x[s] * rz;
-                    st2<E>(sKr + r * PK + c0, kv[s][0] * xp[0], kv[s][1] * xp[1]);
-                    st2<E>(sQr + r * PK + c0, qv[s][0] * xp[0], qv[s][1] * xp[1]);
-                    st2<E>(sKc + r * PK + c0, ky[s][0], ky[s][1]);
+                    const float xp = x[s] * rz;
+                    sKr[r * PK + kc] = from_f32<E>(kv[s] * xp);
+                    sQr[r * PK + kc] = from_f32<E>(qv[s] * xp);
+                    sKc[r * PK + kc] = from_f32<E>(ky[s]);
                 }
-                sZ[R * DK + c0] = x[15][0];
-                sZ[R * DK + c0 + 1] = x[15][1];
+                sZ[R * DK + kc] = x[15];
             }
         } else {
-            // k: row-major copy and transposed copy; invalid rows become zero
-            if (tid < NKT) {
-                uint4 tin[TW], tout[TW];
-#pragma unroll
-                for (int i = 0; i < TW; ++i) {
-                    tin[i] = (kt_r0 + i) < n ? rkt[i] : make_uint4(0u, 0u, 0u, 0u);
-                    *(uint4*)(sKr + (kt_r0 + i) * PK + kt_c0) = tin[i];
-                }
-                transpose_tile(tin, tout);
-#pragma unroll
-                for (int e = 0; e < TW; ++e) *(uint4*)(sKT + (kt_c0 + e) * PC + kt_r0) = tout[e];
-            }
+            // q, k rows; invalid rows become zero
 #pragma unroll
             for (int i = 0; i < QPT; ++i) {
-                const int idx = tid + 256 * i;
-                const int r0 = idx / (DK / TW), cc = (idx % (DK / TW)) * TW;
-                *(uint4*)(sQr + r0 * PK + cc) = r0 < n ? rqp[i] : make_uint4(0u, 0u, 0u, 0u);
+                const int idx = tid + NT * i;
+                const int r0 = idx / PPR, cc = (idx % PPR) * TW;
+                *(uint4*)(sQr + r0 * PK + cc) = keep_or_zero(rqp[i], r0 < n);
+                *(uint4*)(sKr + r0 * PK + cc) = keep_or_zero(rkp[i], r0 < n);
             }
             // per-token decay: g = inclusive prefix sum of ln(alpha) over the chunk
             if (w == 0) {
                 float g = 0.f;
                 if constexpr (AMODE == KDA_ALPHA_HEAD) {
-                    const float la = GBF ? __uint_as_float(rla << 16) : __uint_as_float(rla);
-                    g = (l < n) ? la : 0.f;
+                    g = (l < n) ? bits_f32(rla, GBF) : 0.f;
 #pragma unroll
                     for (int off = 1; off < 64; off <<= 1) {
                         const float y = __shfl_up(g, off, 64);
@@ -449,18 +415,13 @@ kda_chunk_kernel(ChunkParams prm) {
                 if (l == 0) sGn1[0] = exp_neg(gn);
             }
         }
-        if (tid < C) {
-            const float b = GBF ? __uint_as_float(rb << 16) : __uint_as_float(rb);
-            sBeta[tid] = (tid < n) ? b : 0.f;
-        }
+        if (tid < C) sBeta[tid] = (tid < n) ? bits_f32(rb, GBF) : 0.f;
 #pragma unroll
         for (int i = 0; i < VPT; ++i) {
-            const int idx = tid + 256 * i;
+            const int idx = tid + NT * i;
             if (idx < C * VPPR) {
                 const int r = idx / VPPR, cc = (idx % VPPR) * VPIECE;
-                uint4 val = rv[i];
-                if (r >= n) val = make_uint4(0u, 0u, 0u, 0u);
-                *(uint4*)(sV + r * PV + cc) = val;
+                *(uint4*)(sV + r * PV + cc) = keep_or_zero(rv[i], r < n);
             }
         }
         // the registers are free again: start fetching the next chunk now, so
@@ -470,60 +431,38 @@ kda_chunk_kernel(ChunkParams prm) {
 
         // ================= G2 (KDA): cross-block factors, K^ tile =============
         if constexpr (KDA) {
-            if (myR >= 0) {
-                const int R = myR;
-                floatx2 Zb[NB];
+            if (kact) {
+                const int R = kR;
+                float Zb[NB];
 #pragma unroll
-                for (int b = 0; b < NB; ++b) {
-                    Zb[b][0] = sZ[b * DK + c0];
-                    Zb[b][1] = sZ[b * DK + c0 + 1];
-                }
-                floatx2 Fr = {1.f, 1.f};  // e^{g_n - G_{R+1}} = prod of later blocks
+                for (int b = 0; b < NB; ++b) Zb[b] = sZ[b * DK + kc];
+                float Fr = 1.f;  // e^{g_n - G_{R+1}} = prod of later blocks
 #pragma unroll
                 for (int b = 0; b < NB; ++b)
-                    if (b > R) Fr = Fr * Zb[b];
-                // K^ = k y F, transposed: [channel][token]
+                    if (b > R) Fr *= Zb[b];
+                // K^ = k y F, row-major [token][channel]
 #pragma unroll
-                for (int s = 0; s < 16; s += F::W) {
-#pragma unroll
-                    for (int ch2 = 0; ch2 < 2; ++ch2) {
-                        E* dst = sKT + (c0 + ch2) * PC + 16 * R + s;
-                        if constexpr (sizeof(E) == 2) {
-                            bf16x8 vv;
-#pragma unroll
-                            for (int e = 0; e < 8; ++e) vv[e] = (bf16)(ky[s + e][ch2] * Fr[ch2]);
-                            *(bf16x8*)dst = vv;
-                        } else {
-                            floatx4 vv;
-#pragma unroll
-                            for (int e = 0; e < 4; ++e) vv[e] = ky[s + e][ch2] * Fr[ch2];
-                            *(floatx4*)dst = vv;
-                        }
-                    }
-                }
+                for (int s = 0; s < 16; ++s) sKh[(16 * R + s) * PKH + kc] = from_f32<E>(ky[s] * Fr);
                 if (R == 0) {
                     // block-end factors E'_R = e^{G_{R+1}}, pair scales
                     // Y'_RJ = e^{G_{R+1} - G_{J+1}} (1 on the diagonal), e^{g_n}
-                    floatx2 run = {1.f, 1.f};
+                    float run = 1.f;
 #pragma unroll
                     for (int b = 0; b < NB; ++b) {
-                        run = run * Zb[b];
-                        sE[b * DK + c0] = run[0];
-                        sE[b * DK + c0 + 1] = run[1];
+                        run *= Zb[b];
+                        sE[b * DK + kc] = run;
                     }
-                    sGnv[c0] = run[0];
-                    sGnv[c0 + 1] = run[1];
+                    sGnv[kc] = run;
                     int p = 0;
 #pragma unroll
                     for (int rb2 = 0; rb2 < NB; ++rb2) {
 #pragma unroll
                         for (int jb = 0; jb <= rb2; ++jb, ++p) {
-                            floatx2 y = {1.f, 1.f};
+                            float y = 1.f;
 #pragma unroll
                             for (int m = 0; m < NB; ++m)
-                                if (m > jb && m <= rb2) y = y * Zb[m];
-                            sY[p * DK + c0] = y[0];
-                            sY[p * DK + c0 + 1] = y[1];
+                                if (m > jb && m <= rb2) y *= Zb[m];
+                            sY[p * DK + kc] = y;
                         }
                     }
                 }
@@ -532,40 +471,48 @@ kda_chunk_kernel(ChunkParams prm) {
         }
 
         // ================= AP: A (fp32) and P (operand type) =================
-        for (int p = w; p < Cfg::NPAIR; p += 4) {
+        for (int p = w; p < Cfg::NPAIR; p += NW) {
             int R, J;
             pair_of(p, R, J);
-            floatx4 accA = {0.f, 0.f, 0.f, 0.f}, accP = {0.f, 0.f, 0.f, 0.f};
+            constexpr int NKS = DK / F::KS;
             const E* pa = (KDA ? sKc : sKr) + (16 * J + lr) * PK + F::W * lq;
             const E* pk = sKr + (16 * R + lr) * PK + F::W * lq;
             const E* pq = sQr + (16 * R + lr) * PK + F::W * lq;
+            typename F::T fa[NKS], fk[NKS], fq[NKS];
             if (!KDA || J == R) {
 #pragma unroll
-                for (int kk = 0; kk < DK; kk += F::KS) {
-                    typename F::T af = F::load(pa + kk);
-                    accA = F::mma(accA, af, F::load(pk + kk));
-                    accP = F::mma(accP, af, F::load(pq + kk));
-                }
+                for (int i = 0; i < NKS; ++i) fa[i] = F::load(pa + F::KS * i);
             } else {
                 const float* ps = sY + p * DK + F::W * lq;
 #pragma unroll
-                for (int kk = 0; kk < DK; kk += F::KS) {
-                    typename F::T af = F::load_scaled(pa + kk, ps + kk);
-                    accA = F::mma(accA, af, F::load(pk + kk));
-                    accP = F::mma(accP, af, F::load(pq + kk));
-                }
+                for (int i = 0; i < NKS; ++i) fa[i] = F::load_scaled(pa + F::KS * i, ps + F::KS * i);
+            }
+#pragma unroll
+            for (int i = 0; i < NKS; ++i) {
+                fk[i] = F::load(pk + F::KS * i);
+                fq[i] = F::load(pq + F::KS * i);
+            }
+            floatx4 accA = {0.f, 0.f, 0.f, 0.f}, accP = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int i = 0; i < NKS; ++i) {
+                accA = F::mma(accA, fa[i], fk[i]);
+                accP = F::mma(accP, fa[i], fq[i]);
             }
             // lane holds [m = j = 16J + 4lq + e][n = r = 16R + lr]
             const int rr = 16 * R + lr;
             const float br = sBeta[rr];
             float gr = 0.f;
-            if constexpr (AMODE == KDA_ALPHA_HEAD) gr = sG[rr];
+            floatx4 gj = {0.f, 0.f, 0.f, 0.f};
+            if constexpr (AMODE == KDA_ALPHA_HEAD) {
+                gr = sG[rr];
+                gj = *(const floatx4*)(sG + 16 * J + 4 * lq);
+            }
             floatx4 va, vp;
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const int jj = 16 * J + 4 * lq + e;
                 float f = 1.f;  // scalar decay e^{g_r - g_j}, applied to the result
-                if constexpr (AMODE == KDA_ALPHA_HEAD) f = exp_neg(gr - sG[jj]);
+                if constexpr (AMODE == KDA_ALPHA_HEAD) f = exp_neg(gr - gj[e]);
                 va[e] = (J < R || jj < rr) ? br * accA[e] * f : 0.f;
                 vp[e] = (J < R || jj <= rr) ? accP[e] * f : 0.f;
             }
@@ -611,10 +558,10 @@ kda_chunk_kernel(ChunkParams prm) {
                 for (int i = 0; i < 16; ++i) sTb[(16 * R + i) * PC + 16 * R + j] = from_f32<E>(acc[i] * bj);
             }
         } else if constexpr (KDA) {
-            // waves 1..3: rescale the row operands in place, K~ = k e^{g},
+            // the other waves: rescale the row operands in place, K~ = k e^{g},
             // Q~ = q e^{g} (row operand x E'_R), for the state products
             constexpr int PER_ROW = DK / VPIECE;
-            for (int i = tid - 64; i < 2 * C * PER_ROW; i += 192) {
+            for (int i = tid - 64; i < 2 * C * PER_ROW; i += NT - 64) {
                 const int which = i / (C * PER_ROW);
                 const int rem = i % (C * PER_ROW);
                 const int r = rem / PER_ROW, cc = (rem % PER_ROW) * VPIECE;
@@ -658,7 +605,7 @@ kda_chunk_kernel(ChunkParams prm) {
         }
 
         // ================= S1: X = V - K~ S ===================================
-        for (int item = w; item < NB * NVB; item += 4) {
+        for (int item = w; item < NB * NVB; item += NW) {
             const int R = item % NB, vb = item / NB;
             floatx4 acc = {0.f, 0.f, 0.f, 0.f};
             acc = mma_block<E>(acc, sKr + (16 * R) * PK, PK, sSTc + (16 * vb) * PK, PK, DK);
@@ -674,7 +621,7 @@ kda_chunk_kernel(ChunkParams prm) {
         __syncthreads();
 
         // ================= S2: u = T' X =======================================
-        for (int item = w; item < NB * NVB; item += 4) {
+        for (int item = w; item < NB * NVB; item += NW) {
             const int R = item % NB, vb = item / NB;
             constexpr int KS = Frag<E>::KS;
             const int K = ((16 * (R + 1) + KS - 1) / KS) * KS;
@@ -691,7 +638,7 @@ kda_chunk_kernel(ChunkParams prm) {
         __syncthreads();
 
         // ================= S3: o = (Q e^g) S + P u ============================
-        for (int item = w; item < NB * NVB; item += 4) {
+        for (int item = w; item < NB * NVB; item += NW) {
             const int R = item % NB, vb = item / NB;
             constexpr int KS = Frag<E>::KS;
             const int K = ((16 * (R + 1) + KS - 1) / KS) * KS;
@@ -708,33 +655,35 @@ kda_chunk_kernel(ChunkParams prm) {
         }
 
         // ================= S4: S = e^{g_n} S + K^^T u =========================
+        // The K^ operand is read transposed out of its row-major tile.
         {
             const E* ub = KDA ? sUT : sUhT;
+            const E* kt = KDA ? sKh : sKr;
+            constexpr int LDK = KDA ? PKH : PK;
 #pragma unroll
-            for (int i = 0; i < SB_PER_WAVE; ++i) {
-                const int item = w + 4 * i;
-                const int cb = item % NCB, vb = item / NCB;
-                floatx4 acc = Sreg[i];
+            for (int i = 0; i < SBW; ++i) {
+                const int item = w + NW * i;
+                if (item < NCB * NVB) {
+                    const int cb = item % NCB, vb = item / NCB;
+                    floatx4 acc = Sreg[i];
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    if constexpr (KDA) acc[e] *= sGnv[16 * cb + 4 * lq + e];
-                    else if constexpr (AMODE == KDA_ALPHA_HEAD) acc[e] *= sGn1[0];
+                    for (int e = 0; e < 4; ++e) {
+                        if constexpr (KDA) acc[e] *= sGnv[16 * cb + 4 * lq + e];
+                        else if constexpr (AMODE == KDA_ALPHA_HEAD) acc[e] *= sGn1[0];
+                    }
+                    acc = mma_block_at<E>(acc, kt, LDK, 16 * cb, ub + (16 * vb) * PC, PC, C);
+                    Sreg[i] = acc;
+                    store_acc_transposed<E>(sSTn + (16 * vb) * PK + 16 * cb, PK, acc);
                 }
-                acc = mma_block<E>(acc, sKT + (16 * cb) * PC, PC, ub + (16 * vb) * PC, PC, C);
-                Sreg[i] = acc;
-                store_acc_transposed<E>(sSTn + (16 * vb) * PK + 16 * cb, PK, acc);
             }
         }
         __syncthreads();
 
         // ================= o tile -> HBM (valid rows only) ====================
-        {
-            for (int i = tid; i < C * VPPR; i += Cfg::NTHREADS) {
-                const int r = i / VPPR, cc = (i % VPPR) * VPIECE;
-                if (r < n)
-                    *(uint4*)(go + (((uint32_t)t0 + r) * DV + cc) * ESZ) =
-                        *(const uint4*)(sO + r * PV + cc);
-            }
+        for (int i = tid; i < C * VPPR; i += NT) {
+            const int r = i / VPPR, cc = (i % VPPR) * VPIECE;
+            if (r < n)
+                *(uint4*)(go + (((uint32_t)t0 + r) * DV + cc) * ESZ) = *(const uint4*)(sO + r * PV + cc);
         }
     }
 
@@ -742,13 +691,12 @@ kda_chunk_kernel(ChunkParams prm) {
     if (prm.S_final) {
         float* sf = prm.S_final + (int64_t)bh * DK * DV + v0;
 #pragma unroll
-        for (int i = 0; i < SB_PER_WAVE; ++i) {
-            const int item = w + 4 * i;
-            const int cb = item % NCB, vb = item / NCB;
+        for (int i = 0; i < SBW; ++i) {
+            const int item = w + NW * i;
+            if (item < NCB * NVB) {
+                const int cb = item % NCB, vb = item / NCB;
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int row = 16 * cb + 4 * lq + e;
-                sf[row * DV + 16 * vb + lr] = Sreg[i][e];
+                for (int e = 0; e < 4; ++e) sf[(16 * cb + 4 * lq + e) * DV + 16 * vb + lr] = Sreg[i][e];
             }
         }
     }

@@ -152,6 +152,52 @@ __device__ __forceinline__ void store_acc_transposed(E* dst, int ld, floatx4 acc
     }
 }
 
+// A operand fragment of K^T-like products read from a row-major [k][m] tile
+// (m contiguous, pitch ld): lane (m = l%16, q = l/16) receives
+// A[m][k0 + W q .. + W - 1] = T[k0 + W q + i][m0 + m].
+//   bf16: two ds_read_b64_tr_b16.  Within a 16-lane group that instruction
+//   hands output lane l element e of source lane (4e + l/4)'s 8 bytes, element
+//   l%4; pointing source lane i at row i/4, column 4(i%4) of a 4-row slab
+//   therefore delivers 4 consecutive rows of column l.
+//   fp32: four scalar reads down the column.
+__device__ __forceinline__ bf16x8 load_frag_tr(const bf16* T, int ld, int k0, int m0) {
+    typedef short v4s __attribute__((ext_vector_type(4)));
+    const int l = lane_id();
+    const int q = l >> 4, i = l & 15;
+    const bf16* p = T + (k0 + 8 * q + (i >> 2)) * ld + m0 + 4 * (i & 3);
+    v4s lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4s*)p);
+    v4s hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (__attribute__((address_space(3))) v4s*)(p + 4 * ld));
+    // repack as whole 32-bit words (per-element bf16 casts were miscompiled)
+    typedef int v2i __attribute__((ext_vector_type(2)));
+    typedef int v4i __attribute__((ext_vector_type(4)));
+    const v2i a = __builtin_bit_cast(v2i, lo), b = __builtin_bit_cast(v2i, hi);
+    const v4i c = {a[0], a[1], b[0], b[1]};
+    return __builtin_bit_cast(bf16x8, c);
+}
+__device__ __forceinline__ floatx4 load_frag_tr(const float* T, int ld, int k0, int m0) {
+    const int l = lane_id();
+    const int q = l >> 4, m = l & 15;
+    const float* p = T + (k0 + 4 * q) * ld + m0 + m;
+    floatx4 r = {p[0], p[ld], p[2 * ld], p[3 * ld]};
+    return r;
+}
+
+// acc(16x16) += A * B^T where A[m][k] = T[k][m0 + m] comes from a row-major
+// [k][m] tile (read transposed) and B is k-contiguous ([n][k], pitch ldb).
+template <typename E>
+__device__ __forceinline__ floatx4 mma_block_at(floatx4 acc, const E* T, int ldt, int m0,
+                                                const E* B, int ldb, int K) {
+    const int l = lane_id();
+    const int r = l & 15, q = l >> 4;
+    typedef Frag<E> F;
+    const E* pb = B + r * ldb + F::W * q;
+#pragma unroll
+    for (int kk = 0; kk < K; kk += F::KS)
+        acc = F::mma(acc, load_frag_tr(T, ldt, kk, m0), F::load(pb + kk));
+    return acc;
+}
+
 // ---- fast exp for decay factors (inputs <= 0) -----------------------------
 __device__ __forceinline__ float exp_neg(float x) { return __expf(x); }
 
