@@ -165,6 +165,9 @@ def main():
     ap.add_argument("--workload", type=int, default=2, help="prefill workload number (1-4)")
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run one plain 256 MiB device copy (a known-size "
+                         "reference for hardware byte counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on exactly one GPU (got --gpus {args.gpus}): the KDA hot path "
@@ -176,6 +179,12 @@ def main():
     from linear_attention_sequence_kda_amd import inputs as gen
 
     kda.library()  # fail loudly if the HIP library is missing
+    if args.copy_calibration:
+        src = torch.ones(64 << 20, dtype=torch.float32, device="cuda:0")  # 256 MiB
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     w = gen.WORKLOADS[args.workload]
     x, wall, kern_ms = bench_prefill(torch, kda, gen, w, args.steps, args.warmup)
     ms_per_step = wall * 1e3 / args.steps

@@ -56,13 +56,15 @@ struct ChunkCfg {
     static constexpr int NB = C / 16;                  // 16-token sub-blocks per chunk
     static constexpr int NPAIR = NB * (NB + 1) / 2;    // (R, J <= R) block pairs
     static constexpr int ESZ = sizeof(E);
-    static constexpr int PADE = 16 / ESZ;              // 16 bytes of padding per row
+    // Row pitches: operand tiles are read 16 bytes per lane as (row l%16,
+    // 16-byte column l/16); on gfx950 those reads are free of bank conflicts
+    // when the pitch is 32 (mod 64) bytes, so rows carry 32 bytes of padding.
+    static constexpr int PADE = 32 / ESZ;
     static constexpr int PK = DK + PADE;               // pitch of [*][DK] tiles
     static constexpr int PC = C + PADE;                // pitch of [*][C] tiles
     static constexpr int PV = NV + PADE;               // pitch of [C][NV] tiles
     static constexpr int PA = C + 4;                   // pitch of the fp32 A/T tile
-    static constexpr int PD = 20;                      // pitch of a transposed 16x16 fp32 block
-    static constexpr int PKH = DK + 32 / ESZ;          // pitch of the KDA K^ tile (read transposed)
+    static constexpr int PKH = PK;                     // pitch of the KDA K^ tile (read transposed)
     static constexpr int NCB = DK / 16, NVB = NV / 16; // 16x16 blocks of the state slice
     static constexpr int NW = 8;                       // waves per workgroup (2 per SIMD)
     static constexpr int NTHREADS = 64 * NW;
@@ -90,8 +92,7 @@ struct ChunkCfg {
     static constexpr int O_UHT = O_UT + NV * PC * ESZ;
     static constexpr int SZ_UHT = KDA ? 0 : NV * PC * ESZ;
     static constexpr int O_A = O_UHT + SZ_UHT;
-    static constexpr int O_AD = O_A + C * PA * 4;      // transposed diagonal blocks of A
-    static constexpr int O_GATE = O_AD + NB * 16 * PD * 4;
+    static constexpr int O_GATE = O_A + C * PA * 4;
     // KDA gate area: Z[NB][DK], E'[NB][DK], Y'[NPAIR][DK], e^{g_n}[DK]
     // scalar gate area: g[C], e^g[C], e^{g_n-g}[C], e^{g_n} (one float, padded)
     static constexpr int SZ_GATE = KDA ? (2 * NB + NPAIR + 1) * DK * 4 : (3 * C + 4) * 4;
@@ -160,7 +161,7 @@ kda_chunk_kernel(ChunkParams prm) {
     typedef Frag<E> F;
     constexpr int DK = Cfg::DK, NV = Cfg::NV, C = Cfg::C, NB = Cfg::NB, AMODE = Cfg::AMODE;
     constexpr bool KDA = Cfg::KDA;
-    constexpr int PK = Cfg::PK, PC = Cfg::PC, PV = Cfg::PV, PA = Cfg::PA, PD = Cfg::PD;
+    constexpr int PK = Cfg::PK, PC = Cfg::PC, PV = Cfg::PV, PA = Cfg::PA;
     constexpr int PKH = Cfg::PKH;
     constexpr int NCB = Cfg::NCB, NVB = Cfg::NVB, NW = Cfg::NW, NT = Cfg::NTHREADS;
     constexpr int SBW = Cfg::SBW;
@@ -181,7 +182,6 @@ kda_chunk_kernel(ChunkParams prm) {
     E* sUT = (E*)(smem + Cfg::O_UT);
     E* sUhT = (E*)(smem + Cfg::O_UHT);
     float* sA = (float*)(smem + Cfg::O_A);
-    float* sAd = (float*)(smem + Cfg::O_AD);
     float* sGate = (float*)(smem + Cfg::O_GATE);
     float* sBeta = (float*)(smem + Cfg::O_BETA);
     // KDA gate views
@@ -398,15 +398,9 @@ kda_chunk_kernel(ChunkParams prm) {
             // per-token decay: g = inclusive prefix sum of ln(alpha) over the chunk
             if (w == 0) {
                 float g = 0.f;
-                if constexpr (AMODE == KDA_ALPHA_HEAD) {
-                    g = (l < n) ? bits_f32(rla, GBF) : 0.f;
-#pragma unroll
-                    for (int off = 1; off < 64; off <<= 1) {
-                        const float y = __shfl_up(g, off, 64);
-                        if (l >= off) g += y;
-                    }
-                }
-                const float gn = __shfl(g, C - 1, 64);
+                if constexpr (AMODE == KDA_ALPHA_HEAD)
+                    g = wave_inclusive_sum((l < n) ? bits_f32(rla, GBF) : 0.f);
+                const float gn = read_lane(g, C - 1);
                 if (l < C) {
                     sG[l] = g;
                     sEg[l] = exp_neg(g);
@@ -518,50 +512,46 @@ kda_chunk_kernel(ChunkParams prm) {
             }
             *(floatx4*)(sA + rr * PA + 16 * J + 4 * lq) = va;
             st4<E>(sP + rr * PC + 16 * J + 4 * lq, vp);
-            if (J == R) {
-                // transposed copy of the diagonal block for the column sweep of T1
-#pragma unroll
-                for (int e = 0; e < 4; ++e) sAd[(R * 16 + 4 * lq + e) * PD + lr] = va[e];
-            }
         }
         __syncthreads();
 
         // ================= T1: diagonal blocks by forward substitution =======
-        // Lane (R, j) owns column j of T_RR.  Right-looking sweep: once t_m is
-        // final, every later row takes its A_RR[i][m] t_m term, so the chain of
-        // dependent steps is 16 long.  Results: T_RR^T (fp32) in the diagonal
-        // block of sA, and T_RR diag(beta) in operand precision in sTb.
-        if (w == 0) {
-            if (l < 16 * NB) {
-                const int R = l >> 4, j = l & 15;
-                float acc[16];
+        // Wave R < NB solves block R.  Lane (j, s) = (l/4, l%4) owns rows
+        // 4s..4s+3 of column j of T_RR, with those rows of A_RR in registers.
+        // Right-looking sweep: once t_m is final, its owner lane hands it to
+        // the other three lanes of the quad (DPP broadcast) and every row takes
+        // its A_RR[i][m] t_m term; the dependent chain is 15 VALU steps long.
+        // (A_RR[i][m] is zero for m >= i, so no row needs masking.)
+        // Results: T_RR^T (fp32) in the diagonal block of sA, and
+        // T_RR diag(beta) in operand precision in sTb.
+        if (w < NB) {
+            const int R = w, j = l >> 2, s4 = l & 3;
+            floatx4 arow[4][4];  // arow[ii][q4] = A_RR[4 s4 + ii][4 q4 .. 4 q4 + 3]
 #pragma unroll
-                for (int i = 0; i < 16; ++i) acc[i] = (i == j) ? 1.f : 0.f;
-                const float* Ad = sAd + (R * 16) * PD;  // Ad[m * PD + i] = A_RR[i][m]
+            for (int ii = 0; ii < 4; ++ii)
 #pragma unroll
-                for (int m = 0; m < 15; ++m) {
-                    floatx4 col[4];
+                for (int q4 = 0; q4 < 4; ++q4)
+                    arow[ii][q4] = *(const floatx4*)(sA + (16 * R + 4 * s4 + ii) * PA + 16 * R + 4 * q4);
+            float acc[4];
 #pragma unroll
-                    for (int q4 = 0; q4 < 4; ++q4) col[q4] = *(const floatx4*)(Ad + m * PD + 4 * q4);
-                    const float tm = acc[m];
+            for (int ii = 0; ii < 4; ++ii) acc[ii] = (4 * s4 + ii == j) ? 1.f : 0.f;
 #pragma unroll
-                    for (int i = m + 1; i < 16; ++i) acc[i] -= col[i >> 2][i & 3] * tm;
-                }
-                float* dst = sA + (16 * R + j) * PA + 16 * R;
+            for (int m = 0; m < 15; ++m) {
+                const float tm = quad_bcast(acc[m & 3], m >> 2);
 #pragma unroll
-                for (int i = 0; i < 16; i += 4) {
-                    floatx4 v4 = {acc[i], acc[i + 1], acc[i + 2], acc[i + 3]};
-                    *(floatx4*)(dst + i) = v4;
-                }
-                const float bj = sBeta[16 * R + j];
-#pragma unroll
-                for (int i = 0; i < 16; ++i) sTb[(16 * R + i) * PC + 16 * R + j] = from_f32<E>(acc[i] * bj);
+                for (int ii = 0; ii < 4; ++ii) acc[ii] -= arow[ii][m >> 2][m & 3] * tm;
             }
+            floatx4 v4 = {acc[0], acc[1], acc[2], acc[3]};
+            *(floatx4*)(sA + (16 * R + j) * PA + 16 * R + 4 * s4) = v4;
+            const float bj = sBeta[16 * R + j];
+#pragma unroll
+            for (int ii = 0; ii < 4; ++ii)
+                sTb[(16 * R + 4 * s4 + ii) * PC + 16 * R + j] = from_f32<E>(acc[ii] * bj);
         } else if constexpr (KDA) {
             // the other waves: rescale the row operands in place, K~ = k e^{g},
             // Q~ = q e^{g} (row operand x E'_R), for the state products
             constexpr int PER_ROW = DK / VPIECE;
-            for (int i = tid - 64; i < 2 * C * PER_ROW; i += NT - 64) {
+            for (int i = tid - 64 * NB; i < 2 * C * PER_ROW; i += NT - 64 * NB) {
                 const int which = i / (C * PER_ROW);
                 const int rem = i % (C * PER_ROW);
                 const int r = rem / PER_ROW, cc = (rem % PER_ROW) * VPIECE;

@@ -198,6 +198,42 @@ __device__ __forceinline__ floatx4 mma_block_at(floatx4 acc, const E* T, int ldt
     return acc;
 }
 
+// ---- cross-lane moves (DPP) -------------------------------------------------
+// Value of lane 4*(l/4) + so (so a compile-time constant after unrolling): a
+// quad_perm broadcast inside every group of four lanes.
+__device__ __forceinline__ float quad_bcast(float x, int so) {
+    int v = __float_as_int(x);
+    switch (so) {
+        case 0: v = __builtin_amdgcn_mov_dpp(v, 0x00, 0xf, 0xf, false); break;
+        case 1: v = __builtin_amdgcn_mov_dpp(v, 0x55, 0xf, 0xf, false); break;
+        case 2: v = __builtin_amdgcn_mov_dpp(v, 0xaa, 0xf, 0xf, false); break;
+        default: v = __builtin_amdgcn_mov_dpp(v, 0xff, 0xf, 0xf, false); break;
+    }
+    return __int_as_float(v);
+}
+
+// Inclusive prefix sum over the 64 lanes of a wave: shifts by 1, 2, 4, 8
+// inside each row of 16 lanes, then the last lane of row 0 (row 2) is added
+// to row 1 (row 3) and the last lane of row 1 to rows 2 and 3.  Lanes with no
+// source add the "old" operand, 0.
+__device__ __forceinline__ float wave_inclusive_sum(float x) {
+#define KDA_DPP_ADD(ctrl, rmask)                                                              \
+    x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), ctrl, rmask, 0xf, \
+                                                    false))
+    KDA_DPP_ADD(0x111, 0xf);  // row_shr:1
+    KDA_DPP_ADD(0x112, 0xf);  // row_shr:2
+    KDA_DPP_ADD(0x114, 0xf);  // row_shr:4
+    KDA_DPP_ADD(0x118, 0xf);  // row_shr:8
+    KDA_DPP_ADD(0x142, 0xa);  // row_bcast:15 into rows 1 and 3
+    KDA_DPP_ADD(0x143, 0xc);  // row_bcast:31 into rows 2 and 3
+#undef KDA_DPP_ADD
+    return x;
+}
+
+__device__ __forceinline__ float read_lane(float x, int lane) {
+    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), lane));
+}
+
 // ---- fast exp for decay factors (inputs <= 0) -----------------------------
 __device__ __forceinline__ float exp_neg(float x) { return __expf(x); }
 
