@@ -62,7 +62,46 @@ int check_shape(const kda_shape* s, bool decode) {
     if (bh > (int64_t)(INT_MAX / 8)) return KDA_ERR_SHAPE;
     if (!mul_ok(bh, s->L, &tok)) return KDA_ERR_SHAPE;
     if (!mul_ok(tok, 128, &x)) return KDA_ERR_SHAPE;
+    // kernels address one head's [L, d] tensors with 32-bit byte offsets
+    if (s->L > (int64_t)(INT_MAX / (128 * 4))) return KDA_ERR_SHAPE;
     return KDA_OK;
+}
+
+// ---- prefill plan: chunk spans and workspace ----------------------------------
+// The intra-chunk kernel writes one record per (head, chunk) of a span of
+// chunks, the inter-chunk kernel consumes them; long inputs run as several
+// spans, so the records of one span stay within a bounded workspace (and, at
+// the target size, within the 256 MiB memory-side cache of an MI355X).  Between
+// spans the state goes through S_final, or through the workspace's state area
+// when no final state is wanted.
+constexpr int64_t kSpanTargetBytes = 96ll << 20;
+
+struct Plan {
+    int C = 0;
+    int64_t nchunks = 0, span = 0, nspans = 0;
+    int64_t rec_bytes = 0, rec_area = 0, state_area = 0;
+    int64_t ws_bytes = 0;
+};
+
+Plan make_plan(const kda_shape* s) {
+    Plan p;
+    const int bf = s->qkv_dtype == KDA_BF16;
+    const int64_t bh = s->B * s->H;
+    p.C = kda::chunk_len(bf);
+    p.nchunks = (s->L + p.C - 1) / p.C;
+    if (bh == 0 || p.nchunks == 0) return p;
+    p.rec_bytes = kda::rec_layout((int)s->dk, (int)s->dv, p.C, bf ? 2 : 4,
+                                  s->alpha_mode == KDA_ALPHA_CHANNEL)
+                      .bytes;
+    int64_t per_chunk = bh * p.rec_bytes;
+    p.span = kSpanTargetBytes / per_chunk;
+    if (p.span < 1) p.span = 1;
+    if (p.span > p.nchunks) p.span = p.nchunks;
+    p.nspans = (p.nchunks + p.span - 1) / p.span;
+    p.rec_area = p.span * per_chunk;
+    p.state_area = p.nspans > 1 ? bh * s->dk * s->dv * 4 : 0;
+    p.ws_bytes = p.rec_area + p.state_area;
+    return p;
 }
 
 }  // namespace
@@ -89,8 +128,8 @@ const char* kda_strerror(int status) {
 const char* kda_last_error(void) { return g_last_error.c_str(); }
 
 size_t kda_chunk_fwd_workspace_bytes(const kda_shape* shape) {
-    (void)check_shape(shape, false);
-    return 0;  // the fused kernel keeps every intermediate on chip
+    if (check_shape(shape, false) != KDA_OK) return 0;
+    return (size_t)make_plan(shape).ws_bytes;
 }
 
 int kda_chunk_fwd(const kda_shape* s, const void* q, const void* k, const void* v,
@@ -111,7 +150,9 @@ int kda_chunk_fwd(const kda_shape* s, const void* q, const void* k, const void* 
     const void* ptrs[] = {q, k, v, has_alpha ? log_alpha : nullptr, beta, S0, o, S_final, workspace};
     for (const void* p : ptrs)
         if (p && !aligned16(p)) return KDA_ERR_ALIGN;
-    if (workspace_bytes < kda_chunk_fwd_workspace_bytes(s)) return KDA_ERR_WORKSPACE;
+    const Plan plan = make_plan(s);
+    if (plan.ws_bytes > 0 && (!workspace || workspace_bytes < (size_t)plan.ws_bytes))
+        return KDA_ERR_WORKSPACE;
 
     const int64_t la_elems = s->alpha_mode == KDA_ALPHA_CHANNEL ? tok * s->dk : tok;
     const Span sq = span_of(q, tok * s->dk * eq), sk = span_of(k, tok * s->dk * eq),
@@ -124,26 +165,57 @@ int kda_chunk_fwd(const kda_shape* s, const void* q, const void* k, const void* 
         if (overlaps(so, in) || overlaps(sf, in)) return KDA_ERR_ALIAS;
     if (overlaps(so, s0) || overlaps(so, sf)) return KDA_ERR_ALIAS;
     if (overlaps(sf, s0) && (const void*)S_final != (const void*)S0) return KDA_ERR_ALIAS;
+    const Span sw = span_of(workspace, plan.ws_bytes);
+    const Span all[] = {sq, sk, sv, sla, sb, s0, so, sf};
+    for (const Span& x : all)
+        if (overlaps(sw, x)) return KDA_ERR_ALIAS;
 
     if (bh == 0) return KDA_OK;
-    kda::ChunkParams prm;
-    prm.q = q;
-    prm.k = k;
-    prm.v = v;
-    prm.log_alpha = has_alpha ? log_alpha : nullptr;
-    prm.beta = beta;
-    prm.S0 = S0;
-    prm.o = o;
-    prm.S_final = S_final;
-    prm.L = s->L;
-    prm.BH = (int)bh;
-    prm.DV = (int)s->dv;
-    prm.n_slices = 0;
-    prm.gate_bf16 = s->gate_dtype == KDA_BF16;
-    prm.alpha_mode = s->alpha_mode;
     const int qbf = s->qkv_dtype == KDA_BF16;
+    const hipStream_t stream = (hipStream_t)hip_stream;
     const int nv = kda::chunk_slice_width((int)s->dk, (int)s->dv, qbf, bh);
-    hipError_t err = kda::launch_chunk(prm, (int)s->dk, qbf, nv, (hipStream_t)hip_stream);
+    float* s_mid = S_final ? S_final : (float*)((char*)workspace + plan.rec_area);
+
+    kda::IntraParams ip;
+    ip.q = q;
+    ip.k = k;
+    ip.v = v;
+    ip.log_alpha = has_alpha ? log_alpha : nullptr;
+    ip.beta = beta;
+    ip.ws = workspace;
+    ip.L = s->L;
+    ip.BH = (int)bh;
+    ip.gate_bf16 = s->gate_dtype == KDA_BF16;
+    kda::InterParams xp;
+    xp.ws = workspace;
+    xp.o = o;
+    xp.L = s->L;
+    xp.BH = (int)bh;
+    xp.DV = (int)s->dv;
+    xp.n_slices = 0;
+
+    hipError_t err = hipSuccess;
+    if (plan.nchunks == 0) {
+        // L == 0: the final state is the initial one
+        xp.S_in = S0;
+        xp.S_out = S_final;
+        xp.c0 = 0;
+        xp.ncs = 0;
+        err = kda::launch_inter(xp, (int)s->dk, qbf, s->alpha_mode, nv, stream);
+    }
+    for (int64_t sp = 0; sp < plan.nspans && err == hipSuccess; ++sp) {
+        const int64_t c0 = sp * plan.span;
+        const int64_t ncs = plan.nchunks - c0 < plan.span ? plan.nchunks - c0 : plan.span;
+        ip.c0 = c0;
+        ip.ncs = (int)ncs;
+        err = kda::launch_intra(ip, (int)s->dk, (int)s->dv, qbf, s->alpha_mode, stream);
+        if (err != hipSuccess) break;
+        xp.S_in = sp == 0 ? S0 : s_mid;
+        xp.S_out = sp == plan.nspans - 1 ? S_final : s_mid;
+        xp.c0 = c0;
+        xp.ncs = (int)ncs;
+        err = kda::launch_inter(xp, (int)s->dk, qbf, s->alpha_mode, nv, stream);
+    }
     if (err != hipSuccess) {
         g_last_error = std::string("kda_chunk_fwd: ") + hipGetErrorString(err);
         return KDA_ERR_HIP;

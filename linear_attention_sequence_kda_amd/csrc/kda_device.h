@@ -198,6 +198,91 @@ __device__ __forceinline__ floatx4 mma_block_at(floatx4 acc, const E* T, int ldt
     return acc;
 }
 
+// acc(16x16) += A * B^T where A is k-contiguous ([m][k], pitch lda) and
+// B[n][k] = T[k][n0 + n] comes from a row-major [k][n] tile read transposed.
+template <typename E>
+__device__ __forceinline__ floatx4 mma_block_bt(floatx4 acc, const E* A, int lda, const E* T,
+                                                int ldt, int n0, int K) {
+    const int l = lane_id();
+    const int r = l & 15, q = l >> 4;
+    typedef Frag<E> F;
+    const E* pa = A + r * lda + F::W * q;
+#pragma unroll
+    for (int kk = 0; kk < K; kk += F::KS)
+        acc = F::mma(acc, F::load(pa + kk), load_frag_tr(T, ldt, kk, n0));
+    return acc;
+}
+
+// ---- operand records ("fragment order") -----------------------------------
+// Element offset of operand element (m, k) of an operand with K columns, in
+// the order a 16x16 MFMA tile loop reads it: 16-byte pieces of W consecutive
+// k, piece ((m/16) * (K/KS) + k/KS) * 64 + ((k % KS) / W) * 16 + m % 16.
+template <typename E>
+__device__ __forceinline__ uint32_t frag_elem(int m, int k, int K) {
+    constexpr int W = Frag<E>::W, KS = Frag<E>::KS;
+    return (uint32_t)((((m >> 4) * (K / KS) + k / KS) * 64 + ((k % KS) / W) * 16 + (m & 15)) * W +
+                      k % W);
+}
+
+// ---- small stores and loads --------------------------------------------------
+template <typename E>
+__device__ __forceinline__ void st4(E* p, floatx4 v) {
+    if constexpr (sizeof(E) == 2) {
+        bf16x4 t;
+        t[0] = (bf16)v[0];
+        t[1] = (bf16)v[1];
+        t[2] = (bf16)v[2];
+        t[3] = (bf16)v[3];
+        *(bf16x4*)p = t;
+    } else {
+        *(floatx4*)p = v;
+    }
+}
+
+// v if keep, else zero (an explicit mask: a select of 16-byte values can be
+// lowered into a select of stack addresses)
+__device__ __forceinline__ uint4 keep_or_zero(uint4 v, bool keep) {
+    const uint32_t m = keep ? 0xffffffffu : 0u;
+    return make_uint4(v.x & m, v.y & m, v.z & m, v.w & m);
+}
+
+// Load through a uniform base pointer plus a 32-bit byte offset (saddr form).
+template <typename T>
+__device__ __forceinline__ T ldg(const void* base, uint32_t byte_off) {
+    return *(const T*)((const char*)base + byte_off);
+}
+
+// Buffer resource over [base, base + bytes): loads past the end return zero
+// and stores past the end are dropped by the hardware.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc((void*)base, (short)0, (int)bytes, 0x00020000);
+}
+// Store four values (converted to E) at byte offset off of a buffer.
+template <typename E>
+__device__ __forceinline__ void buf_st4(__amdgpu_buffer_rsrc_t r, uint32_t off, floatx4 v) {
+    typedef int v2i __attribute__((ext_vector_type(2)));
+    typedef int v4i __attribute__((ext_vector_type(4)));
+    if constexpr (sizeof(E) == 2) {
+        bf16x4 t;
+        t[0] = (bf16)v[0];
+        t[1] = (bf16)v[1];
+        t[2] = (bf16)v[2];
+        t[3] = (bf16)v[3];
+        __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(v2i, t), r, (int)off, 0, 0);
+    } else {
+        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(v4i, v), r, (int)off, 0, 0);
+    }
+}
+
+__device__ __forceinline__ void pair_of(int p, int& R, int& J) {
+    R = 0;
+    while (p >= R + 1) {
+        p -= R + 1;
+        ++R;
+    }
+    J = p;
+}
+
 // ---- cross-lane moves (DPP) -------------------------------------------------
 // Value of lane 4*(l/4) + so (so a compile-time constant after unrolling): a
 // quad_perm broadcast inside every group of four lanes.

@@ -8,23 +8,87 @@
 
 namespace kda {
 
-// Arguments of the fused chunkwise prefill kernel (one (b,h) per BH index).
-struct ChunkParams {
+// ---- two-kernel prefill --------------------------------------------------
+// The intra-chunk kernel writes, per (b,h) head and chunk, one record of the
+// chunk's state-independent factors; the inter-chunk kernel walks the chunks
+// in order and carries the state.  Record sections (byte offsets, each
+// section 256-byte aligned), C = chunk length, E = the q/k/v element type:
+//   w    W   = T diag(beta e^g) K     [C][DK]  E, fragment order (rows = token)
+//   ut   U   = T diag(beta) V         [C][DV]  E, accumulator order
+//   p    P   (decayed causal Q K^T)   [C][C]   E, fragment order (rows = token)
+//   kt   K^T (KDA: (K e^{g_n-g})^T)   [DK][C]  E, fragment order (rows = channel)
+//   qt   Q (KDA: Q e^g)               [C][DK]  E, fragment order (rows = token)
+//   gam  KDA only: e^{g_n} per key channel, DK floats
+//   rs   scalar decay only: e^{g_r} [C], e^{g_n-g_r} [C], e^{g_n}, fp32
+// "Fragment order" stores an operand with rows m and contraction index k the
+// way a 16x16 MFMA tile loop consumes it: 16-byte pieces (W = 16/sizeof(E)
+// consecutive k) of row m, piece index ((m/16) * (K/KS) + k/KS) * 64 + lane,
+// lane = ((k % KS) / W) * 16 + m % 16, KS = 4 W, so each lane of a wave reads
+// its operand for one k step of one 16-row block with one 16-byte load and the
+// 64 lanes read 1 KiB of contiguous memory.  "Accumulator order" stores the
+// 16x16 blocks (R, vb) of U as lane-major quads, PF = 16 / (4 sizeof(E))
+// column blocks side by side in each lane's 16 bytes: element
+// (16R + 4(l/16) + i, 16vb + l%16) at
+// ((R * DV/(16 PF) + vb/PF) * 64 + l) * 4 PF + (vb % PF) * 4 + i.
+struct RecLayout {
+    uint32_t w, ut, p, kt, qt, gam, rs, bytes;
+};
+__host__ __device__ constexpr uint32_t rec_align(uint32_t x) { return (x + 255u) & ~255u; }
+__host__ __device__ constexpr RecLayout rec_layout(int dk, int dv, int c, int esz, bool kda) {
+    RecLayout r{0, 0, 0, 0, 0, 0, 0, 0};
+    uint32_t o = 0;
+    r.w = o;
+    o = rec_align(o + (uint32_t)(c * dk * esz));
+    r.ut = o;
+    o = rec_align(o + (uint32_t)(c * dv * esz));
+    r.p = o;
+    o = rec_align(o + (uint32_t)(c * c * esz));
+    r.kt = o;
+    o = rec_align(o + (uint32_t)(dk * c * esz));
+    r.qt = o;
+    o = rec_align(o + (uint32_t)(c * dk * esz));
+    r.gam = o;
+    if (kda) o = rec_align(o + (uint32_t)(dk * 4));
+    r.rs = o;
+    if (!kda) o = rec_align(o + (uint32_t)((2 * c + 4) * 4));
+    r.bytes = o;
+    return r;
+}
+
+// Chunk length of the prefill kernels: 64 tokens with bf16 operands, 32 in fp32.
+constexpr int chunk_len(int qkv_bf16) { return qkv_bf16 ? 64 : 32; }
+
+struct IntraParams {
     const void* q;          // [BH, L, DK]  qkv type
     const void* k;          // [BH, L, DK]
     const void* v;          // [BH, L, DV]
     const void* log_alpha;  // [BH, L, DK] | [BH, L] | unused, gate type
     const void* beta;       // [BH, L] gate type
-    const float* S0;        // [BH, DK, DV] or null
-    void* o;                // [BH, L, DV]  qkv type
-    float* S_final;         // [BH, DK, DV] or null
+    void* ws;               // records [BH][ncs]
     int64_t L;
+    int64_t c0;             // first chunk of this span
+    int ncs;                // chunks in this span
+    int BH;
+    int gate_bf16;
+};
+
+struct InterParams {
+    const void* ws;         // records [BH][ncs] written by the intra-chunk kernel
+    const float* S_in;      // [BH, DK, DV] or null (zero state)
+    float* S_out;           // [BH, DK, DV] or null; may equal S_in
+    void* o;                // [BH, L, DV]  qkv type
+    int64_t L;
+    int64_t c0;
+    int ncs;
     int BH;
     int DV;
-    int n_slices;           // DV / slice width (set by launch_chunk)
-    int gate_bf16;
-    int alpha_mode;
+    int n_slices;           // DV / slice width (set by launch_inter)
 };
+
+hipError_t launch_intra(const IntraParams& prm, int dk, int dv, int qkv_bf16, int alpha_mode,
+                        hipStream_t stream);
+hipError_t launch_inter(InterParams prm, int dk, int qkv_bf16, int alpha_mode, int nv,
+                        hipStream_t stream);
 
 // Arguments of the decode step kernel.
 struct DecodeParams {
@@ -40,10 +104,9 @@ struct DecodeParams {
     int alpha_mode;
 };
 
-// State-column slice width the prefill kernel uses for this problem.
+// State-column slice width the inter-chunk kernel uses for this problem.
 int chunk_slice_width(int dk, int dv, int qkv_bf16, int64_t BH);
 
-hipError_t launch_chunk(ChunkParams prm, int dk, int qkv_bf16, int nv, hipStream_t stream);
 hipError_t launch_decode(const DecodeParams& prm, int dk, int dv, int qkv_bf16,
                          hipStream_t stream);
 

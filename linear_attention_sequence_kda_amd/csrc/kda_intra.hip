@@ -1,0 +1,555 @@
+// kda_intra.hip -- intra-chunk kernel of the two-kernel chunkwise prefill
+// (gfx950 / MI355X).
+//
+// Math: "22,580: From GPT-2 to Kimi K3" (yichencityu.github.io) section 6.3
+// gives the alpha = 1 chunk form (A, T = (I + A)^-1 by forward substitution,
+// W = T diag(beta) K, U = T diag(beta) V, u = U - W S, O = Q S + P u); the
+// gated and per-channel forms follow from unrolling the recurrence inside a
+// chunk (the pages stop before printing them, sections 08 and 9.1).  For a
+// chunk of C tokens with g_r = sum_{s<=r} ln(alpha_s) (chunk-relative,
+// inclusive; per key channel in KDA, per token otherwise):
+//
+//   A_rj = beta_r sum_c k_rc k_jc e^{g_rc - g_jc}   (j < r)       strictly lower
+//   T    = (I + A)^-1
+//   W    = T diag(beta) (K * e^g),   U = T diag(beta) V
+//   P_rj = sum_c q_rc k_jc e^{g_rc - g_jc}           (j <= r)
+//
+// and the inter-chunk kernel then runs, chunk after chunk,
+//   u = U - W S,  O = (Q * e^g) S + P u,  S <- diag(e^{g_n}) S + (K * e^{g_n-g})^T u.
+//
+// None of this depends on the state, so one workgroup (8 waves) takes one
+// (head, chunk) pair and the whole grid runs at once.  It writes one record
+// per chunk (layout in kda_internal.h) with every operand already in the
+// register order of the inter-chunk kernel's MFMA loops.
+//
+// Phases: G inputs to LDS and decay factors; AP A (fp32) and P on MFMA;
+// T1 diagonal 16x16 blocks of T by forward substitution (one wave per block,
+// pivots broadcast inside lane quads); T2 off-diagonal blocks
+// T_RJ = -T_RR sum_M A_RM T_MJ on fp32 MFMA, level by level; WU W and U on
+// MFMA.
+//
+// Scalar decay (one alpha per token: Gated DeltaNet, or alpha = 1): e^{g_r - g_j}
+// leaves every channel sum, so A and P take the stored inputs as MFMA operands
+// unchanged and the decay is applied to the fp32 results; W takes e^{g_j} on
+// the columns of T diag(beta).
+//
+// Per-channel decay (KDA): e^{g_rc - g_jc} stays inside the sums and is split
+// at the end of r's 16-token sub-block R (cumulative G_{R+1}): the row operand
+// carries e^{g_r - G_{R+1}} (>= 1, at most e^{16 |ln alpha|}), the column
+// operand e^{G_{J+1} - g_j} (<= 1) and, for J < R, a per-channel pair scale
+// e^{G_{R+1} - G_{J+1}} (<= 1).  A diagonal pair therefore uses both stored
+// operands unscaled.  The bound on the row factor is why the KDA path asks for
+// ln(alpha) >= -5 per token and channel.
+#include "kda_device.h"
+#include "kda_internal.h"
+
+namespace kda {
+
+template <int DK_, int DV_, int C_, typename E_, int AMODE_>
+struct IntraCfg {
+    typedef E_ E;
+    static constexpr int DK = DK_, DV = DV_, C = C_, AMODE = AMODE_;
+    static constexpr bool KDA = AMODE == KDA_ALPHA_CHANNEL;   // per-channel decay
+    static constexpr bool HEADG = AMODE == KDA_ALPHA_HEAD;    // one decay per token
+    static constexpr int NB = C / 16;                         // 16-token sub-blocks
+    static constexpr int NPAIR = NB * (NB + 1) / 2;           // (R, J <= R) block pairs
+    static constexpr int ESZ = sizeof(E);
+    // Row pitches: operand tiles are read 16 bytes per lane as (row l%16,
+    // 16-byte column l/16); on gfx950 those reads are free of bank conflicts
+    // when the pitch is 32 (mod 64) bytes, so rows carry 32 bytes of padding.
+    static constexpr int PADE = 32 / ESZ;
+    static constexpr int PK = DK + PADE;                      // [C][DK] tiles
+    static constexpr int PVV = DV + PADE;                     // [C][DV] tile
+    static constexpr int PC = C + PADE;                       // [C][C] operand tiles
+    static constexpr int PA = C + 4;                          // fp32 A / T^T tile
+    static constexpr int NCB = DK / 16, NVB = DV / 16;
+    static constexpr int NW = 8;
+    static constexpr int NT = 64 * NW;
+
+    // LDS: K row operand (KDA: k e^{g - G_{R+1}}, then K e^g in place),
+    // Q row operand (then V), KDA column operand k e^{G_{J+1} - g}, A / T^T
+    // (fp32), T diag(beta), scalar decay: T diag(beta e^g), gate factors, beta.
+    static constexpr int SZ_K = C * PK * ESZ;
+    static constexpr int SZ_QV = (PK > PVV ? PK : PVV) * C * ESZ;
+    static constexpr int O_KR = 0;
+    static constexpr int O_QV = O_KR + SZ_K;
+    static constexpr int O_KC = O_QV + SZ_QV;
+    static constexpr int O_A = O_KC + (KDA ? SZ_K : 0);
+    static constexpr int O_TB = O_A + C * PA * 4;
+    static constexpr int O_TBG = O_TB + C * PC * ESZ;
+    static constexpr int O_GATE = O_TBG + (HEADG ? C * PC * ESZ : 0);
+    // KDA: Z[NB][DK], E'[NB][DK], Y'[NPAIR][DK]; scalar: g[C], e^g[C]
+    static constexpr int SZ_GATE = KDA ? (2 * NB + NPAIR) * DK * 4 : 2 * C * 4;
+    static constexpr int O_BETA = O_GATE + SZ_GATE;
+    static constexpr int LDS_BYTES = O_BETA + C * 4;
+
+    static_assert(DK % 32 == 0 && DV % 16 == 0 && (C == 32 || C == 64), "tile shape");
+    static_assert(!KDA || NB * DK <= NT, "one thread per (channel, sub-block)");
+    static_assert(LDS_BYTES <= 160 * 1024, "LDS budget of one gfx950 CU");
+};
+
+template <class Cfg, bool GBF>
+__global__ void __launch_bounds__(Cfg::NT) kda_intra_kernel(IntraParams prm) {
+    typedef typename Cfg::E E;
+    typedef Frag<E> F;
+    constexpr int DK = Cfg::DK, DV = Cfg::DV, C = Cfg::C, NB = Cfg::NB;
+    constexpr bool KDA = Cfg::KDA, HEADG = Cfg::HEADG;
+    constexpr int PK = Cfg::PK, PVV = Cfg::PVV, PC = Cfg::PC, PA = Cfg::PA;
+    constexpr int NCB = Cfg::NCB, NVB = Cfg::NVB, NW = Cfg::NW, NT = Cfg::NT;
+    constexpr int ESZ = Cfg::ESZ;
+    constexpr int W = F::W, KS = F::KS;
+    constexpr RecLayout RL = rec_layout(DK, DV, C, ESZ, KDA);
+
+    __shared__ __attribute__((aligned(16))) char smem[Cfg::LDS_BYTES];
+    E* sKr = (E*)(smem + Cfg::O_KR);
+    E* sQr = (E*)(smem + Cfg::O_QV);
+    E* sV = (E*)(smem + Cfg::O_QV);  // V replaces the Q operand once A and P are done
+    E* sKc = (E*)(smem + Cfg::O_KC);
+    float* sA = (float*)(smem + Cfg::O_A);
+    E* sTb = (E*)(smem + Cfg::O_TB);
+    E* sTbg = (E*)(smem + Cfg::O_TBG);
+    float* sGate = (float*)(smem + Cfg::O_GATE);
+    float* sBeta = (float*)(smem + Cfg::O_BETA);
+    float* sZ = sGate;                // KDA views
+    float* sE = sGate + NB * DK;
+    float* sY = sGate + 2 * NB * DK;
+    float* sG = sGate;                // scalar views
+    float* sEg = sGate + C;
+
+    const int tid = threadIdx.x;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int l = tid & 63;
+    const int lr = l & 15, lq = l >> 4;
+
+    const int bh = blockIdx.x / prm.ncs;
+    const int cs = blockIdx.x - bh * prm.ncs;
+    const int64_t L = prm.L;
+    const int64_t t0 = (prm.c0 + cs) * C;
+    const int n = (int)((L - t0) < C ? (L - t0) : C);  // valid tokens, >= 1
+
+    // chunk base pointers (64-bit, uniform); offsets below are 32-bit
+    const char* gq = (const char*)prm.q + ((int64_t)bh * L + t0) * DK * ESZ;
+    const char* gk = (const char*)prm.k + ((int64_t)bh * L + t0) * DK * ESZ;
+    const char* gv = (const char*)prm.v + ((int64_t)bh * L + t0) * DV * ESZ;
+    constexpr int GSZ = GBF ? 2 : 4;
+    const char* gla = (const char*)prm.log_alpha + ((int64_t)bh * L + t0) * (KDA ? DK : 1) * GSZ;
+    const char* gbeta = (const char*)prm.beta + ((int64_t)bh * L + t0) * GSZ;
+    char* rec = (char*)prm.ws + ((int64_t)bh * prm.ncs + cs) * RL.bytes;
+    E* rW = (E*)(rec + RL.w);
+    E* rU = (E*)(rec + RL.ut);
+    E* rP = (E*)(rec + RL.p);
+    E* rKt = (E*)(rec + RL.kt);
+    E* rQt = (E*)(rec + RL.qt);
+    float* rGam = (float*)(rec + RL.gam);
+    float* rRs = (float*)(rec + RL.rs);
+
+    auto bits_f32 = [](uint32_t u, bool half) -> float {
+        return half ? __uint_as_float(u << 16) : __uint_as_float(u);
+    };
+
+    // upper blocks of the T' tiles are read as zeros by the W and U products
+    for (int i = tid; i < C * PC; i += NT) {
+        sTb[i] = from_f32<E>(0.f);
+        if constexpr (HEADG) sTbg[i] = from_f32<E>(0.f);
+    }
+
+    // ---- v: into registers now, into LDS once the Q tile is free ------------
+    constexpr int VPIECE = 16 / ESZ;
+    constexpr int VPPR = DV / VPIECE;
+    constexpr int VPT = (C * VPPR + NT - 1) / NT;
+    uint4 rv[VPT];
+#pragma unroll
+    for (int i = 0; i < VPT; ++i) {
+        int idx = tid + NT * i;
+        idx = idx < C * VPPR ? idx : C * VPPR - 1;
+        const int r = idx / VPPR, cc = (idx % VPPR) * VPIECE;
+        const int rr = r < n ? r : n - 1;
+        rv[i] = ldg<uint4>(gv, (rr * DV + cc) * ESZ);
+    }
+
+    // ================= G: inputs into LDS, decay factors =====================
+    const int kc = tid % DK, kR = tid / DK;  // KDA: (key channel, sub-block)
+    const bool kact = KDA && kR < NB;
+    float ky[KDA ? 16 : 1];                  // KDA: k * y, kept for K^
+    if constexpr (KDA) {
+        if (kact) {
+            const int R = kR;
+            float a[16], qv[16], kv[16];
+#pragma unroll
+            for (int s = 0; s < 16; ++s) {
+                const int r = 16 * R + s;
+                const int rr = r < n ? r : n - 1;
+                const uint32_t el = rr * DK + kc;
+                float qq, kk2, la;
+                if constexpr (ESZ == 2) {
+                    qq = bits_f32(ldg<uint16_t>(gq, el * 2), true);
+                    kk2 = bits_f32(ldg<uint16_t>(gk, el * 2), true);
+                } else {
+                    qq = ldg<float>(gq, el * 4);
+                    kk2 = ldg<float>(gk, el * 4);
+                }
+                if constexpr (GBF) la = bits_f32(ldg<uint16_t>(gla, el * 2), true);
+                else la = ldg<float>(gla, el * 4);
+                const bool valid = r < n;
+                qv[s] = valid ? qq : 0.f;
+                kv[s] = valid ? kk2 : 0.f;
+                a[s] = valid ? la : 0.f;
+            }
+            // alpha = exp(ln alpha); x_s = prod_{s'<=s} alpha (within block)
+            float x[16];
+            float run = 1.f;
+#pragma unroll
+            for (int s = 0; s < 16; ++s) {
+                a[s] = exp_neg(a[s]);
+                run *= a[s];
+                x[s] = run;
+            }
+            // y_s = prod_{s' > s} alpha = e^{G_{R+1} - g_s} (<= 1)
+            float yrun = 1.f;
+#pragma unroll
+            for (int s = 15; s >= 0; --s) {
+                ky[s] = kv[s] * yrun;
+                yrun *= a[s];
+            }
+            // x'_s = x_s / Z_R = e^{g_s - G_{R+1}} (>= 1)
+            const float rz = 1.f / x[15];
+#pragma unroll
+            for (int s = 0; s < 16; ++s) {
+                const int r = 16 * R + s;
+                const float xp = x[s] * rz;
+                sKr[r * PK + kc] = from_f32<E>(kv[s] * xp);
+                sQr[r * PK + kc] = from_f32<E>(qv[s] * xp);
+                sKc[r * PK + kc] = from_f32<E>(ky[s]);
+            }
+            sZ[R * DK + kc] = x[15];
+        }
+    } else {
+        constexpr int PPR = DK / VPIECE;          // 16-byte pieces per q/k row
+        constexpr int QPT = (C * PPR + NT - 1) / NT;
+#pragma unroll
+        for (int i = 0; i < QPT; ++i) {
+            const int idx = tid + NT * i;
+            if (idx < C * PPR) {
+                const int r0 = idx / PPR, cc = (idx % PPR) * VPIECE;
+                const int r = r0 < n ? r0 : n - 1;
+                const uint4 a = ldg<uint4>(gq, (r * DK + cc) * ESZ);
+                const uint4 b = ldg<uint4>(gk, (r * DK + cc) * ESZ);
+                *(uint4*)(sQr + r0 * PK + cc) = keep_or_zero(a, r0 < n);
+                *(uint4*)(sKr + r0 * PK + cc) = keep_or_zero(b, r0 < n);
+            }
+        }
+        // g = inclusive prefix sum of ln(alpha) over the chunk (wave 0)
+        if (w == 0) {
+            float g = 0.f;
+            if constexpr (HEADG) {
+                float la = 0.f;
+                if (l < n) la = GBF ? bits_f32(ldg<uint16_t>(gla, l * 2), true) : ldg<float>(gla, l * 4);
+                g = wave_inclusive_sum(la);
+            }
+            const float gn = read_lane(g, C - 1);
+            if (l < C) {
+                const float eg = exp_neg(g);
+                sG[l] = g;
+                sEg[l] = eg;
+                rRs[l] = eg;
+                rRs[C + l] = exp_neg(gn - g);
+            }
+            if (l == 0) rRs[2 * C] = exp_neg(gn);
+        }
+    }
+    if (tid < C) {
+        float b = 0.f;
+        if (tid < n) b = GBF ? bits_f32(ldg<uint16_t>(gbeta, tid * 2), true) : ldg<float>(gbeta, tid * 4);
+        sBeta[tid] = b;
+    }
+    __syncthreads();
+
+    // ================= G2 (KDA): cross-block factors, K^ ======================
+    if constexpr (KDA) {
+        if (kact) {
+            const int R = kR;
+            float Zb[NB];
+#pragma unroll
+            for (int b = 0; b < NB; ++b) Zb[b] = sZ[b * DK + kc];
+            float Fr = 1.f;  // e^{g_n - G_{R+1}} = prod of later blocks
+#pragma unroll
+            for (int b = 0; b < NB; ++b)
+                if (b > R) Fr *= Zb[b];
+            // K^ = k y F = k e^{g_n - g}, written as the A operand of the state
+            // update (rows = key channel, k = token)
+#pragma unroll
+            for (int pc = 0; pc < 16 / W; ++pc) {
+                const int j0 = 16 * R + W * pc;
+                if constexpr (ESZ == 2) {
+                    bf16x8 v;
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) v[e] = (bf16)(ky[W * pc + e] * Fr);
+                    *(bf16x8*)(rKt + frag_elem<E>(kc, j0, C)) = v;
+                } else {
+                    floatx4 v;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) v[e] = ky[W * pc + e] * Fr;
+                    *(floatx4*)(rKt + frag_elem<E>(kc, j0, C)) = v;
+                }
+            }
+            if (R == 0) {
+                // block-end factors E'_R = e^{G_{R+1}}, pair scales
+                // Y'_RJ = e^{G_{R+1} - G_{J+1}} (1 on the diagonal), e^{g_n}
+                float run = 1.f;
+#pragma unroll
+                for (int b = 0; b < NB; ++b) {
+                    run *= Zb[b];
+                    sE[b * DK + kc] = run;
+                }
+                rGam[kc] = run;
+                int p = 0;
+#pragma unroll
+                for (int rb2 = 0; rb2 < NB; ++rb2) {
+#pragma unroll
+                    for (int jb = 0; jb <= rb2; ++jb, ++p) {
+                        float y = 1.f;
+#pragma unroll
+                        for (int m = 0; m < NB; ++m)
+                            if (m > jb && m <= rb2) y *= Zb[m];
+                        sY[p * DK + kc] = y;
+                    }
+                }
+            }
+        }
+        __syncthreads();
+    }
+
+    // ================= AP: A (fp32, LDS) and P (record) ======================
+    for (int p = w; p < Cfg::NPAIR; p += NW) {
+        int R, J;
+        pair_of(p, R, J);
+        constexpr int NKS = DK / KS;
+        const E* pa = (KDA ? sKc : sKr) + (16 * J + lr) * PK + W * lq;
+        const E* pk = sKr + (16 * R + lr) * PK + W * lq;
+        const E* pq = sQr + (16 * R + lr) * PK + W * lq;
+        typename F::T fa[NKS], fk[NKS], fq[NKS];
+        if (!KDA || J == R) {
+#pragma unroll
+            for (int i = 0; i < NKS; ++i) fa[i] = F::load(pa + KS * i);
+        } else {
+            const float* ps = sY + p * DK + W * lq;
+#pragma unroll
+            for (int i = 0; i < NKS; ++i) fa[i] = F::load_scaled(pa + KS * i, ps + KS * i);
+        }
+#pragma unroll
+        for (int i = 0; i < NKS; ++i) {
+            fk[i] = F::load(pk + KS * i);
+            fq[i] = F::load(pq + KS * i);
+        }
+        floatx4 accA = {0.f, 0.f, 0.f, 0.f}, accP = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int i = 0; i < NKS; ++i) {
+            accA = F::mma(accA, fa[i], fk[i]);
+            accP = F::mma(accP, fa[i], fq[i]);
+        }
+        // lane holds [m = j = 16J + 4lq + e][n = r = 16R + lr]
+        const int rr = 16 * R + lr;
+        const float br = sBeta[rr];
+        float gr = 0.f;
+        floatx4 gj = {0.f, 0.f, 0.f, 0.f};
+        if constexpr (HEADG) {
+            gr = sG[rr];
+            gj = *(const floatx4*)(sG + 16 * J + 4 * lq);
+        }
+        floatx4 va, vp;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int jj = 16 * J + 4 * lq + e;
+            float f = 1.f;  // scalar decay e^{g_r - g_j}, applied to the result
+            if constexpr (HEADG) f = exp_neg(gr - gj[e]);
+            va[e] = (J < R || jj < rr) ? br * accA[e] * f : 0.f;
+            vp[e] = (J < R || jj <= rr) ? accP[e] * f : 0.f;
+        }
+        *(floatx4*)(sA + rr * PA + 16 * J + 4 * lq) = va;
+        st4<E>(rP + frag_elem<E>(rr, 16 * J + 4 * lq, C), vp);
+    }
+    // blocks above the diagonal of P are zero
+    for (int b = w; b < NB * NB; b += NW) {
+        const int R = b / NB, J = b % NB;
+        if (J > R) st4<E>(rP + frag_elem<E>(16 * R + lr, 16 * J + 4 * lq, C), floatx4{0.f, 0.f, 0.f, 0.f});
+    }
+    __syncthreads();
+
+    // ================= T1: diagonal blocks by forward substitution ===========
+    // Wave R < NB solves block R.  Lane (j, s) = (l/4, l%4) owns rows
+    // 4s..4s+3 of column j of T_RR, with those rows of A_RR in registers.
+    // Right-looking sweep: once t_m is final, its owner lane hands it to the
+    // other three lanes of the quad (DPP broadcast) and every row takes its
+    // A_RR[i][m] t_m term; the dependent chain is 15 steps long.  (A_RR[i][m]
+    // is zero for m >= i, so no row needs masking.)  Results: T_RR^T (fp32) in
+    // the diagonal block of sA, T_RR diag(beta) in operand precision in sTb
+    // (and T_RR diag(beta e^g) in sTbg).
+    if (w < NB) {
+        const int R = w, j = l >> 2, s4 = l & 3;
+        floatx4 arow[4][4];  // arow[ii][q4] = A_RR[4 s4 + ii][4 q4 .. 4 q4 + 3]
+#pragma unroll
+        for (int ii = 0; ii < 4; ++ii)
+#pragma unroll
+            for (int q4 = 0; q4 < 4; ++q4)
+                arow[ii][q4] = *(const floatx4*)(sA + (16 * R + 4 * s4 + ii) * PA + 16 * R + 4 * q4);
+        float acc[4];
+#pragma unroll
+        for (int ii = 0; ii < 4; ++ii) acc[ii] = (4 * s4 + ii == j) ? 1.f : 0.f;
+#pragma unroll
+        for (int m = 0; m < 15; ++m) {
+            const float tm = quad_bcast(acc[m & 3], m >> 2);
+#pragma unroll
+            for (int ii = 0; ii < 4; ++ii) acc[ii] -= arow[ii][m >> 2][m & 3] * tm;
+        }
+        floatx4 v4 = {acc[0], acc[1], acc[2], acc[3]};
+        *(floatx4*)(sA + (16 * R + j) * PA + 16 * R + 4 * s4) = v4;
+        const float bj = sBeta[16 * R + j];
+        float bgj = 0.f;
+        if constexpr (HEADG) bgj = bj * sEg[16 * R + j];
+#pragma unroll
+        for (int ii = 0; ii < 4; ++ii) {
+            sTb[(16 * R + 4 * s4 + ii) * PC + 16 * R + j] = from_f32<E>(acc[ii] * bj);
+            if constexpr (HEADG) sTbg[(16 * R + 4 * s4 + ii) * PC + 16 * R + j] = from_f32<E>(acc[ii] * bgj);
+        }
+    } else if constexpr (KDA) {
+        // the other waves: K~ = k e^{g} in place (row operand x E'_R) for W,
+        // and Q~ = q e^{g} straight to the record (A operand of Q~ S)
+        constexpr int PER_ROW = DK / VPIECE;
+        for (int i = tid - 64 * NB; i < 2 * C * PER_ROW; i += NT - 64 * NB) {
+            const int which = i / (C * PER_ROW);
+            const int rem = i % (C * PER_ROW);
+            const int r = rem / PER_ROW, cc = (rem % PER_ROW) * VPIECE;
+            const float* sc = sE + (r >> 4) * DK + cc;
+            if (which == 0) {
+                E* p = sKr + r * PK + cc;
+                *(typename F::T*)p = F::load_scaled(p, sc);
+            } else {
+                const E* p = sQr + r * PK + cc;
+                *(typename F::T*)(rQt + frag_elem<E>(r, cc, DK)) = F::load_scaled(p, sc);
+            }
+        }
+    } else {
+        // the other waves: K^T fragments (raw k; the inter-chunk kernel puts
+        // e^{g_n - g} on u) for the state update, and Q fragments (raw q; the
+        // inter-chunk kernel puts e^g on Q S)
+        constexpr int NKT = NCB * (C / KS), NQF = NB * (DK / KS);
+        for (int it = w - NB; it < NKT + NQF; it += NW - NB) {
+            if (it < NKT) {
+                const int cb = it / (C / KS), kk = it % (C / KS);
+                *(typename F::T*)(rKt + ((cb * (C / KS) + kk) * 64 + l) * W) =
+                    load_frag_tr(sKr, PK, kk * KS, 16 * cb);
+            } else {
+                const int f = it - NKT, R = f / (DK / KS), kk = f % (DK / KS);
+                *(typename F::T*)(rQt + (f * 64 + l) * W) =
+                    F::load(sQr + (16 * R + lr) * PK + kk * KS + W * lq);
+            }
+        }
+    }
+    __syncthreads();
+
+    // ================= T2: off-diagonal blocks, by distance ==================
+    // T_RJ = -T_RR sum_{M=J}^{R-1} A_RM T_MJ; T_RJ^T is stored at block (J, R)
+    // of sA, and T_RJ diag(beta) in sTb.  V enters LDS during the first level.
+#pragma unroll
+    for (int d = 1; d < NB; ++d) {
+        if (d == 1) {
+#pragma unroll
+            for (int i = 0; i < VPT; ++i) {
+                const int idx = tid + NT * i;
+                if (idx < C * VPPR) {
+                    const int r = idx / VPPR, cc = (idx % VPPR) * VPIECE;
+                    *(uint4*)(sV + r * PVV + cc) = keep_or_zero(rv[i], r < n);
+                }
+            }
+        }
+        const int R = d + w, J = w;
+        if (R < NB) {
+            floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+            for (int M = J; M < R; ++M) {
+                floatx4 af = *(const floatx4*)(sA + (16 * R + lr) * PA + 16 * M + 4 * lq);
+                floatx4 bfv = *(const floatx4*)(sA + (16 * J + lr) * PA + 16 * M + 4 * lq);
+                acc = Frag<float>::mma(acc, af, bfv);
+            }
+            // A operand T_RR[m][k] with m = lr, k = 4lq + s: stored transposed
+            floatx4 tf;
+#pragma unroll
+            for (int s = 0; s < 4; ++s) tf[s] = sA[(16 * R + 4 * lq + s) * PA + 16 * R + lr];
+            floatx4 z = {0.f, 0.f, 0.f, 0.f};
+            floatx4 res = -Frag<float>::mma(z, tf, acc);
+            *(floatx4*)(sA + (16 * J + lr) * PA + 16 * R + 4 * lq) = res;
+            const float bj = sBeta[16 * J + lr];
+            float bgj = 0.f;
+            if constexpr (HEADG) bgj = bj * sEg[16 * J + lr];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                sTb[(16 * R + 4 * lq + e) * PC + 16 * J + lr] = from_f32<E>(res[e] * bj);
+                if constexpr (HEADG) sTbg[(16 * R + 4 * lq + e) * PC + 16 * J + lr] = from_f32<E>(res[e] * bgj);
+            }
+        }
+        __syncthreads();
+    }
+
+    // ================= WU: W = T' K~ and U = T diag(beta) V ==================
+    // W tile (R, cb) is computed transposed so each lane holds four adjacent
+    // channels of one row; U tile (R, vb) lands directly in accumulator order.
+    const E* sTw = HEADG ? sTbg : sTb;
+    for (int it = w; it < NB * (NCB + NVB); it += NW) {
+        if (it < NB * NCB) {
+            const int R = it % NB, cb = it / NB;
+            const int K = ((16 * (R + 1) + KS - 1) / KS) * KS;
+            floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+            acc = mma_block_at<E>(acc, sKr, PK, 16 * cb, sTw + (16 * R) * PC, PC, K);
+            st4<E>(rW + frag_elem<E>(16 * R + lr, 16 * cb + 4 * lq, DK), acc);
+        } else {
+            const int u = it - NB * NCB;
+            const int R = u % NB, vb = u / NB;
+            const int K = ((16 * (R + 1) + KS - 1) / KS) * KS;
+            floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+            acc = mma_block_bt<E>(acc, sTb + (16 * R) * PC, PC, sV, PVV, 16 * vb, K);
+            constexpr int PF = 16 / (4 * ESZ);  // column blocks per 16-byte lane piece
+            st4<E>(rU + ((R * (NVB / PF) + vb / PF) * 64 + l) * 4 * PF + (vb % PF) * 4, acc);
+        }
+    }
+}
+
+// ---- host-side dispatch -----------------------------------------------------
+
+template <int DK, int DV, int C, typename E, int AMODE>
+static hipError_t launch_intra_cfg(const IntraParams& prm, hipStream_t stream) {
+    typedef IntraCfg<DK, DV, C, E, AMODE> Cfg;
+    const int64_t grid = (int64_t)prm.BH * prm.ncs;
+    if (prm.gate_bf16)
+        hipLaunchKernelGGL((kda_intra_kernel<Cfg, true>), dim3((unsigned)grid), dim3(Cfg::NT), 0,
+                           stream, prm);
+    else
+        hipLaunchKernelGGL((kda_intra_kernel<Cfg, false>), dim3((unsigned)grid), dim3(Cfg::NT), 0,
+                           stream, prm);
+    return hipGetLastError();
+}
+
+template <int DK, int DV, int C, typename E>
+static hipError_t launch_intra_mode(const IntraParams& prm, int alpha_mode, hipStream_t stream) {
+    switch (alpha_mode) {
+        case KDA_ALPHA_NONE: return launch_intra_cfg<DK, DV, C, E, KDA_ALPHA_NONE>(prm, stream);
+        case KDA_ALPHA_HEAD: return launch_intra_cfg<DK, DV, C, E, KDA_ALPHA_HEAD>(prm, stream);
+        case KDA_ALPHA_CHANNEL: return launch_intra_cfg<DK, DV, C, E, KDA_ALPHA_CHANNEL>(prm, stream);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+hipError_t launch_intra(const IntraParams& prm, int dk, int dv, int qkv_bf16, int alpha_mode,
+                        hipStream_t stream) {
+    if (prm.BH == 0 || prm.ncs == 0) return hipSuccess;
+#define KDA_CASE(DK_, DV_)                                                          \
+    if (dk == DK_ && dv == DV_)                                                     \
+        return qkv_bf16 ? launch_intra_mode<DK_, DV_, 64, bf16>(prm, alpha_mode, stream) \
+                        : launch_intra_mode<DK_, DV_, 32, float>(prm, alpha_mode, stream);
+    KDA_CASE(128, 128)
+    KDA_CASE(128, 64)
+    KDA_CASE(64, 128)
+    KDA_CASE(64, 64)
+#undef KDA_CASE
+    return hipErrorInvalidValue;
+}
+
+}  // namespace kda

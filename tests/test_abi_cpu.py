@@ -43,14 +43,14 @@ def shape(B=2, H=3, L=100, dk=128, dv=128, qd=binding.KDA_BF16, gd=binding.KDA_F
 
 
 def bufs():
-    """Disjoint fake buffers, 64 MiB apart."""
-    names = ["q", "k", "v", "la", "beta", "S0", "o", "Sf"]
+    """Disjoint fake buffers, 64 MiB apart (the workspace last, 1 GiB)."""
+    names = ["q", "k", "v", "la", "beta", "S0", "o", "Sf", "ws"]
     return {n: BASE + i * 64 * MB for i, n in enumerate(names)}
 
 
-def chunk(lib, s, b, ws=None, wsb=0):
+def chunk(lib, s, b, wsb=1 << 30):
     return lib.kda_chunk_fwd(ctypes.byref(s) if s is not None else None, b["q"], b["k"], b["v"],
-                             b["la"], b["beta"], b["S0"], b["o"], b["Sf"], ws, wsb, None)
+                             b["la"], b["beta"], b["S0"], b["o"], b["Sf"], b["ws"], wsb, None)
 
 
 def decode(lib, s, b):
@@ -59,8 +59,38 @@ def decode(lib, s, b):
 
 
 def test_workspace_query(lib):
-    assert lib.kda_chunk_fwd_workspace_bytes(ctypes.byref(shape())) == 0
+    # one record per (head, chunk) of a span of chunks, plus a state area when
+    # the sequence runs as several spans
+    s = shape(B=2, H=3, L=100)
+    ws = lib.kda_chunk_fwd_workspace_bytes(ctypes.byref(s))
+    assert ws > 0 and ws % 256 == 0
+    assert lib.kda_chunk_fwd_workspace_bytes(ctypes.byref(shape(L=10 ** 6))) <= (96 << 20) + 6 * 128 * 128 * 4
+    assert lib.kda_chunk_fwd_workspace_bytes(ctypes.byref(shape(B=0))) == 0
+    assert lib.kda_chunk_fwd_workspace_bytes(ctypes.byref(shape(L=0))) == 0
     assert lib.kda_chunk_fwd_workspace_bytes(None) == 0
+    bad = shape()
+    bad.dk = 96
+    assert lib.kda_chunk_fwd_workspace_bytes(ctypes.byref(bad)) == 0
+
+
+def test_workspace_too_small(lib):
+    s = shape()
+    ws = lib.kda_chunk_fwd_workspace_bytes(ctypes.byref(s))
+    assert chunk(lib, s, bufs(), wsb=ws - 1) == 6  # KDA_ERR_WORKSPACE
+    b = bufs()
+    b["ws"] = None
+    assert chunk(lib, s, b) == 6
+
+
+def test_workspace_overlap(lib):
+    b = bufs()
+    b["ws"] = b["v"] + 4096
+    assert chunk(lib, shape(), b) == 7
+
+
+def test_long_sequence_rejected(lib):
+    # one head's [L, d] tensors must stay addressable with 32-bit byte offsets
+    assert chunk(lib, shape(B=1, H=1, L=1 << 23), bufs()) == 2
 
 
 def test_null_shape(lib):
