@@ -74,7 +74,10 @@ int check_shape(const kda_shape* s, bool decode) {
 // the target size, within the 256 MiB memory-side cache of an MI355X).  Between
 // spans the state goes through S_final, or through the workspace's state area
 // when no final state is wanted.
-constexpr int64_t kSpanTargetBytes = 96ll << 20;
+#ifndef KDA_SPAN_TARGET_BYTES
+#define KDA_SPAN_TARGET_BYTES (96ll << 20)
+#endif
+constexpr int64_t kSpanTargetBytes = KDA_SPAN_TARGET_BYTES;
 
 struct Plan {
     int C = 0;
@@ -90,9 +93,9 @@ Plan make_plan(const kda_shape* s) {
     p.C = kda::chunk_len(bf);
     p.nchunks = (s->L + p.C - 1) / p.C;
     if (bh == 0 || p.nchunks == 0) return p;
-    p.rec_bytes = kda::rec_layout((int)s->dk, (int)s->dv, p.C, bf ? 2 : 4,
-                                  s->alpha_mode == KDA_ALPHA_CHANNEL)
-                      .bytes;
+    p.rec_bytes = s->alpha_mode == KDA_ALPHA_CHANNEL
+                      ? kda::rec_layout((int)s->dk, (int)s->dv, p.C, bf ? 2 : 4, true).bytes
+                      : kda::rec_layout_thin(p.C, bf ? 2 : 4).bytes;
     int64_t per_chunk = bh * p.rec_bytes;
     p.span = kSpanTargetBytes / per_chunk;
     if (p.span < 1) p.span = 1;
@@ -187,6 +190,9 @@ int kda_chunk_fwd(const kda_shape* s, const void* q, const void* k, const void* 
     ip.BH = (int)bh;
     ip.gate_bf16 = s->gate_dtype == KDA_BF16;
     kda::InterParams xp;
+    xp.q = q;
+    xp.k = k;
+    xp.v = v;
     xp.ws = workspace;
     xp.o = o;
     xp.L = s->L;
@@ -194,6 +200,13 @@ int kda_chunk_fwd(const kda_shape* s, const void* q, const void* k, const void* 
     xp.DV = (int)s->dv;
     xp.n_slices = 0;
 
+    // per-channel decay: records hold every operand (inter-chunk kernel);
+    // one decay per token: records hold T diag(beta) and the decay scalars
+    auto launch_state = [&](const kda::InterParams& x) {
+        return s->alpha_mode == KDA_ALPHA_CHANNEL
+                   ? kda::launch_inter(x, (int)s->dk, qbf, s->alpha_mode, nv, stream)
+                   : kda::launch_inter_scalar(x, (int)s->dk, qbf, nv, stream);
+    };
     hipError_t err = hipSuccess;
     if (plan.nchunks == 0) {
         // L == 0: the final state is the initial one
@@ -201,7 +214,7 @@ int kda_chunk_fwd(const kda_shape* s, const void* q, const void* k, const void* 
         xp.S_out = S_final;
         xp.c0 = 0;
         xp.ncs = 0;
-        err = kda::launch_inter(xp, (int)s->dk, qbf, s->alpha_mode, nv, stream);
+        err = launch_state(xp);
     }
     for (int64_t sp = 0; sp < plan.nspans && err == hipSuccess; ++sp) {
         const int64_t c0 = sp * plan.span;
@@ -214,7 +227,7 @@ int kda_chunk_fwd(const kda_shape* s, const void* q, const void* k, const void* 
         xp.S_out = sp == plan.nspans - 1 ? S_final : s_mid;
         xp.c0 = c0;
         xp.ncs = (int)ncs;
-        err = kda::launch_inter(xp, (int)s->dk, qbf, s->alpha_mode, nv, stream);
+        err = launch_state(xp);
     }
     if (err != hipSuccess) {
         g_last_error = std::string("kda_chunk_fwd: ") + hipGetErrorString(err);

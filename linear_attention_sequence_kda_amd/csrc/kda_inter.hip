@@ -12,24 +12,27 @@
 // (section 08 and 9.1 for the decay; with one decay per token the e^g factors
 // are scalars per row, applied to Q S and to u, and K is the stored input).
 //
-// One workgroup (8 waves) owns one (b, h) head and a slice of NV state
-// columns (columns of S evolve independently, so slices never talk) and walks
-// the chunks in order.  Its fp32 state slice lives in registers as 16x16
-// blocks spread over the waves, with a transposed operand copy in LDS.  Every
-// other operand comes straight from HBM into registers in MFMA order (the
-// records are laid out for exactly these loads), one chunk ahead: a chunk
-// costs two barriers.
+// One workgroup owns one (b, h) head and a slice of NV state columns
+// (columns of S evolve independently, so slices never talk) and walks the
+// chunks in order.  Its fp32 state slice lives in registers as 16x16 blocks
+// spread over eight compute waves, with a transposed operand copy in LDS.
+//
+// Eight more waves only move data.  They keep two chunks' records in flight
+// in registers (a chunk's loads cost about one and a half microseconds of
+// latency, several chunks' worth of compute) and write each into one half of
+// a two-slot LDS ring one chunk ahead of use (the record is stored in 1 KiB
+// wave pieces in exactly the order the compute waves read their MFMA
+// fragments, so each piece is one load and one LDS write), and they write the
+// previous chunk's o tile to HBM.  The compute waves never issue a global
+// memory instruction inside the loop.  Per chunk:
 //   phase A  u tiles: u = U - W S        (then u, and e^{g_n-g} u, to LDS)
 //            o tiles: o = (Q S) e^g      (kept in registers)
 //   phase B  S tiles: S = e^{g_n} S + K^T u  (new operand copy to LDS)
 //            o tiles: o += P u, to an LDS tile
-// and the o tile goes to HBM at the start of the next chunk, through a buffer
-// resource bounded by the sequence end (the ragged last chunk needs no
-// branch).  o tiles are computed transposed (lane = one token, four adjacent
-// columns).  On gfx9 loads and stores share one wait counter, so the loop is
-// ordered to never wait on a store it has just issued.
-#include <type_traits>
-
+// with one barrier after each phase; the data waves wait for their copies
+// between the two barriers.  o tiles are computed transposed (lane = one
+// token, four adjacent columns); the o store goes through a buffer resource
+// bounded by the sequence end, so the ragged last chunk needs no branch.
 #include "kda_device.h"
 #include "kda_internal.h"
 
@@ -42,30 +45,48 @@ struct InterCfg {
     static constexpr bool KDA = KDA_;
     static constexpr int NB = C / 16, NCB = DK / 16, NVB = NV / 16;
     static constexpr int ESZ = sizeof(E);
+    static constexpr int KS = 64 / ESZ;    // MFMA k step (16-byte lane pieces x 4)
+    static constexpr int NKA = DK / KS, NKP = C / KS;
     static constexpr int PADE = 32 / ESZ;
     static constexpr int PK = DK + PADE;   // S^T operand copy [NV][DK]
     static constexpr int PC = C + PADE;    // u^T [NV][C]
-    static constexpr int NW = 8, NT = 64 * NW;
+    static constexpr int PO = NV + PADE;   // o tile [C][NV]
+    static constexpr int NWC = 8;          // compute waves
+    static constexpr int NWP = 8;          // data waves (hold two chunks in flight)
+    static constexpr int NT = 64 * (NWC + NWP);
     // Phase-A items: (role, R, column group) with role u (u = U - W S) or o
     // (o = Q S ...), R a 16-token block, and the NVB column blocks of the
-    // slice split into NG groups of VG blocks, so one wave loads a W or Q row
+    // slice split into NG groups of VG blocks, so one wave reads a W or Q row
     // block once and uses it for every column block of its group.
-    static constexpr int NG = (2 * NB >= NW || NVB == 1) ? 1 : (NW / (2 * NB) < NVB ? NW / (2 * NB) : NVB);
+    static constexpr int NG = (2 * NB >= NWC || NVB == 1) ? 1 : (NWC / (2 * NB) < NVB ? NWC / (2 * NB) : NVB);
     static constexpr int VG = NVB / NG;
     static constexpr int NIA = 2 * NB * NG;
     // State items: (cb, column group): K^T row block cb for SG column blocks.
-    static constexpr int NGS = (NCB >= NW || NVB == 1) ? 1 : (NW / NCB < NVB ? NW / NCB : NVB);
+    static constexpr int NGS = (NCB >= NWC || NVB == 1) ? 1 : (NWC / NCB < NVB ? NWC / NCB : NVB);
     static constexpr int SG = NVB / NGS;
     static constexpr int NIS = NCB * NGS;
-    static_assert(NIA <= NW && NIS <= NW, "one phase-A item and one state item per wave");
+    static_assert(NIA <= NWC && NIS <= NWC, "one phase-A item and one state item per wave");
     static_assert(VG * NG == NVB && SG * NGS == NVB, "column groups");
-    static constexpr int O_ST = 0;
+    // ring slot: 1 KiB pieces W [NB][NKA], Q [NB][NKA], P [NB][NKP],
+    // K^T [NCB][NKP], U [NB][NUP], decay scalars
+    static constexpr int PF = 16 / (4 * ESZ);            // U blocks per lane piece
+    static constexpr int NUP = (NVB + PF - 1) / PF;      // U pieces per R in a slice
+    static constexpr int P_W = 0, P_Q = P_W + NB * NKA, P_P = P_Q + NB * NKA;
+    static constexpr int P_KT = P_P + NB * NKP, P_U = P_KT + NCB * NKP;
+    static constexpr int P_SC = P_U + NB * NUP;          // decay scalars (gam | rs)
+    static constexpr int NPIECE = P_SC + 1;
+    static constexpr int O_SC = P_SC * 1024;
+    static constexpr int SLOT = NPIECE * 1024;
+    // LDS: ring, a 1 KiB sink for the data waves' padding pieces, ...
+    static constexpr int O_RING = 0;
+    static constexpr int O_SINK = O_RING + 2 * SLOT;
+    static constexpr int O_ST = O_SINK + 1024;
     static constexpr int O_UT = O_ST + NV * PK * ESZ;
     static constexpr int O_UHT = O_UT + NV * PC * ESZ;
-    static constexpr int PO = NV + PADE;   // o tile [C][NV]
     static constexpr int O_O = O_UHT + (KDA ? 0 : NV * PC * ESZ);
     static constexpr int LDS_BYTES = O_O + C * PO * ESZ;
     static_assert(DK % 32 == 0 && NV % 16 == 0 && (C == 32 || C == 64), "tile shape");
+    static_assert(LDS_BYTES <= 160 * 1024, "LDS budget of one gfx950 CU");
 };
 
 template <class Cfg>
@@ -75,19 +96,20 @@ __global__ void __launch_bounds__(Cfg::NT) kda_inter_kernel(InterParams prm) {
     typedef typename F::T FT;
     constexpr int DK = Cfg::DK, NV = Cfg::NV, C = Cfg::C, NB = Cfg::NB;
     constexpr bool KDA = Cfg::KDA;
-    constexpr int PK = Cfg::PK, PC = Cfg::PC, NCB = Cfg::NCB, NVB = Cfg::NVB;
-    constexpr int NW = Cfg::NW, NG = Cfg::NG, VG = Cfg::VG, NIA = Cfg::NIA;
+    constexpr int PK = Cfg::PK, PC = Cfg::PC, PO = Cfg::PO, NCB = Cfg::NCB, NVB = Cfg::NVB;
+    constexpr int NWC = Cfg::NWC, NWP = Cfg::NWP, NG = Cfg::NG, VG = Cfg::VG, NIA = Cfg::NIA;
     constexpr int NGS = Cfg::NGS, SG = Cfg::SG, NIS = Cfg::NIS;
     constexpr int ESZ = Cfg::ESZ, W = F::W, KS = F::KS;
-    constexpr int NKA = DK / KS;  // k steps over key channels
-    constexpr int NKP = C / KS;   // k steps over the chunk's tokens
+    constexpr int NKA = Cfg::NKA, NKP = Cfg::NKP, PF = Cfg::PF, NUP = Cfg::NUP;
+    constexpr int SLOT = Cfg::SLOT, O_SC = Cfg::O_SC;
+    static_assert(KS == Cfg::KS, "k step");
 
     __shared__ __attribute__((aligned(16))) char smem[Cfg::LDS_BYTES];
+    char* ring = smem + Cfg::O_RING;
     E* sST = (E*)(smem + Cfg::O_ST);
     E* sUT = (E*)(smem + Cfg::O_UT);
     E* sUHT = (E*)(smem + Cfg::O_UHT);
     E* sO = (E*)(smem + Cfg::O_O);
-    constexpr int PO = Cfg::PO;
 
     const int tid = threadIdx.x;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -96,7 +118,7 @@ __global__ void __launch_bounds__(Cfg::NT) kda_inter_kernel(InterParams prm) {
 
     // ---- which (head, column slice) this workgroup owns --------------------
     // Dispatch places workgroup i on XCD i % 8; give all slices of a head the
-    // same XCD so their shared operand reads hit one L2.
+    // same XCD so their shared record reads hit one L2.
     const int total = prm.BH * prm.n_slices;
     int pidx = blockIdx.x;
     if ((total & 7) == 0) pidx = (blockIdx.x & 7) * (total >> 3) + (blockIdx.x >> 3);
@@ -106,16 +128,142 @@ __global__ void __launch_bounds__(Cfg::NT) kda_inter_kernel(InterParams prm) {
     const int64_t L = prm.L;
     const int DV = prm.DV;
     const RecLayout rl = rec_layout(DK, DV, C, ESZ, KDA);
-
     const char* recs = (const char*)prm.ws + (int64_t)bh * prm.ncs * rl.bytes;
-    // o of this head as a buffer: stores past token L are dropped
-    const __amdgpu_buffer_rsrc_t orsrc =
-        make_rsrc((const char*)prm.o + (int64_t)bh * L * DV * ESZ, (uint32_t)(L * DV * ESZ));
+    const int ncs = prm.ncs;
 
-    // ---- this wave's items -----------------------------------------------------
+    if (w >= NWC) {
+        // ======================= data waves ==================================
+        // Chunk x travels HBM -> registers (set x % 2) -> LDS slot x % 2.
+        // In iteration c a data wave: waits for chunk c+1's loads, writes
+        // them to slot (c+1) % 2 (free since the compute waves left it at the
+        // end of chunk c-1), loads chunk c+3 into the set just emptied and
+        // stores o of chunk c-1.  Every iteration issues the same NL loads
+        // and NS stores per wave (past the last chunk it re-reads the last
+        // record, and missing o pieces go past the buffer end), so the wait
+        // for chunk c+1 is exactly "all but the last NL + 2 NS operations".
+        constexpr int NL = (Cfg::NPIECE + NWP - 1) / NWP;  // 1 KiB pieces per wave
+        constexpr int PPR = NV * ESZ / 16, NPC = C * PPR;   // o pieces per chunk
+        constexpr int NS = (NPC + 64 * NWP - 1) / (64 * NWP);
+        static_assert(NL + 2 * NS <= 63, "vmcnt range");
+        const int pw = w - NWC;
+        const __amdgpu_buffer_rsrc_t orsrc =
+            make_rsrc((const char*)prm.o + (int64_t)bh * L * DV * ESZ, (uint32_t)(L * DV * ESZ));
+        const int gp0 = (slice * NVB) / PF;  // first U piece column of the slice
+        // record and ring offsets of this wave's j-th piece (wave-uniform;
+        // pieces past the list re-read a valid piece and land in the sink)
+        uint32_t pg[NL], pl[NL];
+#pragma unroll
+        for (int j = 0; j < NL; ++j) {
+            const int i0 = pw + NWP * j;
+            const int i = i0 < Cfg::NPIECE ? i0 : pw;
+            uint32_t g;
+            if (i < Cfg::P_Q) g = rl.w + (i - Cfg::P_W) * 1024;
+            else if (i < Cfg::P_P) g = rl.qt + (i - Cfg::P_Q) * 1024;
+            else if (i < Cfg::P_KT) g = rl.p + (i - Cfg::P_P) * 1024;
+            else if (i < Cfg::P_U) g = rl.kt + (i - Cfg::P_KT) * 1024;
+            else if (i < Cfg::P_SC) {
+                const int u = i - Cfg::P_U, R = u / NUP, jj = u % NUP;
+                g = rl.ut + (R * (DV / (16 * PF)) + gp0 + jj) * 1024;
+            } else {
+                g = KDA ? rl.gam : rl.rs;
+            }
+            pg[j] = __builtin_amdgcn_readfirstlane(g);
+            pl[j] = __builtin_amdgcn_readfirstlane(i0 < Cfg::NPIECE ? i0 * 1024 : -1);
+        }
+        const uint32_t l16 = l * 16;
+        typedef int v4i __attribute__((ext_vector_type(4)));
+        struct DSet {
+            v4i v[NL];
+        };
+        // Loads through a buffer resource over the record (the only vector
+        // register involved is the lane offset).  They are issued as inline
+        // assembly, which the compiler's wait insertion does not track: it
+        // would otherwise merge the two sets' loads across the loop and wait
+        // for the newest ones; the waits below are exact instead.
+        auto fetch = [&](DSet& st, int cs) {
+            cs = cs < ncs ? cs : ncs - 1;
+            const uint64_t base = (uint64_t)(recs + (int64_t)cs * rl.bytes);
+            const v4i rr = {(int)(uint32_t)base, (int)((uint32_t)(base >> 32) & 0xffffu), (int)rl.bytes,
+                            0x00020000};
+#pragma unroll
+            for (int j = 0; j < NL; ++j)
+                asm volatile("buffer_load_dwordx4 %0, %1, %2, %3 offen"
+                             : "=v"(st.v[j])
+                             : "v"(l16), "s"(rr), "s"(pg[j])
+                             : "memory");
+        };
+        auto put = [&](const DSet& st, int cs) {
+            char* slot = ring + (cs & 1) * SLOT;
+            char* sink = smem + Cfg::O_SINK;
+#pragma unroll
+            for (int j = 0; j < NL; ++j) *(v4i*)((pl[j] == 0xffffffffu ? sink : slot + pl[j]) + l16) = st.v[j];
+        };
+        // o tile of chunk cs (cs < 0: every store falls past the buffer end)
+        auto store_o = [&](int cs) {
+            const int64_t t0 = (prm.c0 + cs) * C;
+#pragma unroll
+            for (int k = 0; k < NS; ++k) {
+                const int i = (tid - 64 * NWC) + 64 * NWP * k;
+                const int ic = i < NPC ? i : 0;
+                const int r = ic / PPR, cc = (ic % PPR) * (16 / ESZ);
+                const uint4 val = *(const uint4*)(sO + r * PO + cc);
+                const uint32_t off = (cs >= 0 && i < NPC) ? (uint32_t)(((t0 + r) * DV + v0 + cc) * ESZ)
+                                                          : 0xfffffff0u;
+                typedef int v4i __attribute__((ext_vector_type(4)));
+                __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(v4i, val), orsrc, (int)off, 0, 0);
+            }
+        };
+        // These waves meet the compute waves' barriers with a bare s_barrier:
+        // a full __syncthreads would also wait for the loads in flight.  The
+        // empty asm statements keep the compiler from moving LDS accesses
+        // across the barriers.
+        auto bare_barrier = []() {
+            asm volatile("" ::: "memory");
+            __builtin_amdgcn_s_barrier();
+            asm volatile("" ::: "memory");
+        };
+        // wait for all but the last NL + 2 NS vector memory operations
+        auto wait_next = []() {
+            constexpr int n = NL + 2 * NS;
+            asm volatile("s_waitcnt vmcnt(%0)" ::"n"(n) : "memory");
+        };
+        // chunk x: loads issued in iteration x-3 into set x % 2, written to
+        // its slot in iteration x-1, used by the compute waves in iteration x
+        DSet s0, s1;
+        if (ncs > 0) {
+            fetch(s0, 0);
+            store_o(-1);
+            fetch(s1, 1);
+            store_o(-1);
+            wait_next();  // chunk 0 is in
+            put(s0, 0);
+            fetch(s0, 2);
+            store_o(-1);
+        }
+        __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0)
+        bare_barrier();
+        // iteration cs: chunk cs+1 is in `nx`, which then takes chunk cs+3
+        auto iteration = [&](DSet& nx, int cs) {
+            wait_next();
+            put(nx, cs + 1);
+            fetch(nx, cs + 3);
+            store_o(cs - 1);
+            __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): slot writes, o reads done
+            bare_barrier();                      // A
+            bare_barrier();                      // B
+        };
+        for (int cs = 0; cs < ncs; cs += 2) {
+            iteration(s1, cs);
+            if (cs + 1 >= ncs) break;
+            iteration(s0, cs + 1);
+        }
+        if (ncs > 0) store_o(ncs - 1);
+        return;
+    }
+
+    // ========================= compute waves =====================================
     // phase A: item w < NIA is (role, R, group): role u for w < NB*NG, else o.
-    // state: item w < NIS is (cb, group).  Waves without an item load the
-    // first item's operands (valid addresses) and skip the arithmetic.
+    // state: item w < NIS is (cb, group).
     const bool aval = w < NIA;
     const int ai = aval ? w : 0;
     const bool isU = ai < NB * NG;
@@ -125,66 +273,6 @@ __global__ void __launch_bounds__(Cfg::NT) kda_inter_kernel(InterParams prm) {
     const int si = sval ? w : 0;
     const int scb = si / NGS;
     const int svb0 = (si % NGS) * SG;
-
-    // ---- one chunk's operands, in registers ---------------------------------
-    // The u and o roles share register slots: b[] holds P rows for an o wave,
-    // U blocks (and e^{g_n-g}) for a u wave.  Both roles issue the same
-    // loads from role-dependent addresses (a role with fewer slots re-reads a
-    // valid one), so the instruction stream is one straight line.
-    constexpr int PF = 16 / (4 * ESZ);                 // U blocks per 16-byte lane piece
-    constexpr int UP = (VG + PF - 1) / PF;             // slots holding U
-    constexpr int RU = KDA ? 0 : 1;                    // slot holding e^{g_n - g}
-    constexpr int NBS = (NKP > UP + RU) ? NKP : UP + RU;
-    struct Set {
-        FT a[NKA];       // u role: W rows aR; o role: Q rows aR
-        uint4 b[NBS];    // o role: P rows aR; u role: U blocks, then e^{g_n - g}
-        float rq;        // scalar decay: e^{g_r} of row 16aR + lr (o role)
-        FT kt[NKP];      // K^T rows of block scb
-        floatx4 gm;      // KDA: e^{g_n} of rows 16scb + 4lq + e
-        float gn;        // scalar decay: e^{g_n}
-    };
-    const int gvb0 = slice * NVB + avb0;               // first global column block
-    const int uhalf = gvb0 % PF;                       // bf16, VG = 1: half of the piece
-    // Loads only (no arithmetic on the loaded values, so nothing waits for
-    // them here); the last chunk's record is re-read past the end.
-    auto load = [&](Set& s, int cs) {
-        cs = cs < prm.ncs ? cs : prm.ncs - 1;
-        const char* rec = recs + (int64_t)cs * rl.bytes;
-        const int R = aR;
-        const char* ab = rec + (isU ? rl.w : rl.qt);
-#pragma unroll
-        for (int kk = 0; kk < NKA; ++kk) s.a[kk] = ldg<FT>(ab, ((R * NKA + kk) * 64 + l) * 16);
-#pragma unroll
-        for (int j = 0; j < NBS; ++j) {
-            const int jp = j < NKP ? j : NKP - 1;
-            const int ju = j < UP ? j : 0;
-            const uint32_t uoff = ((R * (DV / (16 * PF)) + gvb0 / PF + ju) * 64 + l) * 16;
-            const uint32_t roff = (C + 16 * R + 4 * lq) * 4;
-            const char* bb = isU ? rec + ((RU && j == UP) ? rl.rs : rl.ut) : rec + rl.p;
-            const uint32_t bo = isU ? ((RU && j == UP) ? roff : uoff)
-                                    : (uint32_t)(((R * NKP + jp) * 64 + l) * 16);
-            s.b[j] = ldg<uint4>(bb, bo);
-        }
-        if constexpr (!KDA) s.rq = ldg<float>(rec + rl.rs, (16 * R + lr) * 4);
-#pragma unroll
-        for (int kk = 0; kk < NKP; ++kk) s.kt[kk] = ldg<FT>(rec + rl.kt, ((scb * NKP + kk) * 64 + l) * 16);
-        if constexpr (KDA) s.gm = ldg<floatx4>(rec + rl.gam, (16 * scb + 4 * lq) * 4);
-        else s.gn = ldg<float>(rec + rl.rs, 2 * C * 4);
-    };
-    // U block g of a u wave, as fp32
-    auto ut_f32 = [&](const Set& s, int g) -> floatx4 {
-        if constexpr (ESZ == 2) {
-            const int h = VG == 1 ? uhalf : g % 2;
-            const uint4 q4 = s.b[VG == 1 ? 0 : g / 2];
-            const uint32_t x = h == 0 ? q4.x : q4.z, y = h == 0 ? q4.y : q4.w;
-            return floatx4{__uint_as_float(x << 16), __uint_as_float(x & 0xffff0000u),
-                           __uint_as_float(y << 16), __uint_as_float(y & 0xffff0000u)};
-        } else {
-            const uint4 u = s.b[g];
-            return floatx4{__uint_as_float(u.x), __uint_as_float(u.y), __uint_as_float(u.z),
-                           __uint_as_float(u.w)};
-        }
-    };
 
     // ---- initial state slice --------------------------------------------------
     // Lane element e of state block g is S[16scb + 4lq + e][v0 + 16(svb0 + g) + lr].
@@ -206,36 +294,59 @@ __global__ void __launch_bounds__(Cfg::NT) kda_inter_kernel(InterParams prm) {
     }
     __syncthreads();
 
+    auto piece = [&](const char* slot, int i) -> FT { return *(const FT*)(slot + i * 1024 + l * 16); };
     floatx4 oacc[VG];
-    auto step = [&](const Set& s) {
+    for (int cs = 0; cs < ncs; ++cs) {
+        const char* slot = ring + (cs & 1) * SLOT;
+        const float* sc = (const float*)(slot + O_SC);
         // ---------------- phase A ----------------
         if (aval) {
             const int R = aR;
             if (isU) {
                 // u[16R + 4lq + e][16vb + lr] = U - sum_c W[r][c] S[c][v]
+                FT wf[NKA];
+#pragma unroll
+                for (int kk = 0; kk < NKA; ++kk) wf[kk] = piece(slot, Cfg::P_W + R * NKA + kk);
+                floatx4 ru = {1.f, 1.f, 1.f, 1.f};
+                if constexpr (!KDA) ru = *(const floatx4*)(sc + C + 16 * R + 4 * lq);
 #pragma unroll
                 for (int g = 0; g < VG; ++g) {
                     const int vb = avb0 + g;
                     const E* pst = sST + (16 * vb + lr) * PK + W * lq;
                     floatx4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                    for (int kk = 0; kk < NKA; ++kk) acc = F::mma(acc, s.a[kk], F::load(pst + KS * kk));
-                    const floatx4 u = ut_f32(s, g) - acc;
+                    for (int kk = 0; kk < NKA; ++kk) acc = F::mma(acc, wf[kk], F::load(pst + KS * kk));
+                    // U block (R, vb): piece gvb / PF - gp0 of row R, half gvb % PF
+                    const int gvb = slice * NVB + vb;
+                    const int j = gvb / PF - (slice * NVB) / PF;
+                    const uint4 q4 = *(const uint4*)(slot + (Cfg::P_U + R * NUP + j) * 1024 + l * 16);
+                    floatx4 uf;
+                    if constexpr (ESZ == 2) {
+                        const int h = gvb % PF;
+                        const uint32_t x = h == 0 ? q4.x : q4.z, y = h == 0 ? q4.y : q4.w;
+                        uf = floatx4{__uint_as_float(x << 16), __uint_as_float(x & 0xffff0000u),
+                                     __uint_as_float(y << 16), __uint_as_float(y & 0xffff0000u)};
+                    } else {
+                        uf = floatx4{__uint_as_float(q4.x), __uint_as_float(q4.y), __uint_as_float(q4.z),
+                                     __uint_as_float(q4.w)};
+                    }
+                    const floatx4 u = uf - acc;
                     store_acc_transposed<E>(sUT + (16 * vb) * PC + 16 * R, PC, u);
-                    if constexpr (!KDA)
-                        store_acc_transposed<E>(sUHT + (16 * vb) * PC + 16 * R, PC,
-                                                u * __builtin_bit_cast(floatx4, s.b[UP]));
+                    if constexpr (!KDA) store_acc_transposed<E>(sUHT + (16 * vb) * PC + 16 * R, PC, u * ru);
                 }
             } else {
                 // transposed: lane holds (Q S)[r = 16R + lr][v = 16vb + 4lq + e]
+                FT qf[NKA];
+#pragma unroll
+                for (int kk = 0; kk < NKA; ++kk) qf[kk] = piece(slot, Cfg::P_Q + R * NKA + kk);
 #pragma unroll
                 for (int g = 0; g < VG; ++g) {
                     const int vb = avb0 + g;
                     const E* pst = sST + (16 * vb + lr) * PK + W * lq;
                     floatx4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                    for (int kk = 0; kk < NKA; ++kk) acc = F::mma(acc, F::load(pst + KS * kk), s.a[kk]);
-                    if constexpr (!KDA) acc *= s.rq;
+                    for (int kk = 0; kk < NKA; ++kk) acc = F::mma(acc, F::load(pst + KS * kk), qf[kk]);
+                    if constexpr (!KDA) acc *= sc[16 * R + lr];
                     oacc[g] = acc;
                 }
             }
@@ -244,21 +355,28 @@ __global__ void __launch_bounds__(Cfg::NT) kda_inter_kernel(InterParams prm) {
         // ---------------- phase B ----------------
         if (sval) {
             const E* ub = KDA ? sUT : sUHT;
+            FT kf[NKP];
+#pragma unroll
+            for (int kk = 0; kk < NKP; ++kk) kf[kk] = piece(slot, Cfg::P_KT + scb * NKP + kk);
+            floatx4 gm;
+            if constexpr (KDA) gm = *(const floatx4*)(sc + 16 * scb + 4 * lq);
+            else gm = floatx4{sc[2 * C], sc[2 * C], sc[2 * C], sc[2 * C]};
 #pragma unroll
             for (int g = 0; g < SG; ++g) {
                 const int vb = svb0 + g;
-                floatx4 acc;
-                if constexpr (KDA) acc = Sreg[g] * s.gm;
-                else acc = Sreg[g] * s.gn;
+                floatx4 acc = Sreg[g] * gm;
                 const E* pu = ub + (16 * vb + lr) * PC + W * lq;
 #pragma unroll
-                for (int kk = 0; kk < NKP; ++kk) acc = F::mma(acc, s.kt[kk], F::load(pu + KS * kk));
+                for (int kk = 0; kk < NKP; ++kk) acc = F::mma(acc, kf[kk], F::load(pu + KS * kk));
                 Sreg[g] = acc;
                 store_acc_transposed<E>(sST + (16 * vb) * PK + 16 * scb, PK, acc);
             }
         }
         if (aval && !isU) {
             const int R = aR;
+            FT pf[NKP];
+#pragma unroll
+            for (int kk = 0; kk < NKP; ++kk) pf[kk] = piece(slot, Cfg::P_P + R * NKP + kk);
 #pragma unroll
             for (int g = 0; g < VG; ++g) {
                 const int vb = avb0 + g;
@@ -266,45 +384,12 @@ __global__ void __launch_bounds__(Cfg::NT) kda_inter_kernel(InterParams prm) {
                 const E* pu = sUT + (16 * vb + lr) * PC + W * lq;
 #pragma unroll
                 for (int kk = 0; kk < NKP; ++kk)
-                    if (KS * kk < 16 * (R + 1))
-                        acc = F::mma(acc, F::load(pu + KS * kk), __builtin_bit_cast(FT, s.b[kk]));
+                    if (KS * kk < 16 * (R + 1)) acc = F::mma(acc, F::load(pu + KS * kk), pf[kk]);
                 st4<E>(sO + (16 * R + lr) * PO + 16 * vb + 4 * lq, acc);
             }
         }
         __syncthreads();
-    };
-    // o tile of chunk cs, LDS -> HBM in 16-byte pieces; rows past the
-    // sequence end fall outside the buffer and are dropped.
-    auto store_o = [&](int cs) {
-        const int64_t t0 = (prm.c0 + cs) * C;
-        constexpr int PPR = NV * ESZ / 16, NPIECE = C * PPR;
-        for (int i = tid; i < NPIECE; i += Cfg::NT) {
-            const int r = i / PPR, cc = (i % PPR) * (16 / ESZ);
-            const uint4 val = *(const uint4*)(sO + r * PO + cc);
-            typedef int v4i __attribute__((ext_vector_type(4)));
-            __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(v4i, val), orsrc,
-                                                   (int)(((t0 + r) * DV + v0 + cc) * ESZ), 0, 0);
-        }
-    };
-    // Per chunk: wait for this chunk's operands (everything older is one
-    // chunk old by now), store the previous chunk's o, fetch the next
-    // chunk's operands, compute.  The waits never cover a fresh store.
-    auto vm_wait_all = []() { __builtin_amdgcn_s_waitcnt(0x0f70); };  // vmcnt(0)
-
-    Set s0, s1;
-    if (prm.ncs > 0) load(s0, 0);
-    for (int cs = 0; cs < prm.ncs; cs += 2) {
-        vm_wait_all();
-        if (cs > 0) store_o(cs - 1);
-        load(s1, cs + 1);
-        step(s0);
-        if (cs + 1 >= prm.ncs) break;
-        vm_wait_all();
-        store_o(cs);
-        load(s0, cs + 2);
-        step(s1);
     }
-    if (prm.ncs > 0) store_o(prm.ncs - 1);
 
     // ---- state out --------------------------------------------------------------
     if (prm.S_out && sval) {

@@ -1,0 +1,440 @@
+// kda_inter_scalar.hip -- inter-chunk kernel of the chunkwise prefill for one
+// decay per token (Gated DeltaNet) or none (DeltaNet), gfx950 / MI355X.
+//
+// "22,580: From GPT-2 to Kimi K3" (yichencityu.github.io), section 6.3: one
+// state is carried from chunk to chunk; inside a chunk the delta corrections
+// come from the WY factors T = (I + A)^-1.  With one decay per token the decay
+// leaves every channel sum (section 08), so with g_r the chunk-relative
+// cumulative ln(alpha), T' = T diag(beta) from the intra-chunk kernel's record
+// and the stored q, k, v:
+//
+//   X = V - diag(e^g) (K S)                     (k against the decayed state)
+//   u = T' X
+//   P_rj = (Q K^T)_rj e^{g_r - g_j}   (j <= r)
+//   O = diag(e^g) (Q S) + P u
+//   S <- e^{g_n} S + K^T diag(e^{g_n - g}) u
+//
+// (merging T' V - T' diag(e^g) K S into T' X keeps W = T' diag(e^g) K off the
+// chip and out of memory).  Every MFMA operand is a stored bf16 (or fp32)
+// input, or T', X and u rounded once to the input type; decays are applied to
+// the fp32 results.
+//
+// One workgroup owns one (b, h) head and a slice of NV state columns (columns
+// of S evolve independently, so slices never talk) and walks the chunks in
+// order; the fp32 state slice lives in registers of eight compute waves, with
+// a transposed operand copy in LDS.  Eight data waves keep two chunks of
+// inputs (q, k, the v slice, the record) in flight in registers, write each
+// into one half of a two-slot LDS ring one chunk ahead of use, and store the
+// previous chunk's o tile.  Per chunk the compute waves run three phases, each
+// ended by a barrier:
+//   1  X = V - e^g (K S),  Q S (kept in registers),  P
+//   2  u = T' X  (and e^{g_n-g} u)
+//   3  S = e^{g_n} S + K^T (e^{g_n-g} u),  o = e^g Q S + P u
+// Inputs are read through buffer resources bounded by the head's sequence, so
+// the ragged last chunk reads zeros past token L and its o stores past token L
+// are dropped, with no branch.
+#include "kda_device.h"
+#include "kda_internal.h"
+
+namespace kda {
+
+template <int DK_, int NV_, int C_, typename E_>
+struct ScalarInterCfg {
+    typedef E_ E;
+    static constexpr int DK = DK_, NV = NV_, C = C_;
+    static constexpr int NB = C / 16, NCB = DK / 16, NVB = NV / 16;
+    static constexpr int NPAIR = NB * (NB + 1) / 2;
+    static constexpr int ESZ = sizeof(E);
+    static constexpr int PADE = 32 / ESZ;
+    static constexpr int PK = DK + PADE;   // [C][DK] tiles, S^T [NV][DK]
+    static constexpr int PV = NV + PADE;   // v slice, o tile [C][NV]
+    static constexpr int PC = C + PADE;    // T', P [C][C]; X^T, u^T [NV][C]
+    static constexpr int NWC = 8, NWP = 8; // compute waves, data waves
+    static constexpr int NT = 64 * (NWC + NWP);
+    static constexpr int NTILE = NB * NVB;             // X / Q S / u / o tiles
+    static constexpr int ITL = (NTILE + NWC - 1) / NWC;
+    static constexpr int NST = NCB * NVB;              // state tiles
+    static constexpr int IST = (NST + NWC - 1) / NWC;
+    // ring slot: q, k tiles, v slice, T', decay scalars
+    static constexpr int O_SQ = 0;
+    static constexpr int O_SK = O_SQ + C * PK * ESZ;
+    static constexpr int O_SV = O_SK + C * PK * ESZ;
+    static constexpr int O_STB = O_SV + C * PV * ESZ;
+    static constexpr int O_SRS = O_STB + C * PC * ESZ;
+    static constexpr int SLOT = O_SRS + 1024;
+    // 1 KiB pieces of one chunk: q, k, v slice, T', scalars
+    static constexpr int NQP = C * DK * ESZ / 1024;
+    static constexpr int NVP = C * NV * ESZ / 1024;
+    static constexpr int NTP = C * C * ESZ / 1024;
+    static constexpr int NPIECE = 2 * NQP + NVP + NTP + 1;
+    // LDS
+    static constexpr int O_RING = 0;
+    static constexpr int O_SINK = O_RING + 2 * SLOT;
+    static constexpr int O_ST = O_SINK + 1024;
+    static constexpr int O_XT = O_ST + NV * PK * ESZ;
+    static constexpr int O_P = O_XT + NV * PC * ESZ;
+    static constexpr int O_UT = O_P + C * PC * ESZ;
+    static constexpr int O_UHT = O_UT + NV * PC * ESZ;
+    static constexpr int O_O = O_UHT + NV * PC * ESZ;
+    static constexpr int LDS_BYTES = O_O + C * PV * ESZ;
+    static_assert(DK % 32 == 0 && NV % 16 == 0 && (C == 32 || C == 64), "tile shape");
+    static_assert(NV * ESZ >= 32 && (C * NV * ESZ) % 1024 == 0, "v slice pieces");
+    static_assert(LDS_BYTES <= 160 * 1024, "LDS budget of one gfx950 CU");
+};
+
+template <class Cfg>
+__global__ void __launch_bounds__(Cfg::NT) kda_inter_scalar_kernel(InterParams prm) {
+    typedef typename Cfg::E E;
+    typedef Frag<E> F;
+    constexpr int DK = Cfg::DK, NV = Cfg::NV, C = Cfg::C, NB = Cfg::NB;
+    constexpr int NCB = Cfg::NCB, NVB = Cfg::NVB, NPAIR = Cfg::NPAIR;
+    constexpr int PK = Cfg::PK, PV = Cfg::PV, PC = Cfg::PC;
+    constexpr int NWC = Cfg::NWC, NWP = Cfg::NWP;
+    constexpr int NTILE = Cfg::NTILE, ITL = Cfg::ITL, NST = Cfg::NST, IST = Cfg::IST;
+    constexpr int ESZ = Cfg::ESZ, W = F::W, KS = F::KS;
+    constexpr int SLOT = Cfg::SLOT;
+    constexpr RecLayout RL = rec_layout_thin(C, ESZ);
+
+    __shared__ __attribute__((aligned(16))) char smem[Cfg::LDS_BYTES];
+    char* ring = smem + Cfg::O_RING;
+    E* sST = (E*)(smem + Cfg::O_ST);
+    E* sXT = (E*)(smem + Cfg::O_XT);
+    E* sP = (E*)(smem + Cfg::O_P);
+    E* sUT = (E*)(smem + Cfg::O_UT);
+    E* sUHT = (E*)(smem + Cfg::O_UHT);
+    E* sO = (E*)(smem + Cfg::O_O);
+
+    const int tid = threadIdx.x;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int l = tid & 63;
+    const int lr = l & 15, lq = l >> 4;
+
+    // ---- which (head, column slice) this workgroup owns --------------------
+    // Dispatch places workgroup i on XCD i % 8; give all slices of a head the
+    // same XCD so their shared q and k reads hit one L2.
+    const int total = prm.BH * prm.n_slices;
+    int pidx = blockIdx.x;
+    if ((total & 7) == 0) pidx = (blockIdx.x & 7) * (total >> 3) + (blockIdx.x >> 3);
+    const int bh = pidx / prm.n_slices;
+    const int slice = pidx - bh * prm.n_slices;
+    const int v0 = slice * NV;
+    const int64_t L = prm.L;
+    const int DV = prm.DV;
+    const int ncs = prm.ncs;
+
+    if (w >= NWC) {
+        // ======================= data waves ==================================
+        // Chunk x travels HBM -> registers (set x % 2) -> LDS slot x % 2.  In
+        // iteration c a data wave waits for chunk c+1's loads, writes them to
+        // slot (c+1) % 2 (free since the compute waves left it at the end of
+        // chunk c-1), loads chunk c+3 into the set just emptied and stores o
+        // of chunk c-1.  Every iteration issues the same NL loads and NS
+        // stores per wave (past the last chunk it re-reads the last one, and
+        // missing o pieces go past the buffer end), so the wait for chunk c+1
+        // is exactly "all but the last NL + 2 NS operations".  The loads are
+        // inline assembly, which the compiler's wait insertion does not track
+        // (it would merge the two sets across the loop and wait for the newer
+        // one); the waits here are explicit.
+        constexpr int NL = (Cfg::NPIECE + NWP - 1) / NWP;
+        constexpr int PPO = NV * ESZ / 16, NPO = C * PPO;  // o pieces per chunk
+        constexpr int NS = (NPO + 64 * NWP - 1) / (64 * NWP);
+        static_assert(NL + 2 * NS <= 63, "vmcnt range");
+        const int pw = w - NWC;
+        typedef int v4i __attribute__((ext_vector_type(4)));
+        auto rsrc = [](const void* base, uint32_t bytes) -> v4i {
+            const uint64_t b = (uint64_t)base;
+            return v4i{(int)(uint32_t)b, (int)((uint32_t)(b >> 32) & 0xffffu), (int)bytes, 0x00020000};
+        };
+        const int64_t hq = (int64_t)bh * L * DK * ESZ, hv = (int64_t)bh * L * DV * ESZ;
+        const char* recs = (const char*)prm.ws + (int64_t)bh * ncs * RL.bytes;
+        const __amdgpu_buffer_rsrc_t orsrc =
+            make_rsrc((const char*)prm.o + hv, (uint32_t)(L * DV * ESZ));
+        // piece j of this wave: source (0 q, 1 k, 2 v, 3 record), per-lane
+        // source offset within the chunk, per-lane LDS offset within a slot
+        // (~0u: the sink)
+        int src[NL];
+        uint32_t goff[NL], loff[NL];
+#pragma unroll
+        for (int j = 0; j < NL; ++j) {
+            const int i0 = pw + NWP * j;
+            const int i = i0 < Cfg::NPIECE ? i0 : pw;
+            int sidx;
+            uint32_t g, d;
+            if (i < 2 * Cfg::NQP) {
+                // q / k: rows of DK elements, 16-byte lanes
+                const int p = i % Cfg::NQP;
+                constexpr int LPR = DK * ESZ / 16, RPP = 64 / LPR;
+                const int r = p * RPP + l / LPR, cc = (l % LPR) * (16 / ESZ);
+                sidx = i < Cfg::NQP ? 0 : 1;
+                g = (r * DK + cc) * ESZ;
+                d = (sidx == 0 ? Cfg::O_SQ : Cfg::O_SK) + (r * PK + cc) * ESZ;
+            } else if (i < 2 * Cfg::NQP + Cfg::NVP) {
+                const int p = i - 2 * Cfg::NQP;
+                constexpr int LPR = NV * ESZ / 16, RPP = 64 / LPR;
+                const int r = p * RPP + l / LPR, cc = (l % LPR) * (16 / ESZ);
+                sidx = 2;
+                g = (r * DV + v0 + cc) * ESZ;
+                d = Cfg::O_SV + (r * PV + cc) * ESZ;
+            } else if (i < 2 * Cfg::NQP + Cfg::NVP + Cfg::NTP) {
+                const int p = i - 2 * Cfg::NQP - Cfg::NVP;
+                constexpr int LPR = C * ESZ / 16, RPP = 64 / LPR;
+                const int r = p * RPP + l / LPR, cc = (l % LPR) * (16 / ESZ);
+                sidx = 3;
+                g = RL.tb + (r * C + cc) * ESZ;
+                d = Cfg::O_STB + (r * PC + cc) * ESZ;
+            } else {
+                sidx = 3;
+                g = RL.rs + l * 16;
+                d = Cfg::O_SRS + l * 16;
+            }
+            src[j] = __builtin_amdgcn_readfirstlane(sidx);
+            goff[j] = g;
+            loff[j] = i0 < Cfg::NPIECE ? d : ~0u;
+        }
+        struct DSet {
+            v4i v[NL];
+        };
+        // Buffer resources start at the chunk and end at the sequence end
+        // (or the record end), so tokens past L read as zeros.
+        auto fetch = [&](DSet& st, int cs) {
+            cs = cs < ncs ? cs : ncs - 1;
+            const int64_t t0 = (prm.c0 + cs) * C;
+            const v4i rq = rsrc((const char*)prm.q + hq + t0 * DK * ESZ, (uint32_t)((L - t0) * DK * ESZ));
+            const v4i rk = rsrc((const char*)prm.k + hq + t0 * DK * ESZ, (uint32_t)((L - t0) * DK * ESZ));
+            const v4i rv = rsrc((const char*)prm.v + hv + t0 * DV * ESZ, (uint32_t)((L - t0) * DV * ESZ));
+            const v4i rr = rsrc(recs + (int64_t)cs * RL.bytes, RL.bytes);
+#pragma unroll
+            for (int j = 0; j < NL; ++j) {
+                const v4i res = src[j] == 0 ? rq : src[j] == 1 ? rk : src[j] == 2 ? rv : rr;
+                asm volatile("buffer_load_dwordx4 %0, %1, %2, 0 offen"
+                             : "=v"(st.v[j])
+                             : "v"(goff[j]), "s"(res)
+                             : "memory");
+            }
+        };
+        auto put = [&](const DSet& st, int cs) {
+            char* slot = ring + (cs & 1) * SLOT;
+            char* sink = smem + Cfg::O_SINK + l * 16;
+#pragma unroll
+            for (int j = 0; j < NL; ++j) *(v4i*)(loff[j] == ~0u ? sink : slot + loff[j]) = st.v[j];
+        };
+        // o tile of chunk cs (cs < 0: every store falls past the buffer end)
+        auto store_o = [&](int cs) {
+            const int64_t t0 = (prm.c0 + cs) * C;
+#pragma unroll
+            for (int k = 0; k < NS; ++k) {
+                const int i = (tid - 64 * NWC) + 64 * NWP * k;
+                const int ic = i < NPO ? i : 0;
+                const int r = ic / PPO, cc = (ic % PPO) * (16 / ESZ);
+                const uint4 val = *(const uint4*)(sO + r * PV + cc);
+                const uint32_t off = (cs >= 0 && i < NPO) ? (uint32_t)(((t0 + r) * DV + v0 + cc) * ESZ)
+                                                          : 0xfffffff0u;
+                __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(v4i, val), orsrc, (int)off, 0, 0);
+            }
+        };
+        // These waves meet the compute waves' barriers with a bare s_barrier
+        // (a full __syncthreads would also wait for the loads in flight); the
+        // empty asm statements keep LDS accesses on their side of it.
+        auto bare_barrier = []() {
+            asm volatile("" ::: "memory");
+            __builtin_amdgcn_s_barrier();
+            asm volatile("" ::: "memory");
+        };
+        auto wait_next = []() {
+            constexpr int n = NL + 2 * NS;
+            asm volatile("s_waitcnt vmcnt(%0)" ::"n"(n) : "memory");
+        };
+        // chunk x: loads issued in iteration x-3 into set x % 2, written to
+        // its slot in iteration x-1, used by the compute waves in iteration x
+        DSet s0, s1;
+        if (ncs > 0) {
+            fetch(s0, 0);
+            store_o(-1);
+            fetch(s1, 1);
+            store_o(-1);
+            wait_next();  // chunk 0 is in
+            put(s0, 0);
+            fetch(s0, 2);
+            store_o(-1);
+        }
+        __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0)
+        bare_barrier();
+        auto iteration = [&](DSet& nx, int cs) {
+            wait_next();
+            put(nx, cs + 1);
+            fetch(nx, cs + 3);
+            store_o(cs - 1);
+            __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): slot writes, o reads done
+            bare_barrier();                      // 1
+            bare_barrier();                      // 2
+            bare_barrier();                      // 3
+        };
+        for (int cs = 0; cs < ncs; cs += 2) {
+            iteration(s1, cs);
+            if (cs + 1 >= ncs) break;
+            iteration(s0, cs + 1);
+        }
+        if (ncs > 0) store_o(ncs - 1);
+        return;
+    }
+
+    // ========================= compute waves =====================================
+    // tile t (X, Q S, u, o): R = t % NB, vb = t / NB, owned by wave t % NWC;
+    // state tile t: cb = t % NCB, vb = t / NCB; P pair p: wave p % NWC.
+    floatx4 Sreg[IST];
+#pragma unroll
+    for (int i = 0; i < IST; ++i) {
+        Sreg[i] = floatx4{0.f, 0.f, 0.f, 0.f};
+        const int t = w + NWC * i;
+        if (t < NST && prm.S_in) {
+            const float* s0 = prm.S_in + (int64_t)bh * DK * DV + v0;
+            const int cb = t % NCB, vb = t / NCB;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) Sreg[i][e] = s0[(16 * cb + 4 * lq + e) * DV + 16 * vb + lr];
+        }
+    }
+#pragma unroll
+    for (int i = 0; i < IST; ++i) {
+        const int t = w + NWC * i;
+        if (t < NST) store_acc_transposed<E>(sST + (16 * (t / NCB)) * PK + 16 * (t % NCB), PK, Sreg[i]);
+    }
+    // blocks of P above the diagonal stay zero
+    for (int i = tid; i < C * PC; i += 64 * NWC) sP[i] = from_f32<E>(0.f);
+    __syncthreads();
+
+    floatx4 oacc[ITL];
+    for (int cs = 0; cs < ncs; ++cs) {
+        const char* slot = ring + (cs & 1) * SLOT;
+        const E* sQ = (const E*)(slot + Cfg::O_SQ);
+        const E* sK = (const E*)(slot + Cfg::O_SK);
+        const E* sV = (const E*)(slot + Cfg::O_SV);
+        const E* sTb = (const E*)(slot + Cfg::O_STB);
+        const float* rs = (const float*)(slot + Cfg::O_SRS);  // g, e^g, e^{g_n-g}, e^{g_n}
+
+        // ---------------- phase 1: X, Q S, P ----------------
+#pragma unroll
+        for (int i = 0; i < ITL; ++i) {
+            const int t = w + NWC * i;
+            if (t < NTILE) {
+                const int R = t % NB, vb = t / NB;
+                // (K S)[16R + 4lq + e][16vb + lr] -> X = V - e^g (K S), stored transposed
+                floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+                acc = mma_block<E>(acc, sK + (16 * R) * PK, PK, sST + (16 * vb) * PK, PK, DK);
+                const floatx4 eg = *(const floatx4*)(rs + C + 16 * R + 4 * lq);
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    acc[e] = to_f32(sV[(16 * R + 4 * lq + e) * PV + 16 * vb + lr]) - eg[e] * acc[e];
+                store_acc_transposed<E>(sXT + (16 * vb) * PC + 16 * R, PC, acc);
+                // transposed: lane holds (Q S)[16R + lr][16vb + 4lq + e], times e^{g_r}
+                floatx4 qs = {0.f, 0.f, 0.f, 0.f};
+                qs = mma_block<E>(qs, sST + (16 * vb) * PK, PK, sQ + (16 * R) * PK, PK, DK);
+                oacc[i] = qs * rs[C + 16 * R + lr];
+            }
+        }
+        for (int p = w; p < NPAIR; p += NWC) {
+            int R, J;
+            pair_of(p, R, J);
+            // lane holds (Q K^T)[r = 16R + lr][j = 16J + 4lq + e]
+            floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+            acc = mma_block<E>(acc, sK + (16 * J) * PK, PK, sQ + (16 * R) * PK, PK, DK);
+            const int r = 16 * R + lr;
+            const float gr = rs[r];
+            const floatx4 gj = *(const floatx4*)(rs + 16 * J + 4 * lq);
+            floatx4 v;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int j = 16 * J + 4 * lq + e;
+                v[e] = (J < R || j <= r) ? acc[e] * exp_neg(gr - gj[e]) : 0.f;
+            }
+            st4<E>(sP + r * PC + 16 * J + 4 * lq, v);
+        }
+        __syncthreads();
+
+        // ---------------- phase 2: u = T' X ----------------
+#pragma unroll
+        for (int i = 0; i < ITL; ++i) {
+            const int t = w + NWC * i;
+            if (t < NTILE) {
+                const int R = t % NB, vb = t / NB;
+                const int K = ((16 * (R + 1) + KS - 1) / KS) * KS;
+                floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+                acc = mma_block<E>(acc, sTb + (16 * R) * PC, PC, sXT + (16 * vb) * PC, PC, K);
+                store_acc_transposed<E>(sUT + (16 * vb) * PC + 16 * R, PC, acc);
+                const floatx4 egn = *(const floatx4*)(rs + 2 * C + 16 * R + 4 * lq);
+                store_acc_transposed<E>(sUHT + (16 * vb) * PC + 16 * R, PC, acc * egn);
+            }
+        }
+        __syncthreads();
+
+        // ---------------- phase 3: S update, o ----------------
+        const float gnv = rs[3 * C];
+#pragma unroll
+        for (int i = 0; i < IST; ++i) {
+            const int t = w + NWC * i;
+            if (t < NST) {
+                const int cb = t % NCB, vb = t / NCB;
+                floatx4 acc = Sreg[i] * gnv;
+                acc = mma_block_at<E>(acc, sK, PK, 16 * cb, sUHT + (16 * vb) * PC, PC, C);
+                Sreg[i] = acc;
+                store_acc_transposed<E>(sST + (16 * vb) * PK + 16 * cb, PK, acc);
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < ITL; ++i) {
+            const int t = w + NWC * i;
+            if (t < NTILE) {
+                const int R = t % NB, vb = t / NB;
+                const int K = ((16 * (R + 1) + KS - 1) / KS) * KS;
+                floatx4 acc = oacc[i];
+                acc = mma_block<E>(acc, sUT + (16 * vb) * PC, PC, sP + (16 * R) * PC, PC, K);
+                st4<E>(sO + (16 * R + lr) * PV + 16 * vb + 4 * lq, acc);
+            }
+        }
+        __syncthreads();
+    }
+
+    // ---- state out --------------------------------------------------------------
+    if (prm.S_out) {
+        float* so = prm.S_out + (int64_t)bh * DK * DV + v0;
+#pragma unroll
+        for (int i = 0; i < IST; ++i) {
+            const int t = w + NWC * i;
+            if (t < NST) {
+                const int cb = t % NCB, vb = t / NCB;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) so[(16 * cb + 4 * lq + e) * DV + 16 * vb + lr] = Sreg[i][e];
+            }
+        }
+    }
+}
+
+// ---- host-side dispatch -----------------------------------------------------
+
+template <int DK, int NV, int C, typename E>
+static hipError_t launch_scalar_cfg(const InterParams& prm, hipStream_t stream) {
+    typedef ScalarInterCfg<DK, NV, C, E> Cfg;
+    const int total = prm.BH * prm.n_slices;
+    hipLaunchKernelGGL((kda_inter_scalar_kernel<Cfg>), dim3(total), dim3(Cfg::NT), 0, stream, prm);
+    return hipGetLastError();
+}
+
+hipError_t launch_inter_scalar(InterParams prm, int dk, int qkv_bf16, int nv, hipStream_t stream) {
+    if (prm.BH == 0) return hipSuccess;
+    prm.n_slices = prm.DV / nv;
+#define KDA_CASE(DK_, NV_, C_, E_)                                      \
+    if (dk == DK_ && nv == NV_ && (qkv_bf16 != 0) == (sizeof(E_) == 2)) \
+        return launch_scalar_cfg<DK_, NV_, C_, E_>(prm, stream);
+    KDA_CASE(128, 16, 64, bf16)
+    KDA_CASE(128, 32, 64, bf16)
+    KDA_CASE(64, 16, 64, bf16)
+    KDA_CASE(64, 32, 64, bf16)
+    KDA_CASE(64, 64, 64, bf16)
+    KDA_CASE(128, 16, 32, float)
+    KDA_CASE(128, 32, 32, float)
+    KDA_CASE(64, 16, 32, float)
+    KDA_CASE(64, 32, 32, float)
+#undef KDA_CASE
+    return hipErrorInvalidValue;
+}
+
+}  // namespace kda

@@ -11,15 +11,17 @@ namespace kda {
 // ---- two-kernel prefill --------------------------------------------------
 // The intra-chunk kernel writes, per (b,h) head and chunk, one record of the
 // chunk's state-independent factors; the inter-chunk kernel walks the chunks
-// in order and carries the state.  Record sections (byte offsets, each
-// section 256-byte aligned), C = chunk length, E = the q/k/v element type:
+// in order and carries the state.  With per-channel decay (KDA) the record
+// holds every operand of the state pass; its sections (byte offsets, each
+// 256-byte aligned), C = chunk length, E = the q/k/v element type:
 //   w    W   = T diag(beta e^g) K     [C][DK]  E, fragment order (rows = token)
 //   ut   U   = T diag(beta) V         [C][DV]  E, accumulator order
 //   p    P   (decayed causal Q K^T)   [C][C]   E, fragment order (rows = token)
 //   kt   K^T (KDA: (K e^{g_n-g})^T)   [DK][C]  E, fragment order (rows = channel)
 //   qt   Q (KDA: Q e^g)               [C][DK]  E, fragment order (rows = token)
-//   gam  KDA only: e^{g_n} per key channel, DK floats
+//   gam  KDA only: e^{g_n} per key channel, DK floats (section of >= 1 KiB)
 //   rs   scalar decay only: e^{g_r} [C], e^{g_n-g_r} [C], e^{g_n}, fp32
+//        (section of >= 1 KiB)
 // "Fragment order" stores an operand with rows m and contraction index k the
 // way a 16x16 MFMA tile loop consumes it: 16-byte pieces (W = 16/sizeof(E)
 // consecutive k) of row m, piece index ((m/16) * (K/KS) + k/KS) * 64 + lane,
@@ -31,11 +33,11 @@ namespace kda {
 // (16R + 4(l/16) + i, 16vb + l%16) at
 // ((R * DV/(16 PF) + vb/PF) * 64 + l) * 4 PF + (vb % PF) * 4 + i.
 struct RecLayout {
-    uint32_t w, ut, p, kt, qt, gam, rs, bytes;
+    uint32_t w, ut, p, kt, qt, gam, rs, tb, bytes;
 };
 __host__ __device__ constexpr uint32_t rec_align(uint32_t x) { return (x + 255u) & ~255u; }
 __host__ __device__ constexpr RecLayout rec_layout(int dk, int dv, int c, int esz, bool kda) {
-    RecLayout r{0, 0, 0, 0, 0, 0, 0, 0};
+    RecLayout r{0, 0, 0, 0, 0, 0, 0, 0, 0};
     uint32_t o = 0;
     r.w = o;
     o = rec_align(o + (uint32_t)(c * dk * esz));
@@ -47,11 +49,25 @@ __host__ __device__ constexpr RecLayout rec_layout(int dk, int dv, int c, int es
     o = rec_align(o + (uint32_t)(dk * c * esz));
     r.qt = o;
     o = rec_align(o + (uint32_t)(c * dk * esz));
+    // the decay scalars take one whole 1 KiB piece (the inter-chunk kernel
+    // copies records in 1 KiB pieces)
     r.gam = o;
-    if (kda) o = rec_align(o + (uint32_t)(dk * 4));
+    if (kda) o = rec_align(o + (uint32_t)(dk * 4 > 1024 ? dk * 4 : 1024));
     r.rs = o;
-    if (!kda) o = rec_align(o + (uint32_t)((2 * c + 4) * 4));
+    if (!kda) o = rec_align(o + (uint32_t)((2 * c + 4) * 4 > 1024 ? (2 * c + 4) * 4 : 1024));
     r.bytes = o;
+    return r;
+}
+
+// Record of the scalar-decay path ("thin": the inter-chunk kernel reads q, k
+// and v itself and only needs the solved triangle and the decay scalars):
+//   tb   T diag(beta)                 [C][C]   E, row-major, zero above the diagonal
+//   rs   g_r [C], e^{g_r} [C], e^{g_n-g_r} [C], e^{g_n}   fp32, 1 KiB section
+__host__ __device__ constexpr RecLayout rec_layout_thin(int c, int esz) {
+    RecLayout r{0, 0, 0, 0, 0, 0, 0, 0, 0};
+    r.tb = 0;
+    r.rs = rec_align((uint32_t)(c * c * esz));
+    r.bytes = r.rs + rec_align((uint32_t)((3 * c + 1) * 4 > 1024 ? (3 * c + 1) * 4 : 1024));
     return r;
 }
 
@@ -73,6 +89,9 @@ struct IntraParams {
 };
 
 struct InterParams {
+    const void* q;          // [BH, L, DK]  (scalar-decay kernel)
+    const void* k;          // [BH, L, DK]  (scalar-decay kernel)
+    const void* v;          // [BH, L, DV]  (scalar-decay kernel)
     const void* ws;         // records [BH][ncs] written by the intra-chunk kernel
     const float* S_in;      // [BH, DK, DV] or null (zero state)
     float* S_out;           // [BH, DK, DV] or null; may equal S_in
@@ -89,6 +108,7 @@ hipError_t launch_intra(const IntraParams& prm, int dk, int dv, int qkv_bf16, in
                         hipStream_t stream);
 hipError_t launch_inter(InterParams prm, int dk, int qkv_bf16, int alpha_mode, int nv,
                         hipStream_t stream);
+hipError_t launch_inter_scalar(InterParams prm, int dk, int qkv_bf16, int nv, hipStream_t stream);
 
 // Arguments of the decode step kernel.
 struct DecodeParams {

@@ -66,18 +66,21 @@ struct IntraCfg {
     static constexpr int NW = 8;
     static constexpr int NT = 64 * NW;
 
+    // Scalar decay ("thin" record): only A and T are built here, the record
+    // holds T diag(beta) and the decay scalars.
+    static constexpr bool THIN = !KDA;
+
     // LDS: K row operand (KDA: k e^{g - G_{R+1}}, then K e^g in place),
-    // Q row operand (then V), KDA column operand k e^{G_{J+1} - g}, A / T^T
-    // (fp32), T diag(beta), scalar decay: T diag(beta e^g), gate factors, beta.
+    // KDA: Q row operand (then V) and column operand k e^{G_{J+1} - g};
+    // A / T^T (fp32), T diag(beta), gate factors, beta.
     static constexpr int SZ_K = C * PK * ESZ;
-    static constexpr int SZ_QV = (PK > PVV ? PK : PVV) * C * ESZ;
+    static constexpr int SZ_QV = THIN ? 0 : (PK > PVV ? PK : PVV) * C * ESZ;
     static constexpr int O_KR = 0;
     static constexpr int O_QV = O_KR + SZ_K;
     static constexpr int O_KC = O_QV + SZ_QV;
     static constexpr int O_A = O_KC + (KDA ? SZ_K : 0);
     static constexpr int O_TB = O_A + C * PA * 4;
-    static constexpr int O_TBG = O_TB + C * PC * ESZ;
-    static constexpr int O_GATE = O_TBG + (HEADG ? C * PC * ESZ : 0);
+    static constexpr int O_GATE = O_TB + C * PC * ESZ;
     // KDA: Z[NB][DK], E'[NB][DK], Y'[NPAIR][DK]; scalar: g[C], e^g[C]
     static constexpr int SZ_GATE = KDA ? (2 * NB + NPAIR) * DK * 4 : 2 * C * 4;
     static constexpr int O_BETA = O_GATE + SZ_GATE;
@@ -93,12 +96,12 @@ __global__ void __launch_bounds__(Cfg::NT) kda_intra_kernel(IntraParams prm) {
     typedef typename Cfg::E E;
     typedef Frag<E> F;
     constexpr int DK = Cfg::DK, DV = Cfg::DV, C = Cfg::C, NB = Cfg::NB;
-    constexpr bool KDA = Cfg::KDA, HEADG = Cfg::HEADG;
+    constexpr bool KDA = Cfg::KDA, HEADG = Cfg::HEADG, THIN = Cfg::THIN;
     constexpr int PK = Cfg::PK, PVV = Cfg::PVV, PC = Cfg::PC, PA = Cfg::PA;
     constexpr int NCB = Cfg::NCB, NVB = Cfg::NVB, NW = Cfg::NW, NT = Cfg::NT;
     constexpr int ESZ = Cfg::ESZ;
     constexpr int W = F::W, KS = F::KS;
-    constexpr RecLayout RL = rec_layout(DK, DV, C, ESZ, KDA);
+    constexpr RecLayout RL = THIN ? rec_layout_thin(C, ESZ) : rec_layout(DK, DV, C, ESZ, KDA);
 
     __shared__ __attribute__((aligned(16))) char smem[Cfg::LDS_BYTES];
     E* sKr = (E*)(smem + Cfg::O_KR);
@@ -107,7 +110,6 @@ __global__ void __launch_bounds__(Cfg::NT) kda_intra_kernel(IntraParams prm) {
     E* sKc = (E*)(smem + Cfg::O_KC);
     float* sA = (float*)(smem + Cfg::O_A);
     E* sTb = (E*)(smem + Cfg::O_TB);
-    E* sTbg = (E*)(smem + Cfg::O_TBG);
     float* sGate = (float*)(smem + Cfg::O_GATE);
     float* sBeta = (float*)(smem + Cfg::O_BETA);
     float* sZ = sGate;                // KDA views
@@ -142,24 +144,23 @@ __global__ void __launch_bounds__(Cfg::NT) kda_intra_kernel(IntraParams prm) {
     E* rQt = (E*)(rec + RL.qt);
     float* rGam = (float*)(rec + RL.gam);
     float* rRs = (float*)(rec + RL.rs);
+    E* rTb = (E*)(rec + RL.tb);
 
     auto bits_f32 = [](uint32_t u, bool half) -> float {
         return half ? __uint_as_float(u << 16) : __uint_as_float(u);
     };
 
-    // upper blocks of the T' tiles are read as zeros by the W and U products
-    for (int i = tid; i < C * PC; i += NT) {
-        sTb[i] = from_f32<E>(0.f);
-        if constexpr (HEADG) sTbg[i] = from_f32<E>(0.f);
-    }
+    // upper blocks of T diag(beta) are zeros (read by the W and U products,
+    // or copied out whole)
+    for (int i = tid; i < C * PC; i += NT) sTb[i] = from_f32<E>(0.f);
 
     // ---- v: into registers now, into LDS once the Q tile is free ------------
     constexpr int VPIECE = 16 / ESZ;
     constexpr int VPPR = DV / VPIECE;
-    constexpr int VPT = (C * VPPR + NT - 1) / NT;
+    constexpr int VPT = THIN ? 1 : (C * VPPR + NT - 1) / NT;
     uint4 rv[VPT];
 #pragma unroll
-    for (int i = 0; i < VPT; ++i) {
+    for (int i = 0; i < (THIN ? 0 : VPT); ++i) {
         int idx = tid + NT * i;
         idx = idx < C * VPPR ? idx : C * VPPR - 1;
         const int r = idx / VPPR, cc = (idx % VPPR) * VPIECE;
@@ -232,9 +233,7 @@ __global__ void __launch_bounds__(Cfg::NT) kda_intra_kernel(IntraParams prm) {
             if (idx < C * PPR) {
                 const int r0 = idx / PPR, cc = (idx % PPR) * VPIECE;
                 const int r = r0 < n ? r0 : n - 1;
-                const uint4 a = ldg<uint4>(gq, (r * DK + cc) * ESZ);
                 const uint4 b = ldg<uint4>(gk, (r * DK + cc) * ESZ);
-                *(uint4*)(sQr + r0 * PK + cc) = keep_or_zero(a, r0 < n);
                 *(uint4*)(sKr + r0 * PK + cc) = keep_or_zero(b, r0 < n);
             }
         }
@@ -251,10 +250,11 @@ __global__ void __launch_bounds__(Cfg::NT) kda_intra_kernel(IntraParams prm) {
                 const float eg = exp_neg(g);
                 sG[l] = g;
                 sEg[l] = eg;
-                rRs[l] = eg;
-                rRs[C + l] = exp_neg(gn - g);
+                rRs[l] = g;
+                rRs[C + l] = eg;
+                rRs[2 * C + l] = exp_neg(gn - g);
             }
-            if (l == 0) rRs[2 * C] = exp_neg(gn);
+            if (l == 0) rRs[3 * C] = exp_neg(gn);
         }
     }
     if (tid < C) {
@@ -327,7 +327,7 @@ __global__ void __launch_bounds__(Cfg::NT) kda_intra_kernel(IntraParams prm) {
         const E* pa = (KDA ? sKc : sKr) + (16 * J + lr) * PK + W * lq;
         const E* pk = sKr + (16 * R + lr) * PK + W * lq;
         const E* pq = sQr + (16 * R + lr) * PK + W * lq;
-        typename F::T fa[NKS], fk[NKS], fq[NKS];
+        typename F::T fa[NKS], fk[NKS], fq[THIN ? 1 : NKS];
         if (!KDA || J == R) {
 #pragma unroll
             for (int i = 0; i < NKS; ++i) fa[i] = F::load(pa + KS * i);
@@ -339,13 +339,13 @@ __global__ void __launch_bounds__(Cfg::NT) kda_intra_kernel(IntraParams prm) {
 #pragma unroll
         for (int i = 0; i < NKS; ++i) {
             fk[i] = F::load(pk + KS * i);
-            fq[i] = F::load(pq + KS * i);
+            if constexpr (!THIN) fq[i] = F::load(pq + KS * i);
         }
         floatx4 accA = {0.f, 0.f, 0.f, 0.f}, accP = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int i = 0; i < NKS; ++i) {
             accA = F::mma(accA, fa[i], fk[i]);
-            accP = F::mma(accP, fa[i], fq[i]);
+            if constexpr (!THIN) accP = F::mma(accP, fa[i], fq[i]);
         }
         // lane holds [m = j = 16J + 4lq + e][n = r = 16R + lr]
         const int rr = 16 * R + lr;
@@ -366,12 +366,14 @@ __global__ void __launch_bounds__(Cfg::NT) kda_intra_kernel(IntraParams prm) {
             vp[e] = (J < R || jj <= rr) ? accP[e] * f : 0.f;
         }
         *(floatx4*)(sA + rr * PA + 16 * J + 4 * lq) = va;
-        st4<E>(rP + frag_elem<E>(rr, 16 * J + 4 * lq, C), vp);
+        if constexpr (!THIN) st4<E>(rP + frag_elem<E>(rr, 16 * J + 4 * lq, C), vp);
     }
     // blocks above the diagonal of P are zero
-    for (int b = w; b < NB * NB; b += NW) {
-        const int R = b / NB, J = b % NB;
-        if (J > R) st4<E>(rP + frag_elem<E>(16 * R + lr, 16 * J + 4 * lq, C), floatx4{0.f, 0.f, 0.f, 0.f});
+    if constexpr (!THIN) {
+        for (int b = w; b < NB * NB; b += NW) {
+            const int R = b / NB, J = b % NB;
+            if (J > R) st4<E>(rP + frag_elem<E>(16 * R + lr, 16 * J + 4 * lq, C), floatx4{0.f, 0.f, 0.f, 0.f});
+        }
     }
     __syncthreads();
 
@@ -382,8 +384,7 @@ __global__ void __launch_bounds__(Cfg::NT) kda_intra_kernel(IntraParams prm) {
     // other three lanes of the quad (DPP broadcast) and every row takes its
     // A_RR[i][m] t_m term; the dependent chain is 15 steps long.  (A_RR[i][m]
     // is zero for m >= i, so no row needs masking.)  Results: T_RR^T (fp32) in
-    // the diagonal block of sA, T_RR diag(beta) in operand precision in sTb
-    // (and T_RR diag(beta e^g) in sTbg).
+    // the diagonal block of sA, T_RR diag(beta) in operand precision in sTb.
     if (w < NB) {
         const int R = w, j = l >> 2, s4 = l & 3;
         floatx4 arow[4][4];  // arow[ii][q4] = A_RR[4 s4 + ii][4 q4 .. 4 q4 + 3]
@@ -404,13 +405,8 @@ __global__ void __launch_bounds__(Cfg::NT) kda_intra_kernel(IntraParams prm) {
         floatx4 v4 = {acc[0], acc[1], acc[2], acc[3]};
         *(floatx4*)(sA + (16 * R + j) * PA + 16 * R + 4 * s4) = v4;
         const float bj = sBeta[16 * R + j];
-        float bgj = 0.f;
-        if constexpr (HEADG) bgj = bj * sEg[16 * R + j];
 #pragma unroll
-        for (int ii = 0; ii < 4; ++ii) {
-            sTb[(16 * R + 4 * s4 + ii) * PC + 16 * R + j] = from_f32<E>(acc[ii] * bj);
-            if constexpr (HEADG) sTbg[(16 * R + 4 * s4 + ii) * PC + 16 * R + j] = from_f32<E>(acc[ii] * bgj);
-        }
+        for (int ii = 0; ii < 4; ++ii) sTb[(16 * R + 4 * s4 + ii) * PC + 16 * R + j] = from_f32<E>(acc[ii] * bj);
     } else if constexpr (KDA) {
         // the other waves: K~ = k e^{g} in place (row operand x E'_R) for W,
         // and Q~ = q e^{g} straight to the record (A operand of Q~ S)
@@ -428,31 +424,16 @@ __global__ void __launch_bounds__(Cfg::NT) kda_intra_kernel(IntraParams prm) {
                 *(typename F::T*)(rQt + frag_elem<E>(r, cc, DK)) = F::load_scaled(p, sc);
             }
         }
-    } else {
-        // the other waves: K^T fragments (raw k; the inter-chunk kernel puts
-        // e^{g_n - g} on u) for the state update, and Q fragments (raw q; the
-        // inter-chunk kernel puts e^g on Q S)
-        constexpr int NKT = NCB * (C / KS), NQF = NB * (DK / KS);
-        for (int it = w - NB; it < NKT + NQF; it += NW - NB) {
-            if (it < NKT) {
-                const int cb = it / (C / KS), kk = it % (C / KS);
-                *(typename F::T*)(rKt + ((cb * (C / KS) + kk) * 64 + l) * W) =
-                    load_frag_tr(sKr, PK, kk * KS, 16 * cb);
-            } else {
-                const int f = it - NKT, R = f / (DK / KS), kk = f % (DK / KS);
-                *(typename F::T*)(rQt + (f * 64 + l) * W) =
-                    F::load(sQr + (16 * R + lr) * PK + kk * KS + W * lq);
-            }
-        }
     }
     __syncthreads();
 
     // ================= T2: off-diagonal blocks, by distance ==================
     // T_RJ = -T_RR sum_{M=J}^{R-1} A_RM T_MJ; T_RJ^T is stored at block (J, R)
-    // of sA, and T_RJ diag(beta) in sTb.  V enters LDS during the first level.
+    // of sA, and T_RJ diag(beta) in sTb.  KDA: V enters LDS during the first
+    // level.
 #pragma unroll
     for (int d = 1; d < NB; ++d) {
-        if (d == 1) {
+        if (!THIN && d == 1) {
 #pragma unroll
             for (int i = 0; i < VPT; ++i) {
                 const int idx = tid + NT * i;
@@ -478,21 +459,26 @@ __global__ void __launch_bounds__(Cfg::NT) kda_intra_kernel(IntraParams prm) {
             floatx4 res = -Frag<float>::mma(z, tf, acc);
             *(floatx4*)(sA + (16 * J + lr) * PA + 16 * R + 4 * lq) = res;
             const float bj = sBeta[16 * J + lr];
-            float bgj = 0.f;
-            if constexpr (HEADG) bgj = bj * sEg[16 * J + lr];
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                sTb[(16 * R + 4 * lq + e) * PC + 16 * J + lr] = from_f32<E>(res[e] * bj);
-                if constexpr (HEADG) sTbg[(16 * R + 4 * lq + e) * PC + 16 * J + lr] = from_f32<E>(res[e] * bgj);
-            }
+            for (int e = 0; e < 4; ++e) sTb[(16 * R + 4 * lq + e) * PC + 16 * J + lr] = from_f32<E>(res[e] * bj);
         }
         __syncthreads();
     }
 
     // ================= WU: W = T' K~ and U = T diag(beta) V ==================
-    // W tile (R, cb) is computed transposed so each lane holds four adjacent
-    // channels of one row; U tile (R, vb) lands directly in accumulator order.
-    const E* sTw = HEADG ? sTbg : sTb;
+    // Scalar decay: T diag(beta) goes out as it is.
+    if constexpr (THIN) {
+        constexpr int PPR = C * ESZ / 16;
+        for (int i = tid; i < C * PPR; i += NT) {
+            const int r = i / PPR, cc = (i % PPR) * (16 / ESZ);
+            *(uint4*)(rTb + r * C + cc) = *(const uint4*)(sTb + r * PC + cc);
+        }
+        return;
+    }
+    // KDA: W tile (R, cb) is computed transposed so each lane holds four
+    // adjacent channels of one row; U tile (R, vb) lands directly in
+    // accumulator order.
+    const E* sTw = sTb;
     for (int it = w; it < NB * (NCB + NVB); it += NW) {
         if (it < NB * NCB) {
             const int R = it % NB, cb = it / NB;
