@@ -58,6 +58,20 @@ template <> struct Frag<bf16> {
         r[7] = (bf16)((float)v[7] * s1[3]);
         return r;
     }
+    // p[0..7] * (s0, s1), rounded back to bf16
+    static __device__ __forceinline__ T load_scaled_v(const bf16* p, floatx4 s0, floatx4 s1) {
+        bf16x8 v = *(const bf16x8*)p;
+        bf16x8 r;
+        r[0] = (bf16)((float)v[0] * s0[0]);
+        r[1] = (bf16)((float)v[1] * s0[1]);
+        r[2] = (bf16)((float)v[2] * s0[2]);
+        r[3] = (bf16)((float)v[3] * s0[3]);
+        r[4] = (bf16)((float)v[4] * s1[0]);
+        r[5] = (bf16)((float)v[5] * s1[1]);
+        r[6] = (bf16)((float)v[6] * s1[2]);
+        r[7] = (bf16)((float)v[7] * s1[3]);
+        return r;
+    }
     static __device__ __forceinline__ T load_scaled_neg(const bf16* p, const float* s) {
         bf16x8 v = *(const bf16x8*)p;
         floatx4 s0 = *(const floatx4*)s;
@@ -85,6 +99,9 @@ template <> struct Frag<float> {
     static __device__ __forceinline__ T load(const float* p) { return *(const floatx4*)p; }
     static __device__ __forceinline__ T load_scaled(const float* p, const float* s) {
         return *(const floatx4*)p * *(const floatx4*)s;
+    }
+    static __device__ __forceinline__ T load_scaled_v(const float* p, floatx4 s0, floatx4) {
+        return *(const floatx4*)p * s0;
     }
     static __device__ __forceinline__ T load_scaled_neg(const float* p, const float* s) {
         return -(*(const floatx4*)p * *(const floatx4*)s);

@@ -312,41 +312,85 @@ __global__ void __launch_bounds__(Cfg::NT) kda_inter_scalar_kernel(InterParams p
         const float* rs = (const float*)(slot + Cfg::O_SRS);  // g, e^g, e^{g_n-g}, e^{g_n}
 
         // ---------------- phase 1: X, Q S, P ----------------
+        // Each fragment is read from LDS once per wave: S^T rows vb serve X
+        // and Q S, K rows R serve X and the diagonal P block, Q rows R serve
+        // Q S and every P block (R, J) this wave owns (J = vb, vb + NVB, ...).
+        constexpr int NKA = DK / KS;
+        typedef typename F::T FT;
 #pragma unroll
         for (int i = 0; i < ITL; ++i) {
             const int t = w + NWC * i;
             if (t < NTILE) {
                 const int R = t % NB, vb = t / NB;
+                FT st[NKA], kr[NKA], qr[NKA];
+                const E* pst = sST + (16 * vb + lr) * PK + W * lq;
+                const E* pkr = sK + (16 * R + lr) * PK + W * lq;
+                const E* pqr = sQ + (16 * R + lr) * PK + W * lq;
+#pragma unroll
+                for (int kk = 0; kk < NKA; ++kk) {
+                    st[kk] = F::load(pst + KS * kk);
+                    kr[kk] = F::load(pkr + KS * kk);
+                    qr[kk] = F::load(pqr + KS * kk);
+                }
                 // (K S)[16R + 4lq + e][16vb + lr] -> X = V - e^g (K S), stored transposed
                 floatx4 acc = {0.f, 0.f, 0.f, 0.f};
-                acc = mma_block<E>(acc, sK + (16 * R) * PK, PK, sST + (16 * vb) * PK, PK, DK);
+#pragma unroll
+                for (int kk = 0; kk < NKA; ++kk) acc = F::mma(acc, kr[kk], st[kk]);
+                // transposed: lane holds (Q S)[16R + lr][16vb + 4lq + e], times e^{g_r}
+                floatx4 qs = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int kk = 0; kk < NKA; ++kk) qs = F::mma(qs, st[kk], qr[kk]);
+                oacc[i] = qs * rs[C + 16 * R + lr];
                 const floatx4 eg = *(const floatx4*)(rs + C + 16 * R + 4 * lq);
 #pragma unroll
                 for (int e = 0; e < 4; ++e)
                     acc[e] = to_f32(sV[(16 * R + 4 * lq + e) * PV + 16 * vb + lr]) - eg[e] * acc[e];
                 store_acc_transposed<E>(sXT + (16 * vb) * PC + 16 * R, PC, acc);
-                // transposed: lane holds (Q S)[16R + lr][16vb + 4lq + e], times e^{g_r}
-                floatx4 qs = {0.f, 0.f, 0.f, 0.f};
-                qs = mma_block<E>(qs, sST + (16 * vb) * PK, PK, sQ + (16 * R) * PK, PK, DK);
-                oacc[i] = qs * rs[C + 16 * R + lr];
+                if constexpr (NVB >= 2) {
+                    // P blocks (R, J), J = vb, vb + NVB, ... <= R:
+                    // lane holds (Q K^T)[r = 16R + lr][j = 16J + 4lq + e]
+                    const int r = 16 * R + lr;
+                    const float gr = rs[r];
+                    for (int J = vb; J <= R; J += NVB) {
+                        floatx4 pa = {0.f, 0.f, 0.f, 0.f};
+                        if (J == R) {
+#pragma unroll
+                            for (int kk = 0; kk < NKA; ++kk) pa = F::mma(pa, kr[kk], qr[kk]);
+                        } else {
+                            const E* pkj = sK + (16 * J + lr) * PK + W * lq;
+#pragma unroll
+                            for (int kk = 0; kk < NKA; ++kk) pa = F::mma(pa, F::load(pkj + KS * kk), qr[kk]);
+                        }
+                        const floatx4 gj = *(const floatx4*)(rs + 16 * J + 4 * lq);
+                        floatx4 v;
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) {
+                            const int j = 16 * J + 4 * lq + e;
+                            v[e] = (J < R || j <= r) ? pa[e] * exp_neg(gr - gj[e]) : 0.f;
+                        }
+                        st4<E>(sP + r * PC + 16 * J + 4 * lq, v);
+                    }
+                }
             }
         }
-        for (int p = w; p < NPAIR; p += NWC) {
-            int R, J;
-            pair_of(p, R, J);
-            // lane holds (Q K^T)[r = 16R + lr][j = 16J + 4lq + e]
-            floatx4 acc = {0.f, 0.f, 0.f, 0.f};
-            acc = mma_block<E>(acc, sK + (16 * J) * PK, PK, sQ + (16 * R) * PK, PK, DK);
-            const int r = 16 * R + lr;
-            const float gr = rs[r];
-            const floatx4 gj = *(const floatx4*)(rs + 16 * J + 4 * lq);
-            floatx4 v;
+        if constexpr (NVB < 2) {
+            for (int p = w; p < NPAIR; p += NWC) {
+                int R, J;
+                pair_of(p, R, J);
+                // lane holds (Q K^T)[r = 16R + lr][j = 16J + 4lq + e]
+                floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+                acc = mma_block<E>(acc, sK + (16 * J) * PK, PK, sQ + (16 * R) * PK, PK, DK);
+                const int r = 16 * R + lr;
+                const float gr = rs[r];
+                const floatx4 gj = *(const floatx4*)(rs + 16 * J + 4 * lq);
+                floatx4 v;
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int j = 16 * J + 4 * lq + e;
-                v[e] = (J < R || j <= r) ? acc[e] * exp_neg(gr - gj[e]) : 0.f;
+                for (int e = 0; e < 4; ++e) {
+                    const int j = 16 * J + 4 * lq + e;
+                    v[e] = (J < R || j <= r) ? acc[e] * exp_neg(gr - gj[e]) : 0.f;
+                }
+                st4<E>(sP + r * PC + 16 * J + 4 * lq, v);
             }
-            st4<E>(sP + r * PC + 16 * J + 4 * lq, v);
         }
         __syncthreads();
 
@@ -368,15 +412,27 @@ __global__ void __launch_bounds__(Cfg::NT) kda_inter_scalar_kernel(InterParams p
 
         // ---------------- phase 3: S update, o ----------------
         const float gnv = rs[3 * C];
+        {
+            // every state tile of this wave has the same channel block
+            // (NCB divides NWC), so its K^T fragments are read once
+            static_assert(NWC % NCB == 0, "state tiles of a wave share cb");
+            constexpr int NKP = C / KS;
+            const int cb = w % NCB;
+            typename F::T kt[NKP];
 #pragma unroll
-        for (int i = 0; i < IST; ++i) {
-            const int t = w + NWC * i;
-            if (t < NST) {
-                const int cb = t % NCB, vb = t / NCB;
-                floatx4 acc = Sreg[i] * gnv;
-                acc = mma_block_at<E>(acc, sK, PK, 16 * cb, sUHT + (16 * vb) * PC, PC, C);
-                Sreg[i] = acc;
-                store_acc_transposed<E>(sST + (16 * vb) * PK + 16 * cb, PK, acc);
+            for (int kk = 0; kk < NKP; ++kk) kt[kk] = load_frag_tr(sK, PK, KS * kk, 16 * cb);
+#pragma unroll
+            for (int i = 0; i < IST; ++i) {
+                const int t = w + NWC * i;
+                if (t < NST) {
+                    const int vb = t / NCB;
+                    floatx4 acc = Sreg[i] * gnv;
+                    const E* pu = sUHT + (16 * vb + lr) * PC + W * lq;
+#pragma unroll
+                    for (int kk = 0; kk < NKP; ++kk) acc = F::mma(acc, kt[kk], F::load(pu + KS * kk));
+                    Sreg[i] = acc;
+                    store_acc_transposed<E>(sST + (16 * vb) * PK + 16 * cb, PK, acc);
+                }
             }
         }
 #pragma unroll

@@ -79,10 +79,12 @@ struct IntraCfg {
     static constexpr int O_QV = O_KR + SZ_K;
     static constexpr int O_KC = O_QV + SZ_QV;
     static constexpr int O_A = O_KC + (KDA ? SZ_K : 0);
-    static constexpr int O_TB = O_A + C * PA * 4;
-    static constexpr int O_GATE = O_TB + C * PC * ESZ;
-    // KDA: Z[NB][DK], E'[NB][DK], Y'[NPAIR][DK]; scalar: g[C], e^g[C]
-    static constexpr int SZ_GATE = KDA ? (2 * NB + NPAIR) * DK * 4 : 2 * C * 4;
+    // KDA: T diag(beta) lives in the column operand's space once A and P
+    // are done (keeps the kernel at two workgroups per CU)
+    static constexpr int O_TB = KDA ? O_KC : O_A + C * PA * 4;
+    static constexpr int O_GATE = KDA ? O_A + C * PA * 4 : O_TB + C * PC * ESZ;
+    // KDA: Z[NB][DK], E'[NB][DK]; scalar: g[C], e^g[C]
+    static constexpr int SZ_GATE = KDA ? 2 * NB * DK * 4 : 2 * C * 4;
     static constexpr int O_BETA = O_GATE + SZ_GATE;
     static constexpr int LDS_BYTES = O_BETA + C * 4;
 
@@ -114,7 +116,6 @@ __global__ void __launch_bounds__(Cfg::NT) kda_intra_kernel(IntraParams prm) {
     float* sBeta = (float*)(smem + Cfg::O_BETA);
     float* sZ = sGate;                // KDA views
     float* sE = sGate + NB * DK;
-    float* sY = sGate + 2 * NB * DK;
     float* sG = sGate;                // scalar views
     float* sEg = sGate + C;
 
@@ -151,8 +152,9 @@ __global__ void __launch_bounds__(Cfg::NT) kda_intra_kernel(IntraParams prm) {
     };
 
     // upper blocks of T diag(beta) are zeros (read by the W and U products,
-    // or copied out whole)
-    for (int i = tid; i < C * PC; i += NT) sTb[i] = from_f32<E>(0.f);
+    // or copied out whole); KDA zeroes them once its column operand is done
+    if constexpr (!KDA)
+        for (int i = tid; i < C * PC; i += NT) sTb[i] = from_f32<E>(0.f);
 
     // ---- v: into registers now, into LDS once the Q tile is free ------------
     constexpr int VPIECE = 16 / ESZ;
@@ -173,28 +175,43 @@ __global__ void __launch_bounds__(Cfg::NT) kda_intra_kernel(IntraParams prm) {
     const bool kact = KDA && kR < NB;
     float ky[KDA ? 16 : 1];                  // KDA: k * y, kept for K^
     if constexpr (KDA) {
+        // q and k rows come in as 16-byte pieces into the tiles they are
+        // rescaled in; each thread (channel, sub-block) then reads its 16
+        // tokens from LDS.  ln(alpha) is read per thread (one coalesced row
+        // segment per wave and token).
+        constexpr int PPR = DK / VPIECE;
+        constexpr int QPT = (C * PPR + NT - 1) / NT;
+#pragma unroll
+        for (int i = 0; i < QPT; ++i) {
+            const int idx = tid + NT * i;
+            if (idx < C * PPR) {
+                const int r0 = idx / PPR, cc = (idx % PPR) * VPIECE;
+                const int r = r0 < n ? r0 : n - 1;
+                const uint4 a = ldg<uint4>(gq, (r * DK + cc) * ESZ);
+                const uint4 b = ldg<uint4>(gk, (r * DK + cc) * ESZ);
+                *(uint4*)(sQr + r0 * PK + cc) = keep_or_zero(a, r0 < n);
+                *(uint4*)(sKr + r0 * PK + cc) = keep_or_zero(b, r0 < n);
+            }
+        }
+        float a[16];
         if (kact) {
-            const int R = kR;
-            float a[16], qv[16], kv[16];
 #pragma unroll
             for (int s = 0; s < 16; ++s) {
-                const int r = 16 * R + s;
+                const int r = 16 * kR + s;
                 const int rr = r < n ? r : n - 1;
                 const uint32_t el = rr * DK + kc;
-                float qq, kk2, la;
-                if constexpr (ESZ == 2) {
-                    qq = bits_f32(ldg<uint16_t>(gq, el * 2), true);
-                    kk2 = bits_f32(ldg<uint16_t>(gk, el * 2), true);
-                } else {
-                    qq = ldg<float>(gq, el * 4);
-                    kk2 = ldg<float>(gk, el * 4);
-                }
-                if constexpr (GBF) la = bits_f32(ldg<uint16_t>(gla, el * 2), true);
-                else la = ldg<float>(gla, el * 4);
-                const bool valid = r < n;
-                qv[s] = valid ? qq : 0.f;
-                kv[s] = valid ? kk2 : 0.f;
-                a[s] = valid ? la : 0.f;
+                const float la = GBF ? bits_f32(ldg<uint16_t>(gla, el * 2), true) : ldg<float>(gla, el * 4);
+                a[s] = r < n ? la : 0.f;
+            }
+        }
+        __syncthreads();
+        if (kact) {
+            const int R = kR;
+            float qv[16], kv[16];
+#pragma unroll
+            for (int s = 0; s < 16; ++s) {
+                qv[s] = to_f32(sQr[(16 * R + s) * PK + kc]);
+                kv[s] = to_f32(sKr[(16 * R + s) * PK + kc]);
             }
             // alpha = exp(ln alpha); x_s = prod_{s'<=s} alpha (within block)
             float x[16];
@@ -293,8 +310,7 @@ __global__ void __launch_bounds__(Cfg::NT) kda_intra_kernel(IntraParams prm) {
                 }
             }
             if (R == 0) {
-                // block-end factors E'_R = e^{G_{R+1}}, pair scales
-                // Y'_RJ = e^{G_{R+1} - G_{J+1}} (1 on the diagonal), e^{g_n}
+                // block-end factors E'_R = e^{G_{R+1}}, and e^{g_n}
                 float run = 1.f;
 #pragma unroll
                 for (int b = 0; b < NB; ++b) {
@@ -302,18 +318,6 @@ __global__ void __launch_bounds__(Cfg::NT) kda_intra_kernel(IntraParams prm) {
                     sE[b * DK + kc] = run;
                 }
                 rGam[kc] = run;
-                int p = 0;
-#pragma unroll
-                for (int rb2 = 0; rb2 < NB; ++rb2) {
-#pragma unroll
-                    for (int jb = 0; jb <= rb2; ++jb, ++p) {
-                        float y = 1.f;
-#pragma unroll
-                        for (int m = 0; m < NB; ++m)
-                            if (m > jb && m <= rb2) y *= Zb[m];
-                        sY[p * DK + kc] = y;
-                    }
-                }
             }
         }
         __syncthreads();
@@ -332,9 +336,17 @@ __global__ void __launch_bounds__(Cfg::NT) kda_intra_kernel(IntraParams prm) {
 #pragma unroll
             for (int i = 0; i < NKS; ++i) fa[i] = F::load(pa + KS * i);
         } else {
-            const float* ps = sY + p * DK + W * lq;
+            // pair scale Y'_RJ = e^{G_{R+1} - G_{J+1}} = prod_{J < m <= R} Z_m, per channel
 #pragma unroll
-            for (int i = 0; i < NKS; ++i) fa[i] = F::load_scaled(pa + KS * i, ps + KS * i);
+            for (int i = 0; i < NKS; ++i) {
+                const float* pz = sZ + KS * i + W * lq;
+                floatx4 y0 = {1.f, 1.f, 1.f, 1.f}, y1 = {1.f, 1.f, 1.f, 1.f};
+                for (int m = J + 1; m <= R; ++m) {
+                    y0 *= *(const floatx4*)(pz + m * DK);
+                    if constexpr (W == 8) y1 *= *(const floatx4*)(pz + m * DK + 4);
+                }
+                fa[i] = F::load_scaled_v(pa + KS * i, y0, y1);
+            }
         }
 #pragma unroll
         for (int i = 0; i < NKS; ++i) {
@@ -408,8 +420,14 @@ __global__ void __launch_bounds__(Cfg::NT) kda_intra_kernel(IntraParams prm) {
 #pragma unroll
         for (int ii = 0; ii < 4; ++ii) sTb[(16 * R + 4 * s4 + ii) * PC + 16 * R + j] = from_f32<E>(acc[ii] * bj);
     } else if constexpr (KDA) {
-        // the other waves: K~ = k e^{g} in place (row operand x E'_R) for W,
-        // and Q~ = q e^{g} straight to the record (A operand of Q~ S)
+        // the other waves: zero the blocks of T diag(beta) above the diagonal
+        // (its tile reuses the column operand's space), K~ = k e^{g} in place
+        // (row operand x E'_R) for W, and Q~ = q e^{g} straight to the record
+        // (A operand of Q~ S)
+        for (int i = tid - 64 * NB; i < C * C; i += NT - 64 * NB) {
+            const int r = i / C, j = i % C;
+            if ((j >> 4) > (r >> 4)) sTb[r * PC + j] = from_f32<E>(0.f);
+        }
         constexpr int PER_ROW = DK / VPIECE;
         for (int i = tid - 64 * NB; i < 2 * C * PER_ROW; i += NT - 64 * NB) {
             const int which = i / (C * PER_ROW);
