@@ -11,6 +11,15 @@ x 32 heads, fp32 state updated in place for 64 steps.
 Inputs are seeded synthetic data (linear_attention_sequence_kda_amd.inputs),
 resident in HBM before the timed region.  The CPU baseline is the fp64 oracle
 (oracle/, C, all host cores of this job) timed on the same workload.
+
+`roofline` covers the kernel with the most time per step, timed with the
+library's HIP event pairs (kda_timing_*) on the call's stream, over K more
+steps right after the timed region: achieved = the compulsory bytes of the call that kernel reads or writes,
+per launch, / its mean launch time.  `path` covers the whole call (every launch)
+against HBM and against bf16 MFMA.  `traffic` is the kernel's measured HBM
+bytes per launch from profiles/traffic.json (rocprofv3 FETCH_SIZE and
+WRITE_SIZE passes scaled by a copy of known size), or null when there is no
+measurement for the current sources.
 """
 
 from __future__ import annotations
@@ -41,28 +50,49 @@ def esize(dt):
     return 2 if dt == "bf16" else 4
 
 
-def prefill_bytes(w):
-    """Compulsory HBM bytes of one kda_chunk_fwd (each tensor touched once)."""
+def tensor_bytes(w):
+    """Bytes of each compulsory tensor of one kda_chunk_fwd (touched once)."""
     tok = w.B * w.H * w.L
     eq, eg = esize(w.qkv_dtype), esize(w.gate_dtype)
-    b = tok * (2 * w.dk + 2 * w.dv) * eq          # q, k, v read; o written
-    if w.alpha_mode == "channel":
-        b += tok * w.dk * eg
-    elif w.alpha_mode == "head":
-        b += tok * eg
-    b += tok * eg                                  # beta
-    b += w.B * w.H * w.dk * w.dv * 4               # S_final written
-    if w.s0_std is not None:
-        b += w.B * w.H * w.dk * w.dv * 4           # S0 read
-    return b
+    st = w.B * w.H * w.dk * w.dv * 4
+    la = {"channel": tok * w.dk * eg, "head": tok * eg}.get(w.alpha_mode, 0)
+    return {"q": tok * w.dk * eq, "k": tok * w.dk * eq, "v": tok * w.dv * eq,
+            "o": tok * w.dv * eq, "log_alpha": la, "beta": tok * eg,
+            "S0": st if w.s0_std is not None else 0, "S_final": st}
+
+
+def prefill_bytes(w):
+    """Compulsory HBM bytes of one kda_chunk_fwd: every input read once, o and
+    S_final written once."""
+    return sum(tensor_bytes(w).values())
 
 
 def prefill_flops(w):
-    """Algorithmic flops: 6 dk dv + 2C(3 dk + 2 dv) per token-head (C = 64):
-    state products Q S, W S, K^T u (2 dk dv each) and the full CxC chunk
-    blocks A, P, T K, T V ("2Ld^2 + 2LCd" counted the same way)."""
+    """Algorithmic flops of the path: 6 dk dv + 2C(3 dk + 2 dv) per token-head
+    (C = 64): state products Q S, W S, K^T u (2 dk dv each) and the full CxC
+    chunk blocks A, P, T K, T V and P u ("2Ld^2 + 2LCd" counted the same way)."""
     per = 6 * w.dk * w.dv + 2 * CHUNK * (3 * w.dk + 2 * w.dv)
     return w.B * w.H * w.L * per
+
+
+def kernel_work(w, kernel):
+    """(compulsory bytes, algorithmic flops) one whole kda_chunk_fwd hands to
+    `kernel`: the compulsory tensors it reads or writes (intermediate records
+    in the workspace are not counted) and the products it computes."""
+    t = tensor_bytes(w)
+    tok = w.B * w.H * w.L
+    dk, dv, C = w.dk, w.dv, CHUNK
+    if kernel == "kda_intra_kernel":
+        if w.alpha_mode == "channel":      # A, P, W = T K, U = T V from q, k, v, gates
+            return (t["q"] + t["k"] + t["v"] + t["log_alpha"] + t["beta"],
+                    tok * 2 * C * (3 * dk + dv))
+        return t["k"] + t["log_alpha"] + t["beta"], tok * 2 * C * dk   # A only
+    if kernel == "kda_inter_kernel":       # u = U - W S, o = Q S + P u, S update
+        return t["o"] + t["S0"] + t["S_final"], tok * (6 * dk * dv + 2 * C * dv)
+    if kernel == "kda_inter_scalar_kernel":  # X, u = T X, P, o, S update
+        return (t["q"] + t["k"] + t["v"] + t["o"] + t["S0"] + t["S_final"],
+                tok * (6 * dk * dv + 2 * C * dk + 4 * C * dv))
+    raise KeyError(kernel)
 
 
 def decode_bytes(w):
@@ -75,6 +105,21 @@ def decode_bytes(w):
     return b
 
 
+def measured_traffic(kernel, workload):
+    """HBM bytes per launch from the committed rocprofv3 counter passes, or None
+    when there are none for this kernel and workload or the kernel's sources
+    have changed since they were taken."""
+    from linear_attention_sequence_kda_amd import profiling
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as fh:
+        rec = json.load(fh).get(f"{kernel}|{workload}")
+    if not rec or rec.get("source_sha256") != profiling.source_digest(kernel):
+        return None
+    return rec["bytes"]
+
+
 def to_dev(torch, arr, dt):
     if arr is None:
         return None
@@ -82,6 +127,27 @@ def to_dev(torch, arr, dt):
         return torch.from_numpy(np.ascontiguousarray(arr).view(np.int16)).view(
             torch.bfloat16).to("cuda:0")
     return torch.from_numpy(np.ascontiguousarray(arr, dtype=np.float32)).to("cuda:0")
+
+
+def kernel_times(torch, kda, steps, step_fn):
+    """Run step_fn `steps` times with the library's HIP event pairs on; return
+    {kernel: (launches per step, mean ms per launch)} for every kernel that
+    ran."""
+    kda.timing_reset()
+    kda.timing_enable(True)
+    try:
+        for _ in range(steps):
+            step_fn()
+        torch.cuda.synchronize()
+    finally:
+        kda.timing_enable(False)
+    out = {}
+    for name in kda.binding.KERNELS:
+        n, ms = kda.timing_read(name)
+        if n:
+            out[name] = (n / steps, ms / n)
+    kda.timing_reset()
+    return out
 
 
 def bench_prefill(torch, kda, gen, w, steps, warmup):
@@ -92,9 +158,11 @@ def bench_prefill(torch, kda, gen, w, steps, warmup):
     S0 = to_dev(torch, x["S0"], "f32") if x["S0"] is not None else None
     o = torch.empty((w.B, w.H, w.L, w.dv), dtype=d["v"].dtype, device="cuda:0")
     Sf = torch.empty((w.B, w.H, w.dk, w.dv), dtype=torch.float32, device="cuda:0")
+    wsb = kda.chunk_fwd_workspace_bytes(d["q"], d["v"], d["log_alpha"], d["beta"])
+    ws = torch.empty(max(wsb, 1), dtype=torch.uint8, device="cuda:0")
     args = (d["q"], d["k"], d["v"], d["log_alpha"], d["beta"], S0)
     for _ in range(warmup):
-        kda.chunk_fwd(*args, o=o, S_final=Sf)
+        kda.chunk_fwd(*args, o=o, S_final=Sf, workspace=ws)
     torch.cuda.synchronize()
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
           for _ in range(steps)]
@@ -102,12 +170,30 @@ def bench_prefill(torch, kda, gen, w, steps, warmup):
     t0 = time.perf_counter()
     for s, e in ev:
         s.record()
-        kda.chunk_fwd(*args, o=o, S_final=Sf)
+        kda.chunk_fwd(*args, o=o, S_final=Sf, workspace=ws)
         e.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    kern_ms = [s.elapsed_time(e) for s, e in ev]
-    return x, wall, kern_ms
+    # per-kernel durations: the same steps again with the library's event
+    # pairs around every launch (kept out of the region above, whose clock
+    # they would slow by a few microseconds per launch)
+    kern = kernel_times(torch, kda, steps,
+                        lambda: kda.chunk_fwd(*args, o=o, S_final=Sf, workspace=ws))
+    call_ms = [s.elapsed_time(e) for s, e in ev]
+    # the same call after a 1 GiB write has flushed the 256 MiB memory-side
+    # cache (as when other layers run between two calls); outside the timing
+    flush = torch.empty(1 << 28, dtype=torch.float32, device="cuda:0")
+    cold_ms = []
+    for _ in range(min(steps, 10)):
+        flush.fill_(1.0)
+        s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        s.record()
+        kda.chunk_fwd(*args, o=o, S_final=Sf, workspace=ws)
+        e.record()
+        torch.cuda.synchronize()
+        cold_ms.append(s.elapsed_time(e))
+    del flush
+    return x, wall, call_ms, kern, wsb, cold_ms
 
 
 def bench_decode(torch, kda, gen, w):
@@ -127,34 +213,38 @@ def bench_decode(torch, kda, gen, w):
         kda.decode_step(*st, S, o=o)
     S.copy_(S0)
     torch.cuda.synchronize()
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-          for _ in range(T)]
     t0 = time.perf_counter()
-    for st, (s, e) in zip(steps, ev):
-        s.record()
+    for st in steps:
         kda.decode_step(*st, S, o=o)
-        e.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    return wall, [s.elapsed_time(e) for s, e in ev]
+    # per-launch durations over the same 64 steps (state restored first)
+    S.copy_(S0)
+    it = iter(steps)
+    kern = kernel_times(torch, kda, T, lambda: kda.decode_step(*next(it), S, o=o))
+    return wall, kern
 
 
-def cpu_baseline(gen, w, x):
+def cpu_baseline(gen, w, x, min_seconds=10.0, max_passes=64):
     """The fp64 oracle (C, threads over (head, 32-column block)) on the whole
-    prefill workload."""
+    prefill workload, repeated until about min_seconds of CPU time have gone."""
     import oracle
     N = w.B * w.H
     f = lambda a: None if a is None else a.reshape((N,) + a.shape[2:])
     threads = oracle.default_threads()
     log(f"cpu baseline: oracle on the full workload with {threads} threads")
-    t0 = time.perf_counter()
-    oracle.forward(f(x["q"]), f(x["k"]), f(x["v"]), f(x["log_alpha"]), f(x["beta"]),
-                   f(x["S0"]), qkv_dtype=w.qkv_dtype, gate_dtype=w.gate_dtype,
-                   alpha_mode=w.alpha_mode, want_o=True, threads=threads)
-    dt = time.perf_counter() - t0
-    return {"value": w.B * w.L / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
-            "sample": f"full {w.name} workload ({N} heads x {w.L} tokens, all columns), "
-                      f"{dt:.2f} s"}
+    passes, dt = 0, 0.0
+    while dt < min_seconds and passes < max_passes:
+        t0 = time.perf_counter()
+        oracle.forward(f(x["q"]), f(x["k"]), f(x["v"]), f(x["log_alpha"]), f(x["beta"]),
+                       f(x["S0"]), qkv_dtype=w.qkv_dtype, gate_dtype=w.gate_dtype,
+                       alpha_mode=w.alpha_mode, want_o=True, threads=threads)
+        dt += time.perf_counter() - t0
+        passes += 1
+    return {"value": passes * w.B * w.L / dt, "unit": "tokens/s", "cores": threads,
+            "kind": "oracle",
+            "sample": f"full {w.name} workload ({N} heads x {w.L} tokens, all columns, "
+                      f"o and S_final) x {passes} passes, {dt:.2f} s"}
 
 
 def main():
@@ -176,6 +266,7 @@ def main():
 
     import torch
     import linear_attention_sequence_kda_amd as kda
+    from linear_attention_sequence_kda_amd import binding  # noqa: F401  (kda.binding)
     from linear_attention_sequence_kda_amd import inputs as gen
 
     kda.library()  # fail loudly if the HIP library is missing
@@ -186,18 +277,32 @@ def main():
         torch.cuda.synchronize()
         del src, dst
     w = gen.WORKLOADS[args.workload]
-    x, wall, kern_ms = bench_prefill(torch, kda, gen, w, args.steps, args.warmup)
+    x, wall, call_ms, kern, wsb, cold_ms = bench_prefill(torch, kda, gen, w, args.steps, args.warmup)
     ms_per_step = wall * 1e3 / args.steps
     tokens = w.B * w.L
     value = tokens / (wall / args.steps)
-    kavg = float(np.mean(kern_ms))
+    cavg = float(np.mean(call_ms))
     bytes_ = prefill_bytes(w)
     flops = prefill_flops(w)
-    gbs = bytes_ / (kavg * 1e-3) / 1e9
-    tflops = flops / (kavg * 1e-3) / 1e12
+    gbs = bytes_ / (cavg * 1e-3) / 1e9
+    tflops = flops / (cavg * 1e-3) / 1e12
     mfma_peak = BF16_MFMA_PEAK_TFLOPS if w.qkv_dtype == "bf16" else FP32_MFMA_PEAK_TFLOPS
-    log(f"prefill: {ms_per_step:.4f} ms/step wall, kernel avg {kavg*1e3:.1f} us "
-        f"(min {min(kern_ms)*1e3:.1f}), {gbs:.0f} GB/s, {tflops:.1f} TFLOP/s")
+    log(f"prefill: {ms_per_step:.4f} ms/step wall, call avg {cavg*1e3:.1f} us "
+        f"(min {min(call_ms)*1e3:.1f}), {gbs:.0f} GB/s, {tflops:.1f} TFLOP/s")
+    kernels = {}
+    for name, (per_step, ms) in kern.items():
+        kb, kf = kernel_work(w, name)
+        kb, kf = kb / per_step, kf / per_step     # per launch
+        kernels[name] = {"launches_per_step": per_step, "avg_us": ms * 1e3,
+                         "algorithmic_bytes_per_launch": kb,
+                         "algorithmic_flops_per_launch": kf,
+                         "GB/s": kb / (ms * 1e-3) / 1e9, "TFLOP/s": kf / (ms * 1e-3) / 1e12}
+        log(f"  {name}: {per_step:g} launch(es)/step, {ms*1e3:.1f} us avg, "
+            f"{kernels[name]['GB/s']:.0f} GB/s, {kernels[name]['TFLOP/s']:.1f} TFLOP/s")
+    # the dominant kernel: most time per step
+    dom = max(kernels, key=lambda n: kernels[n]["avg_us"] * kernels[n]["launches_per_step"])
+    kd = kernels[dom]
+    traffic = measured_traffic(dom, w.name)
 
     out = {
         "metric": "KDA prefill tokens/s + MFMA util; decode tokens/s + HBM GB/s (1 MI355X)",
@@ -214,30 +319,42 @@ def main():
         "data": "synthetic (seeded; shapes and distributions of the pages' workloads)",
         "config": {"workload": w.name, "batch": w.B, "heads": w.H, "seq_len": w.L,
                    "d_k": w.dk, "d_v": w.dv, "chunk": CHUNK, "alpha": w.alpha_mode,
-                   "gate_dtype": w.gate_dtype, "state_dtype": "f32"},
-        "roofline": {"kernel": "kda_chunk_kernel", "bound": "hbm", "achieved": gbs,
-                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": gbs / HBM_PEAK_GBS,
-                     "traffic": None, "algorithmic_bytes_per_launch": bytes_,
-                     "avg_kernel_us": kavg * 1e3},
-        "mfma": {"achieved": tflops, "peak": mfma_peak, "unit": "TFLOP/s",
-                 "frac": tflops / mfma_peak, "algorithmic_flops_per_launch": flops},
+                   "gate_dtype": w.gate_dtype, "state_dtype": "f32",
+                   "workspace_bytes": wsb},
+        # dominant kernel: compulsory bytes it moves per launch / its mean
+        # launch time (HIP events on the call's stream); the prefill's
+        # arithmetic intensity is left of the MI355X ridge, so HBM binds
+        "roofline": {"kernel": dom, "bound": "hbm", "achieved": kd["GB/s"],
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": kd["GB/s"] / HBM_PEAK_GBS,
+                     "traffic": traffic,
+                     "algorithmic_bytes_per_launch": kd["algorithmic_bytes_per_launch"],
+                     "avg_kernel_us": kd["avg_us"]},
+        "kernels": kernels,
+        # the whole kda_chunk_fwd call (every launch), against both roofs
+        "path": {"avg_call_us": cavg * 1e3, "min_call_us": min(call_ms) * 1e3,
+                 "avg_call_us_after_cache_flush": float(np.mean(cold_ms)) * 1e3,
+                 "hbm": {"achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": gbs / HBM_PEAK_GBS, "compulsory_bytes_per_call": bytes_},
+                 "mfma": {"achieved": tflops, "peak": mfma_peak, "unit": "TFLOP/s",
+                          "frac": tflops / mfma_peak, "algorithmic_flops_per_call": flops}},
     }
     if not args.no_decode:
         wd = gen.WORKLOADS[5]
-        dwall, dk_ms = bench_decode(torch, kda, gen, wd)
-        davg = float(np.mean(dk_ms))
+        dwall, dkern = bench_decode(torch, kda, gen, wd)
+        dper, dms = dkern["kda_decode_kernel"]
         dbytes = decode_bytes(wd)
-        dgbs = dbytes / (davg * 1e-3) / 1e9
+        dgbs = dbytes / (dms * 1e-3) / 1e9
         log(f"decode: {dwall*1e3/wd.decode_steps:.4f} ms/step wall, kernel avg "
-            f"{davg*1e3:.1f} us, {dgbs:.0f} GB/s")
+            f"{dms*1e3:.1f} us, {dgbs:.0f} GB/s")
         out["decode"] = {
             "workload": wd.name, "tokens_per_s": wd.B * wd.decode_steps / dwall,
             "unit": "tokens/s", "ms_per_step": dwall * 1e3 / wd.decode_steps,
             "steps": wd.decode_steps,
             "roofline": {"kernel": "kda_decode_kernel", "bound": "hbm", "achieved": dgbs,
                          "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": dgbs / HBM_PEAK_GBS,
-                         "traffic": None, "algorithmic_bytes_per_launch": dbytes,
-                         "avg_kernel_us": davg * 1e3},
+                         "traffic": measured_traffic("kda_decode_kernel", wd.name),
+                         "algorithmic_bytes_per_launch": dbytes,
+                         "avg_kernel_us": dms * 1e3},
         }
     if not args.no_cpu:
         out["cpu_baseline"] = cpu_baseline(gen, w, x)

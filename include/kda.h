@@ -127,6 +127,31 @@ int kda_decode_step(const kda_shape* shape, const void* q, const void* k, const 
                     const void* log_alpha, const void* beta, float* S, void* o,
                     void* hip_stream);
 
+/*
+ * Kernel timing, for measurement tools (not part of the computation).  While
+ * timing is on, every kernel that kda_chunk_fwd or kda_decode_step launches is
+ * bracketed by two HIP events recorded on the call's stream; the event pairs
+ * are kept until kda_timing_reset.  The events add a few microseconds of
+ * stream work per launch and nothing else changes.
+ *
+ *   kda_timing_enable(on)   on != 0 starts recording for later calls, 0 stops.
+ *   kda_timing_reset()      destroys every kept event pair.  KDA_ERR_HIP if a
+ *                           destroy failed.
+ *   kda_timing_read(name, &launches, &total_ms)
+ *                           waits for the kept launches of the kernel `name`
+ *                           ("kda_intra_kernel", "kda_inter_kernel",
+ *                           "kda_inter_scalar_kernel" or "kda_decode_kernel")
+ *                           and returns how many there were and their summed
+ *                           duration in milliseconds.  KDA_ERR_NULL for a NULL
+ *                           argument, KDA_ERR_SHAPE for an unknown name,
+ *                           KDA_ERR_HIP if an event query failed.
+ *
+ * The three calls share one process-wide record; use them from one thread.
+ */
+int kda_timing_enable(int on);
+int kda_timing_reset(void);
+int kda_timing_read(const char* kernel, int64_t* launches, double* total_ms);
+
 /* Static text for a kda_status code. */
 const char* kda_strerror(int status);
 

@@ -9,6 +9,8 @@ The compute path is libkda.so (hand-written HIP for gfx950, C ABI in
 ``inputs`` holds the seeded synthetic workloads.
 """
 
-from .binding import KdaError, chunk_fwd, decode_step, library  # noqa: F401
+from .binding import (KdaError, chunk_fwd, chunk_fwd_workspace_bytes, decode_step,  # noqa: F401
+                      library, timing_enable, timing_read, timing_reset)
 
-__all__ = ["chunk_fwd", "decode_step", "library", "KdaError"]
+__all__ = ["chunk_fwd", "chunk_fwd_workspace_bytes", "decode_step", "library", "KdaError",
+           "timing_enable", "timing_read", "timing_reset"]

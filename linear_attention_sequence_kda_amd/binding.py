@@ -63,6 +63,13 @@ def library() -> ctypes.CDLL:
         lib.kda_last_error.restype = ctypes.c_char_p
         lib.kda_abi_version.argtypes = []
         lib.kda_abi_version.restype = ctypes.c_int
+        lib.kda_timing_enable.argtypes = [ctypes.c_int]
+        lib.kda_timing_enable.restype = ctypes.c_int
+        lib.kda_timing_reset.argtypes = []
+        lib.kda_timing_reset.restype = ctypes.c_int
+        lib.kda_timing_read.argtypes = [ctypes.c_char_p, ctypes.POINTER(ctypes.c_int64),
+                                        ctypes.POINTER(ctypes.c_double)]
+        lib.kda_timing_read.restype = ctypes.c_int
         _lib = lib
     return _lib
 
@@ -117,18 +124,34 @@ def _stream(t) -> int:
     return torch.cuda.current_stream(t.device).cuda_stream
 
 
-def chunk_fwd(q, k, v, log_alpha, beta, S0=None, *, output_final_state: bool = True,
-              o=None, S_final=None) -> Tuple[object, Optional[object]]:
-    """Chunkwise prefill: returns (o [B,H,L,dv], S_final [B,H,dk,dv] fp32 or None).
+KERNELS = ("kda_intra_kernel", "kda_inter_kernel", "kda_inter_scalar_kernel",
+           "kda_decode_kernel")
 
-    q, k: [B,H,L,dk]; v: [B,H,L,dv] (bf16 or fp32, same dtype);
-    log_alpha: None (alpha = 1), [B,H,L] (one decay per head) or [B,H,L,dk]
-    (one per key channel); beta: [B,H,L] (same dtype as log_alpha, or any
-    float dtype when log_alpha is None); S0: [B,H,dk,dv] fp32 or None.
-    ``o`` / ``S_final`` may be given to write into existing buffers
-    (S_final may be S0 itself).
-    """
-    torch = _torch()
+
+def timing_enable(on: bool = True) -> None:
+    """Bracket every later kernel launch with HIP events on its stream."""
+    _check(library().kda_timing_enable(1 if on else 0))
+
+
+def timing_reset() -> None:
+    """Drop the kept event pairs."""
+    _check(library().kda_timing_reset())
+
+
+def timing_read(kernel: str) -> Tuple[int, float]:
+    """(launches, summed milliseconds) of one kernel since the last reset."""
+    n, ms = ctypes.c_int64(0), ctypes.c_double(0.0)
+    _check(library().kda_timing_read(kernel.encode(), ctypes.byref(n), ctypes.byref(ms)))
+    return n.value, ms.value
+
+
+def chunk_fwd_workspace_bytes(q, v, log_alpha, beta) -> int:
+    """Device workspace bytes chunk_fwd needs for these inputs."""
+    return library().kda_chunk_fwd_workspace_bytes(ctypes.byref(_chunk_shape(q, v, log_alpha,
+                                                                             beta)))
+
+
+def _chunk_shape(q, v, log_alpha, beta) -> KdaShape:
     B, H, L, dk = q.shape
     dv = v.shape[-1]
     if log_alpha is None:
@@ -137,6 +160,25 @@ def chunk_fwd(q, k, v, log_alpha, beta, S0=None, *, output_final_state: bool = T
         mode = KDA_ALPHA_HEAD
     else:
         mode = KDA_ALPHA_CHANNEL
+    return KdaShape(B, H, L, dk, dv, _dtype_code(q),
+                    _dtype_code(log_alpha if log_alpha is not None else beta), mode)
+
+
+def chunk_fwd(q, k, v, log_alpha, beta, S0=None, *, output_final_state: bool = True,
+              o=None, S_final=None, workspace=None) -> Tuple[object, Optional[object]]:
+    """Chunkwise prefill: returns (o [B,H,L,dv], S_final [B,H,dk,dv] fp32 or None).
+
+    q, k: [B,H,L,dk]; v: [B,H,L,dv] (bf16 or fp32, same dtype);
+    log_alpha: None (alpha = 1), [B,H,L] (one decay per head) or [B,H,L,dk]
+    (one per key channel); beta: [B,H,L] (same dtype as log_alpha, or any
+    float dtype when log_alpha is None); S0: [B,H,dk,dv] fp32 or None.
+    ``o`` / ``S_final`` may be given to write into existing buffers
+    (S_final may be S0 itself); ``workspace`` may be a uint8 GPU tensor of at
+    least chunk_fwd_workspace_bytes() bytes (else one is allocated per call).
+    """
+    torch = _torch()
+    B, H, L, dk = q.shape
+    dv = v.shape[-1]
     for name, t in (("q", q), ("k", k), ("v", v), ("beta", beta), ("log_alpha", log_alpha),
                     ("S0", S0)):
         if t is not None:
@@ -147,15 +189,18 @@ def chunk_fwd(q, k, v, log_alpha, beta, S0=None, *, output_final_state: bool = T
         S_final = torch.empty((B, H, dk, dv), dtype=torch.float32, device=v.device)
     if S0 is not None and S0.dtype != torch.float32:
         raise TypeError("S0 must be float32")
-    shape = KdaShape(B, H, L, dk, dv, _dtype_code(q),
-                     _dtype_code(log_alpha if log_alpha is not None else beta), mode)
+    shape = _chunk_shape(q, v, log_alpha, beta)
     lib = library()
     ws = lib.kda_chunk_fwd_workspace_bytes(ctypes.byref(shape))
-    workspace = torch.empty(ws, dtype=torch.uint8, device=v.device) if ws else None
+    if workspace is None:
+        workspace = torch.empty(ws, dtype=torch.uint8, device=v.device) if ws else None
+    else:
+        _require(workspace, "workspace")
+    ws_given = workspace.numel() * workspace.element_size() if workspace is not None else 0
     rc = lib.kda_chunk_fwd(ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha),
                            _ptr(beta), _ptr(S0), _ptr(o),
                            _ptr(S_final) if output_final_state else None,
-                           _ptr(workspace), ws, _stream(v))
+                           _ptr(workspace), ws_given, _stream(v))
     _check(rc)
     return o, (S_final if output_final_state else None)
 

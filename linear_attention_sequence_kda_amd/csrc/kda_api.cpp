@@ -6,7 +6,9 @@
 #include <stdint.h>
 #include <string.h>
 
+#include <mutex>
 #include <string>
+#include <vector>
 
 #include "kda.h"
 #include "kda_internal.h"
@@ -14,6 +16,42 @@
 namespace {
 
 thread_local std::string g_last_error;
+
+// ---- kernel timing (kda_timing_*) --------------------------------------------
+// While enabled, each kernel launch is bracketed by two events recorded on the
+// launch's stream; the pairs are kept until read or reset.
+enum KernelId { K_INTRA = 0, K_INTER, K_INTER_SCALAR, K_DECODE, K_COUNT };
+const char* const kKernelNames[K_COUNT] = {"kda_intra_kernel", "kda_inter_kernel",
+                                           "kda_inter_scalar_kernel", "kda_decode_kernel"};
+struct TimedLaunch {
+    int kernel;
+    hipEvent_t start, stop;
+};
+std::mutex g_timing_mu;
+bool g_timing_on = false;
+std::vector<TimedLaunch> g_timed;
+
+template <class Launch>
+hipError_t timed_launch(int kernel, hipStream_t stream, Launch&& launch) {
+    {
+        std::lock_guard<std::mutex> lock(g_timing_mu);
+        if (!g_timing_on) return launch();
+    }
+    TimedLaunch t{kernel, nullptr, nullptr};
+    hipError_t err = hipEventCreate(&t.start);
+    if (err == hipSuccess) err = hipEventCreate(&t.stop);
+    if (err == hipSuccess) err = hipEventRecord(t.start, stream);
+    if (err == hipSuccess) err = launch();
+    if (err == hipSuccess) err = hipEventRecord(t.stop, stream);
+    if (err != hipSuccess) {
+        if (t.start) (void)hipEventDestroy(t.start);
+        if (t.stop) (void)hipEventDestroy(t.stop);
+        return err;
+    }
+    std::lock_guard<std::mutex> lock(g_timing_mu);
+    g_timed.push_back(t);
+    return hipSuccess;
+}
 
 struct Span {
     uintptr_t lo = 0, hi = 0;  // [lo, hi); empty when lo == hi
@@ -204,8 +242,12 @@ int kda_chunk_fwd(const kda_shape* s, const void* q, const void* k, const void* 
     // one decay per token: records hold T diag(beta) and the decay scalars
     auto launch_state = [&](const kda::InterParams& x) {
         return s->alpha_mode == KDA_ALPHA_CHANNEL
-                   ? kda::launch_inter(x, (int)s->dk, qbf, s->alpha_mode, nv, stream)
-                   : kda::launch_inter_scalar(x, (int)s->dk, qbf, nv, stream);
+                   ? timed_launch(K_INTER, stream, [&] {
+                         return kda::launch_inter(x, (int)s->dk, qbf, s->alpha_mode, nv, stream);
+                     })
+                   : timed_launch(K_INTER_SCALAR, stream, [&] {
+                         return kda::launch_inter_scalar(x, (int)s->dk, qbf, nv, stream);
+                     });
     };
     hipError_t err = hipSuccess;
     if (plan.nchunks == 0) {
@@ -221,7 +263,9 @@ int kda_chunk_fwd(const kda_shape* s, const void* q, const void* k, const void* 
         const int64_t ncs = plan.nchunks - c0 < plan.span ? plan.nchunks - c0 : plan.span;
         ip.c0 = c0;
         ip.ncs = (int)ncs;
-        err = kda::launch_intra(ip, (int)s->dk, (int)s->dv, qbf, s->alpha_mode, stream);
+        err = timed_launch(K_INTRA, stream, [&] {
+            return kda::launch_intra(ip, (int)s->dk, (int)s->dv, qbf, s->alpha_mode, stream);
+        });
         if (err != hipSuccess) break;
         xp.S_in = sp == 0 ? S0 : s_mid;
         xp.S_out = sp == plan.nspans - 1 ? S_final : s_mid;
@@ -275,12 +319,64 @@ int kda_decode_step(const kda_shape* s, const void* q, const void* k, const void
     prm.BH = (int)bh;
     prm.gate_bf16 = s->gate_dtype == KDA_BF16;
     prm.alpha_mode = s->alpha_mode;
-    hipError_t err = kda::launch_decode(prm, (int)s->dk, (int)s->dv,
-                                        s->qkv_dtype == KDA_BF16, (hipStream_t)hip_stream);
+    const hipStream_t stream = (hipStream_t)hip_stream;
+    hipError_t err = timed_launch(K_DECODE, stream, [&] {
+        return kda::launch_decode(prm, (int)s->dk, (int)s->dv, s->qkv_dtype == KDA_BF16, stream);
+    });
     if (err != hipSuccess) {
         g_last_error = std::string("kda_decode_step: ") + hipGetErrorString(err);
         return KDA_ERR_HIP;
     }
+    return KDA_OK;
+}
+
+int kda_timing_enable(int on) {
+    std::lock_guard<std::mutex> lock(g_timing_mu);
+    g_timing_on = on != 0;
+    return KDA_OK;
+}
+
+int kda_timing_reset(void) {
+    std::vector<TimedLaunch> old;
+    {
+        std::lock_guard<std::mutex> lock(g_timing_mu);
+        old.swap(g_timed);
+    }
+    hipError_t err = hipSuccess;
+    for (const TimedLaunch& t : old) {
+        hipError_t e1 = hipEventDestroy(t.start), e2 = hipEventDestroy(t.stop);
+        if (err == hipSuccess) err = e1 != hipSuccess ? e1 : e2;
+    }
+    if (err != hipSuccess) {
+        g_last_error = std::string("kda_timing_reset: ") + hipGetErrorString(err);
+        return KDA_ERR_HIP;
+    }
+    return KDA_OK;
+}
+
+int kda_timing_read(const char* kernel, int64_t* launches, double* total_ms) {
+    if (!kernel || !launches || !total_ms) return KDA_ERR_NULL;
+    int id = -1;
+    for (int i = 0; i < K_COUNT; ++i)
+        if (strcmp(kernel, kKernelNames[i]) == 0) id = i;
+    if (id < 0) return KDA_ERR_SHAPE;
+    std::lock_guard<std::mutex> lock(g_timing_mu);
+    int64_t n = 0;
+    double sum = 0.0;
+    for (const TimedLaunch& t : g_timed) {
+        if (t.kernel != id) continue;
+        float ms = 0.f;
+        hipError_t err = hipEventSynchronize(t.stop);
+        if (err == hipSuccess) err = hipEventElapsedTime(&ms, t.start, t.stop);
+        if (err != hipSuccess) {
+            g_last_error = std::string("kda_timing_read: ") + hipGetErrorString(err);
+            return KDA_ERR_HIP;
+        }
+        ++n;
+        sum += ms;
+    }
+    *launches = n;
+    *total_ms = sum;
     return KDA_OK;
 }
 

@@ -134,17 +134,14 @@ __global__ void __launch_bounds__(Cfg::NT) kda_inter_kernel(InterParams prm) {
     if (w >= NWC) {
         // ======================= data waves ==================================
         // Chunk x travels HBM -> registers (set x % 2) -> LDS slot x % 2.
-        // In iteration c a data wave: waits for chunk c+1's loads, writes
-        // them to slot (c+1) % 2 (free since the compute waves left it at the
-        // end of chunk c-1), loads chunk c+3 into the set just emptied and
-        // stores o of chunk c-1.  Every iteration issues the same NL loads
-        // and NS stores per wave (past the last chunk it re-reads the last
-        // record, and missing o pieces go past the buffer end), so the wait
-        // for chunk c+1 is exactly "all but the last NL + 2 NS operations".
+        // In iteration c a data wave writes chunk c+1's registers to slot
+        // (c+1) % 2 (free since the compute waves left it at the end of chunk
+        // c-1), loads chunk c+3 into the set just emptied and stores o of
+        // chunk c-1.  Past the last chunk it re-reads the last record, and o
+        // pieces beyond the tile go past the buffer end.
         constexpr int NL = (Cfg::NPIECE + NWP - 1) / NWP;  // 1 KiB pieces per wave
         constexpr int PPR = NV * ESZ / 16, NPC = C * PPR;   // o pieces per chunk
         constexpr int NS = (NPC + 64 * NWP - 1) / (64 * NWP);
-        static_assert(NL + 2 * NS <= 63, "vmcnt range");
         const int pw = w - NWC;
         const __amdgpu_buffer_rsrc_t orsrc =
             make_rsrc((const char*)prm.o + (int64_t)bh * L * DV * ESZ, (uint32_t)(L * DV * ESZ));
@@ -176,21 +173,14 @@ __global__ void __launch_bounds__(Cfg::NT) kda_inter_kernel(InterParams prm) {
             v4i v[NL];
         };
         // Loads through a buffer resource over the record (the only vector
-        // register involved is the lane offset).  They are issued as inline
-        // assembly, which the compiler's wait insertion does not track: it
-        // would otherwise merge the two sets' loads across the loop and wait
-        // for the newest ones; the waits below are exact instead.
+        // register involved is the lane offset).
         auto fetch = [&](DSet& st, int cs) {
             cs = cs < ncs ? cs : ncs - 1;
-            const uint64_t base = (uint64_t)(recs + (int64_t)cs * rl.bytes);
-            const v4i rr = {(int)(uint32_t)base, (int)((uint32_t)(base >> 32) & 0xffffu), (int)rl.bytes,
-                            0x00020000};
+            const __amdgpu_buffer_rsrc_t rr = make_rsrc(recs + (int64_t)cs * rl.bytes, rl.bytes);
 #pragma unroll
             for (int j = 0; j < NL; ++j)
-                asm volatile("buffer_load_dwordx4 %0, %1, %2, %3 offen"
-                             : "=v"(st.v[j])
-                             : "v"(l16), "s"(rr), "s"(pg[j])
-                             : "memory");
+                st.v[j] = __builtin_bit_cast(
+                    v4i, __builtin_amdgcn_raw_buffer_load_b128(rr, (int)l16, (int)pg[j], 0));
         };
         auto put = [&](const DSet& st, int cs) {
             char* slot = ring + (cs & 1) * SLOT;
@@ -208,7 +198,7 @@ __global__ void __launch_bounds__(Cfg::NT) kda_inter_kernel(InterParams prm) {
                 const int r = ic / PPR, cc = (ic % PPR) * (16 / ESZ);
                 const uint4 val = *(const uint4*)(sO + r * PO + cc);
                 const uint32_t off = (cs >= 0 && i < NPC) ? (uint32_t)(((t0 + r) * DV + v0 + cc) * ESZ)
-                                                          : 0xfffffff0u;
+                                                          : 0x80000000u;
                 typedef int v4i __attribute__((ext_vector_type(4)));
                 __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(v4i, val), orsrc, (int)off, 0, 0);
             }
@@ -222,11 +212,6 @@ __global__ void __launch_bounds__(Cfg::NT) kda_inter_kernel(InterParams prm) {
             __builtin_amdgcn_s_barrier();
             asm volatile("" ::: "memory");
         };
-        // wait for all but the last NL + 2 NS vector memory operations
-        auto wait_next = []() {
-            constexpr int n = NL + 2 * NS;
-            asm volatile("s_waitcnt vmcnt(%0)" ::"n"(n) : "memory");
-        };
         // chunk x: loads issued in iteration x-3 into set x % 2, written to
         // its slot in iteration x-1, used by the compute waves in iteration x
         DSet s0, s1;
@@ -235,7 +220,6 @@ __global__ void __launch_bounds__(Cfg::NT) kda_inter_kernel(InterParams prm) {
             store_o(-1);
             fetch(s1, 1);
             store_o(-1);
-            wait_next();  // chunk 0 is in
             put(s0, 0);
             fetch(s0, 2);
             store_o(-1);
@@ -244,7 +228,6 @@ __global__ void __launch_bounds__(Cfg::NT) kda_inter_kernel(InterParams prm) {
         bare_barrier();
         // iteration cs: chunk cs+1 is in `nx`, which then takes chunk cs+3
         auto iteration = [&](DSet& nx, int cs) {
-            wait_next();
             put(nx, cs + 1);
             fetch(nx, cs + 3);
             store_o(cs - 1);

@@ -23,10 +23,12 @@
 // of S evolve independently, so slices never talk) and walks the chunks in
 // order; the fp32 state slice lives in registers of eight compute waves, with
 // a transposed operand copy in LDS.  Eight data waves keep two chunks of
-// inputs (q, k, the v slice, the record) in flight in registers, write each
-// into one half of a two-slot LDS ring one chunk ahead of use, and store the
-// previous chunk's o tile.  Per chunk the compute waves run three phases, each
-// ended by a barrier:
+// inputs (k, the v slice, T' from the record) in flight in registers, write
+// each into one half of a two-slot LDS ring one chunk ahead of use, and store
+// the previous chunk's o tile.  q is only ever a B operand (of Q S and of
+// P), so the compute waves load their q fragments straight from memory into
+// registers, two chunks ahead, and q never passes through LDS.  Per chunk the
+// compute waves run three phases, each ended by a barrier:
 //   1  X = V - e^g (K S),  Q S (kept in registers),  P
 //   2  u = T' X  (and e^{g_n-g} u)
 //   3  S = e^{g_n} S + K^T (e^{g_n-g} u),  o = e^g Q S + P u
@@ -46,7 +48,7 @@ struct ScalarInterCfg {
     static constexpr int NPAIR = NB * (NB + 1) / 2;
     static constexpr int ESZ = sizeof(E);
     static constexpr int PADE = 32 / ESZ;
-    static constexpr int PK = DK + PADE;   // [C][DK] tiles, S^T [NV][DK]
+    static constexpr int PK = DK + PADE;   // k tile [C][DK], S^T [NV][DK]
     static constexpr int PV = NV + PADE;   // v slice, o tile [C][NV]
     static constexpr int PC = C + PADE;    // T', P [C][C]; X^T, u^T [NV][C]
     static constexpr int NWC = 8, NWP = 8; // compute waves, data waves
@@ -55,18 +57,17 @@ struct ScalarInterCfg {
     static constexpr int ITL = (NTILE + NWC - 1) / NWC;
     static constexpr int NST = NCB * NVB;              // state tiles
     static constexpr int IST = (NST + NWC - 1) / NWC;
-    // ring slot: q, k tiles, v slice, T', decay scalars
-    static constexpr int O_SQ = 0;
-    static constexpr int O_SK = O_SQ + C * PK * ESZ;
+    // ring slot: k tile, v slice, T', decay scalars
+    static constexpr int O_SK = 0;
     static constexpr int O_SV = O_SK + C * PK * ESZ;
     static constexpr int O_STB = O_SV + C * PV * ESZ;
     static constexpr int O_SRS = O_STB + C * PC * ESZ;
     static constexpr int SLOT = O_SRS + 1024;
-    // 1 KiB pieces of one chunk: q, k, v slice, T', scalars
-    static constexpr int NQP = C * DK * ESZ / 1024;
+    // 1 KiB pieces of one chunk: k, v slice, T', scalars
+    static constexpr int NKP = C * DK * ESZ / 1024;
     static constexpr int NVP = C * NV * ESZ / 1024;
     static constexpr int NTP = C * C * ESZ / 1024;
-    static constexpr int NPIECE = 2 * NQP + NVP + NTP + 1;
+    static constexpr int NPIECE = NKP + NVP + NTP + 1;
     // LDS
     static constexpr int O_RING = 0;
     static constexpr int O_SINK = O_RING + 2 * SLOT;
@@ -76,7 +77,7 @@ struct ScalarInterCfg {
     static constexpr int O_UT = O_P + C * PC * ESZ;
     static constexpr int O_UHT = O_UT + NV * PC * ESZ;
     static constexpr int O_O = O_UHT + NV * PC * ESZ;
-    static constexpr int LDS_BYTES = O_O + C * PV * ESZ;
+    static constexpr int LDS_BYTES = O_O + 2 * C * PV * ESZ;   // o tiles of two chunks
     static_assert(DK % 32 == 0 && NV % 16 == 0 && (C == 32 || C == 64), "tile shape");
     static_assert(NV * ESZ >= 32 && (C * NV * ESZ) % 1024 == 0, "v slice pieces");
     static_assert(LDS_BYTES <= 160 * 1024, "LDS budget of one gfx950 CU");
@@ -87,7 +88,7 @@ __global__ void __launch_bounds__(Cfg::NT) kda_inter_scalar_kernel(InterParams p
     typedef typename Cfg::E E;
     typedef Frag<E> F;
     constexpr int DK = Cfg::DK, NV = Cfg::NV, C = Cfg::C, NB = Cfg::NB;
-    constexpr int NCB = Cfg::NCB, NVB = Cfg::NVB, NPAIR = Cfg::NPAIR;
+    constexpr int NCB = Cfg::NCB;
     constexpr int PK = Cfg::PK, PV = Cfg::PV, PC = Cfg::PC;
     constexpr int NWC = Cfg::NWC, NWP = Cfg::NWP;
     constexpr int NTILE = Cfg::NTILE, ITL = Cfg::ITL, NST = Cfg::NST, IST = Cfg::IST;
@@ -125,33 +126,27 @@ __global__ void __launch_bounds__(Cfg::NT) kda_inter_scalar_kernel(InterParams p
     if (w >= NWC) {
         // ======================= data waves ==================================
         // Chunk x travels HBM -> registers (set x % 2) -> LDS slot x % 2.  In
-        // iteration c a data wave waits for chunk c+1's loads, writes them to
-        // slot (c+1) % 2 (free since the compute waves left it at the end of
-        // chunk c-1), loads chunk c+3 into the set just emptied and stores o
-        // of chunk c-1.  Every iteration issues the same NL loads and NS
-        // stores per wave (past the last chunk it re-reads the last one, and
-        // missing o pieces go past the buffer end), so the wait for chunk c+1
-        // is exactly "all but the last NL + 2 NS operations".  The loads are
-        // inline assembly, which the compiler's wait insertion does not track
-        // (it would merge the two sets across the loop and wait for the newer
-        // one); the waits here are explicit.
+        // iteration c (compute chunk c) a data wave writes chunk c+1's
+        // registers to slot (c+1) % 2 (free since the compute waves left it
+        // at the end of chunk c-1) before the first barrier, stores o of
+        // chunk c-1 (its own LDS tile of two) before the second, and loads
+        // chunk c+3 into the set just emptied before the third, so each
+        // barrier interval carries a share of the traffic (the compute
+        // waves' own q requests go out at the end of the first).  Past the last chunk the
+        // last one is loaded again, and o pieces beyond the tile go past the
+        // buffer end.
         constexpr int NL = (Cfg::NPIECE + NWP - 1) / NWP;
         constexpr int PPO = NV * ESZ / 16, NPO = C * PPO;  // o pieces per chunk
         constexpr int NS = (NPO + 64 * NWP - 1) / (64 * NWP);
-        static_assert(NL + 2 * NS <= 63, "vmcnt range");
         const int pw = w - NWC;
         typedef int v4i __attribute__((ext_vector_type(4)));
-        auto rsrc = [](const void* base, uint32_t bytes) -> v4i {
-            const uint64_t b = (uint64_t)base;
-            return v4i{(int)(uint32_t)b, (int)((uint32_t)(b >> 32) & 0xffffu), (int)bytes, 0x00020000};
-        };
         const int64_t hq = (int64_t)bh * L * DK * ESZ, hv = (int64_t)bh * L * DV * ESZ;
         const char* recs = (const char*)prm.ws + (int64_t)bh * ncs * RL.bytes;
         const __amdgpu_buffer_rsrc_t orsrc =
             make_rsrc((const char*)prm.o + hv, (uint32_t)(L * DV * ESZ));
-        // piece j of this wave: source (0 q, 1 k, 2 v, 3 record), per-lane
-        // source offset within the chunk, per-lane LDS offset within a slot
-        // (~0u: the sink)
+        // piece j of this wave: source (1 k, 2 v, 3 record), per-lane source
+        // offset within the chunk, per-lane LDS offset within a slot (~0u:
+        // the sink)
         int src[NL];
         uint32_t goff[NL], loff[NL];
 #pragma unroll
@@ -160,23 +155,24 @@ __global__ void __launch_bounds__(Cfg::NT) kda_inter_scalar_kernel(InterParams p
             const int i = i0 < Cfg::NPIECE ? i0 : pw;
             int sidx;
             uint32_t g, d;
-            if (i < 2 * Cfg::NQP) {
-                // q / k: rows of DK elements, 16-byte lanes
-                const int p = i % Cfg::NQP;
+            if (i < Cfg::NKP) {
+                // k: rows of DK elements, 16-byte lanes
+                const int p = i;
                 constexpr int LPR = DK * ESZ / 16, RPP = 64 / LPR;
                 const int r = p * RPP + l / LPR, cc = (l % LPR) * (16 / ESZ);
-                sidx = i < Cfg::NQP ? 0 : 1;
+                sidx = 1;
                 g = (r * DK + cc) * ESZ;
-                d = (sidx == 0 ? Cfg::O_SQ : Cfg::O_SK) + (r * PK + cc) * ESZ;
-            } else if (i < 2 * Cfg::NQP + Cfg::NVP) {
-                const int p = i - 2 * Cfg::NQP;
+                d = Cfg::O_SK + (r * PK + cc) * ESZ;
+            } else if (i < Cfg::NKP + Cfg::NVP) {
+                const int p = i - Cfg::NKP;
                 constexpr int LPR = NV * ESZ / 16, RPP = 64 / LPR;
                 const int r = p * RPP + l / LPR, cc = (l % LPR) * (16 / ESZ);
                 sidx = 2;
                 g = (r * DV + v0 + cc) * ESZ;
                 d = Cfg::O_SV + (r * PV + cc) * ESZ;
-            } else if (i < 2 * Cfg::NQP + Cfg::NVP + Cfg::NTP) {
-                const int p = i - 2 * Cfg::NQP - Cfg::NVP;
+            } else if (i < Cfg::NKP + Cfg::NVP + Cfg::NTP) {
+                // T': [C][C] row-major in the record
+                const int p = i - Cfg::NKP - Cfg::NVP;
                 constexpr int LPR = C * ESZ / 16, RPP = 64 / LPR;
                 const int r = p * RPP + l / LPR, cc = (l % LPR) * (16 / ESZ);
                 sidx = 3;
@@ -199,17 +195,15 @@ __global__ void __launch_bounds__(Cfg::NT) kda_inter_scalar_kernel(InterParams p
         auto fetch = [&](DSet& st, int cs) {
             cs = cs < ncs ? cs : ncs - 1;
             const int64_t t0 = (prm.c0 + cs) * C;
-            const v4i rq = rsrc((const char*)prm.q + hq + t0 * DK * ESZ, (uint32_t)((L - t0) * DK * ESZ));
-            const v4i rk = rsrc((const char*)prm.k + hq + t0 * DK * ESZ, (uint32_t)((L - t0) * DK * ESZ));
-            const v4i rv = rsrc((const char*)prm.v + hv + t0 * DV * ESZ, (uint32_t)((L - t0) * DV * ESZ));
-            const v4i rr = rsrc(recs + (int64_t)cs * RL.bytes, RL.bytes);
+            const __amdgpu_buffer_rsrc_t rk =
+                make_rsrc((const char*)prm.k + hq + t0 * DK * ESZ, (uint32_t)((L - t0) * DK * ESZ));
+            const __amdgpu_buffer_rsrc_t rv =
+                make_rsrc((const char*)prm.v + hv + t0 * DV * ESZ, (uint32_t)((L - t0) * DV * ESZ));
+            const __amdgpu_buffer_rsrc_t rr = make_rsrc(recs + (int64_t)cs * RL.bytes, RL.bytes);
 #pragma unroll
             for (int j = 0; j < NL; ++j) {
-                const v4i res = src[j] == 0 ? rq : src[j] == 1 ? rk : src[j] == 2 ? rv : rr;
-                asm volatile("buffer_load_dwordx4 %0, %1, %2, 0 offen"
-                             : "=v"(st.v[j])
-                             : "v"(goff[j]), "s"(res)
-                             : "memory");
+                const __amdgpu_buffer_rsrc_t res = src[j] == 1 ? rk : src[j] == 2 ? rv : rr;
+                st.v[j] = __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(res, (int)goff[j], 0, 0));
             }
         };
         auto put = [&](const DSet& st, int cs) {
@@ -221,14 +215,15 @@ __global__ void __launch_bounds__(Cfg::NT) kda_inter_scalar_kernel(InterParams p
         // o tile of chunk cs (cs < 0: every store falls past the buffer end)
         auto store_o = [&](int cs) {
             const int64_t t0 = (prm.c0 + cs) * C;
+            const E* so = sO + (cs & 1) * C * PV;
 #pragma unroll
             for (int k = 0; k < NS; ++k) {
                 const int i = (tid - 64 * NWC) + 64 * NWP * k;
                 const int ic = i < NPO ? i : 0;
                 const int r = ic / PPO, cc = (ic % PPO) * (16 / ESZ);
-                const uint4 val = *(const uint4*)(sO + r * PV + cc);
+                const uint4 val = *(const uint4*)(so + r * PV + cc);
                 const uint32_t off = (cs >= 0 && i < NPO) ? (uint32_t)(((t0 + r) * DV + v0 + cc) * ESZ)
-                                                          : 0xfffffff0u;
+                                                          : 0x80000000u;
                 __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(v4i, val), orsrc, (int)off, 0, 0);
             }
         };
@@ -240,10 +235,6 @@ __global__ void __launch_bounds__(Cfg::NT) kda_inter_scalar_kernel(InterParams p
             __builtin_amdgcn_s_barrier();
             asm volatile("" ::: "memory");
         };
-        auto wait_next = []() {
-            constexpr int n = NL + 2 * NS;
-            asm volatile("s_waitcnt vmcnt(%0)" ::"n"(n) : "memory");
-        };
         // chunk x: loads issued in iteration x-3 into set x % 2, written to
         // its slot in iteration x-1, used by the compute waves in iteration x
         DSet s0, s1;
@@ -252,7 +243,6 @@ __global__ void __launch_bounds__(Cfg::NT) kda_inter_scalar_kernel(InterParams p
             store_o(-1);
             fetch(s1, 1);
             store_o(-1);
-            wait_next();  // chunk 0 is in
             put(s0, 0);
             fetch(s0, 2);
             store_o(-1);
@@ -260,13 +250,13 @@ __global__ void __launch_bounds__(Cfg::NT) kda_inter_scalar_kernel(InterParams p
         __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0)
         bare_barrier();
         auto iteration = [&](DSet& nx, int cs) {
-            wait_next();
             put(nx, cs + 1);
-            fetch(nx, cs + 3);
-            store_o(cs - 1);
-            __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): slot writes, o reads done
+            __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): slot writes done
             bare_barrier();                      // 1
+            store_o(cs - 1);
+            __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): o reads done
             bare_barrier();                      // 2
+            fetch(nx, cs + 3);
             bare_barrier();                      // 3
         };
         for (int cs = 0; cs < ncs; cs += 2) {
@@ -280,7 +270,7 @@ __global__ void __launch_bounds__(Cfg::NT) kda_inter_scalar_kernel(InterParams p
 
     // ========================= compute waves =====================================
     // tile t (X, Q S, u, o): R = t % NB, vb = t / NB, owned by wave t % NWC;
-    // state tile t: cb = t % NCB, vb = t / NCB; P pair p: wave p % NWC.
+    // state tile t: cb = t % NCB, vb = t / NCB.
     floatx4 Sreg[IST];
 #pragma unroll
     for (int i = 0; i < IST; ++i) {
@@ -302,35 +292,53 @@ __global__ void __launch_bounds__(Cfg::NT) kda_inter_scalar_kernel(InterParams p
     for (int i = tid; i < C * PC; i += 64 * NWC) sP[i] = from_f32<E>(0.f);
     __syncthreads();
 
+    // Every tile of wave w has R = w % NB (NB divides NWC), and so do its P
+    // blocks.  q rows R come straight from memory as the B operand of
+    // (Q S)^T and of P: lane l holds q[16R + l%16][KS kk + W (l/16) .. + W].
+    // Chunk x lands in register set x % 2, loaded two chunks ahead (past the
+    // last chunk the last one is loaded again); rows past token L read zero.
+    static_assert(NWC % NB == 0, "a wave's tiles share one row block");
+    constexpr int NKA = DK / KS;
+    typedef typename F::T FT;
+    const int Rw = w % NB;
+    struct QSet {
+        FT f[NKA];
+    };
+    const char* qhead = (const char*)prm.q + (int64_t)bh * L * DK * ESZ;
+    auto load_q = [&](QSet& qs, int cs) {
+        cs = cs < ncs ? cs : ncs - 1;
+        const int64_t t0 = (prm.c0 + cs) * C;
+        const __amdgpu_buffer_rsrc_t r =
+            make_rsrc(qhead + t0 * DK * ESZ, (uint32_t)((L - t0) * DK * ESZ));
+#pragma unroll
+        for (int kk = 0; kk < NKA; ++kk) {
+            const int off = ((16 * Rw + lr) * DK + KS * kk + W * lq) * ESZ;
+            qs.f[kk] = __builtin_bit_cast(FT, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+        }
+    };
+
     floatx4 oacc[ITL];
-    for (int cs = 0; cs < ncs; ++cs) {
+    auto chunk = [&](int cs, QSet& qc) {
         const char* slot = ring + (cs & 1) * SLOT;
-        const E* sQ = (const E*)(slot + Cfg::O_SQ);
         const E* sK = (const E*)(slot + Cfg::O_SK);
         const E* sV = (const E*)(slot + Cfg::O_SV);
         const E* sTb = (const E*)(slot + Cfg::O_STB);
         const float* rs = (const float*)(slot + Cfg::O_SRS);  // g, e^g, e^{g_n-g}, e^{g_n}
 
         // ---------------- phase 1: X, Q S, P ----------------
-        // Each fragment is read from LDS once per wave: S^T rows vb serve X
-        // and Q S, K rows R serve X and the diagonal P block, Q rows R serve
-        // Q S and every P block (R, J) this wave owns (J = vb, vb + NVB, ...).
-        constexpr int NKA = DK / KS;
-        typedef typename F::T FT;
+        // S^T rows vb serve X and Q S, read once per wave.
 #pragma unroll
         for (int i = 0; i < ITL; ++i) {
             const int t = w + NWC * i;
             if (t < NTILE) {
                 const int R = t % NB, vb = t / NB;
-                FT st[NKA], kr[NKA], qr[NKA];
+                FT st[NKA], kr[NKA];
                 const E* pst = sST + (16 * vb + lr) * PK + W * lq;
                 const E* pkr = sK + (16 * R + lr) * PK + W * lq;
-                const E* pqr = sQ + (16 * R + lr) * PK + W * lq;
 #pragma unroll
                 for (int kk = 0; kk < NKA; ++kk) {
                     st[kk] = F::load(pst + KS * kk);
                     kr[kk] = F::load(pkr + KS * kk);
-                    qr[kk] = F::load(pqr + KS * kk);
                 }
                 // (K S)[16R + 4lq + e][16vb + lr] -> X = V - e^g (K S), stored transposed
                 floatx4 acc = {0.f, 0.f, 0.f, 0.f};
@@ -339,59 +347,36 @@ __global__ void __launch_bounds__(Cfg::NT) kda_inter_scalar_kernel(InterParams p
                 // transposed: lane holds (Q S)[16R + lr][16vb + 4lq + e], times e^{g_r}
                 floatx4 qs = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                for (int kk = 0; kk < NKA; ++kk) qs = F::mma(qs, st[kk], qr[kk]);
+                for (int kk = 0; kk < NKA; ++kk) qs = F::mma(qs, st[kk], qc.f[kk]);
                 oacc[i] = qs * rs[C + 16 * R + lr];
                 const floatx4 eg = *(const floatx4*)(rs + C + 16 * R + 4 * lq);
 #pragma unroll
                 for (int e = 0; e < 4; ++e)
                     acc[e] = to_f32(sV[(16 * R + 4 * lq + e) * PV + 16 * vb + lr]) - eg[e] * acc[e];
                 store_acc_transposed<E>(sXT + (16 * vb) * PC + 16 * R, PC, acc);
-                if constexpr (NVB >= 2) {
-                    // P blocks (R, J), J = vb, vb + NVB, ... <= R:
-                    // lane holds (Q K^T)[r = 16R + lr][j = 16J + 4lq + e]
-                    const int r = 16 * R + lr;
-                    const float gr = rs[r];
-                    for (int J = vb; J <= R; J += NVB) {
-                        floatx4 pa = {0.f, 0.f, 0.f, 0.f};
-                        if (J == R) {
-#pragma unroll
-                            for (int kk = 0; kk < NKA; ++kk) pa = F::mma(pa, kr[kk], qr[kk]);
-                        } else {
-                            const E* pkj = sK + (16 * J + lr) * PK + W * lq;
-#pragma unroll
-                            for (int kk = 0; kk < NKA; ++kk) pa = F::mma(pa, F::load(pkj + KS * kk), qr[kk]);
-                        }
-                        const floatx4 gj = *(const floatx4*)(rs + 16 * J + 4 * lq);
-                        floatx4 v;
-#pragma unroll
-                        for (int e = 0; e < 4; ++e) {
-                            const int j = 16 * J + 4 * lq + e;
-                            v[e] = (J < R || j <= r) ? pa[e] * exp_neg(gr - gj[e]) : 0.f;
-                        }
-                        st4<E>(sP + r * PC + 16 * J + 4 * lq, v);
-                    }
-                }
             }
         }
-        if constexpr (NVB < 2) {
-            for (int p = w; p < NPAIR; p += NWC) {
-                int R, J;
-                pair_of(p, R, J);
-                // lane holds (Q K^T)[r = 16R + lr][j = 16J + 4lq + e]
-                floatx4 acc = {0.f, 0.f, 0.f, 0.f};
-                acc = mma_block<E>(acc, sK + (16 * J) * PK, PK, sQ + (16 * R) * PK, PK, DK);
-                const int r = 16 * R + lr;
-                const float gr = rs[r];
+        // P blocks (Rw, J) for J = w / NB, w / NB + NWC / NB, ... <= Rw:
+        // lane holds (Q K^T)[r = 16 Rw + lr][j = 16J + 4lq + e]
+        {
+            const int r = 16 * Rw + lr;
+            const float gr = rs[r];
+            for (int J = w / NB; J <= Rw; J += NWC / NB) {
+                floatx4 pa = {0.f, 0.f, 0.f, 0.f};
+                const E* pkj = sK + (16 * J + lr) * PK + W * lq;
+#pragma unroll
+                for (int kk = 0; kk < NKA; ++kk) pa = F::mma(pa, F::load(pkj + KS * kk), qc.f[kk]);
                 const floatx4 gj = *(const floatx4*)(rs + 16 * J + 4 * lq);
                 floatx4 v;
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
                     const int j = 16 * J + 4 * lq + e;
-                    v[e] = (J < R || j <= r) ? acc[e] * exp_neg(gr - gj[e]) : 0.f;
+                    v[e] = (J < Rw || j <= r) ? pa[e] * exp_neg(gr - gj[e]) : 0.f;
                 }
                 st4<E>(sP + r * PC + 16 * J + 4 * lq, v);
             }
         }
+        load_q(qc, cs + 2);
         __syncthreads();
 
         // ---------------- phase 2: u = T' X ----------------
@@ -443,10 +428,20 @@ __global__ void __launch_bounds__(Cfg::NT) kda_inter_scalar_kernel(InterParams p
                 const int K = ((16 * (R + 1) + KS - 1) / KS) * KS;
                 floatx4 acc = oacc[i];
                 acc = mma_block<E>(acc, sUT + (16 * vb) * PC, PC, sP + (16 * R) * PC, PC, K);
-                st4<E>(sO + (16 * R + lr) * PV + 16 * vb + 4 * lq, acc);
+                st4<E>(sO + (cs & 1) * C * PV + (16 * R + lr) * PV + 16 * vb + 4 * lq, acc);
             }
         }
         __syncthreads();
+    };
+    QSet qa, qb;
+    if (ncs > 0) {
+        load_q(qa, 0);
+        load_q(qb, 1);
+    }
+    for (int cs = 0; cs < ncs; cs += 2) {
+        chunk(cs, qa);
+        if (cs + 1 >= ncs) break;
+        chunk(cs + 1, qb);
     }
 
     // ---- state out --------------------------------------------------------------

@@ -1,0 +1,127 @@
+"""Measurement helpers: HBM traffic of one kernel from rocprofv3 counters.
+
+rocprofv3 ``--pmc FETCH_SIZE`` and ``--pmc WRITE_SIZE`` report KiB per
+dispatch as the memory side sees them.  Their scale is calibrated against a
+plain device-to-device copy of known size run in the same process (bench.py
+``--copy-calibration``: 256 MiB read and 256 MiB written by the runtime's copy
+kernel), so traffic = FETCH_SIZE / (copy FETCH_SIZE / copy bytes) + the same for
+WRITE_SIZE.  A measurement is tied to a digest of the kernel's sources and
+build flags; bench.py reports it only while the digest still matches.
+
+    python -m linear_attention_sequence_kda_amd.profiling traffic \\
+        --fetch <dir of the FETCH_SIZE pass> --write <dir of the WRITE_SIZE pass> \\
+        --kernel kda_inter_scalar_kernel --workload <name> --out profiles/traffic.json
+"""
+
+from __future__ import annotations
+
+import argparse
+import csv
+import glob
+import hashlib
+import json
+import os
+from typing import Dict, List
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG)
+CSRC = os.path.join(PKG, "csrc")
+
+COPY_BYTES = 256 << 20          # bench.py --copy-calibration: one 256 MiB copy
+COPY_KERNEL = "__amd_rocclr_copyBuffer"
+
+# sources whose change changes the kernel's memory traffic
+KERNEL_SOURCES = {
+    "kda_intra_kernel": ["kda_intra.hip"],
+    "kda_inter_kernel": ["kda_inter.hip"],
+    "kda_inter_scalar_kernel": ["kda_inter_scalar.hip"],
+    "kda_decode_kernel": ["kda_decode.hip"],
+}
+COMMON_SOURCES = ["kda_device.h", "kda_internal.h"]
+# the prefill kernels' launch shapes (spans, column slices) are set by the ABI layer
+PREFILL_HOST = ["kda_api.cpp"]
+
+
+def source_digest(kernel: str) -> str:
+    """sha256 over the kernel's source files, the shared headers and build.py."""
+    h = hashlib.sha256()
+    names = KERNEL_SOURCES[kernel] + COMMON_SOURCES
+    if kernel != "kda_decode_kernel":
+        names = names + PREFILL_HOST
+    files = [os.path.join(CSRC, f) for f in names]
+    files.append(os.path.join(PKG, "build.py"))
+    for f in files:
+        h.update(os.path.basename(f).encode())
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def _rows(pass_dir: str) -> List[dict]:
+    paths = glob.glob(os.path.join(pass_dir, "**", "*counter_collection.csv"), recursive=True)
+    if not paths:
+        raise FileNotFoundError(f"no *counter_collection.csv under {pass_dir}")
+    rows: List[dict] = []
+    for p in paths:
+        with open(p, newline="") as fh:
+            rows.extend(csv.DictReader(fh))
+    return rows
+
+
+def per_dispatch_kib(pass_dir: str, counter: str, match: str) -> List[float]:
+    """Counter value (KiB) of every dispatch whose kernel name contains `match`."""
+    vals: Dict[str, float] = {}
+    for r in _rows(pass_dir):
+        if r["Counter_Name"] == counter and match in r["Kernel_Name"]:
+            vals[r["Dispatch_Id"]] = vals.get(r["Dispatch_Id"], 0.0) + float(r["Counter_Value"])
+    return [vals[k] for k in sorted(vals, key=int)]
+
+
+def traffic(fetch_dir: str, write_dir: str, kernel: str) -> dict:
+    fk = per_dispatch_kib(fetch_dir, "FETCH_SIZE", kernel)
+    wk = per_dispatch_kib(write_dir, "WRITE_SIZE", kernel)
+    fc = per_dispatch_kib(fetch_dir, "FETCH_SIZE", COPY_KERNEL)
+    wc = per_dispatch_kib(write_dir, "WRITE_SIZE", COPY_KERNEL)
+    if not fk or not wk:
+        raise ValueError(f"no dispatch of {kernel} in the counter files")
+    if not fc or not wc:
+        raise ValueError("no calibration copy in the counter files (run bench.py with "
+                         "--copy-calibration)")
+    # the calibration copy is the first copy of the run (later copies are the
+    # benchmark's own, e.g. restoring a decode state)
+    f_factor = fc[0] * 1024.0 / COPY_BYTES   # counter bytes per real byte read
+    w_factor = wc[0] * 1024.0 / COPY_BYTES
+    fetch = sum(fk) / len(fk) * 1024.0 / f_factor
+    write = sum(wk) / len(wk) * 1024.0 / w_factor
+    return {"fetch_bytes": fetch, "write_bytes": write, "bytes": fetch + write,
+            "fetch_kib_per_dispatch": sum(fk) / len(fk),
+            "write_kib_per_dispatch": sum(wk) / len(wk),
+            "dispatches": len(fk), "copy_fetch_factor": f_factor,
+            "copy_write_factor": w_factor}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    sub = ap.add_subparsers(dest="cmd", required=True)
+    t = sub.add_parser("traffic")
+    t.add_argument("--fetch", required=True)
+    t.add_argument("--write", required=True)
+    t.add_argument("--kernel", required=True, choices=sorted(KERNEL_SOURCES))
+    t.add_argument("--workload", required=True)
+    t.add_argument("--out", required=True)
+    a = ap.parse_args()
+    rec = traffic(a.fetch, a.write, a.kernel)
+    rec["source_sha256"] = source_digest(a.kernel)
+    data = {}
+    if os.path.exists(a.out):
+        with open(a.out) as fh:
+            data = json.load(fh)
+    data[f"{a.kernel}|{a.workload}"] = rec
+    with open(a.out, "w") as fh:
+        json.dump(data, fh, indent=1, sort_keys=True)
+        fh.write("\n")
+    print(json.dumps(rec))
+
+
+if __name__ == "__main__":
+    main()

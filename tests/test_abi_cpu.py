@@ -164,3 +164,20 @@ def test_header_mentions_every_status():
     text = open(binding.HEADER).read()
     for name in binding.STATUS.values():
         assert name in text
+
+
+def test_timing_calls_without_launches(lib):
+    n, ms = ctypes.c_int64(-1), ctypes.c_double(-1.0)
+    assert lib.kda_timing_read(None, ctypes.byref(n), ctypes.byref(ms)) == 1
+    assert lib.kda_timing_read(b"kda_intra_kernel", None, ctypes.byref(ms)) == 1
+    assert lib.kda_timing_read(b"no_such_kernel", ctypes.byref(n), ctypes.byref(ms)) == 2
+    assert lib.kda_timing_enable(1) == 0
+    try:
+        # a rejected call launches nothing, so nothing is recorded
+        assert chunk(lib, shape(dk=96), bufs()) == 2
+        for name in binding.KERNELS:
+            assert lib.kda_timing_read(name.encode(), ctypes.byref(n), ctypes.byref(ms)) == 0
+            assert n.value == 0 and ms.value == 0.0
+    finally:
+        assert lib.kda_timing_enable(0) == 0
+        assert lib.kda_timing_reset() == 0
