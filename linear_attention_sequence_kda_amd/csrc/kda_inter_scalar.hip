@@ -88,7 +88,7 @@ __global__ void __launch_bounds__(Cfg::NT) kda_inter_scalar_kernel(InterParams p
     typedef typename Cfg::E E;
     typedef Frag<E> F;
     constexpr int DK = Cfg::DK, NV = Cfg::NV, C = Cfg::C, NB = Cfg::NB;
-    constexpr int NCB = Cfg::NCB;
+    constexpr int NCB = Cfg::NCB, NVB = Cfg::NVB;
     constexpr int PK = Cfg::PK, PV = Cfg::PV, PC = Cfg::PC;
     constexpr int NWC = Cfg::NWC, NWP = Cfg::NWP;
     constexpr int NTILE = Cfg::NTILE, ITL = Cfg::ITL, NST = Cfg::NST, IST = Cfg::IST;
@@ -269,8 +269,14 @@ __global__ void __launch_bounds__(Cfg::NT) kda_inter_scalar_kernel(InterParams p
     }
 
     // ========================= compute waves =====================================
-    // tile t (X, Q S, u, o): R = t % NB, vb = t / NB, owned by wave t % NWC;
-    // state tile t: cb = t % NCB, vb = t / NCB.
+    // Tiles (X, Q S, u, o): wave w owns (Rw, vb) for vb = jw, jw + NWC/NB,
+    // ... < NVB, with jw = w / NB; successive groups of NB waves take the row
+    // blocks in opposite orders, so the two compute waves that share a SIMD
+    // (w and w + 4) hold a short and a long row of the triangular products.
+    // State tile t: cb = t % NCB, vb = t / NCB.
+    static_assert(NWC % NB == 0, "whole groups of NB waves");
+    const int jw = w / NB;
+    const int Rw = (jw & 1) ? NB - 1 - w % NB : w % NB;
     floatx4 Sreg[IST];
 #pragma unroll
     for (int i = 0; i < IST; ++i) {
@@ -292,15 +298,13 @@ __global__ void __launch_bounds__(Cfg::NT) kda_inter_scalar_kernel(InterParams p
     for (int i = tid; i < C * PC; i += 64 * NWC) sP[i] = from_f32<E>(0.f);
     __syncthreads();
 
-    // Every tile of wave w has R = w % NB (NB divides NWC), and so do its P
-    // blocks.  q rows R come straight from memory as the B operand of
-    // (Q S)^T and of P: lane l holds q[16R + l%16][KS kk + W (l/16) .. + W].
+    // Every tile and P block of wave w has row block Rw.  q rows Rw come
+    // straight from memory as the B operand of (Q S)^T and of P: lane l
+    // holds q[16 Rw + l%16][KS kk + W (l/16) .. + W].
     // Chunk x lands in register set x % 2, loaded two chunks ahead (past the
     // last chunk the last one is loaded again); rows past token L read zero.
-    static_assert(NWC % NB == 0, "a wave's tiles share one row block");
     constexpr int NKA = DK / KS;
     typedef typename F::T FT;
-    const int Rw = w % NB;
     struct QSet {
         FT f[NKA];
     };
@@ -329,9 +333,9 @@ __global__ void __launch_bounds__(Cfg::NT) kda_inter_scalar_kernel(InterParams p
         // S^T rows vb serve X and Q S, read once per wave.
 #pragma unroll
         for (int i = 0; i < ITL; ++i) {
-            const int t = w + NWC * i;
-            if (t < NTILE) {
-                const int R = t % NB, vb = t / NB;
+            const int vb = jw + (NWC / NB) * i;
+            if (vb < NVB) {
+                const int R = Rw;
                 FT st[NKA], kr[NKA];
                 const E* pst = sST + (16 * vb + lr) * PK + W * lq;
                 const E* pkr = sK + (16 * R + lr) * PK + W * lq;
@@ -356,12 +360,12 @@ __global__ void __launch_bounds__(Cfg::NT) kda_inter_scalar_kernel(InterParams p
                 store_acc_transposed<E>(sXT + (16 * vb) * PC + 16 * R, PC, acc);
             }
         }
-        // P blocks (Rw, J) for J = w / NB, w / NB + NWC / NB, ... <= Rw:
+        // P blocks (Rw, J) for J = jw, jw + NWC / NB, ... <= Rw:
         // lane holds (Q K^T)[r = 16 Rw + lr][j = 16J + 4lq + e]
         {
             const int r = 16 * Rw + lr;
             const float gr = rs[r];
-            for (int J = w / NB; J <= Rw; J += NWC / NB) {
+            for (int J = jw; J <= Rw; J += NWC / NB) {
                 floatx4 pa = {0.f, 0.f, 0.f, 0.f};
                 const E* pkj = sK + (16 * J + lr) * PK + W * lq;
 #pragma unroll
@@ -382,9 +386,9 @@ __global__ void __launch_bounds__(Cfg::NT) kda_inter_scalar_kernel(InterParams p
         // ---------------- phase 2: u = T' X ----------------
 #pragma unroll
         for (int i = 0; i < ITL; ++i) {
-            const int t = w + NWC * i;
-            if (t < NTILE) {
-                const int R = t % NB, vb = t / NB;
+            const int vb = jw + (NWC / NB) * i;
+            if (vb < NVB) {
+                const int R = Rw;
                 const int K = ((16 * (R + 1) + KS - 1) / KS) * KS;
                 floatx4 acc = {0.f, 0.f, 0.f, 0.f};
                 acc = mma_block<E>(acc, sTb + (16 * R) * PC, PC, sXT + (16 * vb) * PC, PC, K);
@@ -422,9 +426,9 @@ __global__ void __launch_bounds__(Cfg::NT) kda_inter_scalar_kernel(InterParams p
         }
 #pragma unroll
         for (int i = 0; i < ITL; ++i) {
-            const int t = w + NWC * i;
-            if (t < NTILE) {
-                const int R = t % NB, vb = t / NB;
+            const int vb = jw + (NWC / NB) * i;
+            if (vb < NVB) {
+                const int R = Rw;
                 const int K = ((16 * (R + 1) + KS - 1) / KS) * KS;
                 floatx4 acc = oacc[i];
                 acc = mma_block<E>(acc, sUT + (16 * vb) * PC, PC, sP + (16 * R) * PC, PC, K);
