@@ -137,6 +137,21 @@ Plan make_plan(const kda_shape* s) {
     int64_t per_chunk = bh * p.rec_bytes;
     p.span = kSpanTargetBytes / per_chunk;
     if (p.span < 1) p.span = 1;
+    if (p.span < p.nchunks) {
+        // Round the span down so one span's intra-chunk grid (B*H*span
+        // workgroups) fills whole rounds of an MI355X's resident workgroups
+        // (256 CUs x 2 for KDA records, x 3 otherwise): a partial last round
+        // would leave most CUs idle.
+        const int64_t slots = 256 * (s->alpha_mode == KDA_ALPHA_CHANNEL ? 2 : 3);
+        int64_t a = bh, b = slots;
+        while (b) {
+            const int64_t t = a % b;
+            a = b;
+            b = t;
+        }
+        const int64_t unit = slots / a;  // smallest span with bh * span a multiple of slots
+        if (unit <= p.span) p.span -= p.span % unit;
+    }
     if (p.span > p.nchunks) p.span = p.nchunks;
     p.nspans = (p.nchunks + p.span - 1) / p.span;
     p.rec_area = p.span * per_chunk;
