@@ -266,3 +266,66 @@ def test_head_gate_equals_broadcast_channel_gate():
         assert oracle.slab_error(to_f64(Sf).reshape(4, 128, 128), S_ref, 1) <= TOL["bf16"]
     assert oracle.slab_error(to_f64(a[0]).reshape(4, 150, 128),
                              to_f64(b[0]).reshape(4, 150, 128), 1) <= 2 * TOL["bf16"]
+
+
+def test_caller_workspace_and_multi_span_state_area():
+    """A caller-supplied workspace of exactly the queried size gives the same
+    bits as the binding's own; a smaller one is rejected before any launch.
+    Without S_final, a multi-span call (KDA records, 2 spans here) carries the
+    state through the workspace's state area and must give the same o."""
+    import torch
+    kda = _kda()
+    from linear_attention_sequence_kda_amd.binding import KdaError
+    w = gen.custom(B=2, H=32, L=2048, dk=128, dv=128, qkv_dtype="bf16", gate_dtype="bf16",
+                   alpha_mode="channel", seed=31)
+    x = gen.prefill_inputs(w)
+    d = device_inputs(w, x)
+    args = (d["q"], d["k"], d["v"], d["log_alpha"], d["beta"], d["S0"])
+    say("caller workspace / multi-span state area")
+    wsb = kda.chunk_fwd_workspace_bytes(d["q"], d["v"], d["log_alpha"], d["beta"])
+    assert wsb > 0
+    o_ref, S_ref = kda.chunk_fwd(*args)
+    ws = torch.empty(wsb, dtype=torch.uint8, device="cuda:0")
+    o1, S1 = kda.chunk_fwd(*args, workspace=ws)
+    o2, none = kda.chunk_fwd(*args, output_final_state=False, workspace=ws)
+    torch.cuda.synchronize()
+    assert none is None
+    assert torch.equal(o1, o_ref) and torch.equal(S1, S_ref)
+    assert torch.equal(o2, o_ref)
+    small = torch.empty(wsb - 256, dtype=torch.uint8, device="cuda:0")
+    with pytest.raises(KdaError) as ei:
+        kda.chunk_fwd(*args, workspace=small)
+    assert ei.value.status == 6
+    N = w.B * w.H
+    o_or, _ = oracle_prefill(w, flat_heads(x, N))
+    assert oracle.slab_error(to_f64(o2).reshape(N, w.L, w.dv), o_or, 1) <= TOL["bf16"]
+
+
+def test_kernel_timing_counts_launches():
+    """kda_timing_* sees one intra-chunk and one inter-chunk launch per
+    single-span call and one decode launch per step, with positive times."""
+    import torch
+    kda = _kda()
+    w = gen.custom(B=1, H=4, L=300, dk=128, dv=128, qkv_dtype="bf16", gate_dtype="f32",
+                   alpha_mode="head", seed=41)
+    d = device_inputs(w, gen.prefill_inputs(w))
+    say("kernel timing")
+    kda.timing_reset()
+    kda.timing_enable(True)
+    try:
+        for _ in range(2):
+            kda.chunk_fwd(d["q"], d["k"], d["v"], d["log_alpha"], d["beta"], d["S0"])
+        S = torch.zeros((1, 4, 128, 128), dtype=torch.float32, device="cuda:0")
+        kda.decode_step(d["q"][:, :, 0].contiguous(), d["k"][:, :, 0].contiguous(),
+                        d["v"][:, :, 0].contiguous(), d["log_alpha"][:, :, 0].contiguous(),
+                        d["beta"][:, :, 0].contiguous(), S)
+        torch.cuda.synchronize()
+    finally:
+        kda.timing_enable(False)
+    got = {k: kda.timing_read(k) for k in kda.binding.KERNELS}
+    kda.timing_reset()
+    assert got["kda_intra_kernel"][0] == 2 and got["kda_inter_scalar_kernel"][0] == 2
+    assert got["kda_decode_kernel"][0] == 1 and got["kda_inter_kernel"][0] == 0
+    for k in ("kda_intra_kernel", "kda_inter_scalar_kernel", "kda_decode_kernel"):
+        assert got[k][1] > 0.0
+    assert kda.timing_read("kda_intra_kernel") == (0, 0.0)
