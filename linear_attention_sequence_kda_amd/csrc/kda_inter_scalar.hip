@@ -55,8 +55,11 @@ struct ScalarInterCfg {
     static constexpr int NT = 64 * (NWC + NWP);
     static constexpr int NTILE = NB * NVB;             // X / Q S / u / o tiles
     static constexpr int ITL = (NTILE + NWC - 1) / NWC;
-    static constexpr int NST = NCB * NVB;              // state tiles
-    static constexpr int IST = (NST + NWC - 1) / NWC;
+    // state tiles (cb, vb): wave w < NSW holds cb = CBW w .. CBW w + CBW-1
+    // for every vb, so the K^T fragments of a channel block and the u^T
+    // fragments of a column block are each read by as few waves as possible
+    static constexpr int CBW = 2;
+    static constexpr int NSW = NCB / CBW;
     // ring slot: k tile, v slice, T', decay scalars
     static constexpr int O_SK = 0;
     static constexpr int O_SV = O_SK + C * PK * ESZ;
@@ -91,7 +94,7 @@ __global__ void __launch_bounds__(Cfg::NT) kda_inter_scalar_kernel(InterParams p
     constexpr int NCB = Cfg::NCB, NVB = Cfg::NVB;
     constexpr int PK = Cfg::PK, PV = Cfg::PV, PC = Cfg::PC;
     constexpr int NWC = Cfg::NWC, NWP = Cfg::NWP;
-    constexpr int NTILE = Cfg::NTILE, ITL = Cfg::ITL, NST = Cfg::NST, IST = Cfg::IST;
+    constexpr int NTILE = Cfg::NTILE, ITL = Cfg::ITL, CBW = Cfg::CBW, NSW = Cfg::NSW;
     constexpr int ESZ = Cfg::ESZ, W = F::W, KS = F::KS;
     constexpr int SLOT = Cfg::SLOT;
     constexpr RecLayout RL = rec_layout_thin(C, ESZ);
@@ -277,23 +280,23 @@ __global__ void __launch_bounds__(Cfg::NT) kda_inter_scalar_kernel(InterParams p
     static_assert(NWC % NB == 0, "whole groups of NB waves");
     const int jw = w / NB;
     const int Rw = (jw & 1) ? NB - 1 - w % NB : w % NB;
-    floatx4 Sreg[IST];
+    static_assert(NCB % CBW == 0 && NSW <= NWC, "state tile blocks");
+    floatx4 Sreg[CBW][NVB];
 #pragma unroll
-    for (int i = 0; i < IST; ++i) {
-        Sreg[i] = floatx4{0.f, 0.f, 0.f, 0.f};
-        const int t = w + NWC * i;
-        if (t < NST && prm.S_in) {
-            const float* s0 = prm.S_in + (int64_t)bh * DK * DV + v0;
-            const int cb = t % NCB, vb = t / NCB;
+    for (int a = 0; a < CBW; ++a)
 #pragma unroll
-            for (int e = 0; e < 4; ++e) Sreg[i][e] = s0[(16 * cb + 4 * lq + e) * DV + 16 * vb + lr];
+        for (int b = 0; b < NVB; ++b) {
+            Sreg[a][b] = floatx4{0.f, 0.f, 0.f, 0.f};
+            if (w < NSW) {
+                const int cb = CBW * w + a;
+                if (prm.S_in) {
+                    const float* s0 = prm.S_in + (int64_t)bh * DK * DV + v0;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) Sreg[a][b][e] = s0[(16 * cb + 4 * lq + e) * DV + 16 * b + lr];
+                }
+                store_acc_transposed<E>(sST + (16 * b) * PK + 16 * cb, PK, Sreg[a][b]);
+            }
         }
-    }
-#pragma unroll
-    for (int i = 0; i < IST; ++i) {
-        const int t = w + NWC * i;
-        if (t < NST) store_acc_transposed<E>(sST + (16 * (t / NCB)) * PK + 16 * (t % NCB), PK, Sreg[i]);
-    }
     // blocks of P above the diagonal stay zero
     for (int i = tid; i < C * PC; i += 64 * NWC) sP[i] = from_f32<E>(0.f);
     __syncthreads();
@@ -401,26 +404,26 @@ __global__ void __launch_bounds__(Cfg::NT) kda_inter_scalar_kernel(InterParams p
 
         // ---------------- phase 3: S update, o ----------------
         const float gnv = rs[3 * C];
-        {
-            // every state tile of this wave has the same channel block
-            // (NCB divides NWC), so its K^T fragments are read once
-            static_assert(NWC % NCB == 0, "state tiles of a wave share cb");
+        if (w < NSW) {
             constexpr int NKP = C / KS;
-            const int cb = w % NCB;
-            typename F::T kt[NKP];
+            typename F::T kt[CBW][NKP];
 #pragma unroll
-            for (int kk = 0; kk < NKP; ++kk) kt[kk] = load_frag_tr(sK, PK, KS * kk, 16 * cb);
+            for (int a = 0; a < CBW; ++a)
 #pragma unroll
-            for (int i = 0; i < IST; ++i) {
-                const int t = w + NWC * i;
-                if (t < NST) {
-                    const int vb = t / NCB;
-                    floatx4 acc = Sreg[i] * gnv;
-                    const E* pu = sUHT + (16 * vb + lr) * PC + W * lq;
+                for (int kk = 0; kk < NKP; ++kk) kt[a][kk] = load_frag_tr(sK, PK, KS * kk, 16 * (CBW * w + a));
 #pragma unroll
-                    for (int kk = 0; kk < NKP; ++kk) acc = F::mma(acc, kt[kk], F::load(pu + KS * kk));
-                    Sreg[i] = acc;
-                    store_acc_transposed<E>(sST + (16 * vb) * PK + 16 * cb, PK, acc);
+            for (int b = 0; b < NVB; ++b) {
+                const E* pu = sUHT + (16 * b + lr) * PC + W * lq;
+                typename F::T uf[NKP];
+#pragma unroll
+                for (int kk = 0; kk < NKP; ++kk) uf[kk] = F::load(pu + KS * kk);
+#pragma unroll
+                for (int a = 0; a < CBW; ++a) {
+                    floatx4 acc = Sreg[a][b] * gnv;
+#pragma unroll
+                    for (int kk = 0; kk < NKP; ++kk) acc = F::mma(acc, kt[a][kk], uf[kk]);
+                    Sreg[a][b] = acc;
+                    store_acc_transposed<E>(sST + (16 * b) * PK + 16 * (CBW * w + a), PK, acc);
                 }
             }
         }
@@ -449,17 +452,16 @@ __global__ void __launch_bounds__(Cfg::NT) kda_inter_scalar_kernel(InterParams p
     }
 
     // ---- state out --------------------------------------------------------------
-    if (prm.S_out) {
+    if (prm.S_out && w < NSW) {
         float* so = prm.S_out + (int64_t)bh * DK * DV + v0;
 #pragma unroll
-        for (int i = 0; i < IST; ++i) {
-            const int t = w + NWC * i;
-            if (t < NST) {
-                const int cb = t % NCB, vb = t / NCB;
+        for (int a = 0; a < CBW; ++a)
 #pragma unroll
-                for (int e = 0; e < 4; ++e) so[(16 * cb + 4 * lq + e) * DV + 16 * vb + lr] = Sreg[i][e];
+            for (int b = 0; b < NVB; ++b) {
+                const int cb = CBW * w + a;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) so[(16 * cb + 4 * lq + e) * DV + 16 * b + lr] = Sreg[a][b][e];
             }
-        }
     }
 }
 
