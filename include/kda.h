@@ -128,6 +128,29 @@ int kda_decode_step(const kda_shape* shape, const void* q, const void* k, const 
                     void* hip_stream);
 
 /*
+ * Decode step over a pool of states, for serving: sequence b of this step
+ * (shape->B sequences, shape->L == 1) reads and updates state slot slots[b]
+ * of S_pool, so a server keeps one state per live request and steps any
+ * subset of them without gathering or scattering states ("22,580: From GPT-2
+ * to Kimi K3", section 5.2: the fixed-size state is the whole per-request
+ * cache).  Same recurrence and the same q, k, v, log_alpha, beta, o layouts
+ * as kda_decode_step.
+ *
+ *   S_pool   [n_slots,H,dk,dv] fp32, updated in place at the used slots only.
+ *   n_slots  number of states in the pool (>= 0).
+ *   slots    device int32 [B]: the slot of each sequence.  A value outside
+ *            [0, n_slots) marks an idle sequence: its o is written as zeros
+ *            and no state is read or written.  Two sequences of one call must
+ *            not share a slot (their updates would race); this is not checked,
+ *            since slots lives in device memory.  4-byte aligned.
+ * Errors as kda_decode_step, plus KDA_ERR_NULL for slots == NULL (B*H > 0)
+ * and KDA_ERR_SHAPE for n_slots < 0.  slots must not overlap o or S_pool.
+ */
+int kda_decode_step_slots(const kda_shape* shape, const void* q, const void* k, const void* v,
+                          const void* log_alpha, const void* beta, float* S_pool,
+                          int64_t n_slots, const int32_t* slots, void* o, void* hip_stream);
+
+/*
  * Kernel timing, for measurement tools (not part of the computation).  While
  * timing is on, every kernel that kda_chunk_fwd or kda_decode_step launches is
  * bracketed by two HIP events recorded on the call's stream; the event pairs

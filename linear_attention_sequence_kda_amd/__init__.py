@@ -5,12 +5,13 @@ The compute path is libkda.so (hand-written HIP for gfx950, C ABI in
 
     o, S_final = chunk_fwd(q, k, v, log_alpha, beta, S0)
     o          = decode_step(q, k, v, log_alpha, beta, S)   # S updated in place
+    o          = decode_step_slots(q, k, v, log_alpha, beta, S_pool, slots)
 
 ``inputs`` holds the seeded synthetic workloads.
 """
 
 from .binding import (KdaError, chunk_fwd, chunk_fwd_workspace_bytes, decode_step,  # noqa: F401
-                      library, timing_enable, timing_read, timing_reset)
+                      decode_step_slots, library, timing_enable, timing_read, timing_reset)
 
-__all__ = ["chunk_fwd", "chunk_fwd_workspace_bytes", "decode_step", "library", "KdaError",
-           "timing_enable", "timing_read", "timing_reset"]
+__all__ = ["chunk_fwd", "chunk_fwd_workspace_bytes", "decode_step", "decode_step_slots",
+           "library", "KdaError", "timing_enable", "timing_read", "timing_reset"]

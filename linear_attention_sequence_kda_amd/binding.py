@@ -57,6 +57,9 @@ def library() -> ctypes.CDLL:
         lib.kda_chunk_fwd_workspace_bytes.restype = sz
         lib.kda_decode_step.argtypes = [sp, vp, vp, vp, vp, vp, vp, vp, vp]
         lib.kda_decode_step.restype = ctypes.c_int
+        lib.kda_decode_step_slots.argtypes = [sp, vp, vp, vp, vp, vp, vp, ctypes.c_int64, vp, vp,
+                                              vp]
+        lib.kda_decode_step_slots.restype = ctypes.c_int
         lib.kda_strerror.argtypes = [ctypes.c_int]
         lib.kda_strerror.restype = ctypes.c_char_p
         lib.kda_last_error.argtypes = []
@@ -232,5 +235,41 @@ def decode_step(q, k, v, log_alpha, beta, S, *, o=None):
                      _dtype_code(log_alpha if log_alpha is not None else beta), mode)
     rc = library().kda_decode_step(ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(v),
                                    _ptr(log_alpha), _ptr(beta), _ptr(S), _ptr(o), _stream(v))
+    _check(rc)
+    return o
+
+
+def decode_step_slots(q, k, v, log_alpha, beta, S_pool, slots, *, o=None):
+    """One decode step where sequence b uses state slot slots[b] of S_pool.
+
+    q, k: [B,H,dk]; v: [B,H,dv]; log_alpha: None, [B,H] or [B,H,dk];
+    beta: [B,H]; S_pool: [n_slots,H,dk,dv] fp32, updated in place at the used
+    slots; slots: int32 [B] on the GPU (a slot outside [0, n_slots) marks an
+    idle sequence whose o is zero).  Returns o [B,H,dv].
+    """
+    torch = _torch()
+    B, H, dk = q.shape
+    dv = v.shape[-1]
+    if log_alpha is None:
+        mode = KDA_ALPHA_NONE
+    elif log_alpha.dim() == 2:
+        mode = KDA_ALPHA_HEAD
+    else:
+        mode = KDA_ALPHA_CHANNEL
+    for name, t in (("q", q), ("k", k), ("v", v), ("beta", beta), ("log_alpha", log_alpha),
+                    ("S_pool", S_pool), ("slots", slots)):
+        if t is not None:
+            _require(t, name)
+    if S_pool.dtype != torch.float32:
+        raise TypeError("S_pool must be float32")
+    if slots.dtype != torch.int32:
+        raise TypeError("slots must be int32")
+    if o is None:
+        o = torch.empty((B, H, dv), dtype=v.dtype, device=v.device)
+    shape = KdaShape(B, H, 1, dk, dv, _dtype_code(q),
+                     _dtype_code(log_alpha if log_alpha is not None else beta), mode)
+    rc = library().kda_decode_step_slots(ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(v),
+                                         _ptr(log_alpha), _ptr(beta), _ptr(S_pool),
+                                         S_pool.shape[0], _ptr(slots), _ptr(o), _stream(v))
     _check(rc)
     return o

@@ -162,6 +162,68 @@ Plan make_plan(const kda_shape* s) {
 
 }  // namespace
 
+namespace {
+// Shared body of kda_decode_step (slots == nullptr: S is [B,H,dk,dv]) and
+// kda_decode_step_slots (S is a pool of n_slots states).
+int decode_common(const char* who, const kda_shape* s, const void* q, const void* k,
+                  const void* v, const void* log_alpha, const void* beta, float* S,
+                  int64_t n_slots, const int32_t* slots, void* o, void* hip_stream) {
+    int rc = check_shape(s, true);
+    if (rc != KDA_OK) return rc;
+    const int64_t bh = s->B * s->H;
+    const int eq = elem_size(s->qkv_dtype), eg = elem_size(s->gate_dtype);
+    const bool has_alpha = s->alpha_mode != KDA_ALPHA_NONE;
+    if (slots && n_slots < 0) return KDA_ERR_SHAPE;
+    int64_t state_elems = 0;
+    if (!mul_ok(slots ? n_slots : s->B, s->H * s->dk * s->dv, &state_elems)) return KDA_ERR_SHAPE;
+    if (bh > 0) {
+        if (!q || !k || !v || !beta || !S || !o) return KDA_ERR_NULL;
+        if (has_alpha && !log_alpha) return KDA_ERR_NULL;
+    }
+    const void* ptrs[] = {q, k, v, has_alpha ? log_alpha : nullptr, beta, S, o};
+    for (const void* p : ptrs)
+        if (p && !aligned16(p)) return KDA_ERR_ALIGN;
+    if (slots && ((uintptr_t)slots & 3u)) return KDA_ERR_ALIGN;
+
+    const int64_t la_elems = s->alpha_mode == KDA_ALPHA_CHANNEL ? bh * s->dk : bh;
+    const Span sq = span_of(q, bh * s->dk * eq), sk = span_of(k, bh * s->dk * eq),
+               sv = span_of(v, bh * s->dv * eq),
+               sla = span_of(has_alpha ? log_alpha : nullptr, la_elems * eg),
+               sb = span_of(beta, bh * eg), ss = span_of(S, state_elems * 4),
+               so = span_of(o, bh * s->dv * eq),
+               si = span_of(slots, slots ? s->B * 4 : 0);
+    const Span inputs[] = {sq, sk, sv, sla, sb, si};
+    for (const Span& in : inputs)
+        if (overlaps(so, in) || overlaps(ss, in)) return KDA_ERR_ALIAS;
+    if (overlaps(so, ss)) return KDA_ERR_ALIAS;
+
+    if (bh == 0) return KDA_OK;
+    kda::DecodeParams prm;
+    prm.q = q;
+    prm.k = k;
+    prm.v = v;
+    prm.log_alpha = has_alpha ? log_alpha : nullptr;
+    prm.beta = beta;
+    prm.S = S;
+    prm.o = o;
+    prm.BH = (int)bh;
+    prm.gate_bf16 = s->gate_dtype == KDA_BF16;
+    prm.alpha_mode = s->alpha_mode;
+    prm.slots = slots;
+    prm.n_slots = n_slots;
+    prm.H = (int)s->H;
+    const hipStream_t stream = (hipStream_t)hip_stream;
+    hipError_t err = timed_launch(K_DECODE, stream, [&] {
+        return kda::launch_decode(prm, (int)s->dk, (int)s->dv, s->qkv_dtype == KDA_BF16, stream);
+    });
+    if (err != hipSuccess) {
+        g_last_error = std::string(who) + ": " + hipGetErrorString(err);
+        return KDA_ERR_HIP;
+    }
+    return KDA_OK;
+}
+}  // namespace
+
 extern "C" {
 
 int kda_abi_version(void) { return KDA_ABI_VERSION; }
@@ -295,54 +357,20 @@ int kda_chunk_fwd(const kda_shape* s, const void* q, const void* k, const void* 
     return KDA_OK;
 }
 
+
 int kda_decode_step(const kda_shape* s, const void* q, const void* k, const void* v,
                     const void* log_alpha, const void* beta, float* S, void* o,
                     void* hip_stream) {
-    int rc = check_shape(s, true);
-    if (rc != KDA_OK) return rc;
-    const int64_t bh = s->B * s->H;
-    const int eq = elem_size(s->qkv_dtype), eg = elem_size(s->gate_dtype);
-    const bool has_alpha = s->alpha_mode != KDA_ALPHA_NONE;
-    if (bh > 0) {
-        if (!q || !k || !v || !beta || !S || !o) return KDA_ERR_NULL;
-        if (has_alpha && !log_alpha) return KDA_ERR_NULL;
-    }
-    const void* ptrs[] = {q, k, v, has_alpha ? log_alpha : nullptr, beta, S, o};
-    for (const void* p : ptrs)
-        if (p && !aligned16(p)) return KDA_ERR_ALIGN;
+    return decode_common("kda_decode_step", s, q, k, v, log_alpha, beta, S, 0, nullptr, o,
+                         hip_stream);
+}
 
-    const int64_t la_elems = s->alpha_mode == KDA_ALPHA_CHANNEL ? bh * s->dk : bh;
-    const Span sq = span_of(q, bh * s->dk * eq), sk = span_of(k, bh * s->dk * eq),
-               sv = span_of(v, bh * s->dv * eq),
-               sla = span_of(has_alpha ? log_alpha : nullptr, la_elems * eg),
-               sb = span_of(beta, bh * eg), ss = span_of(S, bh * s->dk * s->dv * 4),
-               so = span_of(o, bh * s->dv * eq);
-    const Span inputs[] = {sq, sk, sv, sla, sb};
-    for (const Span& in : inputs)
-        if (overlaps(so, in) || overlaps(ss, in)) return KDA_ERR_ALIAS;
-    if (overlaps(so, ss)) return KDA_ERR_ALIAS;
-
-    if (bh == 0) return KDA_OK;
-    kda::DecodeParams prm;
-    prm.q = q;
-    prm.k = k;
-    prm.v = v;
-    prm.log_alpha = has_alpha ? log_alpha : nullptr;
-    prm.beta = beta;
-    prm.S = S;
-    prm.o = o;
-    prm.BH = (int)bh;
-    prm.gate_bf16 = s->gate_dtype == KDA_BF16;
-    prm.alpha_mode = s->alpha_mode;
-    const hipStream_t stream = (hipStream_t)hip_stream;
-    hipError_t err = timed_launch(K_DECODE, stream, [&] {
-        return kda::launch_decode(prm, (int)s->dk, (int)s->dv, s->qkv_dtype == KDA_BF16, stream);
-    });
-    if (err != hipSuccess) {
-        g_last_error = std::string("kda_decode_step: ") + hipGetErrorString(err);
-        return KDA_ERR_HIP;
-    }
-    return KDA_OK;
+int kda_decode_step_slots(const kda_shape* s, const void* q, const void* k, const void* v,
+                          const void* log_alpha, const void* beta, float* S_pool,
+                          int64_t n_slots, const int32_t* slots, void* o, void* hip_stream) {
+    if (s && !slots && s->B * s->H > 0) return KDA_ERR_NULL;
+    return decode_common("kda_decode_step_slots", s, q, k, v, log_alpha, beta, S_pool, n_slots,
+                         slots, o, hip_stream);
 }
 
 int kda_timing_enable(int on) {

@@ -9,7 +9,8 @@
 // o = q (S~ + k^T u) = r_q + (q . k) u, so the state is read once and written
 // once.  The step is bound by that 8 dk dv bytes of HBM traffic per head.
 //
-// One 256-thread workgroup per head.  Thread (row group rg, column group cg)
+// One 256-thread workgroup per head (per (sequence, head) in slot mode, where
+// the state comes from a pool through the sequence's slot index).  Thread (row group rg, column group cg)
 // holds RPT rows x 4 columns of S in registers (float4 loads: each row of a
 // wave's access is 512 contiguous bytes), forms partial r_k / r_q over its
 // rows, and the row groups are summed through LDS.  The new state is written
@@ -38,6 +39,22 @@ __global__ void __launch_bounds__(256) kda_decode_kernel(DecodeParams p) {
     const int64_t bh = blockIdx.x;
     const bool gbf = p.gate_bf16 != 0;
 
+    float* S = p.S + bh * DK * DV;
+    if (p.slots) {
+        // state pool: (slot, h) of sequence b; an idle sequence writes o = 0
+        const int64_t b = bh / p.H, h = bh - b * p.H;
+        const int64_t slot = p.slots[b];
+        if (slot < 0 || slot >= p.n_slots) {
+            if (tid < DV / 4) {
+                E* po = (E*)p.o + bh * DV + 4 * tid;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) po[e] = from_f32<E>(0.f);
+            }
+            return;
+        }
+        S = p.S + (slot * p.H + h) * DK * DV;
+    }
+
     if (tid < DK) {
         sq[tid] = to_f32(((const E*)p.q)[bh * DK + tid]);
         sk[tid] = to_f32(((const E*)p.k)[bh * DK + tid]);
@@ -51,7 +68,6 @@ __global__ void __launch_bounds__(256) kda_decode_kernel(DecodeParams p) {
     }
     const float beta = gbf ? (float)((const bf16*)p.beta)[bh] : ((const float*)p.beta)[bh];
 
-    float* S = p.S + bh * DK * DV;
     floatx4 s[RPT];
 #pragma unroll
     for (int i = 0; i < RPT; ++i)

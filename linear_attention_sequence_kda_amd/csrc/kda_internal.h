@@ -117,11 +117,17 @@ struct DecodeParams {
     const void* v;          // [BH, DV]
     const void* log_alpha;  // [BH, DK] | [BH] | unused
     const void* beta;       // [BH]
-    float* S;               // [BH, DK, DV], updated in place
+    float* S;               // [BH, DK, DV] (or a pool, see slots), updated in place
     void* o;                // [BH, DV]
     int BH;
     int gate_bf16;
     int alpha_mode;
+    // slot mode: sequence b's state is S + (slots[b] * H + h) * DK * DV, a
+    // pool of n_slots states; a slot outside [0, n_slots) marks an idle
+    // sequence (o = 0, no state touched).  slots == nullptr: S is [BH, ...].
+    const int32_t* slots = nullptr;
+    int64_t n_slots = 0;
+    int H = 1;
 };
 
 // State-column slice width the inter-chunk kernel uses for this problem.

@@ -181,3 +181,22 @@ def test_timing_calls_without_launches(lib):
     finally:
         assert lib.kda_timing_enable(0) == 0
         assert lib.kda_timing_reset() == 0
+
+
+def decode_slots(lib, s, b, n_slots=4, slots=None):
+    return lib.kda_decode_step_slots(ctypes.byref(s) if s is not None else None, b["q"], b["k"],
+                                     b["v"], b["la"], b["beta"], b["S0"], n_slots,
+                                     b["ws"] if slots is None else slots, b["o"], None)
+
+
+def test_decode_slots_host_checks(lib):
+    s = shape(L=1)
+    b = bufs()
+    assert lib.kda_decode_step_slots(ctypes.byref(s), b["q"], b["k"], b["v"], b["la"], b["beta"],
+                                     b["S0"], 4, None, b["o"], None) == 1
+    assert decode_slots(lib, s, b, n_slots=-1) == 2
+    assert decode_slots(lib, shape(L=2), b) == 2
+    assert decode_slots(lib, s, b, slots=b["ws"] + 2) == 5
+    assert decode_slots(lib, s, b, slots=b["o"]) == 7            # slots overlap o
+    assert decode_slots(lib, s, dict(b, o=b["S0"] + 64)) == 7    # o inside the pool
+    assert decode_slots(lib, shape(B=0, L=1), b) == 0           # empty: nothing to do

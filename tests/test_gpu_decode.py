@@ -116,3 +116,46 @@ def test_decode_deterministic():
     o2 = kda.decode_step(*args, S2)
     torch.cuda.synchronize()
     assert torch.equal(o1, o2) and torch.equal(S1, S2)
+
+
+@pytest.mark.parametrize("mode", ["channel", "head"])
+def test_decode_state_pool_slots(mode):
+    """kda_decode_step_slots over a pool equals kda_decode_step on the gathered
+    states, scatters back only the used slots, and writes o = 0 for an idle
+    sequence (slot -1); both also meet the oracle."""
+    import torch
+    kda = _kda()
+    B, H, n_slots = 5, 4, 8
+    w = gen.custom(B=B, H=H, L=1, dk=128, dv=128, qkv_dtype="bf16", gate_dtype="f32",
+                   alpha_mode=mode, seed=77).replace(decode_steps=1)
+    pool_w = w.replace(B=n_slots)
+    pool0 = to_dev(gen.decode_state(pool_w), "f32")
+    xt = gen.decode_inputs(w, 0)
+    d = [to_dev(xt[n], w.qkv_dtype if n in ("q", "k", "v") else w.gate_dtype)
+         for n in ("q", "k", "v", "log_alpha", "beta")]
+    slots_h = [6, 1, -1, 3, 0]
+    slots = torch.tensor(slots_h, dtype=torch.int32, device="cuda:0")
+    say(f"decode slots {mode}")
+    pool = pool0.clone()
+    o = kda.decode_step_slots(*d, pool, slots)
+    live = [b for b, sl in enumerate(slots_h) if sl >= 0]
+    S_g = pool0[[slots_h[b] for b in live]].contiguous()
+    o_ref = kda.decode_step(*[t[live].contiguous() for t in d], S_g)
+    torch.cuda.synchronize()
+    assert torch.equal(o[live], o_ref)
+    assert torch.count_nonzero(o[2]) == 0
+    for b in live:
+        assert torch.equal(pool[slots_h[b]], S_g[live.index(b)])
+    untouched = [sl for sl in range(n_slots) if sl not in slots_h]
+    assert torch.equal(pool[untouched], pool0[untouched])
+    # oracle on the live sequences
+    N = len(live) * H
+    f = lambda a: None if a is None else np.ascontiguousarray(a[live]).reshape((N,) + a.shape[2:])
+    S_np = gen.decode_state(pool_w)[[slots_h[b] for b in live]].reshape(N, 128, 128)
+    o_or, S_or = oracle.forward(f(xt["q"])[:, None], f(xt["k"])[:, None], f(xt["v"])[:, None],
+                                None if xt["log_alpha"] is None else f(xt["log_alpha"])[:, None],
+                                f(xt["beta"])[:, None], S_np, qkv_dtype=w.qkv_dtype,
+                                gate_dtype=w.gate_dtype, alpha_mode=w.alpha_mode)
+    assert oracle.slab_error(to_f64(o[live]).reshape(N, 1, 128), o_or, 1) <= TOL["bf16"]
+    S_new = torch.stack([pool[slots_h[b]] for b in live]).reshape(N, 128, 128)
+    assert oracle.slab_error(to_f64(S_new), S_or, 1) <= TOL["bf16"]
