@@ -19,6 +19,11 @@ Recipe (shared by every workload):
 * beta: sigmoid(N(0, 1));
 * S0: N(0, std) in fp32 when the workload has one, otherwise absent (zero).
 
+Raw mode (``raw=True``, the inputs of the fused preprocessing) draws from the
+same streams and stores the values before the last step: q, k are the N(0, 1)
+rows unnormalised, log_alpha holds g ~ N(mu, sigma) (the op takes
+ln alpha = -exp(g)) and beta holds the N(0, 1) logits.
+
 N(mu, sigma) names the mean and the standard deviation.  Storage rounding is
 fp64 -> fp32 (round to nearest even) and, for bf16 tensors, fp32 -> bf16
 (round to nearest even).  bf16 tensors are returned as their raw ``uint16``
@@ -136,30 +141,36 @@ def _rng(*entropy: int) -> np.random.Generator:
         [int(e) for e in entropy])))
 
 
-def _unit_rows(rng: np.random.Generator, shape) -> np.ndarray:
+def _unit_rows(rng: np.random.Generator, shape, raw: bool = False) -> np.ndarray:
     x = rng.standard_normal(shape)
+    if raw:
+        return x
     n = np.sqrt(np.sum(x * x, axis=-1, keepdims=True))
     return x / n
 
 
-def _log_alpha(rng, shape, mu, sigma) -> np.ndarray:
-    return -np.exp(rng.normal(mu, sigma, size=shape))
+def _log_alpha(rng, shape, mu, sigma, raw: bool = False) -> np.ndarray:
+    g = rng.normal(mu, sigma, size=shape)
+    return g if raw else -np.exp(g)
 
 
-def _sigmoid_normal(rng, shape) -> np.ndarray:
-    return 1.0 / (1.0 + np.exp(-rng.standard_normal(shape)))
+def _sigmoid_normal(rng, shape, raw: bool = False) -> np.ndarray:
+    x = rng.standard_normal(shape)
+    return x if raw else 1.0 / (1.0 + np.exp(-x))
 
 
-def head_inputs(w: Workload, b: int, h: int) -> dict:
+def head_inputs(w: Workload, b: int, h: int, raw: bool = False) -> dict:
     """Inputs of one (b, h) head of a prefill workload, in storage types.
 
     Returns q [L,dk], k [L,dk], v [L,dv], log_alpha ([L,dk], [L] or None),
-    beta [L] and S0 ([dk,dv] float32 or None).
+    beta [L] and S0 ([dk,dv] float32 or None).  ``raw``: see the module notes.
     """
     L, dk, dv = w.L, w.dk, w.dv
     out = {
-        "q": to_storage(_unit_rows(_rng(w.seed, _TENSOR_IDS["q"], b, h), (L, dk)), w.qkv_dtype),
-        "k": to_storage(_unit_rows(_rng(w.seed, _TENSOR_IDS["k"], b, h), (L, dk)), w.qkv_dtype),
+        "q": to_storage(_unit_rows(_rng(w.seed, _TENSOR_IDS["q"], b, h), (L, dk), raw),
+                        w.qkv_dtype),
+        "k": to_storage(_unit_rows(_rng(w.seed, _TENSOR_IDS["k"], b, h), (L, dk), raw),
+                        w.qkv_dtype),
         "v": to_storage(_rng(w.seed, _TENSOR_IDS["v"], b, h).standard_normal((L, dv)), w.qkv_dtype),
     }
     if w.alpha_mode == ALPHA_NONE:
@@ -167,9 +178,9 @@ def head_inputs(w: Workload, b: int, h: int) -> dict:
     else:
         shape = (L, dk) if w.alpha_mode == ALPHA_CHANNEL else (L,)
         out["log_alpha"] = to_storage(
-            _log_alpha(_rng(w.seed, _TENSOR_IDS["log_alpha"], b, h), shape, w.la_mu, w.la_sigma),
-            w.gate_dtype)
-    out["beta"] = to_storage(_sigmoid_normal(_rng(w.seed, _TENSOR_IDS["beta"], b, h), (L,)),
+            _log_alpha(_rng(w.seed, _TENSOR_IDS["log_alpha"], b, h), shape, w.la_mu, w.la_sigma,
+                       raw), w.gate_dtype)
+    out["beta"] = to_storage(_sigmoid_normal(_rng(w.seed, _TENSOR_IDS["beta"], b, h), (L,), raw),
                              w.gate_dtype)
     if w.s0_std is None:
         out["S0"] = None
@@ -179,7 +190,7 @@ def head_inputs(w: Workload, b: int, h: int) -> dict:
     return out
 
 
-def prefill_inputs(w: Workload, heads=None, threads: int = 8) -> dict:
+def prefill_inputs(w: Workload, heads=None, threads: int = 8, raw: bool = False) -> dict:
     """Stack head_inputs over all (b, h) (or the given list of (b, h) pairs).
 
     With ``heads=None`` the arrays are [B, H, ...]; with a list of n pairs they
@@ -190,9 +201,9 @@ def prefill_inputs(w: Workload, heads=None, threads: int = 8) -> dict:
     if threads > 1 and len(pairs) > 1:
         from concurrent.futures import ThreadPoolExecutor
         with ThreadPoolExecutor(min(threads, len(pairs))) as ex:
-            blocks = list(ex.map(lambda bh: head_inputs(w, *bh), pairs))
+            blocks = list(ex.map(lambda bh: head_inputs(w, *bh, raw=raw), pairs))
     else:
-        blocks = [head_inputs(w, b, h) for (b, h) in pairs]
+        blocks = [head_inputs(w, b, h, raw=raw) for (b, h) in pairs]
     out = {}
     for key in ("q", "k", "v", "log_alpha", "beta", "S0"):
         if blocks[0][key] is None:
@@ -213,13 +224,15 @@ def decode_state(w: Workload) -> Optional[np.ndarray]:
             * w.s0_std).astype(np.float32)
 
 
-def decode_inputs(w: Workload, step: int) -> dict:
+def decode_inputs(w: Workload, step: int, raw: bool = False) -> dict:
     """Inputs of one decode step: q,k [B,H,dk], v [B,H,dv], log_alpha
-    ([B,H,dk], [B,H] or None), beta [B,H]."""
+    ([B,H,dk], [B,H] or None), beta [B,H].  ``raw``: see the module notes."""
     B, H, dk, dv = w.B, w.H, w.dk, w.dv
     out = {
-        "q": to_storage(_unit_rows(_rng(w.seed, _TENSOR_IDS["q"], step), (B, H, dk)), w.qkv_dtype),
-        "k": to_storage(_unit_rows(_rng(w.seed, _TENSOR_IDS["k"], step), (B, H, dk)), w.qkv_dtype),
+        "q": to_storage(_unit_rows(_rng(w.seed, _TENSOR_IDS["q"], step), (B, H, dk), raw),
+                        w.qkv_dtype),
+        "k": to_storage(_unit_rows(_rng(w.seed, _TENSOR_IDS["k"], step), (B, H, dk), raw),
+                        w.qkv_dtype),
         "v": to_storage(_rng(w.seed, _TENSOR_IDS["v"], step).standard_normal((B, H, dv)), w.qkv_dtype),
     }
     if w.alpha_mode == ALPHA_NONE:
@@ -227,10 +240,10 @@ def decode_inputs(w: Workload, step: int) -> dict:
     else:
         shape = (B, H, dk) if w.alpha_mode == ALPHA_CHANNEL else (B, H)
         out["log_alpha"] = to_storage(
-            _log_alpha(_rng(w.seed, _TENSOR_IDS["log_alpha"], step), shape, w.la_mu, w.la_sigma),
-            w.gate_dtype)
-    out["beta"] = to_storage(_sigmoid_normal(_rng(w.seed, _TENSOR_IDS["beta"], step), (B, H)),
-                             w.gate_dtype)
+            _log_alpha(_rng(w.seed, _TENSOR_IDS["log_alpha"], step), shape, w.la_mu, w.la_sigma,
+                       raw), w.gate_dtype)
+    out["beta"] = to_storage(_sigmoid_normal(_rng(w.seed, _TENSOR_IDS["beta"], step), (B, H),
+                                             raw), w.gate_dtype)
     return out
 
 

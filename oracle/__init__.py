@@ -20,6 +20,9 @@ Contents
                        batched indexing read per chunk.
 ``forward_substitution`` the pages' in-place inversion of (I + A).
 ``slab_error``         the parity metric.
+``preprocess``         the token mixer's input steps (L2-normalized q and k,
+                       sigmoid beta, alpha = exp(-exp(g))) in fp64, applied to
+                       raw stored inputs before ``forward``.
 
 Every function takes fp64 NumPy arrays for one head unless said otherwise.
 """
@@ -37,9 +40,11 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "kda_oracle.c")
 _LIB = os.path.join(_HERE, "libkda_oracle.so")
 
-F32, BF16 = 0, 1
+F32, BF16, F64 = 0, 1, 2
 ALPHA_NONE, ALPHA_HEAD, ALPHA_CHANNEL = 0, 1, 2
-_DT = {"f32": F32, "bf16": BF16}
+_DT = {"f32": F32, "bf16": BF16, "f64": F64}
+# input preprocessing bits (the same meaning as the library's input flags)
+NORM_QK, BETA_LOGIT, GATE_RAW = 1, 2, 4
 _AM = {"none": ALPHA_NONE, "head": ALPHA_HEAD, "channel": ALPHA_CHANNEL}
 
 
@@ -117,6 +122,63 @@ def forward(q, k, v, log_alpha, beta, S0=None, *, qkv_dtype="f32", gate_dtype="f
     if rc != 0:
         raise ValueError("kda_oracle_forward rejected its arguments")
     return o, sf
+
+
+# ---------------------------------------------------------------------------
+# input preprocessing of the token mixer (fp64)
+# ---------------------------------------------------------------------------
+
+def _widen(x, dtype: str):
+    """Stored values as fp64: float32 as is, bf16 bits shifted into float32."""
+    x = np.asarray(x)
+    if dtype == "bf16":
+        return (x.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    return x.astype(np.float64)
+
+
+def l2_normalize(x):
+    """x / max(|x|, 1e-12) over the last axis ("22,580: From GPT-2 to Kimi K3",
+    sections 5.1-5.2: the DeltaNet layer normalizes q and k so that reading a
+    stored key returns its value exactly; the 1e-12 floor keeps a zero row
+    zero)."""
+    x = np.asarray(x, dtype=np.float64)
+    n = np.sqrt(np.sum(x * x, axis=-1, keepdims=True))
+    return x / np.maximum(n, 1e-12)
+
+
+def sigmoid(x):
+    """1 / (1 + e^-x), evaluated on the side that does not overflow (the
+    write strength beta of the delta rule, same page, section 5.2)."""
+    x = np.asarray(x, dtype=np.float64)
+    e = np.exp(-np.abs(x))
+    return np.where(x >= 0, 1.0 / (1.0 + e), e / (1.0 + e))
+
+
+def log_alpha_of_raw(g):
+    """ln alpha = -exp(g), i.e. alpha = exp(-exp(g)) in (0, 1) ("22580: From
+    GPT-2 to Kimi K3, Explained", "Key code and formulas", "KDA (per-channel
+    alpha)")."""
+    return -np.exp(np.asarray(g, dtype=np.float64))
+
+
+def preprocess(q, k, v, log_alpha, beta, flags, *, qkv_dtype="f32", gate_dtype="f32"):
+    """Raw stored inputs -> fp64 inputs of the recurrence.
+
+    Each set bit applies one step: NORM_QK normalizes q and k per token over
+    d_k, BETA_LOGIT takes beta = sigmoid(beta), GATE_RAW takes
+    ln alpha = -exp(log_alpha).  Returns fp64 (q, k, v, log_alpha, beta) to
+    pass to ``forward`` with qkv_dtype = gate_dtype = "f64".
+    """
+    q, k, v = (_widen(t, qkv_dtype) for t in (q, k, v))
+    la = None if log_alpha is None else _widen(log_alpha, gate_dtype)
+    b = _widen(beta, gate_dtype)
+    if flags & NORM_QK:
+        q, k = l2_normalize(q), l2_normalize(k)
+    if flags & BETA_LOGIT:
+        b = sigmoid(b)
+    if flags & GATE_RAW and la is not None:
+        la = log_alpha_of_raw(la)
+    return q, k, v, la, b
 
 
 # ---------------------------------------------------------------------------

@@ -28,8 +28,10 @@ typedef struct {
     pthread_mutex_t mu;
 } job_t;
 
-/* exact widening of one stored element */
+/* exact widening of one stored element (fp64 inputs are values already
+ * preprocessed on the host in fp64) */
 static double load(const void* base, int64_t idx, int dtype) {
+    if (dtype == ORACLE_F64) return ((const double*)base)[idx];
     if (dtype == ORACLE_BF16) {
         uint16_t bits = ((const uint16_t*)base)[idx];
         uint32_t w = (uint32_t)bits << 16;
@@ -133,8 +135,8 @@ int kda_oracle_forward(int64_t B, int64_t H, int64_t L, int64_t dk, int64_t dv,
                        double* o, double* S_final, int nthreads) {
     if (B < 0 || H < 0 || L < 0 || dk <= 0 || dv <= 0) return -1;
     if (col0 < 0 || ncols < 0 || col0 + ncols > dv) return -1;
-    if (qkv_dtype != ORACLE_F32 && qkv_dtype != ORACLE_BF16) return -1;
-    if (gate_dtype != ORACLE_F32 && gate_dtype != ORACLE_BF16) return -1;
+    if (qkv_dtype < ORACLE_F32 || qkv_dtype > ORACLE_F64) return -1;
+    if (gate_dtype < ORACLE_F32 || gate_dtype > ORACLE_F64) return -1;
     if (alpha_mode < ORACLE_ALPHA_NONE || alpha_mode > ORACLE_ALPHA_CHANNEL) return -1;
     if (L > 0 && (!q || !k || !v || !beta)) return -1;
     if (L > 0 && alpha_mode != ORACLE_ALPHA_NONE && !log_alpha) return -1;

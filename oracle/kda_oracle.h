@@ -40,7 +40,7 @@
 extern "C" {
 #endif
 
-enum { ORACLE_F32 = 0, ORACLE_BF16 = 1 };
+enum { ORACLE_F32 = 0, ORACLE_BF16 = 1, ORACLE_F64 = 2 };
 enum { ORACLE_ALPHA_NONE = 0, ORACLE_ALPHA_HEAD = 1, ORACLE_ALPHA_CHANNEL = 2 };
 
 /*
