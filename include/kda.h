@@ -76,7 +76,31 @@ enum kda_status {
     KDA_ERR_WORKSPACE = 6,  /* workspace smaller than the size query returns  */
     KDA_ERR_ALIAS = 7,      /* an output overlaps an input, or S_final only
                                partly overlaps S0                             */
-    KDA_ERR_HIP = 8         /* a HIP launch failed; kda_last_error() has text */
+    KDA_ERR_HIP = 8,        /* a HIP launch failed; kda_last_error() has text */
+    KDA_ERR_FLAGS = 9       /* an unknown kda_input_flags bit                 */
+};
+
+/*
+ * Input preprocessing fused into the kernels' loads (kda_chunk_fwd_ex,
+ * kda_decode_step_ex, kda_decode_step_slots_ex).  The token mixer's layer feeds the recurrence with
+ * L2-normalized q and k, beta = sigmoid(x W_beta) and alpha = exp(-exp(g))
+ * ("22,580: From GPT-2 to Kimi K3" (yichencityu.github.io), section 5.2: the
+ * DeltaNet layer normalizes q and k, which makes reading a written key exact,
+ * and squashes beta with a sigmoid; "22580: From GPT-2 to Kimi K3, Explained"
+ * (lukebest.github.io), "Key code and formulas", "KDA (per-channel alpha)":
+ * alpha = exp(-exp(g))).
+ * With these bits the caller passes the raw values and the kernels apply the
+ * step as they load them, so no preprocessed copy goes through memory:
+ *   KDA_IN_NORM_QK     q, k are raw: the op uses q / max(|q|, 1e-12) and the
+ *                      same for k (L2 over d_k, per token and head)
+ *   KDA_IN_BETA_LOGIT  beta holds logits: the op uses sigmoid(beta)
+ *   KDA_IN_GATE_RAW    log_alpha holds g: the op uses ln(alpha) = -exp(g)
+ *                      (ignored with KDA_ALPHA_NONE)
+ */
+enum kda_input_flags {
+    KDA_IN_NORM_QK = 1,
+    KDA_IN_BETA_LOGIT = 2,
+    KDA_IN_GATE_RAW = 4
 };
 
 typedef struct kda_shape {
@@ -107,6 +131,13 @@ int kda_chunk_fwd(const kda_shape* shape, const void* q, const void* k, const vo
                   const void* log_alpha, const void* beta, const float* S0, void* o,
                   float* S_final, void* workspace, size_t workspace_bytes,
                   void* hip_stream);
+
+/* kda_chunk_fwd on raw inputs: flags is a set of kda_input_flags (0 gives
+ * kda_chunk_fwd exactly); KDA_ERR_FLAGS for an unknown bit.  Same workspace. */
+int kda_chunk_fwd_ex(const kda_shape* shape, uint32_t flags, const void* q, const void* k,
+                     const void* v, const void* log_alpha, const void* beta, const float* S0,
+                     void* o, float* S_final, void* workspace, size_t workspace_bytes,
+                     void* hip_stream);
 
 /* Bytes of device workspace kda_chunk_fwd needs for this shape (0 for a
  * shape the call would reject). */
@@ -174,6 +205,19 @@ int kda_decode_step_slots(const kda_shape* shape, const void* q, const void* k, 
 int kda_timing_enable(int on);
 int kda_timing_reset(void);
 int kda_timing_read(const char* kernel, int64_t* launches, double* total_ms);
+
+/* kda_decode_step and kda_decode_step_slots on raw inputs: flags is a set of
+ * kda_input_flags, as for kda_chunk_fwd_ex (0 gives the plain call exactly;
+ * KDA_ERR_FLAGS for an unknown bit, checked after the shape).  Every other
+ * argument, its layout, ownership and check is that of the plain call; the
+ * raw q and k are normalized per (b, h) over d_k, so no copy is written. */
+int kda_decode_step_ex(const kda_shape* shape, uint32_t flags, const void* q, const void* k,
+                       const void* v, const void* log_alpha, const void* beta, float* S, void* o,
+                       void* hip_stream);
+int kda_decode_step_slots_ex(const kda_shape* shape, uint32_t flags, const void* q,
+                             const void* k, const void* v, const void* log_alpha,
+                             const void* beta, float* S_pool, int64_t n_slots,
+                             const int32_t* slots, void* o, void* hip_stream);
 
 /* Static text for a kda_status code. */
 const char* kda_strerror(int status);

@@ -7,11 +7,16 @@ The compute path is libkda.so (hand-written HIP for gfx950, C ABI in
     o          = decode_step(q, k, v, log_alpha, beta, S)   # S updated in place
     o          = decode_step_slots(q, k, v, log_alpha, beta, S_pool, slots)
 
+Each takes ``flags=NORM_QK | BETA_LOGIT | GATE_RAW`` (any subset) to feed raw
+q, k, beta logits and gate pre-activations that the kernels preprocess.
+
 ``inputs`` holds the seeded synthetic workloads.
 """
 
-from .binding import (KdaError, chunk_fwd, chunk_fwd_workspace_bytes, decode_step,  # noqa: F401
-                      decode_step_slots, library, timing_enable, timing_read, timing_reset)
+from .binding import (BETA_LOGIT, GATE_RAW, NORM_QK, KdaError, chunk_fwd,  # noqa: F401
+                      chunk_fwd_workspace_bytes, decode_step, decode_step_slots, library,
+                      timing_enable, timing_read, timing_reset)
 
 __all__ = ["chunk_fwd", "chunk_fwd_workspace_bytes", "decode_step", "decode_step_slots",
-           "library", "KdaError", "timing_enable", "timing_read", "timing_reset"]
+           "library", "KdaError", "timing_enable", "timing_read", "timing_reset", "NORM_QK",
+           "BETA_LOGIT", "GATE_RAW"]

@@ -21,7 +21,9 @@ KDA_F32, KDA_BF16 = 0, 1
 KDA_ALPHA_NONE, KDA_ALPHA_HEAD, KDA_ALPHA_CHANNEL = 0, 1, 2
 STATUS = {0: "KDA_OK", 1: "KDA_ERR_NULL", 2: "KDA_ERR_SHAPE", 3: "KDA_ERR_DTYPE",
           4: "KDA_ERR_ALPHA_MODE", 5: "KDA_ERR_ALIGN", 6: "KDA_ERR_WORKSPACE",
-          7: "KDA_ERR_ALIAS", 8: "KDA_ERR_HIP"}
+          7: "KDA_ERR_ALIAS", 8: "KDA_ERR_HIP", 9: "KDA_ERR_FLAGS"}
+# kda_input_flags: preprocessing applied by the kernels as they load raw inputs
+NORM_QK, BETA_LOGIT, GATE_RAW = 1, 2, 4
 
 
 class KdaShape(ctypes.Structure):
@@ -60,6 +62,14 @@ def library() -> ctypes.CDLL:
         lib.kda_decode_step_slots.argtypes = [sp, vp, vp, vp, vp, vp, vp, ctypes.c_int64, vp, vp,
                                               vp]
         lib.kda_decode_step_slots.restype = ctypes.c_int
+        u32 = ctypes.c_uint32
+        lib.kda_chunk_fwd_ex.argtypes = [sp, u32, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+        lib.kda_chunk_fwd_ex.restype = ctypes.c_int
+        lib.kda_decode_step_ex.argtypes = [sp, u32, vp, vp, vp, vp, vp, vp, vp, vp]
+        lib.kda_decode_step_ex.restype = ctypes.c_int
+        lib.kda_decode_step_slots_ex.argtypes = [sp, u32, vp, vp, vp, vp, vp, vp, ctypes.c_int64,
+                                                 vp, vp, vp]
+        lib.kda_decode_step_slots_ex.restype = ctypes.c_int
         lib.kda_strerror.argtypes = [ctypes.c_int]
         lib.kda_strerror.restype = ctypes.c_char_p
         lib.kda_last_error.argtypes = []
@@ -168,7 +178,8 @@ def _chunk_shape(q, v, log_alpha, beta) -> KdaShape:
 
 
 def chunk_fwd(q, k, v, log_alpha, beta, S0=None, *, output_final_state: bool = True,
-              o=None, S_final=None, workspace=None) -> Tuple[object, Optional[object]]:
+              o=None, S_final=None, workspace=None,
+              flags: Optional[int] = None) -> Tuple[object, Optional[object]]:
     """Chunkwise prefill: returns (o [B,H,L,dv], S_final [B,H,dk,dv] fp32 or None).
 
     q, k: [B,H,L,dk]; v: [B,H,L,dv] (bf16 or fp32, same dtype);
@@ -178,6 +189,8 @@ def chunk_fwd(q, k, v, log_alpha, beta, S0=None, *, output_final_state: bool = T
     ``o`` / ``S_final`` may be given to write into existing buffers
     (S_final may be S0 itself); ``workspace`` may be a uint8 GPU tensor of at
     least chunk_fwd_workspace_bytes() bytes (else one is allocated per call).
+    ``flags`` (a set of NORM_QK | BETA_LOGIT | GATE_RAW) calls kda_chunk_fwd_ex
+    on raw inputs; None calls kda_chunk_fwd.
     """
     torch = _torch()
     B, H, L, dk = q.shape
@@ -200,19 +213,23 @@ def chunk_fwd(q, k, v, log_alpha, beta, S0=None, *, output_final_state: bool = T
     else:
         _require(workspace, "workspace")
     ws_given = workspace.numel() * workspace.element_size() if workspace is not None else 0
-    rc = lib.kda_chunk_fwd(ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha),
-                           _ptr(beta), _ptr(S0), _ptr(o),
-                           _ptr(S_final) if output_final_state else None,
-                           _ptr(workspace), ws_given, _stream(v))
+    args = (_ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(beta), _ptr(S0), _ptr(o),
+            _ptr(S_final) if output_final_state else None, _ptr(workspace), ws_given,
+            _stream(v))
+    if flags is None:
+        rc = lib.kda_chunk_fwd(ctypes.byref(shape), *args)
+    else:
+        rc = lib.kda_chunk_fwd_ex(ctypes.byref(shape), flags, *args)
     _check(rc)
     return o, (S_final if output_final_state else None)
 
 
-def decode_step(q, k, v, log_alpha, beta, S, *, o=None):
+def decode_step(q, k, v, log_alpha, beta, S, *, o=None, flags: Optional[int] = None):
     """One decode step for every (b, h); S [B,H,dk,dv] fp32 is updated in place.
 
     q, k: [B,H,dk]; v: [B,H,dv]; log_alpha: None, [B,H] or [B,H,dk];
-    beta: [B,H].  Returns o [B,H,dv].
+    beta: [B,H].  Returns o [B,H,dv].  ``flags`` as in chunk_fwd
+    (kda_decode_step_ex).
     """
     torch = _torch()
     B, H, dk = q.shape
@@ -233,19 +250,25 @@ def decode_step(q, k, v, log_alpha, beta, S, *, o=None):
         o = torch.empty((B, H, dv), dtype=v.dtype, device=v.device)
     shape = KdaShape(B, H, 1, dk, dv, _dtype_code(q),
                      _dtype_code(log_alpha if log_alpha is not None else beta), mode)
-    rc = library().kda_decode_step(ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(v),
-                                   _ptr(log_alpha), _ptr(beta), _ptr(S), _ptr(o), _stream(v))
+    args = (_ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(beta), _ptr(S), _ptr(o),
+            _stream(v))
+    if flags is None:
+        rc = library().kda_decode_step(ctypes.byref(shape), *args)
+    else:
+        rc = library().kda_decode_step_ex(ctypes.byref(shape), flags, *args)
     _check(rc)
     return o
 
 
-def decode_step_slots(q, k, v, log_alpha, beta, S_pool, slots, *, o=None):
+def decode_step_slots(q, k, v, log_alpha, beta, S_pool, slots, *, o=None,
+                      flags: Optional[int] = None):
     """One decode step where sequence b uses state slot slots[b] of S_pool.
 
     q, k: [B,H,dk]; v: [B,H,dv]; log_alpha: None, [B,H] or [B,H,dk];
     beta: [B,H]; S_pool: [n_slots,H,dk,dv] fp32, updated in place at the used
     slots; slots: int32 [B] on the GPU (a slot outside [0, n_slots) marks an
-    idle sequence whose o is zero).  Returns o [B,H,dv].
+    idle sequence whose o is zero).  Returns o [B,H,dv].  ``flags`` as in
+    chunk_fwd (kda_decode_step_slots_ex).
     """
     torch = _torch()
     B, H, dk = q.shape
@@ -268,8 +291,11 @@ def decode_step_slots(q, k, v, log_alpha, beta, S_pool, slots, *, o=None):
         o = torch.empty((B, H, dv), dtype=v.dtype, device=v.device)
     shape = KdaShape(B, H, 1, dk, dv, _dtype_code(q),
                      _dtype_code(log_alpha if log_alpha is not None else beta), mode)
-    rc = library().kda_decode_step_slots(ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(v),
-                                         _ptr(log_alpha), _ptr(beta), _ptr(S_pool),
-                                         S_pool.shape[0], _ptr(slots), _ptr(o), _stream(v))
+    args = (_ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(beta), _ptr(S_pool),
+            S_pool.shape[0], _ptr(slots), _ptr(o), _stream(v))
+    if flags is None:
+        rc = library().kda_decode_step_slots(ctypes.byref(shape), *args)
+    else:
+        rc = library().kda_decode_step_slots_ex(ctypes.byref(shape), flags, *args)
     _check(rc)
     return o

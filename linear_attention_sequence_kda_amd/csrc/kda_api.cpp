@@ -74,6 +74,8 @@ bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
 int elem_size(int32_t dtype) { return dtype == KDA_BF16 ? 2 : 4; }
 
+constexpr uint32_t kAllFlags = KDA_IN_NORM_QK | KDA_IN_BETA_LOGIT | KDA_IN_GATE_RAW;
+
 // a * b with an overflow check against INT64_MAX / 8 (room for byte counts)
 bool mul_ok(int64_t a, int64_t b, int64_t* out) {
     const int64_t lim = INT64_MAX / 8;
@@ -165,11 +167,12 @@ Plan make_plan(const kda_shape* s) {
 namespace {
 // Shared body of kda_decode_step (slots == nullptr: S is [B,H,dk,dv]) and
 // kda_decode_step_slots (S is a pool of n_slots states).
-int decode_common(const char* who, const kda_shape* s, const void* q, const void* k,
-                  const void* v, const void* log_alpha, const void* beta, float* S,
-                  int64_t n_slots, const int32_t* slots, void* o, void* hip_stream) {
+int decode_common(const char* who, const kda_shape* s, uint32_t flags, const void* q,
+                  const void* k, const void* v, const void* log_alpha, const void* beta,
+                  float* S, int64_t n_slots, const int32_t* slots, void* o, void* hip_stream) {
     int rc = check_shape(s, true);
     if (rc != KDA_OK) return rc;
+    if (flags & ~kAllFlags) return KDA_ERR_FLAGS;
     const int64_t bh = s->B * s->H;
     const int eq = elem_size(s->qkv_dtype), eg = elem_size(s->gate_dtype);
     const bool has_alpha = s->alpha_mode != KDA_ALPHA_NONE;
@@ -212,6 +215,7 @@ int decode_common(const char* who, const kda_shape* s, const void* q, const void
     prm.slots = slots;
     prm.n_slots = n_slots;
     prm.H = (int)s->H;
+    prm.flags = flags;
     const hipStream_t stream = (hipStream_t)hip_stream;
     hipError_t err = timed_launch(K_DECODE, stream, [&] {
         return kda::launch_decode(prm, (int)s->dk, (int)s->dv, s->qkv_dtype == KDA_BF16, stream);
@@ -239,6 +243,7 @@ const char* kda_strerror(int status) {
         case KDA_ERR_WORKSPACE: return "workspace smaller than kda_chunk_fwd_workspace_bytes()";
         case KDA_ERR_ALIAS: return "an output buffer overlaps an input (or S_final partly overlaps S0)";
         case KDA_ERR_HIP: return "HIP launch failed";
+        case KDA_ERR_FLAGS: return "unknown kda_input_flags bit";
         default: return "unknown kda status";
     }
 }
@@ -254,8 +259,17 @@ int kda_chunk_fwd(const kda_shape* s, const void* q, const void* k, const void* 
                   const void* log_alpha, const void* beta, const float* S0, void* o,
                   float* S_final, void* workspace, size_t workspace_bytes,
                   void* hip_stream) {
+    return kda_chunk_fwd_ex(s, 0u, q, k, v, log_alpha, beta, S0, o, S_final, workspace,
+                            workspace_bytes, hip_stream);
+}
+
+int kda_chunk_fwd_ex(const kda_shape* s, uint32_t flags, const void* q, const void* k,
+                     const void* v, const void* log_alpha, const void* beta, const float* S0,
+                     void* o, float* S_final, void* workspace, size_t workspace_bytes,
+                     void* hip_stream) {
     int rc = check_shape(s, false);
     if (rc != KDA_OK) return rc;
+    if (flags & ~kAllFlags) return KDA_ERR_FLAGS;
     const int64_t bh = s->B * s->H;
     const int64_t tok = bh * s->L;
     const int eq = elem_size(s->qkv_dtype), eg = elem_size(s->gate_dtype);
@@ -304,6 +318,7 @@ int kda_chunk_fwd(const kda_shape* s, const void* q, const void* k, const void* 
     ip.L = s->L;
     ip.BH = (int)bh;
     ip.gate_bf16 = s->gate_dtype == KDA_BF16;
+    ip.flags = flags;
     kda::InterParams xp;
     xp.q = q;
     xp.k = k;
@@ -314,6 +329,7 @@ int kda_chunk_fwd(const kda_shape* s, const void* q, const void* k, const void* 
     xp.BH = (int)bh;
     xp.DV = (int)s->dv;
     xp.n_slices = 0;
+    xp.flags = flags;
 
     // per-channel decay: records hold every operand (inter-chunk kernel);
     // one decay per token: records hold T diag(beta) and the decay scalars
@@ -361,16 +377,31 @@ int kda_chunk_fwd(const kda_shape* s, const void* q, const void* k, const void* 
 int kda_decode_step(const kda_shape* s, const void* q, const void* k, const void* v,
                     const void* log_alpha, const void* beta, float* S, void* o,
                     void* hip_stream) {
-    return decode_common("kda_decode_step", s, q, k, v, log_alpha, beta, S, 0, nullptr, o,
+    return decode_common("kda_decode_step", s, 0u, q, k, v, log_alpha, beta, S, 0, nullptr, o,
                          hip_stream);
+}
+
+int kda_decode_step_ex(const kda_shape* s, uint32_t flags, const void* q, const void* k,
+                       const void* v, const void* log_alpha, const void* beta, float* S, void* o,
+                       void* hip_stream) {
+    return decode_common("kda_decode_step_ex", s, flags, q, k, v, log_alpha, beta, S, 0,
+                         nullptr, o, hip_stream);
 }
 
 int kda_decode_step_slots(const kda_shape* s, const void* q, const void* k, const void* v,
                           const void* log_alpha, const void* beta, float* S_pool,
                           int64_t n_slots, const int32_t* slots, void* o, void* hip_stream) {
+    return kda_decode_step_slots_ex(s, 0u, q, k, v, log_alpha, beta, S_pool, n_slots, slots, o,
+                                    hip_stream);
+}
+
+int kda_decode_step_slots_ex(const kda_shape* s, uint32_t flags, const void* q,
+                             const void* k, const void* v, const void* log_alpha,
+                             const void* beta, float* S_pool, int64_t n_slots,
+                             const int32_t* slots, void* o, void* hip_stream) {
     if (s && !slots && s->B * s->H > 0) return KDA_ERR_NULL;
-    return decode_common("kda_decode_step_slots", s, q, k, v, log_alpha, beta, S_pool, n_slots,
-                         slots, o, hip_stream);
+    return decode_common("kda_decode_step_slots", s, flags, q, k, v, log_alpha, beta, S_pool,
+                         n_slots, slots, o, hip_stream);
 }
 
 int kda_timing_enable(int on) {

@@ -33,6 +33,7 @@ __global__ void __launch_bounds__(256) kda_decode_kernel(DecodeParams p) {
     __shared__ __attribute__((aligned(16))) float red_q[NRG][DV];
     __shared__ float red_qk[NRG];
     __shared__ float sq[DK], sk[DK], sa[DK];
+    __shared__ float snorm[2];
 
     const int tid = threadIdx.x;
     const int cg = tid % NCG, rg = tid / NCG;
@@ -64,15 +65,39 @@ __global__ void __launch_bounds__(256) kda_decode_kernel(DecodeParams p) {
                      : ((const float*)p.log_alpha)[bh * DK + tid];
         else if (p.alpha_mode == KDA_ALPHA_HEAD)
             la = gbf ? (float)((const bf16*)p.log_alpha)[bh] : ((const float*)p.log_alpha)[bh];
+        if (p.flags & KDA_IN_GATE_RAW) la = log_alpha_of_raw(la);
         sa[tid] = (p.alpha_mode == KDA_ALPHA_NONE) ? 1.f : __expf(la);
     }
-    const float beta = gbf ? (float)((const bf16*)p.beta)[bh] : ((const float*)p.beta)[bh];
+    float beta = gbf ? (float)((const bf16*)p.beta)[bh] : ((const float*)p.beta)[bh];
+    if (p.flags & KDA_IN_BETA_LOGIT) beta = sigmoid(beta);
 
     floatx4 s[RPT];
 #pragma unroll
     for (int i = 0; i < RPT; ++i)
         s[i] = *(const floatx4*)(S + (int64_t)(rg * RPT + i) * DV + 4 * cg);
     __syncthreads();
+    if (p.flags & KDA_IN_NORM_QK) {
+        // q / |q| and k / |k| (the state loads above are already in flight)
+        if (tid < 64) {
+            float a = 0.f, b = 0.f;
+            for (int i = tid; i < DK; i += 64) {
+                a += sq[i] * sq[i];
+                b += sk[i] * sk[i];
+            }
+            a = group_sum<64>(a);
+            b = group_sum<64>(b);
+            if (tid == 0) {
+                snorm[0] = inv_norm(a);
+                snorm[1] = inv_norm(b);
+            }
+        }
+        __syncthreads();
+        if (tid < DK) {
+            sq[tid] *= snorm[0];
+            sk[tid] *= snorm[1];
+        }
+        __syncthreads();
+    }
 
     floatx4 pk = {0.f, 0.f, 0.f, 0.f}, pq = {0.f, 0.f, 0.f, 0.f};
     float pqk = 0.f;

@@ -339,4 +339,51 @@ __device__ __forceinline__ float read_lane(float x, int lane) {
 // ---- fast exp for decay factors (inputs <= 0) -----------------------------
 __device__ __forceinline__ float exp_neg(float x) { return __expf(x); }
 
+// ---- input preprocessing (kda_input_flags) ---------------------------------
+// sum of x over each aligned group of G lanes (G a power of two <= 64),
+// returned in every lane of the group
+template <int G>
+__device__ __forceinline__ float group_sum(float x) {
+#pragma unroll
+    for (int o = 1; o < G; o <<= 1) x += __shfl_xor(x, o);
+    return x;
+}
+// sum of x over lanes l, l ^ 16, l ^ 32, l ^ 48
+__device__ __forceinline__ float sum_over_lq(float x) {
+    x += __shfl_xor(x, 16);
+    x += __shfl_xor(x, 32);
+    return x;
+}
+// sum of squares of one MFMA operand fragment
+__device__ __forceinline__ float frag_sumsq(bf16x8 v) {
+    float s = 0.f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) s += (float)v[i] * (float)v[i];
+    return s;
+}
+__device__ __forceinline__ float frag_sumsq(floatx4 v) {
+    return v[0] * v[0] + v[1] * v[1] + v[2] * v[2] + v[3] * v[3];
+}
+// 1 / max(|x|, 1e-12) from the sum of squares (a zero row normalizes to zero)
+__device__ __forceinline__ float inv_norm(float ss) { return 1.f / fmaxf(sqrtf(ss), 1e-12f); }
+__device__ __forceinline__ float sigmoid(float x) { return 1.f / (1.f + __expf(-x)); }
+// ln(alpha) from the raw gate g: -exp(g)
+__device__ __forceinline__ float log_alpha_of_raw(float g) { return -__expf(g); }
+// sum of squares of a 16-byte piece of E elements
+__device__ __forceinline__ float sumsq16(uint4 u, bf16) {
+    const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+    float s = 0.f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const float a = __uint_as_float(w[i] << 16), b = __uint_as_float(w[i] & 0xffff0000u);
+        s += a * a + b * b;
+    }
+    return s;
+}
+__device__ __forceinline__ float sumsq16(uint4 u, float) {
+    const float a = __uint_as_float(u.x), b = __uint_as_float(u.y), c = __uint_as_float(u.z),
+                d = __uint_as_float(u.w);
+    return a * a + b * b + c * c + d * d;
+}
+
 }  // namespace kda

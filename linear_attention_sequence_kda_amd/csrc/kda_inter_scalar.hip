@@ -86,7 +86,9 @@ struct ScalarInterCfg {
     static_assert(LDS_BYTES <= 160 * 1024, "LDS budget of one gfx950 CU");
 };
 
-template <class Cfg>
+// NORM: q and k arrive raw (KDA_IN_NORM_QK); a separate instance, so the
+// registers the row norms take never cost the plain path.
+template <class Cfg, bool NORM>
 __global__ void __launch_bounds__(Cfg::NT) kda_inter_scalar_kernel(InterParams prm) {
     typedef typename Cfg::E E;
     typedef Frag<E> F;
@@ -325,6 +327,8 @@ __global__ void __launch_bounds__(Cfg::NT) kda_inter_scalar_kernel(InterParams p
     };
 
     floatx4 oacc[ITL];
+    floatx4 kinv[ITL];  // KDA_IN_NORM_QK: 1/|k| of a tile's rows 16R + 4lq + e
+    constexpr bool norm_qk = NORM;
     auto chunk = [&](int cs, QSet& qc) {
         const char* slot = ring + (cs & 1) * SLOT;
         const E* sK = (const E*)(slot + Cfg::O_SK);
@@ -334,6 +338,15 @@ __global__ void __launch_bounds__(Cfg::NT) kda_inter_scalar_kernel(InterParams p
 
         // ---------------- phase 1: X, Q S, P ----------------
         // S^T rows vb serve X and Q S, read once per wave.
+        // KDA_IN_NORM_QK: q and k arrive raw; the row norms, summed over the
+        // four lanes that hold a row's fragments, scale the products.
+        float qinv = 1.f;  // 1/|q| of row 16 Rw + lr
+        if constexpr (norm_qk) {
+            float sq = 0.f;
+#pragma unroll
+            for (int kk = 0; kk < NKA; ++kk) sq += frag_sumsq(qc.f[kk]);
+            qinv = inv_norm(sum_over_lq(sq));
+        }
 #pragma unroll
         for (int i = 0; i < ITL; ++i) {
             const int vb = jw + (NWC / NB) * i;
@@ -355,8 +368,18 @@ __global__ void __launch_bounds__(Cfg::NT) kda_inter_scalar_kernel(InterParams p
                 floatx4 qs = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                 for (int kk = 0; kk < NKA; ++kk) qs = F::mma(qs, st[kk], qc.f[kk]);
-                oacc[i] = qs * rs[C + 16 * R + lr];
-                const floatx4 eg = *(const floatx4*)(rs + C + 16 * R + 4 * lq);
+                oacc[i] = qs * (rs[C + 16 * R + lr] * qinv);
+                floatx4 eg = *(const floatx4*)(rs + C + 16 * R + 4 * lq);
+                if constexpr (norm_qk) {
+                    // 1/|k| of rows 16R + 4lq + e, from the lanes that own those rows
+                    float sk = 0.f;
+#pragma unroll
+                    for (int kk = 0; kk < NKA; ++kk) sk += frag_sumsq(kr[kk]);
+                    const float kin = inv_norm(sum_over_lq(sk));
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) kinv[i][e] = __shfl(kin, 4 * lq + e);
+                    eg *= kinv[i];
+                }
 #pragma unroll
                 for (int e = 0; e < 4; ++e)
                     acc[e] = to_f32(sV[(16 * R + 4 * lq + e) * PV + 16 * vb + lr]) - eg[e] * acc[e];
@@ -371,14 +394,26 @@ __global__ void __launch_bounds__(Cfg::NT) kda_inter_scalar_kernel(InterParams p
             for (int J = jw; J <= Rw; J += NWC / NB) {
                 floatx4 pa = {0.f, 0.f, 0.f, 0.f};
                 const E* pkj = sK + (16 * J + lr) * PK + W * lq;
+                FT kj[NKA];
 #pragma unroll
-                for (int kk = 0; kk < NKA; ++kk) pa = F::mma(pa, F::load(pkj + KS * kk), qc.f[kk]);
+                for (int kk = 0; kk < NKA; ++kk) kj[kk] = F::load(pkj + KS * kk);
+#pragma unroll
+                for (int kk = 0; kk < NKA; ++kk) pa = F::mma(pa, kj[kk], qc.f[kk]);
                 const floatx4 gj = *(const floatx4*)(rs + 16 * J + 4 * lq);
+                floatx4 sc = {qinv, qinv, qinv, qinv};
+                if constexpr (norm_qk) {
+                    float sk = 0.f;
+#pragma unroll
+                    for (int kk = 0; kk < NKA; ++kk) sk += frag_sumsq(kj[kk]);
+                    const float kin = inv_norm(sum_over_lq(sk));  // row 16J + lr
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) sc[e] *= __shfl(kin, 4 * lq + e);
+                }
                 floatx4 v;
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
                     const int j = 16 * J + 4 * lq + e;
-                    v[e] = (J < Rw || j <= r) ? pa[e] * exp_neg(gr - gj[e]) : 0.f;
+                    v[e] = (J < Rw || j <= r) ? pa[e] * sc[e] * exp_neg(gr - gj[e]) : 0.f;
                 }
                 st4<E>(sP + r * PC + 16 * J + 4 * lq, v);
             }
@@ -396,7 +431,9 @@ __global__ void __launch_bounds__(Cfg::NT) kda_inter_scalar_kernel(InterParams p
                 floatx4 acc = {0.f, 0.f, 0.f, 0.f};
                 acc = mma_block<E>(acc, sTb + (16 * R) * PC, PC, sXT + (16 * vb) * PC, PC, K);
                 store_acc_transposed<E>(sUT + (16 * vb) * PC + 16 * R, PC, acc);
-                const floatx4 egn = *(const floatx4*)(rs + 2 * C + 16 * R + 4 * lq);
+                // the state update takes raw K^T: e^{g_n-g_t} / |k_t| on u
+                floatx4 egn = *(const floatx4*)(rs + 2 * C + 16 * R + 4 * lq);
+                if constexpr (norm_qk) egn *= kinv[i];
                 store_acc_transposed<E>(sUHT + (16 * vb) * PC + 16 * R, PC, acc * egn);
             }
         }
@@ -471,7 +508,12 @@ template <int DK, int NV, int C, typename E>
 static hipError_t launch_scalar_cfg(const InterParams& prm, hipStream_t stream) {
     typedef ScalarInterCfg<DK, NV, C, E> Cfg;
     const int total = prm.BH * prm.n_slices;
-    hipLaunchKernelGGL((kda_inter_scalar_kernel<Cfg>), dim3(total), dim3(Cfg::NT), 0, stream, prm);
+    if (prm.flags & KDA_IN_NORM_QK)
+        hipLaunchKernelGGL((kda_inter_scalar_kernel<Cfg, true>), dim3(total), dim3(Cfg::NT), 0,
+                           stream, prm);
+    else
+        hipLaunchKernelGGL((kda_inter_scalar_kernel<Cfg, false>), dim3(total), dim3(Cfg::NT), 0,
+                           stream, prm);
     return hipGetLastError();
 }
 

@@ -86,6 +86,7 @@ struct IntraParams {
     int ncs;                // chunks in this span
     int BH;
     int gate_bf16;
+    uint32_t flags = 0;     // kda_input_flags
 };
 
 struct InterParams {
@@ -102,6 +103,7 @@ struct InterParams {
     int BH;
     int DV;
     int n_slices;           // DV / slice width (set by launch_inter)
+    uint32_t flags = 0;     // kda_input_flags (the scalar kernel normalizes q, k)
 };
 
 hipError_t launch_intra(const IntraParams& prm, int dk, int dv, int qkv_bf16, int alpha_mode,
@@ -128,6 +130,7 @@ struct DecodeParams {
     const int32_t* slots = nullptr;
     int64_t n_slots = 0;
     int H = 1;
+    uint32_t flags = 0;     // kda_input_flags
 };
 
 // State-column slice width the inter-chunk kernel uses for this problem.

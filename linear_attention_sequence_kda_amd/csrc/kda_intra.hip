@@ -86,7 +86,10 @@ struct IntraCfg {
     // KDA: Z[NB][DK], E'[NB][DK]; scalar: g[C], e^g[C]
     static constexpr int SZ_GATE = KDA ? 2 * NB * DK * 4 : 2 * C * 4;
     static constexpr int O_BETA = O_GATE + SZ_GATE;
-    static constexpr int LDS_BYTES = O_BETA + C * 4;
+    // 1/|q_r| and 1/|k_r| of each token (KDA_IN_NORM_QK)
+    static constexpr int O_QN = O_BETA + C * 4;
+    static constexpr int O_KN = O_QN + C * 4;
+    static constexpr int LDS_BYTES = O_KN + C * 4;
 
     static_assert(DK % 32 == 0 && DV % 16 == 0 && (C == 32 || C == 64), "tile shape");
     static_assert(!KDA || NB * DK <= NT, "one thread per (channel, sub-block)");
@@ -114,6 +117,11 @@ __global__ void __launch_bounds__(Cfg::NT) kda_intra_kernel(IntraParams prm) {
     E* sTb = (E*)(smem + Cfg::O_TB);
     float* sGate = (float*)(smem + Cfg::O_GATE);
     float* sBeta = (float*)(smem + Cfg::O_BETA);
+    float* sQn = (float*)(smem + Cfg::O_QN);
+    float* sKn = (float*)(smem + Cfg::O_KN);
+    const bool norm_qk = (prm.flags & KDA_IN_NORM_QK) != 0;
+    const bool gate_raw = (prm.flags & KDA_IN_GATE_RAW) != 0;
+    const bool beta_logit = (prm.flags & KDA_IN_BETA_LOGIT) != 0;
     float* sZ = sGate;                // KDA views
     float* sE = sGate + NB * DK;
     float* sG = sGate;                // scalar views
@@ -187,10 +195,19 @@ __global__ void __launch_bounds__(Cfg::NT) kda_intra_kernel(IntraParams prm) {
             if (idx < C * PPR) {
                 const int r0 = idx / PPR, cc = (idx % PPR) * VPIECE;
                 const int r = r0 < n ? r0 : n - 1;
-                const uint4 a = ldg<uint4>(gq, (r * DK + cc) * ESZ);
-                const uint4 b = ldg<uint4>(gk, (r * DK + cc) * ESZ);
-                *(uint4*)(sQr + r0 * PK + cc) = keep_or_zero(a, r0 < n);
-                *(uint4*)(sKr + r0 * PK + cc) = keep_or_zero(b, r0 < n);
+                const uint4 a = keep_or_zero(ldg<uint4>(gq, (r * DK + cc) * ESZ), r0 < n);
+                const uint4 b = keep_or_zero(ldg<uint4>(gk, (r * DK + cc) * ESZ), r0 < n);
+                *(uint4*)(sQr + r0 * PK + cc) = a;
+                *(uint4*)(sKr + r0 * PK + cc) = b;
+                if (norm_qk) {
+                    // the PPR pieces of a row sit in PPR consecutive lanes
+                    const float nq = inv_norm(group_sum<PPR>(sumsq16(a, E{})));
+                    const float nk = inv_norm(group_sum<PPR>(sumsq16(b, E{})));
+                    if (idx % PPR == 0) {
+                        sQn[r0] = nq;
+                        sKn[r0] = nk;
+                    }
+                }
             }
         }
         float a[16];
@@ -200,7 +217,8 @@ __global__ void __launch_bounds__(Cfg::NT) kda_intra_kernel(IntraParams prm) {
                 const int r = 16 * kR + s;
                 const int rr = r < n ? r : n - 1;
                 const uint32_t el = rr * DK + kc;
-                const float la = GBF ? bits_f32(ldg<uint16_t>(gla, el * 2), true) : ldg<float>(gla, el * 4);
+                float la = GBF ? bits_f32(ldg<uint16_t>(gla, el * 2), true) : ldg<float>(gla, el * 4);
+                if (gate_raw) la = log_alpha_of_raw(la);
                 a[s] = r < n ? la : 0.f;
             }
         }
@@ -212,6 +230,10 @@ __global__ void __launch_bounds__(Cfg::NT) kda_intra_kernel(IntraParams prm) {
             for (int s = 0; s < 16; ++s) {
                 qv[s] = to_f32(sQr[(16 * R + s) * PK + kc]);
                 kv[s] = to_f32(sKr[(16 * R + s) * PK + kc]);
+                if (norm_qk) {
+                    qv[s] *= sQn[16 * R + s];
+                    kv[s] *= sKn[16 * R + s];
+                }
             }
             // alpha = exp(ln alpha); x_s = prod_{s'<=s} alpha (within block)
             float x[16];
@@ -250,8 +272,13 @@ __global__ void __launch_bounds__(Cfg::NT) kda_intra_kernel(IntraParams prm) {
             if (idx < C * PPR) {
                 const int r0 = idx / PPR, cc = (idx % PPR) * VPIECE;
                 const int r = r0 < n ? r0 : n - 1;
-                const uint4 b = ldg<uint4>(gk, (r * DK + cc) * ESZ);
-                *(uint4*)(sKr + r0 * PK + cc) = keep_or_zero(b, r0 < n);
+                const uint4 b = keep_or_zero(ldg<uint4>(gk, (r * DK + cc) * ESZ), r0 < n);
+                *(uint4*)(sKr + r0 * PK + cc) = b;
+                if (norm_qk) {
+                    // the PPR pieces of a row sit in PPR consecutive lanes
+                    const float nk = inv_norm(group_sum<PPR>(sumsq16(b, E{})));
+                    if (idx % PPR == 0) sKn[r0] = nk;
+                }
             }
         }
         // g = inclusive prefix sum of ln(alpha) over the chunk (wave 0)
@@ -259,7 +286,10 @@ __global__ void __launch_bounds__(Cfg::NT) kda_intra_kernel(IntraParams prm) {
             float g = 0.f;
             if constexpr (HEADG) {
                 float la = 0.f;
-                if (l < n) la = GBF ? bits_f32(ldg<uint16_t>(gla, l * 2), true) : ldg<float>(gla, l * 4);
+                if (l < n) {
+                    la = GBF ? bits_f32(ldg<uint16_t>(gla, l * 2), true) : ldg<float>(gla, l * 4);
+                    if (gate_raw) la = log_alpha_of_raw(la);
+                }
                 g = wave_inclusive_sum(la);
             }
             const float gn = read_lane(g, C - 1);
@@ -276,7 +306,10 @@ __global__ void __launch_bounds__(Cfg::NT) kda_intra_kernel(IntraParams prm) {
     }
     if (tid < C) {
         float b = 0.f;
-        if (tid < n) b = GBF ? bits_f32(ldg<uint16_t>(gbeta, tid * 2), true) : ldg<float>(gbeta, tid * 4);
+        if (tid < n) {
+            b = GBF ? bits_f32(ldg<uint16_t>(gbeta, tid * 2), true) : ldg<float>(gbeta, tid * 4);
+            if (beta_logit) b = sigmoid(b);
+        }
         sBeta[tid] = b;
     }
     __syncthreads();
@@ -369,11 +402,14 @@ __global__ void __launch_bounds__(Cfg::NT) kda_intra_kernel(IntraParams prm) {
             gj = *(const floatx4*)(sG + 16 * J + 4 * lq);
         }
         floatx4 va, vp;
+        // scalar decay: the raw k rows, so the norms scale the product
+        const float nr = THIN && norm_qk ? sKn[rr] : 1.f;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
             const int jj = 16 * J + 4 * lq + e;
             float f = 1.f;  // scalar decay e^{g_r - g_j}, applied to the result
             if constexpr (HEADG) f = exp_neg(gr - gj[e]);
+            if (THIN && norm_qk) f *= nr * sKn[jj];
             va[e] = (J < R || jj < rr) ? br * accA[e] * f : 0.f;
             vp[e] = (J < R || jj <= rr) ? accP[e] * f : 0.f;
         }

@@ -31,7 +31,7 @@ def test_exports_every_declared_function(lib):
 
 def test_version_and_strings(lib):
     assert lib.kda_abi_version() == 1
-    for code in range(9):
+    for code in range(10):
         assert lib.kda_strerror(code)
     assert lib.kda_strerror(0) == b"ok"
     assert lib.kda_last_error() == b""
@@ -200,3 +200,39 @@ def test_decode_slots_host_checks(lib):
     assert decode_slots(lib, s, b, slots=b["o"]) == 7            # slots overlap o
     assert decode_slots(lib, s, dict(b, o=b["S0"] + 64)) == 7    # o inside the pool
     assert decode_slots(lib, shape(B=0, L=1), b) == 0           # empty: nothing to do
+
+
+def test_input_flags_host_checks(lib):
+    """Unknown kda_input_flags bits are rejected before any other work; known
+    bits pass the flag check and reach the ordinary argument checks."""
+    b = bufs()
+    s = shape()
+    args = (b["q"], b["k"], b["v"], b["la"], b["beta"], b["S0"], b["o"], b["Sf"], b["ws"],
+            1 << 30, None)
+    for bad in (8, 16, 1 << 31, 0xFFFFFFFF):
+        assert lib.kda_chunk_fwd_ex(ctypes.byref(s), bad, *args) == 9
+        d = shape(L=1)
+        assert lib.kda_decode_step_ex(ctypes.byref(d), bad, b["q"], b["k"], b["v"], b["la"],
+                                      b["beta"], b["S0"], b["o"], None) == 9
+        assert lib.kda_decode_step_slots_ex(ctypes.byref(d), bad, b["q"], b["k"], b["v"],
+                                            b["la"], b["beta"], b["S0"], 4, b["ws"], b["o"],
+                                            None) == 9
+    assert b"flags" in lib.kda_strerror(9)
+    all_bits = binding.NORM_QK | binding.BETA_LOGIT | binding.GATE_RAW
+    # a valid flag set with a bad shape fails on the shape, as the plain call does
+    assert lib.kda_chunk_fwd_ex(ctypes.byref(shape(dk=96)), all_bits, *args) == 2
+    assert lib.kda_chunk_fwd_ex(ctypes.byref(s), all_bits, b["q"], None, *args[2:]) == 1
+    assert lib.kda_decode_step_ex(ctypes.byref(shape(L=2)), all_bits, b["q"], b["k"], b["v"],
+                                  b["la"], b["beta"], b["S0"], b["o"], None) == 2
+    # empty problems are fine with any valid flag set
+    none = {n: None for n in bufs()}
+    assert lib.kda_chunk_fwd_ex(ctypes.byref(shape(B=0)), all_bits, none["q"], none["k"],
+                                none["v"], none["la"], none["beta"], none["S0"], none["o"],
+                                none["Sf"], none["ws"], 0, None) == 0
+
+
+def test_flag_values_match_header():
+    text = open(binding.HEADER).read()
+    for name, val in (("KDA_IN_NORM_QK", binding.NORM_QK), ("KDA_IN_BETA_LOGIT",
+                      binding.BETA_LOGIT), ("KDA_IN_GATE_RAW", binding.GATE_RAW)):
+        assert f"{name} = {val}" in text
