@@ -182,6 +182,40 @@ int kda_decode_step_slots(const kda_shape* shape, const void* q, const void* k, 
                           int64_t n_slots, const int32_t* slots, void* o, void* hip_stream);
 
 /*
+ * Prefill of a batch of packed variable-length sequences, for serving: each
+ * sequence runs the recurrence of kda_chunk_fwd over its own tokens from its
+ * own initial state, chunks never cross a sequence boundary, and no padding
+ * is stored or computed ("22,580: From GPT-2 to Kimi K3", section 6.3 for the
+ * chunk algorithm; section 5.2 for the per-sequence state the decode steps
+ * then continue).
+ *   shape       B = number of sequences N, L = T = total tokens, H, dk, dv,
+ *               dtypes and alpha_mode as for kda_chunk_fwd.
+ *   cu_seqlens  device int32 [N + 1]: sequence i owns tokens cu_seqlens[i] ..
+ *               cu_seqlens[i+1] - 1.  Must be nondecreasing with
+ *               cu_seqlens[0] = 0 and cu_seqlens[N] = T; the kernels clamp it
+ *               to [0, T] (a malformed table gives undefined results but no
+ *               access outside the tensors).  4-byte aligned; an input.
+ *   max_seqlen  host: >= every sequence length (the chunk plan and the
+ *               workspace follow min(max_seqlen, T)); tokens of a longer
+ *               sequence beyond it are not processed.
+ *   q, k        [H, T, dk]; v, o [H, T, dv]; log_alpha [H, T, dk] | [H, T];
+ *               beta [H, T]  (sequence i of head h at rows h T + cu_seqlens[i]..)
+ *   S0, S_final [N, H, dk, dv] fp32, per sequence (NULL as for kda_chunk_fwd).
+ *   flags       kda_input_flags, as for kda_chunk_fwd_ex.
+ *   workspace   >= kda_chunk_fwd_varlen_workspace_bytes(shape, max_seqlen).
+ * Errors as for kda_chunk_fwd_ex, plus KDA_ERR_SHAPE for max_seqlen < 0 and
+ * KDA_ERR_NULL for a NULL cu_seqlens with N > 0.
+ */
+int kda_chunk_fwd_varlen(const kda_shape* shape, uint32_t flags, const int32_t* cu_seqlens,
+                         int64_t max_seqlen, const void* q, const void* k, const void* v,
+                         const void* log_alpha, const void* beta, const float* S0, void* o,
+                         float* S_final, void* workspace, size_t workspace_bytes,
+                         void* hip_stream);
+/* Device workspace bytes kda_chunk_fwd_varlen needs (0 if it would reject the
+ * shape or max_seqlen). */
+size_t kda_chunk_fwd_varlen_workspace_bytes(const kda_shape* shape, int64_t max_seqlen);
+
+/*
  * Kernel timing, for measurement tools (not part of the computation).  While
  * timing is on, every kernel that kda_chunk_fwd or kda_decode_step launches is
  * bracketed by two HIP events recorded on the call's stream; the event pairs

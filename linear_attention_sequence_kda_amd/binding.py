@@ -63,6 +63,12 @@ def library() -> ctypes.CDLL:
                                               vp]
         lib.kda_decode_step_slots.restype = ctypes.c_int
         u32 = ctypes.c_uint32
+        i64 = ctypes.c_int64
+        lib.kda_chunk_fwd_varlen.argtypes = [sp, u32, vp, i64, vp, vp, vp, vp, vp, vp, vp, vp, vp,
+                                             sz, vp]
+        lib.kda_chunk_fwd_varlen.restype = ctypes.c_int
+        lib.kda_chunk_fwd_varlen_workspace_bytes.argtypes = [sp, i64]
+        lib.kda_chunk_fwd_varlen_workspace_bytes.restype = sz
         lib.kda_chunk_fwd_ex.argtypes = [sp, u32, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
         lib.kda_chunk_fwd_ex.restype = ctypes.c_int
         lib.kda_decode_step_ex.argtypes = [sp, u32, vp, vp, vp, vp, vp, vp, vp, vp]
@@ -220,6 +226,62 @@ def chunk_fwd(q, k, v, log_alpha, beta, S0=None, *, output_final_state: bool = T
         rc = lib.kda_chunk_fwd(ctypes.byref(shape), *args)
     else:
         rc = lib.kda_chunk_fwd_ex(ctypes.byref(shape), flags, *args)
+    _check(rc)
+    return o, (S_final if output_final_state else None)
+
+
+def _varlen_shape(q, v, log_alpha, beta, n_seq: int) -> KdaShape:
+    H, T, dk = q.shape
+    dv = v.shape[-1]
+    if log_alpha is None:
+        mode = KDA_ALPHA_NONE
+    elif log_alpha.dim() == 2:
+        mode = KDA_ALPHA_HEAD
+    else:
+        mode = KDA_ALPHA_CHANNEL
+    return KdaShape(n_seq, H, T, dk, dv, _dtype_code(q),
+                    _dtype_code(log_alpha if log_alpha is not None else beta), mode)
+
+
+def chunk_fwd_varlen(q, k, v, log_alpha, beta, cu_seqlens, max_seqlen: int, S0=None, *,
+                     output_final_state: bool = True, o=None, S_final=None, workspace=None,
+                     flags: int = 0) -> Tuple[object, Optional[object]]:
+    """Prefill of N packed sequences: returns (o [H,T,dv], S_final [N,H,dk,dv] or None).
+
+    q, k: [H,T,dk]; v: [H,T,dv]; log_alpha: None, [H,T] or [H,T,dk]; beta:
+    [H,T]; sequence i owns tokens cu_seqlens[i] .. cu_seqlens[i+1]-1
+    (cu_seqlens: int32 [N+1] on the GPU); max_seqlen: an int >= every length;
+    S0: [N,H,dk,dv] fp32 or None.  ``flags`` as for chunk_fwd.
+    """
+    torch = _torch()
+    H, T, dk = q.shape
+    dv = v.shape[-1]
+    for name, t in (("q", q), ("k", k), ("v", v), ("beta", beta), ("log_alpha", log_alpha),
+                    ("S0", S0), ("cu_seqlens", cu_seqlens)):
+        if t is not None:
+            _require(t, name)
+    if cu_seqlens.dtype != torch.int32:
+        raise TypeError("cu_seqlens must be int32")
+    n_seq = cu_seqlens.numel() - 1
+    if o is None:
+        o = torch.empty((H, T, dv), dtype=v.dtype, device=v.device)
+    if output_final_state and S_final is None:
+        S_final = torch.empty((n_seq, H, dk, dv), dtype=torch.float32, device=v.device)
+    if S0 is not None and S0.dtype != torch.float32:
+        raise TypeError("S0 must be float32")
+    shape = _varlen_shape(q, v, log_alpha, beta, n_seq)
+    lib = library()
+    ws = lib.kda_chunk_fwd_varlen_workspace_bytes(ctypes.byref(shape), int(max_seqlen))
+    if workspace is None:
+        workspace = torch.empty(ws, dtype=torch.uint8, device=v.device) if ws else None
+    else:
+        _require(workspace, "workspace")
+    ws_given = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    rc = lib.kda_chunk_fwd_varlen(ctypes.byref(shape), flags, _ptr(cu_seqlens), int(max_seqlen),
+                                  _ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(beta),
+                                  _ptr(S0), _ptr(o),
+                                  _ptr(S_final) if output_final_state else None,
+                                  _ptr(workspace), ws_given, _stream(v))
     _check(rc)
     return o, (S_final if output_final_state else None)
 

@@ -263,26 +263,41 @@ int kda_chunk_fwd(const kda_shape* s, const void* q, const void* k, const void* 
                             workspace_bytes, hip_stream);
 }
 
-int kda_chunk_fwd_ex(const kda_shape* s, uint32_t flags, const void* q, const void* k,
-                     const void* v, const void* log_alpha, const void* beta, const float* S0,
-                     void* o, float* S_final, void* workspace, size_t workspace_bytes,
-                     void* hip_stream) {
+}  // extern "C"
+
+namespace {
+// Shared body of kda_chunk_fwd_ex (cu == nullptr: dense [B,H,L,*] tensors) and
+// kda_chunk_fwd_varlen (B packed sequences in [H, L = T, *] tensors, token
+// offsets cu on the device, the longest sequence max_len tokens).
+int chunk_common(const char* who, const kda_shape* s, uint32_t flags, const int32_t* cu,
+                 int64_t max_len, const void* q, const void* k, const void* v,
+                 const void* log_alpha, const void* beta, const float* S0, void* o,
+                 float* S_final, void* workspace, size_t workspace_bytes, void* hip_stream) {
     int rc = check_shape(s, false);
     if (rc != KDA_OK) return rc;
     if (flags & ~kAllFlags) return KDA_ERR_FLAGS;
+    const bool packed = cu != nullptr || max_len >= 0;
+    if (packed && max_len < 0) return KDA_ERR_SHAPE;
     const int64_t bh = s->B * s->H;
-    const int64_t tok = bh * s->L;
+    // token rows of every [*, d] tensor: B H L dense, H T packed
+    const int64_t tok = packed ? s->H * s->L : bh * s->L;
     const int eq = elem_size(s->qkv_dtype), eg = elem_size(s->gate_dtype);
     const bool has_alpha = s->alpha_mode != KDA_ALPHA_NONE;
+    // the plan (spans, records) follows the longest sequence, which no
+    // sequence of T tokens can exceed
+    kda_shape ps = *s;
+    if (packed) ps.L = max_len < s->L ? max_len : s->L;
 
     if (tok > 0) {
         if (!q || !k || !v || !beta || !o) return KDA_ERR_NULL;
         if (has_alpha && !log_alpha) return KDA_ERR_NULL;
     }
+    if (packed && s->B > 0 && !cu) return KDA_ERR_NULL;
     const void* ptrs[] = {q, k, v, has_alpha ? log_alpha : nullptr, beta, S0, o, S_final, workspace};
     for (const void* p : ptrs)
         if (p && !aligned16(p)) return KDA_ERR_ALIGN;
-    const Plan plan = make_plan(s);
+    if (cu && ((uintptr_t)cu & 3u)) return KDA_ERR_ALIGN;
+    const Plan plan = make_plan(&ps);
     if (plan.ws_bytes > 0 && (!workspace || workspace_bytes < (size_t)plan.ws_bytes))
         return KDA_ERR_WORKSPACE;
 
@@ -291,14 +306,15 @@ int kda_chunk_fwd_ex(const kda_shape* s, uint32_t flags, const void* q, const vo
                sv = span_of(v, tok * s->dv * eq),
                sla = span_of(has_alpha ? log_alpha : nullptr, la_elems * eg),
                sb = span_of(beta, tok * eg), s0 = span_of(S0, bh * s->dk * s->dv * 4),
-               so = span_of(o, tok * s->dv * eq), sf = span_of(S_final, bh * s->dk * s->dv * 4);
-    const Span inputs[] = {sq, sk, sv, sla, sb};
+               so = span_of(o, tok * s->dv * eq), sf = span_of(S_final, bh * s->dk * s->dv * 4),
+               sc = span_of(cu, packed ? (s->B + 1) * 4 : 0);
+    const Span inputs[] = {sq, sk, sv, sla, sb, sc};
     for (const Span& in : inputs)
         if (overlaps(so, in) || overlaps(sf, in)) return KDA_ERR_ALIAS;
     if (overlaps(so, s0) || overlaps(so, sf)) return KDA_ERR_ALIAS;
     if (overlaps(sf, s0) && (const void*)S_final != (const void*)S0) return KDA_ERR_ALIAS;
     const Span sw = span_of(workspace, plan.ws_bytes);
-    const Span all[] = {sq, sk, sv, sla, sb, s0, so, sf};
+    const Span all[] = {sq, sk, sv, sla, sb, s0, so, sf, sc};
     for (const Span& x : all)
         if (overlaps(sw, x)) return KDA_ERR_ALIAS;
 
@@ -319,6 +335,8 @@ int kda_chunk_fwd_ex(const kda_shape* s, uint32_t flags, const void* q, const vo
     ip.BH = (int)bh;
     ip.gate_bf16 = s->gate_dtype == KDA_BF16;
     ip.flags = flags;
+    ip.cu = cu;
+    ip.H = (int)s->H;
     kda::InterParams xp;
     xp.q = q;
     xp.k = k;
@@ -330,7 +348,8 @@ int kda_chunk_fwd_ex(const kda_shape* s, uint32_t flags, const void* q, const vo
     xp.DV = (int)s->dv;
     xp.n_slices = 0;
     xp.flags = flags;
-
+    xp.cu = cu;
+    xp.H = (int)s->H;
     // per-channel decay: records hold every operand (inter-chunk kernel);
     // one decay per token: records hold T diag(beta) and the decay scalars
     auto launch_state = [&](const kda::InterParams& x) {
@@ -367,10 +386,39 @@ int kda_chunk_fwd_ex(const kda_shape* s, uint32_t flags, const void* q, const vo
         err = launch_state(xp);
     }
     if (err != hipSuccess) {
-        g_last_error = std::string("kda_chunk_fwd: ") + hipGetErrorString(err);
+        g_last_error = std::string(who) + ": " + hipGetErrorString(err);
         return KDA_ERR_HIP;
     }
     return KDA_OK;
+}
+}  // namespace
+
+extern "C" {
+
+int kda_chunk_fwd_ex(const kda_shape* s, uint32_t flags, const void* q, const void* k,
+                     const void* v, const void* log_alpha, const void* beta, const float* S0,
+                     void* o, float* S_final, void* workspace, size_t workspace_bytes,
+                     void* hip_stream) {
+    return chunk_common("kda_chunk_fwd", s, flags, nullptr, -1, q, k, v, log_alpha, beta, S0, o,
+                        S_final, workspace, workspace_bytes, hip_stream);
+}
+
+size_t kda_chunk_fwd_varlen_workspace_bytes(const kda_shape* shape, int64_t max_seqlen) {
+    if (check_shape(shape, false) != KDA_OK) return 0;
+    if (max_seqlen < 0) return 0;
+    kda_shape ps = *shape;
+    ps.L = max_seqlen < shape->L ? max_seqlen : shape->L;
+    return (size_t)make_plan(&ps).ws_bytes;
+}
+
+int kda_chunk_fwd_varlen(const kda_shape* s, uint32_t flags, const int32_t* cu_seqlens,
+                         int64_t max_seqlen, const void* q, const void* k, const void* v,
+                         const void* log_alpha, const void* beta, const float* S0, void* o,
+                         float* S_final, void* workspace, size_t workspace_bytes,
+                         void* hip_stream) {
+    if (max_seqlen < 0) return KDA_ERR_SHAPE;
+    return chunk_common("kda_chunk_fwd_varlen", s, flags, cu_seqlens, max_seqlen, q, k, v,
+                        log_alpha, beta, S0, o, S_final, workspace, workspace_bytes, hip_stream);
 }
 
 

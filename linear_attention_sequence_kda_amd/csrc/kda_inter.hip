@@ -125,11 +125,15 @@ __global__ void __launch_bounds__(Cfg::NT) kda_inter_kernel(InterParams prm) {
     const int bh = pidx / prm.n_slices;
     const int slice = pidx - bh * prm.n_slices;
     const int v0 = slice * NV;
-    const int64_t L = prm.L;
+    const SeqRange sr = seq_range(prm.cu, prm.L, prm.H, bh);
+    const int64_t L = sr.len;
     const int DV = prm.DV;
     const RecLayout rl = rec_layout(DK, DV, C, ESZ, KDA);
     const char* recs = (const char*)prm.ws + (int64_t)bh * prm.ncs * rl.bytes;
-    const int ncs = prm.ncs;
+    // chunks of this span that hold tokens of this head (fewer than the span's
+    // for a packed sequence that ends early)
+    int64_t left = (L + C - 1) / C - prm.c0;
+    const int ncs = (int)(left < 0 ? 0 : (left < prm.ncs ? left : prm.ncs));
 
     if (w >= NWC) {
         // ======================= data waves ==================================
@@ -144,7 +148,7 @@ __global__ void __launch_bounds__(Cfg::NT) kda_inter_kernel(InterParams prm) {
         constexpr int NS = (NPC + 64 * NWP - 1) / (64 * NWP);
         const int pw = w - NWC;
         const __amdgpu_buffer_rsrc_t orsrc =
-            make_rsrc((const char*)prm.o + (int64_t)bh * L * DV * ESZ, (uint32_t)(L * DV * ESZ));
+            make_rsrc((const char*)prm.o + sr.base * DV * ESZ, (uint32_t)(L * DV * ESZ));
         const int gp0 = (slice * NVB) / PF;  // first U piece column of the slice
         // record and ring offsets of this wave's j-th piece (wave-uniform;
         // pieces past the list re-read a valid piece and land in the sink)

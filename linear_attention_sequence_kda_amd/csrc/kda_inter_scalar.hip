@@ -124,9 +124,13 @@ __global__ void __launch_bounds__(Cfg::NT) kda_inter_scalar_kernel(InterParams p
     const int bh = pidx / prm.n_slices;
     const int slice = pidx - bh * prm.n_slices;
     const int v0 = slice * NV;
-    const int64_t L = prm.L;
+    const SeqRange sr = seq_range(prm.cu, prm.L, prm.H, bh);
+    const int64_t L = sr.len;
     const int DV = prm.DV;
-    const int ncs = prm.ncs;
+    // chunks of this span that hold tokens of this head (fewer than the span's
+    // for a packed sequence that ends early)
+    int64_t left = (L + C - 1) / C - prm.c0;
+    const int ncs = (int)(left < 0 ? 0 : (left < prm.ncs ? left : prm.ncs));
 
     if (w >= NWC) {
         // ======================= data waves ==================================
@@ -145,8 +149,8 @@ __global__ void __launch_bounds__(Cfg::NT) kda_inter_scalar_kernel(InterParams p
         constexpr int NS = (NPO + 64 * NWP - 1) / (64 * NWP);
         const int pw = w - NWC;
         typedef int v4i __attribute__((ext_vector_type(4)));
-        const int64_t hq = (int64_t)bh * L * DK * ESZ, hv = (int64_t)bh * L * DV * ESZ;
-        const char* recs = (const char*)prm.ws + (int64_t)bh * ncs * RL.bytes;
+        const int64_t hq = sr.base * DK * ESZ, hv = sr.base * DV * ESZ;
+        const char* recs = (const char*)prm.ws + (int64_t)bh * prm.ncs * RL.bytes;
         const __amdgpu_buffer_rsrc_t orsrc =
             make_rsrc((const char*)prm.o + hv, (uint32_t)(L * DV * ESZ));
         // piece j of this wave: source (1 k, 2 v, 3 record), per-lane source
@@ -313,7 +317,7 @@ __global__ void __launch_bounds__(Cfg::NT) kda_inter_scalar_kernel(InterParams p
     struct QSet {
         FT f[NKA];
     };
-    const char* qhead = (const char*)prm.q + (int64_t)bh * L * DK * ESZ;
+    const char* qhead = (const char*)prm.q + sr.base * DK * ESZ;
     auto load_q = [&](QSet& qs, int cs) {
         cs = cs < ncs ? cs : ncs - 1;
         const int64_t t0 = (prm.c0 + cs) * C;

@@ -74,6 +74,24 @@ __host__ __device__ constexpr RecLayout rec_layout_thin(int c, int esz) {
 // Chunk length of the prefill kernels: 64 tokens with bf16 operands, 32 in fp32.
 constexpr int chunk_len(int qkv_bf16) { return qkv_bf16 ? 64 : 32; }
 
+// Token range of workgroup head bh in the [*, d] input rows: rows base ..
+// base + len - 1.  Dense layout ([BH, L, d]): base = bh L, len = L.  Packed
+// sequences (cu != null, L = T total tokens, [H, T, d] tensors): bh = i H + h
+// is head h of sequence i, which owns tokens cu[i] .. cu[i+1] - 1; the table
+// is clamped to [0, T], so a malformed one cannot move an access outside the
+// tensors.
+struct SeqRange {
+    int64_t base, len;
+};
+__device__ __forceinline__ SeqRange seq_range(const int32_t* cu, int64_t L, int H, int bh) {
+    if (!cu) return SeqRange{(int64_t)bh * L, L};
+    const int i = bh / H, h = bh - i * H;
+    int64_t s = cu[i], e = cu[i + 1];
+    s = s < 0 ? 0 : (s > L ? L : s);
+    e = e < s ? s : (e > L ? L : e);
+    return SeqRange{(int64_t)h * L + s, e - s};
+}
+
 struct IntraParams {
     const void* q;          // [BH, L, DK]  qkv type
     const void* k;          // [BH, L, DK]
@@ -87,6 +105,8 @@ struct IntraParams {
     int BH;
     int gate_bf16;
     uint32_t flags = 0;     // kda_input_flags
+    const int32_t* cu = nullptr;  // packed sequences: [B + 1] token offsets
+    int H = 1;              // heads per sequence (packed sequences)
 };
 
 struct InterParams {
@@ -104,6 +124,8 @@ struct InterParams {
     int DV;
     int n_slices;           // DV / slice width (set by launch_inter)
     uint32_t flags = 0;     // kda_input_flags (the scalar kernel normalizes q, k)
+    const int32_t* cu = nullptr;  // packed sequences, as in IntraParams
+    int H = 1;
 };
 
 hipError_t launch_intra(const IntraParams& prm, int dk, int dv, int qkv_bf16, int alpha_mode,

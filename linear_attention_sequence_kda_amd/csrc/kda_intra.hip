@@ -134,17 +134,20 @@ __global__ void __launch_bounds__(Cfg::NT) kda_intra_kernel(IntraParams prm) {
 
     const int bh = blockIdx.x / prm.ncs;
     const int cs = blockIdx.x - bh * prm.ncs;
-    const int64_t L = prm.L;
+    const SeqRange sr = seq_range(prm.cu, prm.L, prm.H, bh);
+    const int64_t L = sr.len;
     const int64_t t0 = (prm.c0 + cs) * C;
+    if (t0 >= L) return;  // packed sequences: past this sequence's last chunk
     const int n = (int)((L - t0) < C ? (L - t0) : C);  // valid tokens, >= 1
 
     // chunk base pointers (64-bit, uniform); offsets below are 32-bit
-    const char* gq = (const char*)prm.q + ((int64_t)bh * L + t0) * DK * ESZ;
-    const char* gk = (const char*)prm.k + ((int64_t)bh * L + t0) * DK * ESZ;
-    const char* gv = (const char*)prm.v + ((int64_t)bh * L + t0) * DV * ESZ;
+    const int64_t row0 = sr.base + t0;
+    const char* gq = (const char*)prm.q + row0 * DK * ESZ;
+    const char* gk = (const char*)prm.k + row0 * DK * ESZ;
+    const char* gv = (const char*)prm.v + row0 * DV * ESZ;
     constexpr int GSZ = GBF ? 2 : 4;
-    const char* gla = (const char*)prm.log_alpha + ((int64_t)bh * L + t0) * (KDA ? DK : 1) * GSZ;
-    const char* gbeta = (const char*)prm.beta + ((int64_t)bh * L + t0) * GSZ;
+    const char* gla = (const char*)prm.log_alpha + row0 * (KDA ? DK : 1) * GSZ;
+    const char* gbeta = (const char*)prm.beta + row0 * GSZ;
     char* rec = (char*)prm.ws + ((int64_t)bh * prm.ncs + cs) * RL.bytes;
     E* rW = (E*)(rec + RL.w);
     E* rU = (E*)(rec + RL.ut);

@@ -236,3 +236,40 @@ def test_flag_values_match_header():
     for name, val in (("KDA_IN_NORM_QK", binding.NORM_QK), ("KDA_IN_BETA_LOGIT",
                       binding.BETA_LOGIT), ("KDA_IN_GATE_RAW", binding.GATE_RAW)):
         assert f"{name} = {val}" in text
+
+
+def varlen(lib, s, b, max_len, cu=None, flags=0, wsb=1 << 30):
+    return lib.kda_chunk_fwd_varlen(ctypes.byref(s) if s is not None else None, flags,
+                                    b["cu"] if cu is None else cu, max_len, b["q"], b["k"],
+                                    b["v"], b["la"], b["beta"], b["S0"], b["o"], b["Sf"],
+                                    b["ws"], wsb, None)
+
+
+def test_varlen_host_checks(lib):
+    """Packed sequences: B = sequences, L = total tokens; the token offsets are
+    an input on the device, max_seqlen sizes the plan."""
+    b = dict(bufs(), cu=BASE + 20 * 64 * MB)
+    s = shape(B=3, H=4, L=1000)
+    assert varlen(lib, s, b, -1) == 2
+    assert varlen(lib, s, b, 500, cu=0) == 1           # no offsets with N > 0
+    assert varlen(lib, s, b, 500, cu=b["cu"] + 2) == 5
+    assert varlen(lib, s, b, 500, cu=b["o"]) == 7      # offsets overlap o
+    assert varlen(lib, s, b, 500, cu=b["ws"]) == 7     # or the workspace
+    assert varlen(lib, s, b, 500, flags=8) == 9
+    assert varlen(lib, shape(B=3, H=4, L=1000, dk=96), b, 500) == 2
+    assert varlen(lib, s, b, 500, wsb=16) == 6         # workspace too small
+    # the workspace follows the longest sequence: that of a dense [N, H, max] call
+    for n, T, m in ((3, 1000, 500), (2, 8192, 8192), (5, 4096, 64), (7, 300, 0)):
+        for mode in (binding.KDA_ALPHA_CHANNEL, binding.KDA_ALPHA_HEAD):
+            sv = shape(B=n, H=32, L=T, mode=mode)
+            got = lib.kda_chunk_fwd_varlen_workspace_bytes(ctypes.byref(sv), m)
+            want = lib.kda_chunk_fwd_workspace_bytes(ctypes.byref(shape(B=n, H=32, L=m,
+                                                                        mode=mode)))
+            assert got == want
+    # no sequence is longer than T: a larger max_seqlen plans for T
+    assert (lib.kda_chunk_fwd_varlen_workspace_bytes(ctypes.byref(s), 10 ** 9)
+            == lib.kda_chunk_fwd_varlen_workspace_bytes(ctypes.byref(s), 1000))
+    assert lib.kda_chunk_fwd_varlen_workspace_bytes(ctypes.byref(s), -5) == 0
+    # no sequences: nothing to do, no pointer needed
+    none = {n: None for n in b}
+    assert varlen(lib, shape(B=0, H=4, L=0), none, 0) == 0
