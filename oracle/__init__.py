@@ -20,6 +20,10 @@ Contents
                        batched indexing read per chunk.
 ``forward_substitution`` the pages' in-place inversion of (I + A).
 ``slab_error``         the parity metric.
+``linear_attention``   normalized linear attention with phi = elu + 1 (fp64:
+                       phi on the host, the C recurrence without the delta
+                       term for the numerator and the state, a running sum
+                       for the normalizer).
 ``preprocess``         the token mixer's input steps (L2-normalized q and k,
                        sigmoid beta, alpha = exp(-exp(g))) in fp64, applied to
                        raw stored inputs before ``forward``.
@@ -179,6 +183,42 @@ def preprocess(q, k, v, log_alpha, beta, flags, *, qkv_dtype="f32", gate_dtype="
     if flags & GATE_RAW and la is not None:
         la = log_alpha_of_raw(la)
     return q, k, v, la, b
+
+
+# ---------------------------------------------------------------------------
+# normalized linear attention (fp64)
+# ---------------------------------------------------------------------------
+
+def elu1(x):
+    """phi(x) = elu(x) + 1: x + 1 for x > 0, e^x otherwise, so phi > 0 ("22,580:
+    From GPT-2 to Kimi K3", section 04: the feature map applied to q and k
+    separately before they meet)."""
+    x = np.asarray(x, dtype=np.float64)
+    return np.where(x > 0, x + 1.0, np.exp(np.minimum(x, 0.0)))
+
+
+def linear_attention(q, k, v, S0=None, z0=None, *, qkv_dtype="f32", threads=None):
+    """Causal normalized linear attention on stacked heads.
+
+    Per head, with phi = elu1 applied to the stored q and k (widened to fp64):
+    S_t = S_{t-1} + phi(k_t)^T v_t, z_t = z_{t-1} + phi(k_t),
+    o_t = phi(q_t) S_t / (phi(q_t) . z_t)  ("22,580: From GPT-2 to Kimi K3",
+    section 04, and "22,580: GPT-2 to Kimi K3, explained" (zharfai.com),
+    "Linear attention collapses history into a fixed state": state, normalizer,
+    readout, division; read after the write).
+    q, k: [N, L, dk]; v: [N, L, dv]; S0: [N, dk, dv] or None; z0: [N, dk] or
+    None.  Returns (o [N, L, dv], S_final [N, dk, dv], z_final [N, dk]), fp64.
+    """
+    q, k, v = (_widen(t, qkv_dtype) for t in (q, k, v))
+    fq, fk = elu1(q), elu1(k)
+    N, L, dk = q.shape
+    ones = np.ones((N, L))
+    num, S = forward(fq, fk, v, None, ones, S0, qkv_dtype="f64", gate_dtype="f64",
+                     alpha_mode="none", delta=False, threads=threads)
+    z_prev = np.zeros((N, dk)) if z0 is None else np.asarray(z0, dtype=np.float64)
+    z = z_prev[:, None, :] + np.cumsum(fk, axis=1)
+    den = np.sum(fq * z, axis=-1)
+    return num / den[:, :, None], S, (z[:, -1] if L else z_prev.copy())
 
 
 # ---------------------------------------------------------------------------
