@@ -4,7 +4,9 @@ Prints ONE JSON line.  Headline: chunkwise prefill (kda_chunk_fwd) on the
 Gated DeltaNet workload B=4, H=16, L=4096, d_k=d_v=128, bf16 q/k/v, fp32 gates
 and state; one step = one kda_chunk_fwd over that batch (o and S_final
 written).  Decode leg in the same line: the KDA decode workload, 256 sequences
-x 32 heads, fp32 state updated in place for 64 steps.
+x 32 heads, fp32 state updated in place for 64 steps.  Linear attention leg:
+normalized linear attention (phi = elu + 1, kda_linear_attn_fwd) on the
+prefill workload's shape.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload N]
 
@@ -225,6 +227,54 @@ def bench_decode(torch, kda, gen, w):
     return wall, kern
 
 
+def bench_linear_attention(torch, kda, gen, w, steps, warmup):
+    """Normalized linear attention (phi = elu + 1) on the prefill workload's
+    shape: raw q, k, v drawn with the same recipe, no decay or gates."""
+    wl = gen.custom(B=w.B, H=w.H, L=w.L, dk=w.dk, dv=w.dv, qkv_dtype=w.qkv_dtype,
+                    gate_dtype="f32", alpha_mode="none", s0_std=None, seed=w.seed)
+    log(f"linear attention on {w.B}x{w.H}x{w.L} d={w.dk}: drawing inputs")
+    x = gen.prefill_inputs(wl, threads=16, raw=True)
+    d = [to_dev(torch, x[n], w.qkv_dtype) for n in ("q", "k", "v")]
+    o = torch.empty((w.B, w.H, w.L, w.dv), dtype=d[2].dtype, device="cuda:0")
+    Sf = torch.empty((w.B, w.H, w.dk, w.dv), dtype=torch.float32, device="cuda:0")
+    zf = torch.empty((w.B, w.H, w.dk), dtype=torch.float32, device="cuda:0")
+    call = lambda: kda.linear_attn_fwd(*d, o=o, S_final=Sf, z_final=zf)
+    for _ in range(warmup):
+        call()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        call()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    kern = kernel_times(torch, kda, steps, call)
+    _, ms = kern["kda_inter_scalar_kernel"]
+    e = esize(w.qkv_dtype)
+    th = w.B * w.H * w.L
+    # q, k, v read, o written; S_final and z_final written
+    bytes_ = th * e * (2 * w.dk + 2 * w.dv) + w.B * w.H * (w.dk * w.dv + w.dk) * 4
+    C = 64 if w.qkv_dtype == "bf16" else 32
+    # Q S, S update (2 dk dv each), P and P V (C dk, C dv), z (C dk): flops per token-head
+    flops = th * (4 * w.dk * w.dv + 2 * C * (2 * w.dk + w.dv))
+    gbs = bytes_ / (ms * 1e-3) / 1e9
+    tflops = flops / (ms * 1e-3) / 1e12
+    fper, fms = kern.get("kda_feature_map_kernel", (0, 0.0))
+    fbytes = 2 * th * w.dk * e   # q read, phi(q) written
+    log(f"linear attention: {wall * 1e3 / steps:.4f} ms/step wall, state pass avg {ms * 1e3:.1f} us, "
+        f"{gbs:.0f} GB/s, {tflops:.1f} TFLOP/s; feature map avg {fms * 1e3:.1f} us, "
+        f"{fbytes / max(fms * 1e-3, 1e-12) / 1e9:.0f} GB/s")
+    return {"shape": f"b{w.B}_h{w.H}_l{w.L}_d{w.dk}_{w.qkv_dtype}",
+            "tokens_per_s": th / w.H / (wall / steps), "unit": "tokens/s",
+            "ms_per_step": wall * 1e3 / steps,
+            "kernel": "kda_inter_scalar_kernel (linear attention instance)",
+            "avg_kernel_us": ms * 1e3, "algorithmic_bytes_per_launch": bytes_,
+            "algorithmic_flops_per_launch": flops,
+            "hbm_frac": gbs / HBM_PEAK_GBS, "GB/s": gbs, "TFLOP/s": tflops,
+            "feature_map": {"kernel": "kda_feature_map_kernel", "avg_us": fms * 1e3,
+                            "algorithmic_bytes_per_launch": fbytes,
+                            "GB/s": fbytes / max(fms * 1e-3, 1e-12) / 1e9}}
+
+
 def cpu_baseline(gen, w, x, min_seconds=10.0, max_passes=64):
     """The fp64 oracle (C, threads over (head, 32-column block)) on the whole
     prefill workload, repeated until about min_seconds of CPU time have gone."""
@@ -254,6 +304,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", type=int, default=2, help="prefill workload number (1-4)")
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-linear-attention", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run one plain 256 MiB device copy (a known-size "
@@ -356,6 +407,9 @@ def main():
                          "algorithmic_bytes_per_launch": dbytes,
                          "avg_kernel_us": dms * 1e3},
         }
+    if not args.no_linear_attention:
+        out["linear_attention"] = bench_linear_attention(torch, kda, gen, w, args.steps,
+                                                         args.warmup)
     if not args.no_cpu:
         out["cpu_baseline"] = cpu_baseline(gen, w, x)
     print(json.dumps(out), flush=True)

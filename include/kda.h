@@ -216,6 +216,36 @@ int kda_chunk_fwd_varlen(const kda_shape* shape, uint32_t flags, const int32_t* 
 size_t kda_chunk_fwd_varlen_workspace_bytes(const kda_shape* shape, int64_t max_seqlen);
 
 /*
+ * Normalized linear attention with the feature map phi(x) = elu(x) + 1, the
+ * recurrent mixer the delta rule improves on ("22,580: From GPT-2 to Kimi K3"
+ * (yichencityu.github.io), section 04; "22,580: GPT-2 to Kimi K3, explained"
+ * (zharfai.com), "Linear attention collapses history into a fixed state").
+ * Per (b, h), with phi applied to the raw q_t and k_t:
+ *     S_t = S_{t-1} + phi(k_t)^T v_t      z_t = z_{t-1} + phi(k_t)
+ *     o_t = phi(q_t) S_t / (phi(q_t) . z_t)
+ * (read after the write, as for kda_chunk_fwd), computed chunkwise with the
+ * same state pass as kda_chunk_fwd's one-decay path, without the delta term.
+ *   shape      alpha_mode must be KDA_ALPHA_NONE (else KDA_ERR_ALPHA_MODE);
+ *              gate_dtype is not used.
+ *   q, k       [B,H,L,dk] raw (before phi); v, o [B,H,L,dv] in qkv_dtype.
+ *   S0, z0     [B,H,dk,dv] and [B,H,dk] fp32 initial state and normalizer,
+ *              or NULL for zero.  With S0 = z0 = 0 the first token gives
+ *              o_1 = v_1.
+ *   S_final, z_final  [B,H,dk,dv], [B,H,dk] fp32 outputs or NULL; each may be
+ *              the same buffer as S0 / z0 (in place).
+ *   workspace  device scratch of kda_linear_attn_fwd_workspace_bytes(shape)
+ *              bytes: phi(q) in qkv_dtype, written once per call and read by
+ *              the state pass; not kept after the call.
+ * Errors and checks as for kda_chunk_fwd.
+ */
+int kda_linear_attn_fwd(const kda_shape* shape, const void* q, const void* k, const void* v,
+                        const float* S0, const float* z0, void* o, float* S_final,
+                        float* z_final, void* workspace, size_t workspace_bytes,
+                        void* hip_stream);
+/* Workspace bytes kda_linear_attn_fwd needs (0 if it would reject the shape). */
+size_t kda_linear_attn_fwd_workspace_bytes(const kda_shape* shape);
+
+/*
  * Kernel timing, for measurement tools (not part of the computation).  While
  * timing is on, every kernel that kda_chunk_fwd or kda_decode_step launches is
  * bracketed by two HIP events recorded on the call's stream; the event pairs

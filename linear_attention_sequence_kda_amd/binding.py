@@ -67,6 +67,10 @@ def library() -> ctypes.CDLL:
         lib.kda_chunk_fwd_varlen.argtypes = [sp, u32, vp, i64, vp, vp, vp, vp, vp, vp, vp, vp, vp,
                                              sz, vp]
         lib.kda_chunk_fwd_varlen.restype = ctypes.c_int
+        lib.kda_linear_attn_fwd.argtypes = [sp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+        lib.kda_linear_attn_fwd.restype = ctypes.c_int
+        lib.kda_linear_attn_fwd_workspace_bytes.argtypes = [sp]
+        lib.kda_linear_attn_fwd_workspace_bytes.restype = sz
         lib.kda_chunk_fwd_varlen_workspace_bytes.argtypes = [sp, i64]
         lib.kda_chunk_fwd_varlen_workspace_bytes.restype = sz
         lib.kda_chunk_fwd_ex.argtypes = [sp, u32, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
@@ -144,6 +148,7 @@ def _stream(t) -> int:
 
 
 KERNELS = ("kda_intra_kernel", "kda_inter_kernel", "kda_inter_scalar_kernel",
+           "kda_feature_map_kernel",
            "kda_decode_kernel")
 
 
@@ -284,6 +289,51 @@ def chunk_fwd_varlen(q, k, v, log_alpha, beta, cu_seqlens, max_seqlen: int, S0=N
                                   _ptr(workspace), ws_given, _stream(v))
     _check(rc)
     return o, (S_final if output_final_state else None)
+
+
+def linear_attn_fwd(q, k, v, S0=None, z0=None, *, output_final_state: bool = True, o=None,
+                    S_final=None, z_final=None, workspace=None):
+    """Normalized linear attention, phi = elu + 1: returns (o, S_final, z_final).
+
+    q, k: [B,H,L,dk] raw (before phi); v: [B,H,L,dv] (bf16 or fp32, same
+    dtype); S0: [B,H,dk,dv] fp32 or None; z0: [B,H,dk] fp32 or None.  The
+    final state and normalizer are fp32 (None unless output_final_state).
+    ``workspace``: a uint8 GPU tensor of at least
+    kda_linear_attn_fwd_workspace_bytes bytes (else one is allocated per call).
+    """
+    torch = _torch()
+    B, H, L, dk = q.shape
+    dv = v.shape[-1]
+    for name, t in (("q", q), ("k", k), ("v", v), ("S0", S0), ("z0", z0)):
+        if t is not None:
+            _require(t, name)
+    for name, t in (("S0", S0), ("z0", z0)):
+        if t is not None and t.dtype != torch.float32:
+            raise TypeError(f"{name} must be float32")
+    if o is None:
+        o = torch.empty((B, H, L, dv), dtype=v.dtype, device=v.device)
+    if output_final_state:
+        if S_final is None:
+            S_final = torch.empty((B, H, dk, dv), dtype=torch.float32, device=v.device)
+        if z_final is None:
+            z_final = torch.empty((B, H, dk), dtype=torch.float32, device=v.device)
+    shape = KdaShape(B, H, L, dk, dv, _dtype_code(q), KDA_F32, KDA_ALPHA_NONE)
+    lib = library()
+    ws = lib.kda_linear_attn_fwd_workspace_bytes(ctypes.byref(shape))
+    if workspace is None:
+        workspace = torch.empty(ws, dtype=torch.uint8, device=v.device) if ws else None
+    else:
+        _require(workspace, "workspace")
+    ws_given = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    rc = lib.kda_linear_attn_fwd(ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(v), _ptr(S0),
+                                 _ptr(z0), _ptr(o),
+                                 _ptr(S_final) if output_final_state else None,
+                                 _ptr(z_final) if output_final_state else None,
+                                 _ptr(workspace), ws_given, _stream(v))
+    _check(rc)
+    if not output_final_state:
+        return o, None, None
+    return o, S_final, z_final
 
 
 def decode_step(q, k, v, log_alpha, beta, S, *, o=None, flags: Optional[int] = None):

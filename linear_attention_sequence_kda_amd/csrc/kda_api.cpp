@@ -20,9 +20,10 @@ thread_local std::string g_last_error;
 // ---- kernel timing (kda_timing_*) --------------------------------------------
 // While enabled, each kernel launch is bracketed by two events recorded on the
 // launch's stream; the pairs are kept until read or reset.
-enum KernelId { K_INTRA = 0, K_INTER, K_INTER_SCALAR, K_DECODE, K_COUNT };
+enum KernelId { K_INTRA = 0, K_INTER, K_INTER_SCALAR, K_DECODE, K_FEATURE, K_COUNT };
 const char* const kKernelNames[K_COUNT] = {"kda_intra_kernel", "kda_inter_kernel",
-                                           "kda_inter_scalar_kernel", "kda_decode_kernel"};
+                                           "kda_inter_scalar_kernel", "kda_decode_kernel",
+                                           "kda_feature_map_kernel"};
 struct TimedLaunch {
     int kernel;
     hipEvent_t start, stop;
@@ -421,6 +422,87 @@ int kda_chunk_fwd_varlen(const kda_shape* s, uint32_t flags, const int32_t* cu_s
                         log_alpha, beta, S0, o, S_final, workspace, workspace_bytes, hip_stream);
 }
 
+
+size_t kda_linear_attn_fwd_workspace_bytes(const kda_shape* s) {
+    if (check_shape(s, false) != KDA_OK || s->alpha_mode != KDA_ALPHA_NONE) return 0;
+    return (size_t)(s->B * s->H * s->L * s->dk * elem_size(s->qkv_dtype));
+}
+
+int kda_linear_attn_fwd(const kda_shape* s, const void* q, const void* k, const void* v,
+                        const float* S0, const float* z0, void* o, float* S_final,
+                        float* z_final, void* workspace, size_t workspace_bytes,
+                        void* hip_stream) {
+    int rc = check_shape(s, false);
+    if (rc != KDA_OK) return rc;
+    if (s->alpha_mode != KDA_ALPHA_NONE) return KDA_ERR_ALPHA_MODE;
+    const int64_t bh = s->B * s->H;
+    const int64_t tok = bh * s->L;
+    const int eq = elem_size(s->qkv_dtype);
+    if (tok > 0 && (!q || !k || !v || !o)) return KDA_ERR_NULL;
+    const void* ptrs[] = {q, k, v, S0, z0, o, S_final, z_final, workspace};
+    for (const void* p : ptrs)
+        if (p && !aligned16(p)) return KDA_ERR_ALIGN;
+    const int64_t one = tok * s->dk * eq;
+    const int64_t wsb = (int64_t)kda_linear_attn_fwd_workspace_bytes(s);
+    if (wsb > 0 && (!workspace || workspace_bytes < (size_t)wsb)) return KDA_ERR_WORKSPACE;
+    const Span sq = span_of(q, one), sk = span_of(k, one),
+               sv = span_of(v, tok * s->dv * eq), so = span_of(o, tok * s->dv * eq),
+               s0 = span_of(S0, bh * s->dk * s->dv * 4), sf = span_of(S_final, bh * s->dk * s->dv * 4),
+               z0s = span_of(z0, bh * s->dk * 4), zfs = span_of(z_final, bh * s->dk * 4),
+               sw = span_of(workspace, wsb);
+    // outputs overlap no input (S_final may be S0 and z_final may be z0 exactly)
+    const Span ins[] = {sq, sk, sv};
+    const Span outs[] = {so, sf, zfs};
+    for (const Span& x : outs)
+        for (const Span& y : ins)
+            if (overlaps(x, y)) return KDA_ERR_ALIAS;
+    if (overlaps(so, s0) || overlaps(so, z0s) || overlaps(so, sf) || overlaps(so, zfs) ||
+        overlaps(sf, zfs) || overlaps(sf, z0s) || overlaps(zfs, s0))
+        return KDA_ERR_ALIAS;
+    if (overlaps(sf, s0) && (const void*)S_final != (const void*)S0) return KDA_ERR_ALIAS;
+    if (overlaps(zfs, z0s) && (const void*)z_final != (const void*)z0) return KDA_ERR_ALIAS;
+    const Span all[] = {sq, sk, sv, so, s0, sf, z0s, zfs};
+    for (const Span& x : all)
+        if (overlaps(sw, x)) return KDA_ERR_ALIAS;
+    if (bh == 0) return KDA_OK;
+
+    const int qbf = s->qkv_dtype == KDA_BF16;
+    const int C = kda::chunk_len(qbf);
+    const hipStream_t stream = (hipStream_t)hip_stream;
+    void* fq = workspace;
+    hipError_t err = hipSuccess;
+    if (tok > 0) {
+        kda::FeatureParams fp{q, fq, one / 16};
+        err = timed_launch(K_FEATURE, stream, [&] { return kda::launch_feature_map(fp, qbf, stream); });
+    }
+    kda::InterParams xp;
+    xp.q = fq;
+    xp.k = k;
+    xp.v = v;
+    xp.ws = nullptr;
+    xp.S_in = S0;
+    xp.S_out = S_final;
+    xp.o = o;
+    xp.L = s->L;
+    xp.c0 = 0;
+    xp.ncs = (int)((s->L + C - 1) / C);
+    xp.BH = (int)bh;
+    xp.DV = (int)s->dv;
+    xp.n_slices = 0;
+    xp.linear_attn = 1;
+    xp.z_in = z0;
+    xp.z_out = z_final;
+    const int nv = kda::chunk_slice_width((int)s->dk, (int)s->dv, qbf, bh);
+    if (err == hipSuccess)
+        err = timed_launch(K_INTER_SCALAR, stream, [&] {
+            return kda::launch_inter_scalar(xp, (int)s->dk, qbf, nv, stream);
+        });
+    if (err != hipSuccess) {
+        g_last_error = std::string("kda_linear_attn_fwd: ") + hipGetErrorString(err);
+        return KDA_ERR_HIP;
+    }
+    return KDA_OK;
+}
 
 int kda_decode_step(const kda_shape* s, const void* q, const void* k, const void* v,
                     const void* log_alpha, const void* beta, float* S, void* o,

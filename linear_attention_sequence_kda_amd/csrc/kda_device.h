@@ -386,4 +386,28 @@ __device__ __forceinline__ float sumsq16(uint4 u, float) {
     return a * a + b * b + c * c + d * d;
 }
 
+// ---- linear attention feature map phi(x) = elu(x) + 1 (positive) ----------
+__device__ __forceinline__ float elu1(float x) { return x > 0.f ? x + 1.f : __expf(x); }
+__device__ __forceinline__ bf16x8 elu1(bf16x8 v) {
+    bf16x8 r;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) r[i] = (bf16)elu1((float)v[i]);
+    return r;
+}
+__device__ __forceinline__ floatx4 elu1(floatx4 v) {
+    floatx4 r;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) r[i] = elu1(v[i]);
+    return r;
+}
+// MFMA B operand of ones over tokens kk KS + W (lane/16) .. + W - 1 that are
+// below n (zeros for padded tokens)
+template <typename E>
+__device__ __forceinline__ typename Frag<E>::T ones_below(int first, int n) {
+    typename Frag<E>::T r;
+#pragma unroll
+    for (int i = 0; i < Frag<E>::W; ++i) r[i] = from_f32<E>(first + i < n ? 1.f : 0.f);
+    return r;
+}
+
 }  // namespace kda

@@ -35,6 +35,19 @@
 // Inputs are read through buffer resources bounded by the head's sequence, so
 // the ragged last chunk reads zeros past token L and its o stores past token L
 // are dropped, with no branch.
+//
+// LA instance: normalized linear attention with the feature map
+// phi(x) = elu(x) + 1 ("22,580: From GPT-2 to Kimi K3", section 4: the state
+// takes phi(k)^T v, a normalizer z takes phi(k), and the output is
+// phi(q) S / (phi(q) z), read after the write).  The same walk with
+// alpha = beta = 1 and no delta term: X = V, u = X (no record, no T'), and
+//   den_r = phi(q_r) z_prev + sum_{j <= r} P_rj,   o = (Q S + P V) / den
+//   z <- z + phi(K)^T 1   (an MFMA of the K^T operand against ones over the
+//                         chunk's valid tokens)
+// q arrives as phi(q) (kda_feature_map_kernel writes it once per call: every
+// compute wave holds q fragments, so applying phi there would repeat the
+// exponentials for each wave and column slice); the data waves apply phi to k
+// on its way into the ring, once per workgroup.
 #include "kda_device.h"
 #include "kda_internal.h"
 
@@ -87,8 +100,9 @@ struct ScalarInterCfg {
 };
 
 // NORM: q and k arrive raw (KDA_IN_NORM_QK); a separate instance, so the
-// registers the row norms take never cost the plain path.
-template <class Cfg, bool NORM>
+// registers the row norms take never cost the plain path.  LA: linear
+// attention (see above).
+template <class Cfg, bool NORM, bool LA>
 __global__ void __launch_bounds__(Cfg::NT) kda_inter_scalar_kernel(InterParams prm) {
     typedef typename Cfg::E E;
     typedef Frag<E> F;
@@ -144,7 +158,9 @@ __global__ void __launch_bounds__(Cfg::NT) kda_inter_scalar_kernel(InterParams p
         // waves' own q requests go out at the end of the first).  Past the last chunk the
         // last one is loaded again, and o pieces beyond the tile go past the
         // buffer end.
-        constexpr int NL = (Cfg::NPIECE + NWP - 1) / NWP;
+        // linear attention reads no record: k and the v slice only
+        constexpr int NPIECE = LA ? Cfg::NKP + Cfg::NVP : Cfg::NPIECE;
+        constexpr int NL = (NPIECE + NWP - 1) / NWP;
         constexpr int PPO = NV * ESZ / 16, NPO = C * PPO;  // o pieces per chunk
         constexpr int NS = (NPO + 64 * NWP - 1) / (64 * NWP);
         const int pw = w - NWC;
@@ -161,7 +177,7 @@ __global__ void __launch_bounds__(Cfg::NT) kda_inter_scalar_kernel(InterParams p
 #pragma unroll
         for (int j = 0; j < NL; ++j) {
             const int i0 = pw + NWP * j;
-            const int i = i0 < Cfg::NPIECE ? i0 : pw;
+            const int i = i0 < NPIECE ? i0 : pw;
             int sidx;
             uint32_t g, d;
             if (i < Cfg::NKP) {
@@ -194,7 +210,7 @@ __global__ void __launch_bounds__(Cfg::NT) kda_inter_scalar_kernel(InterParams p
             }
             src[j] = __builtin_amdgcn_readfirstlane(sidx);
             goff[j] = g;
-            loff[j] = i0 < Cfg::NPIECE ? d : ~0u;
+            loff[j] = i0 < NPIECE ? d : ~0u;
         }
         struct DSet {
             v4i v[NL];
@@ -219,7 +235,19 @@ __global__ void __launch_bounds__(Cfg::NT) kda_inter_scalar_kernel(InterParams p
             char* slot = ring + (cs & 1) * SLOT;
             char* sink = smem + Cfg::O_SINK + l * 16;
 #pragma unroll
-            for (int j = 0; j < NL; ++j) *(v4i*)(loff[j] == ~0u ? sink : slot + loff[j]) = st.v[j];
+            for (int j = 0; j < NL; ++j) {
+                v4i x = st.v[j];
+                if constexpr (LA) {
+                    // phi(k) on the way into the ring
+                    if (src[j] == 1) {
+                        if constexpr (ESZ == 2)
+                            x = __builtin_bit_cast(v4i, elu1(__builtin_bit_cast(bf16x8, x)));
+                        else
+                            x = __builtin_bit_cast(v4i, elu1(__builtin_bit_cast(floatx4, x)));
+                    }
+                }
+                *(v4i*)(loff[j] == ~0u ? sink : slot + loff[j]) = x;
+            }
         };
         // o tile of chunk cs (cs < 0: every store falls past the buffer end)
         auto store_o = [&](int cs) {
@@ -305,6 +333,19 @@ __global__ void __launch_bounds__(Cfg::NT) kda_inter_scalar_kernel(InterParams p
         }
     // blocks of P above the diagonal stay zero
     for (int i = tid; i < C * PC; i += 64 * NWC) sP[i] = from_f32<E>(0.f);
+    // linear attention: u and the state update's operand are X itself, and
+    // the u areas hold the normalizer instead: z_prev of two chunks [2][DK]
+    // and each wave group's share of the row sums of P plus phi(q) z_prev
+    // [NWC/NB][C]
+    E* sUTc = LA ? sXT : sUT;
+    E* sUHTc = LA ? sXT : sUHT;
+    float* sZ = (float*)(smem + Cfg::O_UT);
+    float* sRow = sZ + 2 * DK;
+    static_assert(!LA || (2 * DK + (NWC / NB) * C) * 4 <= NV * PC * ESZ, "normalizer in LDS");
+    // z lives in LDS only (z_prev of chunk c in half c % 2)
+    if constexpr (LA) {
+        for (int i = tid; i < DK; i += 64 * NWC) sZ[i] = prm.z_in ? prm.z_in[(int64_t)bh * DK + i] : 0.f;
+    }
     __syncthreads();
 
     // Every tile and P block of wave w has row block Rw.  q rows Rw come
@@ -345,6 +386,19 @@ __global__ void __launch_bounds__(Cfg::NT) kda_inter_scalar_kernel(InterParams p
         // KDA_IN_NORM_QK: q and k arrive raw; the row norms, summed over the
         // four lanes that hold a row's fragments, scale the products.
         float qinv = 1.f;  // 1/|q| of row 16 Rw + lr
+        // LA: this wave's share of phi(q_r) . z_prev, row 16 Rw + lr (the
+        // waves of a row block split the channel steps kk between them)
+        float qz = 0.f;
+        if constexpr (LA) {
+            const float* zp = sZ + (cs & 1) * DK;
+#pragma unroll
+            for (int kk = 0; kk < NKA; ++kk)
+                if (kk % (NWC / NB) == jw)
+#pragma unroll
+                    for (int e = 0; e < W; ++e)
+                        qz += to_f32(qc.f[kk][e]) * zp[KS * kk + W * lq + e];
+            qz = sum_over_lq(qz);
+        }
         if constexpr (norm_qk) {
             float sq = 0.f;
 #pragma unroll
@@ -362,7 +416,20 @@ __global__ void __launch_bounds__(Cfg::NT) kda_inter_scalar_kernel(InterParams p
 #pragma unroll
                 for (int kk = 0; kk < NKA; ++kk) {
                     st[kk] = F::load(pst + KS * kk);
-                    kr[kk] = F::load(pkr + KS * kk);
+                    if constexpr (!LA) kr[kk] = F::load(pkr + KS * kk);
+                }
+                if constexpr (LA) {
+                    // X = V: no delta term; Q S kept for o
+                    floatx4 qs = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                    for (int kk = 0; kk < NKA; ++kk) qs = F::mma(qs, st[kk], qc.f[kk]);
+                    oacc[i] = qs;
+                    floatx4 xv;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        xv[e] = to_f32(sV[(16 * R + 4 * lq + e) * PV + 16 * vb + lr]);
+                    store_acc_transposed<E>(sXT + (16 * vb) * PC + 16 * R, PC, xv);
+                    continue;
                 }
                 // (K S)[16R + 4lq + e][16vb + lr] -> X = V - e^g (K S), stored transposed
                 floatx4 acc = {0.f, 0.f, 0.f, 0.f};
@@ -394,7 +461,8 @@ __global__ void __launch_bounds__(Cfg::NT) kda_inter_scalar_kernel(InterParams p
         // lane holds (Q K^T)[r = 16 Rw + lr][j = 16J + 4lq + e]
         {
             const int r = 16 * Rw + lr;
-            const float gr = rs[r];
+            const float gr = LA ? 0.f : rs[r];
+            float rsum = 0.f;  // LA: this wave's share of sum_j P_rj
             for (int J = jw; J <= Rw; J += NWC / NB) {
                 floatx4 pa = {0.f, 0.f, 0.f, 0.f};
                 const E* pkj = sK + (16 * J + lr) * PK + W * lq;
@@ -403,7 +471,8 @@ __global__ void __launch_bounds__(Cfg::NT) kda_inter_scalar_kernel(InterParams p
                 for (int kk = 0; kk < NKA; ++kk) kj[kk] = F::load(pkj + KS * kk);
 #pragma unroll
                 for (int kk = 0; kk < NKA; ++kk) pa = F::mma(pa, kj[kk], qc.f[kk]);
-                const floatx4 gj = *(const floatx4*)(rs + 16 * J + 4 * lq);
+                floatx4 gj = {0.f, 0.f, 0.f, 0.f};
+                if constexpr (!LA) gj = *(const floatx4*)(rs + 16 * J + 4 * lq);
                 floatx4 sc = {qinv, qinv, qinv, qinv};
                 if constexpr (norm_qk) {
                     float sk = 0.f;
@@ -417,9 +486,18 @@ __global__ void __launch_bounds__(Cfg::NT) kda_inter_scalar_kernel(InterParams p
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
                     const int j = 16 * J + 4 * lq + e;
-                    v[e] = (J < Rw || j <= r) ? pa[e] * sc[e] * exp_neg(gr - gj[e]) : 0.f;
+                    if constexpr (LA) {
+                        v[e] = (J < Rw || j <= r) ? pa[e] : 0.f;
+                        rsum += v[e];
+                    } else {
+                        v[e] = (J < Rw || j <= r) ? pa[e] * sc[e] * exp_neg(gr - gj[e]) : 0.f;
+                    }
                 }
                 st4<E>(sP + r * PC + 16 * J + 4 * lq, v);
+            }
+            if constexpr (LA) {
+                rsum = sum_over_lq(rsum);
+                if (lq == 0) sRow[jw * C + r] = rsum + qz;
             }
         }
         load_q(qc, cs + 2);
@@ -429,7 +507,7 @@ __global__ void __launch_bounds__(Cfg::NT) kda_inter_scalar_kernel(InterParams p
 #pragma unroll
         for (int i = 0; i < ITL; ++i) {
             const int vb = jw + (NWC / NB) * i;
-            if (vb < NVB) {
+            if (!LA && vb < NVB) {
                 const int R = Rw;
                 const int K = ((16 * (R + 1) + KS - 1) / KS) * KS;
                 floatx4 acc = {0.f, 0.f, 0.f, 0.f};
@@ -444,7 +522,7 @@ __global__ void __launch_bounds__(Cfg::NT) kda_inter_scalar_kernel(InterParams p
         __syncthreads();
 
         // ---------------- phase 3: S update, o ----------------
-        const float gnv = rs[3 * C];
+        const float gnv = LA ? 1.f : rs[3 * C];
         if (w < NSW) {
             constexpr int NKP = C / KS;
             typename F::T kt[CBW][NKP];
@@ -454,7 +532,7 @@ __global__ void __launch_bounds__(Cfg::NT) kda_inter_scalar_kernel(InterParams p
                 for (int kk = 0; kk < NKP; ++kk) kt[a][kk] = load_frag_tr(sK, PK, KS * kk, 16 * (CBW * w + a));
 #pragma unroll
             for (int b = 0; b < NVB; ++b) {
-                const E* pu = sUHT + (16 * b + lr) * PC + W * lq;
+                const E* pu = sUHTc + (16 * b + lr) * PC + W * lq;
                 typename F::T uf[NKP];
 #pragma unroll
                 for (int kk = 0; kk < NKP; ++kk) uf[kk] = F::load(pu + KS * kk);
@@ -467,6 +545,23 @@ __global__ void __launch_bounds__(Cfg::NT) kda_inter_scalar_kernel(InterParams p
                     store_acc_transposed<E>(sST + (16 * b) * PK + 16 * (CBW * w + a), PK, acc);
                 }
             }
+            if constexpr (LA) {
+                // z += phi(K)^T 1 over this chunk's valid tokens; z_prev of
+                // the next chunk goes to the other half of sZ
+                const int64_t t0 = (prm.c0 + cs) * C;
+                const int n = (int)(L - t0 < C ? L - t0 : C);
+                const float* zp = sZ + (cs & 1) * DK;
+                float* zn = sZ + ((cs + 1) & 1) * DK;
+#pragma unroll
+                for (int a = 0; a < CBW; ++a) {
+                    const int c0 = 16 * (CBW * w + a) + 4 * lq;
+                    floatx4 acc = *(const floatx4*)(zp + c0);
+#pragma unroll
+                    for (int kk = 0; kk < NKP; ++kk)
+                        acc = F::mma(acc, kt[a][kk], ones_below<E>(KS * kk + W * lq, n));
+                    if (lr == 0) *(floatx4*)(zn + c0) = acc;
+                }
+            }
         }
 #pragma unroll
         for (int i = 0; i < ITL; ++i) {
@@ -475,7 +570,15 @@ __global__ void __launch_bounds__(Cfg::NT) kda_inter_scalar_kernel(InterParams p
                 const int R = Rw;
                 const int K = ((16 * (R + 1) + KS - 1) / KS) * KS;
                 floatx4 acc = oacc[i];
-                acc = mma_block<E>(acc, sUT + (16 * vb) * PC, PC, sP + (16 * R) * PC, PC, K);
+                acc = mma_block<E>(acc, sUTc + (16 * vb) * PC, PC, sP + (16 * R) * PC, PC, K);
+                if constexpr (LA) {
+                    // lane holds row 16R + lr: divide by phi(q_r) z_r, the sum
+                    // of the row block's waves' shares
+                    float den = 0.f;
+#pragma unroll
+                    for (int g = 0; g < NWC / NB; ++g) den += sRow[g * C + 16 * R + lr];
+                    acc = acc * (1.f / den);
+                }
                 st4<E>(sO + (cs & 1) * C * PV + (16 * R + lr) * PV + 16 * vb + 4 * lq, acc);
             }
         }
@@ -492,6 +595,11 @@ __global__ void __launch_bounds__(Cfg::NT) kda_inter_scalar_kernel(InterParams p
         chunk(cs + 1, qb);
     }
 
+    if constexpr (LA) {
+        // the last chunk's barrier has published z; chunk c wrote half (c+1) % 2
+        if (prm.z_out)
+            for (int i = tid; i < DK; i += 64 * NWC) prm.z_out[(int64_t)bh * DK + i] = sZ[(ncs & 1) * DK + i];
+    }
     // ---- state out --------------------------------------------------------------
     if (prm.S_out && w < NSW) {
         float* so = prm.S_out + (int64_t)bh * DK * DV + v0;
@@ -512,12 +620,15 @@ template <int DK, int NV, int C, typename E>
 static hipError_t launch_scalar_cfg(const InterParams& prm, hipStream_t stream) {
     typedef ScalarInterCfg<DK, NV, C, E> Cfg;
     const int total = prm.BH * prm.n_slices;
-    if (prm.flags & KDA_IN_NORM_QK)
-        hipLaunchKernelGGL((kda_inter_scalar_kernel<Cfg, true>), dim3(total), dim3(Cfg::NT), 0,
-                           stream, prm);
+    if (prm.linear_attn)
+        hipLaunchKernelGGL((kda_inter_scalar_kernel<Cfg, false, true>), dim3(total),
+                           dim3(Cfg::NT), 0, stream, prm);
+    else if (prm.flags & KDA_IN_NORM_QK)
+        hipLaunchKernelGGL((kda_inter_scalar_kernel<Cfg, true, false>), dim3(total),
+                           dim3(Cfg::NT), 0, stream, prm);
     else
-        hipLaunchKernelGGL((kda_inter_scalar_kernel<Cfg, false>), dim3(total), dim3(Cfg::NT), 0,
-                           stream, prm);
+        hipLaunchKernelGGL((kda_inter_scalar_kernel<Cfg, false, false>), dim3(total),
+                           dim3(Cfg::NT), 0, stream, prm);
     return hipGetLastError();
 }
 

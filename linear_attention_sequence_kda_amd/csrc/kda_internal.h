@@ -126,6 +126,11 @@ struct InterParams {
     uint32_t flags = 0;     // kda_input_flags (the scalar kernel normalizes q, k)
     const int32_t* cu = nullptr;  // packed sequences, as in IntraParams
     int H = 1;
+    // normalized linear attention (scalar kernel only): no records; the
+    // normalizer z [BH, DK] fp32 in (null: zero) and out (null: not written)
+    int linear_attn = 0;
+    const float* z_in = nullptr;
+    float* z_out = nullptr;
 };
 
 hipError_t launch_intra(const IntraParams& prm, int dk, int dv, int qkv_bf16, int alpha_mode,
@@ -154,6 +159,14 @@ struct DecodeParams {
     int H = 1;
     uint32_t flags = 0;     // kda_input_flags
 };
+
+// phi(q) of normalized linear attention: n16 16-byte pieces.
+struct FeatureParams {
+    const void* q;
+    void* fq;
+    int64_t n16;
+};
+hipError_t launch_feature_map(const FeatureParams& prm, int qkv_bf16, hipStream_t stream);
 
 // State-column slice width the inter-chunk kernel uses for this problem.
 int chunk_slice_width(int dk, int dv, int qkv_bf16, int64_t BH);

@@ -273,3 +273,31 @@ def test_varlen_host_checks(lib):
     # no sequences: nothing to do, no pointer needed
     none = {n: None for n in b}
     assert varlen(lib, shape(B=0, H=4, L=0), none, 0) == 0
+
+
+def test_linear_attn_host_checks(lib):
+    b = dict(bufs(), z0=BASE + 21 * 64 * MB, zf=BASE + 22 * 64 * MB)
+    s = shape(mode=binding.KDA_ALPHA_NONE)
+
+    def la(s_, wsb=1 << 30, **kw):
+        x = dict(b, **kw)
+        return lib.kda_linear_attn_fwd(ctypes.byref(s_) if s_ is not None else None, x["q"],
+                                       x["k"], x["v"], x["S0"], x["z0"], x["o"], x["Sf"],
+                                       x["zf"], x["ws"], wsb, None)
+    assert la(None) == 1
+    assert la(shape(mode=binding.KDA_ALPHA_CHANNEL)) == 4     # no decay in this op
+    assert la(shape(mode=binding.KDA_ALPHA_NONE, dk=96)) == 2
+    assert la(s, q=0) == 1
+    assert la(s, z0=b["z0"] + 4) == 5
+    assert la(s, o=b["q"]) == 7
+    assert la(s, zf=b["v"]) == 7
+    assert la(s, zf=b["Sf"]) == 7
+    assert la(s, zf=b["z0"] + 16) == 7                       # partial overlap with z0
+    assert la(s, ws=b["v"]) == 7                             # workspace over an input
+    # phi(q) in the input type
+    need = lib.kda_linear_attn_fwd_workspace_bytes(ctypes.byref(s))
+    assert need == 2 * 3 * 100 * 128 * 2
+    assert la(s, wsb=need - 1) == 6
+    assert lib.kda_linear_attn_fwd_workspace_bytes(ctypes.byref(shape())) == 0  # has decay
+    none = {n: None for n in b}
+    assert la(shape(B=0, mode=binding.KDA_ALPHA_NONE), wsb=0, **none) == 0
