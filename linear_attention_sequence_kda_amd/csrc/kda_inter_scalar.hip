@@ -372,7 +372,7 @@ __global__ void __launch_bounds__(Cfg::NT) kda_inter_scalar_kernel(InterParams p
     };
 
     floatx4 oacc[ITL];
-    floatx4 kinv[ITL];  // KDA_IN_NORM_QK: 1/|k| of a tile's rows 16R + 4lq + e
+    floatx4 kinv;  // KDA_IN_NORM_QK: 1/|k| of rows 16 Rw + 4lq + e
     constexpr bool norm_qk = NORM;
     auto chunk = [&](int cs, QSet& qc) {
         const char* slot = ring + (cs & 1) * SLOT;
@@ -405,19 +405,80 @@ __global__ void __launch_bounds__(Cfg::NT) kda_inter_scalar_kernel(InterParams p
             for (int kk = 0; kk < NKA; ++kk) sq += frag_sumsq(qc.f[kk]);
             qinv = inv_norm(sum_over_lq(sq));
         }
+        // P blocks (Rw, J) for J = jw, jw + NWC / NB, ... <= Rw:
+        // lane holds (Q K^T)[r = 16 Rw + lr][j = 16J + 4lq + e]
+        const int r = 16 * Rw + lr;
+        const float gr = LA ? 0.f : rs[r];
+        float rsum = 0.f;  // LA: this wave's share of sum_j P_rj
+        auto p_block = [&](int J, const FT* kj) {
+            floatx4 pa = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int kk = 0; kk < NKA; ++kk) pa = F::mma(pa, kj[kk], qc.f[kk]);
+            floatx4 gj = {0.f, 0.f, 0.f, 0.f};
+            if constexpr (!LA) gj = *(const floatx4*)(rs + 16 * J + 4 * lq);
+            floatx4 sc = {qinv, qinv, qinv, qinv};
+            if constexpr (norm_qk) {
+                float sk = 0.f;
+#pragma unroll
+                for (int kk = 0; kk < NKA; ++kk) sk += frag_sumsq(kj[kk]);
+                const float kin = inv_norm(sum_over_lq(sk));  // row 16J + lr
+#pragma unroll
+                for (int e = 0; e < 4; ++e) sc[e] *= __shfl(kin, 4 * lq + e);
+            }
+            floatx4 v;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int j = 16 * J + 4 * lq + e;
+                if constexpr (LA) {
+                    v[e] = (J < Rw || j <= r) ? pa[e] : 0.f;
+                    rsum += v[e];
+                } else {
+                    v[e] = (J < Rw || j <= r) ? pa[e] * sc[e] * exp_neg(gr - gj[e]) : 0.f;
+                }
+            }
+            st4<E>(sP + r * PC + 16 * J + 4 * lq, v);
+        };
+        // blocks below the diagonal, each with its own K rows
+        for (int J = jw; J < Rw; J += NWC / NB) {
+            FT kj[NKA];
+            const E* pkj = sK + (16 * J + lr) * PK + W * lq;
+#pragma unroll
+            for (int kk = 0; kk < NKA; ++kk) kj[kk] = F::load(pkj + KS * kk);
+            p_block(J, kj);
+        }
+        // K rows Rw serve the diagonal block (if this wave owns it) and X,
+        // read once
+        const bool diag = jw <= Rw && (Rw - jw) % (NWC / NB) == 0;
+        FT kr[NKA];
+        if (!LA || diag) {
+            const E* pkr = sK + (16 * Rw + lr) * PK + W * lq;
+#pragma unroll
+            for (int kk = 0; kk < NKA; ++kk) kr[kk] = F::load(pkr + KS * kk);
+        }
+        if (diag) p_block(Rw, kr);
+        if constexpr (LA) {
+            rsum = sum_over_lq(rsum);
+            if (lq == 0) sRow[jw * C + r] = rsum + qz;
+        }
+        if constexpr (norm_qk) {
+            // 1/|k| of rows 16Rw + 4lq + e, from the lanes that own those rows
+            float sk = 0.f;
+#pragma unroll
+            for (int kk = 0; kk < NKA; ++kk) sk += frag_sumsq(kr[kk]);
+            const float kin = inv_norm(sum_over_lq(sk));
+#pragma unroll
+            for (int e = 0; e < 4; ++e) kinv[e] = __shfl(kin, 4 * lq + e);
+        }
+        // S^T rows vb serve X and Q S, read once per wave.
 #pragma unroll
         for (int i = 0; i < ITL; ++i) {
             const int vb = jw + (NWC / NB) * i;
             if (vb < NVB) {
                 const int R = Rw;
-                FT st[NKA], kr[NKA];
+                FT st[NKA];
                 const E* pst = sST + (16 * vb + lr) * PK + W * lq;
-                const E* pkr = sK + (16 * R + lr) * PK + W * lq;
 #pragma unroll
-                for (int kk = 0; kk < NKA; ++kk) {
-                    st[kk] = F::load(pst + KS * kk);
-                    if constexpr (!LA) kr[kk] = F::load(pkr + KS * kk);
-                }
+                for (int kk = 0; kk < NKA; ++kk) st[kk] = F::load(pst + KS * kk);
                 if constexpr (LA) {
                     // X = V: no delta term; Q S kept for o
                     floatx4 qs = {0.f, 0.f, 0.f, 0.f};
@@ -441,63 +502,11 @@ __global__ void __launch_bounds__(Cfg::NT) kda_inter_scalar_kernel(InterParams p
                 for (int kk = 0; kk < NKA; ++kk) qs = F::mma(qs, st[kk], qc.f[kk]);
                 oacc[i] = qs * (rs[C + 16 * R + lr] * qinv);
                 floatx4 eg = *(const floatx4*)(rs + C + 16 * R + 4 * lq);
-                if constexpr (norm_qk) {
-                    // 1/|k| of rows 16R + 4lq + e, from the lanes that own those rows
-                    float sk = 0.f;
-#pragma unroll
-                    for (int kk = 0; kk < NKA; ++kk) sk += frag_sumsq(kr[kk]);
-                    const float kin = inv_norm(sum_over_lq(sk));
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) kinv[i][e] = __shfl(kin, 4 * lq + e);
-                    eg *= kinv[i];
-                }
+                if constexpr (norm_qk) eg *= kinv;
 #pragma unroll
                 for (int e = 0; e < 4; ++e)
                     acc[e] = to_f32(sV[(16 * R + 4 * lq + e) * PV + 16 * vb + lr]) - eg[e] * acc[e];
                 store_acc_transposed<E>(sXT + (16 * vb) * PC + 16 * R, PC, acc);
-            }
-        }
-        // P blocks (Rw, J) for J = jw, jw + NWC / NB, ... <= Rw:
-        // lane holds (Q K^T)[r = 16 Rw + lr][j = 16J + 4lq + e]
-        {
-            const int r = 16 * Rw + lr;
-            const float gr = LA ? 0.f : rs[r];
-            float rsum = 0.f;  // LA: this wave's share of sum_j P_rj
-            for (int J = jw; J <= Rw; J += NWC / NB) {
-                floatx4 pa = {0.f, 0.f, 0.f, 0.f};
-                const E* pkj = sK + (16 * J + lr) * PK + W * lq;
-                FT kj[NKA];
-#pragma unroll
-                for (int kk = 0; kk < NKA; ++kk) kj[kk] = F::load(pkj + KS * kk);
-#pragma unroll
-                for (int kk = 0; kk < NKA; ++kk) pa = F::mma(pa, kj[kk], qc.f[kk]);
-                floatx4 gj = {0.f, 0.f, 0.f, 0.f};
-                if constexpr (!LA) gj = *(const floatx4*)(rs + 16 * J + 4 * lq);
-                floatx4 sc = {qinv, qinv, qinv, qinv};
-                if constexpr (norm_qk) {
-                    float sk = 0.f;
-#pragma unroll
-                    for (int kk = 0; kk < NKA; ++kk) sk += frag_sumsq(kj[kk]);
-                    const float kin = inv_norm(sum_over_lq(sk));  // row 16J + lr
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) sc[e] *= __shfl(kin, 4 * lq + e);
-                }
-                floatx4 v;
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const int j = 16 * J + 4 * lq + e;
-                    if constexpr (LA) {
-                        v[e] = (J < Rw || j <= r) ? pa[e] : 0.f;
-                        rsum += v[e];
-                    } else {
-                        v[e] = (J < Rw || j <= r) ? pa[e] * sc[e] * exp_neg(gr - gj[e]) : 0.f;
-                    }
-                }
-                st4<E>(sP + r * PC + 16 * J + 4 * lq, v);
-            }
-            if constexpr (LA) {
-                rsum = sum_over_lq(rsum);
-                if (lq == 0) sRow[jw * C + r] = rsum + qz;
             }
         }
         load_q(qc, cs + 2);
@@ -515,7 +524,7 @@ __global__ void __launch_bounds__(Cfg::NT) kda_inter_scalar_kernel(InterParams p
                 store_acc_transposed<E>(sUT + (16 * vb) * PC + 16 * R, PC, acc);
                 // the state update takes raw K^T: e^{g_n-g_t} / |k_t| on u
                 floatx4 egn = *(const floatx4*)(rs + 2 * C + 16 * R + 4 * lq);
-                if constexpr (norm_qk) egn *= kinv[i];
+                if constexpr (norm_qk) egn *= kinv;
                 store_acc_transposed<E>(sUHT + (16 * vb) * PC + 16 * R, PC, acc * egn);
             }
         }
