@@ -246,6 +246,19 @@ int kda_linear_attn_fwd(const kda_shape* shape, const void* q, const void* k, co
 size_t kda_linear_attn_fwd_workspace_bytes(const kda_shape* shape);
 
 /*
+ * One decode step of the same normalized linear attention for every (b, h):
+ * S += phi(k)^T v and z += phi(k) in place, o = phi(q) S / (phi(q) . z).
+ *   shape   L = 1, alpha_mode KDA_ALPHA_NONE (else KDA_ERR_SHAPE /
+ *           KDA_ERR_ALPHA_MODE); gate_dtype is not used.
+ *   q, k    [B,H,dk] raw; v, o [B,H,dv] in qkv_dtype.
+ *   S, z    [B,H,dk,dv] and [B,H,dk] fp32, read and updated in place (the
+ *           S_final / z_final of kda_linear_attn_fwd continue here).
+ * Outputs overlap no input and each other (KDA_ERR_ALIAS).
+ */
+int kda_linear_attn_decode_step(const kda_shape* shape, const void* q, const void* k,
+                                const void* v, float* S, float* z, void* o, void* hip_stream);
+
+/*
  * Kernel timing, for measurement tools (not part of the computation).  While
  * timing is on, every kernel that kda_chunk_fwd or kda_decode_step launches is
  * bracketed by two HIP events recorded on the call's stream; the event pairs

@@ -69,6 +69,8 @@ def library() -> ctypes.CDLL:
         lib.kda_chunk_fwd_varlen.restype = ctypes.c_int
         lib.kda_linear_attn_fwd.argtypes = [sp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
         lib.kda_linear_attn_fwd.restype = ctypes.c_int
+        lib.kda_linear_attn_decode_step.argtypes = [sp, vp, vp, vp, vp, vp, vp, vp]
+        lib.kda_linear_attn_decode_step.restype = ctypes.c_int
         lib.kda_linear_attn_fwd_workspace_bytes.argtypes = [sp]
         lib.kda_linear_attn_fwd_workspace_bytes.restype = sz
         lib.kda_chunk_fwd_varlen_workspace_bytes.argtypes = [sp, i64]
@@ -334,6 +336,26 @@ def linear_attn_fwd(q, k, v, S0=None, z0=None, *, output_final_state: bool = Tru
     if not output_final_state:
         return o, None, None
     return o, S_final, z_final
+
+
+def linear_attn_decode_step(q, k, v, S, z, *, o=None):
+    """One normalized linear attention step (phi = elu + 1) for every (b, h):
+    S [B,H,dk,dv] and z [B,H,dk] fp32 are updated in place.  q, k: [B,H,dk]
+    raw; v: [B,H,dv].  Returns o [B,H,dv]."""
+    torch = _torch()
+    B, H, dk = q.shape
+    dv = v.shape[-1]
+    for name, t in (("q", q), ("k", k), ("v", v), ("S", S), ("z", z)):
+        _require(t, name)
+    if S.dtype != torch.float32 or z.dtype != torch.float32:
+        raise TypeError("S and z must be float32")
+    if o is None:
+        o = torch.empty((B, H, dv), dtype=v.dtype, device=v.device)
+    shape = KdaShape(B, H, 1, dk, dv, _dtype_code(q), KDA_F32, KDA_ALPHA_NONE)
+    rc = library().kda_linear_attn_decode_step(ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(v),
+                                               _ptr(S), _ptr(z), _ptr(o), _stream(v))
+    _check(rc)
+    return o
 
 
 def decode_step(q, k, v, log_alpha, beta, S, *, o=None, flags: Optional[int] = None):

@@ -504,6 +504,53 @@ int kda_linear_attn_fwd(const kda_shape* s, const void* q, const void* k, const 
     return KDA_OK;
 }
 
+int kda_linear_attn_decode_step(const kda_shape* s, const void* q, const void* k,
+                                const void* v, float* S, float* z, void* o,
+                                void* hip_stream) {
+    int rc = check_shape(s, true);
+    if (rc != KDA_OK) return rc;
+    if (s->alpha_mode != KDA_ALPHA_NONE) return KDA_ERR_ALPHA_MODE;
+    const int64_t bh = s->B * s->H;
+    const int eq = elem_size(s->qkv_dtype);
+    if (bh > 0 && (!q || !k || !v || !S || !z || !o)) return KDA_ERR_NULL;
+    const void* ptrs[] = {q, k, v, S, z, o};
+    for (const void* p : ptrs)
+        if (p && !aligned16(p)) return KDA_ERR_ALIGN;
+    const Span sq = span_of(q, bh * s->dk * eq), sk = span_of(k, bh * s->dk * eq),
+               sv = span_of(v, bh * s->dv * eq), ss = span_of(S, bh * s->dk * s->dv * 4),
+               sz = span_of(z, bh * s->dk * 4), so = span_of(o, bh * s->dv * eq);
+    const Span ins[] = {sq, sk, sv};
+    const Span outs[] = {ss, sz, so};
+    for (const Span& x : outs)
+        for (const Span& y : ins)
+            if (overlaps(x, y)) return KDA_ERR_ALIAS;
+    if (overlaps(ss, sz) || overlaps(ss, so) || overlaps(sz, so)) return KDA_ERR_ALIAS;
+    if (bh == 0) return KDA_OK;
+    kda::DecodeParams prm;
+    prm.q = q;
+    prm.k = k;
+    prm.v = v;
+    prm.log_alpha = nullptr;
+    prm.beta = nullptr;
+    prm.S = S;
+    prm.o = o;
+    prm.BH = (int)bh;
+    prm.gate_bf16 = 0;
+    prm.alpha_mode = KDA_ALPHA_NONE;
+    prm.H = (int)s->H;
+    prm.linear_attn = 1;
+    prm.z = z;
+    const hipStream_t stream = (hipStream_t)hip_stream;
+    hipError_t err = timed_launch(K_DECODE, stream, [&] {
+        return kda::launch_decode(prm, (int)s->dk, (int)s->dv, s->qkv_dtype == KDA_BF16, stream);
+    });
+    if (err != hipSuccess) {
+        g_last_error = std::string("kda_linear_attn_decode_step: ") + hipGetErrorString(err);
+        return KDA_ERR_HIP;
+    }
+    return KDA_OK;
+}
+
 int kda_decode_step(const kda_shape* s, const void* q, const void* k, const void* v,
                     const void* log_alpha, const void* beta, float* S, void* o,
                     void* hip_stream) {

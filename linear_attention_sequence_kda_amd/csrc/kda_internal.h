@@ -158,6 +158,9 @@ struct DecodeParams {
     int64_t n_slots = 0;
     int H = 1;
     uint32_t flags = 0;     // kda_input_flags
+    // normalized linear attention step: z [BH, DK] fp32 normalizer, in place
+    int linear_attn = 0;
+    float* z = nullptr;
 };
 
 // phi(q) of normalized linear attention: n16 16-byte pieces.

@@ -301,3 +301,23 @@ def test_linear_attn_host_checks(lib):
     assert lib.kda_linear_attn_fwd_workspace_bytes(ctypes.byref(shape())) == 0  # has decay
     none = {n: None for n in b}
     assert la(shape(B=0, mode=binding.KDA_ALPHA_NONE), wsb=0, **none) == 0
+
+
+def test_linear_attn_decode_host_checks(lib):
+    b = dict(bufs(), z=BASE + 21 * 64 * MB)
+
+    def st(s_, **kw):
+        x = dict(b, **kw)
+        return lib.kda_linear_attn_decode_step(ctypes.byref(s_) if s_ is not None else None,
+                                               x["q"], x["k"], x["v"], x["S0"], x["z"], x["o"],
+                                               None)
+    s = shape(L=1, mode=binding.KDA_ALPHA_NONE)
+    assert st(None) == 1
+    assert st(shape(L=2, mode=binding.KDA_ALPHA_NONE)) == 2
+    assert st(shape(L=1, mode=binding.KDA_ALPHA_HEAD)) == 4
+    assert st(s, z=0) == 1
+    assert st(s, z=b["z"] + 8) == 5
+    assert st(s, z=b["S0"] + 64) == 7     # normalizer inside the state
+    assert st(s, o=b["k"]) == 7
+    none = {n: None for n in b}
+    assert st(shape(B=0, L=1, mode=binding.KDA_ALPHA_NONE), **none) == 0

@@ -107,3 +107,67 @@ def test_linear_attention_chaining():
                              to_f64(S).reshape(8, 128, 128), 1) <= 1e-5
     assert oracle.slab_error(to_f64(z2).reshape(8, 1, 128), to_f64(z).reshape(8, 1, 128),
                              1) <= 1e-5
+
+
+@pytest.mark.parametrize("qd", ["bf16", "f32"])
+@pytest.mark.parametrize("dk,dv", [(128, 128), (64, 128), (128, 64), (64, 64)],
+                         ids=lambda x: str(x))
+def test_linear_attention_prefill_then_decode(qd, dk, dv):
+    """Serving: prefill a prompt, then decode steps continue its (S, z) in
+    place; every output against the oracle over prompt + generated tokens."""
+    import torch
+    kda = _kda()
+    B, H, L, steps = 3, 4, 130, 5
+    w = gen.custom(B=B, H=H, L=L + steps, dk=dk, dv=dv, qkv_dtype=qd, gate_dtype="f32",
+                   alpha_mode="none", s0_std=None, seed=41 + dk)
+    x = gen.prefill_inputs(w, raw=True)
+    d = {n: to_dev(x[n], qd) for n in ("q", "k", "v")}
+    say(f"la prefill {L} then {steps} decode steps {qd} dk={dk} dv={dv}")
+    pre = {n: t[:, :, :L].contiguous() for n, t in d.items()}
+    o, S, z = kda.linear_attn_fwd(pre["q"], pre["k"], pre["v"])
+    outs = [to_f64(o)]
+    for t in range(L, L + steps):
+        step = {n: d[n][:, :, t].contiguous() for n in d}
+        outs.append(to_f64(kda.linear_attn_decode_step(step["q"], step["k"], step["v"], S, z))
+                    [:, :, None])
+    torch.cuda.synchronize()
+    N = B * H
+    og = np.concatenate(outs, axis=2).reshape(N, L + steps, dv)
+    fl = lambda a, tail: a.reshape((N,) + tail)
+    o_ref, S_ref, z_ref = oracle.linear_attention(fl(x["q"], (L + steps, dk)),
+                                                  fl(x["k"], (L + steps, dk)),
+                                                  fl(x["v"], (L + steps, dv)), qkv_dtype=qd)
+    tol = TOL[qd]
+    assert oracle.slab_error(og, o_ref, 1) <= tol
+    assert oracle.slab_error(to_f64(S).reshape(N, dk, dv), S_ref, 1) <= tol
+    assert oracle.slab_error(to_f64(z).reshape(N, 1, dk), z_ref[:, None, :], 1) <= tol
+
+
+def test_linear_attention_decode_serving_size():
+    """256 sequences x 32 heads, d = 128 (the decode workload's size), 3 steps
+    from a given (S, z)."""
+    import torch
+    kda = _kda()
+    B, H, d, steps = 256, 32, 128, 3
+    S0n, z0n = _init(B, H, d, d, 5)
+    S = to_dev(S0n, "f32")
+    z = to_dev(z0n, "f32")
+    w = gen.custom(B=B, H=H, L=1, dk=d, dv=d, qkv_dtype="bf16", gate_dtype="f32",
+                   alpha_mode="none", s0_std=None, seed=6).replace(decode_steps=steps)
+    say("la decode 256x32 3 steps")
+    xs, outs = [], []
+    for t in range(steps):
+        xt = gen.decode_inputs(w, t, raw=True)
+        xs.append(xt)
+        outs.append(to_f64(kda.linear_attn_decode_step(*(to_dev(xt[n], "bf16")
+                                                         for n in ("q", "k", "v")), S, z)))
+    torch.cuda.synchronize()
+    N = B * H
+    cat = lambda key, dd: np.stack([xt[key] for xt in xs], axis=2).reshape(N, steps, dd)
+    o_ref, S_ref, z_ref = oracle.linear_attention(cat("q", d), cat("k", d), cat("v", d),
+                                                  S0n.reshape(N, d, d), z0n.reshape(N, d),
+                                                  qkv_dtype="bf16")
+    og = np.stack(outs, axis=2).reshape(N, steps, d)
+    assert oracle.slab_error(og, o_ref, 1) <= TOL["bf16"]
+    assert oracle.slab_error(to_f64(S).reshape(N, d, d), S_ref, 1) <= TOL["bf16"]
+    assert oracle.slab_error(to_f64(z).reshape(N, 1, d), z_ref[:, None, :], 1) <= TOL["bf16"]
