@@ -143,9 +143,9 @@ Plan make_plan(const kda_shape* s) {
     if (p.span < p.nchunks) {
         // Round the span down so one span's intra-chunk grid (B*H*span
         // workgroups) fills whole rounds of an MI355X's resident workgroups
-        // (256 CUs x 2 for KDA records, x 3 otherwise): a partial last round
+        // (256 CUs x 2 for KDA records, x 4 otherwise): a partial last round
         // would leave most CUs idle.
-        const int64_t slots = 256 * (s->alpha_mode == KDA_ALPHA_CHANNEL ? 2 : 3);
+        const int64_t slots = 256 * (s->alpha_mode == KDA_ALPHA_CHANNEL ? 2 : 4);
         int64_t a = bh, b = slots;
         while (b) {
             const int64_t t = a % b;

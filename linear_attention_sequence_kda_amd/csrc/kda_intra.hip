@@ -79,10 +79,11 @@ struct IntraCfg {
     static constexpr int O_QV = O_KR + SZ_K;
     static constexpr int O_KC = O_QV + SZ_QV;
     static constexpr int O_A = O_KC + (KDA ? SZ_K : 0);
-    // KDA: T diag(beta) lives in the column operand's space once A and P
-    // are done (keeps the kernel at two workgroups per CU)
-    static constexpr int O_TB = KDA ? O_KC : O_A + C * PA * 4;
-    static constexpr int O_GATE = KDA ? O_A + C * PA * 4 : O_TB + C * PC * ESZ;
+    // T diag(beta) lives in space whose operand is done once A (and P) are:
+    // KDA's column operand (keeps the kernel at two workgroups per CU), the
+    // scalar path's K tile (four workgroups per CU)
+    static constexpr int O_TB = KDA ? O_KC : O_KR;
+    static constexpr int O_GATE = O_A + C * PA * 4;
     // KDA: Z[NB][DK], E'[NB][DK]; scalar: g[C], e^g[C]
     static constexpr int SZ_GATE = KDA ? 2 * NB * DK * 4 : 2 * C * 4;
     static constexpr int O_BETA = O_GATE + SZ_GATE;
@@ -94,10 +95,14 @@ struct IntraCfg {
     static_assert(DK % 32 == 0 && DV % 16 == 0 && (C == 32 || C == 64), "tile shape");
     static_assert(!KDA || NB * DK <= NT, "one thread per (channel, sub-block)");
     static_assert(LDS_BYTES <= 160 * 1024, "LDS budget of one gfx950 CU");
+    static_assert(C * PC * ESZ <= SZ_K, "T diag(beta) fits the K tile's space");
+    // scalar path: registers for eight waves per SIMD (four workgroups per CU)
+    static constexpr int MIN_WAVES = THIN ? 8 : 1;
 };
 
 template <class Cfg, bool GBF>
-__global__ void __launch_bounds__(Cfg::NT) kda_intra_kernel(IntraParams prm) {
+__global__ void __launch_bounds__(Cfg::NT) __attribute__((amdgpu_waves_per_eu(Cfg::MIN_WAVES)))
+kda_intra_kernel(IntraParams prm) {
     typedef typename Cfg::E E;
     typedef Frag<E> F;
     constexpr int DK = Cfg::DK, DV = Cfg::DV, C = Cfg::C, NB = Cfg::NB;
@@ -163,9 +168,8 @@ __global__ void __launch_bounds__(Cfg::NT) kda_intra_kernel(IntraParams prm) {
     };
 
     // upper blocks of T diag(beta) are zeros (read by the W and U products,
-    // or copied out whole); KDA zeroes them once its column operand is done
-    if constexpr (!KDA)
-        for (int i = tid; i < C * PC; i += NT) sTb[i] = from_f32<E>(0.f);
+    // or copied out whole); both paths zero them once the operand whose
+    // space they share is done
 
     // ---- v: into registers now, into LDS once the Q tile is free ------------
     constexpr int VPIECE = 16 / ESZ;
@@ -427,6 +431,14 @@ __global__ void __launch_bounds__(Cfg::NT) kda_intra_kernel(IntraParams prm) {
         }
     }
     __syncthreads();
+    if constexpr (THIN) {
+        // the K tile is done: its space takes T diag(beta), whose blocks above
+        // the diagonal (written by nobody else) are zero
+        for (int i = tid; i < C * C; i += NT) {
+            const int r = i / C, j = i - r * C;
+            if ((j >> 4) > (r >> 4)) sTb[r * PC + j] = from_f32<E>(0.f);
+        }
+    }
 
     // ================= T1: diagonal blocks by forward substitution ===========
     // Wave R < NB solves block R.  Lane (j, s) = (l/4, l%4) owns rows
