@@ -6,7 +6,8 @@ and state; one step = one kda_chunk_fwd over that batch (o and S_final
 written).  Decode leg in the same line: the KDA decode workload, 256 sequences
 x 32 heads, fp32 state updated in place for 64 steps.  Linear attention leg:
 normalized linear attention (phi = elu + 1, kda_linear_attn_fwd) on the
-prefill workload's shape.
+prefill workload's shape.  Raw-input leg: the same prefill on raw inputs with
+the input preprocessing fused (kda_chunk_fwd_ex, all three flags).
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload N]
 
@@ -227,6 +228,37 @@ def bench_decode(torch, kda, gen, w):
     return wall, kern
 
 
+def bench_prefill_raw(torch, kda, gen, w, steps, warmup):
+    """The same prefill on raw inputs (unnormalized q, k, beta logits, gate
+    pre-activations) with the preprocessing fused into the kernels' loads."""
+    log(f"prefill workload {w.name}, raw inputs: drawing inputs")
+    x = gen.prefill_inputs(w, threads=16, raw=True)
+    d = {n: to_dev(torch, x[n], w.qkv_dtype if n in ("q", "k", "v") else w.gate_dtype)
+         for n in ("q", "k", "v", "log_alpha", "beta")}
+    S0 = to_dev(torch, x["S0"], "f32") if x["S0"] is not None else None
+    o = torch.empty((w.B, w.H, w.L, w.dv), dtype=d["v"].dtype, device="cuda:0")
+    Sf = torch.empty((w.B, w.H, w.dk, w.dv), dtype=torch.float32, device="cuda:0")
+    wsb = kda.chunk_fwd_workspace_bytes(d["q"], d["v"], d["log_alpha"], d["beta"])
+    ws = torch.empty(max(wsb, 1), dtype=torch.uint8, device="cuda:0")
+    flags = kda.NORM_QK | kda.BETA_LOGIT | kda.GATE_RAW
+    call = lambda: kda.chunk_fwd(d["q"], d["k"], d["v"], d["log_alpha"], d["beta"], S0, o=o,
+                                 S_final=Sf, workspace=ws, flags=flags)
+    for _ in range(warmup):
+        call()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        call()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    kern = kernel_times(torch, kda, steps, call)
+    per = {k: {"launches_per_step": n, "avg_us": ms * 1e3} for k, (n, ms) in kern.items()}
+    log(f"prefill, raw inputs + fused preprocessing: {wall * 1e3 / steps:.4f} ms/step wall; "
+        + ", ".join(f"{k} {v['avg_us']:.1f} us" for k, v in per.items()))
+    return {"flags": "NORM_QK | BETA_LOGIT | GATE_RAW", "tokens_per_s": w.B * w.L / (wall / steps),
+            "unit": "tokens/s", "ms_per_step": wall * 1e3 / steps, "kernels": per}
+
+
 def bench_linear_attention(torch, kda, gen, w, steps, warmup):
     """Normalized linear attention (phi = elu + 1) on the prefill workload's
     shape: raw q, k, v drawn with the same recipe, no decay or gates."""
@@ -305,6 +337,7 @@ def main():
     ap.add_argument("--workload", type=int, default=2, help="prefill workload number (1-4)")
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-linear-attention", action="store_true")
+    ap.add_argument("--no-raw", action="store_true", help="skip the raw-input prefill leg")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run one plain 256 MiB device copy (a known-size "
@@ -407,6 +440,8 @@ def main():
                          "algorithmic_bytes_per_launch": dbytes,
                          "avg_kernel_us": dms * 1e3},
         }
+    if not args.no_raw:
+        out["prefill_raw_inputs"] = bench_prefill_raw(torch, kda, gen, w, args.steps, args.warmup)
     if not args.no_linear_attention:
         out["linear_attention"] = bench_linear_attention(torch, kda, gen, w, args.steps,
                                                          args.warmup)

@@ -372,7 +372,6 @@ __global__ void __launch_bounds__(Cfg::NT) kda_inter_scalar_kernel(InterParams p
     };
 
     floatx4 oacc[ITL];
-    floatx4 kinv;  // KDA_IN_NORM_QK: 1/|k| of rows 16 Rw + 4lq + e
     constexpr bool norm_qk = NORM;
     auto chunk = [&](int cs, QSet& qc) {
         const char* slot = ring + (cs & 1) * SLOT;
@@ -383,8 +382,9 @@ __global__ void __launch_bounds__(Cfg::NT) kda_inter_scalar_kernel(InterParams p
 
         // ---------------- phase 1: X, Q S, P ----------------
         // S^T rows vb serve X and Q S, read once per wave.
-        // KDA_IN_NORM_QK: q and k arrive raw; the row norms, summed over the
-        // four lanes that hold a row's fragments, scale the products.
+        // KDA_IN_NORM_QK: q and k arrive raw.  1/|q_r| comes from the q
+        // fragments (summed over the four lanes that hold a row), 1/|k_t|
+        // from the record; both scale the fp32 products.
         float qinv = 1.f;  // 1/|q| of row 16 Rw + lr
         // LA: this wave's share of phi(q_r) . z_prev, row 16 Rw + lr (the
         // waves of a row block split the channel steps kk between them)
@@ -417,14 +417,8 @@ __global__ void __launch_bounds__(Cfg::NT) kda_inter_scalar_kernel(InterParams p
             floatx4 gj = {0.f, 0.f, 0.f, 0.f};
             if constexpr (!LA) gj = *(const floatx4*)(rs + 16 * J + 4 * lq);
             floatx4 sc = {qinv, qinv, qinv, qinv};
-            if constexpr (norm_qk) {
-                float sk = 0.f;
-#pragma unroll
-                for (int kk = 0; kk < NKA; ++kk) sk += frag_sumsq(kj[kk]);
-                const float kin = inv_norm(sum_over_lq(sk));  // row 16J + lr
-#pragma unroll
-                for (int e = 0; e < 4; ++e) sc[e] *= __shfl(kin, 4 * lq + e);
-            }
+            // raw k: 1/|k_j| from the record
+            if constexpr (norm_qk) sc *= *(const floatx4*)(rs + 3 * C + 16 * J + 4 * lq);
             floatx4 v;
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
@@ -460,15 +454,6 @@ __global__ void __launch_bounds__(Cfg::NT) kda_inter_scalar_kernel(InterParams p
             rsum = sum_over_lq(rsum);
             if (lq == 0) sRow[jw * C + r] = rsum + qz;
         }
-        if constexpr (norm_qk) {
-            // 1/|k| of rows 16Rw + 4lq + e, from the lanes that own those rows
-            float sk = 0.f;
-#pragma unroll
-            for (int kk = 0; kk < NKA; ++kk) sk += frag_sumsq(kr[kk]);
-            const float kin = inv_norm(sum_over_lq(sk));
-#pragma unroll
-            for (int e = 0; e < 4; ++e) kinv[e] = __shfl(kin, 4 * lq + e);
-        }
         // S^T rows vb serve X and Q S, read once per wave.
 #pragma unroll
         for (int i = 0; i < ITL; ++i) {
@@ -502,7 +487,7 @@ __global__ void __launch_bounds__(Cfg::NT) kda_inter_scalar_kernel(InterParams p
                 for (int kk = 0; kk < NKA; ++kk) qs = F::mma(qs, st[kk], qc.f[kk]);
                 oacc[i] = qs * (rs[C + 16 * R + lr] * qinv);
                 floatx4 eg = *(const floatx4*)(rs + C + 16 * R + 4 * lq);
-                if constexpr (norm_qk) eg *= kinv;
+                if constexpr (norm_qk) eg *= *(const floatx4*)(rs + 3 * C + 16 * R + 4 * lq);
 #pragma unroll
                 for (int e = 0; e < 4; ++e)
                     acc[e] = to_f32(sV[(16 * R + 4 * lq + e) * PV + 16 * vb + lr]) - eg[e] * acc[e];
@@ -524,14 +509,14 @@ __global__ void __launch_bounds__(Cfg::NT) kda_inter_scalar_kernel(InterParams p
                 store_acc_transposed<E>(sUT + (16 * vb) * PC + 16 * R, PC, acc);
                 // the state update takes raw K^T: e^{g_n-g_t} / |k_t| on u
                 floatx4 egn = *(const floatx4*)(rs + 2 * C + 16 * R + 4 * lq);
-                if constexpr (norm_qk) egn *= kinv;
+                if constexpr (norm_qk) egn *= *(const floatx4*)(rs + 3 * C + 16 * R + 4 * lq);
                 store_acc_transposed<E>(sUHT + (16 * vb) * PC + 16 * R, PC, acc * egn);
             }
         }
         __syncthreads();
 
         // ---------------- phase 3: S update, o ----------------
-        const float gnv = LA ? 1.f : rs[3 * C];
+        const float gnv = LA ? 1.f : rs[2 * C - 1];  // e^{g_n}
         if (w < NSW) {
             constexpr int NKP = C / KS;
             typename F::T kt[CBW][NKP];

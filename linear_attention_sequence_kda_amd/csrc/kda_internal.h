@@ -62,12 +62,14 @@ __host__ __device__ constexpr RecLayout rec_layout(int dk, int dv, int c, int es
 // Record of the scalar-decay path ("thin": the inter-chunk kernel reads q, k
 // and v itself and only needs the solved triangle and the decay scalars):
 //   tb   T diag(beta)                 [C][C]   E, row-major, zero above the diagonal
-//   rs   g_r [C], e^{g_r} [C], e^{g_n-g_r} [C], e^{g_n}   fp32, 1 KiB section
+//   rs   g_r [C], e^{g_r} [C], e^{g_n-g_r} [C], and with KDA_IN_NORM_QK
+//        1/|k_r| [C] (0 past the sequence end); fp32, 1 KiB section.
+//        e^{g_n} is e^{g_r} at r = C-1 (padded tokens keep g).
 __host__ __device__ constexpr RecLayout rec_layout_thin(int c, int esz) {
     RecLayout r{0, 0, 0, 0, 0, 0, 0, 0, 0};
     r.tb = 0;
     r.rs = rec_align((uint32_t)(c * c * esz));
-    r.bytes = r.rs + rec_align((uint32_t)((3 * c + 1) * 4 > 1024 ? (3 * c + 1) * 4 : 1024));
+    r.bytes = r.rs + rec_align((uint32_t)(4 * c * 4 > 1024 ? 4 * c * 4 : 1024));
     return r;
 }
 

@@ -308,7 +308,6 @@ kda_intra_kernel(IntraParams prm) {
                 rRs[C + l] = eg;
                 rRs[2 * C + l] = exp_neg(gn - g);
             }
-            if (l == 0) rRs[3 * C] = exp_neg(gn);
         }
     }
     if (tid < C) {
@@ -542,6 +541,8 @@ kda_intra_kernel(IntraParams prm) {
             const int r = i / PPR, cc = (i % PPR) * (16 / ESZ);
             *(uint4*)(rTb + r * C + cc) = *(const uint4*)(sTb + r * PC + cc);
         }
+        // raw k: 1/|k_t| for the state pass (zero past the sequence end)
+        if (norm_qk && tid < C) rRs[3 * C + tid] = tid < n ? sKn[tid] : 0.f;
         return;
     }
     // KDA: W tile (R, cb) is computed transposed so each lane holds four
