@@ -199,6 +199,63 @@ def bench_prefill(torch, kda, gen, w, steps, warmup):
     return x, wall, call_ms, kern, wsb, cold_ms
 
 
+def summarize_prefill(w, wall, call_ms, kern, steps, cold_ms=None):
+    """tokens/s of one prefill workload, each kernel's figures, the kernel with
+    the most time per step against HBM, and the whole call against both roofs."""
+    cavg = float(np.mean(call_ms))
+    bytes_ = prefill_bytes(w)
+    flops = prefill_flops(w)
+    gbs = bytes_ / (cavg * 1e-3) / 1e9
+    tflops = flops / (cavg * 1e-3) / 1e12
+    mfma_peak = BF16_MFMA_PEAK_TFLOPS if w.qkv_dtype == "bf16" else FP32_MFMA_PEAK_TFLOPS
+    log(f"prefill {w.name}: {wall * 1e3 / steps:.4f} ms/step wall, call avg {cavg*1e3:.1f} us "
+        f"(min {min(call_ms)*1e3:.1f}), {gbs:.0f} GB/s, {tflops:.1f} TFLOP/s")
+    kernels = {}
+    for name, (per_step, ms) in kern.items():
+        kb, kf = kernel_work(w, name)
+        kb, kf = kb / per_step, kf / per_step     # per launch
+        kernels[name] = {"launches_per_step": per_step, "avg_us": ms * 1e3,
+                         "algorithmic_bytes_per_launch": kb,
+                         "algorithmic_flops_per_launch": kf,
+                         "GB/s": kb / (ms * 1e-3) / 1e9, "TFLOP/s": kf / (ms * 1e-3) / 1e12}
+        log(f"  {name}: {per_step:g} launch(es)/step, {ms*1e3:.1f} us avg, "
+            f"{kernels[name]['GB/s']:.0f} GB/s, {kernels[name]['TFLOP/s']:.1f} TFLOP/s")
+    # the dominant kernel: most time per step
+    dom = max(kernels, key=lambda n: kernels[n]["avg_us"] * kernels[n]["launches_per_step"])
+    kd = kernels[dom]
+    path = {"avg_call_us": cavg * 1e3, "min_call_us": min(call_ms) * 1e3,
+            "hbm": {"achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                    "frac": gbs / HBM_PEAK_GBS, "compulsory_bytes_per_call": bytes_},
+            "mfma": {"achieved": tflops, "peak": mfma_peak, "unit": "TFLOP/s",
+                     "frac": tflops / mfma_peak, "algorithmic_flops_per_call": flops}}
+    if cold_ms:
+        path["avg_call_us_after_cache_flush"] = float(np.mean(cold_ms)) * 1e3
+    # dominant kernel: compulsory bytes it moves per launch / its mean launch
+    # time (HIP events on the call's stream); the prefill's arithmetic
+    # intensity is left of the MI355X ridge, so HBM binds
+    roof = {"kernel": dom, "bound": "hbm", "achieved": kd["GB/s"],
+            "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": kd["GB/s"] / HBM_PEAK_GBS,
+            "traffic": measured_traffic(dom, w.name),
+            "algorithmic_bytes_per_launch": kd["algorithmic_bytes_per_launch"],
+            "avg_kernel_us": kd["avg_us"]}
+    return {"tokens_per_s": w.B * w.L / (wall / steps), "ms_per_step": wall * 1e3 / steps,
+            "roofline": roof, "kernels": kernels, "path": path}
+
+
+def bench_prefill_leg(torch, kda, gen, w, steps, warmup):
+    """A further prefill workload in the same line (same timing as the headline)."""
+    x, wall, call_ms, kern, wsb, cold_ms = bench_prefill(torch, kda, gen, w, steps, warmup)
+    del x
+    out = {"workload": w.name, "unit": "tokens/s",
+           "config": {"batch": w.B, "heads": w.H, "seq_len": w.L, "d_k": w.dk, "d_v": w.dv,
+                      "chunk": CHUNK, "alpha": w.alpha_mode, "qkv_dtype": w.qkv_dtype,
+                      "gate_dtype": w.gate_dtype, "state_dtype": "f32",
+                      "S0": w.s0_std is not None, "workspace_bytes": wsb}}
+    out.update(summarize_prefill(w, wall, call_ms, kern, steps, cold_ms))
+    torch.cuda.empty_cache()
+    return out
+
+
 def bench_decode(torch, kda, gen, w):
     log(f"decode workload {w.name}: drawing inputs")
     T = w.decode_steps
@@ -338,6 +395,8 @@ def main():
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-linear-attention", action="store_true")
     ap.add_argument("--no-raw", action="store_true", help="skip the raw-input prefill leg")
+    ap.add_argument("--no-kda", action="store_true",
+                    help="skip the KDA (per-channel decay) prefill legs, workloads 3 and 4")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run one plain 256 MiB device copy (a known-size "
@@ -362,32 +421,9 @@ def main():
         del src, dst
     w = gen.WORKLOADS[args.workload]
     x, wall, call_ms, kern, wsb, cold_ms = bench_prefill(torch, kda, gen, w, args.steps, args.warmup)
-    ms_per_step = wall * 1e3 / args.steps
-    tokens = w.B * w.L
-    value = tokens / (wall / args.steps)
-    cavg = float(np.mean(call_ms))
-    bytes_ = prefill_bytes(w)
-    flops = prefill_flops(w)
-    gbs = bytes_ / (cavg * 1e-3) / 1e9
-    tflops = flops / (cavg * 1e-3) / 1e12
-    mfma_peak = BF16_MFMA_PEAK_TFLOPS if w.qkv_dtype == "bf16" else FP32_MFMA_PEAK_TFLOPS
-    log(f"prefill: {ms_per_step:.4f} ms/step wall, call avg {cavg*1e3:.1f} us "
-        f"(min {min(call_ms)*1e3:.1f}), {gbs:.0f} GB/s, {tflops:.1f} TFLOP/s")
-    kernels = {}
-    for name, (per_step, ms) in kern.items():
-        kb, kf = kernel_work(w, name)
-        kb, kf = kb / per_step, kf / per_step     # per launch
-        kernels[name] = {"launches_per_step": per_step, "avg_us": ms * 1e3,
-                         "algorithmic_bytes_per_launch": kb,
-                         "algorithmic_flops_per_launch": kf,
-                         "GB/s": kb / (ms * 1e-3) / 1e9, "TFLOP/s": kf / (ms * 1e-3) / 1e12}
-        log(f"  {name}: {per_step:g} launch(es)/step, {ms*1e3:.1f} us avg, "
-            f"{kernels[name]['GB/s']:.0f} GB/s, {kernels[name]['TFLOP/s']:.1f} TFLOP/s")
-    # the dominant kernel: most time per step
-    dom = max(kernels, key=lambda n: kernels[n]["avg_us"] * kernels[n]["launches_per_step"])
-    kd = kernels[dom]
-    traffic = measured_traffic(dom, w.name)
-
+    head = summarize_prefill(w, wall, call_ms, kern, args.steps, cold_ms)
+    ms_per_step = head["ms_per_step"]
+    value = head["tokens_per_s"]
     out = {
         "metric": "KDA prefill tokens/s + MFMA util; decode tokens/s + HBM GB/s (1 MI355X)",
         "value": value,
@@ -405,22 +441,10 @@ def main():
                    "d_k": w.dk, "d_v": w.dv, "chunk": CHUNK, "alpha": w.alpha_mode,
                    "gate_dtype": w.gate_dtype, "state_dtype": "f32",
                    "workspace_bytes": wsb},
-        # dominant kernel: compulsory bytes it moves per launch / its mean
-        # launch time (HIP events on the call's stream); the prefill's
-        # arithmetic intensity is left of the MI355X ridge, so HBM binds
-        "roofline": {"kernel": dom, "bound": "hbm", "achieved": kd["GB/s"],
-                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": kd["GB/s"] / HBM_PEAK_GBS,
-                     "traffic": traffic,
-                     "algorithmic_bytes_per_launch": kd["algorithmic_bytes_per_launch"],
-                     "avg_kernel_us": kd["avg_us"]},
-        "kernels": kernels,
+        "roofline": head["roofline"],
+        "kernels": head["kernels"],
         # the whole kda_chunk_fwd call (every launch), against both roofs
-        "path": {"avg_call_us": cavg * 1e3, "min_call_us": min(call_ms) * 1e3,
-                 "avg_call_us_after_cache_flush": float(np.mean(cold_ms)) * 1e3,
-                 "hbm": {"achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                         "frac": gbs / HBM_PEAK_GBS, "compulsory_bytes_per_call": bytes_},
-                 "mfma": {"achieved": tflops, "peak": mfma_peak, "unit": "TFLOP/s",
-                          "frac": tflops / mfma_peak, "algorithmic_flops_per_call": flops}},
+        "path": head["path"],
     }
     if not args.no_decode:
         wd = gen.WORKLOADS[5]
@@ -440,6 +464,13 @@ def main():
                          "algorithmic_bytes_per_launch": dbytes,
                          "avg_kernel_us": dms * 1e3},
         }
+    if not args.no_kda:
+        # the KDA (per-channel decay) workloads: 2 x 32 heads x 8192 tokens,
+        # and the long-context one, 16 heads x 524288 tokens with S_final
+        for key, n in (("prefill_kda", 3), ("prefill_kda_long_context", 4)):
+            if n != args.workload:
+                out[key] = bench_prefill_leg(torch, kda, gen, gen.WORKLOADS[n], args.steps,
+                                             args.warmup)
     if not args.no_raw:
         out["prefill_raw_inputs"] = bench_prefill_raw(torch, kda, gen, w, args.steps, args.warmup)
     if not args.no_linear_attention:

@@ -268,6 +268,39 @@ def test_head_gate_equals_broadcast_channel_gate():
                              to_f64(b[0]).reshape(4, 150, 128), 1) <= 2 * TOL["bf16"]
 
 
+@pytest.mark.parametrize("mode,gd,L", [("channel", "bf16", 100_000), ("head", "f32", 330_000)])
+def test_few_heads_several_spans(mode, gd, L):
+    """Two heads and a sequence long enough for several record spans (4 with
+    per-channel decay; 2 with one decay per token, the second only 37 chunks),
+    with 16-column state slices.  Checked against the oracle on a block of
+    state columns, with and without S_final (the state then crosses spans
+    through the workspace), and bit for bit across repeated calls."""
+    import torch
+    kda = _kda()
+    w = gen.custom(B=1, H=2, L=L, dk=128, dv=128, qkv_dtype="bf16", gate_dtype=gd,
+                   alpha_mode=mode, s0_std=0.02, seed=L + 5)
+    x = gen.prefill_inputs(w, threads=16)
+    d = device_inputs(w, x)
+    args = (d["q"], d["k"], d["v"], d["log_alpha"], d["beta"], d["S0"])
+    say(f"few heads, several spans: {mode} L={L}")
+    o1, S1 = kda.chunk_fwd(*args)
+    o2, S2 = kda.chunk_fwd(*args)
+    o3, none = kda.chunk_fwd(*args, output_final_state=False)
+    torch.cuda.synchronize()
+    assert none is None
+    assert torch.equal(o1, o2) and torch.equal(S1, S2) and torch.equal(o1, o3)
+    col0, ncols = 72, 16
+    xs = {k: (None if v is None else np.ascontiguousarray(v[0])) for k, v in x.items()}
+    say(f"few heads, several spans {mode}: oracle on a column block")
+    o_ref, S_ref = oracle.forward(xs["q"], xs["k"], xs["v"], xs["log_alpha"], xs["beta"],
+                                  np.ascontiguousarray(xs["S0"]), qkv_dtype="bf16",
+                                  gate_dtype=gd, alpha_mode=mode, col0=col0, ncols=ncols)
+    e_o = oracle.slab_error(to_f64(o1[0, :, :, col0:col0 + ncols]), o_ref, 1)
+    e_s = oracle.slab_error(to_f64(S1[0, :, :, col0:col0 + ncols]), S_ref, 1)
+    say(f"few heads, several spans {mode}: err o={e_o:.3e} S={e_s:.3e}")
+    assert e_o <= TOL["bf16"] and e_s <= TOL["bf16"]
+
+
 def test_caller_workspace_and_multi_span_state_area():
     """A caller-supplied workspace of exactly the queried size gives the same
     bits as the binding's own; a smaller one is rejected before any launch.
