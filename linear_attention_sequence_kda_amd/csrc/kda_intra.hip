@@ -189,21 +189,55 @@ kda_intra_kernel(IntraParams prm) {
     const int kc = tid % DK, kR = tid / DK;  // KDA: (key channel, sub-block)
     const bool kact = KDA && kR < NB;
     float ky[KDA ? 16 : 1];                  // KDA: k * y, kept for K^
+    // Every global load of the chunk (q and k pieces, ln(alpha), beta) is
+    // issued here, before the first of them is waited for, so the inputs
+    // arrive in one memory round trip; they are used below in order.
+    constexpr int PPR = DK / VPIECE;          // 16-byte pieces per q/k row
+    constexpr int QPT = (C * PPR + NT - 1) / NT;
+    uint4 gqp[KDA ? QPT : 1], gkp[QPT];
+#pragma unroll
+    for (int i = 0; i < QPT; ++i) {
+        const int idx = tid + NT * i;
+        if (idx < C * PPR) {
+            const int r0 = idx / PPR, cc = (idx % PPR) * VPIECE;
+            const int r = r0 < n ? r0 : n - 1;
+            if constexpr (KDA) gqp[i] = ldg<uint4>(gq, (r * DK + cc) * ESZ);
+            gkp[i] = ldg<uint4>(gk, (r * DK + cc) * ESZ);
+        }
+    }
+    // raw bits of ln(alpha): KDA, thread (channel, sub-block) holds its 16
+    // tokens; one decay per token, lane l holds token l.  These small loads
+    // are made by every thread, at rows clamped into the chunk (the values
+    // of inactive threads and rows are never used), so no branch sits
+    // between a load and the later loads.
+    uint32_t la_bits[KDA ? 16 : 1];
+    if constexpr (KDA) {
+        const int kRc = kR < NB ? kR : NB - 1;
+#pragma unroll
+        for (int s = 0; s < 16; ++s) {
+            const int r = 16 * kRc + s;
+            const int rr = r < n ? r : n - 1;
+            const uint32_t el = rr * DK + kc;
+            la_bits[s] = GBF ? (uint32_t)ldg<uint16_t>(gla, el * 2) : ldg<uint32_t>(gla, el * 4);
+        }
+    } else if constexpr (HEADG) {
+        const int rr = l < n ? l : n - 1;
+        la_bits[0] = GBF ? (uint32_t)ldg<uint16_t>(gla, rr * 2) : ldg<uint32_t>(gla, rr * 4);
+    }
+    const int tb = tid < n ? tid : n - 1;
+    const uint32_t beta_bits = GBF ? (uint32_t)ldg<uint16_t>(gbeta, tb * 2) : ldg<uint32_t>(gbeta, tb * 4);
     if constexpr (KDA) {
         // q and k rows come in as 16-byte pieces into the tiles they are
         // rescaled in; each thread (channel, sub-block) then reads its 16
         // tokens from LDS.  ln(alpha) is read per thread (one coalesced row
         // segment per wave and token).
-        constexpr int PPR = DK / VPIECE;
-        constexpr int QPT = (C * PPR + NT - 1) / NT;
 #pragma unroll
         for (int i = 0; i < QPT; ++i) {
             const int idx = tid + NT * i;
             if (idx < C * PPR) {
                 const int r0 = idx / PPR, cc = (idx % PPR) * VPIECE;
-                const int r = r0 < n ? r0 : n - 1;
-                const uint4 a = keep_or_zero(ldg<uint4>(gq, (r * DK + cc) * ESZ), r0 < n);
-                const uint4 b = keep_or_zero(ldg<uint4>(gk, (r * DK + cc) * ESZ), r0 < n);
+                const uint4 a = keep_or_zero(gqp[i], r0 < n);
+                const uint4 b = keep_or_zero(gkp[i], r0 < n);
                 *(uint4*)(sQr + r0 * PK + cc) = a;
                 *(uint4*)(sKr + r0 * PK + cc) = b;
                 if (norm_qk) {
@@ -222,9 +256,7 @@ kda_intra_kernel(IntraParams prm) {
 #pragma unroll
             for (int s = 0; s < 16; ++s) {
                 const int r = 16 * kR + s;
-                const int rr = r < n ? r : n - 1;
-                const uint32_t el = rr * DK + kc;
-                float la = GBF ? bits_f32(ldg<uint16_t>(gla, el * 2), true) : ldg<float>(gla, el * 4);
+                float la = bits_f32(la_bits[s], GBF);
                 if (gate_raw) la = log_alpha_of_raw(la);
                 a[s] = r < n ? la : 0.f;
             }
@@ -271,15 +303,12 @@ kda_intra_kernel(IntraParams prm) {
             sZ[R * DK + kc] = x[15];
         }
     } else {
-        constexpr int PPR = DK / VPIECE;          // 16-byte pieces per q/k row
-        constexpr int QPT = (C * PPR + NT - 1) / NT;
 #pragma unroll
         for (int i = 0; i < QPT; ++i) {
             const int idx = tid + NT * i;
             if (idx < C * PPR) {
                 const int r0 = idx / PPR, cc = (idx % PPR) * VPIECE;
-                const int r = r0 < n ? r0 : n - 1;
-                const uint4 b = keep_or_zero(ldg<uint4>(gk, (r * DK + cc) * ESZ), r0 < n);
+                const uint4 b = keep_or_zero(gkp[i], r0 < n);
                 *(uint4*)(sKr + r0 * PK + cc) = b;
                 if (norm_qk) {
                     // the PPR pieces of a row sit in PPR consecutive lanes
@@ -294,7 +323,7 @@ kda_intra_kernel(IntraParams prm) {
             if constexpr (HEADG) {
                 float la = 0.f;
                 if (l < n) {
-                    la = GBF ? bits_f32(ldg<uint16_t>(gla, l * 2), true) : ldg<float>(gla, l * 4);
+                    la = bits_f32(la_bits[0], GBF);
                     if (gate_raw) la = log_alpha_of_raw(la);
                 }
                 g = wave_inclusive_sum(la);
@@ -313,7 +342,7 @@ kda_intra_kernel(IntraParams prm) {
     if (tid < C) {
         float b = 0.f;
         if (tid < n) {
-            b = GBF ? bits_f32(ldg<uint16_t>(gbeta, tid * 2), true) : ldg<float>(gbeta, tid * 4);
+            b = bits_f32(beta_bits, GBF);
             if (beta_logit) b = sigmoid(b);
         }
         sBeta[tid] = b;
