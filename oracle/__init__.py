@@ -27,6 +27,10 @@ Contents
 ``preprocess``         the token mixer's input steps (L2-normalized q and k,
                        sigmoid beta, alpha = exp(-exp(g))) in fp64, applied to
                        raw stored inputs before ``forward``.
+``backward``           gradients of the recurrence (reverse-mode through the
+                       token loop) for a training backward pass: dq, dk, dv,
+                       d ln(alpha), dbeta and dS0 from the gradients of o and
+                       of the final state.
 
 Every function takes fp64 NumPy arrays for one head unless said otherwise.
 """
@@ -250,6 +254,74 @@ def recurrence(q, k, v, log_alpha, beta, S0=None, delta=True):
         S = S + np.outer(k[t], u)
         o[t] = q[t] @ S
     return o, S
+
+
+def backward(q, k, v, log_alpha, beta, S0, do, dS_final=None):
+    """Gradients of the token recurrence of one head (the `recurrence` above:
+    S~_t = diag(alpha_t) S_{t-1}, e_t = v_t - k_t S~_t, u_t = beta_t e_t,
+    S_t = S~_t + k_t^T u_t, o_t = q_t S_t), by reverse-mode differentiation
+    through the token loop.  The pages give the forward recurrence only
+    ("trainable on GPUs" is their motivation for the chunk form); these are
+    its derivatives, written out step by step and pinned by finite differences
+    and by automatic differentiation of an independent forward.
+
+    do: [L, dv] gradient of o; dS_final: [dk, dv] gradient of the final state
+    (None: zero).  log_alpha: [L, dk] (per channel), [L] (per head) or None.
+    Returns (dq [L,dk], dk [L,dk], dv [L,dv], dlog_alpha (shape of log_alpha,
+    or None), dbeta [L], dS0 [dk,dv]).
+    """
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    beta = np.asarray(beta, dtype=np.float64)
+    do = np.asarray(do, dtype=np.float64)
+    L, dk = q.shape
+    dv = v.shape[1]
+    a = _decay(log_alpha, L, dk)
+    # forward: the state entering each token
+    S = np.zeros((dk, dv)) if S0 is None else np.array(S0, dtype=np.float64)
+    S_in = []
+    for t in range(L):
+        S_in.append(S)
+        St = a[t][:, None] * S
+        u = beta[t] * (v[t] - k[t] @ St)
+        S = St + np.outer(k[t], u)
+    dq = np.zeros((L, dk))
+    dkk = np.zeros((L, dk))
+    dvv = np.zeros((L, dv))
+    dbeta = np.zeros(L)
+    dla = np.zeros((L, dk))
+    G = np.zeros((dk, dv)) if dS_final is None else np.array(dS_final, dtype=np.float64)
+    for t in range(L - 1, -1, -1):
+        # recompute step t
+        St = a[t][:, None] * S_in[t]
+        e = v[t] - k[t] @ St
+        u = beta[t] * e
+        S_t = St + np.outer(k[t], u)
+        # o_t = q_t S_t
+        dq[t] = S_t @ do[t]
+        G = G + np.outer(q[t], do[t])          # total gradient of S_t
+        # S_t = S~_t + k_t^T u_t
+        gSt = G.copy()
+        gk = G @ u
+        gu = k[t] @ G
+        # u_t = beta_t e_t, e_t = v_t - k_t S~_t
+        dbeta[t] = gu @ e
+        ge = beta[t] * gu
+        dvv[t] = ge
+        gk = gk - St @ ge
+        gSt = gSt - np.outer(k[t], ge)
+        dkk[t] = gk
+        # S~_t = diag(alpha_t) S_{t-1}, alpha_t = exp(ln alpha_t)
+        dla[t] = np.sum(gSt * St, axis=1)
+        G = a[t][:, None] * gSt
+    if log_alpha is None:
+        dlog = None
+    elif np.ndim(log_alpha) == 1:
+        dlog = dla.sum(axis=1)
+    else:
+        dlog = dla
+    return dq, dkk, dvv, dlog, dbeta, G
 
 
 def brute_force(q, k, v, log_alpha, beta, S0=None):
