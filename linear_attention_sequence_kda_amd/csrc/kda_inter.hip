@@ -179,7 +179,9 @@ __global__ void __launch_bounds__(Cfg::NT) kda_inter_kernel(InterParams prm) {
         // Loads through a buffer resource over the record (the only vector
         // register involved is the lane offset).
         auto fetch = [&](DSet& st, int cs) {
-            cs = cs < ncs ? cs : ncs - 1;
+            // wave-uniform by construction; said so, the buffer resources
+            // below are scalar (no per-lane loop over resource values)
+            cs = __builtin_amdgcn_readfirstlane(cs < ncs ? cs : ncs - 1);
             const __amdgpu_buffer_rsrc_t rr = make_rsrc(recs + (int64_t)cs * rl.bytes, rl.bytes);
 #pragma unroll
             for (int j = 0; j < NL; ++j)

@@ -218,7 +218,9 @@ __global__ void __launch_bounds__(Cfg::NT) kda_inter_scalar_kernel(InterParams p
         // Buffer resources start at the chunk and end at the sequence end
         // (or the record end), so tokens past L read as zeros.
         auto fetch = [&](DSet& st, int cs) {
-            cs = cs < ncs ? cs : ncs - 1;
+            // wave-uniform by construction; said so, the buffer resources
+            // below are scalar (no per-lane loop over resource values)
+            cs = __builtin_amdgcn_readfirstlane(cs < ncs ? cs : ncs - 1);
             const int64_t t0 = (prm.c0 + cs) * C;
             const __amdgpu_buffer_rsrc_t rk =
                 make_rsrc((const char*)prm.k + hq + t0 * DK * ESZ, (uint32_t)((L - t0) * DK * ESZ));
@@ -360,7 +362,8 @@ __global__ void __launch_bounds__(Cfg::NT) kda_inter_scalar_kernel(InterParams p
     };
     const char* qhead = (const char*)prm.q + sr.base * DK * ESZ;
     auto load_q = [&](QSet& qs, int cs) {
-        cs = cs < ncs ? cs : ncs - 1;
+        // wave-uniform (scalar buffer resources, as in the data waves)
+        cs = __builtin_amdgcn_readfirstlane(cs < ncs ? cs : ncs - 1);
         const int64_t t0 = (prm.c0 + cs) * C;
         const __amdgpu_buffer_rsrc_t r =
             make_rsrc(qhead + t0 * DK * ESZ, (uint32_t)((L - t0) * DK * ESZ));
