@@ -503,22 +503,37 @@ kda_intra_kernel(IntraParams prm) {
         // (its tile reuses the column operand's space), K~ = k e^{g} in place
         // (row operand x E'_R) for W, and Q~ = q e^{g} straight to the record
         // (A operand of Q~ S)
-        for (int i = tid - 64 * NB; i < C * C; i += NT - 64 * NB) {
-            const int r = i / C, j = i % C;
-            if ((j >> 4) > (r >> 4)) sTb[r * PC + j] = from_f32<E>(0.f);
+        // (both loops have trip counts known here, so they are unrolled and
+        // each thread's LDS reads go out together; the zeros go out as
+        // 16-byte pieces, which never straddle a 16-column block)
+        constexpr int NTO = NT - 64 * NB;               // threads of these waves
+        constexpr int ZPR = C / VPIECE;                 // 16-byte pieces per row
+        constexpr int NZ = (C * ZPR + NTO - 1) / NTO;
+#pragma unroll
+        for (int it = 0; it < NZ; ++it) {
+            const int i = (tid - 64 * NB) + NTO * it;
+            if (i < C * ZPR) {
+                const int r = i / ZPR, j = (i % ZPR) * VPIECE;
+                if ((j >> 4) > (r >> 4)) *(uint4*)(sTb + r * PC + j) = make_uint4(0u, 0u, 0u, 0u);
+            }
         }
         constexpr int PER_ROW = DK / VPIECE;
-        for (int i = tid - 64 * NB; i < 2 * C * PER_ROW; i += NT - 64 * NB) {
-            const int which = i / (C * PER_ROW);
-            const int rem = i % (C * PER_ROW);
-            const int r = rem / PER_ROW, cc = (rem % PER_ROW) * VPIECE;
-            const float* sc = sE + (r >> 4) * DK + cc;
-            if (which == 0) {
-                E* p = sKr + r * PK + cc;
-                *(typename F::T*)p = F::load_scaled(p, sc);
-            } else {
-                const E* p = sQr + r * PK + cc;
-                *(typename F::T*)(rQt + frag_elem<E>(r, cc, DK)) = F::load_scaled(p, sc);
+        constexpr int NS = (2 * C * PER_ROW + NTO - 1) / NTO;
+#pragma unroll
+        for (int it = 0; it < NS; ++it) {
+            const int i = (tid - 64 * NB) + NTO * it;
+            if (i < 2 * C * PER_ROW) {
+                const int which = i / (C * PER_ROW);
+                const int rem = i % (C * PER_ROW);
+                const int r = rem / PER_ROW, cc = (rem % PER_ROW) * VPIECE;
+                const float* sc = sE + (r >> 4) * DK + cc;
+                if (which == 0) {
+                    E* p = sKr + r * PK + cc;
+                    *(typename F::T*)p = F::load_scaled(p, sc);
+                } else {
+                    const E* p = sQr + r * PK + cc;
+                    *(typename F::T*)(rQt + frag_elem<E>(r, cc, DK)) = F::load_scaled(p, sc);
+                }
             }
         }
     }
