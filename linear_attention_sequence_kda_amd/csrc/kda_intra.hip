@@ -461,10 +461,17 @@ kda_intra_kernel(IntraParams prm) {
     __syncthreads();
     if constexpr (THIN) {
         // the K tile is done: its space takes T diag(beta), whose blocks above
-        // the diagonal (written by nobody else) are zero
-        for (int i = tid; i < C * C; i += NT) {
-            const int r = i / C, j = i - r * C;
-            if ((j >> 4) > (r >> 4)) sTb[r * PC + j] = from_f32<E>(0.f);
+        // the diagonal (written by nobody else) are zero (16-byte pieces,
+        // which never straddle a 16-column block)
+        constexpr int ZPR = C / VPIECE;
+        constexpr int NZ = (C * ZPR + NT - 1) / NT;
+#pragma unroll
+        for (int it = 0; it < NZ; ++it) {
+            const int i = tid + NT * it;
+            if (i < C * ZPR) {
+                const int r = i / ZPR, j = (i % ZPR) * VPIECE;
+                if ((j >> 4) > (r >> 4)) *(uint4*)(sTb + r * PC + j) = make_uint4(0u, 0u, 0u, 0u);
+            }
         }
     }
 
@@ -593,7 +600,12 @@ kda_intra_kernel(IntraParams prm) {
     // adjacent channels of one row; U tile (R, vb) lands directly in
     // accumulator order.
     const E* sTw = sTb;
-    for (int it = w; it < NB * (NCB + NVB); it += NW) {
+    // every wave has the same number of tiles (a static trip count, so the
+    // next tile's operand loads can go out before this tile's stores)
+    static_assert((NB * (NCB + NVB)) % NW == 0, "W and U tiles per wave");
+#pragma unroll 2
+    for (int m = 0; m < NB * (NCB + NVB) / NW; ++m) {
+        const int it = w + NW * m;
         if (it < NB * NCB) {
             const int R = it % NB, cb = it / NB;
             const int K = ((16 * (R + 1) + KS - 1) / KS) * KS;
