@@ -271,7 +271,8 @@ int kda_linear_attn_decode_step(const kda_shape* shape, const void* q, const voi
  *   kda_timing_read(name, &launches, &total_ms)
  *                           waits for the kept launches of the kernel `name`
  *                           ("kda_intra_kernel", "kda_inter_kernel",
- *                           "kda_inter_scalar_kernel" or "kda_decode_kernel")
+ *                           "kda_inter_scalar_kernel", "kda_decode_kernel",
+ *                           "kda_feature_map_kernel" or "kda_bwd_kernel")
  *                           and returns how many there were and their summed
  *                           duration in milliseconds.  KDA_ERR_NULL for a NULL
  *                           argument, KDA_ERR_SHAPE for an unknown name,
@@ -295,6 +296,41 @@ int kda_decode_step_slots_ex(const kda_shape* shape, uint32_t flags, const void*
                              const void* k, const void* v, const void* log_alpha,
                              const void* beta, float* S_pool, int64_t n_slots,
                              const int32_t* slots, void* o, void* hip_stream);
+
+/*
+ * Gradients of the recurrence above through all L tokens of every (b, h), for
+ * training: given dJ/do and dJ/dS_final, the reverse sweep of the step (its
+ * chain rule; the forward step is the one of "22,580: From GPT-2 to Kimi K3",
+ * section 5.2 with section 08's decay) gives dJ/dq, dJ/dk, dJ/dv,
+ * dJ/dln(alpha), dJ/dbeta and dJ/dS0.  It runs token by token (the state is
+ * recomputed from checkpoints taken every 8 tokens), not in chunkwise form.
+ *
+ *   q, k, v, log_alpha, beta, S0: the inputs of kda_chunk_fwd (preprocessed
+ *            values: no kda_input_flags), same layouts and dtypes.
+ *   dout     [B,H,L,dv] in qkv_dtype: dJ/do.
+ *   dS_final [B,H,dk,dv] fp32 dJ/dS_final, or NULL for zero.
+ *   dq, dk   [B,H,L,dk] fp32;  dv [B,H,L,dv] fp32;  dbeta [B,H,L] fp32.
+ *   dlog_alpha  fp32 with log_alpha's layout ([B,H,L,dk] or [B,H,L]);
+ *            unused (may be NULL) with KDA_ALPHA_NONE.
+ *   dS0      [B,H,dk,dv] fp32, or NULL to skip it (with S0 NULL it is the
+ *            gradient with respect to a zero initial state).
+ *   workspace, workspace_bytes: device scratch of at least
+ *            kda_recurrence_bwd_workspace_bytes(shape) bytes
+ *            (B*H*ceil(L/8)*dk*dv*4); not kept after the call's kernels end.
+ * The outputs are written in full (dq, dk, dlog_alpha and dbeta are zeroed on
+ * the stream first, then accumulated with float atomics, so their last bits
+ * may differ between runs).  Outputs must not overlap each other, the
+ * workspace or any input (KDA_ERR_ALIAS).  All pointers 16-byte aligned.
+ * Errors as for kda_chunk_fwd; KDA_ERR_NULL for a missing required gradient.
+ */
+int kda_recurrence_bwd(const kda_shape* shape, const void* q, const void* k, const void* v,
+                       const void* log_alpha, const void* beta, const float* S0,
+                       const void* dout, const float* dS_final, float* dq, float* dk,
+                       float* dv, float* dlog_alpha, float* dbeta, float* dS0, void* workspace,
+                       size_t workspace_bytes, void* hip_stream);
+
+/* Bytes of device workspace kda_recurrence_bwd needs (0 for a rejected shape). */
+size_t kda_recurrence_bwd_workspace_bytes(const kda_shape* shape);
 
 /* Static text for a kda_status code. */
 const char* kda_strerror(int status);

@@ -20,10 +20,10 @@ thread_local std::string g_last_error;
 // ---- kernel timing (kda_timing_*) --------------------------------------------
 // While enabled, each kernel launch is bracketed by two events recorded on the
 // launch's stream; the pairs are kept until read or reset.
-enum KernelId { K_INTRA = 0, K_INTER, K_INTER_SCALAR, K_DECODE, K_FEATURE, K_COUNT };
+enum KernelId { K_INTRA = 0, K_INTER, K_INTER_SCALAR, K_DECODE, K_FEATURE, K_BWD, K_COUNT };
 const char* const kKernelNames[K_COUNT] = {"kda_intra_kernel", "kda_inter_kernel",
                                            "kda_inter_scalar_kernel", "kda_decode_kernel",
-                                           "kda_feature_map_kernel"};
+                                           "kda_feature_map_kernel", "kda_bwd_kernel"};
 struct TimedLaunch {
     int kernel;
     hipEvent_t start, stop;
@@ -556,6 +556,93 @@ int kda_linear_attn_decode_step(const kda_shape* s, const void* q, const void* k
     });
     if (err != hipSuccess) {
         g_last_error = std::string("kda_linear_attn_decode_step: ") + hipGetErrorString(err);
+        return KDA_ERR_HIP;
+    }
+    return KDA_OK;
+}
+
+size_t kda_recurrence_bwd_workspace_bytes(const kda_shape* s) {
+    if (check_shape(s, false) != KDA_OK) return 0;
+    return (size_t)kda::bwd_workspace_bytes(s->B * s->H, s->L, (int)s->dk, (int)s->dv);
+}
+
+int kda_recurrence_bwd(const kda_shape* s, const void* q, const void* k, const void* v,
+                       const void* log_alpha, const void* beta, const float* S0,
+                       const void* dout, const float* dS_final, float* dq, float* dk,
+                       float* dv, float* dlog_alpha, float* dbeta, float* dS0, void* workspace,
+                       size_t workspace_bytes, void* hip_stream) {
+    int rc = check_shape(s, false);
+    if (rc != KDA_OK) return rc;
+    const int64_t bh = s->B * s->H, tok = bh * s->L;
+    const int eq = elem_size(s->qkv_dtype), eg = elem_size(s->gate_dtype);
+    const bool has_alpha = s->alpha_mode != KDA_ALPHA_NONE;
+    const int64_t la_elems = s->alpha_mode == KDA_ALPHA_CHANNEL ? tok * s->dk : tok;
+    const int64_t ws = kda::bwd_workspace_bytes(bh, s->L, (int)s->dk, (int)s->dv);
+    // one 64-lane workgroup per (head, 8 state columns): keep the grid in int
+    if (bh > (int64_t)(INT_MAX / 64 / (s->dv / 8))) return KDA_ERR_SHAPE;
+    if (bh > 0) {
+        if (tok > 0) {
+            if (!q || !k || !v || !beta || !dout || !dq || !dk || !dv || !dbeta)
+                return KDA_ERR_NULL;
+            if (has_alpha && (!log_alpha || !dlog_alpha)) return KDA_ERR_NULL;
+        }
+        if (ws > 0 && !workspace) return KDA_ERR_NULL;
+    }
+    if ((int64_t)workspace_bytes < ws) return KDA_ERR_WORKSPACE;
+    const void* ptrs[] = {q, k, v, has_alpha ? log_alpha : nullptr, beta, S0, dout, dS_final,
+                          dq, dk, dv, has_alpha ? dlog_alpha : nullptr, dbeta, dS0, workspace};
+    for (const void* p : ptrs)
+        if (p && !aligned16(p)) return KDA_ERR_ALIGN;
+
+    const int64_t st = bh * s->dk * s->dv * 4;
+    const Span in[] = {span_of(q, tok * s->dk * eq), span_of(k, tok * s->dk * eq),
+                       span_of(v, tok * s->dv * eq),
+                       span_of(has_alpha ? log_alpha : nullptr, la_elems * eg),
+                       span_of(beta, tok * eg), span_of(S0, st),
+                       span_of(dout, tok * s->dv * eq), span_of(dS_final, st)};
+    const Span out[] = {span_of(dq, tok * s->dk * 4), span_of(dk, tok * s->dk * 4),
+                        span_of(dv, tok * s->dv * 4),
+                        span_of(has_alpha ? dlog_alpha : nullptr, la_elems * 4),
+                        span_of(dbeta, tok * 4), span_of(dS0, st),
+                        span_of(workspace, ws)};
+    const int nout = sizeof(out) / sizeof(out[0]);
+    for (int i = 0; i < nout; ++i) {
+        for (const Span& x : in)
+            if (overlaps(out[i], x)) return KDA_ERR_ALIAS;
+        for (int j = i + 1; j < nout; ++j)
+            if (overlaps(out[i], out[j])) return KDA_ERR_ALIAS;
+    }
+    if (bh == 0) return KDA_OK;
+
+    kda::BwdParams prm;
+    prm.q = q;
+    prm.k = k;
+    prm.v = v;
+    prm.log_alpha = has_alpha ? log_alpha : nullptr;
+    prm.beta = beta;
+    prm.dout = dout;
+    prm.S0 = S0;
+    prm.dS_final = dS_final;
+    prm.dq = dq;
+    prm.dk = dk;
+    prm.dv_out = dv;
+    prm.dlog_alpha = has_alpha ? dlog_alpha : nullptr;
+    prm.dbeta = dbeta;
+    prm.dS0 = dS0;
+    prm.ckpt = (float*)workspace;
+    prm.BH = bh;
+    prm.L = s->L;
+    prm.dv = (int)s->dv;
+    prm.gate_bf16 = s->gate_dtype == KDA_BF16;
+    prm.alpha_mode = s->alpha_mode;
+    const hipStream_t stream = (hipStream_t)hip_stream;
+    hipError_t err = kda::zero_bwd_outputs(prm, (int)s->dk, stream);
+    if (err == hipSuccess)
+        err = timed_launch(K_BWD, stream, [&] {
+            return kda::launch_bwd(prm, (int)s->dk, s->qkv_dtype == KDA_BF16, stream);
+        });
+    if (err != hipSuccess) {
+        g_last_error = std::string("kda_recurrence_bwd: ") + hipGetErrorString(err);
         return KDA_ERR_HIP;
     }
     return KDA_OK;

@@ -1,0 +1,414 @@
+// kda_bwd.hip -- gradients of the KDA / gated delta rule recurrence on gfx950.
+//
+// The forward step is the one of the prefill and decode kernels ("22,580:
+// From GPT-2 to Kimi K3" (yichencityu.github.io) section 5.2 with section 08's
+// decay; "22580: From GPT-2 to Kimi K3, Explained" (lukebest.github.io), "Key
+// code and formulas"):
+//     S~_t = diag(alpha_t) S_{t-1};  e_t = v_t - k_t S~_t;  u_t = beta_t e_t
+//     S_t  = S~_t + k_t^T u_t;        o_t = q_t S_t
+// The pages give no backward pass; its gradients follow from the step by the
+// chain rule, walking the tokens from last to first with G = dJ/dS_t (G starts
+// at dS_final):
+//     G     += q_t^T do_t                 dq_t   = S_t do_t^T
+//     gu     = k_t G                      dbeta_t = gu . e_t
+//     ge     = beta_t gu                  dv_t   = ge
+//     dk_t   = G u_t^T - S~_t ge^T        gS~    = G - k_t^T ge
+//     dln(alpha_t)_i = sum_j gS~_ij S~_ij (summed over i too for one decay per
+//     head)                                G      = diag(alpha_t) gS~
+// and dS0 = G after the first token.
+//
+// Columns of the state evolve independently in both directions, so the grid
+// is one single-wave workgroup per (head, slice of W = 8 state columns).  Lane
+// l holds rows l and l + 64 (d_k = 128) of its slice in registers; sums over
+// the slice's columns (dq, dk, d ln alpha) are per lane and reach the outputs
+// through float atomics (one add per slice, so the order of the adds, and the
+// last bits of those outputs, vary from run to run); sums over rows (k S~,
+// k G) are wave reductions whose totals are wave-uniform.
+//
+// Pass 1 runs the forward recurrence and stores the slice's state before
+// every CK = 8th token (the workspace holds ceil(L / 8) states per head).
+// Pass 2 walks the checkpoints backwards: it recomputes the CK states of an
+// interval from its checkpoint into LDS (with e_t), then runs the reverse step
+// above over them.  Each pass loads the next interval's inputs before working
+// on the current one.
+//
+// The step is a chain of dependent wave reductions (three per token over the
+// two passes), so the kernel is bound by their latency, not by memory.
+#include "kda_device.h"
+#include "kda_internal.h"
+
+namespace kda {
+namespace {
+
+constexpr int W = 8;    // state columns per workgroup
+constexpr int CK = 8;   // tokens per checkpoint interval
+
+template <int C>
+__device__ __forceinline__ float dpp(float x) {
+    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), C, 0xf, 0xf, false));
+}
+
+// Totals over the 64 lanes of the eight per-lane partials x[0..7]:
+// reduce-scatter over lane bits 5, 4 and 3 (lane l keeps column
+// 4 b5 + 2 b4 + b3), sums inside each group of eight lanes, then the total of
+// column c is read from lane 8c into a wave-uniform value.
+__device__ __forceinline__ void column_totals(const float (&x)[W], float (&tot)[W]) {
+    const int l = lane_id();
+    const bool b5 = l & 32, b4 = l & 16, b3 = l & 8;
+    float y[4], z[2];
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+        const float keep = b5 ? x[c + 4] : x[c], send = b5 ? x[c] : x[c + 4];
+        y[c] = keep + __shfl_xor(send, 32);
+    }
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+        const float keep = b4 ? y[c + 2] : y[c], send = b4 ? y[c] : y[c + 2];
+        z[c] = keep + __shfl_xor(send, 16);
+    }
+    // row_mirror pairs lane i of a row of 16 with lane 15 - i: opposite b3,
+    // same b5 and b4, so it completes the scatter over b3
+    float w = (b3 ? z[1] : z[0]) + dpp<0x140>(b3 ? z[0] : z[1]);
+    w += dpp<0x141>(w);   // row_half_mirror: i <-> 7 - i inside eight lanes
+    w += dpp<0xB1>(w);    // quad_perm [1,0,3,2]
+    w += dpp<0x4E>(w);    // quad_perm [2,3,0,1]
+#pragma unroll
+    for (int c = 0; c < W; ++c) tot[c] = read_lane(w, 8 * c);
+}
+
+template <typename T>
+__device__ __forceinline__ float f32(T x) { return (float)x; }
+
+// Inputs of one interval of CK tokens t0 .. t0 + CK - 1 (positions past the
+// end are clamped to the last token and never used).  Per-row values are kept
+// in their stored type until used, so the loads stay in flight across the
+// previous interval's work.  Column values are spread over the lanes: lane l
+// holds token t0 + l / W, column l % W; per-token scalars sit in lanes < CK.
+template <int RPL, typename E>
+struct Interval {
+    E k[RPL][CK], q[RPL][CK];
+    uint32_t a[RPL][CK];   // channel gate bits (bf16 in the low half, or fp32)
+    E vcol, docol;
+    uint32_t bcol, hcol;   // beta, head gate bits
+};
+
+template <int DK, typename E>
+__device__ __forceinline__ void load_interval(const BwdParams& p, int64_t bh, int slice,
+                                              int64_t t0, bool want_q, Interval<DK / 64, E>& in) {
+    constexpr int RPL = DK / 64;
+    const int l = lane_id();
+    const int64_t last = p.L - 1;
+    const bool gbf = p.gate_bf16 != 0;
+#pragma unroll
+    for (int tau = 0; tau < CK; ++tau) {
+        const int64_t t = t0 + tau < last ? t0 + tau : last;
+#pragma unroll
+        for (int m = 0; m < RPL; ++m) {
+            const int64_t off = (bh * p.L + t) * DK + l + 64 * m;
+            in.k[m][tau] = ((const E*)p.k)[off];
+            if (want_q) in.q[m][tau] = ((const E*)p.q)[off];
+            if (p.alpha_mode == KDA_ALPHA_CHANNEL)
+                in.a[m][tau] = gbf ? (uint32_t)((const uint16_t*)p.log_alpha)[off] << 16
+                                   : ((const uint32_t*)p.log_alpha)[off];
+        }
+    }
+    {
+        const int64_t tl = t0 + l / W < last ? t0 + l / W : last;
+        const int64_t off = (bh * p.L + tl) * p.dv + slice * W + l % W;
+        in.vcol = ((const E*)p.v)[off];
+        if (want_q) in.docol = ((const E*)p.dout)[off];
+    }
+    {
+        const int64_t tl = t0 + (l & (CK - 1)) < last ? t0 + (l & (CK - 1)) : last;
+        const int64_t off = bh * p.L + tl;
+        in.bcol = gbf ? (uint32_t)((const uint16_t*)p.beta)[off] << 16
+                      : ((const uint32_t*)p.beta)[off];
+        if (p.alpha_mode == KDA_ALPHA_HEAD)
+            in.hcol = gbf ? (uint32_t)((const uint16_t*)p.log_alpha)[off] << 16
+                          : ((const uint32_t*)p.log_alpha)[off];
+    }
+}
+
+__device__ __forceinline__ float bits(uint32_t b) { return __uint_as_float(b); }
+
+template <int DK, typename E>
+__global__ void __launch_bounds__(64) kda_bwd_kernel(BwdParams p) {
+    constexpr int RPL = DK / 64;
+    __shared__ __attribute__((aligned(16))) float sSin[CK][RPL][64][W];
+    __shared__ __attribute__((aligned(16))) float sE[CK][W];
+
+    const int l = lane_id();
+    const int ns = p.dv / W;
+    const int64_t bh = blockIdx.x / ns;
+    const int slice = blockIdx.x - (int)(bh * ns);
+    const int j0 = slice * W;
+    const int64_t L = p.L;
+    const int64_t nck = (L + CK - 1) / CK;
+    const int mode = p.alpha_mode;
+    float* ck = p.ckpt + (int64_t)blockIdx.x * nck * DK * W;
+
+    // decay of row m at token tau of an interval
+    auto decay = [&](const Interval<RPL, E>& in, int m, int tau) -> float {
+        if (mode == KDA_ALPHA_CHANNEL) return __expf(bits(in.a[m][tau]));
+        if (mode == KDA_ALPHA_HEAD) return __expf(read_lane(bits(in.hcol), tau));
+        return 1.f;
+    };
+
+    // ---- pass 1: forward recurrence, checkpoint before every CK-th token --------
+    float S[RPL][W];
+#pragma unroll
+    for (int m = 0; m < RPL; ++m) {
+        floatx4 lo = {0.f, 0.f, 0.f, 0.f}, hi = lo;
+        if (p.S0) {
+            const float* r = p.S0 + (bh * DK + l + 64 * m) * p.dv + j0;
+            lo = *(const floatx4*)r;
+            hi = *(const floatx4*)(r + 4);
+        }
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            S[m][j] = lo[j];
+            S[m][j + 4] = hi[j];
+        }
+    }
+    Interval<RPL, E> nxt;
+    if (nck > 0) load_interval<DK, E>(p, bh, slice, 0, false, nxt);
+    for (int64_t c = 0; c < nck; ++c) {
+        const Interval<RPL, E> cur = nxt;
+        if (c + 1 < nck) load_interval<DK, E>(p, bh, slice, (c + 1) * CK, false, nxt);
+#pragma unroll
+        for (int m = 0; m < RPL; ++m) {
+            float* r = ck + (c * DK + l + 64 * m) * W;
+            *(floatx4*)r = floatx4{S[m][0], S[m][1], S[m][2], S[m][3]};
+            *(floatx4*)(r + 4) = floatx4{S[m][4], S[m][5], S[m][6], S[m][7]};
+        }
+        const int n = L - c * CK < CK ? (int)(L - c * CK) : CK;
+#pragma unroll
+        for (int tau = 0; tau < CK; ++tau) {
+            if (tau < n) {
+                float part[W] = {};
+#pragma unroll
+                for (int m = 0; m < RPL; ++m) {
+                    const float a = decay(cur, m, tau), km = f32(cur.k[m][tau]);
+#pragma unroll
+                    for (int j = 0; j < W; ++j) {
+                        S[m][j] *= a;
+                        part[j] += km * S[m][j];
+                    }
+                }
+                float tot[W];
+                column_totals(part, tot);
+                const float beta = read_lane(bits(cur.bcol), tau);
+                const float vv = f32(cur.vcol);
+#pragma unroll
+                for (int j = 0; j < W; ++j) {
+                    const float u = beta * (read_lane(vv, tau * W + j) - tot[j]);
+#pragma unroll
+                    for (int m = 0; m < RPL; ++m) S[m][j] += f32(cur.k[m][tau]) * u;
+                }
+            }
+        }
+    }
+
+    // ---- pass 2: reverse sweep over the intervals ----------------------------------
+    float G[RPL][W];
+#pragma unroll
+    for (int m = 0; m < RPL; ++m) {
+        floatx4 lo = {0.f, 0.f, 0.f, 0.f}, hi = lo;
+        if (p.dS_final) {
+            const float* r = p.dS_final + (bh * DK + l + 64 * m) * p.dv + j0;
+            lo = *(const floatx4*)r;
+            hi = *(const floatx4*)(r + 4);
+        }
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            G[m][j] = lo[j];
+            G[m][j + 4] = hi[j];
+        }
+    }
+    if (nck > 0) load_interval<DK, E>(p, bh, slice, (nck - 1) * CK, true, nxt);
+    for (int64_t c = nck - 1; c >= 0; --c) {
+        const Interval<RPL, E> cur = nxt;
+        if (c > 0) load_interval<DK, E>(p, bh, slice, (c - 1) * CK, true, nxt);
+        const int64_t t0 = c * CK;
+        const int n = L - t0 < CK ? (int)(L - t0) : CK;
+#pragma unroll
+        for (int m = 0; m < RPL; ++m) {
+            const float* r = ck + (c * DK + l + 64 * m) * W;
+            const floatx4 lo = *(const floatx4*)r, hi = *(const floatx4*)(r + 4);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                S[m][j] = lo[j];
+                S[m][j + 4] = hi[j];
+            }
+        }
+        // recompute the interval's states S_{t-1} and residuals e_t
+        const float vv = f32(cur.vcol);
+#pragma unroll
+        for (int tau = 0; tau < CK; ++tau) {
+            if (tau < n) {
+                float part[W] = {};
+#pragma unroll
+                for (int m = 0; m < RPL; ++m) {
+                    *(floatx4*)&sSin[tau][m][l][0] = floatx4{S[m][0], S[m][1], S[m][2], S[m][3]};
+                    *(floatx4*)&sSin[tau][m][l][4] = floatx4{S[m][4], S[m][5], S[m][6], S[m][7]};
+                    const float a = decay(cur, m, tau), km = f32(cur.k[m][tau]);
+#pragma unroll
+                    for (int j = 0; j < W; ++j) {
+                        S[m][j] *= a;
+                        part[j] += km * S[m][j];
+                    }
+                }
+                float tot[W];
+                column_totals(part, tot);
+                const float beta = read_lane(bits(cur.bcol), tau);
+                float e[W];
+#pragma unroll
+                for (int j = 0; j < W; ++j) {
+                    e[j] = read_lane(vv, tau * W + j) - tot[j];
+                    const float u = beta * e[j];
+#pragma unroll
+                    for (int m = 0; m < RPL; ++m) S[m][j] += f32(cur.k[m][tau]) * u;
+                }
+                if (l == 0) {
+                    *(floatx4*)&sE[tau][0] = floatx4{e[0], e[1], e[2], e[3]};
+                    *(floatx4*)&sE[tau][4] = floatx4{e[4], e[5], e[6], e[7]};
+                }
+            }
+        }
+        __syncthreads();
+        // reverse step over the interval's tokens
+        const float dov = f32(cur.docol);
+#pragma unroll
+        for (int tau = CK - 1; tau >= 0; --tau) {
+            if (tau < n) {
+                const int64_t t = t0 + tau;
+                const float beta = read_lane(bits(cur.bcol), tau);
+                float e[W], u[W], dd[W];
+                {
+                    const floatx4 lo = *(const floatx4*)&sE[tau][0], hi = *(const floatx4*)&sE[tau][4];
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        e[j] = lo[j];
+                        e[j + 4] = hi[j];
+                    }
+                }
+#pragma unroll
+                for (int j = 0; j < W; ++j) {
+                    u[j] = beta * e[j];
+                    dd[j] = read_lane(dov, tau * W + j);
+                }
+                float St[RPL][W], a[RPL], part[W] = {};
+#pragma unroll
+                for (int m = 0; m < RPL; ++m) {
+                    const floatx4 lo = *(const floatx4*)&sSin[tau][m][l][0];
+                    const floatx4 hi = *(const floatx4*)&sSin[tau][m][l][4];
+                    a[m] = decay(cur, m, tau);
+                    const float km = f32(cur.k[m][tau]), qm = f32(cur.q[m][tau]);
+                    float dq = 0.f;
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        St[m][j] = a[m] * lo[j];
+                        St[m][j + 4] = a[m] * hi[j];
+                    }
+#pragma unroll
+                    for (int j = 0; j < W; ++j) {
+                        dq += (St[m][j] + km * u[j]) * dd[j];
+                        G[m][j] += qm * dd[j];
+                        part[j] += km * G[m][j];
+                    }
+                    unsafeAtomicAdd(p.dq + (bh * L + t) * DK + l + 64 * m, dq);
+                }
+                float gu[W];
+                column_totals(part, gu);
+                float db = 0.f;
+#pragma unroll
+                for (int j = 0; j < W; ++j) db += gu[j] * e[j];
+                float ge[W];
+#pragma unroll
+                for (int j = 0; j < W; ++j) ge[j] = beta * gu[j];
+                if (l == 0) {
+                    unsafeAtomicAdd(p.dbeta + bh * L + t, db);
+                    float* r = p.dv_out + (bh * L + t) * p.dv + j0;
+                    *(floatx4*)r = floatx4{ge[0], ge[1], ge[2], ge[3]};
+                    *(floatx4*)(r + 4) = floatx4{ge[4], ge[5], ge[6], ge[7]};
+                }
+                float dla_head = 0.f;
+#pragma unroll
+                for (int m = 0; m < RPL; ++m) {
+                    const float km = f32(cur.k[m][tau]);
+                    float dkm = 0.f, dla = 0.f;
+#pragma unroll
+                    for (int j = 0; j < W; ++j) {
+                        dkm += G[m][j] * u[j] - St[m][j] * ge[j];
+                        const float g = G[m][j] - km * ge[j];
+                        dla += g * St[m][j];
+                        G[m][j] = a[m] * g;
+                    }
+                    unsafeAtomicAdd(p.dk + (bh * L + t) * DK + l + 64 * m, dkm);
+                    if (mode == KDA_ALPHA_CHANNEL)
+                        unsafeAtomicAdd(p.dlog_alpha + (bh * L + t) * DK + l + 64 * m, dla);
+                    dla_head += dla;
+                }
+                if (mode == KDA_ALPHA_HEAD) {
+                    dla_head = group_sum<64>(dla_head);
+                    if (l == 0) unsafeAtomicAdd(p.dlog_alpha + bh * L + t, dla_head);
+                }
+            }
+        }
+        __syncthreads();
+    }
+    if (p.dS0) {
+#pragma unroll
+        for (int m = 0; m < RPL; ++m) {
+            float* r = p.dS0 + (bh * DK + l + 64 * m) * p.dv + j0;
+            *(floatx4*)r = floatx4{G[m][0], G[m][1], G[m][2], G[m][3]};
+            *(floatx4*)(r + 4) = floatx4{G[m][4], G[m][5], G[m][6], G[m][7]};
+        }
+    }
+}
+
+__global__ void __launch_bounds__(256) kda_zero_kernel(float* a, int64_t n) {
+    for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256)
+        a[i] = 0.f;
+}
+
+hipError_t zero(float* a, int64_t n, hipStream_t stream) {
+    if (!a || n == 0) return hipSuccess;
+    const int64_t blocks = (n + 255) / 256 < 4096 ? (n + 255) / 256 : 4096;
+    hipLaunchKernelGGL(kda_zero_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, a, n);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+int64_t bwd_workspace_bytes(int64_t bh, int64_t L, int dk, int dv) {
+    return bh * ((L + CK - 1) / CK) * dk * dv * 4;
+}
+
+hipError_t zero_bwd_outputs(const BwdParams& prm, int dk, hipStream_t stream) {
+    const int64_t tok = prm.BH * prm.L;
+    hipError_t err = zero(prm.dq, tok * dk, stream);
+    if (err == hipSuccess) err = zero(prm.dk, tok * dk, stream);
+    if (err == hipSuccess && prm.alpha_mode != KDA_ALPHA_NONE)
+        err = zero(prm.dlog_alpha, prm.alpha_mode == KDA_ALPHA_CHANNEL ? tok * dk : tok, stream);
+    if (err == hipSuccess) err = zero(prm.dbeta, tok, stream);
+    return err;
+}
+
+hipError_t launch_bwd(const BwdParams& prm, int dk, int qkv_bf16, hipStream_t stream) {
+    if (prm.BH == 0) return hipSuccess;
+    const dim3 grid((unsigned)(prm.BH * (prm.dv / W)));
+#define KDA_CASE(DK_, E_)                                                                  \
+    if (dk == DK_ && (qkv_bf16 != 0) == (sizeof(E_) == 2)) {                              \
+        hipLaunchKernelGGL((kda_bwd_kernel<DK_, E_>), grid, dim3(64), 0, stream, prm);     \
+        return hipGetLastError();                                                          \
+    }
+    KDA_CASE(128, bf16)
+    KDA_CASE(64, bf16)
+    KDA_CASE(128, float)
+    KDA_CASE(64, float)
+#undef KDA_CASE
+    return hipErrorInvalidValue;
+}
+
+}  // namespace kda

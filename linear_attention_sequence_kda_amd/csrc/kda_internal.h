@@ -179,4 +179,32 @@ int chunk_slice_width(int dk, int dv, int qkv_bf16, int64_t BH);
 hipError_t launch_decode(const DecodeParams& prm, int dk, int dv, int qkv_bf16,
                          hipStream_t stream);
 
+// Arguments of the gradient kernel (reverse sweep of the recurrence).
+struct BwdParams {
+    const void* q;          // [BH, L, DK] qkv type
+    const void* k;          // [BH, L, DK]
+    const void* v;          // [BH, L, DV]
+    const void* log_alpha;  // [BH, L, DK] | [BH, L] | unused; gate type
+    const void* beta;       // [BH, L] gate type
+    const void* dout;       // [BH, L, DV] qkv type: dJ/do
+    const float* S0;        // [BH, DK, DV] or null (zero state)
+    const float* dS_final;  // [BH, DK, DV] or null (zero)
+    float* dq;              // [BH, L, DK]
+    float* dk;              // [BH, L, DK]
+    float* dv_out;          // [BH, L, DV]
+    float* dlog_alpha;      // like log_alpha, fp32; unused without a decay
+    float* dbeta;           // [BH, L]
+    float* dS0;             // [BH, DK, DV] or null
+    float* ckpt;            // bwd_workspace_bytes of scratch
+    int64_t BH;
+    int64_t L;
+    int dv;
+    int gate_bf16;
+    int alpha_mode;
+};
+int64_t bwd_workspace_bytes(int64_t bh, int64_t L, int dk, int dv);
+// zero the outputs the gradient kernel accumulates into (dq, dk, dlog_alpha, dbeta)
+hipError_t zero_bwd_outputs(const BwdParams& prm, int dk, hipStream_t stream);
+hipError_t launch_bwd(const BwdParams& prm, int dk, int qkv_bf16, hipStream_t stream);
+
 }  // namespace kda

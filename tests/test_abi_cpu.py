@@ -321,3 +321,48 @@ def test_linear_attn_decode_host_checks(lib):
     assert st(s, o=b["k"]) == 7
     none = {n: None for n in b}
     assert st(shape(B=0, L=1, mode=binding.KDA_ALPHA_NONE), **none) == 0
+
+
+def bwd(lib, s, b, wsb=1 << 30):
+    return lib.kda_recurrence_bwd(ctypes.byref(s) if s is not None else None, b["q"], b["k"],
+                                  b["v"], b["la"], b["beta"], b["S0"], b["do"], b["dSf"],
+                                  b["dq"], b["dk"], b["dv"], b["dla"], b["dbeta"], b["dS0"],
+                                  b["ws"], wsb, None)
+
+
+def bwd_bufs():
+    names = ["q", "k", "v", "la", "beta", "S0", "do", "dSf", "dq", "dk", "dv", "dla", "dbeta",
+             "dS0", "ws"]
+    return {n: BASE + i * 64 * MB for i, n in enumerate(names)}
+
+
+def test_recurrence_bwd_host_checks(lib):
+    s = shape()
+    # one fp32 state slice per (head, 8 tokens)
+    ws = lib.kda_recurrence_bwd_workspace_bytes(ctypes.byref(s))
+    assert ws == 2 * 3 * 13 * 128 * 128 * 4
+    assert lib.kda_recurrence_bwd_workspace_bytes(ctypes.byref(shape(L=0))) == 0
+    assert lib.kda_recurrence_bwd_workspace_bytes(None) == 0
+    assert bwd(lib, None, bwd_bufs()) == 1
+    assert bwd(lib, s, bwd_bufs(), wsb=ws - 1) == 6                 # workspace too small
+    for name in ["q", "k", "v", "la", "beta", "do", "dq", "dk", "dv", "dla", "dbeta", "ws"]:
+        b = bwd_bufs()
+        b[name] = None
+        assert bwd(lib, s, b) == 1, name                             # required pointer
+    b = bwd_bufs()
+    b["la"] = b["dla"] = None                                        # no decay: both unused
+    assert bwd(lib, shape(mode=binding.KDA_ALPHA_NONE), b, wsb=0) == 6
+    for name in bwd_bufs():
+        b = bwd_bufs()
+        b[name] += 8
+        assert bwd(lib, s, b) == 5, name                             # misaligned
+    for out, inp in [("dq", "q"), ("dv", "do"), ("dS0", "dSf"), ("dk", "dq"), ("ws", "dla"),
+                     ("dbeta", "beta")]:
+        b = bwd_bufs()
+        b[out] = b[inp] + 1024
+        assert bwd(lib, s, b) == 7, (out, inp)                       # overlap
+    bad = shape()
+    bad.dv = 96
+    assert bwd(lib, bad, bwd_bufs()) == 2
+    none = {n: None for n in bwd_bufs()}
+    assert bwd(lib, shape(B=0), none) == 0                           # empty problem
