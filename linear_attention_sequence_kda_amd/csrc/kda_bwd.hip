@@ -27,9 +27,11 @@
 //
 // Pass 1 runs the forward recurrence and stores the slice's state before
 // every CK = 8th token (the workspace holds ceil(L / 8) states per head).
-// Pass 2 walks the checkpoints backwards: it recomputes the CK states of an
-// interval from its checkpoint into LDS (with e_t), then runs the reverse step
-// above over them.  Each pass loads the next interval's inputs before working
+// Pass 2 walks the checkpoints backwards: it recomputes the decayed states
+// S~_t of an interval from its checkpoint into LDS (with e_t), then runs the
+// reverse step above over them.  Row and column reductions go through the
+// gfx950 lane-swap instructions (v_permlane32_swap / v_permlane16_swap) and
+// DPP, not through LDS.  Each pass loads the next interval's inputs before working
 // on the current one.
 //
 // The step is a chain of dependent wave reductions (three per token over the
@@ -48,24 +50,33 @@ __device__ __forceinline__ float dpp(float x) {
     return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), C, 0xf, 0xf, false));
 }
 
+// x + y after swapping the upper 32 lanes of x with the lower 32 lanes of y:
+// lanes 0-31 get x_l + x_{l+32}, lanes 32-63 get y_{l-32} + y_l.
+__device__ __forceinline__ float swap32_add(float x, float y) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(y),
+                                                    false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// The same over rows of 16 lanes: odd rows of x swapped with even rows of y,
+// so lanes with bit 4 clear get x_l + x_{l+16}, the others y_{l-16} + y_l.
+__device__ __forceinline__ float swap16_add(float x, float y) {
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(y),
+                                                    false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
 // Totals over the 64 lanes of the eight per-lane partials x[0..7]:
 // reduce-scatter over lane bits 5, 4 and 3 (lane l keeps column
 // 4 b5 + 2 b4 + b3), sums inside each group of eight lanes, then the total of
 // column c is read from lane 8c into a wave-uniform value.
 __device__ __forceinline__ void column_totals(const float (&x)[W], float (&tot)[W]) {
-    const int l = lane_id();
-    const bool b5 = l & 32, b4 = l & 16, b3 = l & 8;
+    const bool b3 = lane_id() & 8;
     float y[4], z[2];
 #pragma unroll
-    for (int c = 0; c < 4; ++c) {
-        const float keep = b5 ? x[c + 4] : x[c], send = b5 ? x[c] : x[c + 4];
-        y[c] = keep + __shfl_xor(send, 32);
-    }
+    for (int c = 0; c < 4; ++c) y[c] = swap32_add(x[c], x[c + 4]);
 #pragma unroll
-    for (int c = 0; c < 2; ++c) {
-        const float keep = b4 ? y[c + 2] : y[c], send = b4 ? y[c] : y[c + 2];
-        z[c] = keep + __shfl_xor(send, 16);
-    }
+    for (int c = 0; c < 2; ++c) z[c] = swap16_add(y[c], y[c + 2]);
     // row_mirror pairs lane i of a row of 16 with lane 15 - i: opposite b3,
     // same b5 and b4, so it completes the scatter over b3
     float w = (b3 ? z[1] : z[0]) + dpp<0x140>(b3 ? z[0] : z[1]);
@@ -92,7 +103,7 @@ struct Interval {
     uint32_t bcol, hcol;   // beta, head gate bits
 };
 
-template <int DK, typename E>
+template <int DK, typename E, int MODE>
 __device__ __forceinline__ void load_interval(const BwdParams& p, int64_t bh, int slice,
                                               int64_t t0, bool want_q, Interval<DK / 64, E>& in) {
     constexpr int RPL = DK / 64;
@@ -107,7 +118,7 @@ __device__ __forceinline__ void load_interval(const BwdParams& p, int64_t bh, in
             const int64_t off = (bh * p.L + t) * DK + l + 64 * m;
             in.k[m][tau] = ((const E*)p.k)[off];
             if (want_q) in.q[m][tau] = ((const E*)p.q)[off];
-            if (p.alpha_mode == KDA_ALPHA_CHANNEL)
+            if constexpr (MODE == KDA_ALPHA_CHANNEL)
                 in.a[m][tau] = gbf ? (uint32_t)((const uint16_t*)p.log_alpha)[off] << 16
                                    : ((const uint32_t*)p.log_alpha)[off];
         }
@@ -123,7 +134,7 @@ __device__ __forceinline__ void load_interval(const BwdParams& p, int64_t bh, in
         const int64_t off = bh * p.L + tl;
         in.bcol = gbf ? (uint32_t)((const uint16_t*)p.beta)[off] << 16
                       : ((const uint32_t*)p.beta)[off];
-        if (p.alpha_mode == KDA_ALPHA_HEAD)
+        if constexpr (MODE == KDA_ALPHA_HEAD)
             in.hcol = gbf ? (uint32_t)((const uint16_t*)p.log_alpha)[off] << 16
                           : ((const uint32_t*)p.log_alpha)[off];
     }
@@ -131,10 +142,10 @@ __device__ __forceinline__ void load_interval(const BwdParams& p, int64_t bh, in
 
 __device__ __forceinline__ float bits(uint32_t b) { return __uint_as_float(b); }
 
-template <int DK, typename E>
+template <int DK, typename E, int MODE>
 __global__ void __launch_bounds__(64) kda_bwd_kernel(BwdParams p) {
     constexpr int RPL = DK / 64;
-    __shared__ __attribute__((aligned(16))) float sSin[CK][RPL][64][W];
+    __shared__ __attribute__((aligned(16))) float sSt[CK][RPL][64][W];  // S~ of each token
     __shared__ __attribute__((aligned(16))) float sE[CK][W];
 
     const int l = lane_id();
@@ -144,14 +155,13 @@ __global__ void __launch_bounds__(64) kda_bwd_kernel(BwdParams p) {
     const int j0 = slice * W;
     const int64_t L = p.L;
     const int64_t nck = (L + CK - 1) / CK;
-    const int mode = p.alpha_mode;
     float* ck = p.ckpt + (int64_t)blockIdx.x * nck * DK * W;
 
     // decay of row m at token tau of an interval
     auto decay = [&](const Interval<RPL, E>& in, int m, int tau) -> float {
-        if (mode == KDA_ALPHA_CHANNEL) return __expf(bits(in.a[m][tau]));
-        if (mode == KDA_ALPHA_HEAD) return __expf(read_lane(bits(in.hcol), tau));
-        return 1.f;
+        if constexpr (MODE == KDA_ALPHA_CHANNEL) return __expf(bits(in.a[m][tau]));
+        else if constexpr (MODE == KDA_ALPHA_HEAD) return __expf(read_lane(bits(in.hcol), tau));
+        else return 1.f;
     };
 
     // ---- pass 1: forward recurrence, checkpoint before every CK-th token --------
@@ -171,10 +181,10 @@ __global__ void __launch_bounds__(64) kda_bwd_kernel(BwdParams p) {
         }
     }
     Interval<RPL, E> nxt;
-    if (nck > 0) load_interval<DK, E>(p, bh, slice, 0, false, nxt);
+    if (nck > 0) load_interval<DK, E, MODE>(p, bh, slice, 0, false, nxt);
     for (int64_t c = 0; c < nck; ++c) {
         const Interval<RPL, E> cur = nxt;
-        if (c + 1 < nck) load_interval<DK, E>(p, bh, slice, (c + 1) * CK, false, nxt);
+        if (c + 1 < nck) load_interval<DK, E, MODE>(p, bh, slice, (c + 1) * CK, false, nxt);
 #pragma unroll
         for (int m = 0; m < RPL; ++m) {
             float* r = ck + (c * DK + l + 64 * m) * W;
@@ -225,10 +235,10 @@ __global__ void __launch_bounds__(64) kda_bwd_kernel(BwdParams p) {
             G[m][j + 4] = hi[j];
         }
     }
-    if (nck > 0) load_interval<DK, E>(p, bh, slice, (nck - 1) * CK, true, nxt);
+    if (nck > 0) load_interval<DK, E, MODE>(p, bh, slice, (nck - 1) * CK, true, nxt);
     for (int64_t c = nck - 1; c >= 0; --c) {
         const Interval<RPL, E> cur = nxt;
-        if (c > 0) load_interval<DK, E>(p, bh, slice, (c - 1) * CK, true, nxt);
+        if (c > 0) load_interval<DK, E, MODE>(p, bh, slice, (c - 1) * CK, true, nxt);
         const int64_t t0 = c * CK;
         const int n = L - t0 < CK ? (int)(L - t0) : CK;
 #pragma unroll
@@ -249,14 +259,14 @@ __global__ void __launch_bounds__(64) kda_bwd_kernel(BwdParams p) {
                 float part[W] = {};
 #pragma unroll
                 for (int m = 0; m < RPL; ++m) {
-                    *(floatx4*)&sSin[tau][m][l][0] = floatx4{S[m][0], S[m][1], S[m][2], S[m][3]};
-                    *(floatx4*)&sSin[tau][m][l][4] = floatx4{S[m][4], S[m][5], S[m][6], S[m][7]};
                     const float a = decay(cur, m, tau), km = f32(cur.k[m][tau]);
 #pragma unroll
                     for (int j = 0; j < W; ++j) {
                         S[m][j] *= a;
                         part[j] += km * S[m][j];
                     }
+                    *(floatx4*)&sSt[tau][m][l][0] = floatx4{S[m][0], S[m][1], S[m][2], S[m][3]};
+                    *(floatx4*)&sSt[tau][m][l][4] = floatx4{S[m][4], S[m][5], S[m][6], S[m][7]};
                 }
                 float tot[W];
                 column_totals(part, tot);
@@ -297,22 +307,26 @@ __global__ void __launch_bounds__(64) kda_bwd_kernel(BwdParams p) {
                     u[j] = beta * e[j];
                     dd[j] = read_lane(dov, tau * W + j);
                 }
+                // dq = S_t do^T with S_t = S~ + k^T u: the k part is k (u . do)
+                float ud = 0.f;
+#pragma unroll
+                for (int j = 0; j < W; ++j) ud += u[j] * dd[j];
                 float St[RPL][W], a[RPL], part[W] = {};
 #pragma unroll
                 for (int m = 0; m < RPL; ++m) {
-                    const floatx4 lo = *(const floatx4*)&sSin[tau][m][l][0];
-                    const floatx4 hi = *(const floatx4*)&sSin[tau][m][l][4];
+                    const floatx4 lo = *(const floatx4*)&sSt[tau][m][l][0];
+                    const floatx4 hi = *(const floatx4*)&sSt[tau][m][l][4];
                     a[m] = decay(cur, m, tau);
                     const float km = f32(cur.k[m][tau]), qm = f32(cur.q[m][tau]);
-                    float dq = 0.f;
 #pragma unroll
                     for (int j = 0; j < 4; ++j) {
-                        St[m][j] = a[m] * lo[j];
-                        St[m][j + 4] = a[m] * hi[j];
+                        St[m][j] = lo[j];
+                        St[m][j + 4] = hi[j];
                     }
+                    float dq = km * ud;
 #pragma unroll
                     for (int j = 0; j < W; ++j) {
-                        dq += (St[m][j] + km * u[j]) * dd[j];
+                        dq += St[m][j] * dd[j];
                         G[m][j] += qm * dd[j];
                         part[j] += km * G[m][j];
                     }
@@ -332,24 +346,29 @@ __global__ void __launch_bounds__(64) kda_bwd_kernel(BwdParams p) {
                     *(floatx4*)r = floatx4{ge[0], ge[1], ge[2], ge[3]};
                     *(floatx4*)(r + 4) = floatx4{ge[4], ge[5], ge[6], ge[7]};
                 }
+                // with gS~ = G - k^T ge:  dk = G u^T - S~ ge^T,
+                // d ln alpha = sum_j gS~ S~ = G.S~ - k (S~ ge^T),  G <- diag(alpha) gS~
                 float dla_head = 0.f;
 #pragma unroll
                 for (int m = 0; m < RPL; ++m) {
                     const float km = f32(cur.k[m][tau]);
-                    float dkm = 0.f, dla = 0.f;
+                    float gu_m = 0.f, sge = 0.f, gs = 0.f;
 #pragma unroll
                     for (int j = 0; j < W; ++j) {
-                        dkm += G[m][j] * u[j] - St[m][j] * ge[j];
-                        const float g = G[m][j] - km * ge[j];
-                        dla += g * St[m][j];
-                        G[m][j] = a[m] * g;
+                        gu_m += G[m][j] * u[j];
+                        sge += St[m][j] * ge[j];
+                        gs += G[m][j] * St[m][j];
                     }
-                    unsafeAtomicAdd(p.dk + (bh * L + t) * DK + l + 64 * m, dkm);
-                    if (mode == KDA_ALPHA_CHANNEL)
+                    const float ak = a[m] * km;
+#pragma unroll
+                    for (int j = 0; j < W; ++j) G[m][j] = a[m] * G[m][j] - ak * ge[j];
+                    unsafeAtomicAdd(p.dk + (bh * L + t) * DK + l + 64 * m, gu_m - sge);
+                    const float dla = gs - km * sge;
+                    if constexpr (MODE == KDA_ALPHA_CHANNEL)
                         unsafeAtomicAdd(p.dlog_alpha + (bh * L + t) * DK + l + 64 * m, dla);
                     dla_head += dla;
                 }
-                if (mode == KDA_ALPHA_HEAD) {
+                if constexpr (MODE == KDA_ALPHA_HEAD) {
                     dla_head = group_sum<64>(dla_head);
                     if (l == 0) unsafeAtomicAdd(p.dlog_alpha + bh * L + t, dla_head);
                 }
@@ -398,16 +417,24 @@ hipError_t zero_bwd_outputs(const BwdParams& prm, int dk, hipStream_t stream) {
 hipError_t launch_bwd(const BwdParams& prm, int dk, int qkv_bf16, hipStream_t stream) {
     if (prm.BH == 0) return hipSuccess;
     const dim3 grid((unsigned)(prm.BH * (prm.dv / W)));
-#define KDA_CASE(DK_, E_)                                                                  \
+#define KDA_MODES(DK_, E_)                                                                 \
     if (dk == DK_ && (qkv_bf16 != 0) == (sizeof(E_) == 2)) {                              \
-        hipLaunchKernelGGL((kda_bwd_kernel<DK_, E_>), grid, dim3(64), 0, stream, prm);     \
+        if (prm.alpha_mode == KDA_ALPHA_CHANNEL)                                           \
+            hipLaunchKernelGGL((kda_bwd_kernel<DK_, E_, KDA_ALPHA_CHANNEL>), grid, dim3(64), 0, \
+                               stream, prm);                                               \
+        else if (prm.alpha_mode == KDA_ALPHA_HEAD)                                         \
+            hipLaunchKernelGGL((kda_bwd_kernel<DK_, E_, KDA_ALPHA_HEAD>), grid, dim3(64), 0,    \
+                               stream, prm);                                               \
+        else                                                                               \
+            hipLaunchKernelGGL((kda_bwd_kernel<DK_, E_, KDA_ALPHA_NONE>), grid, dim3(64), 0,    \
+                               stream, prm);                                               \
         return hipGetLastError();                                                          \
     }
-    KDA_CASE(128, bf16)
-    KDA_CASE(64, bf16)
-    KDA_CASE(128, float)
-    KDA_CASE(64, float)
-#undef KDA_CASE
+    KDA_MODES(128, bf16)
+    KDA_MODES(64, bf16)
+    KDA_MODES(128, float)
+    KDA_MODES(64, float)
+#undef KDA_MODES
     return hipErrorInvalidValue;
 }
 
