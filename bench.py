@@ -256,6 +256,63 @@ def bench_prefill_leg(torch, kda, gen, w, steps, warmup):
     return out
 
 
+def bwd_flops(w):
+    """Algorithmic flops of one kda_recurrence_bwd: 20 dk dv per token-head.
+    The forward step it has to redo (S~ = diag(alpha) S, k S~, S~ + k^T u:
+    5 per state element) and the reverse step (G += q^T do, k G, dq = S do^T,
+    dk = G u^T - S~ ge^T, gS~ = G - k^T ge, d ln alpha = sum gS~ S~,
+    G = diag(alpha) gS~: 15 per element); the recomputation of states from
+    checkpoints is the kernel's own cost and is not counted."""
+    return w.B * w.H * w.L * 20 * w.dk * w.dv
+
+
+def bench_bwd(torch, kda, gen, w, steps, warmup):
+    """Gradients of the recurrence for one prefill workload (dJ/do given,
+    dJ/dS_final zero): tokens/s, and the gradient kernel against the fp32
+    vector ALU peak (the kernel is a chain of per-token vector updates)."""
+    log(f"gradients, workload {w.name}: drawing inputs")
+    x = gen.prefill_inputs(w, threads=16)
+    d = {n: to_dev(torch, x[n], w.qkv_dtype if n in ("q", "k", "v") else w.gate_dtype)
+         for n in ("q", "k", "v", "log_alpha", "beta")}
+    S0 = to_dev(torch, x["S0"], "f32") if x["S0"] is not None else None
+    del x
+    rng = np.random.default_rng(w.seed + 101)
+    do = to_dev(torch, gen.to_storage(rng.normal(size=(w.B, w.H, w.L, w.dv)), w.qkv_dtype),
+                w.qkv_dtype)
+    wsb = kda.recurrence_bwd_workspace_bytes(d["q"], d["v"], d["log_alpha"], d["beta"])
+    ws = torch.empty(wsb, dtype=torch.uint8, device="cuda:0")
+
+    def step():
+        return kda.recurrence_bwd(d["q"], d["k"], d["v"], d["log_alpha"], d["beta"], S0, do,
+                                  None, want_dS0=S0 is not None, workspace=ws)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        step()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    kern = kernel_times(torch, kda, steps, step)
+    per, ms = kern["kda_bwd_kernel"]
+    flops = bwd_flops(w) / per
+    tflops = flops / (ms * 1e-3) / 1e12
+    log(f"gradients {w.name}: {wall * 1e3 / steps:.3f} ms/step wall, kernel avg {ms:.3f} ms, "
+        f"{tflops:.2f} TFLOP/s")
+    out = {"workload": w.name, "tokens_per_s": w.B * w.L / (wall / steps), "unit": "tokens/s",
+           "ms_per_step": wall * 1e3 / steps, "workspace_bytes": wsb,
+           "kernels": {n: {"launches_per_step": pk, "avg_us": m * 1e3} for n, (pk, m) in kern.items()},
+           "roofline": {"kernel": "kda_bwd_kernel", "bound": "alu", "achieved": tflops,
+                        "peak": FP32_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
+                        "frac": tflops / FP32_MFMA_PEAK_TFLOPS,
+                        "traffic": measured_traffic("kda_bwd_kernel", w.name),
+                        "algorithmic_flops_per_launch": flops, "avg_kernel_us": ms * 1e3}}
+    del d, do, ws
+    torch.cuda.empty_cache()
+    return out
+
+
 def bench_decode(torch, kda, gen, w):
     log(f"decode workload {w.name}: drawing inputs")
     T = w.decode_steps
@@ -397,6 +454,8 @@ def main():
     ap.add_argument("--no-raw", action="store_true", help="skip the raw-input prefill leg")
     ap.add_argument("--no-kda", action="store_true",
                     help="skip the KDA (per-channel decay) prefill legs, workloads 3 and 4")
+    ap.add_argument("--no-bwd", action="store_true",
+                    help="skip the gradient (kda_recurrence_bwd) leg")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run one plain 256 MiB device copy (a known-size "
@@ -471,6 +530,8 @@ def main():
             if n != args.workload:
                 out[key] = bench_prefill_leg(torch, kda, gen, gen.WORKLOADS[n], args.steps,
                                              args.warmup)
+    if not args.no_bwd:
+        out["gradients"] = bench_bwd(torch, kda, gen, w, min(args.steps, 10), min(args.warmup, 2))
     if not args.no_raw:
         out["prefill_raw_inputs"] = bench_prefill_raw(torch, kda, gen, w, args.steps, args.warmup)
     if not args.no_linear_attention:

@@ -36,6 +36,7 @@ KERNEL_SOURCES = {
     "kda_inter_kernel": ["kda_inter.hip"],
     "kda_inter_scalar_kernel": ["kda_inter_scalar.hip"],
     "kda_decode_kernel": ["kda_decode.hip"],
+    "kda_bwd_kernel": ["kda_bwd.hip"],
 }
 COMMON_SOURCES = ["kda_device.h", "kda_internal.h"]
 # the prefill kernels' launch shapes (spans, column slices) are set by the ABI layer
