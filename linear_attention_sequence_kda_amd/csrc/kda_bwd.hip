@@ -101,11 +101,19 @@ struct Interval {
     uint32_t a[RPL][CK];   // channel gate bits (bf16 in the low half, or fp32)
     E vcol, docol;
     uint32_t bcol, hcol;   // beta, head gate bits
+    floatx4 ck[RPL][2];    // reverse pass: the interval's checkpoint rows
 };
 
-template <int DK, typename E, int MODE>
+template <bool B>
+struct Flag {
+    static constexpr bool value = B;
+};
+
+// REV: the reverse pass's loads (q, dJ/do and the checkpoint at ckp as well)
+template <int DK, typename E, int MODE, bool REV>
 __device__ __forceinline__ void load_interval(const BwdParams& p, int64_t bh, int slice,
-                                              int64_t t0, bool want_q, Interval<DK / 64, E>& in) {
+                                              int64_t t0, const float* ckp,
+                                              Interval<DK / 64, E>& in) {
     constexpr int RPL = DK / 64;
     const int l = lane_id();
     const int64_t last = p.L - 1;
@@ -117,7 +125,7 @@ __device__ __forceinline__ void load_interval(const BwdParams& p, int64_t bh, in
         for (int m = 0; m < RPL; ++m) {
             const int64_t off = (bh * p.L + t) * DK + l + 64 * m;
             in.k[m][tau] = ((const E*)p.k)[off];
-            if (want_q) in.q[m][tau] = ((const E*)p.q)[off];
+            if constexpr (REV) in.q[m][tau] = ((const E*)p.q)[off];
             if constexpr (MODE == KDA_ALPHA_CHANNEL)
                 in.a[m][tau] = gbf ? (uint32_t)((const uint16_t*)p.log_alpha)[off] << 16
                                    : ((const uint32_t*)p.log_alpha)[off];
@@ -127,7 +135,15 @@ __device__ __forceinline__ void load_interval(const BwdParams& p, int64_t bh, in
         const int64_t tl = t0 + l / W < last ? t0 + l / W : last;
         const int64_t off = (bh * p.L + tl) * p.dv + slice * W + l % W;
         in.vcol = ((const E*)p.v)[off];
-        if (want_q) in.docol = ((const E*)p.dout)[off];
+        if constexpr (REV) in.docol = ((const E*)p.dout)[off];
+    }
+    if constexpr (REV) {
+#pragma unroll
+        for (int m = 0; m < RPL; ++m) {
+            const float* r = ckp + (l + 64 * m) * W;
+            in.ck[m][0] = *(const floatx4*)r;
+            in.ck[m][1] = *(const floatx4*)(r + 4);
+        }
     }
     {
         const int64_t tl = t0 + (l & (CK - 1)) < last ? t0 + (l & (CK - 1)) : last;
@@ -181,10 +197,11 @@ __global__ void __launch_bounds__(64) kda_bwd_kernel(BwdParams p) {
         }
     }
     Interval<RPL, E> nxt;
-    if (nck > 0) load_interval<DK, E, MODE>(p, bh, slice, 0, false, nxt);
+    if (nck > 0) load_interval<DK, E, MODE, false>(p, bh, slice, 0, nullptr, nxt);
     for (int64_t c = 0; c < nck; ++c) {
         const Interval<RPL, E> cur = nxt;
-        if (c + 1 < nck) load_interval<DK, E, MODE>(p, bh, slice, (c + 1) * CK, false, nxt);
+        if (c + 1 < nck)
+            load_interval<DK, E, MODE, false>(p, bh, slice, (c + 1) * CK, nullptr, nxt);
 #pragma unroll
         for (int m = 0; m < RPL; ++m) {
             float* r = ck + (c * DK + l + 64 * m) * W;
@@ -192,9 +209,12 @@ __global__ void __launch_bounds__(64) kda_bwd_kernel(BwdParams p) {
             *(floatx4*)(r + 4) = floatx4{S[m][4], S[m][5], S[m][6], S[m][7]};
         }
         const int n = L - c * CK < CK ? (int)(L - c * CK) : CK;
+        // full intervals run without per-token guards (the tail one with them),
+        // so the compiler sees every token's loads and waits consumed in order
+        auto forward = [&](auto full) {
 #pragma unroll
         for (int tau = 0; tau < CK; ++tau) {
-            if (tau < n) {
+            if (decltype(full)::value || tau < n) {
                 float part[W] = {};
 #pragma unroll
                 for (int m = 0; m < RPL; ++m) {
@@ -217,6 +237,11 @@ __global__ void __launch_bounds__(64) kda_bwd_kernel(BwdParams p) {
                 }
             }
         }
+        };
+        if (n == CK)
+            forward(Flag<true>{});
+        else
+            forward(Flag<false>{});
     }
 
     // ---- pass 2: reverse sweep over the intervals ----------------------------------
@@ -235,27 +260,30 @@ __global__ void __launch_bounds__(64) kda_bwd_kernel(BwdParams p) {
             G[m][j + 4] = hi[j];
         }
     }
-    if (nck > 0) load_interval<DK, E, MODE>(p, bh, slice, (nck - 1) * CK, true, nxt);
+    if (nck > 0)
+        load_interval<DK, E, MODE, true>(p, bh, slice, (nck - 1) * CK, ck + (nck - 1) * DK * W,
+                                         nxt);
     for (int64_t c = nck - 1; c >= 0; --c) {
         const Interval<RPL, E> cur = nxt;
-        if (c > 0) load_interval<DK, E, MODE>(p, bh, slice, (c - 1) * CK, true, nxt);
+        if (c > 0)
+            load_interval<DK, E, MODE, true>(p, bh, slice, (c - 1) * CK, ck + (c - 1) * DK * W,
+                                             nxt);
         const int64_t t0 = c * CK;
         const int n = L - t0 < CK ? (int)(L - t0) : CK;
+        auto reverse = [&](auto full) {
 #pragma unroll
         for (int m = 0; m < RPL; ++m) {
-            const float* r = ck + (c * DK + l + 64 * m) * W;
-            const floatx4 lo = *(const floatx4*)r, hi = *(const floatx4*)(r + 4);
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
-                S[m][j] = lo[j];
-                S[m][j + 4] = hi[j];
+                S[m][j] = cur.ck[m][0][j];
+                S[m][j + 4] = cur.ck[m][1][j];
             }
         }
         // recompute the interval's states S_{t-1} and residuals e_t
         const float vv = f32(cur.vcol);
 #pragma unroll
         for (int tau = 0; tau < CK; ++tau) {
-            if (tau < n) {
+            if (decltype(full)::value || tau < n) {
                 float part[W] = {};
 #pragma unroll
                 for (int m = 0; m < RPL; ++m) {
@@ -290,7 +318,7 @@ __global__ void __launch_bounds__(64) kda_bwd_kernel(BwdParams p) {
         const float dov = f32(cur.docol);
 #pragma unroll
         for (int tau = CK - 1; tau >= 0; --tau) {
-            if (tau < n) {
+            if (decltype(full)::value || tau < n) {
                 const int64_t t = t0 + tau;
                 const float beta = read_lane(bits(cur.bcol), tau);
                 float e[W], u[W], dd[W];
@@ -375,6 +403,11 @@ __global__ void __launch_bounds__(64) kda_bwd_kernel(BwdParams p) {
             }
         }
         __syncthreads();
+        };
+        if (n == CK)
+            reverse(Flag<true>{});
+        else
+            reverse(Flag<false>{});
     }
     if (p.dS0) {
 #pragma unroll
