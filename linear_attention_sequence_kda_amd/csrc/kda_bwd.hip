@@ -98,9 +98,9 @@ __device__ __forceinline__ float f32(T x) { return (float)x; }
 template <int RPL, typename E>
 struct Interval {
     E k[RPL][CK], q[RPL][CK];
-    uint32_t a[RPL][CK];   // channel gate bits (bf16 in the low half, or fp32)
+    uint32_t a[RPL][CK];   // channel gate as loaded: bf16 bits (zero-extended) or fp32
     E vcol, docol;
-    uint32_t bcol, hcol;   // beta, head gate bits
+    uint32_t bcol, hcol;   // beta, head gate, as loaded
     floatx4 ck[RPL][2];    // reverse pass: the interval's checkpoint rows
 };
 
@@ -127,7 +127,7 @@ __device__ __forceinline__ void load_interval(const BwdParams& p, int64_t bh, in
             in.k[m][tau] = ((const E*)p.k)[off];
             if constexpr (REV) in.q[m][tau] = ((const E*)p.q)[off];
             if constexpr (MODE == KDA_ALPHA_CHANNEL)
-                in.a[m][tau] = gbf ? (uint32_t)((const uint16_t*)p.log_alpha)[off] << 16
+                in.a[m][tau] = gbf ? (uint32_t)((const uint16_t*)p.log_alpha)[off]
                                    : ((const uint32_t*)p.log_alpha)[off];
         }
     }
@@ -148,15 +148,20 @@ __device__ __forceinline__ void load_interval(const BwdParams& p, int64_t bh, in
     {
         const int64_t tl = t0 + (l & (CK - 1)) < last ? t0 + (l & (CK - 1)) : last;
         const int64_t off = bh * p.L + tl;
-        in.bcol = gbf ? (uint32_t)((const uint16_t*)p.beta)[off] << 16
+        in.bcol = gbf ? (uint32_t)((const uint16_t*)p.beta)[off]
                       : ((const uint32_t*)p.beta)[off];
         if constexpr (MODE == KDA_ALPHA_HEAD)
-            in.hcol = gbf ? (uint32_t)((const uint16_t*)p.log_alpha)[off] << 16
+            in.hcol = gbf ? (uint32_t)((const uint16_t*)p.log_alpha)[off]
                           : ((const uint32_t*)p.log_alpha)[off];
     }
 }
 
-__device__ __forceinline__ float bits(uint32_t b) { return __uint_as_float(b); }
+// A gate value as loaded (bf16 bits zero-extended, or fp32 bits) -> float.  The
+// widening happens here, at the use, so that it does not wait for the load in
+// the interval that issues it.
+__device__ __forceinline__ float gate(uint32_t b, bool gbf) {
+    return __uint_as_float(gbf ? b << 16 : b);
+}
 
 template <int DK, typename E, int MODE>
 __global__ void __launch_bounds__(64) kda_bwd_kernel(BwdParams p) {
@@ -171,12 +176,13 @@ __global__ void __launch_bounds__(64) kda_bwd_kernel(BwdParams p) {
     const int j0 = slice * W;
     const int64_t L = p.L;
     const int64_t nck = (L + CK - 1) / CK;
+    const bool gbf = p.gate_bf16 != 0;
     float* ck = p.ckpt + (int64_t)blockIdx.x * nck * DK * W;
 
     // decay of row m at token tau of an interval
     auto decay = [&](const Interval<RPL, E>& in, int m, int tau) -> float {
-        if constexpr (MODE == KDA_ALPHA_CHANNEL) return __expf(bits(in.a[m][tau]));
-        else if constexpr (MODE == KDA_ALPHA_HEAD) return __expf(read_lane(bits(in.hcol), tau));
+        if constexpr (MODE == KDA_ALPHA_CHANNEL) return __expf(gate(in.a[m][tau], gbf));
+        else if constexpr (MODE == KDA_ALPHA_HEAD) return __expf(read_lane(gate(in.hcol, gbf), tau));
         else return 1.f;
     };
 
@@ -227,7 +233,7 @@ __global__ void __launch_bounds__(64) kda_bwd_kernel(BwdParams p) {
                 }
                 float tot[W];
                 column_totals(part, tot);
-                const float beta = read_lane(bits(cur.bcol), tau);
+                const float beta = read_lane(gate(cur.bcol, gbf), tau);
                 const float vv = f32(cur.vcol);
 #pragma unroll
                 for (int j = 0; j < W; ++j) {
@@ -298,7 +304,7 @@ __global__ void __launch_bounds__(64) kda_bwd_kernel(BwdParams p) {
                 }
                 float tot[W];
                 column_totals(part, tot);
-                const float beta = read_lane(bits(cur.bcol), tau);
+                const float beta = read_lane(gate(cur.bcol, gbf), tau);
                 float e[W];
 #pragma unroll
                 for (int j = 0; j < W; ++j) {
@@ -320,7 +326,7 @@ __global__ void __launch_bounds__(64) kda_bwd_kernel(BwdParams p) {
         for (int tau = CK - 1; tau >= 0; --tau) {
             if (decltype(full)::value || tau < n) {
                 const int64_t t = t0 + tau;
-                const float beta = read_lane(bits(cur.bcol), tau);
+                const float beta = read_lane(gate(cur.bcol, gbf), tau);
                 float e[W], u[W], dd[W];
                 {
                     const floatx4 lo = *(const floatx4*)&sE[tau][0], hi = *(const floatx4*)&sE[tau][4];
