@@ -532,6 +532,10 @@ def main():
                                              args.warmup)
     if not args.no_bwd:
         out["gradients"] = bench_bwd(torch, kda, gen, w, min(args.steps, 10), min(args.warmup, 2))
+        if not args.no_kda and args.workload != 3:
+            # the KDA workload's gradients (per-channel decay, 2 x 32 x 8192)
+            out["gradients_kda"] = bench_bwd(torch, kda, gen, gen.WORKLOADS[3],
+                                             min(args.steps, 5), min(args.warmup, 1))
     if not args.no_raw:
         out["prefill_raw_inputs"] = bench_prefill_raw(torch, kda, gen, w, args.steps, args.warmup)
     if not args.no_linear_attention:
