@@ -168,6 +168,8 @@ __global__ void __launch_bounds__(64) kda_bwd_kernel(BwdParams p) {
     constexpr int RPL = DK / 64;
     __shared__ __attribute__((aligned(16))) float sSt[CK][RPL][64][W];  // S~ of each token
     __shared__ __attribute__((aligned(16))) float sE[CK][W];
+    __shared__ __attribute__((aligned(16))) float sDV[CK * W];   // dv of an interval
+    __shared__ float sDB[CK], sDH[CK];                           // dbeta, head d ln alpha
 
     const int l = lane_id();
     const int ns = p.dv / W;
@@ -374,11 +376,12 @@ __global__ void __launch_bounds__(64) kda_bwd_kernel(BwdParams p) {
                 float ge[W];
 #pragma unroll
                 for (int j = 0; j < W; ++j) ge[j] = beta * gu[j];
+                // dv and dbeta (and a head gate's d ln alpha below) are staged
+                // in LDS and written once per interval by all lanes
                 if (l == 0) {
-                    unsafeAtomicAdd(p.dbeta + bh * L + t, db);
-                    float* r = p.dv_out + (bh * L + t) * p.dv + j0;
-                    *(floatx4*)r = floatx4{ge[0], ge[1], ge[2], ge[3]};
-                    *(floatx4*)(r + 4) = floatx4{ge[4], ge[5], ge[6], ge[7]};
+                    *(floatx4*)&sDV[tau * W] = floatx4{ge[0], ge[1], ge[2], ge[3]};
+                    *(floatx4*)&sDV[tau * W + 4] = floatx4{ge[4], ge[5], ge[6], ge[7]};
+                    sDB[tau] = db;
                 }
                 // with gS~ = G - k^T ge:  dk = G u^T - S~ ge^T,
                 // d ln alpha = sum_j gS~ S~ = G.S~ - k (S~ ge^T),  G <- diag(alpha) gS~
@@ -404,9 +407,19 @@ __global__ void __launch_bounds__(64) kda_bwd_kernel(BwdParams p) {
                 }
                 if constexpr (MODE == KDA_ALPHA_HEAD) {
                     dla_head = group_sum<64>(dla_head);
-                    if (l == 0) unsafeAtomicAdd(p.dlog_alpha + bh * L + t, dla_head);
+                    if (l == 0) sDH[tau] = dla_head;
                 }
             }
+        }
+        __syncthreads();
+        // lane l: dv of token t0 + l / W, column j0 + l % W; lanes < CK: dbeta
+        // (and d ln alpha of a head gate) of token t0 + l
+        if (decltype(full)::value || (l / W) < n)
+            p.dv_out[(bh * L + t0 + l / W) * p.dv + j0 + l % W] = sDV[l];
+        if (l < CK && (decltype(full)::value || l < n)) {
+            unsafeAtomicAdd(p.dbeta + bh * L + t0 + l, sDB[l]);
+            if constexpr (MODE == KDA_ALPHA_HEAD)
+                unsafeAtomicAdd(p.dlog_alpha + bh * L + t0 + l, sDH[l]);
         }
         __syncthreads();
         };
