@@ -366,7 +366,10 @@ __global__ void __launch_bounds__(64) kda_bwd_kernel(BwdParams p) {
                         G[m][j] += qm * dd[j];
                         part[j] += km * G[m][j];
                     }
-                    unsafeAtomicAdd(p.dq + (bh * L + t) * DK + l + 64 * m, dq);
+                    // S~ of this row and token is in registers now: its LDS slot
+                    // keeps the row's dq, dk and d ln alpha until the interval's
+                    // atomics
+                    sSt[tau][m][l][0] = dq;
                 }
                 float gu[W];
                 column_totals(part, gu);
@@ -399,10 +402,10 @@ __global__ void __launch_bounds__(64) kda_bwd_kernel(BwdParams p) {
                     const float ak = a[m] * km;
 #pragma unroll
                     for (int j = 0; j < W; ++j) G[m][j] = a[m] * G[m][j] - ak * ge[j];
-                    unsafeAtomicAdd(p.dk + (bh * L + t) * DK + l + 64 * m, gu_m - sge);
+                    sSt[tau][m][l][1] = gu_m - sge;
                     const float dla = gs - km * sge;
                     if constexpr (MODE == KDA_ALPHA_CHANNEL)
-                        unsafeAtomicAdd(p.dlog_alpha + (bh * L + t) * DK + l + 64 * m, dla);
+                        sSt[tau][m][l][2] = dla;
                     dla_head += dla;
                 }
                 if constexpr (MODE == KDA_ALPHA_HEAD) {
@@ -416,6 +419,21 @@ __global__ void __launch_bounds__(64) kda_bwd_kernel(BwdParams p) {
         // (and d ln alpha of a head gate) of token t0 + l
         if (decltype(full)::value || (l / W) < n)
             p.dv_out[(bh * L + t0 + l / W) * p.dv + j0 + l % W] = sDV[l];
+        // this slice's share of dq, dk (and a channel gate's d ln alpha) for
+        // the interval's tokens, added with one atomic per row and token
+#pragma unroll
+        for (int tau = 0; tau < CK; ++tau) {
+            if (decltype(full)::value || tau < n) {
+                const int64_t row0 = (bh * L + t0 + tau) * DK + l;
+#pragma unroll
+                for (int m = 0; m < RPL; ++m) {
+                    unsafeAtomicAdd(p.dq + row0 + 64 * m, sSt[tau][m][l][0]);
+                    unsafeAtomicAdd(p.dk + row0 + 64 * m, sSt[tau][m][l][1]);
+                    if constexpr (MODE == KDA_ALPHA_CHANNEL)
+                        unsafeAtomicAdd(p.dlog_alpha + row0 + 64 * m, sSt[tau][m][l][2]);
+                }
+            }
+        }
         if (l < CK && (decltype(full)::value || l < n)) {
             unsafeAtomicAdd(p.dbeta + bh * L + t0 + l, sDB[l]);
             if constexpr (MODE == KDA_ALPHA_HEAD)
