@@ -66,25 +66,46 @@ __device__ __forceinline__ float swap16_add(float x, float y) {
     return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
-// Totals over the 64 lanes of the eight per-lane partials x[0..7]:
-// reduce-scatter over lane bits 5, 4 and 3 (lane l keeps column
-// 4 b5 + 2 b4 + b3), sums inside each group of eight lanes, then the total of
-// column c is read from lane 8c into a wave-uniform value.
+// Totals over the 64 lanes of the W per-lane partials x[0..W-1]:
+// reduce-scatter over lane bits 5, 4 (and 3 for W = 8), so that lane l keeps
+// one column, sums inside each group of 64 / W lanes, then the total of
+// column c is read from lane (64 / W) c into a wave-uniform value.
 __device__ __forceinline__ void column_totals(const float (&x)[W], float (&tot)[W]) {
-    const bool b3 = lane_id() & 8;
-    float y[4], z[2];
+    static_assert(W == 4 || W == 8, "column_totals: W is 4 or 8");
+    float y[W / 2], z[W / 4];
 #pragma unroll
-    for (int c = 0; c < 4; ++c) y[c] = swap32_add(x[c], x[c + 4]);
+    for (int c = 0; c < W / 2; ++c) y[c] = swap32_add(x[c], x[c + W / 2]);
 #pragma unroll
-    for (int c = 0; c < 2; ++c) z[c] = swap16_add(y[c], y[c + 2]);
-    // row_mirror pairs lane i of a row of 16 with lane 15 - i: opposite b3,
-    // same b5 and b4, so it completes the scatter over b3
-    float w = (b3 ? z[1] : z[0]) + dpp<0x140>(b3 ? z[0] : z[1]);
+    for (int c = 0; c < W / 4; ++c) z[c] = swap16_add(y[c], y[c + W / 4]);
+    // row_mirror pairs lane i of a row of 16 with lane 15 - i (opposite bit 3,
+    // same bits 5 and 4): for W = 8 it completes the scatter over bit 3
+    float w;
+    if constexpr (W == 8) {
+        const bool b3 = lane_id() & 8;
+        w = (b3 ? z[1] : z[0]) + dpp<0x140>(b3 ? z[0] : z[1]);
+    } else {
+        w = z[0] + dpp<0x140>(z[0]);
+    }
     w += dpp<0x141>(w);   // row_half_mirror: i <-> 7 - i inside eight lanes
     w += dpp<0xB1>(w);    // quad_perm [1,0,3,2]
     w += dpp<0x4E>(w);    // quad_perm [2,3,0,1]
 #pragma unroll
-    for (int c = 0; c < W; ++c) tot[c] = read_lane(w, 8 * c);
+    for (int c = 0; c < W; ++c) tot[c] = read_lane(w, (64 / W) * c);
+}
+
+// W consecutive floats <-> registers, in 16-byte pieces
+__device__ __forceinline__ void ld_row(const float* r, float (&x)[W]) {
+#pragma unroll
+    for (int h = 0; h < W / 4; ++h) {
+        const floatx4 v = *(const floatx4*)(r + 4 * h);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) x[4 * h + i] = v[i];
+    }
+}
+__device__ __forceinline__ void st_row(float* r, const float (&x)[W]) {
+#pragma unroll
+    for (int h = 0; h < W / 4; ++h)
+        *(floatx4*)(r + 4 * h) = floatx4{x[4 * h], x[4 * h + 1], x[4 * h + 2], x[4 * h + 3]};
 }
 
 template <typename T>
@@ -101,7 +122,7 @@ struct Interval {
     uint32_t a[RPL][CK];   // channel gate as loaded: bf16 bits (zero-extended) or fp32
     E vcol, docol;
     uint32_t bcol, hcol;   // beta, head gate, as loaded
-    floatx4 ck[RPL][2];    // reverse pass: the interval's checkpoint rows
+    float ck[RPL][W];      // reverse pass: the interval's checkpoint rows
 };
 
 template <bool B>
@@ -140,9 +161,7 @@ __device__ __forceinline__ void load_interval(const BwdParams& p, int64_t bh, in
     if constexpr (REV) {
 #pragma unroll
         for (int m = 0; m < RPL; ++m) {
-            const float* r = ckp + (l + 64 * m) * W;
-            in.ck[m][0] = *(const floatx4*)r;
-            in.ck[m][1] = *(const floatx4*)(r + 4);
+            ld_row(ckp + (l + 64 * m) * W, in.ck[m]);
         }
     }
     {
@@ -192,16 +211,11 @@ __global__ void __launch_bounds__(64) kda_bwd_kernel(BwdParams p) {
     float S[RPL][W];
 #pragma unroll
     for (int m = 0; m < RPL; ++m) {
-        floatx4 lo = {0.f, 0.f, 0.f, 0.f}, hi = lo;
         if (p.S0) {
-            const float* r = p.S0 + (bh * DK + l + 64 * m) * p.dv + j0;
-            lo = *(const floatx4*)r;
-            hi = *(const floatx4*)(r + 4);
-        }
+            ld_row(p.S0 + (bh * DK + l + 64 * m) * p.dv + j0, S[m]);
+        } else {
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            S[m][j] = lo[j];
-            S[m][j + 4] = hi[j];
+            for (int j = 0; j < W; ++j) S[m][j] = 0.f;
         }
     }
     Interval<RPL, E> nxt;
@@ -212,9 +226,7 @@ __global__ void __launch_bounds__(64) kda_bwd_kernel(BwdParams p) {
             load_interval<DK, E, MODE, false>(p, bh, slice, (c + 1) * CK, nullptr, nxt);
 #pragma unroll
         for (int m = 0; m < RPL; ++m) {
-            float* r = ck + (c * DK + l + 64 * m) * W;
-            *(floatx4*)r = floatx4{S[m][0], S[m][1], S[m][2], S[m][3]};
-            *(floatx4*)(r + 4) = floatx4{S[m][4], S[m][5], S[m][6], S[m][7]};
+            st_row(ck + (c * DK + l + 64 * m) * W, S[m]);
         }
         const int n = L - c * CK < CK ? (int)(L - c * CK) : CK;
         // full intervals run without per-token guards (the tail one with them),
@@ -256,16 +268,11 @@ __global__ void __launch_bounds__(64) kda_bwd_kernel(BwdParams p) {
     float G[RPL][W];
 #pragma unroll
     for (int m = 0; m < RPL; ++m) {
-        floatx4 lo = {0.f, 0.f, 0.f, 0.f}, hi = lo;
         if (p.dS_final) {
-            const float* r = p.dS_final + (bh * DK + l + 64 * m) * p.dv + j0;
-            lo = *(const floatx4*)r;
-            hi = *(const floatx4*)(r + 4);
-        }
+            ld_row(p.dS_final + (bh * DK + l + 64 * m) * p.dv + j0, G[m]);
+        } else {
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            G[m][j] = lo[j];
-            G[m][j + 4] = hi[j];
+            for (int j = 0; j < W; ++j) G[m][j] = 0.f;
         }
     }
     if (nck > 0)
@@ -282,10 +289,7 @@ __global__ void __launch_bounds__(64) kda_bwd_kernel(BwdParams p) {
 #pragma unroll
         for (int m = 0; m < RPL; ++m) {
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                S[m][j] = cur.ck[m][0][j];
-                S[m][j + 4] = cur.ck[m][1][j];
-            }
+            for (int j = 0; j < W; ++j) S[m][j] = cur.ck[m][j];
         }
         // recompute the interval's states S_{t-1} and residuals e_t
         const float vv = f32(cur.vcol);
@@ -301,8 +305,7 @@ __global__ void __launch_bounds__(64) kda_bwd_kernel(BwdParams p) {
                         S[m][j] *= a;
                         part[j] += km * S[m][j];
                     }
-                    *(floatx4*)&sSt[tau][m][l][0] = floatx4{S[m][0], S[m][1], S[m][2], S[m][3]};
-                    *(floatx4*)&sSt[tau][m][l][4] = floatx4{S[m][4], S[m][5], S[m][6], S[m][7]};
+                    st_row(&sSt[tau][m][l][0], S[m]);
                 }
                 float tot[W];
                 column_totals(part, tot);
@@ -315,10 +318,7 @@ __global__ void __launch_bounds__(64) kda_bwd_kernel(BwdParams p) {
 #pragma unroll
                     for (int m = 0; m < RPL; ++m) S[m][j] += f32(cur.k[m][tau]) * u;
                 }
-                if (l == 0) {
-                    *(floatx4*)&sE[tau][0] = floatx4{e[0], e[1], e[2], e[3]};
-                    *(floatx4*)&sE[tau][4] = floatx4{e[4], e[5], e[6], e[7]};
-                }
+                if (l == 0) st_row(&sE[tau][0], e);
             }
         }
         __syncthreads();
@@ -330,14 +330,7 @@ __global__ void __launch_bounds__(64) kda_bwd_kernel(BwdParams p) {
                 const int64_t t = t0 + tau;
                 const float beta = read_lane(gate(cur.bcol, gbf), tau);
                 float e[W], u[W], dd[W];
-                {
-                    const floatx4 lo = *(const floatx4*)&sE[tau][0], hi = *(const floatx4*)&sE[tau][4];
-#pragma unroll
-                    for (int j = 0; j < 4; ++j) {
-                        e[j] = lo[j];
-                        e[j + 4] = hi[j];
-                    }
-                }
+                ld_row(&sE[tau][0], e);
 #pragma unroll
                 for (int j = 0; j < W; ++j) {
                     u[j] = beta * e[j];
@@ -350,15 +343,9 @@ __global__ void __launch_bounds__(64) kda_bwd_kernel(BwdParams p) {
                 float St[RPL][W], a[RPL], part[W] = {};
 #pragma unroll
                 for (int m = 0; m < RPL; ++m) {
-                    const floatx4 lo = *(const floatx4*)&sSt[tau][m][l][0];
-                    const floatx4 hi = *(const floatx4*)&sSt[tau][m][l][4];
+                    ld_row(&sSt[tau][m][l][0], St[m]);
                     a[m] = decay(cur, m, tau);
                     const float km = f32(cur.k[m][tau]), qm = f32(cur.q[m][tau]);
-#pragma unroll
-                    for (int j = 0; j < 4; ++j) {
-                        St[m][j] = lo[j];
-                        St[m][j + 4] = hi[j];
-                    }
                     float dq = km * ud;
 #pragma unroll
                     for (int j = 0; j < W; ++j) {
@@ -382,8 +369,7 @@ __global__ void __launch_bounds__(64) kda_bwd_kernel(BwdParams p) {
                 // dv and dbeta (and a head gate's d ln alpha below) are staged
                 // in LDS and written once per interval by all lanes
                 if (l == 0) {
-                    *(floatx4*)&sDV[tau * W] = floatx4{ge[0], ge[1], ge[2], ge[3]};
-                    *(floatx4*)&sDV[tau * W + 4] = floatx4{ge[4], ge[5], ge[6], ge[7]};
+                    st_row(&sDV[tau * W], ge);
                     sDB[tau] = db;
                 }
                 // with gS~ = G - k^T ge:  dk = G u^T - S~ ge^T,
@@ -417,7 +403,7 @@ __global__ void __launch_bounds__(64) kda_bwd_kernel(BwdParams p) {
         __syncthreads();
         // lane l: dv of token t0 + l / W, column j0 + l % W; lanes < CK: dbeta
         // (and d ln alpha of a head gate) of token t0 + l
-        if (decltype(full)::value || (l / W) < n)
+        if (l < CK * W && (decltype(full)::value || (l / W) < n))
             p.dv_out[(bh * L + t0 + l / W) * p.dv + j0 + l % W] = sDV[l];
         // this slice's share of dq, dk (and a channel gate's d ln alpha) for
         // the interval's tokens, added with one atomic per row and token
@@ -449,9 +435,7 @@ __global__ void __launch_bounds__(64) kda_bwd_kernel(BwdParams p) {
     if (p.dS0) {
 #pragma unroll
         for (int m = 0; m < RPL; ++m) {
-            float* r = p.dS0 + (bh * DK + l + 64 * m) * p.dv + j0;
-            *(floatx4*)r = floatx4{G[m][0], G[m][1], G[m][2], G[m][3]};
-            *(floatx4*)(r + 4) = floatx4{G[m][4], G[m][5], G[m][6], G[m][7]};
+            st_row(p.dS0 + (bh * DK + l + 64 * m) * p.dv + j0, G[m]);
         }
     }
 }
