@@ -324,6 +324,36 @@ def backward(q, k, v, log_alpha, beta, S0, do, dS_final=None):
     return dq, dkk, dvv, dlog, dbeta, G
 
 
+def backward_raw(q, k, v, g, b, S0, do, dS_final, flags):
+    """Gradients with respect to raw inputs: the recurrence fed through the
+    preprocessing steps of ``preprocess`` (the flags), all fp64, one head.
+
+    q, k: [L, dk] (raw when NORM_QK); g: raw gate (GATE_RAW) or ln alpha,
+    [L, dk], [L] or None; b: beta logits (BETA_LOGIT) or beta, [L].  The
+    gradient of each step, from its definition:
+      q / max(|q|, eps):  (dq_n - q_n (q_n . dq_n)) / |q| when |q| > eps,
+                          dq_n / eps otherwise
+      sigmoid(x):         dbeta sigmoid(x) (1 - sigmoid(x))
+      -exp(g):            d ln alpha (-exp(g))
+    Returns (dq, dk, dv, dg, db, dS0) like ``backward``.
+    """
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    qn, kn, v64, la, beta = preprocess(q, k, v, g, b, flags, qkv_dtype="f64", gate_dtype="f64")
+    dq, dk, dv, dla, dbeta, dS0 = backward(qn, kn, v64, la, beta, S0, do, dS_final)
+    if flags & NORM_QK:
+        def through_norm(x, xn, dxn):
+            n = np.sqrt(np.sum(x * x, axis=-1, keepdims=True))
+            proj = dxn - xn * np.sum(xn * dxn, axis=-1, keepdims=True)
+            return np.where(n > 1e-12, proj / np.maximum(n, 1e-300), dxn / 1e-12)
+        dq, dk = through_norm(q, qn, dq), through_norm(k, kn, dk)
+    if flags & BETA_LOGIT:
+        dbeta = dbeta * beta * (1.0 - beta)
+    if flags & GATE_RAW and dla is not None:
+        dla = dla * la
+    return dq, dk, dv, dla, dbeta, dS0
+
+
 def brute_force(q, k, v, log_alpha, beta, S0=None):
     """S_t = M_t S_{t-1} + beta_t k_t^T v_t with M_t = (I - beta_t k_t^T k_t) D_t
     formed as an explicit d_k x d_k matrix ("Gated DeltaNet adds controlled

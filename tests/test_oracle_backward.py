@@ -211,3 +211,68 @@ def test_planted_mistakes_fail_the_pin(mistake):
     assert max(rel(clean[n], fd[n]) for n in fd) <= 1e-7      # the copy itself is right
     bad = _reverse_sweep_with(mistake, q, k, v, la, beta, S0, Wo, Ws)
     assert max(rel(bad[n], fd[n]) for n in fd) > 1e-3, mistake
+
+
+# ---- gradients with respect to raw inputs (the preprocessing steps) ----------
+
+def _raw_draw(L, dk, dv, mode, seed):
+    rng = np.random.default_rng(seed)
+    q = rng.normal(size=(L, dk)) * 3.0          # raw: normalized by the op
+    k = rng.normal(size=(L, dk)) * 2.0
+    v = rng.normal(size=(L, dv))
+    g = {"channel": rng.normal(-1.0, 0.5, size=(L, dk)), "head": rng.normal(-1.0, 0.5, size=L),
+         "none": None}[mode]                    # raw gate: ln alpha = -exp(g)
+    x = rng.normal(size=L)                      # beta logits
+    S0 = rng.normal(size=(dk, dv))
+    return q, k, v, g, x, S0
+
+
+def _raw_loss(Wo, Ws, flags):
+    def J(q, k, v, g, x, S0):
+        qn, kn, v64, la, b = oracle.preprocess(q, k, v, g, x, flags, qkv_dtype="f64",
+                                               gate_dtype="f64")
+        o, S = oracle.recurrence(qn, kn, v64, la, b, S0)
+        return float((o * Wo).sum() + (S * Ws).sum())
+    return J
+
+
+@pytest.mark.parametrize("mode", ["channel", "head"])
+@pytest.mark.parametrize("flags", [oracle.NORM_QK, oracle.BETA_LOGIT, oracle.GATE_RAW,
+                                   oracle.NORM_QK | oracle.BETA_LOGIT | oracle.GATE_RAW])
+def test_raw_input_gradients_match_finite_differences(mode, flags):
+    L, dk, dv = 6, 3, 2
+    q, k, v, g, x, S0 = _raw_draw(L, dk, dv, mode, seed=13)
+    if not flags & oracle.BETA_LOGIT:
+        x = 1.0 / (1.0 + np.exp(-x))            # already a strength in (0, 1)
+    if not flags & oracle.GATE_RAW:
+        g = -np.exp(g)                           # already ln alpha
+    rng = np.random.default_rng(4)
+    Wo, Ws = rng.normal(size=(L, dv)), rng.normal(size=(dk, dv))
+    fd = finite_differences(_raw_loss(Wo, Ws, flags), [q, k, v, g, x, S0])
+    got = oracle.backward_raw(q, k, v, g, x, S0, Wo, Ws, flags)
+    for name, a, f in zip(["q", "k", "v", "g", "beta", "S0"], got, fd):
+        assert rel(a, f) <= 1e-6, (name, rel(a, f))
+
+
+def test_raw_gradients_without_flags_equal_backward():
+    q, k, v, g, x, S0 = _raw_draw(7, 4, 3, "channel", seed=2)
+    la, b = -np.exp(g), 1.0 / (1.0 + np.exp(-x))
+    rng = np.random.default_rng(1)
+    do, dSf = rng.normal(size=(7, 3)), rng.normal(size=(4, 3))
+    a = oracle.backward_raw(q, k, v, la, b, S0, do, dSf, 0)
+    r = oracle.backward(q, k, v, la, b, S0, do, dSf)
+    assert all(np.array_equal(x1, x2) for x1, x2 in zip(a, r))
+
+
+def test_zero_raw_row_follows_the_floor():
+    """A zero q row is scaled by 1 / 1e-12 (the floor), so its gradient is the
+    normalized-row gradient times 1e12, not the projection."""
+    q, k, v, g, x, S0 = _raw_draw(5, 3, 2, "head", seed=8)
+    q[2] = 0.0
+    rng = np.random.default_rng(3)
+    do = rng.normal(size=(5, 2))
+    dq = oracle.backward_raw(q, k, v, g, x, S0, do, None, oracle.NORM_QK | oracle.GATE_RAW
+                             | oracle.BETA_LOGIT)[0]
+    qn, kn, v64, la, b = oracle.preprocess(q, k, v, g, x, 7, qkv_dtype="f64", gate_dtype="f64")
+    dqn = oracle.backward(qn, kn, v64, la, b, S0, do, None)[0]
+    assert np.allclose(dq[2], dqn[2] * 1e12, rtol=1e-14, atol=0.0)
