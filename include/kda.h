@@ -332,6 +332,24 @@ int kda_recurrence_bwd(const kda_shape* shape, const void* q, const void* k, con
 /* Bytes of device workspace kda_recurrence_bwd needs (0 for a rejected shape). */
 size_t kda_recurrence_bwd_workspace_bytes(const kda_shape* shape);
 
+/*
+ * kda_recurrence_bwd on raw inputs: flags is a set of kda_input_flags, as for
+ * kda_chunk_fwd_ex, and the gradients are with respect to the raw values the
+ * caller passes (through the q/k normalization, the beta sigmoid and
+ * ln alpha = -exp(g)).  The inputs are preprocessed into fp32 copies in the
+ * workspace, the gradient kernel runs on them, and the chain rule of each
+ * flagged step is applied to its outputs in place.  workspace_bytes >=
+ * kda_recurrence_bwd_ex_workspace_bytes(shape, flags) (0 for L = 0, where
+ * the call is kda_recurrence_bwd's).  Arguments, layouts, ownership and
+ * errors as for kda_recurrence_bwd; KDA_ERR_FLAGS for an unknown bit.
+ */
+int kda_recurrence_bwd_ex(const kda_shape* shape, uint32_t flags, const void* q, const void* k,
+                          const void* v, const void* log_alpha, const void* beta,
+                          const float* S0, const void* dout, const float* dS_final, float* dq,
+                          float* dk, float* dv, float* dlog_alpha, float* dbeta, float* dS0,
+                          void* workspace, size_t workspace_bytes, void* hip_stream);
+size_t kda_recurrence_bwd_ex_workspace_bytes(const kda_shape* shape, uint32_t flags);
+
 /* Static text for a kda_status code. */
 const char* kda_strerror(int status);
 

@@ -86,6 +86,10 @@ def library() -> ctypes.CDLL:
         lib.kda_recurrence_bwd.restype = ctypes.c_int
         lib.kda_recurrence_bwd_workspace_bytes.argtypes = [sp]
         lib.kda_recurrence_bwd_workspace_bytes.restype = sz
+        lib.kda_recurrence_bwd_ex.argtypes = [sp, u32] + [vp] * 15 + [sz, vp]
+        lib.kda_recurrence_bwd_ex.restype = ctypes.c_int
+        lib.kda_recurrence_bwd_ex_workspace_bytes.argtypes = [sp, u32]
+        lib.kda_recurrence_bwd_ex_workspace_bytes.restype = sz
         lib.kda_strerror.argtypes = [ctypes.c_int]
         lib.kda_strerror.restype = ctypes.c_char_p
         lib.kda_last_error.argtypes = []
@@ -247,13 +251,15 @@ def recurrence_bwd_workspace_bytes(q, v, log_alpha, beta) -> int:
 
 
 def recurrence_bwd(q, k, v, log_alpha, beta, S0, do, dS_final=None, *, want_dS0: bool = True,
-                   workspace=None):
+                   workspace=None, flags: Optional[int] = None):
     """Gradients of the recurrence (kda_recurrence_bwd): returns
     (dq, dk, dv, dlog_alpha or None, dbeta, dS0 or None), all fp32.
 
     Inputs as for chunk_fwd (preprocessed values); do: [B,H,L,dv] in v's dtype;
     dS_final: [B,H,dk,dv] fp32 or None.  ``workspace`` may be a uint8 GPU
-    tensor of at least recurrence_bwd_workspace_bytes() bytes.
+    tensor of at least recurrence_bwd_workspace_bytes() bytes.  ``flags`` (a
+    set of NORM_QK | BETA_LOGIT | GATE_RAW) calls kda_recurrence_bwd_ex on raw
+    inputs, whose gradients are then with respect to the raw values.
     """
     torch = _torch()
     B, H, L, dk = q.shape
@@ -274,16 +280,22 @@ def recurrence_bwd(q, k, v, log_alpha, beta, S0, do, dS_final=None, *, want_dS0:
     dS0 = torch.empty((B, H, dk, dv), dtype=f32, device=dev) if want_dS0 else None
     shape = _chunk_shape(q, v, log_alpha, beta)
     lib = library()
-    ws = lib.kda_recurrence_bwd_workspace_bytes(ctypes.byref(shape))
+    if flags is None:
+        ws = lib.kda_recurrence_bwd_workspace_bytes(ctypes.byref(shape))
+    else:
+        ws = lib.kda_recurrence_bwd_ex_workspace_bytes(ctypes.byref(shape), flags)
     if workspace is None:
         workspace = torch.empty(ws, dtype=torch.uint8, device=dev) if ws else None
     else:
         _require(workspace, "workspace")
     ws_given = workspace.numel() * workspace.element_size() if workspace is not None else 0
-    _check(lib.kda_recurrence_bwd(ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha),
-                                  _ptr(beta), _ptr(S0), _ptr(do), _ptr(dS_final), _ptr(dq),
-                                  _ptr(dk_), _ptr(dv_), _ptr(dla), _ptr(dbeta), _ptr(dS0),
-                                  _ptr(workspace), ws_given, _stream(v)))
+    args = (_ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(beta), _ptr(S0), _ptr(do),
+            _ptr(dS_final), _ptr(dq), _ptr(dk_), _ptr(dv_), _ptr(dla), _ptr(dbeta), _ptr(dS0),
+            _ptr(workspace), ws_given, _stream(v))
+    if flags is None:
+        _check(lib.kda_recurrence_bwd(ctypes.byref(shape), *args))
+    else:
+        _check(lib.kda_recurrence_bwd_ex(ctypes.byref(shape), flags, *args))
     return dq, dk_, dv_, dla, dbeta, dS0
 
 

@@ -648,6 +648,127 @@ int kda_recurrence_bwd(const kda_shape* s, const void* q, const void* k, const v
     return KDA_OK;
 }
 
+namespace {
+// Layout of kda_recurrence_bwd_ex's workspace: the gradient kernel's own
+// area, then the fp32 preprocessed inputs and the row norms, each piece
+// rounded up to 256 bytes.
+struct BwdExPlan {
+    int64_t ckpt = 0, qn = 0, kn = 0, v32 = 0, do32 = 0, la32 = 0, b32 = 0, nq = 0, nk = 0;
+    int64_t total = 0;
+};
+BwdExPlan bwd_ex_plan(const kda_shape* s) {
+    auto up = [](int64_t x) { return (x + 255) / 256 * 256; };
+    const int64_t rows = s->B * s->H * s->L;
+    BwdExPlan p;
+    int64_t off = up(kda::bwd_workspace_bytes(s->B * s->H, s->L, (int)s->dk, (int)s->dv));
+    p.ckpt = 0;
+    p.qn = off; off += up(rows * s->dk * 4);
+    p.kn = off; off += up(rows * s->dk * 4);
+    p.v32 = off; off += up(rows * s->dv * 4);
+    p.do32 = off; off += up(rows * s->dv * 4);
+    p.la32 = off; off += up(s->alpha_mode == KDA_ALPHA_CHANNEL ? rows * s->dk * 4 : rows * 4);
+    p.b32 = off; off += up(rows * 4);
+    p.nq = off; off += up(rows * 4);
+    p.nk = off; off += up(rows * 4);
+    p.total = off;
+    return p;
+}
+}  // namespace
+
+size_t kda_recurrence_bwd_ex_workspace_bytes(const kda_shape* s, uint32_t flags) {
+    if (check_shape(s, false) != KDA_OK || (flags & ~kAllFlags)) return 0;
+    if (s->B * s->H * s->L == 0) return 0;
+    return (size_t)bwd_ex_plan(s).total;
+}
+
+int kda_recurrence_bwd_ex(const kda_shape* s, uint32_t flags, const void* q, const void* k,
+                          const void* v, const void* log_alpha, const void* beta,
+                          const float* S0, const void* dout, const float* dS_final, float* dq,
+                          float* dk, float* dv, float* dlog_alpha, float* dbeta, float* dS0,
+                          void* workspace, size_t workspace_bytes, void* hip_stream) {
+    int rc = check_shape(s, false);
+    if (rc != KDA_OK) return rc;
+    if (flags & ~kAllFlags) return KDA_ERR_FLAGS;
+    const int64_t bh = s->B * s->H, rows = bh * s->L;
+    if (rows == 0)  // nothing to preprocess: the plain call (dS0 = dS_final)
+        return kda_recurrence_bwd(s, q, k, v, log_alpha, beta, S0, dout, dS_final, dq, dk, dv,
+                                  dlog_alpha, dbeta, dS0, workspace, workspace_bytes, hip_stream);
+    const bool has_alpha = s->alpha_mode != KDA_ALPHA_NONE;
+    if (!q || !k || !v || !beta || !dout || !dq || !dk || !dv || !dbeta) return KDA_ERR_NULL;
+    if (has_alpha && (!log_alpha || !dlog_alpha)) return KDA_ERR_NULL;
+    if (!workspace) return KDA_ERR_NULL;
+    const BwdExPlan pl = bwd_ex_plan(s);
+    if ((int64_t)workspace_bytes < pl.total) return KDA_ERR_WORKSPACE;
+    const void* ptrs[] = {q, k, v, has_alpha ? log_alpha : nullptr, beta, S0, dout, dS_final,
+                          dq, dk, dv, has_alpha ? dlog_alpha : nullptr, dbeta, dS0, workspace};
+    for (const void* p : ptrs)
+        if (p && !aligned16(p)) return KDA_ERR_ALIGN;
+    // the raw inputs against the outputs and the workspace (the plain call
+    // below checks the outputs against each other and the fp32 copies)
+    const int eq = elem_size(s->qkv_dtype), eg = elem_size(s->gate_dtype);
+    const int64_t la_elems = s->alpha_mode == KDA_ALPHA_CHANNEL ? rows * s->dk : rows;
+    const int64_t st = bh * s->dk * s->dv * 4;
+    const Span in[] = {span_of(q, rows * s->dk * eq), span_of(k, rows * s->dk * eq),
+                       span_of(v, rows * s->dv * eq),
+                       span_of(has_alpha ? log_alpha : nullptr, la_elems * eg),
+                       span_of(beta, rows * eg), span_of(S0, st),
+                       span_of(dout, rows * s->dv * eq), span_of(dS_final, st)};
+    const Span out[] = {span_of(dq, rows * s->dk * 4), span_of(dk, rows * s->dk * 4),
+                        span_of(dv, rows * s->dv * 4),
+                        span_of(has_alpha ? dlog_alpha : nullptr, la_elems * 4),
+                        span_of(dbeta, rows * 4), span_of(dS0, st),
+                        span_of(workspace, pl.total)};
+    for (const Span& o : out)
+        for (const Span& x : in)
+            if (overlaps(o, x)) return KDA_ERR_ALIAS;
+
+    char* ws = (char*)workspace;
+    kda::BwdPrep pp;
+    pp.q = q;
+    pp.k = k;
+    pp.v = v;
+    pp.dout = dout;
+    pp.log_alpha = has_alpha ? log_alpha : nullptr;
+    pp.beta = beta;
+    pp.qn = (float*)(ws + pl.qn);
+    pp.kn = (float*)(ws + pl.kn);
+    pp.v32 = (float*)(ws + pl.v32);
+    pp.do32 = (float*)(ws + pl.do32);
+    pp.la32 = (float*)(ws + pl.la32);
+    pp.b32 = (float*)(ws + pl.b32);
+    pp.nq = (float*)(ws + pl.nq);
+    pp.nk = (float*)(ws + pl.nk);
+    pp.dq = dq;
+    pp.dk = dk;
+    pp.dlog_alpha = has_alpha ? dlog_alpha : nullptr;
+    pp.dbeta = dbeta;
+    pp.rows = rows;
+    pp.DK = (int)s->dk;
+    pp.DV = (int)s->dv;
+    pp.alpha_mode = s->alpha_mode;
+    pp.flags = flags;
+    const hipStream_t stream = (hipStream_t)hip_stream;
+    hipError_t err = kda::launch_bwd_prep(pp, s->qkv_dtype == KDA_BF16,
+                                          s->gate_dtype == KDA_BF16, stream);
+    if (err != hipSuccess) {
+        g_last_error = std::string("kda_recurrence_bwd_ex: ") + hipGetErrorString(err);
+        return KDA_ERR_HIP;
+    }
+    kda_shape s32 = *s;
+    s32.qkv_dtype = KDA_F32;
+    s32.gate_dtype = KDA_F32;
+    rc = kda_recurrence_bwd(&s32, pp.qn, pp.kn, pp.v32, has_alpha ? pp.la32 : nullptr, pp.b32,
+                            S0, pp.do32, dS_final, dq, dk, dv, dlog_alpha, dbeta, dS0,
+                            ws + pl.ckpt, (size_t)pl.qn, hip_stream);
+    if (rc != KDA_OK) return rc;
+    err = kda::launch_bwd_post(pp, stream);
+    if (err != hipSuccess) {
+        g_last_error = std::string("kda_recurrence_bwd_ex: ") + hipGetErrorString(err);
+        return KDA_ERR_HIP;
+    }
+    return KDA_OK;
+}
+
 int kda_decode_step(const kda_shape* s, const void* q, const void* k, const void* v,
                     const void* log_alpha, const void* beta, float* S, void* o,
                     void* hip_stream) {

@@ -452,6 +452,83 @@ hipError_t zero(float* a, int64_t n, hipStream_t stream) {
     return hipGetLastError();
 }
 
+// ---- raw inputs: preprocessing before, chain rule after --------------------
+// One wave per (head, token) row.  Prep: q and k (normalized when asked) and
+// v, dJ/do as fp32; beta (through the sigmoid when asked) and ln alpha (-exp
+// of the raw gate when asked) as fp32; |q| and |k|.  Post: dq and dk through
+// the normalization, dbeta through the sigmoid, d ln alpha through -exp.
+template <typename E, typename G>
+__global__ void __launch_bounds__(64) kda_bwd_prep_kernel(BwdPrep p) {
+    const int l = lane_id();
+    const int64_t row = blockIdx.x;  // bh * L + t
+    const E* q = (const E*)p.q + row * p.DK;
+    const E* k = (const E*)p.k + row * p.DK;
+    float sq = 0.f, sk = 0.f;
+    for (int i = l; i < p.DK; i += 64) {
+        const float a = to_f32(q[i]), b = to_f32(k[i]);
+        sq += a * a;
+        sk += b * b;
+    }
+    sq = group_sum<64>(sq);
+    sk = group_sum<64>(sk);
+    const bool norm = p.flags & KDA_IN_NORM_QK;
+    const float iq = norm ? inv_norm(sq) : 1.f, ik = norm ? inv_norm(sk) : 1.f;
+    for (int i = l; i < p.DK; i += 64) {
+        p.qn[row * p.DK + i] = to_f32(q[i]) * iq;
+        p.kn[row * p.DK + i] = to_f32(k[i]) * ik;
+    }
+    for (int i = l; i < p.DV; i += 64) {
+        p.v32[row * p.DV + i] = to_f32(((const E*)p.v)[row * p.DV + i]);
+        p.do32[row * p.DV + i] = to_f32(((const E*)p.dout)[row * p.DV + i]);
+    }
+    const bool raw_gate = p.flags & KDA_IN_GATE_RAW;
+    if (p.alpha_mode == KDA_ALPHA_CHANNEL) {
+        for (int i = l; i < p.DK; i += 64) {
+            const float g = to_f32(((const G*)p.log_alpha)[row * p.DK + i]);
+            p.la32[row * p.DK + i] = raw_gate ? log_alpha_of_raw(g) : g;
+        }
+    }
+    if (l == 0) {
+        const float b = to_f32(((const G*)p.beta)[row]);
+        p.b32[row] = (p.flags & KDA_IN_BETA_LOGIT) ? sigmoid(b) : b;
+        if (p.alpha_mode == KDA_ALPHA_HEAD) {
+            const float g = to_f32(((const G*)p.log_alpha)[row]);
+            p.la32[row] = raw_gate ? log_alpha_of_raw(g) : g;
+        }
+        p.nq[row] = sqrtf(sq);
+        p.nk[row] = sqrtf(sk);
+    }
+}
+
+__global__ void __launch_bounds__(64) kda_bwd_post_kernel(BwdPrep p) {
+    const int l = lane_id();
+    const int64_t row = blockIdx.x;
+    if (p.flags & KDA_IN_NORM_QK) {
+        // d raw = (dn - n (n . dn)) / |x| above the 1e-12 floor, dn / 1e-12 at it
+#pragma unroll
+        for (int w = 0; w < 2; ++w) {
+            float* d = (w ? p.dk : p.dq) + row * p.DK;
+            const float* xn = (w ? p.kn : p.qn) + row * p.DK;
+            const float nrm = (w ? p.nk : p.nq)[row];
+            float dot = 0.f;
+            for (int i = l; i < p.DK; i += 64) dot += xn[i] * d[i];
+            dot = group_sum<64>(dot);
+            for (int i = l; i < p.DK; i += 64)
+                d[i] = nrm > 1e-12f ? (d[i] - xn[i] * dot) / nrm : d[i] / 1e-12f;
+        }
+    }
+    if ((p.flags & KDA_IN_GATE_RAW) && p.alpha_mode == KDA_ALPHA_CHANNEL)
+        for (int i = l; i < p.DK; i += 64) p.dlog_alpha[row * p.DK + i] *= p.la32[row * p.DK + i];
+    if (l == 0) {
+        if (p.flags & KDA_IN_BETA_LOGIT) {
+            const float b = p.b32[row];
+            p.dbeta[row] *= b * (1.f - b);
+        }
+        if ((p.flags & KDA_IN_GATE_RAW) && p.alpha_mode == KDA_ALPHA_HEAD)
+            p.dlog_alpha[row] *= p.la32[row];
+    }
+}
+
 }  // namespace
 
 int64_t bwd_workspace_bytes(int64_t bh, int64_t L, int dk, int dv) {
@@ -490,6 +567,26 @@ hipError_t launch_bwd(const BwdParams& prm, int dk, int qkv_bf16, hipStream_t st
     KDA_MODES(64, float)
 #undef KDA_MODES
     return hipErrorInvalidValue;
+}
+
+hipError_t launch_bwd_prep(const BwdPrep& prm, int qkv_bf16, int gate_bf16, hipStream_t stream) {
+    if (prm.rows == 0) return hipSuccess;
+    const dim3 grid((unsigned)prm.rows);
+    if (qkv_bf16 && gate_bf16)
+        hipLaunchKernelGGL((kda_bwd_prep_kernel<bf16, bf16>), grid, dim3(64), 0, stream, prm);
+    else if (qkv_bf16)
+        hipLaunchKernelGGL((kda_bwd_prep_kernel<bf16, float>), grid, dim3(64), 0, stream, prm);
+    else if (gate_bf16)
+        hipLaunchKernelGGL((kda_bwd_prep_kernel<float, bf16>), grid, dim3(64), 0, stream, prm);
+    else
+        hipLaunchKernelGGL((kda_bwd_prep_kernel<float, float>), grid, dim3(64), 0, stream, prm);
+    return hipGetLastError();
+}
+
+hipError_t launch_bwd_post(const BwdPrep& prm, hipStream_t stream) {
+    if (prm.rows == 0) return hipSuccess;
+    hipLaunchKernelGGL(kda_bwd_post_kernel, dim3((unsigned)prm.rows), dim3(64), 0, stream, prm);
+    return hipGetLastError();
 }
 
 }  // namespace kda

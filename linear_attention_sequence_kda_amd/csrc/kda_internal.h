@@ -207,4 +207,19 @@ int64_t bwd_workspace_bytes(int64_t bh, int64_t L, int dk, int dv);
 hipError_t zero_bwd_outputs(const BwdParams& prm, int dk, hipStream_t stream);
 hipError_t launch_bwd(const BwdParams& prm, int dk, int qkv_bf16, hipStream_t stream);
 
+// Raw-input gradients: the preprocessed fp32 copies the gradient kernel reads,
+// and the chain rule applied to its outputs in place afterwards.
+struct BwdPrep {
+    const void *q, *k, *v, *dout, *log_alpha, *beta;  // raw inputs
+    float *qn, *kn, *v32, *do32, *la32, *b32;          // [rows, dk|dv] / [rows]
+    float *nq, *nk;                                    // |q|, |k| per row
+    float *dq, *dk, *dlog_alpha, *dbeta;               // gradients (post, in place)
+    int64_t rows;                                      // B * H * L
+    int DK, DV;
+    int alpha_mode;
+    uint32_t flags;
+};
+hipError_t launch_bwd_prep(const BwdPrep& prm, int qkv_bf16, int gate_bf16, hipStream_t stream);
+hipError_t launch_bwd_post(const BwdPrep& prm, hipStream_t stream);
+
 }  // namespace kda

@@ -366,3 +366,36 @@ def test_recurrence_bwd_host_checks(lib):
     assert bwd(lib, bad, bwd_bufs()) == 2
     none = {n: None for n in bwd_bufs()}
     assert bwd(lib, shape(B=0), none) == 0                           # empty problem
+
+
+def bwd_ex(lib, s, flags, b, wsb=1 << 30):
+    return lib.kda_recurrence_bwd_ex(ctypes.byref(s) if s is not None else None, flags, b["q"],
+                                     b["k"], b["v"], b["la"], b["beta"], b["S0"], b["do"],
+                                     b["dSf"], b["dq"], b["dk"], b["dv"], b["dla"], b["dbeta"],
+                                     b["dS0"], b["ws"], wsb, None)
+
+
+def test_recurrence_bwd_ex_host_checks(lib):
+    s = shape()
+    plain = lib.kda_recurrence_bwd_workspace_bytes(ctypes.byref(s))
+    ws = lib.kda_recurrence_bwd_ex_workspace_bytes(ctypes.byref(s), 7)
+    assert ws > plain                                  # plus the fp32 copies and norms
+    assert lib.kda_recurrence_bwd_ex_workspace_bytes(ctypes.byref(s), 8) == 0
+    assert lib.kda_recurrence_bwd_ex_workspace_bytes(ctypes.byref(shape(L=0)), 7) == 0
+    assert bwd_ex(lib, s, 8, bwd_bufs()) == 9          # unknown flag bit
+    assert bwd_ex(lib, None, 7, bwd_bufs()) == 1
+    assert bwd_ex(lib, s, 7, bwd_bufs(), wsb=ws - 1) == 6
+    for name in ["q", "k", "v", "la", "beta", "do", "dq", "dk", "dv", "dla", "dbeta", "ws"]:
+        b = bwd_bufs()
+        b[name] = None
+        assert bwd_ex(lib, s, 7, b) == 1, name
+    for name in bwd_bufs():
+        b = bwd_bufs()
+        b[name] += 8
+        assert bwd_ex(lib, s, 7, b) == 5, name
+    for out, inp in [("dq", "q"), ("ws", "k"), ("dbeta", "beta"), ("dS0", "S0")]:
+        b = bwd_bufs()
+        b[out] = b[inp] + 1024
+        assert bwd_ex(lib, s, 7, b) == 7, (out, inp)
+    none = {n: None for n in bwd_bufs()}
+    assert bwd_ex(lib, shape(B=0), 7, none) == 0

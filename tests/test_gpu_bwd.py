@@ -162,3 +162,59 @@ def test_workload_full_sampled_heads(cfg):
     8192 KDA) in the launch the benchmark times; the oracle checks two heads."""
     w = gen.WORKLOADS[cfg]
     run_and_compare(w, f"bwd-workload{cfg}", heads=[(0, 0), (w.B - 1, w.H - 1)])
+
+
+# ---- raw inputs (kda_recurrence_bwd_ex) ---------------------------------------
+
+ALL = oracle.NORM_QK | oracle.BETA_LOGIT | oracle.GATE_RAW
+
+
+def _mixed(w, flags):
+    """The raw draw where a flag asks for it, the preprocessed draw elsewhere."""
+    x, r = gen.prefill_inputs(w), gen.prefill_inputs(w, raw=True)
+    out = dict(x)
+    if flags & oracle.NORM_QK:
+        out["q"], out["k"] = r["q"], r["k"]
+    if flags & oracle.BETA_LOGIT:
+        out["beta"] = r["beta"]
+    if flags & oracle.GATE_RAW and w.alpha_mode != gen.ALPHA_NONE:
+        out["log_alpha"] = r["log_alpha"]
+    return out
+
+
+@pytest.mark.parametrize("flags", [ALL, oracle.NORM_QK, oracle.BETA_LOGIT | oracle.GATE_RAW])
+@pytest.mark.parametrize("qd,gd,mode", [("bf16", "bf16", "channel"), ("f32", "f32", "head"),
+                                        ("bf16", "f32", "none")])
+def test_raw_inputs_against_oracle(flags, qd, gd, mode):
+    import torch
+    kda = _kda()
+    w = gen.custom(B=2, H=2, L=77, dk=128, dv=64, qkv_dtype=qd, gate_dtype=gd, alpha_mode=mode,
+                   seed=500 + flags)
+    x = _mixed(w, flags)
+    do, dSf = upstream(w, 17, True)
+    d = device_inputs(w, x)
+    say(f"bwd-raw: recurrence_bwd_ex flags={flags} {qd}/{gd}/{mode} L={w.L}")
+    got = kda.recurrence_bwd(d["q"], d["k"], d["v"], d["log_alpha"], d["beta"], d["S0"],
+                             to_dev(do, w.qkv_dtype), to_dev(dSf, gen.F32), flags=flags)
+    torch.cuda.synchronize()
+    got = [None if g is None else to_f64(g) for g in got]
+    worst = {}
+    for b in range(w.B):
+        for h in range(w.H):
+            la = None if x["log_alpha"] is None else gen.widen(x["log_alpha"][b, h], w.gate_dtype)
+            ref = oracle.backward_raw(gen.widen(x["q"][b, h], w.qkv_dtype),
+                                      gen.widen(x["k"][b, h], w.qkv_dtype),
+                                      gen.widen(x["v"][b, h], w.qkv_dtype), la,
+                                      gen.widen(x["beta"][b, h], w.gate_dtype),
+                                      np.asarray(x["S0"][b, h], dtype=np.float64),
+                                      gen.widen(do[b, h], w.qkv_dtype),
+                                      dSf[b, h].astype(np.float64), flags)
+            for name, g, r in zip(NAMES, got, ref):
+                if r is None:
+                    assert g is None, name
+                    continue
+                err = np.abs(g[b, h] - r).max() / np.abs(r).max()
+                worst[name] = max(worst.get(name, 0.0), err)
+    say("bwd-raw: " + " ".join(f"{n}={e:.2e}" for n, e in worst.items()))
+    for name, e in worst.items():
+        assert e <= TOL, f"{name} error {e}"
