@@ -185,11 +185,12 @@ def _mixed(w, flags):
 @pytest.mark.parametrize("flags", [ALL, oracle.NORM_QK, oracle.BETA_LOGIT | oracle.GATE_RAW])
 @pytest.mark.parametrize("qd,gd,mode", [("bf16", "bf16", "channel"), ("f32", "f32", "head"),
                                         ("bf16", "f32", "none")])
-def test_raw_inputs_against_oracle(flags, qd, gd, mode):
+@pytest.mark.parametrize("dk,dv", [(128, 64), (64, 128)])
+def test_raw_inputs_against_oracle(flags, qd, gd, mode, dk, dv):
     import torch
     kda = _kda()
-    w = gen.custom(B=2, H=2, L=77, dk=128, dv=64, qkv_dtype=qd, gate_dtype=gd, alpha_mode=mode,
-                   seed=500 + flags)
+    w = gen.custom(B=2, H=2, L=77, dk=dk, dv=dv, qkv_dtype=qd, gate_dtype=gd, alpha_mode=mode,
+                   seed=500 + flags + dk)
     x = _mixed(w, flags)
     do, dSf = upstream(w, 17, True)
     d = device_inputs(w, x)
