@@ -1,26 +1,32 @@
 """Benchmark of the KDA / gated delta rule hot path on one MI355X.
 
-Prints ONE JSON line.  Headline: chunkwise prefill (kda_chunk_fwd) on the
-Gated DeltaNet workload B=4, H=16, L=4096, d_k=d_v=128, bf16 q/k/v, fp32 gates
-and state; one step = one kda_chunk_fwd over that batch (o and S_final
-written).  Decode leg in the same line: the KDA decode workload, 256 sequences
-x 32 heads, fp32 state updated in place for 64 steps.  Linear attention leg:
-normalized linear attention (phi = elu + 1, kda_linear_attn_fwd) on the
-prefill workload's shape.  Raw-input leg: the same prefill on raw inputs with
-the input preprocessing fused (kda_chunk_fwd_ex, all three flags).
+Prints ONE JSON line.  Headline: chunkwise KDA prefill (kda_chunk_fwd,
+per-channel decay) on the long-context workload B=1, H=16, L=524288,
+d_k=d_v=128, all inputs bf16, fp32 state, S_final returned; one step = one
+kda_chunk_fwd over that batch.  Further legs in the same line: the Gated
+DeltaNet workload (4 x 16 heads x 4096, scalar decay), the KDA workload
+(2 x 32 heads x 8192), the KDA decode workload (256 sequences x 32 heads, fp32
+state updated in place for 64 steps), gradients, raw inputs with fused
+preprocessing, and normalized linear attention.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload N]
 
 Inputs are seeded synthetic data (linear_attention_sequence_kda_amd.inputs),
 resident in HBM before the timed region.  The CPU baseline is the fp64 oracle
-(oracle/, C, all host cores of this job) timed on the same workload.
+(oracle/, C, all host cores of this job) timed on the headline workload.
+
+Timing: the headline value is K back-to-back calls between two device
+synchronizations (wall clock).  Every prefill leg is also timed call by call
+with HIP events after a 1 GiB write has flushed the 256 MiB memory-side cache
+(outside the events), which is the figure its `tokens_per_s` reports.
 
 `roofline` covers the kernel with the most time per step, timed with the
 library's HIP event pairs (kda_timing_*) on the call's stream, over K more
-steps right after the timed region: achieved = the compulsory bytes of the call that kernel reads or writes,
-per launch, / its mean launch time.  `path` covers the whole call (every launch)
-against HBM and against bf16 MFMA.  `traffic` is the kernel's measured HBM
-bytes per launch from profiles/traffic.json (rocprofv3 FETCH_SIZE and
+steps: achieved = the path's compulsory bytes per token-head (every input read
+once, o and the states written once) x the token-heads one launch of that
+kernel covers / its mean launch time.  `path` covers the whole call (every
+launch) against HBM and against bf16 MFMA.  `traffic` is the kernel's measured
+HBM bytes per launch from profiles/traffic.json (rocprofv3 FETCH_SIZE and
 WRITE_SIZE passes scaled by a copy of known size), or null when there is no
 measurement for the current sources.
 """
@@ -164,52 +170,50 @@ def bench_prefill(torch, kda, gen, w, steps, warmup):
     wsb = kda.chunk_fwd_workspace_bytes(d["q"], d["v"], d["log_alpha"], d["beta"])
     ws = torch.empty(max(wsb, 1), dtype=torch.uint8, device="cuda:0")
     args = (d["q"], d["k"], d["v"], d["log_alpha"], d["beta"], S0)
+    call = lambda: kda.chunk_fwd(*args, o=o, S_final=Sf, workspace=ws)
     for _ in range(warmup):
-        kda.chunk_fwd(*args, o=o, S_final=Sf, workspace=ws)
-    torch.cuda.synchronize()
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-          for _ in range(steps)]
+        call()
+    # K back-to-back calls between two synchronizations
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for s, e in ev:
-        s.record()
-        kda.chunk_fwd(*args, o=o, S_final=Sf, workspace=ws)
-        e.record()
+    for _ in range(steps):
+        call()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    # per-kernel durations: the same steps again with the library's event
-    # pairs around every launch (kept out of the region above, whose clock
-    # they would slow by a few microseconds per launch)
-    kern = kernel_times(torch, kda, steps,
-                        lambda: kda.chunk_fwd(*args, o=o, S_final=Sf, workspace=ws))
-    call_ms = [s.elapsed_time(e) for s, e in ev]
-    # the same call after a 1 GiB write has flushed the 256 MiB memory-side
-    # cache (as when other layers run between two calls); outside the timing
+    # the same K calls one by one, each after a 1 GiB write has flushed the
+    # 256 MiB memory-side cache (as when other layers run between two calls);
+    # the flush is outside the events
     flush = torch.empty(1 << 28, dtype=torch.float32, device="cuda:0")
-    cold_ms = []
-    for _ in range(min(steps, 10)):
+    call_ms = []
+    for _ in range(steps):
         flush.fill_(1.0)
         s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         s.record()
-        kda.chunk_fwd(*args, o=o, S_final=Sf, workspace=ws)
+        call()
         e.record()
         torch.cuda.synchronize()
-        cold_ms.append(s.elapsed_time(e))
+        call_ms.append(s.elapsed_time(e))
     del flush
-    return x, wall, call_ms, kern, wsb, cold_ms
+    # per-kernel durations: the same steps again with the library's event
+    # pairs around every launch (kept out of the regions above, whose clock
+    # they would slow by a few microseconds per launch)
+    kern = kernel_times(torch, kda, steps, call)
+    return x, wall, call_ms, kern, wsb
 
 
-def summarize_prefill(w, wall, call_ms, kern, steps, cold_ms=None):
+def summarize_prefill(w, wall, call_ms, kern, steps):
     """tokens/s of one prefill workload, each kernel's figures, the kernel with
-    the most time per step against HBM, and the whole call against both roofs."""
+    the most time per step against HBM, and the whole call against both roofs.
+    Call figures are the cache-flushed per-call times."""
     cavg = float(np.mean(call_ms))
     bytes_ = prefill_bytes(w)
     flops = prefill_flops(w)
+    th = w.B * w.H * w.L
     gbs = bytes_ / (cavg * 1e-3) / 1e9
     tflops = flops / (cavg * 1e-3) / 1e12
     mfma_peak = BF16_MFMA_PEAK_TFLOPS if w.qkv_dtype == "bf16" else FP32_MFMA_PEAK_TFLOPS
-    log(f"prefill {w.name}: {wall * 1e3 / steps:.4f} ms/step wall, call avg {cavg*1e3:.1f} us "
-        f"(min {min(call_ms)*1e3:.1f}), {gbs:.0f} GB/s, {tflops:.1f} TFLOP/s")
+    log(f"prefill {w.name}: {wall * 1e3 / steps:.4f} ms/step back-to-back, flushed call avg "
+        f"{cavg*1e3:.1f} us (min {min(call_ms)*1e3:.1f}), {gbs:.0f} GB/s, {tflops:.1f} TFLOP/s")
     kernels = {}
     for name, (per_step, ms) in kern.items():
         kb, kf = kernel_work(w, name)
@@ -224,34 +228,40 @@ def summarize_prefill(w, wall, call_ms, kern, steps, cold_ms=None):
     dom = max(kernels, key=lambda n: kernels[n]["avg_us"] * kernels[n]["launches_per_step"])
     kd = kernels[dom]
     path = {"avg_call_us": cavg * 1e3, "min_call_us": min(call_ms) * 1e3,
+            "back_to_back_call_us": wall * 1e6 / steps,
             "hbm": {"achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                    "frac": gbs / HBM_PEAK_GBS, "compulsory_bytes_per_call": bytes_},
+                    "frac": gbs / HBM_PEAK_GBS, "compulsory_bytes_per_call": bytes_,
+                    "bytes_per_token_head": bytes_ / th},
             "mfma": {"achieved": tflops, "peak": mfma_peak, "unit": "TFLOP/s",
-                     "frac": tflops / mfma_peak, "algorithmic_flops_per_call": flops}}
-    if cold_ms:
-        path["avg_call_us_after_cache_flush"] = float(np.mean(cold_ms)) * 1e3
-    # dominant kernel: compulsory bytes it moves per launch / its mean launch
-    # time (HIP events on the call's stream); the prefill's arithmetic
-    # intensity is left of the MI355X ridge, so HBM binds
-    roof = {"kernel": dom, "bound": "hbm", "achieved": kd["GB/s"],
-            "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": kd["GB/s"] / HBM_PEAK_GBS,
+                     "frac": tflops / mfma_peak, "algorithmic_flops_per_call": flops,
+                     "flops_per_token_head": flops / th}}
+    # dominant kernel: the path's compulsory bytes per token-head times the
+    # token-heads one launch covers, over its mean launch time (HIP events on
+    # the call's stream); the prefill's arithmetic intensity is left of the
+    # MI355X ridge, so HBM binds
+    per_launch = bytes_ / kd["launches_per_step"]
+    achieved = per_launch / (kd["avg_us"] * 1e-6) / 1e9
+    roof = {"kernel": dom, "bound": "hbm", "achieved": achieved,
+            "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
             "traffic": measured_traffic(dom, w.name),
-            "algorithmic_bytes_per_launch": kd["algorithmic_bytes_per_launch"],
+            "algorithmic_bytes_per_launch": per_launch,
+            "token_heads_per_launch": th / kd["launches_per_step"],
             "avg_kernel_us": kd["avg_us"]}
-    return {"tokens_per_s": w.B * w.L / (wall / steps), "ms_per_step": wall * 1e3 / steps,
+    return {"tokens_per_s": w.B * w.L / (cavg * 1e-3), "ms_per_step": cavg,
+            "back_to_back_tokens_per_s": w.B * w.L / (wall / steps),
             "roofline": roof, "kernels": kernels, "path": path}
 
 
 def bench_prefill_leg(torch, kda, gen, w, steps, warmup):
     """A further prefill workload in the same line (same timing as the headline)."""
-    x, wall, call_ms, kern, wsb, cold_ms = bench_prefill(torch, kda, gen, w, steps, warmup)
+    x, wall, call_ms, kern, wsb = bench_prefill(torch, kda, gen, w, steps, warmup)
     del x
     out = {"workload": w.name, "unit": "tokens/s",
            "config": {"batch": w.B, "heads": w.H, "seq_len": w.L, "d_k": w.dk, "d_v": w.dv,
                       "chunk": CHUNK, "alpha": w.alpha_mode, "qkv_dtype": w.qkv_dtype,
                       "gate_dtype": w.gate_dtype, "state_dtype": "f32",
                       "S0": w.s0_std is not None, "workspace_bytes": wsb}}
-    out.update(summarize_prefill(w, wall, call_ms, kern, steps, cold_ms))
+    out.update(summarize_prefill(w, wall, call_ms, kern, steps))
     torch.cuda.empty_cache()
     return out
 
@@ -422,25 +432,38 @@ def bench_linear_attention(torch, kda, gen, w, steps, warmup):
 
 
 def cpu_baseline(gen, w, x, min_seconds=10.0, max_passes=64):
-    """The fp64 oracle (C, threads over (head, 32-column block)) on the whole
-    prefill workload, repeated until about min_seconds of CPU time have gone."""
+    """The fp64 oracle (C, one worker per (head, 32-column block), all host
+    cores of the job) on the workload the headline times.  Heads run a few at
+    a time, so the fp64 outputs stay within a few GB of host memory; heads are
+    taken in order until every head has run once and about min_seconds of
+    compute have passed (whole passes over the workload are repeated while
+    they take less).  Value: the token rate this gives for the whole batch."""
     import oracle
     N = w.B * w.H
     f = lambda a: None if a is None else a.reshape((N,) + a.shape[2:])
+    xf = {k: f(v) for k, v in x.items()}
     threads = oracle.default_threads()
-    log(f"cpu baseline: oracle on the full workload with {threads} threads")
-    passes, dt = 0, 0.0
-    while dt < min_seconds and passes < max_passes:
+    group = max(1, min(N, threads // max(1, w.dv // 32)))
+    log(f"cpu baseline: oracle on {w.name}, {threads} threads, {group} heads at a time")
+    heads_done, dt, passes = 0, 0.0, 0
+    while passes < max_passes and (heads_done < N or dt < min_seconds):
+        h0 = heads_done % N
+        hs = slice(h0, min(N, h0 + group))
+        sl = {k: (None if v is None else np.ascontiguousarray(v[hs])) for k, v in xf.items()}
         t0 = time.perf_counter()
-        oracle.forward(f(x["q"]), f(x["k"]), f(x["v"]), f(x["log_alpha"]), f(x["beta"]),
-                       f(x["S0"]), qkv_dtype=w.qkv_dtype, gate_dtype=w.gate_dtype,
-                       alpha_mode=w.alpha_mode, want_o=True, threads=threads)
+        oracle.forward(sl["q"], sl["k"], sl["v"], sl["log_alpha"], sl["beta"], sl["S0"],
+                       qkv_dtype=w.qkv_dtype, gate_dtype=w.gate_dtype, alpha_mode=w.alpha_mode,
+                       want_o=True, threads=threads)
         dt += time.perf_counter() - t0
-        passes += 1
-    return {"value": passes * w.B * w.L / dt, "unit": "tokens/s", "cores": threads,
-            "kind": "oracle",
-            "sample": f"full {w.name} workload ({N} heads x {w.L} tokens, all columns, "
-                      f"o and S_final) x {passes} passes, {dt:.2f} s"}
+        heads_done += hs.stop - hs.start
+        passes = heads_done // N
+    # heads_done x L token-heads in dt seconds; the batch's tokens/s is that
+    # rate divided by the heads each token passes through
+    value = heads_done * w.L / w.H / dt
+    return {"value": value, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"{w.name}: {heads_done} head runs of {w.L} tokens (all {w.dv} columns, "
+                      f"o and S_final; the batch has {N} heads), {group} heads at a time, "
+                      f"{dt:.2f} s of oracle compute"}
 
 
 def main():
@@ -448,7 +471,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", type=int, default=2, help="prefill workload number (1-4)")
+    ap.add_argument("--workload", type=int, default=4, help="headline prefill workload number (1-4)")
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-linear-attention", action="store_true")
     ap.add_argument("--no-raw", action="store_true", help="skip the raw-input prefill leg")
@@ -479,10 +502,11 @@ def main():
         torch.cuda.synchronize()
         del src, dst
     w = gen.WORKLOADS[args.workload]
-    x, wall, call_ms, kern, wsb, cold_ms = bench_prefill(torch, kda, gen, w, args.steps, args.warmup)
-    head = summarize_prefill(w, wall, call_ms, kern, args.steps, cold_ms)
-    ms_per_step = head["ms_per_step"]
-    value = head["tokens_per_s"]
+    x, wall, call_ms, kern, wsb = bench_prefill(torch, kda, gen, w, args.steps, args.warmup)
+    head = summarize_prefill(w, wall, call_ms, kern, args.steps)
+    # the headline: K back-to-back calls between two synchronizations
+    ms_per_step = wall * 1e3 / args.steps
+    value = w.B * w.L / (wall / args.steps)
     out = {
         "metric": "KDA prefill tokens/s + MFMA util; decode tokens/s + HBM GB/s (1 MI355X)",
         "value": value,
@@ -498,12 +522,15 @@ def main():
         "data": "synthetic (seeded; shapes and distributions of the pages' workloads)",
         "config": {"workload": w.name, "batch": w.B, "heads": w.H, "seq_len": w.L,
                    "d_k": w.dk, "d_v": w.dv, "chunk": CHUNK, "alpha": w.alpha_mode,
-                   "gate_dtype": w.gate_dtype, "state_dtype": "f32",
+                   "qkv_dtype": w.qkv_dtype, "gate_dtype": w.gate_dtype,
+                   "state_dtype": "f32", "S0": w.s0_std is not None, "S_final": True,
                    "workspace_bytes": wsb},
         "roofline": head["roofline"],
         "kernels": head["kernels"],
-        # the whole kda_chunk_fwd call (every launch), against both roofs
+        # the whole kda_chunk_fwd call (every launch), against both roofs;
+        # flushed per-call figures
         "path": head["path"],
+        "flushed_tokens_per_s": head["tokens_per_s"],
     }
     if not args.no_decode:
         wd = gen.WORKLOADS[5]
@@ -523,23 +550,29 @@ def main():
                          "algorithmic_bytes_per_launch": dbytes,
                          "avg_kernel_us": dms * 1e3},
         }
+    # further prefill workloads: Gated DeltaNet (scalar decay, 4 x 16 x 4096)
+    # and the other KDA ones (2 x 32 x 8192; 1 x 16 x 524288)
+    legs = [("prefill_gated_deltanet", 2)]
     if not args.no_kda:
-        # the KDA (per-channel decay) workloads: 2 x 32 heads x 8192 tokens,
-        # and the long-context one, 16 heads x 524288 tokens with S_final
-        for key, n in (("prefill_kda", 3), ("prefill_kda_long_context", 4)):
-            if n != args.workload:
-                out[key] = bench_prefill_leg(torch, kda, gen, gen.WORKLOADS[n], args.steps,
-                                             args.warmup)
+        legs += [("prefill_kda", 3), ("prefill_kda_long_context", 4)]
+    for key, n in legs:
+        if n != args.workload:
+            out[key] = bench_prefill_leg(torch, kda, gen, gen.WORKLOADS[n], args.steps,
+                                         args.warmup)
+    # gradients, raw inputs and linear attention run on the Gated DeltaNet
+    # workload's shape (the gradient kernel's checkpoints of the long-context
+    # workload would not fit in HBM)
+    w2 = gen.WORKLOADS[2]
     if not args.no_bwd:
-        out["gradients"] = bench_bwd(torch, kda, gen, w, min(args.steps, 10), min(args.warmup, 2))
-        if not args.no_kda and args.workload != 3:
+        out["gradients"] = bench_bwd(torch, kda, gen, w2, min(args.steps, 10), min(args.warmup, 2))
+        if not args.no_kda:
             # the KDA workload's gradients (per-channel decay, 2 x 32 x 8192)
             out["gradients_kda"] = bench_bwd(torch, kda, gen, gen.WORKLOADS[3],
                                              min(args.steps, 5), min(args.warmup, 1))
     if not args.no_raw:
-        out["prefill_raw_inputs"] = bench_prefill_raw(torch, kda, gen, w, args.steps, args.warmup)
+        out["prefill_raw_inputs"] = bench_prefill_raw(torch, kda, gen, w2, args.steps, args.warmup)
     if not args.no_linear_attention:
-        out["linear_attention"] = bench_linear_attention(torch, kda, gen, w, args.steps,
+        out["linear_attention"] = bench_linear_attention(torch, kda, gen, w2, args.steps,
                                                          args.warmup)
     if not args.no_cpu:
         out["cpu_baseline"] = cpu_baseline(gen, w, x)

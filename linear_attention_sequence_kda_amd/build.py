@@ -28,21 +28,39 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found (ROCm is required to build libkda)")
 
 
-def build(verbose: bool = False) -> str:
-    """Compile every source into libkda.so for gfx950 (always recompiles)."""
-    tmp = LIB + ".tmp"
-    cmd = [hipcc(), f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared",
-           # packed fp32 VALU forms are kept out of the generated code
-           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-           "-Wno-unused-result", "-I", INCLUDE, "-I", CSRC]
-    cmd += [os.path.join(CSRC, s) for s in SOURCES]
-    cmd += ["-o", tmp]
+def _flags():
+    return [f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",
+            # packed fp32 VALU forms are kept out of the generated code
+            "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+            "-Wno-unused-result", "-I", INCLUDE, "-I", CSRC]
+
+
+def _run(cmd, verbose):
     if verbose:
         print(" ".join(cmd), flush=True)
     proc = subprocess.run(cmd, capture_output=True, text=True)
     if proc.returncode != 0:
         sys.stderr.write(proc.stdout + proc.stderr)
-        raise RuntimeError("building libkda.so failed")
+        raise RuntimeError("building libkda.so failed: " + " ".join(cmd[-3:]))
+
+
+def build(verbose: bool = False) -> str:
+    """Compile every source into libkda.so for gfx950 (always recompiles).
+
+    Each source is compiled to an object of its own, in parallel, then the
+    objects are linked into the shared library."""
+    from concurrent.futures import ThreadPoolExecutor
+
+    objdir = os.path.join(ROOT, "_build", "obj")
+    os.makedirs(objdir, exist_ok=True)
+    objs = [os.path.join(objdir, os.path.splitext(s)[0] + ".o") for s in SOURCES]
+    jobs = [[hipcc()] + _flags() + ["-c", os.path.join(CSRC, s), "-o", o]
+            for s, o in zip(SOURCES, objs)]
+    with ThreadPoolExecutor(max(1, min(len(jobs), os.cpu_count() or 1))) as ex:
+        for f in [ex.submit(_run, j, verbose) for j in jobs]:
+            f.result()
+    tmp = LIB + ".tmp"
+    _run([hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC"] + objs + ["-o", tmp], verbose)
     os.replace(tmp, LIB)
     return LIB
 

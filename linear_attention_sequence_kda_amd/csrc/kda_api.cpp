@@ -566,11 +566,15 @@ size_t kda_recurrence_bwd_workspace_bytes(const kda_shape* s) {
     return (size_t)kda::bwd_workspace_bytes(s->B * s->H, s->L, (int)s->dk, (int)s->dv);
 }
 
-int kda_recurrence_bwd(const kda_shape* s, const void* q, const void* k, const void* v,
-                       const void* log_alpha, const void* beta, const float* S0,
-                       const void* dout, const float* dS_final, float* dq, float* dk,
-                       float* dv, float* dlog_alpha, float* dbeta, float* dS0, void* workspace,
-                       size_t workspace_bytes, void* hip_stream) {
+}  // extern "C"
+
+namespace {
+// Every host check of kda_recurrence_bwd (no HIP call); KDA_OK when a launch
+// may follow.
+int bwd_checks(const kda_shape* s, const void* q, const void* k, const void* v,
+               const void* log_alpha, const void* beta, const float* S0, const void* dout,
+               const float* dS_final, float* dq, float* dk, float* dv, float* dlog_alpha,
+               float* dbeta, float* dS0, void* workspace, size_t workspace_bytes) {
     int rc = check_shape(s, false);
     if (rc != KDA_OK) return rc;
     const int64_t bh = s->B * s->H, tok = bh * s->L;
@@ -612,6 +616,22 @@ int kda_recurrence_bwd(const kda_shape* s, const void* q, const void* k, const v
         for (int j = i + 1; j < nout; ++j)
             if (overlaps(out[i], out[j])) return KDA_ERR_ALIAS;
     }
+    return KDA_OK;
+}
+}  // namespace
+
+extern "C" {
+
+int kda_recurrence_bwd(const kda_shape* s, const void* q, const void* k, const void* v,
+                       const void* log_alpha, const void* beta, const float* S0,
+                       const void* dout, const float* dS_final, float* dq, float* dk,
+                       float* dv, float* dlog_alpha, float* dbeta, float* dS0, void* workspace,
+                       size_t workspace_bytes, void* hip_stream) {
+    int rc = bwd_checks(s, q, k, v, log_alpha, beta, S0, dout, dS_final, dq, dk, dv, dlog_alpha,
+                        dbeta, dS0, workspace, workspace_bytes);
+    if (rc != KDA_OK) return rc;
+    const int64_t bh = s->B * s->H;
+    const bool has_alpha = s->alpha_mode != KDA_ALPHA_NONE;
     if (bh == 0) return KDA_OK;
 
     kda::BwdParams prm;
@@ -718,9 +738,17 @@ int kda_recurrence_bwd_ex(const kda_shape* s, uint32_t flags, const void* q, con
                         span_of(has_alpha ? dlog_alpha : nullptr, la_elems * 4),
                         span_of(dbeta, rows * 4), span_of(dS0, st),
                         span_of(workspace, pl.total)};
-    for (const Span& o : out)
+    const int nout = sizeof(out) / sizeof(out[0]);
+    for (int i = 0; i < nout; ++i) {
         for (const Span& x : in)
-            if (overlaps(o, x)) return KDA_ERR_ALIAS;
+            if (overlaps(out[i], x)) return KDA_ERR_ALIAS;
+        // the outputs against each other and against the whole workspace
+        // (which holds the fp32 copies and the row norms the chain rule reads)
+        for (int j = i + 1; j < nout; ++j)
+            if (overlaps(out[i], out[j])) return KDA_ERR_ALIAS;
+    }
+    // the prep and post kernels run one 64-lane workgroup per token row
+    if (rows > (int64_t)(UINT32_MAX / 64)) return KDA_ERR_SHAPE;
 
     char* ws = (char*)workspace;
     kda::BwdPrep pp;
@@ -747,6 +775,14 @@ int kda_recurrence_bwd_ex(const kda_shape* s, uint32_t flags, const void* q, con
     pp.DV = (int)s->dv;
     pp.alpha_mode = s->alpha_mode;
     pp.flags = flags;
+    kda_shape s32 = *s;
+    s32.qkv_dtype = KDA_F32;
+    s32.gate_dtype = KDA_F32;
+    // the inner call's own checks, before anything is enqueued
+    rc = bwd_checks(&s32, pp.qn, pp.kn, pp.v32, has_alpha ? pp.la32 : nullptr, pp.b32, S0,
+                    pp.do32, dS_final, dq, dk, dv, dlog_alpha, dbeta, dS0, ws + pl.ckpt,
+                    (size_t)pl.qn);
+    if (rc != KDA_OK) return rc;
     const hipStream_t stream = (hipStream_t)hip_stream;
     hipError_t err = kda::launch_bwd_prep(pp, s->qkv_dtype == KDA_BF16,
                                           s->gate_dtype == KDA_BF16, stream);
@@ -754,9 +790,6 @@ int kda_recurrence_bwd_ex(const kda_shape* s, uint32_t flags, const void* q, con
         g_last_error = std::string("kda_recurrence_bwd_ex: ") + hipGetErrorString(err);
         return KDA_ERR_HIP;
     }
-    kda_shape s32 = *s;
-    s32.qkv_dtype = KDA_F32;
-    s32.gate_dtype = KDA_F32;
     rc = kda_recurrence_bwd(&s32, pp.qn, pp.kn, pp.v32, has_alpha ? pp.la32 : nullptr, pp.b32,
                             S0, pp.do32, dS_final, dq, dk, dv, dlog_alpha, dbeta, dS0,
                             ws + pl.ckpt, (size_t)pl.qn, hip_stream);

@@ -101,9 +101,52 @@ def traffic(fetch_dir: str, write_dir: str, kernel: str) -> dict:
             "copy_write_factor": w_factor}
 
 
+# MFMA-busy pass: one rocprofv3 run with these counters (all in the SQ and
+# GRBM blocks, within one pass's limits)
+MFMA_COUNTERS = ["SQ_VALU_MFMA_BUSY_CYCLES", "SQ_INSTS_VALU_MFMA_MOPS_BF16",
+                 "SQ_INSTS_VALU_MFMA_MOPS_F32", "SQ_BUSY_CU_CYCLES", "GRBM_GUI_ACTIVE",
+                 "MfmaUtil"]
+SIMDS = 256 * 4   # MI355X: 256 CUs x 4 SIMDs
+
+
+def per_dispatch(pass_dir: str, counter: str, match: str, how=sum) -> Dict[str, float]:
+    """Counter value of every dispatch whose kernel name contains `match`,
+    keyed by dispatch id (rows of one dispatch combined by `how`)."""
+    vals: Dict[str, List[float]] = {}
+    for r in _rows(pass_dir):
+        if r["Counter_Name"] == counter and match in r["Kernel_Name"]:
+            vals.setdefault(r["Dispatch_Id"], []).append(float(r["Counter_Value"]))
+    return {k: how(v) for k, v in vals.items()}
+
+
+def mfma(pass_dir: str, kernel: str) -> dict:
+    """MFMA utilisation of one kernel's dispatches: the MFMA pipes' busy
+    cycles summed over all SIMDs / (GPU active cycles x SIMDs), and the bf16
+    and fp32 MFMA flops the SQ counted (MOPS x 512)."""
+    busy = per_dispatch(pass_dir, "SQ_VALU_MFMA_BUSY_CYCLES", kernel)
+    gui = per_dispatch(pass_dir, "GRBM_GUI_ACTIVE", kernel, max)
+    tool = per_dispatch(pass_dir, "MfmaUtil", kernel)
+    bf = per_dispatch(pass_dir, "SQ_INSTS_VALU_MFMA_MOPS_BF16", kernel)
+    f32 = per_dispatch(pass_dir, "SQ_INSTS_VALU_MFMA_MOPS_F32", kernel)
+    cu = per_dispatch(pass_dir, "SQ_BUSY_CU_CYCLES", kernel)
+    ids = sorted(set(busy) & set(gui), key=int)
+    if not ids:
+        raise ValueError(f"no dispatch of {kernel} with MFMA counters under {pass_dir}")
+    n = len(ids)
+    avg = lambda d: sum(d.get(i, 0.0) for i in ids) / n
+    util = sum(busy[i] / (gui[i] * SIMDS) for i in ids if gui[i] > 0) / n
+    return {"dispatches": n, "mfma_busy_cycles": avg(busy), "gui_active_cycles": avg(gui),
+            "mfma_util": util, "bf16_mfma_flops": avg(bf) * 512, "f32_mfma_flops": avg(f32) * 512,
+            "busy_cu_quad_cycles": avg(cu),
+            "mfma_util_rocprof_pct": avg(tool) if tool else None}
+
+
 def main():
     ap = argparse.ArgumentParser()
     sub = ap.add_subparsers(dest="cmd", required=True)
+    m = sub.add_parser("mfma")
+    m.add_argument("--pmc", required=True, help="directory of the MFMA counter pass")
+    m.add_argument("--kernel", required=True, action="append")
     t = sub.add_parser("traffic")
     t.add_argument("--fetch", required=True)
     t.add_argument("--write", required=True)
@@ -111,6 +154,10 @@ def main():
     t.add_argument("--workload", required=True)
     t.add_argument("--out", required=True)
     a = ap.parse_args()
+    if a.cmd == "mfma":
+        for k in a.kernel:
+            print(json.dumps({"kernel": k, **mfma(a.pmc, k)}))
+        return
     rec = traffic(a.fetch, a.write, a.kernel)
     rec["source_sha256"] = source_digest(a.kernel)
     data = {}

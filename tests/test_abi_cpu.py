@@ -399,3 +399,34 @@ def test_recurrence_bwd_ex_host_checks(lib):
         assert bwd_ex(lib, s, 7, b) == 7, (out, inp)
     none = {n: None for n in bwd_bufs()}
     assert bwd_ex(lib, shape(B=0), 7, none) == 0
+
+
+def test_recurrence_bwd_ex_outputs_against_workspace_and_each_other(lib):
+    """Every output is checked against the whole raw-input workspace (its fp32
+    copies and row norms) and against the other outputs before anything is
+    enqueued."""
+    s = shape()
+    ws = lib.kda_recurrence_bwd_ex_workspace_bytes(ctypes.byref(s), 7)
+    plain = lib.kda_recurrence_bwd_workspace_bytes(ctypes.byref(s))
+    for out in ["dq", "dk", "dv", "dla", "dbeta", "dS0"]:
+        # inside the workspace, past the gradient kernel's own area (the
+        # fp32 copies and the norms at its end)
+        for off in (plain + 4096, ws - 4096):
+            b = bwd_bufs()
+            b[out] = b["ws"] + (off // 256) * 256
+            assert bwd_ex(lib, s, 7, b) == 7, (out, off)
+    for a, c in [("dq", "dk"), ("dv", "dbeta"), ("dla", "dS0"), ("dk", "dv")]:
+        b = bwd_bufs()
+        b[a] = b[c] + 1024
+        assert bwd_ex(lib, s, 7, b) == 7, (a, c)
+
+
+def test_recurrence_bwd_ex_row_limit(lib):
+    """The prep and post kernels take one 64-lane workgroup per token row:
+    more rows than 2^32 / 64 are rejected on the host."""
+    # 17 x 4,000,000 rows: a valid shape otherwise (L within the per-head
+    # limit), just above 2^26 rows
+    s = shape(B=17, H=1, L=4_000_000, dk=64, dv=64)
+    assert lib.kda_recurrence_bwd_workspace_bytes(ctypes.byref(s)) > 0
+    b = {n: BASE + i * (1 << 40) for i, n in enumerate(bwd_bufs())}
+    assert bwd_ex(lib, s, 7, b, wsb=1 << 62) == 2
