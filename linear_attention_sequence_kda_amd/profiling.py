@@ -104,41 +104,45 @@ def traffic(fetch_dir: str, write_dir: str, kernel: str) -> dict:
 # MFMA-busy pass: one rocprofv3 run with these counters (all in the SQ and
 # GRBM blocks, within one pass's limits)
 MFMA_COUNTERS = ["SQ_VALU_MFMA_BUSY_CYCLES", "SQ_INSTS_VALU_MFMA_MOPS_BF16",
-                 "SQ_INSTS_VALU_MFMA_MOPS_F32", "SQ_BUSY_CU_CYCLES", "GRBM_GUI_ACTIVE",
-                 "MfmaUtil"]
+                 "SQ_INSTS_VALU_MFMA_MOPS_F32", "SQ_BUSY_CU_CYCLES", "GRBM_GUI_ACTIVE"]
 SIMDS = 256 * 4   # MI355X: 256 CUs x 4 SIMDs
+XCDS = 8          # GRBM_GUI_ACTIVE comes summed over the 8 XCDs
 
 
-def per_dispatch(pass_dir: str, counter: str, match: str, how=sum) -> Dict[str, float]:
-    """Counter value of every dispatch whose kernel name contains `match`,
-    keyed by dispatch id (rows of one dispatch combined by `how`)."""
-    vals: Dict[str, List[float]] = {}
+def mfma(pass_dir: str, kernel: str) -> List[dict]:
+    """MFMA utilisation of one kernel's dispatches, grouped by grid size (one
+    group per workload): the MFMA pipes' busy cycles summed over all SIMDs /
+    (the GPU's active cycles x SIMDs), and the bf16 and fp32 MFMA flops the SQ
+    counted (MOPS x 512).  rocprofv3 gives one row per dispatch and counter;
+    GRBM_GUI_ACTIVE is the sum of the XCDs' counts, so one XCD's active
+    cycles are that / 8."""
+    disp: Dict[str, dict] = {}
     for r in _rows(pass_dir):
-        if r["Counter_Name"] == counter and match in r["Kernel_Name"]:
-            vals.setdefault(r["Dispatch_Id"], []).append(float(r["Counter_Value"]))
-    return {k: how(v) for k, v in vals.items()}
-
-
-def mfma(pass_dir: str, kernel: str) -> dict:
-    """MFMA utilisation of one kernel's dispatches: the MFMA pipes' busy
-    cycles summed over all SIMDs / (GPU active cycles x SIMDs), and the bf16
-    and fp32 MFMA flops the SQ counted (MOPS x 512)."""
-    busy = per_dispatch(pass_dir, "SQ_VALU_MFMA_BUSY_CYCLES", kernel)
-    gui = per_dispatch(pass_dir, "GRBM_GUI_ACTIVE", kernel, max)
-    tool = per_dispatch(pass_dir, "MfmaUtil", kernel)
-    bf = per_dispatch(pass_dir, "SQ_INSTS_VALU_MFMA_MOPS_BF16", kernel)
-    f32 = per_dispatch(pass_dir, "SQ_INSTS_VALU_MFMA_MOPS_F32", kernel)
-    cu = per_dispatch(pass_dir, "SQ_BUSY_CU_CYCLES", kernel)
-    ids = sorted(set(busy) & set(gui), key=int)
-    if not ids:
+        if kernel not in r["Kernel_Name"]:
+            continue
+        d = disp.setdefault(r["Dispatch_Id"], {"grid": int(r["Grid_Size"]),
+                                                "ns": int(r["End_Timestamp"]) - int(r["Start_Timestamp"])})
+        d[r["Counter_Name"]] = float(r["Counter_Value"])
+    groups: Dict[int, List[dict]] = {}
+    for d in disp.values():
+        if "SQ_VALU_MFMA_BUSY_CYCLES" in d and d.get("GRBM_GUI_ACTIVE", 0) > 0:
+            groups.setdefault(d["grid"], []).append(d)
+    if not groups:
         raise ValueError(f"no dispatch of {kernel} with MFMA counters under {pass_dir}")
-    n = len(ids)
-    avg = lambda d: sum(d.get(i, 0.0) for i in ids) / n
-    util = sum(busy[i] / (gui[i] * SIMDS) for i in ids if gui[i] > 0) / n
-    return {"dispatches": n, "mfma_busy_cycles": avg(busy), "gui_active_cycles": avg(gui),
-            "mfma_util": util, "bf16_mfma_flops": avg(bf) * 512, "f32_mfma_flops": avg(f32) * 512,
-            "busy_cu_quad_cycles": avg(cu),
-            "mfma_util_rocprof_pct": avg(tool) if tool else None}
+    out = []
+    for grid, ds in sorted(groups.items()):
+        n = len(ds)
+        avg = lambda key: sum(d.get(key, 0.0) for d in ds) / n
+        util = sum(d["SQ_VALU_MFMA_BUSY_CYCLES"] / (d["GRBM_GUI_ACTIVE"] / XCDS * SIMDS)
+                   for d in ds) / n
+        out.append({"kernel": kernel, "grid_size": grid, "dispatches": n,
+                    "avg_dispatch_us": avg("ns") / 1e3,
+                    "mfma_busy_cycles": avg("SQ_VALU_MFMA_BUSY_CYCLES"),
+                    "gui_active_cycles_per_xcd": avg("GRBM_GUI_ACTIVE") / XCDS,
+                    "mfma_util": util,
+                    "bf16_mfma_flops": avg("SQ_INSTS_VALU_MFMA_MOPS_BF16") * 512,
+                    "f32_mfma_flops": avg("SQ_INSTS_VALU_MFMA_MOPS_F32") * 512})
+    return out
 
 
 def main():
@@ -156,7 +160,8 @@ def main():
     a = ap.parse_args()
     if a.cmd == "mfma":
         for k in a.kernel:
-            print(json.dumps({"kernel": k, **mfma(a.pmc, k)}))
+            for rec in mfma(a.pmc, k):
+                print(json.dumps(rec))
         return
     rec = traffic(a.fetch, a.write, a.kernel)
     rec["source_sha256"] = source_digest(a.kernel)
