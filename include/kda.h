@@ -25,11 +25,13 @@
  *   log_alpha: [B,H,L,dk] (KDA_ALPHA_CHANNEL) or [B,H,L] (KDA_ALPHA_HEAD) or
  *   unused (KDA_ALPHA_NONE, alpha = 1; may be NULL).  States are fp32
  *   [B,H,dk,dv] with d_v contiguous.  Decode drops the L axis (L must be 1).
- * - log_alpha holds ln(alpha_t), which must be finite and <= 0.  The GPU
- *   kernels factor the decay inside a 16-token sub-block and are exact to
- *   rounding for log_alpha >= -5 per token and channel (alpha >= 0.0067);
- *   smaller values are not checked and may lose accuracy.  beta should be in
- *   [0, 1].  Neither is checked; NaN or Inf stays inside its own (b, h).
+ * - log_alpha holds ln(alpha_t), which must be finite and <= 0; any such
+ *   value is supported (alpha may underflow to 0, which wipes the channel).
+ *   The prefill kernels split each per-channel decay factor at 16-token
+ *   sub-block boundaries so that no intermediate leaves the float range; a
+ *   sub-block whose summed ln(alpha) falls below -69 in some channel has its
+ *   diagonal blocks summed directly (slower, same result).  beta should be
+ *   in [0, 1].  Neither is checked; NaN or Inf stays inside its own (b, h).
  * - q, k, v and o share qkv_dtype; log_alpha and beta share gate_dtype.
  *   Arithmetic: fp32 inputs are computed entirely in fp32 (fp32 MFMA); bf16
  *   inputs use bf16 MFMA operands with fp32 accumulation, and the state is

@@ -34,12 +34,20 @@
 // the columns of T diag(beta).
 //
 // Per-channel decay (KDA): e^{g_rc - g_jc} stays inside the sums and is split
-// at the end of r's 16-token sub-block R (cumulative G_{R+1}): the row operand
-// carries e^{g_r - G_{R+1}} (>= 1, at most e^{16 |ln alpha|}), the column
-// operand e^{G_{J+1} - g_j} (<= 1) and, for J < R, a per-channel pair scale
-// e^{G_{R+1} - G_{J+1}} (<= 1).  A diagonal pair therefore uses both stored
-// operands unscaled.  The bound on the row factor is why the KDA path asks for
-// ln(alpha) >= -5 per token and channel.
+// at 16-token sub-block boundaries (G_R = g just before sub-block R, Z_R =
+// e^{G_{R+1} - G_R} the sub-block's decay, per channel).  The column operand
+// carries e^{G_{J+1} - g_j} (<= 1).  For the row operand each sub-block R
+// takes one of two splits:
+//  * while Z_R >= 1e-30 in every channel (summed ln(alpha) >= -69): the
+//    split at the sub-block's end, row factor e^{g_r - G_{R+1}} (>= 1, at
+//    most 1e30), pair scale e^{G_{R+1} - G_{J+1}} = prod_{J<m<=R} Z_m (<= 1)
+//    below the diagonal and none on it, so a diagonal pair multiplies the
+//    stored operands as they are;
+//  * otherwise ("flagged"): the split at its start, row factor e^{g_r - G_R}
+//    (<= 1) and pair scale prod_{J<m<R} Z_m (<= 1), so no factor exceeds 1
+//    whatever the decay; the diagonal blocks of A and P are then summed
+//    directly, channel by channel with running products of alpha (exponents
+//    never above 0), reduced across the wave and added into LDS.
 #include "kda_device.h"
 #include "kda_internal.h"
 
@@ -90,7 +98,18 @@ struct IntraCfg {
     // 1/|q_r| and 1/|k_r| of each token (KDA_IN_NORM_QK)
     static constexpr int O_QN = O_BETA + C * 4;
     static constexpr int O_KN = O_QN + C * 4;
-    static constexpr int LDS_BYTES = O_KN + C * 4;
+    // KDA: one flag per wave (its sub-block's decay leaves the range of the
+    // split), and the diagonal blocks of P summed directly for such
+    // sub-blocks: with four sub-blocks they sit in blocks of the A tile above
+    // its diagonal (free until T2 writes T^T there), with two in an area of
+    // their own
+    static constexpr int O_FLAG = O_KN + C * 4;
+    static constexpr bool PD_IN_A = NB == 4;
+    static constexpr int O_PD = O_FLAG + (KDA ? 64 : 0);
+    static constexpr int LDS_BYTES = O_PD + (KDA && !PD_IN_A ? NB * 256 * 4 : 0);
+    // a sub-block takes the direct path when some channel's summed ln(alpha)
+    // is below this (e^-69 ~ 1e-30, so 1 / Z_R stays below ~1e30)
+    static constexpr float UNSAFE_LOG = -69.0f;
 
     static_assert(DK % 32 == 0 && DV % 16 == 0 && (C == 32 || C == 64), "tile shape");
     static_assert(!KDA || NB * DK <= NT, "one thread per (channel, sub-block)");
@@ -124,6 +143,19 @@ kda_intra_kernel(IntraParams prm) {
     float* sBeta = (float*)(smem + Cfg::O_BETA);
     float* sQn = (float*)(smem + Cfg::O_QN);
     float* sKn = (float*)(smem + Cfg::O_KN);
+    int* sFlag = (int*)(smem + Cfg::O_FLAG);
+    float* sPd = (float*)(smem + Cfg::O_PD);
+    // diagonal block R of P (direct sums) as 16 x 16 floats, pitch pd_ld
+    constexpr int pd_ld = Cfg::PD_IN_A ? PA : 16;
+    auto pd_block = [&](int R) -> float* {
+        if constexpr (Cfg::PD_IN_A) {
+            // blocks (0,1), (1,2), (2,3), (0,2) of the A tile (row, column)
+            const int rb = R < 3 ? R : 0, cb = R < 3 ? R + 1 : 2;
+            return sA + (16 * rb) * PA + 16 * cb;
+        } else {
+            return sPd + R * 256;
+        }
+    };
     const bool norm_qk = (prm.flags & KDA_IN_NORM_QK) != 0;
     const bool gate_raw = (prm.flags & KDA_IN_GATE_RAW) != 0;
     const bool beta_logit = (prm.flags & KDA_IN_BETA_LOGIT) != 0;
@@ -252,6 +284,7 @@ kda_intra_kernel(IntraParams prm) {
             }
         }
         float a[16];
+        float lsum = 0.f;
         if (kact) {
 #pragma unroll
             for (int s = 0; s < 16; ++s) {
@@ -259,7 +292,22 @@ kda_intra_kernel(IntraParams prm) {
                 float la = bits_f32(la_bits[s], GBF);
                 if (gate_raw) la = log_alpha_of_raw(la);
                 a[s] = r < n ? la : 0.f;
+                lsum += a[s];
             }
+        }
+        // a wave holds 64 channels of one sub-block: flag it when some
+        // channel's decay over the sub-block leaves the split's range
+        {
+            const bool unsafe = kact && lsum < Cfg::UNSAFE_LOG;
+            const uint64_t m = __ballot(unsafe);
+            if (l == 0) sFlag[w] = m != 0;
+        }
+        // the diagonal blocks of A (in sA) and of P (sPd) start at zero for
+        // the direct sums; the MFMA path overwrites sA's blocks otherwise
+        for (int i = tid; i < NB * 256; i += NT) {
+            const int R = i >> 8, e = i & 255;
+            sA[(16 * R + (e >> 4)) * PA + 16 * R + (e & 15)] = 0.f;
+            pd_block(R)[(e >> 4) * pd_ld + (e & 15)] = 0.f;
         }
         __syncthreads();
         if (kact) {
@@ -290,8 +338,12 @@ kda_intra_kernel(IntraParams prm) {
                 ky[s] = kv[s] * yrun;
                 yrun *= a[s];
             }
-            // x'_s = x_s / Z_R = e^{g_s - G_{R+1}} (>= 1)
-            const float rz = 1.f / x[15];
+            bool flagged = false;
+#pragma unroll
+            for (int u = 0; u < DK / 64; ++u) flagged |= sFlag[R * (DK / 64) + u] != 0;
+            // row factor: e^{g_s - G_{R+1}} = x_s / Z_R (<= 1e30), or for a
+            // flagged sub-block x_s = e^{g_s - G_R} (<= 1)
+            const float rz = flagged ? 1.f : 1.f / x[15];
 #pragma unroll
             for (int s = 0; s < 16; ++s) {
                 const int r = 16 * R + s;
@@ -377,13 +429,64 @@ kda_intra_kernel(IntraParams prm) {
                     *(floatx4*)(rKt + frag_elem<E>(kc, j0, C)) = v;
                 }
             }
+            // direct sums of the diagonal blocks of a flagged sub-block:
+            // entry (r, j), j <= r, takes q_r k_j prod_{j<t<=r} alpha_t (and
+            // k_r k_j ... for A, beta applied later) from every channel; the
+            // wave's 64 channels are reduced and lane 0 adds them to LDS.
+            // The thread's 16 tokens are read again (they are in L2), so the
+            // registers of the common path are not held for this one.
+            bool flagged = false;
+#pragma unroll
+            for (int u = 0; u < DK / 64; ++u) flagged |= sFlag[R * (DK / 64) + u] != 0;
+            if (flagged) {
+                float qd[16], kd[16], ad[16];
+#pragma unroll
+                for (int s = 0; s < 16; ++s) {
+                    const int r = 16 * R + s;
+                    const int rr = r < n ? r : n - 1;
+                    const uint32_t el = rr * DK + kc;
+                    float qv = ESZ == 2 ? bits_f32(ldg<uint16_t>(gq, el * 2), true)
+                                        : bits_f32(ldg<uint32_t>(gq, el * 4), false);
+                    float kv = ESZ == 2 ? bits_f32(ldg<uint16_t>(gk, el * 2), true)
+                                        : bits_f32(ldg<uint32_t>(gk, el * 4), false);
+                    float la = bits_f32(GBF ? (uint32_t)ldg<uint16_t>(gla, el * 2) : ldg<uint32_t>(gla, el * 4), GBF);
+                    if (norm_qk) {
+                        qv *= sQn[r];
+                        kv *= sKn[r];
+                    }
+                    if (gate_raw) la = log_alpha_of_raw(la);
+                    qd[s] = r < n ? qv : 0.f;
+                    kd[s] = r < n ? kv : 0.f;
+                    ad[s] = exp_neg(r < n ? la : 0.f);
+                }
+                float* pdb = pd_block(R);
+#pragma unroll
+                for (int jj = 0; jj < 16; ++jj) {
+                    float f = 1.f;
+#pragma unroll
+                    for (int rr = jj; rr < 16; ++rr) {
+                        if (rr > jj) f *= ad[rr];
+                        const float tk = group_sum<64>(kd[rr] * kd[jj] * f);
+                        const float tq = group_sum<64>(qd[rr] * kd[jj] * f);
+                        if (l == 0) {
+                            atomicAdd(sA + (16 * R + rr) * PA + 16 * R + jj, tk);
+                            atomicAdd(pdb + rr * pd_ld + jj, tq);
+                        }
+                    }
+                }
+            }
             if (R == 0) {
-                // block-end factors E'_R = e^{G_{R+1}}, and e^{g_n}
+                // E_b turns sub-block b's row operand into k e^{g}: e^{G_{b+1}}
+                // (e^{G_b} for a flagged sub-block); and e^{g_n}
                 float run = 1.f;
 #pragma unroll
                 for (int b = 0; b < NB; ++b) {
+                    bool fb = false;
+#pragma unroll
+                    for (int u = 0; u < DK / 64; ++u) fb |= sFlag[b * (DK / 64) + u] != 0;
+                    if (fb) sE[b * DK + kc] = run;
                     run *= Zb[b];
-                    sE[b * DK + kc] = run;
+                    if (!fb) sE[b * DK + kc] = run;
                 }
                 rGam[kc] = run;
             }
@@ -399,36 +502,49 @@ kda_intra_kernel(IntraParams prm) {
         const E* pa = (KDA ? sKc : sKr) + (16 * J + lr) * PK + W * lq;
         const E* pk = sKr + (16 * R + lr) * PK + W * lq;
         const E* pq = sQr + (16 * R + lr) * PK + W * lq;
-        typename F::T fa[NKS], fk[NKS], fq[THIN ? 1 : NKS];
-        if (!KDA || J == R) {
-#pragma unroll
-            for (int i = 0; i < NKS; ++i) fa[i] = F::load(pa + KS * i);
-        } else {
-            // pair scale Y'_RJ = e^{G_{R+1} - G_{J+1}} = prod_{J < m <= R} Z_m, per channel
-#pragma unroll
-            for (int i = 0; i < NKS; ++i) {
-                const float* pz = sZ + KS * i + W * lq;
-                floatx4 y0 = {1.f, 1.f, 1.f, 1.f}, y1 = {1.f, 1.f, 1.f, 1.f};
-                for (int m = J + 1; m <= R; ++m) {
-                    y0 *= *(const floatx4*)(pz + m * DK);
-                    if constexpr (W == 8) y1 *= *(const floatx4*)(pz + m * DK + 4);
-                }
-                fa[i] = F::load_scaled_v(pa + KS * i, y0, y1);
-            }
-        }
-#pragma unroll
-        for (int i = 0; i < NKS; ++i) {
-            fk[i] = F::load(pk + KS * i);
-            if constexpr (!THIN) fq[i] = F::load(pq + KS * i);
-        }
-        floatx4 accA = {0.f, 0.f, 0.f, 0.f}, accP = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int i = 0; i < NKS; ++i) {
-            accA = F::mma(accA, fa[i], fk[i]);
-            if constexpr (!THIN) accP = F::mma(accP, fa[i], fq[i]);
-        }
         // lane holds [m = j = 16J + 4lq + e][n = r = 16R + lr]
         const int rr = 16 * R + lr;
+        floatx4 accA = {0.f, 0.f, 0.f, 0.f}, accP = {0.f, 0.f, 0.f, 0.f};
+        bool flagR = false;  // sub-block R takes the split at its start
+        if constexpr (KDA) {
+#pragma unroll
+            for (int u = 0; u < DK / 64; ++u) flagR |= sFlag[R * (DK / 64) + u] != 0;
+        }
+        if (flagR && J == R) {
+            // summed channel by channel in phase G (A without beta)
+            accA = *(const floatx4*)(sA + rr * PA + 16 * J + 4 * lq);
+            accP = *(const floatx4*)(pd_block(R) + lr * pd_ld + 4 * lq);
+        } else {
+            typename F::T fa[NKS], fk[NKS], fq[THIN ? 1 : NKS];
+            if (!KDA || J == R) {
+#pragma unroll
+                for (int i = 0; i < NKS; ++i) fa[i] = F::load(pa + KS * i);
+            } else {
+                // pair scale per channel: prod_{J < m <= R} Z_m, or up to
+                // m < R for a flagged sub-block R
+                const int mend = flagR ? R : R + 1;
+#pragma unroll
+                for (int i = 0; i < NKS; ++i) {
+                    const float* pz = sZ + KS * i + W * lq;
+                    floatx4 y0 = {1.f, 1.f, 1.f, 1.f}, y1 = {1.f, 1.f, 1.f, 1.f};
+                    for (int m = J + 1; m < mend; ++m) {
+                        y0 *= *(const floatx4*)(pz + m * DK);
+                        if constexpr (W == 8) y1 *= *(const floatx4*)(pz + m * DK + 4);
+                    }
+                    fa[i] = F::load_scaled_v(pa + KS * i, y0, y1);
+                }
+            }
+#pragma unroll
+            for (int i = 0; i < NKS; ++i) {
+                fk[i] = F::load(pk + KS * i);
+                if constexpr (!THIN) fq[i] = F::load(pq + KS * i);
+            }
+#pragma unroll
+            for (int i = 0; i < NKS; ++i) {
+                accA = F::mma(accA, fa[i], fk[i]);
+                if constexpr (!THIN) accP = F::mma(accP, fa[i], fq[i]);
+            }
+        }
         const float br = sBeta[rr];
         float gr = 0.f;
         floatx4 gj = {0.f, 0.f, 0.f, 0.f};
@@ -508,7 +624,7 @@ kda_intra_kernel(IntraParams prm) {
     } else if constexpr (KDA) {
         // the other waves: zero the blocks of T diag(beta) above the diagonal
         // (its tile reuses the column operand's space), K~ = k e^{g} in place
-        // (row operand x E'_R) for W, and Q~ = q e^{g} straight to the record
+        // (row operand x E_R) for W, and Q~ = q e^{g} straight to the record
         // (A operand of Q~ S)
         // (both loops have trip counts known here, so they are unrolled and
         // each thread's LDS reads go out together; the zeros go out as

@@ -240,21 +240,54 @@ def test_deterministic():
         assert torch.equal(o, ref[0]) and torch.equal(Sf, ref[1])
 
 
-def test_strong_decay_documented_range():
-    """ln(alpha) down to -5 per token and channel stays within tolerance."""
-    w = gen.custom(B=1, H=4, L=200, dk=128, dv=128, qkv_dtype="bf16", gate_dtype="f32",
-                   alpha_mode="channel", seed=31, la_mu=1.2, la_sigma=0.3)
-    x = gen.prefill_inputs(w)
-    x["log_alpha"] = np.maximum(x["log_alpha"], -5.0).astype(np.float32)
+def _strong_decay_case(w, x, label):
     import torch
     kda = _kda()
+    N = w.B * w.H
     d = device_inputs(w, x)
-    say("strong decay")
+    say(f"{label}: B={w.B} H={w.H} L={w.L} dk={w.dk} dv={w.dv} {w.qkv_dtype}/{w.gate_dtype} "
+        f"ln(alpha) in [{float(np.min(gen.widen(x['log_alpha'], w.gate_dtype))):.1f}, "
+        f"{float(np.max(gen.widen(x['log_alpha'], w.gate_dtype))):.3f}]")
     o, Sf = kda.chunk_fwd(d["q"], d["k"], d["v"], d["log_alpha"], d["beta"], d["S0"])
     torch.cuda.synchronize()
-    o_ref, S_ref = oracle_prefill(w, flat_heads(x, 4))
-    assert oracle.slab_error(to_f64(o).reshape(4, 200, 128), o_ref, 1) <= TOL["bf16"]
-    assert oracle.slab_error(to_f64(Sf).reshape(4, 128, 128), S_ref, 1) <= TOL["bf16"]
+    o_ref, S_ref = oracle_prefill(w, flat_heads(x, N))
+    tol = TOL[w.qkv_dtype]
+    e_o = oracle.slab_error(to_f64(o).reshape(N, w.L, w.dv), o_ref, 1)
+    e_s = oracle.slab_error(to_f64(Sf).reshape(N, w.dk, w.dv), S_ref, 1)
+    say(f"{label}: err o={e_o:.3e} S={e_s:.3e}")
+    assert e_o <= tol and e_s <= tol, (e_o, e_s)
+
+
+# ln(alpha) = -exp(N(mu, sigma)): mu = 1.2 reaches about -5, mu = 3.0 about
+# -20 (every 16-token sub-block leaves the split's range), mu = 1.5 with
+# sigma = 1 mixes weak and very strong channels within one sub-block
+@pytest.mark.parametrize("mu,sigma", [(1.2, 0.3), (3.0, 0.3), (1.5, 1.0)])
+@pytest.mark.parametrize("qd,gd,dk", [("bf16", "f32", 128), ("bf16", "bf16", 64),
+                                      ("f32", "f32", 128)])
+def test_strong_decay(mu, sigma, qd, gd, dk):
+    """Per-channel decay of any strength meets the bar: nothing in the
+    factored decay may overflow (the oracle has no limit either)."""
+    w = gen.custom(B=1, H=4, L=200, dk=dk, dv=128, qkv_dtype=qd, gate_dtype=gd,
+                   alpha_mode="channel", seed=31 + int(10 * mu) + dk, la_mu=mu, la_sigma=sigma)
+    _strong_decay_case(w, gen.prefill_inputs(w), f"strong decay mu={mu} sigma={sigma}")
+
+
+def test_decay_wipes_and_mixed_sub_blocks():
+    """Single tokens that wipe a channel (ln(alpha) = -1000) inside otherwise
+    weakly decaying sub-blocks, and sub-blocks where only one channel leaves
+    the split's range."""
+    w = gen.custom(B=1, H=3, L=300, dk=128, dv=128, qkv_dtype="bf16", gate_dtype="f32",
+                   alpha_mode="channel", seed=77)
+    x = gen.prefill_inputs(w)
+    la = x["log_alpha"].copy()
+    rng = np.random.default_rng(5)
+    t = rng.integers(0, w.L, size=40)
+    c = rng.integers(0, w.dk, size=40)
+    la[0, 0, t, c] = -1000.0                      # wipes on head 0
+    la[0, 1, 64:80, 7] = -12.0                    # one channel of one sub-block on head 1
+    la[0, 2, :, :5] = -30.0                       # five channels everywhere on head 2
+    x["log_alpha"] = la.astype(np.float32)
+    _strong_decay_case(w, x, "wipes and mixed sub-blocks")
 
 
 def test_head_gate_equals_broadcast_channel_gate():

@@ -235,3 +235,13 @@ def test_decode_slots_raw(mode):
     assert oracle.slab_error(to_f64(o[live]).reshape(N, 1, 128), o_or, 1) <= TOL["bf16"]
     S_new = torch.stack([pool[slots_h[b]] for b in live]).reshape(N, 128, 128)
     assert oracle.slab_error(to_f64(S_new), S_or, 1) <= TOL["bf16"]
+
+
+@pytest.mark.parametrize("gd,dk", [("f32", 128), ("bf16", 64)])
+def test_prefill_raw_gate_strong(gd, dk):
+    """Raw gates g up to about 4.5 give ln(alpha) = -exp(g) down to about -90:
+    every sub-block's decay leaves the range of the kernel's factored split
+    and takes its direct path."""
+    w = gen.custom(B=1, H=3, L=150, dk=dk, dv=128, qkv_dtype="bf16", gate_dtype=gd,
+                   alpha_mode="channel", seed=91 + dk, la_mu=3.0, la_sigma=0.6)
+    run_prefill(w, oracle.GATE_RAW | oracle.NORM_QK | oracle.BETA_LOGIT, "raw strong gate")
