@@ -79,7 +79,9 @@ enum kda_status {
     KDA_ERR_ALIAS = 7,      /* an output overlaps an input, or S_final only
                                partly overlaps S0                             */
     KDA_ERR_HIP = 8,        /* a HIP launch failed; kda_last_error() has text */
-    KDA_ERR_FLAGS = 9       /* an unknown kda_input_flags bit                 */
+    KDA_ERR_FLAGS = 9,      /* an unknown kda_input_flags bit                 */
+    KDA_ERR_SCRATCH = 10    /* kda_chunk_fwd_noalloc: the problem needs more
+                               work memory than its static buffer holds       */
 };
 
 /*
@@ -144,6 +146,33 @@ int kda_chunk_fwd_ex(const kda_shape* shape, uint32_t flags, const void* q, cons
 /* Bytes of device workspace kda_chunk_fwd needs for this shape (0 for a
  * shape the call would reject). */
 size_t kda_chunk_fwd_workspace_bytes(const kda_shape* shape);
+
+/*
+ * kda_chunk_fwd_ex without a workspace argument and without any device
+ * allocation, for callers that cannot allocate: code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc.  The work
+ * memory (the per-chunk records of one span of chunks, and with several spans
+ * and no S_final the state carried between them) is a static device buffer of
+ * KDA_NOALLOC_SCRATCH_BYTES inside the library: one per GPU, at its own
+ * address, held until the process ends.  The span plan is shortened so that
+ * it fits (results equal kda_chunk_fwd_ex's bit for bit).  The buffer of the
+ * calling thread's current device is used, so hip_stream must belong to that
+ * device.
+ *   Arguments, layouts and checks: as kda_chunk_fwd_ex, without workspace.
+ *   Errors: as kda_chunk_fwd_ex, plus KDA_ERR_SCRATCH when one chunk of every
+ *   head (and the state area) does not fit in the buffer (e.g. more than 896
+ *   heads with per-channel decay at dk = dv = 128 in bf16); that check runs
+ *   on the host before any HIP call.  KDA_ERR_HIP if the buffer's device
+ *   address cannot be looked up.
+ *   Concurrency: every call on a GPU shares that GPU's buffer, which keeps the
+ *   last call's contents (nothing in it needs to start at zero).  Calls that
+ *   overlap in time on one GPU (other streams, other host threads) race on
+ *   it; serialize them.  No event is recorded even with kda_timing_enable.
+ */
+#define KDA_NOALLOC_SCRATCH_BYTES (64ll << 20)
+int kda_chunk_fwd_noalloc(const kda_shape* shape, uint32_t flags, const void* q, const void* k,
+                          const void* v, const void* log_alpha, const void* beta,
+                          const float* S0, void* o, float* S_final, void* hip_stream);
 
 /*
  * One decode step for every (b, h): the recurrence above for a single token,

@@ -4,6 +4,7 @@ The compute path is libkda.so (hand-written HIP for gfx950, C ABI in
 ``include/kda.h``); this package only marshals arguments to it:
 
     o, S_final = chunk_fwd(q, k, v, log_alpha, beta, S0)
+    o, S_final = chunk_fwd_noalloc(q, k, v, log_alpha, beta, S0)   # no device allocation
     o, S_final = chunk_fwd_varlen(q, k, v, log_alpha, beta, cu_seqlens, max_seqlen, S0)
     o, S_final, z_final = linear_attn_fwd(q, k, v, S0, z0)     # phi = elu + 1
     o          = linear_attn_decode_step(q, k, v, S, z)        # S, z updated in place
@@ -18,10 +19,10 @@ q, k, beta logits and gate pre-activations that the kernels preprocess.
 """
 
 from .binding import (BETA_LOGIT, GATE_RAW, NORM_QK, KdaError, chunk_fwd,  # noqa: F401
-                      chunk_fwd_varlen, chunk_fwd_workspace_bytes, decode_step, linear_attn_decode_step,
+                      chunk_fwd_noalloc, chunk_fwd_varlen, chunk_fwd_workspace_bytes, decode_step, linear_attn_decode_step,
                       linear_attn_fwd, decode_step_slots, library, recurrence_bwd,
                       recurrence_bwd_workspace_bytes, timing_enable, timing_read, timing_reset)
 
-__all__ = ["chunk_fwd", "chunk_fwd_varlen", "linear_attn_fwd", "linear_attn_decode_step",
+__all__ = ["chunk_fwd", "chunk_fwd_noalloc", "chunk_fwd_varlen", "linear_attn_fwd", "linear_attn_decode_step",
            "chunk_fwd_workspace_bytes", "decode_step", "decode_step_slots", "library", "KdaError", "timing_enable", "timing_read", "timing_reset", "NORM_QK",
            "BETA_LOGIT", "GATE_RAW", "recurrence_bwd", "recurrence_bwd_workspace_bytes"]

@@ -21,7 +21,7 @@ KDA_F32, KDA_BF16 = 0, 1
 KDA_ALPHA_NONE, KDA_ALPHA_HEAD, KDA_ALPHA_CHANNEL = 0, 1, 2
 STATUS = {0: "KDA_OK", 1: "KDA_ERR_NULL", 2: "KDA_ERR_SHAPE", 3: "KDA_ERR_DTYPE",
           4: "KDA_ERR_ALPHA_MODE", 5: "KDA_ERR_ALIGN", 6: "KDA_ERR_WORKSPACE",
-          7: "KDA_ERR_ALIAS", 8: "KDA_ERR_HIP", 9: "KDA_ERR_FLAGS"}
+          7: "KDA_ERR_ALIAS", 8: "KDA_ERR_HIP", 9: "KDA_ERR_FLAGS", 10: "KDA_ERR_SCRATCH"}
 # kda_input_flags: preprocessing applied by the kernels as they load raw inputs
 NORM_QK, BETA_LOGIT, GATE_RAW = 1, 2, 4
 
@@ -77,6 +77,8 @@ def library() -> ctypes.CDLL:
         lib.kda_chunk_fwd_varlen_workspace_bytes.restype = sz
         lib.kda_chunk_fwd_ex.argtypes = [sp, u32, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
         lib.kda_chunk_fwd_ex.restype = ctypes.c_int
+        lib.kda_chunk_fwd_noalloc.argtypes = [sp, u32, vp, vp, vp, vp, vp, vp, vp, vp, vp]
+        lib.kda_chunk_fwd_noalloc.restype = ctypes.c_int
         lib.kda_decode_step_ex.argtypes = [sp, u32, vp, vp, vp, vp, vp, vp, vp, vp]
         lib.kda_decode_step_ex.restype = ctypes.c_int
         lib.kda_decode_step_slots_ex.argtypes = [sp, u32, vp, vp, vp, vp, vp, vp, ctypes.c_int64,
@@ -241,6 +243,34 @@ def chunk_fwd(q, k, v, log_alpha, beta, S0=None, *, output_final_state: bool = T
         rc = lib.kda_chunk_fwd(ctypes.byref(shape), *args)
     else:
         rc = lib.kda_chunk_fwd_ex(ctypes.byref(shape), flags, *args)
+    _check(rc)
+    return o, (S_final if output_final_state else None)
+
+
+def chunk_fwd_noalloc(q, k, v, log_alpha, beta, S0=None, *, output_final_state: bool = True,
+                      o=None, S_final=None, flags: int = 0) -> Tuple[object, Optional[object]]:
+    """Chunkwise prefill through kda_chunk_fwd_noalloc: the library keeps its
+    work memory in a static device buffer, so the call itself allocates
+    nothing on the device (pass ``o`` and, if wanted, ``S_final`` to avoid
+    the two output allocations made here otherwise).  Arguments and results
+    as chunk_fwd with ``flags`` (0 = preprocessed inputs)."""
+    torch = _torch()
+    B, H, L, dk = q.shape
+    dv = v.shape[-1]
+    for name, t in (("q", q), ("k", k), ("v", v), ("beta", beta), ("log_alpha", log_alpha),
+                    ("S0", S0)):
+        if t is not None:
+            _require(t, name)
+    if o is None:
+        o = torch.empty((B, H, L, dv), dtype=v.dtype, device=v.device)
+    if output_final_state and S_final is None:
+        S_final = torch.empty((B, H, dk, dv), dtype=torch.float32, device=v.device)
+    if S0 is not None and S0.dtype != torch.float32:
+        raise TypeError("S0 must be float32")
+    shape = _chunk_shape(q, v, log_alpha, beta)
+    rc = library().kda_chunk_fwd_noalloc(
+        ctypes.byref(shape), flags, _ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(beta),
+        _ptr(S0), _ptr(o), _ptr(S_final) if output_final_state else None, _stream(v))
     _check(rc)
     return o, (S_final if output_final_state else None)
 

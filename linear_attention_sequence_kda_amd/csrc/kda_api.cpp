@@ -133,9 +133,16 @@ struct Plan {
     int64_t nchunks = 0, span = 0, nspans = 0;
     int64_t rec_bytes = 0, rec_area = 0, state_area = 0;
     int64_t ws_bytes = 0;
+    bool fits = true;  // false: no plan fits the byte cap make_plan was given
 };
 
-Plan make_plan(const kda_shape* s) {
+// The plan above, shortened so that its workspace fits in cap bytes when cap
+// >= 0 (kda_chunk_fwd_noalloc's static buffer): one span of every chunk if
+// the records alone fit, else the longest spans that fit beside the state
+// area; fits = false when not even one chunk per span does.
+Plan make_plan(const kda_shape* s, int64_t cap = -1);
+
+Plan make_plan_uncapped(const kda_shape* s) {
     Plan p;
     const int bf = s->qkv_dtype == KDA_BF16;
     const int64_t bh = s->B * s->H;
@@ -169,6 +176,27 @@ Plan make_plan(const kda_shape* s) {
     p.nspans = (p.nchunks + p.span - 1) / p.span;
     p.rec_area = p.span * per_chunk;
     p.state_area = p.nspans > 1 ? bh * s->dk * s->dv * 4 : 0;
+    p.ws_bytes = p.rec_area + p.state_area;
+    return p;
+}
+
+Plan make_plan(const kda_shape* s, int64_t cap) {
+    Plan p = make_plan_uncapped(s);
+    if (cap < 0 || p.ws_bytes <= cap) return p;
+    const int64_t per_chunk = s->B * s->H * p.rec_bytes;
+    if (p.nchunks * per_chunk <= cap) {
+        p.span = p.nchunks;
+    } else {
+        const int64_t st = s->B * s->H * s->dk * s->dv * 4;
+        p.span = cap > st ? (cap - st) / per_chunk : 0;
+        if (p.span < 1) {
+            p.fits = false;
+            return p;
+        }
+    }
+    p.nspans = (p.nchunks + p.span - 1) / p.span;
+    p.rec_area = p.span * per_chunk;
+    p.state_area = p.nspans > 1 ? s->B * s->H * s->dk * s->dv * 4 : 0;
     p.ws_bytes = p.rec_area + p.state_area;
     return p;
 }
@@ -255,6 +283,7 @@ const char* kda_strerror(int status) {
         case KDA_ERR_ALIAS: return "an output buffer overlaps an input (or S_final partly overlaps S0)";
         case KDA_ERR_HIP: return "HIP launch failed";
         case KDA_ERR_FLAGS: return "unknown kda_input_flags bit";
+        case KDA_ERR_SCRATCH: return "the problem needs more work memory than kda_chunk_fwd_noalloc's static buffer (KDA_NOALLOC_SCRATCH_BYTES) holds";
         default: return "unknown kda status";
     }
 }
@@ -280,10 +309,14 @@ namespace {
 // Shared body of kda_chunk_fwd_ex (cu == nullptr: dense [B,H,L,*] tensors) and
 // kda_chunk_fwd_varlen (B packed sequences in [H, L = T, *] tensors, token
 // offsets cu on the device, the longest sequence max_len tokens).
+// noalloc: kda_chunk_fwd_noalloc -- the plan is capped to the static buffer,
+// whose address replaces workspace once every host check has passed, and no
+// timing event is created.
 int chunk_common(const char* who, const kda_shape* s, uint32_t flags, const int32_t* cu,
                  int64_t max_len, const void* q, const void* k, const void* v,
                  const void* log_alpha, const void* beta, const float* S0, void* o,
-                 float* S_final, void* workspace, size_t workspace_bytes, void* hip_stream) {
+                 float* S_final, void* workspace, size_t workspace_bytes, void* hip_stream,
+                 bool noalloc = false) {
     int rc = check_shape(s, false);
     if (rc != KDA_OK) return rc;
     if (flags & ~kAllFlags) return KDA_ERR_FLAGS;
@@ -308,8 +341,9 @@ int chunk_common(const char* who, const kda_shape* s, uint32_t flags, const int3
     for (const void* p : ptrs)
         if (p && !aligned16(p)) return KDA_ERR_ALIGN;
     if (cu && ((uintptr_t)cu & 3u)) return KDA_ERR_ALIGN;
-    const Plan plan = make_plan(&ps);
-    if (plan.ws_bytes > 0 && (!workspace || workspace_bytes < (size_t)plan.ws_bytes))
+    const Plan plan = make_plan(&ps, noalloc ? (int64_t)KDA_NOALLOC_SCRATCH_BYTES : -1);
+    if (!plan.fits) return KDA_ERR_SCRATCH;
+    if (!noalloc && plan.ws_bytes > 0 && (!workspace || workspace_bytes < (size_t)plan.ws_bytes))
         return KDA_ERR_WORKSPACE;
 
     const int64_t la_elems = s->alpha_mode == KDA_ALPHA_CHANNEL ? tok * s->dk : tok;
@@ -324,7 +358,7 @@ int chunk_common(const char* who, const kda_shape* s, uint32_t flags, const int3
         if (overlaps(so, in) || overlaps(sf, in)) return KDA_ERR_ALIAS;
     if (overlaps(so, s0) || overlaps(so, sf)) return KDA_ERR_ALIAS;
     if (overlaps(sf, s0) && (const void*)S_final != (const void*)S0) return KDA_ERR_ALIAS;
-    const Span sw = span_of(workspace, plan.ws_bytes);
+    const Span sw = span_of(noalloc ? nullptr : workspace, plan.ws_bytes);
     const Span all[] = {sq, sk, sv, sla, sb, s0, so, sf, sc};
     for (const Span& x : all)
         if (overlaps(sw, x)) return KDA_ERR_ALIAS;
@@ -332,6 +366,17 @@ int chunk_common(const char* who, const kda_shape* s, uint32_t flags, const int3
     if (bh == 0) return KDA_OK;
     const int qbf = s->qkv_dtype == KDA_BF16;
     const hipStream_t stream = (hipStream_t)hip_stream;
+    if (noalloc) {
+        hipError_t e = kda::scratch_address(&workspace);
+        if (e != hipSuccess) {
+            g_last_error = std::string(who) + ": " + hipGetErrorString(e);
+            return KDA_ERR_HIP;
+        }
+    }
+    // the allocation-free call records no timing events
+    auto launch = [&](int kernel, auto&& fn) -> hipError_t {
+        return noalloc ? fn() : timed_launch(kernel, stream, fn);
+    };
     const int nv = kda::chunk_slice_width((int)s->dk, (int)s->dv, qbf, bh);
     float* s_mid = S_final ? S_final : (float*)((char*)workspace + plan.rec_area);
 
@@ -365,10 +410,10 @@ int chunk_common(const char* who, const kda_shape* s, uint32_t flags, const int3
     // one decay per token: records hold T diag(beta) and the decay scalars
     auto launch_state = [&](const kda::InterParams& x) {
         return s->alpha_mode == KDA_ALPHA_CHANNEL
-                   ? timed_launch(K_INTER, stream, [&] {
+                   ? launch(K_INTER, [&] {
                          return kda::launch_inter(x, (int)s->dk, qbf, s->alpha_mode, nv, stream);
                      })
-                   : timed_launch(K_INTER_SCALAR, stream, [&] {
+                   : launch(K_INTER_SCALAR, [&] {
                          return kda::launch_inter_scalar(x, (int)s->dk, qbf, nv, stream);
                      });
     };
@@ -386,7 +431,7 @@ int chunk_common(const char* who, const kda_shape* s, uint32_t flags, const int3
         const int64_t ncs = plan.nchunks - c0 < plan.span ? plan.nchunks - c0 : plan.span;
         ip.c0 = c0;
         ip.ncs = (int)ncs;
-        err = timed_launch(K_INTRA, stream, [&] {
+        err = launch(K_INTRA, [&] {
             return kda::launch_intra(ip, (int)s->dk, (int)s->dv, qbf, s->alpha_mode, stream);
         });
         if (err != hipSuccess) break;
@@ -412,6 +457,13 @@ int kda_chunk_fwd_ex(const kda_shape* s, uint32_t flags, const void* q, const vo
                      void* hip_stream) {
     return chunk_common("kda_chunk_fwd", s, flags, nullptr, -1, q, k, v, log_alpha, beta, S0, o,
                         S_final, workspace, workspace_bytes, hip_stream);
+}
+
+int kda_chunk_fwd_noalloc(const kda_shape* s, uint32_t flags, const void* q, const void* k,
+                          const void* v, const void* log_alpha, const void* beta,
+                          const float* S0, void* o, float* S_final, void* hip_stream) {
+    return chunk_common("kda_chunk_fwd_noalloc", s, flags, nullptr, -1, q, k, v, log_alpha, beta,
+                        S0, o, S_final, nullptr, 0, hip_stream, true);
 }
 
 size_t kda_chunk_fwd_varlen_workspace_bytes(const kda_shape* shape, int64_t max_seqlen) {

@@ -135,6 +135,10 @@ struct InterParams {
     float* z_out = nullptr;
 };
 
+// Device address of the calling thread's current device's static buffer of
+// kda_chunk_fwd_noalloc (KDA_NOALLOC_SCRATCH_BYTES), looked up once per device.
+hipError_t scratch_address(void** out);
+
 hipError_t launch_intra(const IntraParams& prm, int dk, int dv, int qkv_bf16, int alpha_mode,
                         hipStream_t stream);
 hipError_t launch_inter(InterParams prm, int dk, int qkv_bf16, int alpha_mode, int nv,

@@ -31,7 +31,7 @@ def test_exports_every_declared_function(lib):
 
 def test_version_and_strings(lib):
     assert lib.kda_abi_version() == 1
-    for code in range(10):
+    for code in range(11):
         assert lib.kda_strerror(code)
     assert lib.kda_strerror(0) == b"ok"
     assert lib.kda_last_error() == b""
@@ -430,3 +430,41 @@ def test_recurrence_bwd_ex_row_limit(lib):
     assert lib.kda_recurrence_bwd_workspace_bytes(ctypes.byref(s)) > 0
     b = {n: BASE + i * (1 << 40) for i, n in enumerate(bwd_bufs())}
     assert bwd_ex(lib, s, 7, b, wsb=1 << 62) == 2
+
+
+def noalloc(lib, s, flags, b):
+    return lib.kda_chunk_fwd_noalloc(ctypes.byref(s) if s is not None else None, flags, b["q"],
+                                     b["k"], b["v"], b["la"], b["beta"], b["S0"], b["o"], b["Sf"],
+                                     None)
+
+
+def test_noalloc_host_checks(lib):
+    """kda_chunk_fwd_noalloc makes kda_chunk_fwd_ex's host checks, and rejects
+    a problem whose one-chunk span does not fit its static buffer, all before
+    any HIP call (no device here)."""
+    s = shape()
+    assert noalloc(lib, None, 0, bufs()) == 1
+    assert noalloc(lib, s, 8, bufs()) == 9                         # unknown flag bit
+    for name in ["q", "k", "v", "la", "beta", "o"]:
+        b = bufs()
+        b[name] = None
+        assert noalloc(lib, s, 0, b) == 1, name
+    for name in ["q", "k", "v", "la", "beta", "S0", "o", "Sf"]:
+        b = bufs()
+        b[name] += 8
+        assert noalloc(lib, s, 0, b) == 5, name
+    b = bufs()
+    b["o"] = b["q"] + 1024
+    assert noalloc(lib, s, 0, b) == 7
+    bad = shape()
+    bad.dk = 96
+    assert noalloc(lib, bad, 0, bufs()) == 2
+    # per-channel decay, d = 128, bf16: 73 KiB of records per (head, chunk),
+    # so 1,024 heads need 75 MB for one chunk each: more than the 64 MiB buffer
+    big = shape(B=8, H=128, L=64)
+    b = {n: BASE + i * (1 << 36) for i, n in enumerate(bufs())}
+    assert noalloc(lib, big, 0, b) == 10                           # KDA_ERR_SCRATCH
+    assert lib.kda_strerror(10).startswith(b"the problem needs more work memory")
+    # the same heads with one decay per head fit (9 KiB records)
+    none = {n: None for n in bufs()}
+    assert noalloc(lib, shape(B=0), 0, none) == 0                  # empty problem

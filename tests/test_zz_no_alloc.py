@@ -1,0 +1,67 @@
+"""kda_chunk_fwd_noalloc (the allocation-free prefill, for callers that
+cannot allocate device memory) against kda_chunk_fwd_ex with a workspace, on
+the GPU through the C ABI: two calls in a row, the second on a smaller input.
+Both entry points run the same kernels; only the span plan differs (the
+static buffer holds fewer chunks per span), and the state crosses spans in
+fp32, so the results must be equal bit for bit, which is stricter than the
+parity bar (2e-2 for bf16 inputs, 1e-4 for fp32) also checked here against
+the oracle.
+"""
+
+import numpy as np
+import pytest
+
+import oracle
+from linear_attention_sequence_kda_amd import inputs as gen
+
+from gpu_util import TOL, device_inputs, flat_heads, oracle_prefill, say, to_f64
+
+pytestmark = pytest.mark.gpu
+
+
+def _compare(w, flags=0, with_final=True, label=""):
+    import torch
+    import linear_attention_sequence_kda_amd as kda
+    x = gen.prefill_inputs(w)
+    d = device_inputs(w, x)
+    args = (d["q"], d["k"], d["v"], d["log_alpha"], d["beta"], d["S0"])
+    say(f"noalloc {label}: B={w.B} H={w.H} L={w.L} dk={w.dk} dv={w.dv} "
+        f"{w.qkv_dtype}/{w.gate_dtype}/{w.alpha_mode} flags={flags} S_final={with_final}")
+    o1, s1 = kda.chunk_fwd(*args, flags=flags, output_final_state=with_final)
+    o2, s2 = kda.chunk_fwd_noalloc(*args, flags=flags, output_final_state=with_final)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2), "o differs from kda_chunk_fwd_ex"
+    if with_final:
+        assert torch.equal(s1, s2), "S_final differs from kda_chunk_fwd_ex"
+    N = w.B * w.H
+    if flags == 0:
+        o_ref, s_ref = oracle_prefill(w, flat_heads(x, N))
+        tol = TOL[w.qkv_dtype]
+        e_o = oracle.slab_error(to_f64(o2).reshape(N, w.L, w.dv), o_ref, 1)
+        say(f"noalloc {label}: err o={e_o:.3e} (tol {tol})")
+        assert e_o <= tol
+        if with_final:
+            assert oracle.slab_error(to_f64(s2).reshape(N, w.dk, w.dv), s_ref, 1) <= tol
+
+
+def test_noalloc_two_calls_second_smaller():
+    # per-channel decay, 64 heads x 2048 tokens: 32 chunks of 4.8 MB of
+    # records, one span with a workspace, three in the 64 MiB static buffer
+    _compare(gen.custom(B=2, H=32, L=2048, dk=128, dv=128, qkv_dtype="bf16",
+                        gate_dtype="bf16", alpha_mode="channel", s0_std=0.02, seed=201),
+             label="first")
+    # then a smaller problem on the same buffer (its old contents left over)
+    _compare(gen.custom(B=1, H=3, L=300, dk=64, dv=128, qkv_dtype="bf16", gate_dtype="f32",
+                        alpha_mode="head", seed=202), label="second, smaller")
+
+
+def test_noalloc_state_between_spans_in_buffer():
+    """No S_final: several spans pass the state through the buffer's state
+    area; then fp32 inputs and raw inputs with every preprocessing flag."""
+    _compare(gen.custom(B=2, H=32, L=2048, dk=128, dv=128, qkv_dtype="bf16",
+                        gate_dtype="bf16", alpha_mode="channel", s0_std=0.02, seed=203),
+             with_final=False, label="no S_final")
+    _compare(gen.custom(B=1, H=8, L=700, dk=128, dv=64, qkv_dtype="f32", gate_dtype="f32",
+                        alpha_mode="channel", seed=204), label="fp32")
+    _compare(gen.custom(B=2, H=4, L=500, dk=128, dv=128, qkv_dtype="bf16", gate_dtype="f32",
+                        alpha_mode="channel", seed=205), flags=7, label="raw inputs")
