@@ -302,7 +302,8 @@ int kda_linear_attn_decode_step(const kda_shape* shape, const void* q, const voi
  *   kda_timing_read(name, &launches, &total_ms)
  *                           waits for the kept launches of the kernel `name`
  *                           ("kda_intra_kernel", "kda_inter_kernel",
- *                           "kda_inter_scalar_kernel", "kda_decode_kernel",
+ *                           "kda_inter_scalar_kernel", "kda_inter_wide_kernel",
+ *                           "kda_decode_kernel",
  *                           "kda_feature_map_kernel" or "kda_bwd_kernel")
  *                           and returns how many there were and their summed
  *                           duration in milliseconds.  KDA_ERR_NULL for a NULL

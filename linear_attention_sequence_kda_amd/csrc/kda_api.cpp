@@ -20,10 +20,12 @@ thread_local std::string g_last_error;
 // ---- kernel timing (kda_timing_*) --------------------------------------------
 // While enabled, each kernel launch is bracketed by two events recorded on the
 // launch's stream; the pairs are kept until read or reset.
-enum KernelId { K_INTRA = 0, K_INTER, K_INTER_SCALAR, K_DECODE, K_FEATURE, K_BWD, K_COUNT };
+enum KernelId { K_INTRA = 0, K_INTER, K_INTER_SCALAR, K_DECODE, K_FEATURE, K_BWD, K_INTER_WIDE,
+                K_COUNT };
 const char* const kKernelNames[K_COUNT] = {"kda_intra_kernel", "kda_inter_kernel",
                                            "kda_inter_scalar_kernel", "kda_decode_kernel",
-                                           "kda_feature_map_kernel", "kda_bwd_kernel"};
+                                           "kda_feature_map_kernel", "kda_bwd_kernel",
+                                           "kda_inter_wide_kernel"};
 struct TimedLaunch {
     int kernel;
     hipEvent_t start, stop;
@@ -153,7 +155,8 @@ Plan make_plan_uncapped(const kda_shape* s) {
                       ? kda::rec_layout((int)s->dk, (int)s->dv, p.C, bf ? 2 : 4, true).bytes
                       : kda::rec_layout_thin(p.C, bf ? 2 : 4).bytes;
     int64_t per_chunk = bh * p.rec_bytes;
-    const int nv = kda::chunk_slice_width((int)s->dk, (int)s->dv, bf, bh);
+    const int wv = kda::wide_slice_width((int)s->dk, (int)s->dv, bf, s->alpha_mode, bh);
+    const int nv = wv ? wv : kda::chunk_slice_width((int)s->dk, (int)s->dv, bf, bh);
     const bool full_chip = bh * (s->dv / nv) >= kChipCUs;
     p.span = kSpanTargetBytes * (full_chip ? kFullChipSpanFactor : 1) / per_chunk;
     if (p.span < 1) p.span = 1;
@@ -378,6 +381,8 @@ int chunk_common(const char* who, const kda_shape* s, uint32_t flags, const int3
         return noalloc ? fn() : timed_launch(kernel, stream, fn);
     };
     const int nv = kda::chunk_slice_width((int)s->dk, (int)s->dv, qbf, bh);
+    // per-channel decay in bf16: the wide state pass (and the record order it reads)
+    const int wv = kda::wide_slice_width((int)s->dk, (int)s->dv, qbf, s->alpha_mode, bh);
     float* s_mid = S_final ? S_final : (float*)((char*)workspace + plan.rec_area);
 
     kda::IntraParams ip;
@@ -393,6 +398,7 @@ int chunk_common(const char* who, const kda_shape* s, uint32_t flags, const int3
     ip.flags = flags;
     ip.cu = cu;
     ip.H = (int)s->H;
+    ip.wide = wv != 0;
     kda::InterParams xp;
     xp.q = q;
     xp.k = k;
@@ -409,6 +415,9 @@ int chunk_common(const char* who, const kda_shape* s, uint32_t flags, const int3
     // per-channel decay: records hold every operand (inter-chunk kernel);
     // one decay per token: records hold T diag(beta) and the decay scalars
     auto launch_state = [&](const kda::InterParams& x) {
+        if (wv)
+            return launch(K_INTER_WIDE,
+                          [&] { return kda::launch_inter_wide(x, (int)s->dk, wv, stream); });
         return s->alpha_mode == KDA_ALPHA_CHANNEL
                    ? launch(K_INTER, [&] {
                          return kda::launch_inter(x, (int)s->dk, qbf, s->alpha_mode, nv, stream);

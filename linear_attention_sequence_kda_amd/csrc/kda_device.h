@@ -241,6 +241,22 @@ __device__ __forceinline__ uint32_t frag_elem(int m, int k, int K) {
                       k % W);
 }
 
+// ---- "wide" operand records -----------------------------------------------------
+// Element offset of bf16 operand element (m, k) of an operand with K columns
+// in the order the wide state pass reads it: 16-byte pieces of 8 values,
+// piece ((m/16) * (K/32) + k/32) * 64 + lane, lane = 16 ((k % 16) / 4) + m % 16,
+// position (k % 4) + 4 ((k % 32) / 16).  Within a 32-wide k step a lane's
+// 8 values are k = 32kk + 4q .. +3 and 32kk + 16 + 4q .. +3 (q = lane / 16):
+// exactly the rows a lane holds of two 16-row MFMA accumulator blocks, so an
+// accumulator pair is an MFMA operand as it is (both operands of a product
+// take the contraction index in this same order, which leaves the sum as it
+// is).  Four consecutive k (a multiple of 4) are four consecutive positions.
+__device__ __forceinline__ uint32_t wide_elem(int m, int k, int K) {
+    const int kp = k & 31;
+    return (uint32_t)(((((m >> 4) * (K >> 5) + (k >> 5)) * 64 + ((kp & 15) >> 2) * 16 + (m & 15)) * 8) +
+                      (kp & 3) + 4 * (kp >> 4));
+}
+
 // ---- small stores and loads --------------------------------------------------
 template <typename E>
 __device__ __forceinline__ void st4(E* p, floatx4 v) {

@@ -52,7 +52,10 @@ struct InterCfg {
     static constexpr int PC = C + PADE;    // u^T [NV][C]
     static constexpr int PO = NV + PADE;   // o tile [C][NV]
     static constexpr int NWC = 8;          // compute waves
-    static constexpr int NWP = 8;          // data waves (hold two chunks in flight)
+    static constexpr int NWP = 8;          // data waves
+    // chunks the data waves keep in flight in registers: the pass waits on
+    // memory latency, so each chunk takes about latency / NSET
+    static constexpr int NSET = 3;
     static constexpr int NT = 64 * (NWC + NWP);
     // Phase-A items: (role, R, column group) with role u (u = U - W S) or o
     // (o = Q S ...), R a 16-token block, and the NVB column blocks of the
@@ -218,33 +221,40 @@ __global__ void __launch_bounds__(Cfg::NT) kda_inter_kernel(InterParams prm) {
             __builtin_amdgcn_s_barrier();
             asm volatile("" ::: "memory");
         };
-        // chunk x: loads issued in iteration x-3 into set x % 2, written to
-        // its slot in iteration x-1, used by the compute waves in iteration x
-        DSet s0, s1;
+        // chunk x: loads issued in iteration x-NSET-1 into set x % NSET,
+        // written to its slot in iteration x-1, used by the compute waves in
+        // iteration x
+        constexpr int NSET = Cfg::NSET;
+        DSet sets[NSET];
         if (ncs > 0) {
-            fetch(s0, 0);
+#pragma unroll
+            for (int j = 0; j < NSET; ++j) fetch(sets[j], j);
             store_o(-1);
-            fetch(s1, 1);
-            store_o(-1);
-            put(s0, 0);
-            fetch(s0, 2);
+            put(sets[0], 0);
+            fetch(sets[0], NSET);
             store_o(-1);
         }
         __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0)
         bare_barrier();
-        // iteration cs: chunk cs+1 is in `nx`, which then takes chunk cs+3
+        // iteration cs: chunk cs+1 is in `nx`, which then takes chunk cs+1+NSET
         auto iteration = [&](DSet& nx, int cs) {
             put(nx, cs + 1);
-            fetch(nx, cs + 3);
+            fetch(nx, cs + 1 + NSET);
             store_o(cs - 1);
             __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): slot writes, o reads done
             bare_barrier();                      // A
             bare_barrier();                      // B
         };
-        for (int cs = 0; cs < ncs; cs += 2) {
-            iteration(s1, cs);
-            if (cs + 1 >= ncs) break;
-            iteration(s0, cs + 1);
+        for (int c0 = 0; c0 < ncs; c0 += NSET) {
+            bool done = false;
+#pragma unroll
+            for (int j = 0; j < NSET; ++j) {
+                if (!done) {
+                    iteration(sets[(j + 1) % NSET], c0 + j);
+                    done = c0 + j + 1 >= ncs;
+                }
+            }
+            if (done) break;
         }
         if (ncs > 0) store_o(ncs - 1);
         return;

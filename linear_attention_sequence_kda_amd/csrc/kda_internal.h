@@ -109,6 +109,9 @@ struct IntraParams {
     uint32_t flags = 0;     // kda_input_flags
     const int32_t* cu = nullptr;  // packed sequences: [B + 1] token offsets
     int H = 1;              // heads per sequence (packed sequences)
+    // per-channel decay, bf16: write the record in the wide state pass's
+    // order (W negated, W / Q~ / P / K^T in wide_elem order)
+    int wide = 0;
 };
 
 struct InterParams {
@@ -144,6 +147,13 @@ hipError_t launch_intra(const IntraParams& prm, int dk, int dv, int qkv_bf16, in
 hipError_t launch_inter(InterParams prm, int dk, int qkv_bf16, int alpha_mode, int nv,
                         hipStream_t stream);
 hipError_t launch_inter_scalar(InterParams prm, int dk, int qkv_bf16, int nv, hipStream_t stream);
+// State pass for per-channel decay with bf16 operands over wide column slices
+// (nv = 64 or 128 state columns per workgroup; dk, nv in {64, 128}); reads
+// records written with IntraParams::wide.
+hipError_t launch_inter_wide(InterParams prm, int dk, int nv, hipStream_t stream);
+// Slice width of launch_inter_wide for this problem, or 0 where that pass
+// does not apply (the other state passes run instead).
+int wide_slice_width(int dk, int dv, int qkv_bf16, int alpha_mode, int64_t BH);
 
 // Arguments of the decode step kernel.
 struct DecodeParams {

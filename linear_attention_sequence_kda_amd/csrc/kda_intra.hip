@@ -119,7 +119,7 @@ struct IntraCfg {
     static constexpr int MIN_WAVES = THIN ? 8 : 1;
 };
 
-template <class Cfg, bool GBF>
+template <class Cfg, bool GBF, bool WIDE>
 __global__ void __launch_bounds__(Cfg::NT) __attribute__((amdgpu_waves_per_eu(Cfg::MIN_WAVES)))
 kda_intra_kernel(IntraParams prm) {
     typedef typename Cfg::E E;
@@ -421,7 +421,13 @@ kda_intra_kernel(IntraParams prm) {
                     bf16x8 v;
 #pragma unroll
                     for (int e = 0; e < 8; ++e) v[e] = (bf16)(ky[W * pc + e] * Fr);
-                    *(bf16x8*)(rKt + frag_elem<E>(kc, j0, C)) = v;
+                    if constexpr (WIDE) {
+                        const bf16x4 lo = {v[0], v[1], v[2], v[3]}, hi = {v[4], v[5], v[6], v[7]};
+                        *(bf16x4*)(rKt + wide_elem(kc, j0, C)) = lo;
+                        *(bf16x4*)(rKt + wide_elem(kc, j0 + 4, C)) = hi;
+                    } else {
+                        *(bf16x8*)(rKt + frag_elem<E>(kc, j0, C)) = v;
+                    }
                 } else {
                     floatx4 v;
 #pragma unroll
@@ -565,13 +571,20 @@ kda_intra_kernel(IntraParams prm) {
             vp[e] = (J < R || jj <= rr) ? accP[e] * f : 0.f;
         }
         *(floatx4*)(sA + rr * PA + 16 * J + 4 * lq) = va;
-        if constexpr (!THIN) st4<E>(rP + frag_elem<E>(rr, 16 * J + 4 * lq, C), vp);
+        if constexpr (!THIN) {
+            if constexpr (WIDE) st4<E>(rP + wide_elem(rr, 16 * J + 4 * lq, C), vp);
+            else st4<E>(rP + frag_elem<E>(rr, 16 * J + 4 * lq, C), vp);
+        }
     }
     // blocks above the diagonal of P are zero
     if constexpr (!THIN) {
         for (int b = w; b < NB * NB; b += NW) {
             const int R = b / NB, J = b % NB;
-            if (J > R) st4<E>(rP + frag_elem<E>(16 * R + lr, 16 * J + 4 * lq, C), floatx4{0.f, 0.f, 0.f, 0.f});
+            if (J > R) {
+                const floatx4 z = {0.f, 0.f, 0.f, 0.f};
+                if constexpr (WIDE) st4<E>(rP + wide_elem(16 * R + lr, 16 * J + 4 * lq, C), z);
+                else st4<E>(rP + frag_elem<E>(16 * R + lr, 16 * J + 4 * lq, C), z);
+            }
         }
     }
     __syncthreads();
@@ -655,7 +668,14 @@ kda_intra_kernel(IntraParams prm) {
                     *(typename F::T*)p = F::load_scaled(p, sc);
                 } else {
                     const E* p = sQr + r * PK + cc;
-                    *(typename F::T*)(rQt + frag_elem<E>(r, cc, DK)) = F::load_scaled(p, sc);
+                    const typename F::T qs = F::load_scaled(p, sc);
+                    if constexpr (WIDE) {
+                        const bf16x4 lo = {qs[0], qs[1], qs[2], qs[3]}, hi = {qs[4], qs[5], qs[6], qs[7]};
+                        *(bf16x4*)(rQt + wide_elem(r, cc, DK)) = lo;
+                        *(bf16x4*)(rQt + wide_elem(r, cc + 4, DK)) = hi;
+                    } else {
+                        *(typename F::T*)(rQt + frag_elem<E>(r, cc, DK)) = qs;
+                    }
                 }
             }
         }
@@ -727,7 +747,8 @@ kda_intra_kernel(IntraParams prm) {
             const int K = ((16 * (R + 1) + KS - 1) / KS) * KS;
             floatx4 acc = {0.f, 0.f, 0.f, 0.f};
             acc = mma_block_at<E>(acc, sKr, PK, 16 * cb, sTw + (16 * R) * PC, PC, K);
-            st4<E>(rW + frag_elem<E>(16 * R + lr, 16 * cb + 4 * lq, DK), acc);
+            if constexpr (WIDE) st4<E>(rW + wide_elem(16 * R + lr, 16 * cb + 4 * lq, DK), -acc);
+            else st4<E>(rW + frag_elem<E>(16 * R + lr, 16 * cb + 4 * lq, DK), acc);
         } else {
             const int u = it - NB * NCB;
             const int R = u % NB, vb = u / NB;
@@ -746,11 +767,25 @@ template <int DK, int DV, int C, typename E, int AMODE>
 static hipError_t launch_intra_cfg(const IntraParams& prm, hipStream_t stream) {
     typedef IntraCfg<DK, DV, C, E, AMODE> Cfg;
     const int64_t grid = (int64_t)prm.BH * prm.ncs;
+    // the wide record order exists for per-channel decay with bf16 operands
+    constexpr bool CAN_WIDE = Cfg::KDA && sizeof(E) == 2;
+    if (prm.wide && !CAN_WIDE) return hipErrorInvalidValue;
+    if constexpr (CAN_WIDE) {
+        if (prm.wide) {
+            if (prm.gate_bf16)
+                hipLaunchKernelGGL((kda_intra_kernel<Cfg, true, true>), dim3((unsigned)grid),
+                                   dim3(Cfg::NT), 0, stream, prm);
+            else
+                hipLaunchKernelGGL((kda_intra_kernel<Cfg, false, true>), dim3((unsigned)grid),
+                                   dim3(Cfg::NT), 0, stream, prm);
+            return hipGetLastError();
+        }
+    }
     if (prm.gate_bf16)
-        hipLaunchKernelGGL((kda_intra_kernel<Cfg, true>), dim3((unsigned)grid), dim3(Cfg::NT), 0,
+        hipLaunchKernelGGL((kda_intra_kernel<Cfg, true, false>), dim3((unsigned)grid), dim3(Cfg::NT), 0,
                            stream, prm);
     else
-        hipLaunchKernelGGL((kda_intra_kernel<Cfg, false>), dim3((unsigned)grid), dim3(Cfg::NT), 0,
+        hipLaunchKernelGGL((kda_intra_kernel<Cfg, false, false>), dim3((unsigned)grid), dim3(Cfg::NT), 0,
                            stream, prm);
     return hipGetLastError();
 }

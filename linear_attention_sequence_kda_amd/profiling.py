@@ -35,6 +35,7 @@ KERNEL_SOURCES = {
     "kda_intra_kernel": ["kda_intra.hip"],
     "kda_inter_kernel": ["kda_inter.hip"],
     "kda_inter_scalar_kernel": ["kda_inter_scalar.hip"],
+    "kda_inter_wide_kernel": ["kda_inter_wide.hip"],
     "kda_decode_kernel": ["kda_decode.hip"],
     "kda_bwd_kernel": ["kda_bwd.hip"],
 }

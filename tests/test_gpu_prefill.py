@@ -74,6 +74,18 @@ def test_slice_widths(B, H, dk, dv, qd):
     run_and_compare(w, "slices")
 
 
+# per-channel decay in bf16 runs a state pass whose slice width follows the
+# number of heads: 16 columns up to 63 heads (d_v = 128), 32 up to 127, 64
+# beyond; each width, with d_k = 64 and 128 and d_v = 64 too
+@pytest.mark.parametrize("B,H,dk,dv", [(1, 5, 128, 128), (2, 48, 128, 128), (4, 40, 128, 128),
+                                       (2, 70, 64, 128), (3, 50, 128, 64), (5, 60, 64, 64),
+                                       (1, 3, 64, 64)])
+def test_kda_state_pass_slice_widths(B, H, dk, dv):
+    w = gen.custom(B=B, H=H, L=150, dk=dk, dv=dv, qkv_dtype="bf16", gate_dtype="bf16",
+                   alpha_mode="channel", s0_std=0.02, seed=B * H + dk + dv)
+    run_and_compare(w, "kda slices")
+
+
 @pytest.mark.parametrize("cfg", [1, 2, 3])
 def test_workload_full(cfg):
     run_and_compare(gen.WORKLOADS[cfg], f"workload{cfg}")
