@@ -70,18 +70,21 @@ def _rows(pass_dir: str) -> List[dict]:
     return rows
 
 
-def per_dispatch_kib(pass_dir: str, counter: str, match: str) -> List[float]:
-    """Counter value (KiB) of every dispatch whose kernel name contains `match`."""
+def per_dispatch_kib(pass_dir: str, counter: str, match: str, also: str = "") -> List[float]:
+    """Counter value (KiB) of every dispatch whose kernel name contains `match`
+    (and `also`)."""
     vals: Dict[str, float] = {}
     for r in _rows(pass_dir):
-        if r["Counter_Name"] == counter and match in r["Kernel_Name"]:
+        if r["Counter_Name"] == counter and match in r["Kernel_Name"] and also in r["Kernel_Name"]:
             vals[r["Dispatch_Id"]] = vals.get(r["Dispatch_Id"], 0.0) + float(r["Counter_Value"])
     return [vals[k] for k in sorted(vals, key=int)]
 
 
-def traffic(fetch_dir: str, write_dir: str, kernel: str) -> dict:
-    fk = per_dispatch_kib(fetch_dir, "FETCH_SIZE", kernel)
-    wk = per_dispatch_kib(write_dir, "WRITE_SIZE", kernel)
+def traffic(fetch_dir: str, write_dir: str, kernel: str, also: str = "") -> dict:
+    """HBM bytes per dispatch of `kernel` (every dispatch whose name also
+    contains `also`: one template instance when a run launches several)."""
+    fk = per_dispatch_kib(fetch_dir, "FETCH_SIZE", kernel, also)
+    wk = per_dispatch_kib(write_dir, "WRITE_SIZE", kernel, also)
     fc = per_dispatch_kib(fetch_dir, "FETCH_SIZE", COPY_KERNEL)
     wc = per_dispatch_kib(write_dir, "WRITE_SIZE", COPY_KERNEL)
     if not fk or not wk:
@@ -158,13 +161,16 @@ def main():
     t.add_argument("--kernel", required=True, choices=sorted(KERNEL_SOURCES))
     t.add_argument("--workload", required=True)
     t.add_argument("--out", required=True)
+    t.add_argument("--also", default="", help="a further substring of the kernel name "
+                   "(one template instance, e.g. Lb1ELb1E for the KDA intra-chunk kernel "
+                   "writing MFMA-order records)")
     a = ap.parse_args()
     if a.cmd == "mfma":
         for k in a.kernel:
             for rec in mfma(a.pmc, k):
                 print(json.dumps(rec))
         return
-    rec = traffic(a.fetch, a.write, a.kernel)
+    rec = traffic(a.fetch, a.write, a.kernel, a.also)
     rec["source_sha256"] = source_digest(a.kernel)
     data = {}
     if os.path.exists(a.out):
