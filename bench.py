@@ -96,7 +96,7 @@ def kernel_work(w, kernel):
             return (t["q"] + t["k"] + t["v"] + t["log_alpha"] + t["beta"],
                     tok * 2 * C * (3 * dk + dv))
         return t["k"] + t["log_alpha"] + t["beta"], tok * 2 * C * dk   # A only
-    if kernel in ("kda_inter_kernel", "kda_inter_wide_kernel"):   # u = U - W S, o = Q S + P u, S update
+    if kernel in ("kda_inter_kernel", "kda_inter_wide_kernel", "kda_inter_quad_kernel"):  # u = U - W S, o = Q S + P u, S update
         return t["o"] + t["S0"] + t["S_final"], tok * (6 * dk * dv + 2 * C * dv)
     if kernel == "kda_inter_scalar_kernel":  # X, u = T X, P, o, S update
         return (t["q"] + t["k"] + t["v"] + t["o"] + t["S0"] + t["S_final"],

@@ -41,15 +41,7 @@
  * - Calls are asynchronous on hip_stream (a hipStream_t; NULL = the null
  *   stream).  Outputs are valid once that stream has been synchronized.  The
  *   library allocates no device memory, keeps no per-call state and is safe
- *   to call from several host threads.  A prefill that runs as several spans
- *   with fewer state-pass workgroups than CUs (few heads, long sequences)
- *   overlaps each span's intra-chunk kernel with the previous span's state
- *   pass on two side streams of the calling thread (created on first use,
- *   default priority, kept until the process ends; the intra-chunk one is
- *   limited to three quarters of every XCD's CUs).  Its first kernels wait
- *   for the work queued on hip_stream before the call, and hip_stream waits
- *   for its last one, so for the caller the call is ordered on hip_stream
- *   as any other.  The allocation-free entry point never uses them.
+ *   to call from several host threads.
  * - Return value: KDA_OK (0) or a kda_status code.  Every check except
  *   KDA_ERR_HIP is made on the host before any HIP call, so a rejected call
  *   touches neither the device nor any buffer.  A fault inside a kernel is
@@ -137,9 +129,7 @@ typedef struct kda_shape {
  *            or with an input is an error.
  *   workspace, workspace_bytes: device scratch of at least
  *            kda_chunk_fwd_workspace_bytes(shape) bytes (may be NULL when that
- *            is 0): one record area per span in flight (two when spans
- *            overlap) and, with several spans, a state area.  The library
- *            does not keep it after the call's kernels end.
+ *            is 0).  The library does not keep it after the call's kernels end.
  */
 int kda_chunk_fwd(const kda_shape* shape, const void* q, const void* k, const void* v,
                   const void* log_alpha, const void* beta, const float* S0, void* o,
@@ -302,11 +292,9 @@ int kda_linear_attn_decode_step(const kda_shape* shape, const void* q, const voi
 /*
  * Kernel timing, for measurement tools (not part of the computation).  While
  * timing is on, every kernel that kda_chunk_fwd or kda_decode_step launches is
- * bracketed by two HIP events recorded on the stream it is launched on (the
- * call's stream, or a side stream of overlapped spans, whose kernels then
- * share the GPU and each take longer than alone); the event pairs are kept
- * until kda_timing_reset.  The events add a few microseconds of stream work
- * per launch and nothing else changes.
+ * bracketed by two HIP events recorded on the call's stream; the event pairs
+ * are kept until kda_timing_reset.  The events add a few microseconds of
+ * stream work per launch and nothing else changes.
  *
  *   kda_timing_enable(on)   on != 0 starts recording for later calls, 0 stops.
  *   kda_timing_reset()      destroys every kept event pair.  KDA_ERR_HIP if a
@@ -315,6 +303,7 @@ int kda_linear_attn_decode_step(const kda_shape* shape, const void* q, const voi
  *                           waits for the kept launches of the kernel `name`
  *                           ("kda_intra_kernel", "kda_inter_kernel",
  *                           "kda_inter_scalar_kernel", "kda_inter_wide_kernel",
+ *                           "kda_inter_quad_kernel",
  *                           "kda_decode_kernel",
  *                           "kda_feature_map_kernel" or "kda_bwd_kernel")
  *                           and returns how many there were and their summed

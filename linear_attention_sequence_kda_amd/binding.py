@@ -160,7 +160,7 @@ def _stream(t) -> int:
 
 
 KERNELS = ("kda_intra_kernel", "kda_inter_kernel", "kda_inter_scalar_kernel",
-           "kda_inter_wide_kernel", "kda_feature_map_kernel",
+           "kda_inter_wide_kernel", "kda_inter_quad_kernel", "kda_feature_map_kernel",
            "kda_decode_kernel", "kda_bwd_kernel")
 
 

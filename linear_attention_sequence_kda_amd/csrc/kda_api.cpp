@@ -21,11 +21,11 @@ thread_local std::string g_last_error;
 // While enabled, each kernel launch is bracketed by two events recorded on the
 // launch's stream; the pairs are kept until read or reset.
 enum KernelId { K_INTRA = 0, K_INTER, K_INTER_SCALAR, K_DECODE, K_FEATURE, K_BWD, K_INTER_WIDE,
-                K_COUNT };
+                K_INTER_QUAD, K_COUNT };
 const char* const kKernelNames[K_COUNT] = {"kda_intra_kernel", "kda_inter_kernel",
                                            "kda_inter_scalar_kernel", "kda_decode_kernel",
                                            "kda_feature_map_kernel", "kda_bwd_kernel",
-                                           "kda_inter_wide_kernel"};
+                                           "kda_inter_wide_kernel", "kda_inter_quad_kernel"};
 struct TimedLaunch {
     int kernel;
     hipEvent_t start, stop;
@@ -53,64 +53,6 @@ hipError_t timed_launch(int kernel, hipStream_t stream, Launch&& launch) {
     }
     std::lock_guard<std::mutex> lock(g_timing_mu);
     g_timed.push_back(t);
-    return hipSuccess;
-}
-
-// ---- side streams for overlapped spans -----------------------------------------
-// When the state pass leaves CUs idle, span s + 1's intra-chunk kernel runs
-// while span s's state pass does, each on a stream of the library's own: the
-// caller's stream may be the null stream, which would serialize any other
-// blocking stream with it.  The intra-chunk stream is limited to a fixed share
-// of every XCD's CUs, so the state pass always finds free CUs for its
-// workgroups (one of them needs most of a CU's LDS and would otherwise wait
-// for two intra-chunk workgroups to leave the same CU).  Per host thread and
-// device, the streams (default priority) and their events are created on
-// first use and kept until the process ends.
-#ifndef KDA_OVERLAP_QUARTERS
-#define KDA_OVERLAP_QUARTERS 3  // quarters of each XCD's CUs open to the intra-chunk stream
-#endif
-struct SideStreams {
-    hipStream_t intra = nullptr, state = nullptr;
-    hipEvent_t start = nullptr, intra_done = nullptr, state_done[2] = {nullptr, nullptr};
-    bool ready = false;
-};
-
-hipError_t side_streams(hipStream_t caller, SideStreams** out) {
-    *out = nullptr;
-    int dev = 0;
-    hipError_t e = hipGetDevice(&dev);
-    if (e != hipSuccess) return e;
-    if (caller) {
-        hipDevice_t sd = 0;
-        e = hipStreamGetDevice(caller, &sd);
-        if (e != hipSuccess) return e;
-        if ((int)sd != dev) return hipSuccess;  // another device's stream: no overlap
-    }
-    constexpr int kMaxDevices = 64;
-    if (dev < 0 || dev >= kMaxDevices) return hipSuccess;
-    thread_local SideStreams per_device[kMaxDevices];
-    SideStreams& ss = per_device[dev];
-    if (!ss.ready) {
-        int cus = 0;
-        e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
-        if (e != hipSuccess) return e;
-        // CU i is open when (i / 8) % 4 < KDA_OVERLAP_QUARTERS: the same share
-        // of every XCD whether the mask numbers CUs XCD by XCD or round-robin
-        // over the XCDs
-        std::vector<uint32_t> mask((size_t)(cus + 31) / 32, 0u);
-        for (int i = 0; i < cus; ++i)
-            if (((i >> 3) & 3) < KDA_OVERLAP_QUARTERS) mask[(size_t)i >> 5] |= 1u << (i & 31);
-        if (ss.intra == nullptr)
-            e = hipExtStreamCreateWithCUMask(&ss.intra, (uint32_t)mask.size(), mask.data());
-        if (e == hipSuccess && ss.state == nullptr)
-            e = hipStreamCreateWithFlags(&ss.state, hipStreamNonBlocking);
-        hipEvent_t* evs[] = {&ss.start, &ss.intra_done, &ss.state_done[0], &ss.state_done[1]};
-        for (hipEvent_t* ev : evs)
-            if (e == hipSuccess && *ev == nullptr) e = hipEventCreateWithFlags(ev, hipEventDisableTiming);
-        if (e != hipSuccess) return e;
-        ss.ready = true;
-    }
-    *out = &ss;
     return hipSuccess;
 }
 
@@ -193,9 +135,6 @@ struct Plan {
     int64_t nchunks = 0, span = 0, nspans = 0;
     int64_t rec_bytes = 0, rec_area = 0, state_area = 0;
     int64_t ws_bytes = 0;
-    // two record areas: span s + 1's intra-chunk kernel overlaps span s's
-    // state pass (several spans and a state pass with fewer workgroups than CUs)
-    bool overlap = false;
     bool fits = true;  // false: no plan fits the byte cap make_plan was given
 };
 
@@ -240,20 +179,13 @@ Plan make_plan_uncapped(const kda_shape* s) {
     p.nspans = (p.nchunks + p.span - 1) / p.span;
     p.rec_area = p.span * per_chunk;
     p.state_area = p.nspans > 1 ? bh * s->dk * s->dv * 4 : 0;
-    p.overlap = p.nspans > 1 && !full_chip;
-    p.ws_bytes = p.rec_area * (p.overlap ? 2 : 1) + p.state_area;
+    p.ws_bytes = p.rec_area + p.state_area;
     return p;
 }
 
 Plan make_plan(const kda_shape* s, int64_t cap) {
     Plan p = make_plan_uncapped(s);
-    if (cap < 0) return p;
-    // a capped workspace (the static buffer) runs every span on one stream
-    if (p.overlap) {
-        p.overlap = false;
-        p.ws_bytes = p.rec_area + p.state_area;
-    }
-    if (p.ws_bytes <= cap) return p;
+    if (cap < 0 || p.ws_bytes <= cap) return p;
     const int64_t per_chunk = s->B * s->H * p.rec_bytes;
     if (p.nchunks * per_chunk <= cap) {
         p.span = p.nchunks;
@@ -268,7 +200,6 @@ Plan make_plan(const kda_shape* s, int64_t cap) {
     p.nspans = (p.nchunks + p.span - 1) / p.span;
     p.rec_area = p.span * per_chunk;
     p.state_area = p.nspans > 1 ? s->B * s->H * s->dk * s->dv * 4 : 0;
-    p.overlap = false;
     p.ws_bytes = p.rec_area + p.state_area;
     return p;
 }
@@ -446,29 +377,13 @@ int chunk_common(const char* who, const kda_shape* s, uint32_t flags, const int3
         }
     }
     // the allocation-free call records no timing events
-    auto launch = [&](int kernel, hipStream_t st, auto&& fn) -> hipError_t {
-        return noalloc ? fn() : timed_launch(kernel, st, fn);
+    auto launch = [&](int kernel, auto&& fn) -> hipError_t {
+        return noalloc ? fn() : timed_launch(kernel, stream, fn);
     };
-    SideStreams* side = nullptr;
-    if (plan.overlap && !noalloc) {
-        hipError_t e = side_streams(stream, &side);
-        if (e != hipSuccess) {
-            g_last_error = std::string(who) + ": " + hipGetErrorString(e);
-            return KDA_ERR_HIP;
-        }
-    }
-    const int nbuf = side ? 2 : 1;
     const int nv = kda::chunk_slice_width((int)s->dk, (int)s->dv, qbf, bh);
-    // per-channel decay in bf16: the wide state pass (and the record order it
-    // reads).  Next to a concurrent intra-chunk kernel it takes 32-column
-    // slices rather than 16: a chain's chunk time is bound by its workgroup's
-    // record loads (about the same bytes per chunk at either width, measured
-    // 74 against 69 us per 64 chunks on the long-context shape), and half as
-    // many workgroups leave more CUs to the other kernel.
-    const int wv0 = kda::wide_slice_width((int)s->dk, (int)s->dv, qbf, s->alpha_mode, bh);
-    const int wv = side && wv0 == 16 ? 32 : wv0;
-    float* s_mid =
-        S_final ? S_final : (float*)((char*)workspace + plan.rec_area * (plan.overlap ? 2 : 1));
+    // per-channel decay in bf16: the wide state pass (and the record order it reads)
+    const int wv = kda::wide_slice_width((int)s->dk, (int)s->dv, qbf, s->alpha_mode, bh);
+    float* s_mid = S_final ? S_final : (float*)((char*)workspace + plan.rec_area);
 
     kda::IntraParams ip;
     ip.q = q;
@@ -499,18 +414,17 @@ int chunk_common(const char* who, const kda_shape* s, uint32_t flags, const int3
     xp.H = (int)s->H;
     // per-channel decay: records hold every operand (inter-chunk kernel);
     // one decay per token: records hold T diag(beta) and the decay scalars
-    const hipStream_t istream = side ? side->intra : stream;
-    const hipStream_t sstream = side ? side->state : stream;
     auto launch_state = [&](const kda::InterParams& x) {
+        // 16-column slices run kda_inter_quad_kernel, wider ones kda_inter_wide_kernel
         if (wv)
-            return launch(K_INTER_WIDE, sstream,
-                          [&] { return kda::launch_inter_wide(x, (int)s->dk, wv, sstream); });
+            return launch(wv == 16 ? K_INTER_QUAD : K_INTER_WIDE,
+                          [&] { return kda::launch_inter_wide(x, (int)s->dk, wv, stream); });
         return s->alpha_mode == KDA_ALPHA_CHANNEL
-                   ? launch(K_INTER, sstream, [&] {
-                         return kda::launch_inter(x, (int)s->dk, qbf, s->alpha_mode, nv, sstream);
+                   ? launch(K_INTER, [&] {
+                         return kda::launch_inter(x, (int)s->dk, qbf, s->alpha_mode, nv, stream);
                      })
-                   : launch(K_INTER_SCALAR, sstream, [&] {
-                         return kda::launch_inter_scalar(x, (int)s->dk, qbf, nv, sstream);
+                   : launch(K_INTER_SCALAR, [&] {
+                         return kda::launch_inter_scalar(x, (int)s->dk, qbf, nv, stream);
                      });
     };
     hipError_t err = hipSuccess;
@@ -522,42 +436,21 @@ int chunk_common(const char* who, const kda_shape* s, uint32_t flags, const int3
         xp.ncs = 0;
         err = launch_state(xp);
     }
-    // With the side streams: both wait for the caller's earlier work; intra(s)
-    // runs after state(s - 2) (which read the same record area), state(s)
-    // after intra(s); the caller's stream waits for the last state pass,
-    // which follows every intra launch.
-    if (side) {
-        err = hipEventRecord(side->start, stream);
-        if (err == hipSuccess) err = hipStreamWaitEvent(side->intra, side->start, 0);
-        if (err == hipSuccess) err = hipStreamWaitEvent(side->state, side->start, 0);
-    }
     for (int64_t sp = 0; sp < plan.nspans && err == hipSuccess; ++sp) {
         const int64_t c0 = sp * plan.span;
         const int64_t ncs = plan.nchunks - c0 < plan.span ? plan.nchunks - c0 : plan.span;
-        void* recs = (char*)workspace + (sp % nbuf) * plan.rec_area;
-        ip.ws = recs;
-        xp.ws = recs;
         ip.c0 = c0;
         ip.ncs = (int)ncs;
-        if (side && sp >= 2) err = hipStreamWaitEvent(side->intra, side->state_done[sp & 1], 0);
-        if (err != hipSuccess) break;
-        err = launch(K_INTRA, istream, [&] {
-            return kda::launch_intra(ip, (int)s->dk, (int)s->dv, qbf, s->alpha_mode, istream);
+        err = launch(K_INTRA, [&] {
+            return kda::launch_intra(ip, (int)s->dk, (int)s->dv, qbf, s->alpha_mode, stream);
         });
-        if (err == hipSuccess && side) {
-            err = hipEventRecord(side->intra_done, side->intra);
-            if (err == hipSuccess) err = hipStreamWaitEvent(side->state, side->intra_done, 0);
-        }
         if (err != hipSuccess) break;
         xp.S_in = sp == 0 ? S0 : s_mid;
         xp.S_out = sp == plan.nspans - 1 ? S_final : s_mid;
         xp.c0 = c0;
         xp.ncs = (int)ncs;
         err = launch_state(xp);
-        if (err == hipSuccess && side) err = hipEventRecord(side->state_done[sp & 1], side->state);
     }
-    if (err == hipSuccess && side)
-        err = hipStreamWaitEvent(stream, side->state_done[(plan.nspans - 1) & 1], 0);
     if (err != hipSuccess) {
         g_last_error = std::string(who) + ": " + hipGetErrorString(err);
         return KDA_ERR_HIP;

@@ -44,6 +44,9 @@
 #ifndef KDA_WIDE_NSET64
 #define KDA_WIDE_NSET64 3
 #endif
+#ifndef KDA_QUAD_NSET
+#define KDA_QUAD_NSET 2
+#endif
 
 namespace kda {
 
@@ -423,6 +426,238 @@ __global__ void __launch_bounds__(Cfg::NT) kda_inter_wide_kernel(InterParams prm
     }
 }
 
+// ---- 16-column slices: four waves, operands straight from memory -----------
+// On gfx950 a CU writes LDS at only about 64-80 bytes per clock (reads reach
+// about 240), so staging every record piece through an LDS ring costs more
+// than loading it (measured on the long-context shape: the ring's writes
+// alone about 1,500 cycles per chunk, the record loads alone about 630).
+// Here nothing of the record passes through LDS.  The chunk's work is dealt
+// over four waves, one per SIMD, so that each needs only about a quarter of
+// the record, which it loads itself into registers two chunks ahead: wave j
+// takes u's token block j (u_j = U_j - W_j S, needing all of S), the state's
+// channel blocks of its quarter (S <- e^{g_n} S + K^T u, needing all of u)
+// and o's token block j.  S and u cross between the waves as bf16 operand
+// fragments through two small LDS exchange areas, two barriers per chunk:
+//   X1 .. X2   u_j, its fragment half to the exchange
+//   X2 .. X1   state update; the new S fragment to the exchange; o_j of the
+//              chunk, stored from registers
+// and each group of a wave's registers is refilled with chunk c + 2 as soon
+// as its last use in chunk c is issued.
+// Every column goes through the same operations, in the same order, as in
+// the other widths' kernel, so the results are the same bit for bit.
+template <int DK_, int NSET_>
+struct QuadCfg {
+    static constexpr int DK = DK_, NV = 16, C = 64;
+    static constexpr int NB = C / 16, NKA = DK / 32, NKP = C / 32, NCB = DK / 16;
+    static constexpr int NW = 4, NT = 64 * NW;
+    static constexpr int CBW = NCB / NW;  // state channel blocks per wave
+    static constexpr int NSET = NSET_;    // chunks of operands in flight per wave
+    static constexpr int O_XS = 0, O_XU = NKA * 1024, LDS_BYTES = O_XU + NKP * 1024;
+    static_assert(NB == NW && (CBW == 1 || CBW == 2), "one token block per wave");
+};
+
+// fp32 accumulator quad -> four bf16 (nearest even): half an operand fragment
+__device__ __forceinline__ bf16x4 pack_half(floatx4 a) {
+    bf16x4 r;
+    r[0] = (bf16)a[0];
+    r[1] = (bf16)a[1];
+    r[2] = (bf16)a[2];
+    r[3] = (bf16)a[3];
+    return r;
+}
+
+template <class Cfg>
+__global__ void __launch_bounds__(Cfg::NT, 2) kda_inter_quad_kernel(InterParams prm) {
+    typedef bf16 E;
+    typedef Frag<E> F;
+    typedef int v2i __attribute__((ext_vector_type(2)));
+    typedef int v4i __attribute__((ext_vector_type(4)));
+    constexpr int DK = Cfg::DK, NV = Cfg::NV, C = Cfg::C, NKA = Cfg::NKA, NKP = Cfg::NKP;
+    constexpr int CBW = Cfg::CBW, NSET = Cfg::NSET;
+
+    __shared__ __attribute__((aligned(16))) char smem[Cfg::LDS_BYTES];
+    char* xs = smem + Cfg::O_XS;
+    char* xu = smem + Cfg::O_XU;
+
+    const int tid = threadIdx.x;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int l = tid & 63;
+    const int lr = l & 15, lq = l >> 4;
+
+    // workgroup i runs on XCD i % 8: the slices of one head share an XCD and
+    // so one L2 for their reads of the head's records
+    const int total = prm.BH * prm.n_slices;
+    int pidx = blockIdx.x;
+    if ((total & 7) == 0) pidx = (blockIdx.x & 7) * (total >> 3) + (blockIdx.x >> 3);
+    const int bh = pidx / prm.n_slices;
+    const int slice = pidx - bh * prm.n_slices;
+    const int v0 = slice * NV;
+    const SeqRange sr = seq_range(prm.cu, prm.L, prm.H, bh);
+    const int64_t L = sr.len;
+    const int DV = prm.DV;
+    const RecLayout rl = rec_layout(DK, DV, C, 2, true);
+    const char* recs = (const char*)prm.ws + (int64_t)bh * prm.ncs * rl.bytes;
+    int64_t left = (L + C - 1) / C - prm.c0;
+    const int ncs = (int)(left < 0 ? 0 : (left < prm.ncs ? left : prm.ncs));
+    // Chunk steps, rounded up to whole rounds of the register sets; steps past
+    // the last chunk repeat its loads and arithmetic but keep neither the state
+    // nor o.  A loop body without branches around its memory operations keeps
+    // the compiler's memory-counter waits exact across the back edge.
+    const int nsteps = ncs > 0 ? (ncs + NSET - 1) / NSET * NSET : 0;
+
+    auto bare_barrier = []() {
+        asm volatile("" ::: "memory");
+        __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0)
+        __builtin_amdgcn_s_barrier();
+        asm volatile("" ::: "memory");
+    };
+
+    // ---- this wave's operands of one chunk, straight from its record ----------
+    struct OSet {
+        bf16x8 wf[NKA];       // W_w (stored negated), contraction blocks kk
+        bf16x8 kf[CBW][NKP];  // K^T rows of this wave's channel blocks
+        bf16x8 qf[NKA];       // Q~_w
+        bf16x8 pf[NKP];       // P_w (blocks past the diagonal not loaded)
+        v2i uf;               // U_w: this slice's half of the 32-column piece
+        floatx4 g[CBW];       // e^{g_n} of this lane's state rows
+    };
+    const uint32_t l16 = l * 16;
+    const int vh = (v0 >> 4) & 1;
+    // piece offsets in the record (wave-uniform)
+    const uint32_t off_w = rl.w + w * NKA * 1024, off_q = rl.qt + w * NKA * 1024;
+    const uint32_t off_k = rl.kt + CBW * w * NKP * 1024, off_p = rl.p + w * NKP * 1024;
+    const uint32_t off_u = rl.ut + (w * (DV / 32) + (v0 >> 5)) * 1024;
+    // The loads of one chunk go out in three groups, each as soon as the
+    // registers it refills are free, so that the texture path (about 64-100
+    // bytes per clock per CU) streams them while the waves compute instead of
+    // stalling all four waves on one burst.
+    auto rsrc_of = [&](int cs) {
+        cs = __builtin_amdgcn_readfirstlane(cs < ncs ? cs : ncs - 1);
+        return make_rsrc(recs + (int64_t)cs * rl.bytes, rl.bytes);
+    };
+    auto ld = [&](__amdgpu_buffer_rsrc_t rr, uint32_t off) -> bf16x8 {
+        return __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(rr, (int)l16, (int)off, 0));
+    };
+    auto fetch_u = [&](OSet& st, __amdgpu_buffer_rsrc_t rr) {  // W, U: used before X2
+#pragma unroll
+        for (int kk = 0; kk < NKA; ++kk) st.wf[kk] = ld(rr, off_w + kk * 1024);
+        st.uf = __builtin_bit_cast(v2i, __builtin_amdgcn_raw_buffer_load_b64(rr, (int)(l16 + vh * 8), (int)off_u, 0));
+    };
+    auto fetch_s = [&](OSet& st, __amdgpu_buffer_rsrc_t rr) {  // K^T, e^{g_n}: the update
+#pragma unroll
+        for (int i = 0; i < CBW; ++i) {
+#pragma unroll
+            for (int kk = 0; kk < NKP; ++kk) st.kf[i][kk] = ld(rr, off_k + (i * NKP + kk) * 1024);
+            st.g[i] = __builtin_bit_cast(floatx4, __builtin_amdgcn_raw_buffer_load_b128(
+                rr, (int)((16 * (CBW * w + i) + 4 * lq) * 4), (int)rl.gam, 0));
+        }
+    };
+    auto fetch_o = [&](OSet& st, __amdgpu_buffer_rsrc_t rr) {  // Q~, P: o
+#pragma unroll
+        for (int kk = 0; kk < NKA; ++kk) st.qf[kk] = ld(rr, off_q + kk * 1024);
+#pragma unroll
+        for (int kk = 0; kk < NKP; ++kk)
+            if (32 * kk <= 16 * w + 15) st.pf[kk] = ld(rr, off_p + kk * 1024);
+    };
+    auto fetch = [&](OSet& st, int cs) {
+        const __amdgpu_buffer_rsrc_t rr = rsrc_of(cs);
+        fetch_u(st, rr);
+        fetch_s(st, rr);
+        fetch_o(st, rr);
+    };
+    auto sched_fence = []() { __builtin_amdgcn_sched_barrier(0); };
+
+    // ---- state: this wave's channel blocks, all 16 columns -------------------
+    floatx4 Sacc[CBW];
+#pragma unroll
+    for (int i = 0; i < CBW; ++i) {
+        Sacc[i] = floatx4{0.f, 0.f, 0.f, 0.f};
+        if (prm.S_in) {
+            const float* s0 = prm.S_in + (int64_t)bh * DK * DV + v0 + lr;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) Sacc[i][e] = s0[(16 * (CBW * w + i) + 4 * lq + e) * DV];
+        }
+    }
+    // this wave's S rows as (half of) operand fragment CBW w / 2 of S
+    auto write_s = [&]() {
+        if constexpr (CBW == 2)
+            *(bf16x8*)(xs + w * 1024 + l * 16) = pack_frag(Sacc[0], Sacc[1]);
+        else
+            *(bf16x4*)(xs + (w >> 1) * 1024 + l * 16 + (w & 1) * 8) = pack_half(Sacc[0]);
+    };
+    // o rows 16 w .. 16 w + 15 of the slice, 4 bf16 per lane; rows past the
+    // sequence (and every row of a step past the last chunk) fall outside
+    // the buffer resource and are dropped
+    const __amdgpu_buffer_rsrc_t orsrc =
+        make_rsrc((const char*)prm.o + sr.base * DV * 2, (uint32_t)(L * DV * 2));
+
+    OSet sets[NSET];
+    if (ncs > 0) {
+#pragma unroll
+        for (int j = 0; j < NSET; ++j) fetch(sets[j], j);
+    }
+    write_s();
+    bare_barrier();  // X1 of step 0
+    for (int c0 = 0; c0 < nsteps; c0 += NSET) {
+#pragma unroll
+        for (int j = 0; j < NSET; ++j) {
+            const int cs = c0 + j;
+            const bool live = cs < ncs;
+            OSet& st = sets[j];
+            const __amdgpu_buffer_rsrc_t rnext = rsrc_of(cs + NSET);
+            // ---- X1 .. X2: u_w = U_w + (-W_w) S ----
+            bf16x8 sb[NKA];
+#pragma unroll
+            for (int kk = 0; kk < NKA; ++kk) sb[kk] = *(const bf16x8*)(xs + kk * 1024 + l * 16);
+            const uint32_t ux = (uint32_t)st.uf[0], uy = (uint32_t)st.uf[1];
+            floatx4 u = {__uint_as_float(ux << 16), __uint_as_float(ux & 0xffff0000u),
+                         __uint_as_float(uy << 16), __uint_as_float(uy & 0xffff0000u)};
+#pragma unroll
+            for (int kk = 0; kk < NKA; ++kk) u = F::mma(u, st.wf[kk], sb[kk]);
+            *(bf16x4*)(xu + (w >> 1) * 1024 + l * 16 + (w & 1) * 8) = pack_half(u);
+            sched_fence();
+            fetch_u(st, rnext);
+            sched_fence();
+            bare_barrier();  // X2
+            // ---- X2 .. X1: S = e^{g_n} S + K^T u; o_w = S^T Q~_w^T + u^T P_w^T ----
+            bf16x8 ub[NKP];
+#pragma unroll
+            for (int kk = 0; kk < NKP; ++kk) ub[kk] = *(const bf16x8*)(xu + kk * 1024 + l * 16);
+#pragma unroll
+            for (int i = 0; i < CBW; ++i) {
+                floatx4 acc = Sacc[i] * st.g[i];
+#pragma unroll
+                for (int kk = 0; kk < NKP; ++kk) acc = F::mma(acc, st.kf[i][kk], ub[kk]);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) Sacc[i][e] = live ? acc[e] : Sacc[i][e];
+            }
+            write_s();
+            sched_fence();
+            fetch_s(st, rnext);
+            sched_fence();
+            floatx4 oacc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int kk = 0; kk < NKA; ++kk) oacc = F::mma(oacc, sb[kk], st.qf[kk]);
+#pragma unroll
+            for (int kk = 0; kk < NKP; ++kk)
+                if (32 * kk <= 16 * w + 15) oacc = F::mma(oacc, ub[kk], st.pf[kk]);
+            const int64_t row = (prm.c0 + cs) * C + 16 * w + lr;
+            const uint32_t off = live && row < L ? (uint32_t)((row * DV + v0 + 4 * lq) * 2) : 0x80000000u;
+            buf_st4<E>(orsrc, off, oacc);
+            sched_fence();
+            fetch_o(st, rnext);
+            bare_barrier();  // X1 of step cs + 1
+        }
+    }
+    if (prm.S_out) {
+        float* so = prm.S_out + (int64_t)bh * DK * DV + v0 + lr;
+#pragma unroll
+        for (int i = 0; i < CBW; ++i)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) so[(16 * (CBW * w + i) + 4 * lq + e) * DV] = Sacc[i][e];
+    }
+}
+
 // ---- host-side dispatch -----------------------------------------------------
 
 template <int DK, int NV, int NWC, int NSET>
@@ -430,6 +665,14 @@ static hipError_t launch_wide_cfg(const InterParams& prm, hipStream_t stream) {
     typedef WideCfg<DK, NV, NWC, NSET> Cfg;
     const int total = prm.BH * prm.n_slices;
     hipLaunchKernelGGL((kda_inter_wide_kernel<Cfg>), dim3(total), dim3(Cfg::NT), 0, stream, prm);
+    return hipGetLastError();
+}
+
+template <int DK, int NSET>
+static hipError_t launch_quad_cfg(const InterParams& prm, hipStream_t stream) {
+    typedef QuadCfg<DK, NSET> Cfg;
+    const int total = prm.BH * prm.n_slices;
+    hipLaunchKernelGGL((kda_inter_quad_kernel<Cfg>), dim3(total), dim3(Cfg::NT), 0, stream, prm);
     return hipGetLastError();
 }
 
@@ -450,10 +693,10 @@ hipError_t launch_inter_wide(InterParams prm, int dk, int nv, hipStream_t stream
     // (columns, compute waves, chunks in flight): every compute wave owns 16
     // or 32 columns; the data waves keep as many chunks in flight as their
     // registers hold
-    if (dk == 128 && nv == 16) return launch_wide_cfg<128, 16, 1, KDA_WIDE_NSET16>(prm, stream);
+    if (dk == 128 && nv == 16) return launch_quad_cfg<128, KDA_QUAD_NSET>(prm, stream);
     if (dk == 128 && nv == 32) return launch_wide_cfg<128, 32, 2, KDA_WIDE_NSET32>(prm, stream);
     if (dk == 128 && nv == 64) return launch_wide_cfg<128, 64, 2, KDA_WIDE_NSET64>(prm, stream);
-    if (dk == 64 && nv == 16) return launch_wide_cfg<64, 16, 1, KDA_WIDE_NSET16>(prm, stream);
+    if (dk == 64 && nv == 16) return launch_quad_cfg<64, KDA_QUAD_NSET>(prm, stream);
     if (dk == 64 && nv == 32) return launch_wide_cfg<64, 32, 2, KDA_WIDE_NSET32>(prm, stream);
     if (dk == 64 && nv == 64) return launch_wide_cfg<64, 64, 2, KDA_WIDE_NSET64>(prm, stream);
     return hipErrorInvalidValue;

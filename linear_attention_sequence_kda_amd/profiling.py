@@ -36,6 +36,7 @@ KERNEL_SOURCES = {
     "kda_inter_kernel": ["kda_inter.hip"],
     "kda_inter_scalar_kernel": ["kda_inter_scalar.hip"],
     "kda_inter_wide_kernel": ["kda_inter_wide.hip"],
+    "kda_inter_quad_kernel": ["kda_inter_wide.hip"],
     "kda_decode_kernel": ["kda_decode.hip"],
     "kda_bwd_kernel": ["kda_bwd.hip"],
 }

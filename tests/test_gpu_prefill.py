@@ -329,9 +329,7 @@ def test_head_gate_equals_broadcast_channel_gate():
 def test_few_heads_several_spans(mode, gd, L):
     """Two heads and a sequence long enough for several record spans (4 with
     per-channel decay; 2 with one decay per token, the second only 37 chunks),
-    so each span's intra-chunk kernel overlaps the previous span's state pass
-    (on the library's side streams; 32-column state slices with per-channel
-    decay, 16-column with one decay per token).  Checked against the oracle on a block of
+    with 16-column state slices.  Checked against the oracle on a block of
     state columns, with and without S_final (the state then crosses spans
     through the workspace), and bit for bit across repeated calls."""
     import torch
@@ -360,20 +358,19 @@ def test_few_heads_several_spans(mode, gd, L):
     assert e_o <= TOL["bf16"] and e_s <= TOL["bf16"]
 
 
-def test_overlapped_spans_follow_the_callers_stream():
-    """A call whose spans overlap runs its kernels on the library's side
-    streams: it must start after the work queued before it on the caller's
-    stream and end before the work queued after it.  Here an input is
-    written on a non-default stream behind a long GPU sleep, the call
-    follows on that stream, and a copy of o and S_final is taken on it
-    right after; all must match a call on settled inputs bit for bit."""
+def test_multi_span_call_follows_the_callers_stream():
+    """A multi-span call on a non-default stream starts after the work queued
+    before it there and ends before the work queued after it.  Here an input
+    is written on that stream behind a long GPU sleep, the call follows, and
+    a copy of o and S_final is taken on it right after; all must match a
+    call on settled inputs bit for bit."""
     import torch
     kda = _kda()
     w = gen.custom(B=1, H=2, L=100_000, dk=128, dv=128, qkv_dtype="bf16", gate_dtype="bf16",
                    alpha_mode="channel", s0_std=0.02, seed=613)
     x = gen.prefill_inputs(w, threads=16)
     d = device_inputs(w, x)
-    say("overlapped spans on a caller's stream")
+    say("multi-span call on a caller's stream")
     o_ref, S_ref = kda.chunk_fwd(d["q"], d["k"], d["v"], d["log_alpha"], d["beta"], d["S0"])
     k2 = torch.zeros_like(d["k"])
     torch.cuda.synchronize()
