@@ -380,14 +380,9 @@ kda_intra_kernel(IntraParams prm) {
                 }
                 g = wave_inclusive_sum(la);
             }
-            const float gn = read_lane(g, C - 1);
             if (l < C) {
-                const float eg = exp_neg(g);
                 sG[l] = g;
-                sEg[l] = eg;
-                rRs[l] = g;
-                rRs[C + l] = eg;
-                rRs[2 * C + l] = exp_neg(gn - g);
+                sEg[l] = exp_neg(g);
             }
         }
     }
@@ -399,6 +394,10 @@ kda_intra_kernel(IntraParams prm) {
         }
         sBeta[tid] = b;
     }
+    // Every load of the chunk has landed before the first record store goes
+    // out: loads and stores share one memory counter, so a later wait for a
+    // load would also wait for every store issued before it.
+    __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0)
     __syncthreads();
 
     // ================= G2 (KDA): cross-block factors, K^ ======================
@@ -728,8 +727,15 @@ kda_intra_kernel(IntraParams prm) {
             const int r = i / PPR, cc = (i % PPR) * (16 / ESZ);
             *(uint4*)(rTb + r * C + cc) = *(const uint4*)(sTb + r * PC + cc);
         }
-        // raw k: 1/|k_t| for the state pass (zero past the sequence end)
-        if (norm_qk && tid < C) rRs[3 * C + tid] = tid < n ? sKn[tid] : 0.f;
+        // the decay scalars g, e^g, e^{g_n - g}; raw k: 1/|k_t| for the
+        // state pass (zero past the sequence end)
+        if (tid < C) {
+            const float g = sG[tid];
+            rRs[tid] = g;
+            rRs[C + tid] = sEg[tid];
+            rRs[2 * C + tid] = exp_neg(sG[C - 1] - g);
+            if (norm_qk) rRs[3 * C + tid] = tid < n ? sKn[tid] : 0.f;
+        }
         return;
     }
     // KDA: W tile (R, cb) is computed transposed so each lane holds four
