@@ -46,6 +46,15 @@
  *   KDA_ERR_HIP is made on the host before any HIP call, so a rejected call
  *   touches neither the device nor any buffer.  A fault inside a kernel is
  *   reported by the stream, not here.
+ * - Diagnostics: with the environment variable KDA_LOG set to anything but
+ *   "" or "0" (read once per process), every call writes to stderr one line
+ *   with its shape and flags, the prefill calls one more with their plan
+ *   (chunks, spans, record and workspace bytes, the state pass and its slice
+ *   width), and any call that does not return KDA_OK one with its status (and
+ *   HIP's message for KDA_ERR_HIP); each line starts with "[kda] ".  Every
+ *   call is also one roctx range (rocprofiler-sdk) named after the entry
+ *   point, which `rocprofv3 --marker-trace` records around the kernels the
+ *   call launched.
  */
 #ifndef KDA_H
 #define KDA_H

@@ -36,6 +36,13 @@ def _flags():
             "-Wno-unused-result", "-I", INCLUDE, "-I", CSRC]
 
 
+def link_flags():
+    """Libraries the ABI layer links: roctx of rocprofiler-sdk (one profiler
+    range per ABI call)."""
+    rocm_lib = os.path.join(os.path.dirname(os.path.dirname(hipcc())), "lib")
+    return ["-L", rocm_lib, "-lrocprofiler-sdk-roctx", f"-Wl,-rpath,{rocm_lib}"]
+
+
 def _run(cmd, verbose):
     if verbose:
         print(" ".join(cmd), flush=True)
@@ -61,7 +68,8 @@ def build(verbose: bool = False) -> str:
         for f in [ex.submit(_run, j, verbose) for j in jobs]:
             f.result()
     tmp = LIB + ".tmp"
-    _run([hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC"] + objs + ["-o", tmp], verbose)
+    _run([hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC"] + objs + link_flags() + ["-o", tmp],
+         verbose)
     os.replace(tmp, LIB)
     return LIB
 

@@ -3,8 +3,13 @@
 // Every check runs on the host before any HIP call, so rejected calls touch
 // neither the device nor any buffer (and can be exercised without a GPU).
 #include <limits.h>
+#include <stdarg.h>
 #include <stdint.h>
+#include <stdio.h>
+#include <stdlib.h>
 #include <string.h>
+
+#include <rocprofiler-sdk-roctx/roctx.h>
 
 #include <mutex>
 #include <string>
@@ -16,6 +21,48 @@
 namespace {
 
 thread_local std::string g_last_error;
+
+// ---- host diagnostics (KDA_LOG) and profiler ranges --------------------------
+// KDA_LOG set to anything but "" or "0": every call writes its shape, the
+// prefill plan and any status other than KDA_OK to stderr, one line each.
+// Every call is also one roctx range named after the entry point, which
+// rocprofv3 --marker-trace records beside the kernels it launched.
+bool log_on() {
+    static const bool on = [] {
+        const char* e = getenv("KDA_LOG");
+        return e && *e && strcmp(e, "0") != 0;
+    }();
+    return on;
+}
+void klog(const char* fmt, ...) {
+    if (!log_on()) return;
+    char line[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(line, sizeof line, fmt, ap);
+    va_end(ap);
+    fprintf(stderr, "[kda] %s\n", line);
+    fflush(stderr);
+}
+const char* dtype_name(int32_t d) { return d == KDA_BF16 ? "bf16" : d == KDA_F32 ? "f32" : "?"; }
+const char* alpha_name(int32_t a) {
+    return a == KDA_ALPHA_NONE ? "none" : a == KDA_ALPHA_HEAD ? "head" : a == KDA_ALPHA_CHANNEL ? "channel" : "?";
+}
+struct CallScope {
+    const char* who;
+    CallScope(const char* w, const kda_shape* s, uint32_t flags) : who(w) {
+        roctxRangePushA(w);
+        if (!log_on()) return;
+        if (s)
+            klog("%s: B=%lld H=%lld L=%lld dk=%lld dv=%lld qkv=%s gate=%s alpha=%s flags=0x%x", w,
+                 (long long)s->B, (long long)s->H, (long long)s->L, (long long)s->dk, (long long)s->dv,
+                 dtype_name(s->qkv_dtype), dtype_name(s->gate_dtype), alpha_name(s->alpha_mode), flags);
+        else
+            klog("%s: no shape", w);
+    }
+    ~CallScope() { roctxRangePop(); }
+    int done(int rc) const;
+};
 
 // ---- kernel timing (kda_timing_*) --------------------------------------------
 // While enabled, each kernel launch is bracketed by two events recorded on the
@@ -209,9 +256,9 @@ Plan make_plan(const kda_shape* s, int64_t cap) {
 namespace {
 // Shared body of kda_decode_step (slots == nullptr: S is [B,H,dk,dv]) and
 // kda_decode_step_slots (S is a pool of n_slots states).
-int decode_common(const char* who, const kda_shape* s, uint32_t flags, const void* q,
-                  const void* k, const void* v, const void* log_alpha, const void* beta,
-                  float* S, int64_t n_slots, const int32_t* slots, void* o, void* hip_stream) {
+int decode_body(const char* who, const kda_shape* s, uint32_t flags, const void* q,
+                const void* k, const void* v, const void* log_alpha, const void* beta,
+                float* S, int64_t n_slots, const int32_t* slots, void* o, void* hip_stream) {
     int rc = check_shape(s, true);
     if (rc != KDA_OK) return rc;
     if (flags & ~kAllFlags) return KDA_ERR_FLAGS;
@@ -268,6 +315,12 @@ int decode_common(const char* who, const kda_shape* s, uint32_t flags, const voi
     }
     return KDA_OK;
 }
+int decode_common(const char* who, const kda_shape* s, uint32_t flags, const void* q,
+                  const void* k, const void* v, const void* log_alpha, const void* beta,
+                  float* S, int64_t n_slots, const int32_t* slots, void* o, void* hip_stream) {
+    const CallScope sc(who, s, flags);
+    return sc.done(decode_body(who, s, flags, q, k, v, log_alpha, beta, S, n_slots, slots, o, hip_stream));
+}
 }  // namespace
 
 extern "C" {
@@ -293,6 +346,19 @@ const char* kda_strerror(int status) {
 
 const char* kda_last_error(void) { return g_last_error.c_str(); }
 
+}  // extern "C"
+
+namespace {
+int CallScope::done(int rc) const {
+    if (rc != KDA_OK)
+        klog("%s: status %d: %s%s%s", who, rc, kda_strerror(rc), rc == KDA_ERR_HIP ? ": " : "",
+             rc == KDA_ERR_HIP ? g_last_error.c_str() : "");
+    return rc;
+}
+}  // namespace
+
+extern "C" {
+
 size_t kda_chunk_fwd_workspace_bytes(const kda_shape* shape) {
     if (check_shape(shape, false) != KDA_OK) return 0;
     return (size_t)make_plan(shape).ws_bytes;
@@ -315,11 +381,11 @@ namespace {
 // noalloc: kda_chunk_fwd_noalloc -- the plan is capped to the static buffer,
 // whose address replaces workspace once every host check has passed, and no
 // timing event is created.
-int chunk_common(const char* who, const kda_shape* s, uint32_t flags, const int32_t* cu,
-                 int64_t max_len, const void* q, const void* k, const void* v,
-                 const void* log_alpha, const void* beta, const float* S0, void* o,
-                 float* S_final, void* workspace, size_t workspace_bytes, void* hip_stream,
-                 bool noalloc = false) {
+int chunk_body(const char* who, const kda_shape* s, uint32_t flags, const int32_t* cu,
+               int64_t max_len, const void* q, const void* k, const void* v,
+               const void* log_alpha, const void* beta, const float* S0, void* o,
+               float* S_final, void* workspace, size_t workspace_bytes, void* hip_stream,
+               bool noalloc) {
     int rc = check_shape(s, false);
     if (rc != KDA_OK) return rc;
     if (flags & ~kAllFlags) return KDA_ERR_FLAGS;
@@ -384,6 +450,14 @@ int chunk_common(const char* who, const kda_shape* s, uint32_t flags, const int3
     // per-channel decay in bf16: the wide state pass (and the record order it reads)
     const int wv = kda::wide_slice_width((int)s->dk, (int)s->dv, qbf, s->alpha_mode, bh);
     float* s_mid = S_final ? S_final : (float*)((char*)workspace + plan.rec_area);
+    if (log_on())
+        klog("%s: %lld chunks of %d in %lld span(s) of %lld; record %lld B per chunk and head; "
+             "workspace %lld B%s; state pass %s, %d-column slices", who, (long long)plan.nchunks, plan.C,
+             (long long)plan.nspans, (long long)plan.span, (long long)plan.rec_bytes,
+             (long long)plan.ws_bytes, noalloc ? " (static buffer)" : "",
+             wv ? (wv == 16 ? "kda_inter_quad_kernel" : "kda_inter_wide_kernel")
+                : (s->alpha_mode == KDA_ALPHA_CHANNEL ? "kda_inter_kernel" : "kda_inter_scalar_kernel"),
+             wv ? wv : nv);
 
     kda::IntraParams ip;
     ip.q = q;
@@ -457,6 +531,15 @@ int chunk_common(const char* who, const kda_shape* s, uint32_t flags, const int3
     }
     return KDA_OK;
 }
+int chunk_common(const char* who, const kda_shape* s, uint32_t flags, const int32_t* cu,
+                 int64_t max_len, const void* q, const void* k, const void* v,
+                 const void* log_alpha, const void* beta, const float* S0, void* o,
+                 float* S_final, void* workspace, size_t workspace_bytes, void* hip_stream,
+                 bool noalloc = false) {
+    const CallScope sc(who, s, flags);
+    return sc.done(chunk_body(who, s, flags, cu, max_len, q, k, v, log_alpha, beta, S0, o, S_final,
+                              workspace, workspace_bytes, hip_stream, noalloc));
+}
 }  // namespace
 
 extern "C" {
@@ -500,7 +583,7 @@ size_t kda_linear_attn_fwd_workspace_bytes(const kda_shape* s) {
     return (size_t)(s->B * s->H * s->L * s->dk * elem_size(s->qkv_dtype));
 }
 
-int kda_linear_attn_fwd(const kda_shape* s, const void* q, const void* k, const void* v,
+static int kda_linear_attn_fwd_body(const kda_shape* s, const void* q, const void* k, const void* v,
                         const float* S0, const float* z0, void* o, float* S_final,
                         float* z_final, void* workspace, size_t workspace_bytes,
                         void* hip_stream) {
@@ -576,7 +659,15 @@ int kda_linear_attn_fwd(const kda_shape* s, const void* q, const void* k, const 
     return KDA_OK;
 }
 
-int kda_linear_attn_decode_step(const kda_shape* s, const void* q, const void* k,
+int kda_linear_attn_fwd(const kda_shape* s, const void* q, const void* k, const void* v,
+                        const float* S0, const float* z0, void* o, float* S_final,
+                        float* z_final, void* workspace, size_t workspace_bytes,
+                        void* hip_stream) {
+    const CallScope sc("kda_linear_attn_fwd", s, 0u);
+    return sc.done(kda_linear_attn_fwd_body(s, q, k, v, S0, z0, o, S_final, z_final, workspace, workspace_bytes, hip_stream));
+}
+
+static int kda_linear_attn_decode_step_body(const kda_shape* s, const void* q, const void* k,
                                 const void* v, float* S, float* z, void* o,
                                 void* hip_stream) {
     int rc = check_shape(s, true);
@@ -621,6 +712,13 @@ int kda_linear_attn_decode_step(const kda_shape* s, const void* q, const void* k
         return KDA_ERR_HIP;
     }
     return KDA_OK;
+}
+
+int kda_linear_attn_decode_step(const kda_shape* s, const void* q, const void* k,
+                                const void* v, float* S, float* z, void* o,
+                                void* hip_stream) {
+    const CallScope sc("kda_linear_attn_decode_step", s, 0u);
+    return sc.done(kda_linear_attn_decode_step_body(s, q, k, v, S, z, o, hip_stream));
 }
 
 size_t kda_recurrence_bwd_workspace_bytes(const kda_shape* s) {
@@ -684,7 +782,7 @@ int bwd_checks(const kda_shape* s, const void* q, const void* k, const void* v,
 
 extern "C" {
 
-int kda_recurrence_bwd(const kda_shape* s, const void* q, const void* k, const void* v,
+static int kda_recurrence_bwd_body(const kda_shape* s, const void* q, const void* k, const void* v,
                        const void* log_alpha, const void* beta, const float* S0,
                        const void* dout, const float* dS_final, float* dq, float* dk,
                        float* dv, float* dlog_alpha, float* dbeta, float* dS0, void* workspace,
@@ -730,6 +828,15 @@ int kda_recurrence_bwd(const kda_shape* s, const void* q, const void* k, const v
     return KDA_OK;
 }
 
+int kda_recurrence_bwd(const kda_shape* s, const void* q, const void* k, const void* v,
+                       const void* log_alpha, const void* beta, const float* S0,
+                       const void* dout, const float* dS_final, float* dq, float* dk,
+                       float* dv, float* dlog_alpha, float* dbeta, float* dS0, void* workspace,
+                       size_t workspace_bytes, void* hip_stream) {
+    const CallScope sc("kda_recurrence_bwd", s, 0u);
+    return sc.done(kda_recurrence_bwd_body(s, q, k, v, log_alpha, beta, S0, dout, dS_final, dq, dk, dv, dlog_alpha, dbeta, dS0, workspace, workspace_bytes, hip_stream));
+}
+
 namespace {
 // Layout of kda_recurrence_bwd_ex's workspace: the gradient kernel's own
 // area, then the fp32 preprocessed inputs and the row norms, each piece
@@ -763,7 +870,7 @@ size_t kda_recurrence_bwd_ex_workspace_bytes(const kda_shape* s, uint32_t flags)
     return (size_t)bwd_ex_plan(s).total;
 }
 
-int kda_recurrence_bwd_ex(const kda_shape* s, uint32_t flags, const void* q, const void* k,
+static int kda_recurrence_bwd_ex_body(const kda_shape* s, uint32_t flags, const void* q, const void* k,
                           const void* v, const void* log_alpha, const void* beta,
                           const float* S0, const void* dout, const float* dS_final, float* dq,
                           float* dk, float* dv, float* dlog_alpha, float* dbeta, float* dS0,
@@ -862,6 +969,15 @@ int kda_recurrence_bwd_ex(const kda_shape* s, uint32_t flags, const void* q, con
         return KDA_ERR_HIP;
     }
     return KDA_OK;
+}
+
+int kda_recurrence_bwd_ex(const kda_shape* s, uint32_t flags, const void* q, const void* k,
+                          const void* v, const void* log_alpha, const void* beta,
+                          const float* S0, const void* dout, const float* dS_final, float* dq,
+                          float* dk, float* dv, float* dlog_alpha, float* dbeta, float* dS0,
+                          void* workspace, size_t workspace_bytes, void* hip_stream) {
+    const CallScope sc("kda_recurrence_bwd_ex", s, flags);
+    return sc.done(kda_recurrence_bwd_ex_body(s, flags, q, k, v, log_alpha, beta, S0, dout, dS_final, dq, dk, dv, dlog_alpha, dbeta, dS0, workspace, workspace_bytes, hip_stream));
 }
 
 int kda_decode_step(const kda_shape* s, const void* q, const void* k, const void* v,

@@ -468,3 +468,60 @@ def test_noalloc_host_checks(lib):
     # the same heads with one decay per head fit (9 KiB records)
     none = {n: None for n in bufs()}
     assert noalloc(lib, shape(B=0), 0, none) == 0                  # empty problem
+
+
+# ---- host diagnostics (KDA_LOG) ---------------------------------------------
+_LOG_PROG = r"""
+import ctypes, sys
+sys.path.insert(0, {root!r})
+from linear_attention_sequence_kda_amd import binding
+lib = binding.library()
+B = 0x7F0000000000
+s = binding.KdaShape(1, 2, 8, 96, 128, binding.KDA_BF16, binding.KDA_F32, binding.KDA_ALPHA_CHANNEL)
+rc = lib.kda_chunk_fwd(ctypes.byref(s), B, B + (1 << 26), B + (2 << 26), B + (3 << 26), B + (4 << 26),
+                       None, B + (5 << 26), None, None, 0, None)
+rc2 = lib.kda_decode_step(None, B, B, B, B, B, B, B, None)
+print("rc", rc, rc2)
+"""
+
+
+def _run_log_prog(env_value):
+    import os
+    import subprocess
+    import sys
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    env = dict(os.environ)
+    env.pop("KDA_LOG", None)
+    if env_value is not None:
+        env["KDA_LOG"] = env_value
+    return subprocess.run([sys.executable, "-c", _LOG_PROG.format(root=root)], env=env,
+                          capture_output=True, text=True, timeout=120)
+
+
+def test_log_reports_shape_and_status_of_rejected_calls():
+    """KDA_LOG=1: each call's shape and its status when it is not KDA_OK go to
+    stderr (checked on calls the host rejects, so no GPU is needed)."""
+    p = _run_log_prog("1")
+    assert p.returncode == 0, p.stderr
+    assert "rc 2 1" in p.stdout  # KDA_ERR_SHAPE, KDA_ERR_NULL
+    lines = [x for x in p.stderr.splitlines() if x.startswith("[kda] ")]
+    assert any("kda_chunk_fwd: B=1 H=2 L=8 dk=96 dv=128 qkv=bf16 gate=f32 alpha=channel" in x for x in lines), lines
+    assert any("kda_chunk_fwd: status 2: unsupported or inconsistent shape" in x
+               for x in lines), lines
+    assert any("kda_decode_step: no shape" in x for x in lines), lines
+    assert any("kda_decode_step: status 1: a required pointer is NULL" in x
+               for x in lines), lines
+
+
+@pytest.mark.parametrize("value", [None, "0", ""])
+def test_log_is_silent_unless_enabled(value):
+    p = _run_log_prog(value)
+    assert p.returncode == 0, p.stderr
+    assert "[kda]" not in p.stderr
+
+
+def test_library_links_profiler_ranges():
+    """Every ABI call is one roctx range (rocprofiler-sdk's roctx library)."""
+    import subprocess
+    out = subprocess.run(["ldd", binding.LIB_PATH], capture_output=True, text=True).stdout
+    assert "librocprofiler-sdk-roctx" in out

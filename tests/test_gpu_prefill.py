@@ -445,3 +445,41 @@ def test_kernel_timing_counts_launches():
     for k in ("kda_intra_kernel", "kda_inter_scalar_kernel", "kda_decode_kernel"):
         assert got[k][1] > 0.0
     assert kda.timing_read("kda_intra_kernel") == (0, 0.0)
+
+
+_PLAN_LOG_PROG = r"""
+import sys
+sys.path.insert(0, {root!r})
+import torch
+import linear_attention_sequence_kda_amd as kda
+from linear_attention_sequence_kda_amd import inputs as gen
+sys.path.insert(0, {tests!r})
+from gpu_util import device_inputs
+w = gen.custom(B=1, H=3, L=200, dk=128, dv=128, qkv_dtype="bf16", gate_dtype="bf16",
+               alpha_mode="channel", seed=5)
+d = device_inputs(w, gen.prefill_inputs(w))
+kda.chunk_fwd(d["q"], d["k"], d["v"], d["log_alpha"], d["beta"], d["S0"])
+torch.cuda.synchronize()
+print("done", flush=True)
+"""
+
+
+def test_log_reports_the_prefill_plan():
+    """KDA_LOG=1 in a child process: a prefill call logs its shape and its plan
+    (chunks, spans, record bytes, the state pass and its slice width)."""
+    import os
+    import subprocess
+    import sys
+    here = os.path.dirname(os.path.abspath(__file__))
+    root = os.path.dirname(here)
+    env = dict(os.environ, KDA_LOG="1")
+    say("KDA_LOG plan line (child process)")
+    p = subprocess.run([sys.executable, "-c", _PLAN_LOG_PROG.format(root=root, tests=here)],
+                       env=env, capture_output=True, text=True, timeout=300)
+    assert p.returncode == 0 and "done" in p.stdout, p.stderr[-2000:]
+    lines = [x for x in p.stderr.splitlines() if x.startswith("[kda] ")]
+    assert any("kda_chunk_fwd: B=1 H=3 L=200 dk=128 dv=128 qkv=bf16 gate=bf16 alpha=channel" in x
+               for x in lines), lines
+    assert any("kda_chunk_fwd: 4 chunks of 64 in 1 span(s) of 4" in x and
+               "state pass kda_inter_quad_kernel, 16-column slices" in x for x in lines), lines
+    assert not any("status" in x for x in lines), lines

@@ -69,7 +69,7 @@ def test_abi_host_checks_under_asan_ubsan():
           "-fno-sanitize-recover=all"] + inc + ["-c", os.path.join(HERE, "abi_driver.c"), "-o", drv])
     exe = os.path.join(OUT, "abi_driver")
     _run([hipcc, f"--offload-arch={kbuild.ARCH}", "-Xarch_host", SAN, drv, api] + kernels +
-         ["-o", exe])
+         kbuild.link_flags() + ["-o", exe])
     p = _run([exe], env=ENV)
     assert "ok" in p.stdout
     assert "runtime error" not in p.stderr and "AddressSanitizer" not in p.stderr
