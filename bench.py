@@ -198,7 +198,7 @@ def bench_prefill(torch, kda, gen, w, steps, warmup):
     # pairs around every launch (kept out of the regions above, whose clock
     # they would slow by a few microseconds per launch)
     kern = kernel_times(torch, kda, steps, call)
-    return x, wall, call_ms, kern, wsb
+    return x, wall, call_ms, kern, wsb, (o, Sf)
 
 
 def summarize_prefill(w, wall, call_ms, kern, steps):
@@ -254,7 +254,7 @@ def summarize_prefill(w, wall, call_ms, kern, steps):
 
 def bench_prefill_leg(torch, kda, gen, w, steps, warmup):
     """A further prefill workload in the same line (same timing as the headline)."""
-    x, wall, call_ms, kern, wsb = bench_prefill(torch, kda, gen, w, steps, warmup)
+    x, wall, call_ms, kern, wsb, _ = bench_prefill(torch, kda, gen, w, steps, warmup)
     del x
     out = {"workload": w.name, "unit": "tokens/s",
            "config": {"batch": w.B, "heads": w.H, "seq_len": w.L, "d_k": w.dk, "d_v": w.dv,
@@ -431,7 +431,7 @@ def bench_linear_attention(torch, kda, gen, w, steps, warmup):
                             "GB/s": fbytes / max(fms * 1e-3, 1e-12) / 1e9}}
 
 
-def cpu_baseline(gen, w, x, min_seconds=10.0, max_passes=64):
+def cpu_baseline(gen, w, x, outs=None, min_seconds=10.0, max_passes=64):
     """The fp64 oracle (C, one worker per (head, 32-column block), all host
     cores of the job) on the workload the headline times.  Heads run a few at
     a time, so the fp64 outputs stay within a few GB of host memory; heads are
@@ -446,15 +446,20 @@ def cpu_baseline(gen, w, x, min_seconds=10.0, max_passes=64):
     group = max(1, min(N, threads // max(1, w.dv // 32)))
     log(f"cpu baseline: oracle on {w.name}, {threads} threads, {group} heads at a time")
     heads_done, dt, passes = 0, 0.0, 0
+    check = None
     while passes < max_passes and (heads_done < N or dt < min_seconds):
         h0 = heads_done % N
         hs = slice(h0, min(N, h0 + group))
         sl = {k: (None if v is None else np.ascontiguousarray(v[hs])) for k, v in xf.items()}
         t0 = time.perf_counter()
-        oracle.forward(sl["q"], sl["k"], sl["v"], sl["log_alpha"], sl["beta"], sl["S0"],
-                       qkv_dtype=w.qkv_dtype, gate_dtype=w.gate_dtype, alpha_mode=w.alpha_mode,
-                       want_o=True, threads=threads)
+        o_ref, s_ref = oracle.forward(sl["q"], sl["k"], sl["v"], sl["log_alpha"], sl["beta"],
+                                      sl["S0"], qkv_dtype=w.qkv_dtype, gate_dtype=w.gate_dtype,
+                                      alpha_mode=w.alpha_mode, want_o=True, threads=threads)
         dt += time.perf_counter() - t0
+        if check is None and outs is not None:
+            # the first heads of the timed call's own outputs against the oracle
+            # (outside the oracle's clock)
+            check = oracle_check(w, outs, hs, o_ref, s_ref)
         heads_done += hs.stop - hs.start
         passes = heads_done // N
     # heads_done x L token-heads in dt seconds; the batch's tokens/s is that
@@ -463,7 +468,44 @@ def cpu_baseline(gen, w, x, min_seconds=10.0, max_passes=64):
     return {"value": value, "unit": "tokens/s", "cores": threads, "kind": "oracle",
             "sample": f"{w.name}: {heads_done} head runs of {w.L} tokens (all {w.dv} columns, "
                       f"o and S_final; the batch has {N} heads), {group} heads at a time, "
-                      f"{dt:.2f} s of oracle compute"}
+                      f"{dt:.2f} s of oracle compute"}, check
+
+
+def oracle_check(w, outs, hs, o_ref, s_ref):
+    """Worst per-head relative error max|x - ref| / max|ref| of the timed
+    call's o and S_final on heads hs (flattened b*H + h) against the fp64
+    oracle, with the parity tests' bar for the workload's dtype."""
+    import oracle
+    o, Sf = outs
+    N = w.B * w.H
+    o_h = o.reshape(N, w.L, w.dv)[hs].float().cpu().numpy()
+    s_h = Sf.reshape(N, w.dk, w.dv)[hs].cpu().numpy()
+    e_o = float(oracle.slab_error(o_h, o_ref, 1))
+    e_s = float(oracle.slab_error(s_h, s_ref, 1))
+    tol = 2e-2 if w.qkv_dtype == "bf16" else 1e-4
+    log(f"oracle check on heads {hs.start}..{hs.stop - 1}: o {e_o:.2e}, S_final {e_s:.2e} (bar {tol})")
+    return {"heads": [hs.start, hs.stop], "o": e_o, "S_final": e_s, "bar": tol,
+            "metric": "max|x - ref| / max|ref| per head, worst head; fp64 oracle",
+            "pass": bool(e_o <= tol and e_s <= tol)}
+
+
+def run_env(torch, workloads):
+    """What the line was measured on: device, HIP and torch versions, a digest
+    of the library's sources and of this file, the input seeds."""
+    import hashlib
+    root = os.path.dirname(os.path.abspath(__file__))
+    h = hashlib.sha256()
+    csrc = os.path.join(root, "linear_attention_sequence_kda_amd", "csrc")
+    files = [os.path.join(csrc, f) for f in sorted(os.listdir(csrc))]
+    files += [os.path.join(root, "include", "kda.h"), os.path.abspath(__file__)]
+    for f in files:
+        with open(f, "rb") as fh:
+            h.update(os.path.basename(f).encode() + b"\0" + fh.read())
+    props = torch.cuda.get_device_properties(0)
+    return {"gpu": torch.cuda.get_device_name(0), "arch": getattr(props, "gcnArchName", None),
+            "cus": props.multi_processor_count, "hip": torch.version.hip, "torch": torch.__version__,
+            "sources_sha256": h.hexdigest()[:16],
+            "seeds": {w.name: w.seed for w in workloads}}
 
 
 def main():
@@ -502,7 +544,7 @@ def main():
         torch.cuda.synchronize()
         del src, dst
     w = gen.WORKLOADS[args.workload]
-    x, wall, call_ms, kern, wsb = bench_prefill(torch, kda, gen, w, args.steps, args.warmup)
+    x, wall, call_ms, kern, wsb, outs = bench_prefill(torch, kda, gen, w, args.steps, args.warmup)
     head = summarize_prefill(w, wall, call_ms, kern, args.steps)
     # the headline: K back-to-back calls between two synchronizations
     ms_per_step = wall * 1e3 / args.steps
@@ -575,7 +617,10 @@ def main():
         out["linear_attention"] = bench_linear_attention(torch, kda, gen, w2, args.steps,
                                                          args.warmup)
     if not args.no_cpu:
-        out["cpu_baseline"] = cpu_baseline(gen, w, x)
+        out["cpu_baseline"], chk = cpu_baseline(gen, w, x, outs)
+        if chk is not None:
+            out["oracle_check"] = chk
+    out["env"] = run_env(torch, [gen.WORKLOADS[n] for n in sorted({args.workload, 2, 3, 4, 5})])
     print(json.dumps(out), flush=True)
 
 
