@@ -520,7 +520,9 @@ def main():
     ap.add_argument("--no-kda", action="store_true",
                     help="skip the KDA (per-channel decay) prefill legs, workloads 3 and 4")
     ap.add_argument("--no-bwd", action="store_true",
-                    help="skip the gradient (kda_recurrence_bwd) leg")
+                    help="skip the gradient (kda_recurrence_bwd) legs")
+    ap.add_argument("--no-gdn-bwd", action="store_true",
+                    help="skip the Gated DeltaNet gradient leg (keep the KDA one)")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run one plain 256 MiB device copy (a known-size "
@@ -606,7 +608,8 @@ def main():
     # workload would not fit in HBM)
     w2 = gen.WORKLOADS[2]
     if not args.no_bwd:
-        out["gradients"] = bench_bwd(torch, kda, gen, w2, min(args.steps, 10), min(args.warmup, 2))
+        if not args.no_gdn_bwd:
+            out["gradients"] = bench_bwd(torch, kda, gen, w2, min(args.steps, 10), min(args.warmup, 2))
         if not args.no_kda:
             # the KDA workload's gradients (per-channel decay, 2 x 32 x 8192)
             out["gradients_kda"] = bench_bwd(torch, kda, gen, gen.WORKLOADS[3],
