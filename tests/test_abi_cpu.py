@@ -525,3 +525,17 @@ def test_library_links_profiler_ranges():
     import subprocess
     out = subprocess.run(["ldd", binding.LIB_PATH], capture_output=True, text=True).stdout
     assert "librocprofiler-sdk-roctx" in out
+
+
+def test_longest_sequence_accepted_one_more_rejected(lib):
+    """Kernels address one head's [L, d] rows with 32-bit byte offsets, so L is
+    capped at INT_MAX / 512 (4,194,303 tokens: fp32 rows of 128 values): that L
+    gets a plan, one more token is rejected as a shape error, before any HIP
+    call (the calls below are host checks or return before launching)."""
+    L_MAX = (2 ** 31 - 1) // 512
+    for qd in (binding.KDA_BF16, binding.KDA_F32):
+        ok = shape(B=1, H=1, L=L_MAX, qd=qd)
+        assert lib.kda_chunk_fwd_workspace_bytes(ctypes.byref(ok)) > 0
+        bad = shape(B=1, H=1, L=L_MAX + 1, qd=qd)
+        assert lib.kda_chunk_fwd_workspace_bytes(ctypes.byref(bad)) == 0
+        assert chunk(lib, bad, bufs()) == 2  # KDA_ERR_SHAPE

@@ -483,3 +483,35 @@ def test_log_reports_the_prefill_plan():
     assert any("kda_chunk_fwd: 4 chunks of 64 in 1 span(s) of 4" in x and
                "state pass kda_inter_quad_kernel, 16-column slices" in x for x in lines), lines
     assert not any("status" in x for x in lines), lines
+
+
+def test_longest_sequence_fp32():
+    """The longest sequence the ABI accepts (L = INT_MAX / 512 = 4,194,303
+    tokens, one head): with fp32 q, k, v and per-channel gates every head's
+    rows span just under 2 GiB, where the kernels' 32-bit byte offsets are at
+    their limit; the last chunk is ragged (31 of 32 tokens).  Every column of
+    o and S_final against the oracle."""
+    import torch
+    kda = _kda()
+    L = (2 ** 31 - 1) // 512
+    w = gen.custom(B=1, H=1, L=L, dk=128, dv=128, qkv_dtype="f32", gate_dtype="f32",
+                   alpha_mode="channel", seed=77)
+    say(f"longest sequence: drawing inputs L={L}")
+    x = gen.prefill_inputs(w, threads=16)
+    d = device_inputs(w, x)
+    say("longest sequence: chunk_fwd")
+    o, Sf = kda.chunk_fwd(d["q"], d["k"], d["v"], d["log_alpha"], d["beta"], d["S0"])
+    torch.cuda.synchronize()
+    del d
+    o_h = o[0].cpu().numpy().astype(np.float64)
+    s_h = to_f64(Sf[0])
+    del o
+    torch.cuda.empty_cache()
+    say("longest sequence: oracle")
+    xf = flat_heads(x, 1)
+    o_ref, S_ref = oracle_prefill(w, xf)
+    e_o = oracle.slab_error(o_h, o_ref, 1)
+    e_s = oracle.slab_error(s_h, S_ref, 1)
+    say(f"longest sequence: err o={e_o:.3e} S={e_s:.3e} (tol {TOL['f32']})")
+    assert e_o <= TOL["f32"], f"o error {e_o}"
+    assert e_s <= TOL["f32"], f"S_final error {e_s}"
