@@ -164,19 +164,21 @@ int check_shape(const kda_shape* s, bool decode) {
 // the target size, within the 256 MiB memory-side cache of an MI355X).  Between
 // spans the state goes through S_final, or through the workspace's state area
 // when no final state is wanted.  When the state pass has a workgroup for
-// every CU, spans three times as long are used: the intra-chunk grid then
-// runs more rounds of workgroups per launch, which lets their input loads
-// overlap other workgroups' work (measured on MI355X: the intra-chunk kernel
-// 20% faster per chunk, the state pass unchanged); a state pass with fewer
-// workgroups reads its records more slowly once they leave that cache, so it
-// keeps the shorter spans (on the 16-head long-context shape 128 MiB spans,
-// 96 chunks, measured 3% faster per call than 96 MiB and 3% faster than
-// 160 MiB).
+// every CU, longer spans are used: the intra-chunk grid then runs more rounds
+// of workgroups per launch, which lets their input loads overlap other
+// workgroups' work (measured on MI355X: the intra-chunk kernel 20% faster per
+// chunk, the state pass unchanged); a state pass with fewer workgroups reads
+// its records more slowly once they leave that cache, so it keeps spans whose
+// records fit there beside the rest of the traffic.  The intra-chunk kernel
+// reads its inputs with the non-temporal hint, which leaves that cache to the
+// records: on the 16-head long-context shape 160 MiB (128-chunk) spans then
+// measured 4% faster per call than 128 MiB (96 chunks, the best length with
+// ordinary loads) and 160 and 192 chunks slower again.
 #ifndef KDA_SPAN_TARGET_BYTES
-#define KDA_SPAN_TARGET_BYTES (128ll << 20)
+#define KDA_SPAN_TARGET_BYTES (160ll << 20)
 #endif
 constexpr int64_t kSpanTargetBytes = KDA_SPAN_TARGET_BYTES;
-constexpr int64_t kFullChipSpanFactor = 3;
+constexpr int64_t kFullChipSpanBytes = 384ll << 20;
 constexpr int64_t kChipCUs = 256;
 
 struct Plan {
@@ -207,7 +209,7 @@ Plan make_plan_uncapped(const kda_shape* s) {
     const int wv = kda::wide_slice_width((int)s->dk, (int)s->dv, bf, s->alpha_mode, bh);
     const int nv = wv ? wv : kda::chunk_slice_width((int)s->dk, (int)s->dv, bf, bh);
     const bool full_chip = bh * (s->dv / nv) >= kChipCUs;
-    p.span = kSpanTargetBytes * (full_chip ? kFullChipSpanFactor : 1) / per_chunk;
+    p.span = (full_chip ? kFullChipSpanBytes : kSpanTargetBytes) / per_chunk;
     if (p.span < 1) p.span = 1;
     if (p.span < p.nchunks) {
         // Round the span down so one span's intra-chunk grid (B*H*span

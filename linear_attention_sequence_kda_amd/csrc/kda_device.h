@@ -284,6 +284,22 @@ template <typename T>
 __device__ __forceinline__ T ldg(const void* base, uint32_t byte_off) {
     return *(const T*)((const char*)base + byte_off);
 }
+// The same load with the non-temporal hint: for inputs read once, which then
+// do not displace data that is read again soon (a prefill span's records in
+// the memory-side cache) from the caches.
+template <typename T>
+__device__ __forceinline__ T ldg_stream(const void* base, uint32_t byte_off) {
+    const char* p = (const char*)base + byte_off;
+    if constexpr (sizeof(T) == 16) {
+        typedef unsigned v4u __attribute__((ext_vector_type(4)));
+        return __builtin_bit_cast(T, __builtin_nontemporal_load((const v4u*)p));
+    } else if constexpr (sizeof(T) == 4) {
+        return __builtin_bit_cast(T, __builtin_nontemporal_load((const uint32_t*)p));
+    } else {
+        static_assert(sizeof(T) == 2, "16-, 4- or 2-byte loads");
+        return __builtin_bit_cast(T, __builtin_nontemporal_load((const uint16_t*)p));
+    }
+}
 
 // Buffer resource over [base, base + bytes): loads past the end return zero
 // and stores past the end are dropped by the hardware.

@@ -214,7 +214,7 @@ kda_intra_kernel(IntraParams prm) {
         idx = idx < C * VPPR ? idx : C * VPPR - 1;
         const int r = idx / VPPR, cc = (idx % VPPR) * VPIECE;
         const int rr = r < n ? r : n - 1;
-        rv[i] = ldg<uint4>(gv, (rr * DV + cc) * ESZ);
+        rv[i] = ldg_stream<uint4>(gv, (rr * DV + cc) * ESZ);
     }
 
     // ================= G: inputs into LDS, decay factors =====================
@@ -223,7 +223,9 @@ kda_intra_kernel(IntraParams prm) {
     float ky[KDA ? 16 : 1];                  // KDA: k * y, kept for K^
     // Every global load of the chunk (q and k pieces, ln(alpha), beta) is
     // issued here, before the first of them is waited for, so the inputs
-    // arrive in one memory round trip; they are used below in order.
+    // arrive in one memory round trip; they are used below in order.  The
+    // inputs are read once, with the non-temporal hint, so they leave the
+    // memory-side cache to the span's records, which the state pass reads.
     constexpr int PPR = DK / VPIECE;          // 16-byte pieces per q/k row
     constexpr int QPT = (C * PPR + NT - 1) / NT;
     uint4 gqp[KDA ? QPT : 1], gkp[QPT];
@@ -233,8 +235,8 @@ kda_intra_kernel(IntraParams prm) {
         if (idx < C * PPR) {
             const int r0 = idx / PPR, cc = (idx % PPR) * VPIECE;
             const int r = r0 < n ? r0 : n - 1;
-            if constexpr (KDA) gqp[i] = ldg<uint4>(gq, (r * DK + cc) * ESZ);
-            gkp[i] = ldg<uint4>(gk, (r * DK + cc) * ESZ);
+            if constexpr (KDA) gqp[i] = ldg_stream<uint4>(gq, (r * DK + cc) * ESZ);
+            gkp[i] = ldg_stream<uint4>(gk, (r * DK + cc) * ESZ);
         }
     }
     // raw bits of ln(alpha): KDA, thread (channel, sub-block) holds its 16
@@ -250,14 +252,14 @@ kda_intra_kernel(IntraParams prm) {
             const int r = 16 * kRc + s;
             const int rr = r < n ? r : n - 1;
             const uint32_t el = rr * DK + kc;
-            la_bits[s] = GBF ? (uint32_t)ldg<uint16_t>(gla, el * 2) : ldg<uint32_t>(gla, el * 4);
+            la_bits[s] = GBF ? (uint32_t)ldg_stream<uint16_t>(gla, el * 2) : ldg_stream<uint32_t>(gla, el * 4);
         }
     } else if constexpr (HEADG) {
         const int rr = l < n ? l : n - 1;
-        la_bits[0] = GBF ? (uint32_t)ldg<uint16_t>(gla, rr * 2) : ldg<uint32_t>(gla, rr * 4);
+        la_bits[0] = GBF ? (uint32_t)ldg_stream<uint16_t>(gla, rr * 2) : ldg_stream<uint32_t>(gla, rr * 4);
     }
     const int tb = tid < n ? tid : n - 1;
-    const uint32_t beta_bits = GBF ? (uint32_t)ldg<uint16_t>(gbeta, tb * 2) : ldg<uint32_t>(gbeta, tb * 4);
+    const uint32_t beta_bits = GBF ? (uint32_t)ldg_stream<uint16_t>(gbeta, tb * 2) : ldg_stream<uint32_t>(gbeta, tb * 4);
     if constexpr (KDA) {
         // q and k rows come in as 16-byte pieces into the tiles they are
         // rescaled in; each thread (channel, sub-block) then reads its 16
@@ -438,8 +440,8 @@ kda_intra_kernel(IntraParams prm) {
             // entry (r, j), j <= r, takes q_r k_j prod_{j<t<=r} alpha_t (and
             // k_r k_j ... for A, beta applied later) from every channel; the
             // wave's 64 channels are reduced and lane 0 adds them to LDS.
-            // The thread's 16 tokens are read again (they are in L2), so the
-            // registers of the common path are not held for this one.
+            // The thread's 16 tokens are read again from memory, so the
+            // registers of the common path are not held for this rare one.
             bool flagged = false;
 #pragma unroll
             for (int u = 0; u < DK / 64; ++u) flagged |= sFlag[R * (DK / 64) + u] != 0;
