@@ -173,12 +173,14 @@ int check_shape(const kda_shape* s, bool decode) {
 // reads its inputs with the non-temporal hint, which leaves that cache to the
 // records: on the 16-head long-context shape 160 MiB (128-chunk) spans then
 // measured 4% faster per call than 128 MiB (96 chunks, the best length with
-// ordinary loads) and 160 and 192 chunks slower again.
+// ordinary loads) and 160 and 192 chunks slower again; on 2 x 32 heads x 8192
+// tokens (full chip) 48-chunk spans (229 MB of records) beat 32, 64, 80 and
+// 128 chunks by 1-4%.
 #ifndef KDA_SPAN_TARGET_BYTES
 #define KDA_SPAN_TARGET_BYTES (160ll << 20)
 #endif
 constexpr int64_t kSpanTargetBytes = KDA_SPAN_TARGET_BYTES;
-constexpr int64_t kFullChipSpanBytes = 384ll << 20;
+constexpr int64_t kFullChipSpanBytes = 240ll << 20;
 constexpr int64_t kChipCUs = 256;
 
 struct Plan {
