@@ -195,6 +195,15 @@ kda_intra_kernel(IntraParams prm) {
     float* rRs = (float*)(rec + RL.rs);
     E* rTb = (E*)(rec + RL.tb);
 
+    // Inputs: with per-channel decay the records carry everything the state
+    // pass needs, so the inputs are read once and with the non-temporal hint
+    // (they leave the memory-side cache to the records); the scalar-decay
+    // state pass reads q, k and v again, so there they are ordinary loads.
+    auto ld_in = [](const void* base, uint32_t off, auto tag) __attribute__((always_inline)) {
+        typedef decltype(tag) T;
+        if constexpr (KDA) return ldg_stream<T>(base, off);
+        else return ldg<T>(base, off);
+    };
     auto bits_f32 = [](uint32_t u, bool half) -> float {
         return half ? __uint_as_float(u << 16) : __uint_as_float(u);
     };
@@ -214,7 +223,7 @@ kda_intra_kernel(IntraParams prm) {
         idx = idx < C * VPPR ? idx : C * VPPR - 1;
         const int r = idx / VPPR, cc = (idx % VPPR) * VPIECE;
         const int rr = r < n ? r : n - 1;
-        rv[i] = ldg_stream<uint4>(gv, (rr * DV + cc) * ESZ);
+        rv[i] = ld_in(gv, (rr * DV + cc) * ESZ, uint4{});
     }
 
     // ================= G: inputs into LDS, decay factors =====================
@@ -235,8 +244,8 @@ kda_intra_kernel(IntraParams prm) {
         if (idx < C * PPR) {
             const int r0 = idx / PPR, cc = (idx % PPR) * VPIECE;
             const int r = r0 < n ? r0 : n - 1;
-            if constexpr (KDA) gqp[i] = ldg_stream<uint4>(gq, (r * DK + cc) * ESZ);
-            gkp[i] = ldg_stream<uint4>(gk, (r * DK + cc) * ESZ);
+            if constexpr (KDA) gqp[i] = ld_in(gq, (r * DK + cc) * ESZ, uint4{});
+            gkp[i] = ld_in(gk, (r * DK + cc) * ESZ, uint4{});
         }
     }
     // raw bits of ln(alpha): KDA, thread (channel, sub-block) holds its 16
@@ -252,14 +261,14 @@ kda_intra_kernel(IntraParams prm) {
             const int r = 16 * kRc + s;
             const int rr = r < n ? r : n - 1;
             const uint32_t el = rr * DK + kc;
-            la_bits[s] = GBF ? (uint32_t)ldg_stream<uint16_t>(gla, el * 2) : ldg_stream<uint32_t>(gla, el * 4);
+            la_bits[s] = GBF ? (uint32_t)ld_in(gla, el * 2, uint16_t{}) : ld_in(gla, el * 4, uint32_t{});
         }
     } else if constexpr (HEADG) {
         const int rr = l < n ? l : n - 1;
-        la_bits[0] = GBF ? (uint32_t)ldg_stream<uint16_t>(gla, rr * 2) : ldg_stream<uint32_t>(gla, rr * 4);
+        la_bits[0] = GBF ? (uint32_t)ld_in(gla, rr * 2, uint16_t{}) : ld_in(gla, rr * 4, uint32_t{});
     }
     const int tb = tid < n ? tid : n - 1;
-    const uint32_t beta_bits = GBF ? (uint32_t)ldg_stream<uint16_t>(gbeta, tb * 2) : ldg_stream<uint32_t>(gbeta, tb * 4);
+    const uint32_t beta_bits = GBF ? (uint32_t)ld_in(gbeta, tb * 2, uint16_t{}) : ld_in(gbeta, tb * 4, uint32_t{});
     if constexpr (KDA) {
         // q and k rows come in as 16-byte pieces into the tiles they are
         // rescaled in; each thread (channel, sub-block) then reads its 16
