@@ -323,6 +323,64 @@ def bench_bwd(torch, kda, gen, w, steps, warmup):
     return out
 
 
+def chunk_grad_flops(w):
+    """Algorithmic matrix-core flops of one kda_chunk_grad_kernel launch:
+    per chunk of C = 64 tokens and head, 2 x (C^2 dv for dY = T^T du, 4 C dk dv
+    for V - K~ S, dO S^T, dY S^T and u G^T, 2 C^2 dv for dY u^T and dO u^T,
+    and 4 triangular decayed sums of C^2/2 dk each)."""
+    C = 64
+    nc = -(-w.L // C)
+    per = 2 * (C * C * w.dv + 4 * C * w.dk * w.dv + 2 * C * C * w.dv + 2 * C * C * w.dk)
+    return w.B * w.H * nc * per
+
+
+def bench_chunk_bwd(torch, kda, gen, w, steps, warmup):
+    """Chunkwise gradients (kda_chunk_bwd) of one prefill workload (dJ/do
+    given, dJ/dS_final zero): tokens/s, every kernel's time, and the
+    chunk-parallel gradient kernel against the bf16 matrix-core peak."""
+    log(f"chunkwise gradients, workload {w.name}: drawing inputs")
+    x = gen.prefill_inputs(w, threads=16)
+    d = {n: to_dev(torch, x[n], w.qkv_dtype if n in ("q", "k", "v") else w.gate_dtype)
+         for n in ("q", "k", "v", "log_alpha", "beta")}
+    S0 = to_dev(torch, x["S0"], "f32") if x["S0"] is not None else None
+    del x
+    rng = np.random.default_rng(w.seed + 101)
+    do = to_dev(torch, gen.to_storage(rng.normal(size=(w.B, w.H, w.L, w.dv)), w.qkv_dtype),
+                w.qkv_dtype)
+    wsb = kda.chunk_bwd_workspace_bytes(d["q"], d["v"], d["log_alpha"], d["beta"])
+    ws = torch.empty(wsb, dtype=torch.uint8, device="cuda:0")
+
+    def step():
+        return kda.chunk_bwd(d["q"], d["k"], d["v"], d["log_alpha"], d["beta"], S0, do, None,
+                             want_dS0=S0 is not None, workspace=ws)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        step()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    kern = kernel_times(torch, kda, steps, step)
+    per, ms = kern["kda_chunk_grad_kernel"]
+    tflops = chunk_grad_flops(w) / per / (ms * 1e-3) / 1e12
+    log(f"chunkwise gradients {w.name}: {wall * 1e3 / steps:.3f} ms/step wall; "
+        + ", ".join(f"{n} {pk:g} x {m * 1e3:.1f} us" for n, (pk, m) in kern.items()))
+    out = {"workload": w.name, "tokens_per_s": w.B * w.L / (wall / steps), "unit": "tokens/s",
+           "ms_per_step": wall * 1e3 / steps, "workspace_bytes": wsb,
+           "kernels": {n: {"launches_per_step": pk, "avg_us": m * 1e3} for n, (pk, m) in kern.items()},
+           "roofline": {"kernel": "kda_chunk_grad_kernel", "bound": "mfma", "achieved": tflops,
+                        "peak": BF16_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
+                        "frac": tflops / BF16_MFMA_PEAK_TFLOPS,
+                        "traffic": measured_traffic("kda_chunk_grad_kernel", w.name),
+                        "algorithmic_flops_per_launch": chunk_grad_flops(w) / per,
+                        "avg_kernel_us": ms * 1e3}}
+    del d, do, ws
+    torch.cuda.empty_cache()
+    return out
+
+
 def bench_decode(torch, kda, gen, w):
     log(f"decode workload {w.name}: drawing inputs")
     T = w.decode_steps
@@ -523,6 +581,8 @@ def main():
                     help="skip the gradient (kda_recurrence_bwd) legs")
     ap.add_argument("--no-gdn-bwd", action="store_true",
                     help="skip the Gated DeltaNet gradient leg (keep the KDA one)")
+    ap.add_argument("--no-chunk-bwd", action="store_true",
+                    help="skip the chunkwise gradient (kda_chunk_bwd) legs")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run one plain 256 MiB device copy (a known-size "
@@ -614,6 +674,13 @@ def main():
             # the KDA workload's gradients (per-channel decay, 2 x 32 x 8192)
             out["gradients_kda"] = bench_bwd(torch, kda, gen, gen.WORKLOADS[3],
                                              min(args.steps, 5), min(args.warmup, 1))
+    if not args.no_chunk_bwd:
+        # the same gradients in chunkwise form (bf16 operands on the matrix cores)
+        out["gradients_chunk"] = bench_chunk_bwd(torch, kda, gen, w2, args.steps,
+                                                 min(args.warmup, 2))
+        if not args.no_kda:
+            out["gradients_chunk_kda"] = bench_chunk_bwd(torch, kda, gen, gen.WORKLOADS[3],
+                                                         args.steps, min(args.warmup, 2))
     if not args.no_raw:
         out["prefill_raw_inputs"] = bench_prefill_raw(torch, kda, gen, w2, args.steps, args.warmup)
     if not args.no_linear_attention:

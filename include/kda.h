@@ -375,6 +375,40 @@ int kda_recurrence_bwd(const kda_shape* shape, const void* q, const void* k, con
 size_t kda_recurrence_bwd_workspace_bytes(const kda_shape* shape);
 
 /*
+ * The same gradients as kda_recurrence_bwd, in chunkwise form: the chunk form
+ * of "22,580: From GPT-2 to Kimi K3" (yichencityu.github.io), section 6.3 with
+ * section 9.1's per-channel decay, differentiated, which is what "Chunkwise
+ * DeltaNet makes the recurrence trainable on GPUs" ("22580: From GPT-2 to
+ * Kimi3, Explained", zharfai.com) asks of it.  The forward's intra-chunk
+ * kernel writes every chunk's factors (and T^T); a scan of the forward state
+ * pass keeps the state entering each chunk; the reverse recursion of dJ/dS,
+ * dJ/dS_in = diag(e^{g_n}) dJ/dS_out + (Q e^g)^T dO - W^T du with
+ * du = P^T dO + (K e^{g_n-g}) dJ/dS_out, runs as the same state pass over
+ * records rebuilt from the forward ones; every chunk's gradients then follow
+ * independently on the matrix cores.
+ *
+ *   Arguments, layouts, ownership and errors as for kda_recurrence_bwd, except:
+ *   qkv_dtype must be KDA_BF16 (q, k, v and dout bf16; KDA_ERR_DTYPE
+ *            otherwise); every decay mode and gate dtype is accepted.
+ *   workspace_bytes >= kda_chunk_bwd_workspace_bytes(shape): the forward's
+ *            chunk records of the whole sequence, two reverse records per
+ *            chunk, and fp32 copies of four states per chunk (about
+ *            4.1 KiB per token and head at d_k = d_v = 128); not kept after
+ *            the call's kernels end.
+ *   Arithmetic: bf16 operands on the matrix cores with fp32 accumulation, as
+ *            the forward's chunked prefill; every output is written once (no
+ *            atomics), so repeated calls give the same bits.
+ */
+int kda_chunk_bwd(const kda_shape* shape, const void* q, const void* k, const void* v,
+                  const void* log_alpha, const void* beta, const float* S0, const void* dout,
+                  const float* dS_final, float* dq, float* dk, float* dv, float* dlog_alpha,
+                  float* dbeta, float* dS0, void* workspace, size_t workspace_bytes,
+                  void* hip_stream);
+
+/* Bytes of device workspace kda_chunk_bwd needs (0 for a rejected shape or L = 0). */
+size_t kda_chunk_bwd_workspace_bytes(const kda_shape* shape);
+
+/*
  * kda_recurrence_bwd on raw inputs: flags is a set of kda_input_flags, as for
  * kda_chunk_fwd_ex, and the gradients are with respect to the raw values the
  * caller passes (through the q/k normalization, the beta sigmoid and

@@ -92,6 +92,10 @@ def library() -> ctypes.CDLL:
         lib.kda_recurrence_bwd_ex.restype = ctypes.c_int
         lib.kda_recurrence_bwd_ex_workspace_bytes.argtypes = [sp, u32]
         lib.kda_recurrence_bwd_ex_workspace_bytes.restype = sz
+        lib.kda_chunk_bwd.argtypes = [sp] + [vp] * 15 + [sz, vp]
+        lib.kda_chunk_bwd.restype = ctypes.c_int
+        lib.kda_chunk_bwd_workspace_bytes.argtypes = [sp]
+        lib.kda_chunk_bwd_workspace_bytes.restype = sz
         lib.kda_strerror.argtypes = [ctypes.c_int]
         lib.kda_strerror.restype = ctypes.c_char_p
         lib.kda_last_error.argtypes = []
@@ -161,7 +165,8 @@ def _stream(t) -> int:
 
 KERNELS = ("kda_intra_kernel", "kda_inter_kernel", "kda_inter_scalar_kernel",
            "kda_inter_wide_kernel", "kda_inter_quad_kernel", "kda_feature_map_kernel",
-           "kda_decode_kernel", "kda_bwd_kernel")
+           "kda_decode_kernel", "kda_bwd_kernel", "kda_inter_wide_scan",
+           "kda_rev_records_kernel", "kda_chunk_grad_kernel", "kda_gate_widen_kernel")
 
 
 def timing_enable(on: bool = True) -> None:
@@ -326,6 +331,49 @@ def recurrence_bwd(q, k, v, log_alpha, beta, S0, do, dS_final=None, *, want_dS0:
         _check(lib.kda_recurrence_bwd(ctypes.byref(shape), *args))
     else:
         _check(lib.kda_recurrence_bwd_ex(ctypes.byref(shape), flags, *args))
+    return dq, dk_, dv_, dla, dbeta, dS0
+
+
+def chunk_bwd_workspace_bytes(q, v, log_alpha, beta) -> int:
+    shape = _chunk_shape(q, v, log_alpha, beta)
+    return int(library().kda_chunk_bwd_workspace_bytes(ctypes.byref(shape)))
+
+
+def chunk_bwd(q, k, v, log_alpha, beta, S0, do, dS_final=None, *, want_dS0: bool = True,
+              workspace=None):
+    """Chunkwise gradients (kda_chunk_bwd): the outputs of recurrence_bwd,
+    (dq, dk, dv, dlog_alpha or None, dbeta, dS0 or None), all fp32; q, k, v
+    and do bf16.  ``workspace`` may be a uint8 GPU tensor of at least
+    chunk_bwd_workspace_bytes() bytes."""
+    torch = _torch()
+    B, H, L, dk = q.shape
+    dv = v.shape[-1]
+    for name, t in (("q", q), ("k", k), ("v", v), ("beta", beta), ("log_alpha", log_alpha),
+                    ("S0", S0), ("do", do), ("dS_final", dS_final)):
+        if t is not None:
+            _require(t, name)
+    for name, t in (("S0", S0), ("dS_final", dS_final)):
+        if t is not None and t.dtype != torch.float32:
+            raise TypeError(name + " must be float32")
+    dev, f32 = v.device, torch.float32
+    dq = torch.empty((B, H, L, dk), dtype=f32, device=dev)
+    dk_ = torch.empty((B, H, L, dk), dtype=f32, device=dev)
+    dv_ = torch.empty((B, H, L, dv), dtype=f32, device=dev)
+    dla = None if log_alpha is None else torch.empty(log_alpha.shape, dtype=f32, device=dev)
+    dbeta = torch.empty((B, H, L), dtype=f32, device=dev)
+    dS0 = torch.empty((B, H, dk, dv), dtype=f32, device=dev) if want_dS0 else None
+    shape = _chunk_shape(q, v, log_alpha, beta)
+    lib = library()
+    ws = lib.kda_chunk_bwd_workspace_bytes(ctypes.byref(shape))
+    if workspace is None:
+        workspace = torch.empty(ws, dtype=torch.uint8, device=dev) if ws else None
+    else:
+        _require(workspace, "workspace")
+    ws_given = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _check(lib.kda_chunk_bwd(ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha),
+                             _ptr(beta), _ptr(S0), _ptr(do), _ptr(dS_final), _ptr(dq), _ptr(dk_),
+                             _ptr(dv_), _ptr(dla), _ptr(dbeta), _ptr(dS0), _ptr(workspace),
+                             ws_given, _stream(v)))
     return dq, dk_, dv_, dla, dbeta, dS0
 
 

@@ -18,7 +18,7 @@ INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libkda.so")
 SOURCES = ["kda_api.cpp", "kda_intra.hip", "kda_inter.hip", "kda_inter_scalar.hip", "kda_decode.hip",
            "kda_feature.hip", "kda_bwd.hip", "kda_scratch.hip",
-           "kda_inter_wide.hip"]
+           "kda_inter_wide.hip", "kda_chunk_bwd.hip"]
 ARCH = "gfx950"
 
 

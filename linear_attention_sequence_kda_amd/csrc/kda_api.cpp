@@ -68,11 +68,14 @@ struct CallScope {
 // While enabled, each kernel launch is bracketed by two events recorded on the
 // launch's stream; the pairs are kept until read or reset.
 enum KernelId { K_INTRA = 0, K_INTER, K_INTER_SCALAR, K_DECODE, K_FEATURE, K_BWD, K_INTER_WIDE,
-                K_INTER_QUAD, K_COUNT };
+                K_INTER_QUAD, K_WIDE_SCAN, K_REV_REC, K_CHUNK_GRAD, K_GATE_WIDEN, K_COUNT };
+// (kda_inter_wide_scan is kda_inter_wide_kernel in its scan form)
 const char* const kKernelNames[K_COUNT] = {"kda_intra_kernel", "kda_inter_kernel",
                                            "kda_inter_scalar_kernel", "kda_decode_kernel",
                                            "kda_feature_map_kernel", "kda_bwd_kernel",
-                                           "kda_inter_wide_kernel", "kda_inter_quad_kernel"};
+                                           "kda_inter_wide_kernel", "kda_inter_quad_kernel",
+                                           "kda_inter_wide_scan", "kda_rev_records_kernel",
+                                           "kda_chunk_grad_kernel", "kda_gate_widen_kernel"};
 struct TimedLaunch {
     int kernel;
     hipEvent_t start, stop;
@@ -737,19 +740,15 @@ size_t kda_recurrence_bwd_workspace_bytes(const kda_shape* s) {
 namespace {
 // Every host check of kda_recurrence_bwd (no HIP call); KDA_OK when a launch
 // may follow.
+// (ws: the workspace bytes the call needs; the shape has passed check_shape)
 int bwd_checks(const kda_shape* s, const void* q, const void* k, const void* v,
                const void* log_alpha, const void* beta, const float* S0, const void* dout,
                const float* dS_final, float* dq, float* dk, float* dv, float* dlog_alpha,
-               float* dbeta, float* dS0, void* workspace, size_t workspace_bytes) {
-    int rc = check_shape(s, false);
-    if (rc != KDA_OK) return rc;
+               float* dbeta, float* dS0, void* workspace, size_t workspace_bytes, int64_t ws) {
     const int64_t bh = s->B * s->H, tok = bh * s->L;
     const int eq = elem_size(s->qkv_dtype), eg = elem_size(s->gate_dtype);
     const bool has_alpha = s->alpha_mode != KDA_ALPHA_NONE;
     const int64_t la_elems = s->alpha_mode == KDA_ALPHA_CHANNEL ? tok * s->dk : tok;
-    const int64_t ws = kda::bwd_workspace_bytes(bh, s->L, (int)s->dk, (int)s->dv);
-    // one 64-lane workgroup per (head, 8 state columns): keep the grid in int
-    if (bh > (int64_t)(INT_MAX / 64 / (s->dv / 8))) return KDA_ERR_SHAPE;
     if (bh > 0) {
         if (tok > 0) {
             if (!q || !k || !v || !beta || !dout || !dq || !dk || !dv || !dbeta)
@@ -793,8 +792,13 @@ static int kda_recurrence_bwd_body(const kda_shape* s, const void* q, const void
                        const void* dout, const float* dS_final, float* dq, float* dk,
                        float* dv, float* dlog_alpha, float* dbeta, float* dS0, void* workspace,
                        size_t workspace_bytes, void* hip_stream) {
-    int rc = bwd_checks(s, q, k, v, log_alpha, beta, S0, dout, dS_final, dq, dk, dv, dlog_alpha,
-                        dbeta, dS0, workspace, workspace_bytes);
+    int rc = check_shape(s, false);
+    if (rc != KDA_OK) return rc;
+    // one 64-lane workgroup per (head, 8 state columns): keep the grid in int
+    if (s->B * s->H > (int64_t)(INT_MAX / 64 / (s->dv / 8))) return KDA_ERR_SHAPE;
+    rc = bwd_checks(s, q, k, v, log_alpha, beta, S0, dout, dS_final, dq, dk, dv, dlog_alpha,
+                    dbeta, dS0, workspace, workspace_bytes,
+                    kda::bwd_workspace_bytes(s->B * s->H, s->L, (int)s->dk, (int)s->dv));
     if (rc != KDA_OK) return rc;
     const int64_t bh = s->B * s->H;
     const bool has_alpha = s->alpha_mode != KDA_ALPHA_NONE;
@@ -954,9 +958,10 @@ static int kda_recurrence_bwd_ex_body(const kda_shape* s, uint32_t flags, const 
     s32.qkv_dtype = KDA_F32;
     s32.gate_dtype = KDA_F32;
     // the inner call's own checks, before anything is enqueued
+    if (bh > (int64_t)(INT_MAX / 64 / (s->dv / 8))) return KDA_ERR_SHAPE;
     rc = bwd_checks(&s32, pp.qn, pp.kn, pp.v32, has_alpha ? pp.la32 : nullptr, pp.b32, S0,
                     pp.do32, dS_final, dq, dk, dv, dlog_alpha, dbeta, dS0, ws + pl.ckpt,
-                    (size_t)pl.qn);
+                    (size_t)pl.qn, kda::bwd_workspace_bytes(bh, s->L, (int)s->dk, (int)s->dv));
     if (rc != KDA_OK) return rc;
     const hipStream_t stream = (hipStream_t)hip_stream;
     hipError_t err = kda::launch_bwd_prep(pp, s->qkv_dtype == KDA_BF16,
@@ -984,6 +989,217 @@ int kda_recurrence_bwd_ex(const kda_shape* s, uint32_t flags, const void* q, con
                           void* workspace, size_t workspace_bytes, void* hip_stream) {
     const CallScope sc("kda_recurrence_bwd_ex", s, flags);
     return sc.done(kda_recurrence_bwd_ex_body(s, flags, q, k, v, log_alpha, beta, S0, dout, dS_final, dq, dk, dv, dlog_alpha, dbeta, dS0, workspace, workspace_bytes, hip_stream));
+}
+
+}  // extern "C"
+
+namespace {
+// Layout of kda_chunk_bwd's workspace (each piece rounded up to 256 bytes):
+// the forward records of every chunk, the reverse records (two per chunk),
+// T^T, the forward scan's S and u and the reverse scan's G and du per chunk,
+// and, with one decay per token or none, per-channel fp32 ln(alpha) and an
+// fp32 beta.
+struct ChunkBwdPlan {
+    int64_t recs = 0, rrecs = 0, tt = 0, S = 0, G = 0, u = 0, du = 0, la = 0, b = 0, total = 0;
+    int64_t nc = 0;
+    bool ok = false;
+};
+ChunkBwdPlan chunk_bwd_plan(const kda_shape* s) {
+    ChunkBwdPlan p;
+    const int64_t bh = s->B * s->H, C = 64;
+    p.nc = (s->L + C - 1) / C;
+    const int64_t rb = kda::rec_layout((int)s->dk, (int)s->dv, (int)C, 2, true).bytes;
+    // sizes in doubles first: a shape whose workspace passes 2^60 bytes is refused
+    const double chunks = (double)bh * (double)p.nc;
+    const double est = chunks * (3.0 * rb + C * C * 4.0 + 2.0 * s->dk * s->dv * 4 + 2.0 * C * s->dv * 4) +
+                       (double)bh * s->L * (s->dk + 1) * 4.0;
+    if (est > 1.0e18 || chunks > (double)INT_MAX) return p;
+    auto up = [](int64_t x) { return (x + 255) / 256 * 256; };
+    const int64_t nch = bh * p.nc;
+    int64_t off = 0;
+    p.recs = off; off += up(nch * rb);
+    p.rrecs = off; off += up(2 * nch * rb);
+    p.tt = off; off += up(nch * C * C * 4);
+    p.S = off; off += up(nch * s->dk * s->dv * 4);
+    p.G = off; off += up(nch * s->dk * s->dv * 4);
+    p.u = off; off += up(nch * C * s->dv * 4);
+    p.du = off; off += up(nch * C * s->dv * 4);
+    if (s->alpha_mode != KDA_ALPHA_CHANNEL) {
+        p.la = off; off += up(bh * s->L * s->dk * 4);
+        p.b = off; off += up(bh * s->L * 4);
+    }
+    p.total = nch > 0 ? off : 0;
+    p.ok = true;
+    return p;
+}
+// kda_chunk_bwd's shape check: kda_chunk_fwd's, bf16 q/k/v/do, and a plan
+int chunk_bwd_shape(const kda_shape* s, ChunkBwdPlan* plan) {
+    int rc = check_shape(s, false);
+    if (rc != KDA_OK) return rc;
+    if (s->qkv_dtype != KDA_BF16) return KDA_ERR_DTYPE;
+    *plan = chunk_bwd_plan(s);
+    return plan->ok ? KDA_OK : KDA_ERR_SHAPE;
+}
+}  // namespace
+
+extern "C" {
+
+size_t kda_chunk_bwd_workspace_bytes(const kda_shape* s) {
+    ChunkBwdPlan p;
+    if (chunk_bwd_shape(s, &p) != KDA_OK) return 0;
+    return (size_t)p.total;
+}
+
+static int kda_chunk_bwd_body(const kda_shape* s, const void* q, const void* k, const void* v,
+                              const void* log_alpha, const void* beta, const float* S0,
+                              const void* dout, const float* dS_final, float* dq, float* dk,
+                              float* dv, float* dlog_alpha, float* dbeta, float* dS0,
+                              void* workspace, size_t workspace_bytes, void* hip_stream) {
+    ChunkBwdPlan pl;
+    int rc = chunk_bwd_shape(s, &pl);
+    if (rc != KDA_OK) return rc;
+    rc = bwd_checks(s, q, k, v, log_alpha, beta, S0, dout, dS_final, dq, dk, dv, dlog_alpha,
+                    dbeta, dS0, workspace, workspace_bytes, pl.total);
+    if (rc != KDA_OK) return rc;
+    const int64_t bh = s->B * s->H;
+    if (bh == 0) return KDA_OK;
+    const hipStream_t stream = (hipStream_t)hip_stream;
+    const int dkk = (int)s->dk, dvv = (int)s->dv;
+    const int nc = (int)pl.nc;
+    char* ws = (char*)workspace;
+    auto fail = [&](hipError_t e) {
+        g_last_error = std::string("kda_chunk_bwd: ") + hipGetErrorString(e);
+        return KDA_ERR_HIP;
+    };
+    hipError_t err = hipSuccess;
+    if (nc == 0) {
+        // L = 0: dJ/dS0 is dJ/dS_final
+        if (dS0) {
+            const size_t st = (size_t)bh * dkk * dvv * 4;
+            err = dS_final ? hipMemcpyAsync(dS0, dS_final, st, hipMemcpyDeviceToDevice, stream)
+                           : hipMemsetAsync(dS0, 0, st, stream);
+        }
+        return err == hipSuccess ? KDA_OK : fail(err);
+    }
+    if (log_on())
+        klog("kda_chunk_bwd: %d chunks of 64; workspace %lld B", nc, (long long)pl.total);
+    // per-channel gates for every decay mode
+    const void* la = log_alpha;
+    const void* bt = beta;
+    int gate_bf16 = s->gate_dtype == KDA_BF16;
+    if (s->alpha_mode != KDA_ALPHA_CHANNEL) {
+        kda::GateWiden gw{};
+        gw.log_alpha = s->alpha_mode == KDA_ALPHA_HEAD ? log_alpha : nullptr;
+        gw.beta = beta;
+        gw.la = (float*)(ws + pl.la);
+        gw.b = (float*)(ws + pl.b);
+        gw.rows = bh * s->L;
+        gw.DK = dkk;
+        gw.gate_bf16 = gate_bf16;
+        err = timed_launch(K_GATE_WIDEN, stream, [&] { return kda::launch_gate_widen(gw, stream); });
+        if (err != hipSuccess) return fail(err);
+        la = gw.la;
+        bt = gw.b;
+        gate_bf16 = 0;
+    }
+    // forward records of every chunk, with T^T
+    kda::IntraParams ip{};
+    ip.q = q;
+    ip.k = k;
+    ip.v = v;
+    ip.log_alpha = la;
+    ip.beta = bt;
+    ip.ws = ws + pl.recs;
+    ip.L = s->L;
+    ip.c0 = 0;
+    ip.ncs = nc;
+    ip.BH = (int)bh;
+    ip.gate_bf16 = gate_bf16;
+    ip.wide = 1;
+    ip.tt = (float*)(ws + pl.tt);
+    err = timed_launch(K_INTRA, stream, [&] {
+        return kda::launch_intra(ip, dkk, dvv, 1, KDA_ALPHA_CHANNEL, stream);
+    });
+    if (err != hipSuccess) return fail(err);
+    // forward scan: the state entering every chunk, and its u
+    const int nv = 32;
+    kda::InterParams xp{};
+    xp.ws = ws + pl.recs;
+    xp.S_in = S0;
+    xp.S_out = nullptr;
+    xp.o = nullptr;
+    xp.L = s->L;
+    xp.c0 = 0;
+    xp.ncs = nc;
+    xp.BH = (int)bh;
+    xp.DV = dvv;
+    xp.S_all = (float*)(ws + pl.S);
+    xp.u_all = (float*)(ws + pl.u);
+    xp.scan_shift = 0;
+    xp.n_store = nc;
+    err = timed_launch(K_WIDE_SCAN, stream, [&] { return kda::launch_inter_wide_scan(xp, dkk, nv, stream); });
+    if (err != hipSuccess) return fail(err);
+    // reverse records, then the reverse scan: dJ/dS leaving every chunk and
+    // dJ/du, and dJ/dS0 at its end
+    kda::RevRecParams rp{};
+    rp.recs = ws + pl.recs;
+    rp.rrecs = ws + pl.rrecs;
+    rp.dout = dout;
+    rp.L = s->L;
+    rp.nc = nc;
+    rp.BH = (int)bh;
+    rp.DV = dvv;
+    err = timed_launch(K_REV_REC, stream, [&] { return kda::launch_rev_records(rp, dkk, stream); });
+    if (err != hipSuccess) return fail(err);
+    kda::InterParams rx = xp;
+    rx.ws = ws + pl.rrecs;
+    rx.S_in = dS_final;
+    rx.S_out = dS0;
+    rx.L = 2 * (int64_t)nc * 64;
+    rx.ncs = 2 * nc;
+    rx.S_all = (float*)(ws + pl.G);
+    rx.u_all = (float*)(ws + pl.du);
+    rx.scan_shift = 1;
+    rx.n_store = nc;
+    err = timed_launch(K_WIDE_SCAN, stream, [&] { return kda::launch_inter_wide_scan(rx, dkk, nv, stream); });
+    if (err != hipSuccess) return fail(err);
+    // every chunk's gradients
+    kda::ChunkGradParams gp{};
+    gp.q = q;
+    gp.k = k;
+    gp.v = v;
+    gp.dout = dout;
+    gp.la = la;
+    gp.beta = bt;
+    gp.tt = (const float*)(ws + pl.tt);
+    gp.S_all = (const float*)(ws + pl.S);
+    gp.u_all = (const float*)(ws + pl.u);
+    gp.G_all = (const float*)(ws + pl.G);
+    gp.du_all = (const float*)(ws + pl.du);
+    gp.dq = dq;
+    gp.dk = dk;
+    gp.dv_out = dv;
+    gp.dbeta = dbeta;
+    gp.dla = s->alpha_mode == KDA_ALPHA_NONE ? nullptr : dlog_alpha;
+    gp.L = s->L;
+    gp.nc = nc;
+    gp.BH = (int)bh;
+    gp.gate_bf16 = gate_bf16;
+    gp.dla_mode = s->alpha_mode == KDA_ALPHA_CHANNEL ? 2 : (s->alpha_mode == KDA_ALPHA_HEAD ? 1 : 0);
+    err = timed_launch(K_CHUNK_GRAD, stream, [&] { return kda::launch_chunk_grad(gp, dkk, dvv, stream); });
+    if (err != hipSuccess) return fail(err);
+    return KDA_OK;
+}
+
+int kda_chunk_bwd(const kda_shape* s, const void* q, const void* k, const void* v,
+                  const void* log_alpha, const void* beta, const float* S0, const void* dout,
+                  const float* dS_final, float* dq, float* dk, float* dv, float* dlog_alpha,
+                  float* dbeta, float* dS0, void* workspace, size_t workspace_bytes,
+                  void* hip_stream) {
+    const CallScope sc("kda_chunk_bwd", s, 0u);
+    return sc.done(kda_chunk_bwd_body(s, q, k, v, log_alpha, beta, S0, dout, dS_final, dq, dk, dv,
+                                      dlog_alpha, dbeta, dS0, workspace, workspace_bytes,
+                                      hip_stream));
 }
 
 int kda_decode_step(const kda_shape* s, const void* q, const void* k, const void* v,

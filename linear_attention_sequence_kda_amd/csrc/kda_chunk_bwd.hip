@@ -1,0 +1,777 @@
+// kda_chunk_bwd.hip -- chunkwise gradients of the gated delta rule
+// (gfx950 / MI355X): the kernels of kda_chunk_bwd besides the prefill's own
+// intra-chunk kernel and state pass.
+//
+// "Chunkwise DeltaNet makes the recurrence trainable on GPUs" ("22580: From
+// GPT-2 to Kimi3, Explained", zharfai.com) is the motivation; the pages print
+// the forward chunk form only ("22,580: From GPT-2 to Kimi K3"
+// (yichencityu.github.io) section 6.3, with section 9.1's per-channel decay),
+// so what follows is that form differentiated.  Per chunk of C tokens, with
+// g_r the chunk-relative cumulative ln(alpha) (per key channel), K~ = K e^g,
+// the forward computes
+//
+//   Y = diag(beta) (V - K~ S),  u = T Y,  T = (I + A)^-1,
+//   A_rj = beta_r sum_c k_rc k_jc e^{g_rc - g_jc} (j < r),
+//   O = (Q e^g) S + P u,  P_rj = sum_c q_rc k_jc e^{g_rc - g_jc} (j <= r),
+//   S' = diag(e^{g_n}) S + (K e^{g_n - g})^T u.
+//
+// Given G = dJ/dS' and dO, the gradient flowing into u is
+// du = P^T dO + (K e^{g_n - g}) G and the one into S is
+// dJ/dS = diag(e^{g_n}) G + (Q e^g)^T dO - W^T du (W = T diag(beta) K~).
+// That recursion runs backwards over the chunks; it has the forward state
+// pass's shape, so it runs as that pass over "reverse records" (built here):
+// chunk c becomes two record steps, (W <- K e^{g_n-g}, U <- P^T dO,
+// K^T <- -W^T, decay e^{g_n}) then (W <- 0, U <- dO, K^T <- (Q e^g)^T, decay 1),
+// taken in reverse chunk order, with the state pass's scan form keeping G and
+// du per chunk.  With S (forward scan), u, G and du per chunk, every chunk's
+// gradients are independent:
+//
+//   dY = T^T du,  dv = beta dY,  dbeta = sum_n (V - K~ S) dY + sum_c k R,
+//   dA = -(dY u^T) strictly lower,  dP = dO u^T lower,
+//   R  = decayed(dA) K,   RP = decayed(dP) K            (rows r, sums j <= r)
+//   RU = decayed^T(diag(beta) dA) K + decayed^T(dP) Q   (rows j, sums r >= j)
+//   dq = RP + e^g (dO S^T)
+//   dk = [beta R - beta e^g (dY S^T)] + [RU + e^{g_n-g} (u G^T)]
+//   dg = q dq + k ([...] - [...]) (+ the e^{g_n} terms on the last row),
+//   d ln(alpha)_t = sum_{r >= t} dg_r within the chunk,
+//
+// "decayed" being the sums with the factor e^{g_rc - g_jc} inside.  Those are
+// split at 16-token blocks: below the diagonal blocks through an anchor token
+// a between j and r (e^{g_r - g_a} and e^{g_a - g_j}, both <= 1) on bf16 MFMA,
+// the diagonal blocks summed directly in fp32.
+#include "kda_device.h"
+#include "kda_internal.h"
+
+namespace kda {
+
+// ---- gate widening ---------------------------------------------------------------
+template <bool GBF>
+__global__ void __launch_bounds__(256) kda_gate_widen_kernel(GateWiden prm) {
+    const int64_t per_row = prm.DK / 4;
+    const int64_t total = prm.rows * per_row;
+    for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < total;
+         i += (int64_t)gridDim.x * 256) {
+        const int64_t row = i / per_row;
+        const int c4 = (int)(i - row * per_row) * 4;
+        float la = 0.f;
+        if (prm.log_alpha) {
+            if constexpr (GBF) la = (float)((const bf16*)prm.log_alpha)[row];
+            else la = ((const float*)prm.log_alpha)[row];
+        }
+        *(floatx4*)(prm.la + row * prm.DK + c4) = floatx4{la, la, la, la};
+        if (c4 == 0) {
+            if constexpr (GBF) prm.b[row] = (float)((const bf16*)prm.beta)[row];
+            else prm.b[row] = ((const float*)prm.beta)[row];
+        }
+    }
+}
+
+hipError_t launch_gate_widen(const GateWiden& prm, hipStream_t stream) {
+    if (prm.rows == 0) return hipSuccess;
+    const int64_t total = prm.rows * (prm.DK / 4);
+    int64_t grid = (total + 255) / 256;
+    if (grid > 65536) grid = 65536;
+    if (prm.gate_bf16)
+        hipLaunchKernelGGL((kda_gate_widen_kernel<true>), dim3((unsigned)grid), dim3(256), 0, stream, prm);
+    else
+        hipLaunchKernelGGL((kda_gate_widen_kernel<false>), dim3((unsigned)grid), dim3(256), 0, stream, prm);
+    return hipGetLastError();
+}
+
+// ---- reverse records ---------------------------------------------------------------
+// Operand (m, 8 consecutive wide-order positions) of 16-byte piece pc of a
+// wide-order operand with K columns: row m and the k of position e.
+__device__ __forceinline__ void wide_piece(int pc, int K, int& m, int& kbase) {
+    const int lane = pc & 63, blk = pc >> 6;
+    const int kk = blk % (K >> 5), mb = blk / (K >> 5);
+    m = 16 * mb + (lane & 15);
+    kbase = 32 * kk + 4 * (lane >> 4);  // positions 0-3: kbase + e, 4-7: kbase + 16 + e - 4
+}
+__device__ __forceinline__ int wide_piece_k(int kbase, int e) { return kbase + (e & 3) + 16 * (e >> 2); }
+
+template <int DK, int DV>
+struct RevCfg {
+    static constexpr int C = 64, NT = 256;
+    static constexpr RecLayout RL = rec_layout(DK, DV, C, 2, true);
+    static constexpr int PDO = DV + 16, PPT = C + 16;  // bf16 pitches
+    static constexpr int O_W = 0, O_KT = O_W + C * DK * 2, O_QT = O_KT + DK * C * 2;
+    static constexpr int O_P = O_QT + C * DK * 2, O_DO = O_P + C * C * 2;
+    static constexpr int O_PT = O_DO + C * PDO * 2;
+    static constexpr int LDS_BYTES = O_PT + C * PPT * 2;
+    static_assert(LDS_BYTES <= 160 * 1024, "LDS budget");
+};
+
+template <int DK, int DV>
+__global__ void __launch_bounds__(256) kda_rev_records_kernel(RevRecParams prm) {
+    typedef RevCfg<DK, DV> Cfg;
+    constexpr int C = Cfg::C, NT = Cfg::NT, PDO = Cfg::PDO, PPT = Cfg::PPT;
+    constexpr RecLayout RL = Cfg::RL;
+    __shared__ __attribute__((aligned(16))) char smem[Cfg::LDS_BYTES];
+    const bf16* sW = (const bf16*)(smem + Cfg::O_W);
+    const bf16* sKt = (const bf16*)(smem + Cfg::O_KT);
+    const bf16* sQt = (const bf16*)(smem + Cfg::O_QT);
+    const bf16* sP = (const bf16*)(smem + Cfg::O_P);
+    bf16* sDO = (bf16*)(smem + Cfg::O_DO);
+    bf16* sPT = (bf16*)(smem + Cfg::O_PT);
+
+    const int tid = threadIdx.x;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int l = tid & 63;
+    const int nc = prm.nc;
+    const int bh = blockIdx.x / nc, c = blockIdx.x - bh * nc;
+    const int64_t t0 = (int64_t)c * C;
+    const int n = (int)(prm.L - t0 < C ? prm.L - t0 : C);
+    const char* src = (const char*)prm.recs + ((int64_t)bh * nc + c) * RL.bytes;
+    char* dA = (char*)prm.rrecs + ((int64_t)bh * 2 * nc + 2 * (nc - 1 - c)) * RL.bytes;
+    char* dB = dA + RL.bytes;
+
+    // the forward record's W (negated), K^T, Q~ and P as stored; dO by rows
+    auto copy_in = [&](uint32_t goff, int loff, int bytes) {
+        for (int i = tid * 16; i < bytes; i += NT * 16)
+            *(uint4*)(smem + loff + i) = *(const uint4*)(src + goff + i);
+    };
+    copy_in(RL.w, Cfg::O_W, C * DK * 2);
+    copy_in(RL.kt, Cfg::O_KT, DK * C * 2);
+    copy_in(RL.qt, Cfg::O_QT, C * DK * 2);
+    copy_in(RL.p, Cfg::O_P, C * C * 2);
+    const bf16* gdo = (const bf16*)prm.dout + ((int64_t)bh * prm.L + t0) * DV;
+    for (int i = tid; i < C * DV / 8; i += NT) {
+        const int r = i / (DV / 8), c8 = (i % (DV / 8)) * 8;
+        uint4 v = make_uint4(0u, 0u, 0u, 0u);
+        if (r < n) v = *(const uint4*)(gdo + (int64_t)r * DV + c8);
+        *(uint4*)(sDO + r * PDO + c8) = v;
+    }
+    __syncthreads();
+
+    // P^T by rows for the product P^T dO
+    for (int i = tid; i < C * C; i += NT) {
+        const int j = i / C, r = i - j * C;
+        sPT[j * PPT + r] = sP[wide_elem(r, j, C)];
+    }
+    // step A: W <- K e^{g_n - g} (the transpose of the stored K^T),
+    //         K^T <- -W^T (the stored W is already negated)
+    // step B: W <- 0, K^T <- (Q e^g)^T
+    {
+        bf16* aw = (bf16*)(dA + RL.w);
+        bf16* akt = (bf16*)(dA + RL.kt);
+        bf16* bw = (bf16*)(dB + RL.w);
+        bf16* bkt = (bf16*)(dB + RL.kt);
+        for (int pc = tid; pc < C * DK / 8; pc += NT) {
+            int m, kb;
+            wide_piece(pc, DK, m, kb);  // m: token, k: channel
+            bf16x8 v;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) v[e] = sKt[wide_elem(wide_piece_k(kb, e), m, C)];
+            *(bf16x8*)(aw + pc * 8) = v;
+            *(uint4*)(bw + pc * 8) = make_uint4(0u, 0u, 0u, 0u);
+        }
+        for (int pc = tid; pc < DK * C / 8; pc += NT) {
+            int m, kb;
+            wide_piece(pc, C, m, kb);  // m: channel, k: token
+            bf16x8 va, vb;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const int r = wide_piece_k(kb, e);
+                va[e] = sW[wide_elem(r, m, DK)];
+                vb[e] = sQt[wide_elem(r, m, DK)];
+            }
+            *(bf16x8*)(akt + pc * 8) = va;
+            *(bf16x8*)(bkt + pc * 8) = vb;
+        }
+        // decays: e^{g_n} (copied), then 1
+        const float* sgam = (const float*)(src + RL.gam);
+        for (int i = tid; i < DK; i += NT) {
+            ((float*)(dA + RL.gam))[i] = sgam[i];
+            ((float*)(dB + RL.gam))[i] = 1.f;
+        }
+        // step B's U = dO in accumulator order: element (16R + 4(l/16) + i,
+        // 16vb + l%16) at ((R * DV/32 + vb/2) * 64 + l) * 8 + (vb % 2) * 4 + i
+        bf16* but = (bf16*)(dB + RL.ut);
+        for (int t = w; t < 4 * (DV / 16); t += NT / 64) {
+            const int R = t / (DV / 16), vb = t % (DV / 16);
+            bf16x4 v;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) v[i] = sDO[(16 * R + 4 * (l >> 4) + i) * PDO + 16 * vb + (l & 15)];
+            *(bf16x4*)(but + ((R * (DV / 32) + vb / 2) * 64 + l) * 8 + (vb % 2) * 4) = v;
+        }
+    }
+    __syncthreads();
+    // step A's U = P^T dO (MFMA), stored in accumulator order
+    bf16* aut = (bf16*)(dA + RL.ut);
+    for (int t = w; t < 4 * (DV / 16); t += NT / 64) {
+        const int jb = t / (DV / 16), vb = t % (DV / 16);
+        floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+        acc = mma_block_bt<bf16>(acc, sPT + 16 * jb * PPT, PPT, sDO, PDO, 16 * vb, C);
+        st4<bf16>(aut + ((jb * (DV / 32) + vb / 2) * 64 + l) * 8 + (vb % 2) * 4, acc);
+    }
+}
+
+hipError_t launch_rev_records(const RevRecParams& prm, int dk, hipStream_t stream) {
+    if (prm.BH == 0 || prm.nc == 0) return hipSuccess;
+    const unsigned grid = (unsigned)((int64_t)prm.BH * prm.nc);
+#define KDA_CASE(DK_, DV_)                                                                     \
+    if (dk == DK_ && prm.DV == DV_) {                                                          \
+        hipLaunchKernelGGL((kda_rev_records_kernel<DK_, DV_>), dim3(grid), dim3(256), 0, stream, prm); \
+        return hipGetLastError();                                                              \
+    }
+    KDA_CASE(128, 128)
+    KDA_CASE(128, 64)
+    KDA_CASE(64, 128)
+    KDA_CASE(64, 64)
+#undef KDA_CASE
+    return hipErrorInvalidValue;
+}
+
+// ---- chunk-parallel gradients -------------------------------------------------------
+// One workgroup of 8 waves per (head, chunk).  Wave w owns the 16 key
+// channels 16w.. of every [C, dk] result (dq, dk, dg) and the 16 value
+// columns 16w.. of every [C, dv] one; a lane holds rows 16R + 4(l/16) + i,
+// column l % 16 of each 16 x 16 block (the MFMA accumulator layout).
+template <int DK_, int DV_>
+struct GradCfg {
+    static constexpr int DK = DK_, DV = DV_, C = 64, NB = 4, NT = 512;
+    static constexpr int NCBK = DK / 16, NVB = DV / 16;
+    // bf16 tiles: rows padded by 32 bytes; fp32 tiles by 16
+    static constexpr int PK = DK + 16, PV = DV + 16, PCC = C + 16;
+    static constexpr int PG = DK + 4, PT = C + 4, PDU = DV + 4;
+    static constexpr int PXU = C + 8;                        // [16][C] x~ tiles
+    static constexpr int XL = C * 16 * 2, XU = 16 * PXU * 2, XW = XL + 2 * XU;
+    // persistent areas
+    static constexpr int O_G = 0;                            // g, fp32 [C][PG]
+    static constexpr int O_K = O_G + C * PG * 4;             // k, bf16 [C][PK]
+    static constexpr int O_DA = O_K + C * PK * 2;            // dA, bf16 [C][PCC]
+    static constexpr int O_DP = O_DA + C * PCC * 2;          // dP
+    static constexpr int O_BETA = O_DP + C * PCC * 2;        // beta [C]
+    // dbeta partials, one row of C per wave for each of its two terms,
+    // summed in a fixed order at the end (the same bits on every run)
+    static constexpr int O_DB = O_BETA + C * 4;              // [2][8][C]
+    static constexpr int O_ROW = O_DB + 2 * 8 * C * 4;       // row sums [C]
+    static constexpr int O_EN = O_ROW + C * 4;               // last-row dg terms [DK]
+    static constexpr int O_PH = O_EN + DK * 4;               // phase area
+    // phase area: (0) T^T fp32 [C][PT] + du fp32 [C][PDU]; (1, 2) dY | dO |
+    // S, later u, bf16 [C or DK][PV]; (3) G bf16 [DK][PV] over dY and dO;
+    // (4) q bf16 [C][PK] + per-wave x~ tiles; (5) dg fp32 [C][PG]
+    static constexpr int PH0 = C * PT * 4 + C * PDU * 4;
+    static constexpr int PH12 = 2 * C * PV * 2 + (DK > C ? DK : C) * PV * 2;
+    static constexpr int PH4 = C * PK * 2 + NCBK * XW;
+    static constexpr int PH5 = C * PG * 4;
+    static constexpr int M01 = PH0 > PH12 ? PH0 : PH12;
+    static constexpr int M45 = PH4 > PH5 ? PH4 : PH5;
+    static constexpr int LDS_BYTES = O_PH + (M01 > M45 ? M01 : M45);
+    static_assert(DK <= 2 * C, "G fits over dY and dO");
+    static_assert(LDS_BYTES <= 160 * 1024, "LDS budget of one gfx950 CU");
+};
+
+__device__ __forceinline__ float sum16(float x) {
+#pragma unroll
+    for (int o = 1; o < 16; o <<= 1) x += __shfl_xor(x, o);
+    return x;
+}
+
+template <int DK, int DV, bool GBF>
+__global__ void __launch_bounds__(512) kda_chunk_grad_kernel(ChunkGradParams prm) {
+    typedef GradCfg<DK, DV> Cfg;
+    typedef Frag<bf16> F;
+    constexpr int C = Cfg::C, NB = Cfg::NB, NT = Cfg::NT, NCBK = Cfg::NCBK, NVB = Cfg::NVB;
+    constexpr int PK = Cfg::PK, PV = Cfg::PV, PCC = Cfg::PCC, PG = Cfg::PG, PT = Cfg::PT;
+    constexpr int PDU = Cfg::PDU, PXU = Cfg::PXU;
+    __shared__ __attribute__((aligned(16))) char smem[Cfg::LDS_BYTES];
+    float* sG = (float*)(smem + Cfg::O_G);
+    bf16* sK = (bf16*)(smem + Cfg::O_K);
+    bf16* sdA = (bf16*)(smem + Cfg::O_DA);
+    bf16* sdP = (bf16*)(smem + Cfg::O_DP);
+    float* sBeta = (float*)(smem + Cfg::O_BETA);
+    float* sDB = (float*)(smem + Cfg::O_DB);
+    float* sRow = (float*)(smem + Cfg::O_ROW);
+    float* sEn = (float*)(smem + Cfg::O_EN);
+    char* ph = smem + Cfg::O_PH;
+    float* sTT = (float*)ph;
+    float* sdu = (float*)(ph + C * PT * 4);
+    bf16* sDY = (bf16*)ph;
+    bf16* sDO = (bf16*)(ph + C * PV * 2);
+    bf16* sS = (bf16*)(ph + 2 * C * PV * 2);
+    bf16* sU = sS;
+    bf16* sGG = (bf16*)ph;
+    bf16* sQ = (bf16*)ph;
+    float* sDg = (float*)ph;
+
+    const int tid = threadIdx.x;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int l = tid & 63, lr = l & 15, q = l >> 4;
+    const int nc = prm.nc;
+    const int bh = blockIdx.x / nc, c = blockIdx.x - bh * nc;
+    const int64_t L = prm.L;
+    const int64_t t0 = (int64_t)c * C;
+    const int n = (int)(L - t0 < C ? L - t0 : C);
+    const int64_t row0 = (int64_t)bh * L + t0;
+    const int64_t xf = (int64_t)bh * nc + c;             // forward-scan entry
+    const int64_t xr = (int64_t)bh * nc + (nc - 1 - c);  // reverse-scan entry
+    auto gate_at = [&](const void* base, int64_t i) -> float {
+        if constexpr (GBF) return (float)((const bf16*)base)[i];
+        else return ((const float*)base)[i];
+    };
+
+    // ---- beta, g (cumulative ln alpha per channel), k, T^T, du --------------------
+    if (tid < C) sBeta[tid] = tid < n ? gate_at(prm.beta, row0 + tid) : 0.f;
+    for (int i = tid; i < 2 * 8 * C; i += NT) sDB[i] = 0.f;
+    {
+        // four threads per channel, 16 rows each; prefix within, offsets across
+        const int ch = tid >> 2, p = tid & 3;
+        float v[16], run = 0.f;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            const int r = 16 * p + i;
+            v[i] = (ch < DK && r < n) ? gate_at(prm.la, (row0 + r) * DK + ch) : 0.f;
+        }
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            run += v[i];
+            v[i] = run;
+        }
+        const int base = l & ~3;
+        const float s0 = __shfl(run, base), s1 = __shfl(run, base + 1), s2 = __shfl(run, base + 2);
+        const float off = (p > 0 ? s0 : 0.f) + (p > 1 ? s1 : 0.f) + (p > 2 ? s2 : 0.f);
+        if (ch < DK) {
+#pragma unroll
+            for (int i = 0; i < 16; ++i) sG[(16 * p + i) * PG + ch] = v[i] + off;
+        }
+    }
+    {
+        const float* gtt = prm.tt + xf * C * C;
+#pragma unroll
+        for (int it = 0; it < C * C / 4 / NT; ++it) {
+            const int i = tid + NT * it;
+            const int r = i / (C / 4), j4 = (i % (C / 4)) * 4;
+            *(floatx4*)(sTT + r * PT + j4) = *(const floatx4*)(gtt + r * C + j4);
+        }
+        const float* gdu = prm.du_all + xr * C * DV;
+#pragma unroll
+        for (int it = 0; it < C * DV / 4 / NT; ++it) {
+            const int i = tid + NT * it;
+            const int r = i / (DV / 4), j4 = (i % (DV / 4)) * 4;
+            *(floatx4*)(sdu + r * PDU + j4) = *(const floatx4*)(gdu + r * DV + j4);
+        }
+        const bf16* gk = (const bf16*)prm.k + row0 * DK;
+#pragma unroll
+        for (int it = 0; it < (C * DK / 8 + NT - 1) / NT; ++it) {
+            const int i = tid + NT * it;
+            if (i < C * DK / 8) {
+                const int r = i / (DK / 8), c8 = (i % (DK / 8)) * 8;
+                uint4 v = make_uint4(0u, 0u, 0u, 0u);
+                if (r < n) v = *(const uint4*)(gk + (int64_t)r * DK + c8);
+                *(uint4*)(sK + r * PK + c8) = v;
+            }
+        }
+    }
+    __syncthreads();
+
+    // ---- dY = T^T du (fp32 MFMA); dv = beta dY ------------------------------------
+    floatx4 dY[NB];
+    if (w < NVB) {
+#pragma unroll
+        for (int R = 0; R < NB; ++R) {
+            floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+            dY[R] = mma_block_bt<float>(acc, sTT + 16 * R * PT, PT, sdu, PDU, 16 * w, C);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int r = 16 * R + 4 * q + i;
+                if (r < n) prm.dv_out[(row0 + r) * DV + 16 * w + lr] = sBeta[r] * dY[R][i];
+            }
+        }
+    }
+    __syncthreads();
+
+    // ---- dY, dO and S to bf16 tiles ------------------------------------------------
+    if (w < NVB) {
+#pragma unroll
+        for (int R = 0; R < NB; ++R)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) sDY[(16 * R + 4 * q + i) * PV + 16 * w + lr] = (bf16)dY[R][i];
+    }
+    {
+        const bf16* gdo = (const bf16*)prm.dout + row0 * DV;
+#pragma unroll
+        for (int it = 0; it < (C * DV / 8 + NT - 1) / NT; ++it) {
+            const int i = tid + NT * it;
+            if (i < C * DV / 8) {
+                const int r = i / (DV / 8), c8 = (i % (DV / 8)) * 8;
+                uint4 v = make_uint4(0u, 0u, 0u, 0u);
+                if (r < n) v = *(const uint4*)(gdo + (int64_t)r * DV + c8);
+                *(uint4*)(sDO + r * PV + c8) = v;
+            }
+        }
+        const float* gS = prm.S_all + xf * DK * DV;
+#pragma unroll
+        for (int it = 0; it < (DK * DV / 8 + NT - 1) / NT; ++it) {
+            const int i = tid + NT * it;
+            if (i < DK * DV / 8) {
+                const int r = i / (DV / 8), c8 = (i % (DV / 8)) * 8;
+                const floatx4 a = *(const floatx4*)(gS + r * DV + c8);
+                const floatx4 b = *(const floatx4*)(gS + r * DV + c8 + 4);
+                bf16x8 v;
+                v[0] = (bf16)a[0]; v[1] = (bf16)a[1]; v[2] = (bf16)a[2]; v[3] = (bf16)a[3];
+                v[4] = (bf16)b[0]; v[5] = (bf16)b[1]; v[6] = (bf16)b[2]; v[7] = (bf16)b[3];
+                *(bf16x8*)(sS + r * PV + c8) = v;
+            }
+        }
+    }
+    __syncthreads();
+
+    // ---- X = V - K~ S (for dbeta), dO S^T, dY S^T ----------------------------------
+    floatx4 dq[NB], dka[NB], dkb[NB];
+#pragma unroll
+    for (int R = 0; R < NB; ++R) {
+        dq[R] = floatx4{0.f, 0.f, 0.f, 0.f};
+        dka[R] = dq[R];
+        dkb[R] = dq[R];
+    }
+    if (w < NVB) {
+        const bf16* gv = (const bf16*)prm.v + row0 * DV;
+#pragma unroll
+        for (int R = 0; R < NB; ++R) {
+            floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+            const int r = 16 * R + lr;
+#pragma unroll
+            for (int kk = 0; kk < DK / 32; ++kk) {
+                const int c0 = 32 * kk + 8 * q;
+                const bf16x8 kv = *(const bf16x8*)(sK + r * PK + c0);
+                const floatx4 g0 = *(const floatx4*)(sG + r * PG + c0);
+                const floatx4 g1 = *(const floatx4*)(sG + r * PG + c0 + 4);
+                bf16x8 a;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    a[e] = (bf16)((float)kv[e] * __expf(g0[e]));
+                    a[4 + e] = (bf16)((float)kv[4 + e] * __expf(g1[e]));
+                }
+                acc = F::mma(acc, a, load_frag_tr(sS, PV, 32 * kk, 16 * w));
+            }
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int rr = 16 * R + 4 * q + i;
+                const float vv = rr < n ? (float)gv[(int64_t)rr * DV + 16 * w + lr] : 0.f;
+                const float part = sum16((vv - acc[i]) * dY[R][i]);
+                if (lr == 0) sDB[w * C + rr] = part;
+            }
+        }
+    }
+    if (w < NCBK) {
+        const int ch = 16 * w + lr;
+#pragma unroll
+        for (int R = 0; R < NB; ++R) {
+            floatx4 z = {0.f, 0.f, 0.f, 0.f};
+            const floatx4 m1 = mma_block<bf16>(z, sDO + 16 * R * PV, PV, sS + 16 * w * PV, PV, DV);
+            const floatx4 m2 = mma_block<bf16>(z, sDY + 16 * R * PV, PV, sS + 16 * w * PV, PV, DV);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int r = 16 * R + 4 * q + i;
+                const float eg = __expf(sG[r * PG + ch]);
+                dq[R][i] = eg * m1[i];
+                dka[R][i] = -sBeta[r] * eg * m2[i];
+            }
+        }
+    }
+    __syncthreads();
+
+    // ---- u over S; dA = -(dY u^T) strictly lower, dP = dO u^T lower ---------------
+    {
+        const float* gu = prm.u_all + xf * C * DV;
+#pragma unroll
+        for (int it = 0; it < (C * DV / 8 + NT - 1) / NT; ++it) {
+            const int i = tid + NT * it;
+            if (i < C * DV / 8) {
+                const int r = i / (DV / 8), c8 = (i % (DV / 8)) * 8;
+                const floatx4 a = *(const floatx4*)(gu + r * DV + c8);
+                const floatx4 b = *(const floatx4*)(gu + r * DV + c8 + 4);
+                bf16x8 v;
+                v[0] = (bf16)a[0]; v[1] = (bf16)a[1]; v[2] = (bf16)a[2]; v[3] = (bf16)a[3];
+                v[4] = (bf16)b[0]; v[5] = (bf16)b[1]; v[6] = (bf16)b[2]; v[7] = (bf16)b[3];
+                *(bf16x8*)(sU + r * PV + c8) = v;
+            }
+        }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+        const int t = w + 8 * m;           // 32 blocks: (matrix, R, J)
+        const int mat = t >> 4, R = (t >> 2) & 3, J = t & 3;
+        bf16* dst = mat ? sdP : sdA;
+        floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+        if (J <= R) acc = mma_block<bf16>(acc, (mat ? sDO : sDY) + 16 * R * PV, PV, sU + 16 * J * PV, PV, DV);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int r = 16 * R + 4 * q + i, j = 16 * J + lr;
+            const float x = mat ? (j <= r ? acc[i] : 0.f) : (j < r ? -acc[i] : 0.f);
+            dst[r * PCC + j] = (bf16)x;
+        }
+    }
+    __syncthreads();
+
+    // ---- G over dY and dO; the e^{g_n} G.S term; u G^T -------------------------------
+    const float* gG = prm.G_all + xr * DK * DV;
+    {
+#pragma unroll
+        for (int it = 0; it < (DK * DV / 8 + NT - 1) / NT; ++it) {
+            const int i = tid + NT * it;
+            if (i < DK * DV / 8) {
+                const int r = i / (DV / 8), c8 = (i % (DV / 8)) * 8;
+                const floatx4 a = *(const floatx4*)(gG + r * DV + c8);
+                const floatx4 b = *(const floatx4*)(gG + r * DV + c8 + 4);
+                bf16x8 v;
+                v[0] = (bf16)a[0]; v[1] = (bf16)a[1]; v[2] = (bf16)a[2]; v[3] = (bf16)a[3];
+                v[4] = (bf16)b[0]; v[5] = (bf16)b[1]; v[6] = (bf16)b[2]; v[7] = (bf16)b[3];
+                *(bf16x8*)(sGG + r * PV + c8) = v;
+            }
+        }
+        // d g_n += e^{g_n} sum_j G[c][j] S[c][j]: four threads per channel
+        const float* gS = prm.S_all + xf * DK * DV;
+        const int ch = tid >> 2, p = tid & 3;
+        float d = 0.f;
+        if (ch < DK) {
+            const float* a = gG + ch * DV + p * (DV / 4);
+            const float* b = gS + ch * DV + p * (DV / 4);
+#pragma unroll
+            for (int j = 0; j < DV / 4; j += 4) {
+                const floatx4 x = *(const floatx4*)(a + j), y = *(const floatx4*)(b + j);
+                d += x[0] * y[0] + x[1] * y[1] + x[2] * y[2] + x[3] * y[3];
+            }
+        }
+        d += __shfl_xor(d, 1);
+        d += __shfl_xor(d, 2);
+        if (ch < DK && p == 0) sEn[ch] = __expf(sG[(C - 1) * PG + ch]) * d;
+    }
+    __syncthreads();
+    if (w < NCBK) {
+        const int ch = 16 * w + lr;
+        const float gn = sG[(C - 1) * PG + ch];
+        float en = 0.f;
+#pragma unroll
+        for (int R = 0; R < NB; ++R) {
+            floatx4 z = {0.f, 0.f, 0.f, 0.f};
+            const floatx4 m3 = mma_block<bf16>(z, sU + 16 * R * PV, PV, sGG + 16 * w * PV, PV, DV);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int r = 16 * R + 4 * q + i;
+                const float t = __expf(gn - sG[r * PG + ch]) * m3[i];
+                dkb[R][i] = t;
+                en += (float)sK[r * PK + ch] * t;
+            }
+        }
+        en = sum_over_lq(en);
+        if (q == 0) atomicAdd(sEn + ch, en);
+    }
+    __syncthreads();
+
+    // ---- q; the decayed products ---------------------------------------------------
+    {
+        const bf16* gq = (const bf16*)prm.q + row0 * DK;
+#pragma unroll
+        for (int it = 0; it < (C * DK / 8 + NT - 1) / NT; ++it) {
+            const int i = tid + NT * it;
+            if (i < C * DK / 8) {
+                const int r = i / (DK / 8), c8 = (i % (DK / 8)) * 8;
+                uint4 v = make_uint4(0u, 0u, 0u, 0u);
+                if (r < n) v = *(const uint4*)(gq + (int64_t)r * DK + c8);
+                *(uint4*)(sQ + r * PK + c8) = v;
+            }
+        }
+    }
+    __syncthreads();
+    bf16* xl = (bf16*)(ph + C * PK * 2 + w * Cfg::XW);  // [C][16]: lower sums' operand
+    bf16* xuk = (bf16*)((char*)xl + Cfg::XL);           // [16][PXU]: upper sums' operands
+    bf16* xuq = (bf16*)((char*)xuk + Cfg::XU);
+    const int ch = 16 * w + lr;
+#pragma unroll 1
+    for (int s = 0; s < NB; ++s) {
+        // operands anchored at token a: lower sums of row block s (a = 16s - 1,
+        // rows j < 16s), upper sums of row block s (a = 16s + 15, rows r > a)
+        if (w < NCBK) {
+            if (s >= 1) {
+                const int a = 16 * s - 1, KR = (16 * s + 31) / 32 * 32;
+                for (int e = l; e < KR * 16; e += 64) {
+                    const int j = e >> 4, cc = 16 * w + (e & 15);
+                    float x = 0.f;
+                    if (j < 16 * s) x = (float)sK[j * PK + cc] * __expf(sG[a * PG + cc] - sG[j * PG + cc]);
+                    xl[e] = (bf16)x;
+                }
+            }
+            if (s <= NB - 2) {
+                const int a = 16 * s + 15, k0 = (16 * s + 16) / 32 * 32;
+                for (int e = l; e < (C - k0) * 16; e += 64) {
+                    const int r = k0 + (e >> 4), c16 = e & 15, cc = 16 * w + c16;
+                    const float f = r > a ? __expf(sG[r * PG + cc] - sG[a * PG + cc]) : 0.f;
+                    xuk[c16 * PXU + r] = (bf16)(sBeta[r] * (float)sK[r * PK + cc] * f);
+                    xuq[c16 * PXU + r] = (bf16)((float)sQ[r * PK + cc] * f);
+                }
+            }
+        }
+        __syncthreads();
+        if (w < NCBK) {
+            // lower sums, rows 16s..: R = decayed(dA) K (j < r), RP = decayed(dP) K (j <= r)
+            {
+                const int R = s;
+                floatx4 accR = {0.f, 0.f, 0.f, 0.f}, accP = accR;
+                if (R >= 1) {
+                    const int a = 16 * R - 1, KR = (16 * R + 31) / 32 * 32;
+                    accR = mma_block_bt<bf16>(accR, sdA + 16 * R * PCC, PCC, xl, 16, 0, KR);
+                    accP = mma_block_bt<bf16>(accP, sdP + 16 * R * PCC, PCC, xl, 16, 0, KR);
+                    const float ga = sG[a * PG + ch];
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const float f = __expf(sG[(16 * R + 4 * q + i) * PG + ch] - ga);
+                        accR[i] *= f;
+                        accP[i] *= f;
+                    }
+                }
+                float gr[4];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) gr[i] = sG[(16 * R + 4 * q + i) * PG + ch];
+#pragma unroll 4
+                for (int jj = 0; jj < 16; ++jj) {
+                    const int j = 16 * R + jj;
+                    const float gj = sG[j * PG + ch], kj = (float)sK[j * PK + ch];
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const int r = 16 * R + 4 * q + i;
+                        const float e = __expf(fminf(gr[i] - gj, 0.f)) * kj;
+                        const float mp = j <= r ? 1.f : 0.f, ma = j < r ? 1.f : 0.f;
+                        accP[i] += mp * (float)sdP[r * PCC + j] * e;
+                        accR[i] += ma * (float)sdA[r * PCC + j] * e;
+                    }
+                }
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int r = 16 * R + 4 * q + i;
+                    dq[R][i] += accP[i];
+                    dka[R][i] += sBeta[r] * accR[i];
+                    const float part = sum16((float)sK[r * PK + ch] * accR[i]);
+                    if (lr == 0) sDB[(8 + w) * C + r] = part;
+                }
+            }
+            // upper sums, rows 16s..: RU = decayed^T(beta dA) K + decayed^T(dP) Q
+            {
+                const int J = s;
+                floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+                if (J <= NB - 2) {
+                    const int a = 16 * J + 15, k0 = (16 * J + 16) / 32 * 32;
+                    acc = mma_block_at<bf16>(acc, sdA + k0 * PCC, PCC, 16 * J, xuk + k0, PXU, C - k0);
+                    acc = mma_block_at<bf16>(acc, sdP + k0 * PCC, PCC, 16 * J, xuq + k0, PXU, C - k0);
+                    const float ga = sG[a * PG + ch];
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) acc[i] *= __expf(ga - sG[(16 * J + 4 * q + i) * PG + ch]);
+                }
+                float gj[4];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) gj[i] = sG[(16 * J + 4 * q + i) * PG + ch];
+#pragma unroll 4
+                for (int rr = 0; rr < 16; ++rr) {
+                    const int r = 16 * J + rr;
+                    const float g_r = sG[r * PG + ch];
+                    const float kr = sBeta[r] * (float)sK[r * PK + ch], qr = (float)sQ[r * PK + ch];
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const int j = 16 * J + 4 * q + i;
+                        const float e = __expf(fminf(g_r - gj[i], 0.f));
+                        const float mp = r >= j ? 1.f : 0.f, ma = r > j ? 1.f : 0.f;
+                        acc[i] += e * (mp * (float)sdP[r * PCC + j] * qr + ma * (float)sdA[r * PCC + j] * kr);
+                    }
+                }
+#pragma unroll
+                for (int i = 0; i < 4; ++i) dkb[J][i] += acc[i];
+            }
+        }
+        __syncthreads();
+    }
+
+    // ---- outputs: dq, dk; dg = q dq + k (dka - dkb) -> reverse sums; dbeta -----------
+    floatx4 dg[NB];
+    if (w < NCBK) {
+#pragma unroll
+        for (int R = 0; R < NB; ++R)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int r = 16 * R + 4 * q + i;
+                if (r < n) {
+                    prm.dq[(row0 + r) * DK + ch] = dq[R][i];
+                    prm.dk[(row0 + r) * DK + ch] = dka[R][i] + dkb[R][i];
+                }
+                dg[R][i] = (float)sQ[r * PK + ch] * dq[R][i] +
+                           (float)sK[r * PK + ch] * (dka[R][i] - dkb[R][i]);
+            }
+    }
+    __syncthreads();
+    if (w < NCBK) {
+#pragma unroll
+        for (int R = 0; R < NB; ++R)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) sDg[(16 * R + 4 * q + i) * PG + ch] = dg[R][i];
+    }
+    __syncthreads();
+    if (prm.dla_mode == 2) {
+        // per channel: suffix sums over rows, four threads per channel
+        const int c4 = tid >> 2, p = tid & 3;
+        float v[16], run = 0.f;
+#pragma unroll
+        for (int i = 15; i >= 0; --i) {
+            run += c4 < DK ? sDg[(16 * p + i) * PG + c4] : 0.f;
+            v[i] = run;
+        }
+        const int base = l & ~3;
+        const float t1 = __shfl(run, base + 1), t2 = __shfl(run, base + 2), t3 = __shfl(run, base + 3);
+        if (c4 < DK) {
+            const float off = (p < 1 ? t1 : 0.f) + (p < 2 ? t2 : 0.f) + (p < 3 ? t3 : 0.f) + sEn[c4];
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                const int r = 16 * p + i;
+                if (r < n) prm.dla[(row0 + r) * DK + c4] = v[i] + off;
+            }
+        }
+    } else if (prm.dla_mode == 1) {
+        // one decay per token: sum over channels, then suffix sums over rows
+        if (tid < C) {
+            float s = 0.f;
+            for (int c2 = 0; c2 < DK; ++c2) s += sDg[tid * PG + c2];
+            sRow[tid] = s;
+        }
+        __syncthreads();
+        if (w == 0) {
+            float x = sRow[l];
+            float en = 0.f;
+            for (int c2 = l; c2 < DK; c2 += 64) en += sEn[c2];
+#pragma unroll
+            for (int o = 1; o < 64; o <<= 1) en += __shfl_xor(en, o);
+#pragma unroll
+            for (int o = 1; o < 64; o <<= 1) {
+                const float y = __shfl_down(x, o);
+                if (l + o < 64) x += y;
+            }
+            if (l < n) prm.dla[row0 + l] = x + en;
+        }
+    }
+    if (tid < n) {
+        float db = 0.f;
+#pragma unroll
+        for (int v = 0; v < 2 * 8; ++v) db += sDB[v * C + tid];
+        prm.dbeta[row0 + tid] = db;
+    }
+}
+
+hipError_t launch_chunk_grad(const ChunkGradParams& prm, int dk, int dv, hipStream_t stream) {
+    if (prm.BH == 0 || prm.nc == 0) return hipSuccess;
+    const unsigned grid = (unsigned)((int64_t)prm.BH * prm.nc);
+#define KDA_CASE(DK_, DV_)                                                                     \
+    if (dk == DK_ && dv == DV_) {                                                              \
+        if (prm.gate_bf16)                                                                     \
+            hipLaunchKernelGGL((kda_chunk_grad_kernel<DK_, DV_, true>), dim3(grid), dim3(512), 0, stream, prm); \
+        else                                                                                   \
+            hipLaunchKernelGGL((kda_chunk_grad_kernel<DK_, DV_, false>), dim3(grid), dim3(512), 0, stream, prm); \
+        return hipGetLastError();                                                              \
+    }
+    KDA_CASE(128, 128)
+    KDA_CASE(128, 64)
+    KDA_CASE(64, 128)
+    KDA_CASE(64, 64)
+#undef KDA_CASE
+    return hipErrorInvalidValue;
+}
+
+}  // namespace kda

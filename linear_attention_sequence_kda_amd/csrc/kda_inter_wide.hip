@@ -96,7 +96,9 @@ __device__ __forceinline__ bf16x8 pack_frag(floatx4 a, floatx4 b) {
     return r;
 }
 
-template <class Cfg>
+// SCAN: the scan form for the chunkwise gradients (no o; the state entering
+// a chunk and the chunk's u are written out, InterParams::S_all / u_all).
+template <class Cfg, bool SCAN = false>
 __global__ void __launch_bounds__(Cfg::NT) kda_inter_wide_kernel(InterParams prm) {
     typedef bf16 E;
     typedef Frag<E> F;
@@ -227,14 +229,14 @@ __global__ void __launch_bounds__(Cfg::NT) kda_inter_wide_kernel(InterParams prm
                     DSet& nx = sets[(j + 1) % NSET];
                     put(nx, cs + 1);
                     fetch(nx, cs + 1 + NSET);
-                    store_o(cs - 1);
+                    if constexpr (!SCAN) store_o(cs - 1);
                     bare_barrier();
                     done = cs + 1 >= ncs;
                 }
             }
             if (done) break;
         }
-        if (ncs > 0) {
+        if (ncs > 0 && !SCAN) {
             asm volatile("" ::: "memory");
             store_o(ncs - 1);
         }
@@ -270,6 +272,22 @@ __global__ void __launch_bounds__(Cfg::NT) kda_inter_wide_kernel(InterParams prm
     auto sched_fence = []() { __builtin_amdgcn_sched_barrier(0); };
     for (int cs = 0; cs < ncs; ++cs) {
         const char* slot = ring + (cs & 1) * SLOT;
+        // scan form: is this chunk's entry kept, and where
+        const int64_t xg = prm.c0 + cs;
+        const bool keep = SCAN && (xg & ((1 << prm.scan_shift) - 1)) == 0;
+        const int64_t xi = xg >> prm.scan_shift;
+        if constexpr (SCAN) {
+            if (keep) {
+                float* sd = prm.S_all + ((int64_t)bh * prm.n_store + xi) * DK * DV + v0 + lr;
+#pragma unroll
+                for (int cb = 0; cb < NCB; ++cb)
+#pragma unroll
+                    for (int b = 0; b < NVBW; ++b)
+#pragma unroll
+                        for (int e = 0; e < 4; ++e)
+                            sd[(16 * cb + 4 * lq + e) * DV + 16 * (NVBW * w + b)] = Sacc[cb][b][e];
+            }
+        }
         auto piece = [&](int i) -> bf16x8 { return *(const bf16x8*)(slot + i * 1024 + l * 16); };
         // U block (R, vb) in accumulator order: two blocks per piece, the
         // slot's pieces starting at column block 2 (v0 / 32)
@@ -348,6 +366,18 @@ __global__ void __launch_bounds__(Cfg::NT) kda_inter_wide_kernel(InterParams prm
 #pragma unroll
                 for (int b = 0; b < NVBW; ++b) Sb[kk][b] = pack_frag(Sacc[2 * kk][b], Sacc[2 * kk + 1][b]);
         };
+        auto store_u = [&]() {
+            if (keep) {
+                float* ud = prm.u_all + ((int64_t)bh * prm.n_store + xi) * C * DV + v0 + lr;
+#pragma unroll
+                for (int R = 0; R < NB; ++R)
+#pragma unroll
+                    for (int b = 0; b < NVBW; ++b)
+#pragma unroll
+                        for (int e = 0; e < 4; ++e)
+                            ud[(16 * R + 4 * lq + e) * DV + 16 * (NVBW * w + b)] = u[R][b][e];
+            }
+        };
         auto pack_u = [&]() {
 #pragma unroll
             for (int kk = 0; kk < NKP; ++kk)
@@ -361,8 +391,10 @@ __global__ void __launch_bounds__(Cfg::NT) kda_inter_wide_kernel(InterParams prm
             for (int R = 0; R < NB; ++R) read_w(R);
 #pragma unroll
             for (int R = 0; R < NB; ++R) u[R][0] = u_init(R, 0);
+            if constexpr (!SCAN) {
 #pragma unroll
-            for (int R = 0; R < NB; ++R) read_q(R);
+                for (int R = 0; R < NB; ++R) read_q(R);
+            }
             sched_fence();
             pack_s();
 #pragma unroll
@@ -371,8 +403,12 @@ __global__ void __launch_bounds__(Cfg::NT) kda_inter_wide_kernel(InterParams prm
             read_k(0, NCB);
             sched_fence();
             pack_u();
+            if constexpr (SCAN) {
+                store_u();
+            } else {
 #pragma unroll
-            for (int R = 0; R < NB; ++R) o_block(R);
+                for (int R = 0; R < NB; ++R) o_block(R);
+            }
             s_update(0, NCB);
         } else {
             // two column blocks: the reads of each group go out one step
@@ -388,23 +424,33 @@ __global__ void __launch_bounds__(Cfg::NT) kda_inter_wide_kernel(InterParams prm
             u_block(0);
             u_block(1);
             sched_fence();
-            read_q(0);
-            read_q(1);
+            if constexpr (!SCAN) {
+                read_q(0);
+                read_q(1);
+            }
             sched_fence();
             u_block(2);
             u_block(3);
             sched_fence();
-            read_q(2);
-            read_q(3);
+            if constexpr (!SCAN) {
+                read_q(2);
+                read_q(3);
+            }
             sched_fence();
             pack_u();
-            o_block(0);
-            o_block(1);
+            if constexpr (SCAN) {
+                store_u();
+            } else {
+                o_block(0);
+                o_block(1);
+            }
             sched_fence();
             read_k(0, HC);
             sched_fence();
-            o_block(2);
-            o_block(3);
+            if constexpr (!SCAN) {
+                o_block(2);
+                o_block(3);
+            }
             sched_fence();
             read_k(HC, NCB);
             sched_fence();
@@ -660,11 +706,12 @@ __global__ void __launch_bounds__(Cfg::NT, 2) kda_inter_quad_kernel(InterParams 
 
 // ---- host-side dispatch -----------------------------------------------------
 
-template <int DK, int NV, int NWC, int NSET>
+template <int DK, int NV, int NWC, int NSET, bool SCAN = false>
 static hipError_t launch_wide_cfg(const InterParams& prm, hipStream_t stream) {
     typedef WideCfg<DK, NV, NWC, NSET> Cfg;
     const int total = prm.BH * prm.n_slices;
-    hipLaunchKernelGGL((kda_inter_wide_kernel<Cfg>), dim3(total), dim3(Cfg::NT), 0, stream, prm);
+    hipLaunchKernelGGL((kda_inter_wide_kernel<Cfg, SCAN>), dim3(total), dim3(Cfg::NT), 0, stream,
+                       prm);
     return hipGetLastError();
 }
 
@@ -699,6 +746,18 @@ hipError_t launch_inter_wide(InterParams prm, int dk, int nv, hipStream_t stream
     if (dk == 64 && nv == 16) return launch_quad_cfg<64, KDA_QUAD_NSET>(prm, stream);
     if (dk == 64 && nv == 32) return launch_wide_cfg<64, 32, 2, KDA_WIDE_NSET32>(prm, stream);
     if (dk == 64 && nv == 64) return launch_wide_cfg<64, 64, 2, KDA_WIDE_NSET64>(prm, stream);
+    return hipErrorInvalidValue;
+}
+
+hipError_t launch_inter_wide_scan(InterParams prm, int dk, int nv, hipStream_t stream) {
+    if (prm.BH == 0) return hipSuccess;
+    if (nv <= 0 || prm.DV % nv || !prm.S_all || !prm.u_all || prm.scan_shift < 0 ||
+        prm.scan_shift > 4)
+        return hipErrorInvalidValue;
+    prm.n_slices = prm.DV / nv;
+    // (32 columns only: the 64-column scan form would spill registers)
+    if (dk == 128 && nv == 32) return launch_wide_cfg<128, 32, 2, KDA_WIDE_NSET32, true>(prm, stream);
+    if (dk == 64 && nv == 32) return launch_wide_cfg<64, 32, 2, KDA_WIDE_NSET32, true>(prm, stream);
     return hipErrorInvalidValue;
 }
 

@@ -112,6 +112,9 @@ struct IntraParams {
     // per-channel decay, bf16: write the record in the wide state pass's
     // order (W negated, W / Q~ / P / K^T in wide_elem order)
     int wide = 0;
+    // per-channel decay: also write T^T = ((I + A)^-1)^T of every chunk,
+    // fp32 [BH][ncs][C][C] row-major (chunkwise gradients), or null
+    float* tt = nullptr;
 };
 
 struct InterParams {
@@ -136,6 +139,14 @@ struct InterParams {
     int linear_attn = 0;
     const float* z_in = nullptr;
     float* z_out = nullptr;
+    // scan form of the wide state pass (launch_inter_wide_scan): no o; the
+    // state entering chunk x and that chunk's u = U - W S are written, fp32,
+    // for every chunk x with x % 2^scan_shift == 0, as entry x >> scan_shift
+    // of S_all [BH][n_store][DK][DV] and u_all [BH][n_store][C][DV]
+    float* S_all = nullptr;
+    float* u_all = nullptr;
+    int scan_shift = 0;
+    int n_store = 0;
 };
 
 // Device address of the calling thread's current device's static buffer of
@@ -154,6 +165,9 @@ hipError_t launch_inter_wide(InterParams prm, int dk, int nv, hipStream_t stream
 // Slice width of launch_inter_wide for this problem, or 0 where that pass
 // does not apply (the other state passes run instead).
 int wide_slice_width(int dk, int dv, int qkv_bf16, int alpha_mode, int64_t BH);
+// The wide state pass in scan form (InterParams::S_all / u_all; no o), 32
+// columns per workgroup.
+hipError_t launch_inter_wide_scan(InterParams prm, int dk, int nv, hipStream_t stream);
 
 // Arguments of the decode step kernel.
 struct DecodeParams {
@@ -235,5 +249,59 @@ struct BwdPrep {
 };
 hipError_t launch_bwd_prep(const BwdPrep& prm, int qkv_bf16, int gate_bf16, hipStream_t stream);
 hipError_t launch_bwd_post(const BwdPrep& prm, hipStream_t stream);
+
+// ---- chunkwise gradients (bf16 q/k/v/do, per-channel records) ------------------
+// One decay per token (or none) widened to fp32 per-channel ln(alpha) and an
+// fp32 beta, so the per-channel kernels serve every decay mode.
+struct GateWiden {
+    const void* log_alpha;  // [rows] | unused (alpha = 1); gate type
+    const void* beta;       // [rows] gate type
+    float* la;              // [rows, DK] out
+    float* b;               // [rows] out
+    int64_t rows;
+    int DK;
+    int gate_bf16;
+};
+hipError_t launch_gate_widen(const GateWiden& prm, hipStream_t stream);
+
+// Records of the reverse state pass, built from the forward's wide records
+// and dJ/do: chunk c of head bh becomes entries 2 (nc - 1 - c) and
+// 2 (nc - 1 - c) + 1 of [BH][2 nc] records of the same layout.
+struct RevRecParams {
+    const void* recs;       // [BH][nc] forward records (wide order)
+    void* rrecs;            // [BH][2 nc]
+    const void* dout;       // [BH, L, DV] bf16
+    int64_t L;
+    int nc;
+    int BH;
+    int DV;
+};
+hipError_t launch_rev_records(const RevRecParams& prm, int dk, hipStream_t stream);
+
+// Chunk-parallel gradients from the two scans' per-chunk states.
+struct ChunkGradParams {
+    const void* q;          // [BH, L, DK] bf16
+    const void* k;
+    const void* v;          // [BH, L, DV] bf16
+    const void* dout;       // [BH, L, DV] bf16
+    const void* la;         // [BH, L, DK] per-channel ln(alpha), gate type
+    const void* beta;       // [BH, L] gate type
+    const float* tt;        // [BH][nc][C][C] T^T
+    const float* S_all;     // [BH][nc][DK][DV] state entering each chunk
+    const float* u_all;     // [BH][nc][C][DV] u of each chunk
+    const float* G_all;     // [BH][nc][DK][DV] dJ/dS leaving each chunk
+    const float* du_all;    // [BH][nc][C][DV] dJ/du of each chunk
+    float* dq;              // [BH, L, DK]
+    float* dk;
+    float* dv_out;          // [BH, L, DV]
+    float* dbeta;           // [BH, L]
+    float* dla;             // [BH, L, DK] (dla_mode 2), [BH, L] (1), unused (0)
+    int64_t L;
+    int nc;
+    int BH;
+    int gate_bf16;
+    int dla_mode;
+};
+hipError_t launch_chunk_grad(const ChunkGradParams& prm, int dk, int dv, hipStream_t stream);
 
 }  // namespace kda

@@ -730,6 +730,18 @@ kda_intra_kernel(IntraParams prm) {
         __syncthreads();
     }
 
+    // T^T for the chunkwise gradients: sA holds it on and above the diagonal
+    // blocks (below them it still holds A)
+    if constexpr (!THIN) {
+        if (prm.tt) {
+            float* dst = prm.tt + ((int64_t)bh * prm.ncs + cs) * C * C;
+            for (int i = tid; i < C * C; i += NT) {
+                const int r = i / C, j = i - r * C;
+                dst[i] = (r >> 4) <= (j >> 4) ? sA[r * PA + j] : 0.f;
+            }
+        }
+    }
+
     // ================= WU: W = T' K~ and U = T diag(beta) V ==================
     // Scalar decay: T diag(beta) goes out as it is.
     if constexpr (THIN) {

@@ -368,6 +368,57 @@ def test_recurrence_bwd_host_checks(lib):
     assert bwd(lib, shape(B=0), none) == 0                           # empty problem
 
 
+def cbwd(lib, s, b, wsb=1 << 30):
+    return lib.kda_chunk_bwd(ctypes.byref(s) if s is not None else None, b["q"], b["k"], b["v"],
+                             b["la"], b["beta"], b["S0"], b["do"], b["dSf"], b["dq"], b["dk"],
+                             b["dv"], b["dla"], b["dbeta"], b["dS0"], b["ws"], wsb, None)
+
+
+def test_chunk_bwd_workspace_size(lib):
+    """Per chunk of 64 tokens and head: the forward record, two reverse
+    records, T^T (fp32 64 x 64), the states S and G (fp32 dk x dv) and u, du
+    (fp32 64 x dv); one decay per token (or none) adds per-channel fp32
+    ln(alpha) and an fp32 beta per token."""
+    up = lambda x: (x + 255) // 256 * 256
+    rec = 64 * 128 * 2 * 4 + 64 * 64 * 2 + 1024     # W, U, K^T, Q~ (bf16), P, decays
+    nch = 2 * 3 * 2                                   # B H ceil(100 / 64)
+    want = (up(nch * rec) + up(2 * nch * rec) + up(nch * 64 * 64 * 4) +
+            2 * up(nch * 128 * 128 * 4) + 2 * up(nch * 64 * 128 * 4))
+    assert lib.kda_chunk_bwd_workspace_bytes(ctypes.byref(shape())) == want
+    head = shape(mode=binding.KDA_ALPHA_HEAD)
+    assert lib.kda_chunk_bwd_workspace_bytes(ctypes.byref(head)) == \
+        want + up(600 * 128 * 4) + up(600 * 4)
+    assert lib.kda_chunk_bwd_workspace_bytes(ctypes.byref(shape(qd=binding.KDA_F32))) == 0
+    assert lib.kda_chunk_bwd_workspace_bytes(ctypes.byref(shape(L=0))) == 0
+    assert lib.kda_chunk_bwd_workspace_bytes(None) == 0
+
+
+def test_chunk_bwd_host_checks(lib):
+    s = shape()
+    ws = lib.kda_chunk_bwd_workspace_bytes(ctypes.byref(s))
+    assert cbwd(lib, None, bwd_bufs()) == 1
+    assert cbwd(lib, shape(qd=binding.KDA_F32), bwd_bufs()) == 3      # bf16 q/k/v/do only
+    assert cbwd(lib, s, bwd_bufs(), wsb=ws - 1) == 6
+    for name in ["q", "k", "v", "la", "beta", "do", "dq", "dk", "dv", "dla", "dbeta", "ws"]:
+        b = bwd_bufs()
+        b[name] = None
+        assert cbwd(lib, s, b) == 1, name
+    for name in bwd_bufs():
+        b = bwd_bufs()
+        b[name] += 8
+        assert cbwd(lib, s, b) == 5, name
+    for out, inp in [("dq", "q"), ("dv", "do"), ("dS0", "dSf"), ("dk", "dq"), ("ws", "dla"),
+                     ("dbeta", "beta"), ("dS0", "ws")]:
+        b = bwd_bufs()
+        b[out] = b[inp] + 1024
+        assert cbwd(lib, s, b) == 7, (out, inp)
+    bad = shape()
+    bad.dv = 96
+    assert cbwd(lib, bad, bwd_bufs()) == 2
+    none = {n: None for n in bwd_bufs()}
+    assert cbwd(lib, shape(B=0), none) == 0
+
+
 def bwd_ex(lib, s, flags, b, wsb=1 << 30):
     return lib.kda_recurrence_bwd_ex(ctypes.byref(s) if s is not None else None, flags, b["q"],
                                      b["k"], b["v"], b["la"], b["beta"], b["S0"], b["do"],
