@@ -1011,7 +1011,7 @@ ChunkBwdPlan chunk_bwd_plan(const kda_shape* s) {
     const int64_t rb = kda::rec_layout((int)s->dk, (int)s->dv, (int)C, 2, true).bytes;
     // sizes in doubles first: a shape whose workspace passes 2^60 bytes is refused
     const double chunks = (double)bh * (double)p.nc;
-    const double est = chunks * (3.0 * rb + C * C * 4.0 + 2.0 * s->dk * s->dv * 4 + 2.0 * C * s->dv * 4) +
+    const double est = chunks * (3.0 * rb + C * C * 4.0 + 2.0 * s->dk * s->dv * 4 + 2.0 * C * s->dv * 2) +
                        (double)bh * s->L * (s->dk + 1) * 4.0;
     if (est > 1.0e18 || chunks > (double)INT_MAX) return p;
     auto up = [](int64_t x) { return (x + 255) / 256 * 256; };
@@ -1022,8 +1022,8 @@ ChunkBwdPlan chunk_bwd_plan(const kda_shape* s) {
     p.tt = off; off += up(nch * C * C * 4);
     p.S = off; off += up(nch * s->dk * s->dv * 4);
     p.G = off; off += up(nch * s->dk * s->dv * 4);
-    p.u = off; off += up(nch * C * s->dv * 4);
-    p.du = off; off += up(nch * C * s->dv * 4);
+    p.u = off; off += up(nch * C * s->dv * 2);
+    p.du = off; off += up(nch * C * s->dv * 2);
     if (s->alpha_mode != KDA_ALPHA_CHANNEL) {
         p.la = off; off += up(bh * s->L * s->dk * 4);
         p.b = off; off += up(bh * s->L * 4);
@@ -1134,7 +1134,7 @@ static int kda_chunk_bwd_body(const kda_shape* s, const void* q, const void* k, 
     xp.BH = (int)bh;
     xp.DV = dvv;
     xp.S_all = (float*)(ws + pl.S);
-    xp.u_all = (float*)(ws + pl.u);
+    xp.u_all = ws + pl.u;
     xp.scan_shift = 0;
     xp.n_store = nc;
     err = timed_launch(K_WIDE_SCAN, stream, [&] { return kda::launch_inter_wide_scan(xp, dkk, nv, stream); });
@@ -1158,7 +1158,7 @@ static int kda_chunk_bwd_body(const kda_shape* s, const void* q, const void* k, 
     rx.L = 2 * (int64_t)nc * 64;
     rx.ncs = 2 * nc;
     rx.S_all = (float*)(ws + pl.G);
-    rx.u_all = (float*)(ws + pl.du);
+    rx.u_all = ws + pl.du;
     rx.scan_shift = 1;
     rx.n_store = nc;
     err = timed_launch(K_WIDE_SCAN, stream, [&] { return kda::launch_inter_wide_scan(rx, dkk, nv, stream); });
@@ -1173,9 +1173,9 @@ static int kda_chunk_bwd_body(const kda_shape* s, const void* q, const void* k, 
     gp.beta = bt;
     gp.tt = (const float*)(ws + pl.tt);
     gp.S_all = (const float*)(ws + pl.S);
-    gp.u_all = (const float*)(ws + pl.u);
+    gp.u_all = ws + pl.u;
     gp.G_all = (const float*)(ws + pl.G);
-    gp.du_all = (const float*)(ws + pl.du);
+    gp.du_all = ws + pl.du;
     gp.dq = dq;
     gp.dk = dk;
     gp.dv_out = dv;

@@ -36,9 +36,13 @@
 //   d ln(alpha)_t = sum_{r >= t} dg_r within the chunk,
 //
 // "decayed" being the sums with the factor e^{g_rc - g_jc} inside.  Those are
-// split at 16-token blocks: below the diagonal blocks through an anchor token
-// a between j and r (e^{g_r - g_a} and e^{g_a - g_j}, both <= 1) on bf16 MFMA,
-// the diagonal blocks summed directly in fp32.
+// split at 16-token blocks through an anchor token a per block (e^{g_r - g_a}
+// on the result, e^{g_a - g_j} on the operand): below the diagonal block both
+// factors are <= 1; a diagonal block whose total decay is at least -60 in
+// every channel of a wave joins the same bf16 MFMA sum (its factors stay
+// within e^60), a stronger one is summed directly in fp32.  dP's diagonal
+// (no decay) stays out of the sums: its terms cancel exactly in dg and are
+// added to dq and dk alone.
 #include "kda_device.h"
 #include "kda_internal.h"
 
@@ -234,19 +238,20 @@ struct GradCfg {
     // bf16 tiles: rows padded by 32 bytes; fp32 tiles by 16
     static constexpr int PK = DK + 16, PV = DV + 16, PCC = C + 16;
     static constexpr int PG = DK + 4, PT = C + 4, PDU = DV + 4;
-    static constexpr int PXU = C + 8;                        // [16][C] x~ tiles
-    static constexpr int XL = C * 16 * 2, XU = 16 * PXU * 2, XW = XL + 2 * XU;
+    // per-wave operands of the decayed sums: [C][16] bf16 row-major tiles
+    static constexpr int XL = C * 16 * 2, XW = 3 * XL;
     // persistent areas
     static constexpr int O_G = 0;                            // g, fp32 [C][PG]
     static constexpr int O_K = O_G + C * PG * 4;             // k, bf16 [C][PK]
     static constexpr int O_DA = O_K + C * PK * 2;            // dA, bf16 [C][PCC]
     static constexpr int O_DP = O_DA + C * PCC * 2;          // dP
     static constexpr int O_BETA = O_DP + C * PCC * 2;        // beta [C]
-    // dbeta partials, one row of C per wave for each of its two terms,
+    // dbeta partials, one row of C per wave for each of its three terms,
     // summed in a fixed order at the end (the same bits on every run)
-    static constexpr int O_DB = O_BETA + C * 4;              // [2][8][C]
-    static constexpr int O_ROW = O_DB + 2 * 8 * C * 4;       // row sums [C]
-    static constexpr int O_EN = O_ROW + C * 4;               // last-row dg terms [DK]
+    static constexpr int O_DB = O_BETA + C * 4;              // [3][8][C]
+    static constexpr int O_ROW = O_DB + 3 * 8 * C * 4;       // row sums [C]
+    static constexpr int O_PD = O_ROW + C * 4;               // diagonal of dP [C]
+    static constexpr int O_EN = O_PD + C * 4;                // last-row dg terms [DK]
     static constexpr int O_PH = O_EN + DK * 4;               // phase area
     // phase area: (0) T^T fp32 [C][PT] + du fp32 [C][PDU]; (1, 2) dY | dO |
     // S, later u, bf16 [C or DK][PV]; (3) G bf16 [DK][PV] over dY and dO;
@@ -274,7 +279,7 @@ __global__ void __launch_bounds__(512) kda_chunk_grad_kernel(ChunkGradParams prm
     typedef Frag<bf16> F;
     constexpr int C = Cfg::C, NB = Cfg::NB, NT = Cfg::NT, NCBK = Cfg::NCBK, NVB = Cfg::NVB;
     constexpr int PK = Cfg::PK, PV = Cfg::PV, PCC = Cfg::PCC, PG = Cfg::PG, PT = Cfg::PT;
-    constexpr int PDU = Cfg::PDU, PXU = Cfg::PXU;
+    constexpr int PDU = Cfg::PDU;
     __shared__ __attribute__((aligned(16))) char smem[Cfg::LDS_BYTES];
     float* sG = (float*)(smem + Cfg::O_G);
     bf16* sK = (bf16*)(smem + Cfg::O_K);
@@ -283,6 +288,7 @@ __global__ void __launch_bounds__(512) kda_chunk_grad_kernel(ChunkGradParams prm
     float* sBeta = (float*)(smem + Cfg::O_BETA);
     float* sDB = (float*)(smem + Cfg::O_DB);
     float* sRow = (float*)(smem + Cfg::O_ROW);
+    float* sPd = (float*)(smem + Cfg::O_PD);
     float* sEn = (float*)(smem + Cfg::O_EN);
     char* ph = smem + Cfg::O_PH;
     float* sTT = (float*)ph;
@@ -313,7 +319,7 @@ __global__ void __launch_bounds__(512) kda_chunk_grad_kernel(ChunkGradParams prm
 
     // ---- beta, g (cumulative ln alpha per channel), k, T^T, du --------------------
     if (tid < C) sBeta[tid] = tid < n ? gate_at(prm.beta, row0 + tid) : 0.f;
-    for (int i = tid; i < 2 * 8 * C; i += NT) sDB[i] = 0.f;
+    for (int i = tid; i < 3 * 8 * C; i += NT) sDB[i] = 0.f;
     {
         // four threads per channel, 16 rows each; prefix within, offsets across
         const int ch = tid >> 2, p = tid & 3;
@@ -344,12 +350,14 @@ __global__ void __launch_bounds__(512) kda_chunk_grad_kernel(ChunkGradParams prm
             const int r = i / (C / 4), j4 = (i % (C / 4)) * 4;
             *(floatx4*)(sTT + r * PT + j4) = *(const floatx4*)(gtt + r * C + j4);
         }
-        const float* gdu = prm.du_all + xr * C * DV;
+        const bf16* gdu = (const bf16*)prm.du_all + xr * C * DV;
 #pragma unroll
-        for (int it = 0; it < C * DV / 4 / NT; ++it) {
+        for (int it = 0; it < C * DV / 8 / NT; ++it) {
             const int i = tid + NT * it;
-            const int r = i / (DV / 4), j4 = (i % (DV / 4)) * 4;
-            *(floatx4*)(sdu + r * PDU + j4) = *(const floatx4*)(gdu + r * DV + j4);
+            const int r = i / (DV / 8), j8 = (i % (DV / 8)) * 8;
+            const bf16x8 v = *(const bf16x8*)(gdu + r * DV + j8);
+            *(floatx4*)(sdu + r * PDU + j8) = floatx4{(float)v[0], (float)v[1], (float)v[2], (float)v[3]};
+            *(floatx4*)(sdu + r * PDU + j8 + 4) = floatx4{(float)v[4], (float)v[5], (float)v[6], (float)v[7]};
         }
         const bf16* gk = (const bf16*)prm.k + row0 * DK;
 #pragma unroll
@@ -381,7 +389,18 @@ __global__ void __launch_bounds__(512) kda_chunk_grad_kernel(ChunkGradParams prm
     }
     __syncthreads();
 
-    // ---- dY, dO and S to bf16 tiles ------------------------------------------------
+    // ---- dY, dO and S to bf16 tiles; this wave's v -----------------------------------
+    float vrow[NB][4];
+    if (w < NVB) {
+        const bf16* gv = (const bf16*)prm.v + row0 * DV;
+#pragma unroll
+        for (int R = 0; R < NB; ++R)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int rr = 16 * R + 4 * q + i;
+                vrow[R][i] = rr < n ? (float)gv[(int64_t)rr * DV + 16 * w + lr] : 0.f;
+            }
+    }
     if (w < NVB) {
 #pragma unroll
         for (int R = 0; R < NB; ++R)
@@ -408,16 +427,16 @@ __global__ void __launch_bounds__(512) kda_chunk_grad_kernel(ChunkGradParams prm
                 const int r = i / (DV / 8), c8 = (i % (DV / 8)) * 8;
                 const floatx4 a = *(const floatx4*)(gS + r * DV + c8);
                 const floatx4 b = *(const floatx4*)(gS + r * DV + c8 + 4);
-                bf16x8 v;
-                v[0] = (bf16)a[0]; v[1] = (bf16)a[1]; v[2] = (bf16)a[2]; v[3] = (bf16)a[3];
-                v[4] = (bf16)b[0]; v[5] = (bf16)b[1]; v[6] = (bf16)b[2]; v[7] = (bf16)b[3];
-                *(bf16x8*)(sS + r * PV + c8) = v;
+                *(bf16x8*)(sS + r * PV + c8) = bf16x8{(bf16)a[0], (bf16)a[1], (bf16)a[2], (bf16)a[3],
+                                                      (bf16)b[0], (bf16)b[1], (bf16)b[2], (bf16)b[3]};
             }
         }
     }
     __syncthreads();
 
-    // ---- X = V - K~ S (for dbeta), dO S^T, dY S^T ----------------------------------
+    // ---- dO S^T, dY S^T; dbeta's first term ---------------------------------------
+    // (V - K~ S) . dY = v . dY - sum_c k e^g (dY S^T): the second part comes
+    // with dY S^T, so V - K~ S is never formed
     floatx4 dq[NB], dka[NB], dkb[NB];
 #pragma unroll
     for (int R = 0; R < NB; ++R) {
@@ -426,33 +445,14 @@ __global__ void __launch_bounds__(512) kda_chunk_grad_kernel(ChunkGradParams prm
         dkb[R] = dq[R];
     }
     if (w < NVB) {
-        const bf16* gv = (const bf16*)prm.v + row0 * DV;
 #pragma unroll
-        for (int R = 0; R < NB; ++R) {
-            floatx4 acc = {0.f, 0.f, 0.f, 0.f};
-            const int r = 16 * R + lr;
-#pragma unroll
-            for (int kk = 0; kk < DK / 32; ++kk) {
-                const int c0 = 32 * kk + 8 * q;
-                const bf16x8 kv = *(const bf16x8*)(sK + r * PK + c0);
-                const floatx4 g0 = *(const floatx4*)(sG + r * PG + c0);
-                const floatx4 g1 = *(const floatx4*)(sG + r * PG + c0 + 4);
-                bf16x8 a;
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    a[e] = (bf16)((float)kv[e] * __expf(g0[e]));
-                    a[4 + e] = (bf16)((float)kv[4 + e] * __expf(g1[e]));
-                }
-                acc = F::mma(acc, a, load_frag_tr(sS, PV, 32 * kk, 16 * w));
-            }
+        for (int R = 0; R < NB; ++R)
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int rr = 16 * R + 4 * q + i;
-                const float vv = rr < n ? (float)gv[(int64_t)rr * DV + 16 * w + lr] : 0.f;
-                const float part = sum16((vv - acc[i]) * dY[R][i]);
+                const float part = sum16(vrow[R][i] * dY[R][i]);
                 if (lr == 0) sDB[w * C + rr] = part;
             }
-        }
     }
     if (w < NCBK) {
         const int ch = 16 * w + lr;
@@ -467,25 +467,25 @@ __global__ void __launch_bounds__(512) kda_chunk_grad_kernel(ChunkGradParams prm
                 const float eg = __expf(sG[r * PG + ch]);
                 dq[R][i] = eg * m1[i];
                 dka[R][i] = -sBeta[r] * eg * m2[i];
+                const float part = sum16((float)sK[r * PK + ch] * eg * m2[i]);
+                if (lr == 0) sDB[(16 + w) * C + r] = -part;
             }
         }
     }
     __syncthreads();
 
     // ---- u over S; dA = -(dY u^T) strictly lower, dP = dO u^T lower ---------------
+    // dP's diagonal is kept apart (fp32): its terms carry no decay, enter dq as
+    // dP_rr k_r and dk as dP_rr q_r and cancel exactly in dg, so they are
+    // added to dq and dk at the end and never enter dg or the decayed sums
     {
-        const float* gu = prm.u_all + xf * C * DV;
+        const bf16* gu = (const bf16*)prm.u_all + xf * C * DV;
 #pragma unroll
         for (int it = 0; it < (C * DV / 8 + NT - 1) / NT; ++it) {
             const int i = tid + NT * it;
             if (i < C * DV / 8) {
                 const int r = i / (DV / 8), c8 = (i % (DV / 8)) * 8;
-                const floatx4 a = *(const floatx4*)(gu + r * DV + c8);
-                const floatx4 b = *(const floatx4*)(gu + r * DV + c8 + 4);
-                bf16x8 v;
-                v[0] = (bf16)a[0]; v[1] = (bf16)a[1]; v[2] = (bf16)a[2]; v[3] = (bf16)a[3];
-                v[4] = (bf16)b[0]; v[5] = (bf16)b[1]; v[6] = (bf16)b[2]; v[7] = (bf16)b[3];
-                *(bf16x8*)(sU + r * PV + c8) = v;
+                *(uint4*)(sU + r * PV + c8) = *(const uint4*)(gu + r * DV + c8);
             }
         }
     }
@@ -500,13 +500,17 @@ __global__ void __launch_bounds__(512) kda_chunk_grad_kernel(ChunkGradParams prm
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const int r = 16 * R + 4 * q + i, j = 16 * J + lr;
-            const float x = mat ? (j <= r ? acc[i] : 0.f) : (j < r ? -acc[i] : 0.f);
+            const float x = j < r ? (mat ? acc[i] : -acc[i]) : 0.f;
             dst[r * PCC + j] = (bf16)x;
+            if (mat && j == r) sPd[r] = acc[i];
         }
     }
     __syncthreads();
 
     // ---- G over dY and dO; the e^{g_n} G.S term; u G^T -------------------------------
+    // (S and G stay fp32 in memory: the sum G.S below is a long dot product
+    // whose terms largely cancel in d ln(alpha), which bf16 copies of S or G
+    // would not resolve)
     const float* gG = prm.G_all + xr * DK * DV;
     {
 #pragma unroll
@@ -516,10 +520,8 @@ __global__ void __launch_bounds__(512) kda_chunk_grad_kernel(ChunkGradParams prm
                 const int r = i / (DV / 8), c8 = (i % (DV / 8)) * 8;
                 const floatx4 a = *(const floatx4*)(gG + r * DV + c8);
                 const floatx4 b = *(const floatx4*)(gG + r * DV + c8 + 4);
-                bf16x8 v;
-                v[0] = (bf16)a[0]; v[1] = (bf16)a[1]; v[2] = (bf16)a[2]; v[3] = (bf16)a[3];
-                v[4] = (bf16)b[0]; v[5] = (bf16)b[1]; v[6] = (bf16)b[2]; v[7] = (bf16)b[3];
-                *(bf16x8*)(sGG + r * PV + c8) = v;
+                *(bf16x8*)(sGG + r * PV + c8) = bf16x8{(bf16)a[0], (bf16)a[1], (bf16)a[2], (bf16)a[3],
+                                                       (bf16)b[0], (bf16)b[1], (bf16)b[2], (bf16)b[3]};
             }
         }
         // d g_n += e^{g_n} sum_j G[c][j] S[c][j]: four threads per channel
@@ -577,44 +579,93 @@ __global__ void __launch_bounds__(512) kda_chunk_grad_kernel(ChunkGradParams prm
     }
     __syncthreads();
     bf16* xl = (bf16*)(ph + C * PK * 2 + w * Cfg::XW);  // [C][16]: lower sums' operand
-    bf16* xuk = (bf16*)((char*)xl + Cfg::XL);           // [16][PXU]: upper sums' operands
-    bf16* xuq = (bf16*)((char*)xuk + Cfg::XU);
+    bf16* xuk = (bf16*)((char*)xl + Cfg::XL);           // [C][16]: upper sums' operands
+    bf16* xuq = (bf16*)((char*)xuk + Cfg::XL);
     const int ch = 16 * w + lr;
 #pragma unroll 1
     for (int s = 0; s < NB; ++s) {
-        // operands anchored at token a: lower sums of row block s (a = 16s - 1,
-        // rows j < 16s), upper sums of row block s (a = 16s + 15, rows r > a)
+        // Block s is "moderate" for this wave when its total decay is at least
+        // -60 in each of the wave's 16 channels: then one anchor per sum
+        // covers the diagonal block too (its factors stay below e^60) and the
+        // whole sum runs on MFMA.  Otherwise the diagonal block is summed
+        // directly and only the blocks off it take anchored MFMA operands.
+        const float zb = w < NCBK ? sG[(16 * s + 15) * PG + ch] - (s ? sG[(16 * s - 1) * PG + ch] : 0.f)
+                                  : 0.f;
+        const bool mild = __all(zb >= -60.f);
+        // operands: lower sums of row block s anchored at a = 16s - 1 (rows
+        // j < 16s, and with a mild block also its rows), upper sums of row
+        // block s anchored at a = 16s + 15 (rows r > a, and with a mild block
+        // also the block's rows)
+        // (each lane builds 8 channels of one row per step: one 16-byte k or q
+        // piece, two of g, one of the anchor's g)
         if (w < NCBK) {
-            if (s >= 1) {
-                const int a = 16 * s - 1, KR = (16 * s + 31) / 32 * 32;
-                for (int e = l; e < KR * 16; e += 64) {
-                    const int j = e >> 4, cc = 16 * w + (e & 15);
-                    float x = 0.f;
-                    if (j < 16 * s) x = (float)sK[j * PK + cc] * __expf(sG[a * PG + cc] - sG[j * PG + cc]);
-                    xl[e] = (bf16)x;
+            const int h8 = 16 * w + 8 * (l & 1);  // this lane's 8 channels
+            const int la = 16 * s - 1;
+            const int lrows = mild ? 16 * s + 16 : 16 * s;
+            const int KR = (lrows + 31) / 32 * 32;
+            if (lrows > 0) {
+                floatx4 a0 = {0.f, 0.f, 0.f, 0.f}, a1 = a0;
+                if (la >= 0) {
+                    a0 = *(const floatx4*)(sG + la * PG + h8);
+                    a1 = *(const floatx4*)(sG + la * PG + h8 + 4);
+                }
+                for (int t = l; t < KR * 2; t += 64) {
+                    const int j = t >> 1;
+                    bf16x8 x = {};
+                    if (j < lrows) {
+                        const bf16x8 kv = *(const bf16x8*)(sK + j * PK + h8);
+                        const floatx4 g0 = *(const floatx4*)(sG + j * PG + h8);
+                        const floatx4 g1 = *(const floatx4*)(sG + j * PG + h8 + 4);
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) {
+                            x[e] = (bf16)((float)kv[e] * __expf(a0[e] - g0[e]));
+                            x[4 + e] = (bf16)((float)kv[4 + e] * __expf(a1[e] - g1[e]));
+                        }
+                    }
+                    *(bf16x8*)(xl + j * 16 + 8 * (l & 1)) = x;
                 }
             }
-            if (s <= NB - 2) {
-                const int a = 16 * s + 15, k0 = (16 * s + 16) / 32 * 32;
-                for (int e = l; e < (C - k0) * 16; e += 64) {
-                    const int r = k0 + (e >> 4), c16 = e & 15, cc = 16 * w + c16;
-                    const float f = r > a ? __expf(sG[r * PG + cc] - sG[a * PG + cc]) : 0.f;
-                    xuk[c16 * PXU + r] = (bf16)(sBeta[r] * (float)sK[r * PK + cc] * f);
-                    xuq[c16 * PXU + r] = (bf16)((float)sQ[r * PK + cc] * f);
+            const int ua = 16 * s + 15;
+            const int ufirst = mild ? 16 * s : ua + 1;  // first row taken
+            if (ufirst < C) {
+                const int k0 = ufirst / 32 * 32;
+                const floatx4 a0 = *(const floatx4*)(sG + ua * PG + h8);
+                const floatx4 a1 = *(const floatx4*)(sG + ua * PG + h8 + 4);
+                for (int t = l; t < (C - k0) * 2; t += 64) {
+                    const int r = k0 + (t >> 1);
+                    bf16x8 xk = {}, xq = {};
+                    if (r >= ufirst) {
+                        const float br = sBeta[r];
+                        const bf16x8 kv = *(const bf16x8*)(sK + r * PK + h8);
+                        const bf16x8 qv = *(const bf16x8*)(sQ + r * PK + h8);
+                        const floatx4 g0 = *(const floatx4*)(sG + r * PG + h8);
+                        const floatx4 g1 = *(const floatx4*)(sG + r * PG + h8 + 4);
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) {
+                            const float f0 = __expf(g0[e] - a0[e]), f1 = __expf(g1[e] - a1[e]);
+                            xk[e] = (bf16)(br * (float)kv[e] * f0);
+                            xk[4 + e] = (bf16)(br * (float)kv[4 + e] * f1);
+                            xq[e] = (bf16)((float)qv[e] * f0);
+                            xq[4 + e] = (bf16)((float)qv[4 + e] * f1);
+                        }
+                    }
+                    *(bf16x8*)(xuk + r * 16 + 8 * (l & 1)) = xk;
+                    *(bf16x8*)(xuq + r * 16 + 8 * (l & 1)) = xq;
                 }
             }
         }
         __syncthreads();
         if (w < NCBK) {
-            // lower sums, rows 16s..: R = decayed(dA) K (j < r), RP = decayed(dP) K (j <= r)
+            // lower sums, rows 16s..: R = decayed(dA) K, RP = decayed(dP) K (j < r)
             {
-                const int R = s;
+                const int R = s, la = 16 * R - 1;
+                const int lrows = mild ? 16 * R + 16 : 16 * R;
                 floatx4 accR = {0.f, 0.f, 0.f, 0.f}, accP = accR;
-                if (R >= 1) {
-                    const int a = 16 * R - 1, KR = (16 * R + 31) / 32 * 32;
+                if (lrows > 0) {
+                    const int KR = (lrows + 31) / 32 * 32;
                     accR = mma_block_bt<bf16>(accR, sdA + 16 * R * PCC, PCC, xl, 16, 0, KR);
                     accP = mma_block_bt<bf16>(accP, sdP + 16 * R * PCC, PCC, xl, 16, 0, KR);
-                    const float ga = sG[a * PG + ch];
+                    const float ga = la >= 0 ? sG[la * PG + ch] : 0.f;
 #pragma unroll
                     for (int i = 0; i < 4; ++i) {
                         const float f = __expf(sG[(16 * R + 4 * q + i) * PG + ch] - ga);
@@ -622,20 +673,21 @@ __global__ void __launch_bounds__(512) kda_chunk_grad_kernel(ChunkGradParams prm
                         accP[i] *= f;
                     }
                 }
-                float gr[4];
+                if (!mild) {
+                    float gr[4];
 #pragma unroll
-                for (int i = 0; i < 4; ++i) gr[i] = sG[(16 * R + 4 * q + i) * PG + ch];
+                    for (int i = 0; i < 4; ++i) gr[i] = sG[(16 * R + 4 * q + i) * PG + ch];
 #pragma unroll 4
-                for (int jj = 0; jj < 16; ++jj) {
-                    const int j = 16 * R + jj;
-                    const float gj = sG[j * PG + ch], kj = (float)sK[j * PK + ch];
+                    for (int jj = 0; jj < 16; ++jj) {
+                        const int j = 16 * R + jj;
+                        const float gj = sG[j * PG + ch], kj = (float)sK[j * PK + ch];
 #pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        const int r = 16 * R + 4 * q + i;
-                        const float e = __expf(fminf(gr[i] - gj, 0.f)) * kj;
-                        const float mp = j <= r ? 1.f : 0.f, ma = j < r ? 1.f : 0.f;
-                        accP[i] += mp * (float)sdP[r * PCC + j] * e;
-                        accR[i] += ma * (float)sdA[r * PCC + j] * e;
+                        for (int i = 0; i < 4; ++i) {
+                            const int r = 16 * R + 4 * q + i;
+                            const float e = __expf(fminf(gr[i] - gj, 0.f)) * kj;
+                            accP[i] += (float)sdP[r * PCC + j] * e;
+                            accR[i] += (float)sdA[r * PCC + j] * e;
+                        }
                     }
                 }
 #pragma unroll
@@ -649,30 +701,35 @@ __global__ void __launch_bounds__(512) kda_chunk_grad_kernel(ChunkGradParams prm
             }
             // upper sums, rows 16s..: RU = decayed^T(beta dA) K + decayed^T(dP) Q
             {
-                const int J = s;
+                const int J = s, ua = 16 * J + 15;
+                const int ufirst = mild ? 16 * J : ua + 1;
                 floatx4 acc = {0.f, 0.f, 0.f, 0.f};
-                if (J <= NB - 2) {
-                    const int a = 16 * J + 15, k0 = (16 * J + 16) / 32 * 32;
-                    acc = mma_block_at<bf16>(acc, sdA + k0 * PCC, PCC, 16 * J, xuk + k0, PXU, C - k0);
-                    acc = mma_block_at<bf16>(acc, sdP + k0 * PCC, PCC, 16 * J, xuq + k0, PXU, C - k0);
-                    const float ga = sG[a * PG + ch];
+                if (ufirst < C) {
+                    const int k0 = ufirst / 32 * 32;
+                    // both operands read transposed: A[j][r] = dA[r][j], B[c][r] = x~[r][c]
+                    for (int kk = k0; kk < C; kk += 32) {
+                        acc = F::mma(acc, load_frag_tr(sdA, PCC, kk, 16 * J), load_frag_tr(xuk, 16, kk, 0));
+                        acc = F::mma(acc, load_frag_tr(sdP, PCC, kk, 16 * J), load_frag_tr(xuq, 16, kk, 0));
+                    }
+                    const float ga = sG[ua * PG + ch];
 #pragma unroll
                     for (int i = 0; i < 4; ++i) acc[i] *= __expf(ga - sG[(16 * J + 4 * q + i) * PG + ch]);
                 }
-                float gj[4];
+                if (!mild) {
+                    float gj[4];
 #pragma unroll
-                for (int i = 0; i < 4; ++i) gj[i] = sG[(16 * J + 4 * q + i) * PG + ch];
+                    for (int i = 0; i < 4; ++i) gj[i] = sG[(16 * J + 4 * q + i) * PG + ch];
 #pragma unroll 4
-                for (int rr = 0; rr < 16; ++rr) {
-                    const int r = 16 * J + rr;
-                    const float g_r = sG[r * PG + ch];
-                    const float kr = sBeta[r] * (float)sK[r * PK + ch], qr = (float)sQ[r * PK + ch];
+                    for (int rr = 0; rr < 16; ++rr) {
+                        const int r = 16 * J + rr;
+                        const float g_r = sG[r * PG + ch];
+                        const float kr = sBeta[r] * (float)sK[r * PK + ch], qr = (float)sQ[r * PK + ch];
 #pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        const int j = 16 * J + 4 * q + i;
-                        const float e = __expf(fminf(g_r - gj[i], 0.f));
-                        const float mp = r >= j ? 1.f : 0.f, ma = r > j ? 1.f : 0.f;
-                        acc[i] += e * (mp * (float)sdP[r * PCC + j] * qr + ma * (float)sdA[r * PCC + j] * kr);
+                        for (int i = 0; i < 4; ++i) {
+                            const int j = 16 * J + 4 * q + i;
+                            const float e = __expf(fminf(g_r - gj[i], 0.f));
+                            acc[i] += e * ((float)sdP[r * PCC + j] * qr + (float)sdA[r * PCC + j] * kr);
+                        }
                     }
                 }
 #pragma unroll
@@ -691,8 +748,9 @@ __global__ void __launch_bounds__(512) kda_chunk_grad_kernel(ChunkGradParams prm
             for (int i = 0; i < 4; ++i) {
                 const int r = 16 * R + 4 * q + i;
                 if (r < n) {
-                    prm.dq[(row0 + r) * DK + ch] = dq[R][i];
-                    prm.dk[(row0 + r) * DK + ch] = dka[R][i] + dkb[R][i];
+                    const float pd = sPd[r];
+                    prm.dq[(row0 + r) * DK + ch] = dq[R][i] + pd * (float)sK[r * PK + ch];
+                    prm.dk[(row0 + r) * DK + ch] = dka[R][i] + dkb[R][i] + pd * (float)sQ[r * PK + ch];
                 }
                 dg[R][i] = (float)sQ[r * PK + ch] * dq[R][i] +
                            (float)sK[r * PK + ch] * (dka[R][i] - dkb[R][i]);
@@ -750,7 +808,7 @@ __global__ void __launch_bounds__(512) kda_chunk_grad_kernel(ChunkGradParams prm
     if (tid < n) {
         float db = 0.f;
 #pragma unroll
-        for (int v = 0; v < 2 * 8; ++v) db += sDB[v * C + tid];
+        for (int v = 0; v < 3 * 8; ++v) db += sDB[v * C + tid];
         prm.dbeta[row0 + tid] = db;
     }
 }

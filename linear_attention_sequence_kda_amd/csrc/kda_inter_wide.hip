@@ -169,6 +169,9 @@ __global__ void __launch_bounds__(Cfg::NT) kda_inter_wide_kernel(InterParams prm
             } else {
                 g = rl.gam;
             }
+            // the scan form never reads Q~ or P: such pieces load the (small,
+            // cached) decay piece instead of streaming their own bytes
+            if (SCAN && i >= Cfg::P_Q && (i < Cfg::P_K || (i >= Cfg::P_P && i < Cfg::P_U))) g = rl.gam;
             pg[j] = __builtin_amdgcn_readfirstlane(g);
             pl[j] = __builtin_amdgcn_readfirstlane(i0 < Cfg::NPIECE ? (uint32_t)i0 * 1024u : 0xffffffffu);
         }
@@ -368,14 +371,14 @@ __global__ void __launch_bounds__(Cfg::NT) kda_inter_wide_kernel(InterParams prm
         };
         auto store_u = [&]() {
             if (keep) {
-                float* ud = prm.u_all + ((int64_t)bh * prm.n_store + xi) * C * DV + v0 + lr;
+                bf16* ud = (bf16*)prm.u_all + ((int64_t)bh * prm.n_store + xi) * C * DV + v0 + lr;
 #pragma unroll
                 for (int R = 0; R < NB; ++R)
 #pragma unroll
                     for (int b = 0; b < NVBW; ++b)
 #pragma unroll
                         for (int e = 0; e < 4; ++e)
-                            ud[(16 * R + 4 * lq + e) * DV + 16 * (NVBW * w + b)] = u[R][b][e];
+                            ud[(16 * R + 4 * lq + e) * DV + 16 * (NVBW * w + b)] = (bf16)u[R][b][e];
             }
         };
         auto pack_u = [&]() {

@@ -140,11 +140,11 @@ struct InterParams {
     const float* z_in = nullptr;
     float* z_out = nullptr;
     // scan form of the wide state pass (launch_inter_wide_scan): no o; the
-    // state entering chunk x and that chunk's u = U - W S are written, fp32,
-    // for every chunk x with x % 2^scan_shift == 0, as entry x >> scan_shift
-    // of S_all [BH][n_store][DK][DV] and u_all [BH][n_store][C][DV]
+    // state entering chunk x (fp32) and that chunk's u = U - W S (bf16) are
+    // written for every chunk x with x % 2^scan_shift == 0, as entry
+    // x >> scan_shift of S_all [BH][n_store][DK][DV] and u_all [BH][n_store][C][DV]
     float* S_all = nullptr;
-    float* u_all = nullptr;
+    void* u_all = nullptr;
     int scan_shift = 0;
     int n_store = 0;
 };
@@ -286,11 +286,11 @@ struct ChunkGradParams {
     const void* dout;       // [BH, L, DV] bf16
     const void* la;         // [BH, L, DK] per-channel ln(alpha), gate type
     const void* beta;       // [BH, L] gate type
-    const float* tt;        // [BH][nc][C][C] T^T
-    const float* S_all;     // [BH][nc][DK][DV] state entering each chunk
-    const float* u_all;     // [BH][nc][C][DV] u of each chunk
-    const float* G_all;     // [BH][nc][DK][DV] dJ/dS leaving each chunk
-    const float* du_all;    // [BH][nc][C][DV] dJ/du of each chunk
+    const float* tt;        // [BH][nc][C][C] T^T, fp32
+    const float* S_all;     // [BH][nc][DK][DV] state entering each chunk, fp32
+    const void* u_all;      // [BH][nc][C][DV] u of each chunk, bf16
+    const float* G_all;     // [BH][nc][DK][DV] dJ/dS leaving each chunk, fp32
+    const void* du_all;     // [BH][nc][C][DV] dJ/du of each chunk, bf16
     float* dq;              // [BH, L, DK]
     float* dk;
     float* dv_out;          // [BH, L, DV]
