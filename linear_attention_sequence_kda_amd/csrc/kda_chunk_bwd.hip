@@ -317,7 +317,77 @@ __global__ void __launch_bounds__(512) kda_chunk_grad_kernel(ChunkGradParams prm
         else return ((const float*)base)[i];
     };
 
-    // ---- beta, g (cumulative ln alpha per channel), k, T^T, du --------------------
+    // Every global load is issued one phase ahead, into registers, and goes
+    // to LDS after that phase's barrier: tiles of 8-element pieces, piece i of
+    // a [rows][cols] tile at row i / (cols / 8), column 8 (i % (cols / 8)).
+    constexpr int NP_CV = (C * DV / 8 + NT - 1) / NT;   // [C][DV] pieces per thread
+    constexpr int NP_CK = (C * DK / 8 + NT - 1) / NT;   // [C][DK]
+    constexpr int NP_KV = (DK * DV / 8 + NT - 1) / NT;  // [DK][DV]
+    constexpr int NP_TT = C * C / 4 / NT;               // T^T, fp32 4-element pieces
+    auto ld_rows = [&](uint4 (&dst)[NP_CV > NP_CK ? NP_CV : NP_CK], const bf16* base, int cols,
+                       int np) {
+        for (int it = 0; it < np; ++it) {
+            const int i = tid + NT * it;
+            const int r = i / (cols / 8), c8 = (i % (cols / 8)) * 8;
+            dst[it] = make_uint4(0u, 0u, 0u, 0u);
+            if (i < C * cols / 8 && r < n) dst[it] = *(const uint4*)(base + (int64_t)r * cols + c8);
+        }
+    };
+    constexpr int NPR = NP_CV > NP_CK ? NP_CV : NP_CK;
+    auto st_rows = [&](const uint4 (&src)[NPR], bf16* dst, int pitch, int cols, int np) {
+        for (int it = 0; it < np; ++it) {
+            const int i = tid + NT * it;
+            if (i < C * cols / 8) {
+                const int r = i / (cols / 8), c8 = (i % (cols / 8)) * 8;
+                *(uint4*)(dst + r * pitch + c8) = src[it];
+            }
+        }
+    };
+    // fp32 [DK][DV] state tiles
+    auto ld_state = [&](floatx4 (&dst)[NP_KV][2], const float* base) {
+#pragma unroll
+        for (int it = 0; it < NP_KV; ++it) {
+            const int i = tid + NT * it;
+            const int r = i / (DV / 8), c8 = (i % (DV / 8)) * 8;
+            if (i < DK * DV / 8) {
+                dst[it][0] = *(const floatx4*)(base + r * DV + c8);
+                dst[it][1] = *(const floatx4*)(base + r * DV + c8 + 4);
+            }
+        }
+    };
+    auto st_state = [&](const floatx4 (&src)[NP_KV][2], bf16* dst) {
+#pragma unroll
+        for (int it = 0; it < NP_KV; ++it) {
+            const int i = tid + NT * it;
+            if (i < DK * DV / 8) {
+                const int r = i / (DV / 8), c8 = (i % (DV / 8)) * 8;
+                const floatx4 a = src[it][0], b = src[it][1];
+                *(bf16x8*)(dst + r * PV + c8) = bf16x8{(bf16)a[0], (bf16)a[1], (bf16)a[2], (bf16)a[3],
+                                                       (bf16)b[0], (bf16)b[1], (bf16)b[2], (bf16)b[3]};
+            }
+        }
+    };
+
+    // ---- T^T, du and k; beta, g (cumulative ln alpha per channel) -------------------
+    floatx4 rtt[NP_TT];
+    uint4 rdu[NPR], rk[NPR];
+    {
+        const float* gtt = prm.tt + xf * C * C;
+#pragma unroll
+        for (int it = 0; it < NP_TT; ++it) {
+            const int i = tid + NT * it;
+            rtt[it] = *(const floatx4*)(gtt + (i / (C / 4)) * C + (i % (C / 4)) * 4);
+        }
+        // du has no rows past the sequence end to drop (the scan wrote zeros)
+        const bf16* gdu = (const bf16*)prm.du_all + xr * C * DV;
+#pragma unroll
+        for (int it = 0; it < NP_CV; ++it) {
+            const int i = tid + NT * it;
+            rdu[it] = make_uint4(0u, 0u, 0u, 0u);
+            if (i < C * DV / 8) rdu[it] = *(const uint4*)(gdu + (i / (DV / 8)) * DV + (i % (DV / 8)) * 8);
+        }
+        ld_rows(rk, (const bf16*)prm.k + row0 * DK, DK, NP_CK);
+    }
     if (tid < C) sBeta[tid] = tid < n ? gate_at(prm.beta, row0 + tid) : 0.f;
     for (int i = tid; i < 3 * 8 * C; i += NT) sDB[i] = 0.f;
     {
@@ -342,38 +412,29 @@ __global__ void __launch_bounds__(512) kda_chunk_grad_kernel(ChunkGradParams prm
             for (int i = 0; i < 16; ++i) sG[(16 * p + i) * PG + ch] = v[i] + off;
         }
     }
-    {
-        const float* gtt = prm.tt + xf * C * C;
 #pragma unroll
-        for (int it = 0; it < C * C / 4 / NT; ++it) {
-            const int i = tid + NT * it;
-            const int r = i / (C / 4), j4 = (i % (C / 4)) * 4;
-            *(floatx4*)(sTT + r * PT + j4) = *(const floatx4*)(gtt + r * C + j4);
-        }
-        const bf16* gdu = (const bf16*)prm.du_all + xr * C * DV;
+    for (int it = 0; it < NP_TT; ++it) {
+        const int i = tid + NT * it;
+        *(floatx4*)(sTT + (i / (C / 4)) * PT + (i % (C / 4)) * 4) = rtt[it];
+    }
 #pragma unroll
-        for (int it = 0; it < C * DV / 8 / NT; ++it) {
-            const int i = tid + NT * it;
+    for (int it = 0; it < NP_CV; ++it) {
+        const int i = tid + NT * it;
+        if (i < C * DV / 8) {
             const int r = i / (DV / 8), j8 = (i % (DV / 8)) * 8;
-            const bf16x8 v = *(const bf16x8*)(gdu + r * DV + j8);
+            const bf16x8 v = __builtin_bit_cast(bf16x8, rdu[it]);
             *(floatx4*)(sdu + r * PDU + j8) = floatx4{(float)v[0], (float)v[1], (float)v[2], (float)v[3]};
             *(floatx4*)(sdu + r * PDU + j8 + 4) = floatx4{(float)v[4], (float)v[5], (float)v[6], (float)v[7]};
         }
-        const bf16* gk = (const bf16*)prm.k + row0 * DK;
-#pragma unroll
-        for (int it = 0; it < (C * DK / 8 + NT - 1) / NT; ++it) {
-            const int i = tid + NT * it;
-            if (i < C * DK / 8) {
-                const int r = i / (DK / 8), c8 = (i % (DK / 8)) * 8;
-                uint4 v = make_uint4(0u, 0u, 0u, 0u);
-                if (r < n) v = *(const uint4*)(gk + (int64_t)r * DK + c8);
-                *(uint4*)(sK + r * PK + c8) = v;
-            }
-        }
     }
+    st_rows(rk, sK, PK, DK, NP_CK);
     __syncthreads();
 
-    // ---- dY = T^T du (fp32 MFMA); dv = beta dY ------------------------------------
+    // ---- dY = T^T du (fp32 MFMA); dv = beta dY  (dO and S on their way) -------------
+    uint4 rdo[NPR];
+    floatx4 rs[NP_KV][2];
+    ld_rows(rdo, (const bf16*)prm.dout + row0 * DV, DV, NP_CV);
+    ld_state(rs, prm.S_all + xf * DK * DV);
     floatx4 dY[NB];
     if (w < NVB) {
 #pragma unroll
@@ -389,49 +450,27 @@ __global__ void __launch_bounds__(512) kda_chunk_grad_kernel(ChunkGradParams prm
     }
     __syncthreads();
 
-    // ---- dY, dO and S to bf16 tiles; this wave's v -----------------------------------
-    float vrow[NB][4];
-    if (w < NVB) {
-        const bf16* gv = (const bf16*)prm.v + row0 * DV;
-#pragma unroll
-        for (int R = 0; R < NB; ++R)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int rr = 16 * R + 4 * q + i;
-                vrow[R][i] = rr < n ? (float)gv[(int64_t)rr * DV + 16 * w + lr] : 0.f;
-            }
-    }
+    // ---- dY, dO and S to bf16 tiles (u and v on their way) -------------------------
     if (w < NVB) {
 #pragma unroll
         for (int R = 0; R < NB; ++R)
 #pragma unroll
             for (int i = 0; i < 4; ++i) sDY[(16 * R + 4 * q + i) * PV + 16 * w + lr] = (bf16)dY[R][i];
     }
+    st_rows(rdo, sDO, PV, DV, NP_CV);
+    st_state(rs, sS);
+    uint4 ru[NPR], rv[NPR];
     {
-        const bf16* gdo = (const bf16*)prm.dout + row0 * DV;
+        // u has no rows past the sequence end to drop (zero records there)
+        const bf16* gu = (const bf16*)prm.u_all + xf * C * DV;
 #pragma unroll
-        for (int it = 0; it < (C * DV / 8 + NT - 1) / NT; ++it) {
+        for (int it = 0; it < NP_CV; ++it) {
             const int i = tid + NT * it;
-            if (i < C * DV / 8) {
-                const int r = i / (DV / 8), c8 = (i % (DV / 8)) * 8;
-                uint4 v = make_uint4(0u, 0u, 0u, 0u);
-                if (r < n) v = *(const uint4*)(gdo + (int64_t)r * DV + c8);
-                *(uint4*)(sDO + r * PV + c8) = v;
-            }
-        }
-        const float* gS = prm.S_all + xf * DK * DV;
-#pragma unroll
-        for (int it = 0; it < (DK * DV / 8 + NT - 1) / NT; ++it) {
-            const int i = tid + NT * it;
-            if (i < DK * DV / 8) {
-                const int r = i / (DV / 8), c8 = (i % (DV / 8)) * 8;
-                const floatx4 a = *(const floatx4*)(gS + r * DV + c8);
-                const floatx4 b = *(const floatx4*)(gS + r * DV + c8 + 4);
-                *(bf16x8*)(sS + r * PV + c8) = bf16x8{(bf16)a[0], (bf16)a[1], (bf16)a[2], (bf16)a[3],
-                                                      (bf16)b[0], (bf16)b[1], (bf16)b[2], (bf16)b[3]};
-            }
+            ru[it] = make_uint4(0u, 0u, 0u, 0u);
+            if (i < C * DV / 8) ru[it] = *(const uint4*)(gu + (i / (DV / 8)) * DV + (i % (DV / 8)) * 8);
         }
     }
+    ld_rows(rv, (const bf16*)prm.v + row0 * DV, DV, NP_CV);
     __syncthreads();
 
     // ---- dO S^T, dY S^T; dbeta's first term ---------------------------------------
@@ -444,15 +483,21 @@ __global__ void __launch_bounds__(512) kda_chunk_grad_kernel(ChunkGradParams prm
         dka[R] = dq[R];
         dkb[R] = dq[R];
     }
-    if (w < NVB) {
+    // v . dY by rows: the DV/8 pieces of a row sit in adjacent lanes
 #pragma unroll
-        for (int R = 0; R < NB; ++R)
+    for (int it = 0; it < NP_CV; ++it) {
+        const int i = tid + NT * it;
+        const int r = i / (DV / 8), c8 = (i % (DV / 8)) * 8;
+        float part = 0.f;
+        if (i < C * DV / 8) {
+            const bf16x8 dyv = *(const bf16x8*)(sDY + r * PV + c8);
+            const bf16x8 vv = __builtin_bit_cast(bf16x8, rv[it]);
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int rr = 16 * R + 4 * q + i;
-                const float part = sum16(vrow[R][i] * dY[R][i]);
-                if (lr == 0) sDB[w * C + rr] = part;
-            }
+            for (int e = 0; e < 8; ++e) part += (float)vv[e] * (float)dyv[e];
+        }
+#pragma unroll
+        for (int o = 1; o < DV / 8; o <<= 1) part += __shfl_xor(part, o);
+        if (i < C * DV / 8 && (i % (DV / 8)) == 0) sDB[r] = part;
     }
     if (w < NCBK) {
         const int ch = 16 * w + lr;
@@ -474,21 +519,13 @@ __global__ void __launch_bounds__(512) kda_chunk_grad_kernel(ChunkGradParams prm
     }
     __syncthreads();
 
-    // ---- u over S; dA = -(dY u^T) strictly lower, dP = dO u^T lower ---------------
+    // ---- u over S; dA = -(dY u^T) strictly lower, dP = dO u^T lower (G on its way) --
     // dP's diagonal is kept apart (fp32): its terms carry no decay, enter dq as
     // dP_rr k_r and dk as dP_rr q_r and cancel exactly in dg, so they are
     // added to dq and dk at the end and never enter dg or the decayed sums
-    {
-        const bf16* gu = (const bf16*)prm.u_all + xf * C * DV;
-#pragma unroll
-        for (int it = 0; it < (C * DV / 8 + NT - 1) / NT; ++it) {
-            const int i = tid + NT * it;
-            if (i < C * DV / 8) {
-                const int r = i / (DV / 8), c8 = (i % (DV / 8)) * 8;
-                *(uint4*)(sU + r * PV + c8) = *(const uint4*)(gu + r * DV + c8);
-            }
-        }
-    }
+    st_rows(ru, sU, PV, DV, NP_CV);
+    floatx4 rg[NP_KV][2];
+    ld_state(rg, prm.G_all + xr * DK * DV);
     __syncthreads();
 #pragma unroll
     for (int m = 0; m < 4; ++m) {
@@ -507,40 +544,33 @@ __global__ void __launch_bounds__(512) kda_chunk_grad_kernel(ChunkGradParams prm
     }
     __syncthreads();
 
-    // ---- G over dY and dO; the e^{g_n} G.S term; u G^T -------------------------------
+    // ---- G over dY and dO; the e^{g_n} G.S term; u G^T  (q on its way) -------------
     // (S and G stay fp32 in memory: the sum G.S below is a long dot product
     // whose terms largely cancel in d ln(alpha), which bf16 copies of S or G
     // would not resolve)
-    const float* gG = prm.G_all + xr * DK * DV;
+    st_state(rg, sGG);
     {
-#pragma unroll
-        for (int it = 0; it < (DK * DV / 8 + NT - 1) / NT; ++it) {
-            const int i = tid + NT * it;
-            if (i < DK * DV / 8) {
-                const int r = i / (DV / 8), c8 = (i % (DV / 8)) * 8;
-                const floatx4 a = *(const floatx4*)(gG + r * DV + c8);
-                const floatx4 b = *(const floatx4*)(gG + r * DV + c8 + 4);
-                *(bf16x8*)(sGG + r * PV + c8) = bf16x8{(bf16)a[0], (bf16)a[1], (bf16)a[2], (bf16)a[3],
-                                                       (bf16)b[0], (bf16)b[1], (bf16)b[2], (bf16)b[3]};
-            }
-        }
-        // d g_n += e^{g_n} sum_j G[c][j] S[c][j]: four threads per channel
+        // d g_n += e^{g_n} sum_j G[c][j] S[c][j]: this thread's pieces of G
+        // against the same pieces of S (the DV/8 pieces of a row in adjacent lanes)
         const float* gS = prm.S_all + xf * DK * DV;
-        const int ch = tid >> 2, p = tid & 3;
-        float d = 0.f;
-        if (ch < DK) {
-            const float* a = gG + ch * DV + p * (DV / 4);
-            const float* b = gS + ch * DV + p * (DV / 4);
 #pragma unroll
-            for (int j = 0; j < DV / 4; j += 4) {
-                const floatx4 x = *(const floatx4*)(a + j), y = *(const floatx4*)(b + j);
-                d += x[0] * y[0] + x[1] * y[1] + x[2] * y[2] + x[3] * y[3];
+        for (int it = 0; it < NP_KV; ++it) {
+            const int i = tid + NT * it;
+            const int r = i / (DV / 8), c8 = (i % (DV / 8)) * 8;
+            float d = 0.f;
+            if (i < DK * DV / 8) {
+                const floatx4 a = *(const floatx4*)(gS + r * DV + c8);
+                const floatx4 b = *(const floatx4*)(gS + r * DV + c8 + 4);
+                d = a[0] * rg[it][0][0] + a[1] * rg[it][0][1] + a[2] * rg[it][0][2] + a[3] * rg[it][0][3] +
+                    b[0] * rg[it][1][0] + b[1] * rg[it][1][1] + b[2] * rg[it][1][2] + b[3] * rg[it][1][3];
             }
+#pragma unroll
+            for (int o = 1; o < DV / 8; o <<= 1) d += __shfl_xor(d, o);
+            if (i < DK * DV / 8 && (i % (DV / 8)) == 0) sEn[r] = __expf(sG[(C - 1) * PG + r]) * d;
         }
-        d += __shfl_xor(d, 1);
-        d += __shfl_xor(d, 2);
-        if (ch < DK && p == 0) sEn[ch] = __expf(sG[(C - 1) * PG + ch]) * d;
     }
+    uint4 rq[NPR];
+    ld_rows(rq, (const bf16*)prm.q + row0 * DK, DK, NP_CK);
     __syncthreads();
     if (w < NCBK) {
         const int ch = 16 * w + lr;
@@ -564,19 +594,7 @@ __global__ void __launch_bounds__(512) kda_chunk_grad_kernel(ChunkGradParams prm
     __syncthreads();
 
     // ---- q; the decayed products ---------------------------------------------------
-    {
-        const bf16* gq = (const bf16*)prm.q + row0 * DK;
-#pragma unroll
-        for (int it = 0; it < (C * DK / 8 + NT - 1) / NT; ++it) {
-            const int i = tid + NT * it;
-            if (i < C * DK / 8) {
-                const int r = i / (DK / 8), c8 = (i % (DK / 8)) * 8;
-                uint4 v = make_uint4(0u, 0u, 0u, 0u);
-                if (r < n) v = *(const uint4*)(gq + (int64_t)r * DK + c8);
-                *(uint4*)(sQ + r * PK + c8) = v;
-            }
-        }
-    }
+    st_rows(rq, sQ, PK, DK, NP_CK);
     __syncthreads();
     bf16* xl = (bf16*)(ph + C * PK * 2 + w * Cfg::XW);  // [C][16]: lower sums' operand
     bf16* xuk = (bf16*)((char*)xl + Cfg::XL);           // [C][16]: upper sums' operands
