@@ -95,7 +95,7 @@ __device__ __forceinline__ int wide_piece_k(int kbase, int e) { return kbase + (
 
 template <int DK, int DV>
 struct RevCfg {
-    static constexpr int C = 64, NT = 256;
+    static constexpr int C = 64, NT = 512;
     static constexpr RecLayout RL = rec_layout(DK, DV, C, 2, true);
     static constexpr int PDO = DV + 16, PPT = C + 16;  // bf16 pitches
     static constexpr int O_W = 0, O_KT = O_W + C * DK * 2, O_QT = O_KT + DK * C * 2;
@@ -106,7 +106,7 @@ struct RevCfg {
 };
 
 template <int DK, int DV>
-__global__ void __launch_bounds__(256) kda_rev_records_kernel(RevRecParams prm) {
+__global__ void __launch_bounds__(512) kda_rev_records_kernel(RevRecParams prm) {
     typedef RevCfg<DK, DV> Cfg;
     constexpr int C = Cfg::C, NT = Cfg::NT, PDO = Cfg::PDO, PPT = Cfg::PPT;
     constexpr RecLayout RL = Cfg::RL;
@@ -215,7 +215,7 @@ hipError_t launch_rev_records(const RevRecParams& prm, int dk, hipStream_t strea
     const unsigned grid = (unsigned)((int64_t)prm.BH * prm.nc);
 #define KDA_CASE(DK_, DV_)                                                                     \
     if (dk == DK_ && prm.DV == DV_) {                                                          \
-        hipLaunchKernelGGL((kda_rev_records_kernel<DK_, DV_>), dim3(grid), dim3(256), 0, stream, prm); \
+        hipLaunchKernelGGL((kda_rev_records_kernel<DK_, DV_>), dim3(grid), dim3(512), 0, stream, prm); \
         return hipGetLastError();                                                              \
     }
     KDA_CASE(128, 128)
