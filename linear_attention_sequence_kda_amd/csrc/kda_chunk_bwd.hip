@@ -324,15 +324,20 @@ __global__ void __launch_bounds__(512) kda_chunk_grad_kernel(ChunkGradParams prm
     constexpr int NP_CK = (C * DK / 8 + NT - 1) / NT;   // [C][DK]
     constexpr int NP_KV = (DK * DV / 8 + NT - 1) / NT;  // [DK][DV]
     constexpr int NP_TT = C * C / 4 / NT;               // T^T, fp32 4-element pieces
+    static_assert((C * DV / 8) % NT == 0 && (C * DK / 8) % NT == 0 && (C * C / 4) % NT == 0,
+                  "every thread takes whole pieces");
+    // (loads are unconditional, from clamped addresses, and masked after:
+    // a load under a branch would be waited for at the branch's end)
     auto ld_rows = [&](uint4 (&dst)[NP_CV > NP_CK ? NP_CV : NP_CK], const bf16* base, int cols,
                        int np) {
         for (int it = 0; it < np; ++it) {
-            const int i = tid + NT * it;
+            const int i = tid + NT * it;  // (C * cols / 8 is a multiple of NT)
             const int r = i / (cols / 8), c8 = (i % (cols / 8)) * 8;
-            dst[it] = make_uint4(0u, 0u, 0u, 0u);
-            if (i < C * cols / 8 && r < n) dst[it] = *(const uint4*)(base + (int64_t)r * cols + c8);
+            const uint4 v = *(const uint4*)(base + (int64_t)(r < n ? r : n - 1) * cols + c8);
+            dst[it] = keep_or_zero(v, r < n);
         }
     };
+
     constexpr int NPR = NP_CV > NP_CK ? NP_CV : NP_CK;
     auto st_rows = [&](const uint4 (&src)[NPR], bf16* dst, int pitch, int cols, int np) {
         for (int it = 0; it < np; ++it) {
@@ -397,7 +402,8 @@ __global__ void __launch_bounds__(512) kda_chunk_grad_kernel(ChunkGradParams prm
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
             const int r = 16 * p + i;
-            v[i] = (ch < DK && r < n) ? gate_at(prm.la, (row0 + r) * DK + ch) : 0.f;
+            const float x = gate_at(prm.la, (row0 + (r < n ? r : n - 1)) * DK + (ch < DK ? ch : DK - 1));
+            v[i] = (ch < DK && r < n) ? x : 0.f;
         }
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
@@ -552,21 +558,34 @@ __global__ void __launch_bounds__(512) kda_chunk_grad_kernel(ChunkGradParams prm
     {
         // d g_n += e^{g_n} sum_j G[c][j] S[c][j]: this thread's pieces of G
         // against the same pieces of S (the DV/8 pieces of a row in adjacent lanes)
+        // (S read again from memory, two pieces at a time: both loads go out
+        // before the first wait)
         const float* gS = prm.S_all + xf * DK * DV;
 #pragma unroll
-        for (int it = 0; it < NP_KV; ++it) {
-            const int i = tid + NT * it;
-            const int r = i / (DV / 8), c8 = (i % (DV / 8)) * 8;
-            float d = 0.f;
-            if (i < DK * DV / 8) {
-                const floatx4 a = *(const floatx4*)(gS + r * DV + c8);
-                const floatx4 b = *(const floatx4*)(gS + r * DV + c8 + 4);
-                d = a[0] * rg[it][0][0] + a[1] * rg[it][0][1] + a[2] * rg[it][0][2] + a[3] * rg[it][0][3] +
-                    b[0] * rg[it][1][0] + b[1] * rg[it][1][1] + b[2] * rg[it][1][2] + b[3] * rg[it][1][3];
+        for (int h = 0; h < NP_KV; h += 2) {
+            floatx4 sa[2][2];
+#pragma unroll
+            for (int u2 = 0; u2 < 2; ++u2) {
+                const int i = tid + NT * (h + u2 < NP_KV ? h + u2 : h);
+                const int r = i / (DV / 8), c8 = (i % (DV / 8)) * 8;
+                sa[u2][0] = *(const floatx4*)(gS + r * DV + c8);
+                sa[u2][1] = *(const floatx4*)(gS + r * DV + c8 + 4);
             }
 #pragma unroll
-            for (int o = 1; o < DV / 8; o <<= 1) d += __shfl_xor(d, o);
-            if (i < DK * DV / 8 && (i % (DV / 8)) == 0) sEn[r] = __expf(sG[(C - 1) * PG + r]) * d;
+            for (int u2 = 0; u2 < 2; ++u2) {
+                const int it = h + u2;
+                if (it < NP_KV) {
+                    const int i = tid + NT * it;
+                    const int r = i / (DV / 8);
+                    const floatx4 a = sa[u2][0], b = sa[u2][1];
+                    float d = a[0] * rg[it][0][0] + a[1] * rg[it][0][1] + a[2] * rg[it][0][2] +
+                              a[3] * rg[it][0][3] + b[0] * rg[it][1][0] + b[1] * rg[it][1][1] +
+                              b[2] * rg[it][1][2] + b[3] * rg[it][1][3];
+#pragma unroll
+                    for (int o = 1; o < DV / 8; o <<= 1) d += __shfl_xor(d, o);
+                    if ((i % (DV / 8)) == 0) sEn[r] = __expf(sG[(C - 1) * PG + r]) * d;
+                }
+            }
         }
     }
     uint4 rq[NPR];
