@@ -43,6 +43,8 @@
 // within e^60), a stronger one is summed directly in fp32.  dP's diagonal
 // (no decay) stays out of the sums: its terms cancel exactly in dg and are
 // added to dq and dk alone.
+#include <type_traits>
+
 #include "kda_device.h"
 #include "kda_internal.h"
 
@@ -237,7 +239,7 @@ struct GradCfg {
     static constexpr int NCBK = DK / 16, NVB = DV / 16;
     // bf16 tiles: rows padded by 32 bytes; fp32 tiles by 16
     static constexpr int PK = DK + 16, PV = DV + 16, PCC = C + 16;
-    static constexpr int PG = DK + 4, PT = C + 4, PDU = DV + 4;
+    static constexpr int PG = DK + 4, PT = C + 4, PDU = C + 4;
     // per-wave operands of the decayed sums: [C][16] bf16 row-major tiles
     static constexpr int XL = C * 16 * 2, XW = 3 * XL;
     // persistent areas
@@ -253,10 +255,10 @@ struct GradCfg {
     static constexpr int O_PD = O_ROW + C * 4;               // diagonal of dP [C]
     static constexpr int O_EN = O_PD + C * 4;                // last-row dg terms [DK]
     static constexpr int O_PH = O_EN + DK * 4;               // phase area
-    // phase area: (0) T^T fp32 [C][PT] + du fp32 [C][PDU]; (1, 2) dY | dO |
+    // phase area: (0) T^T fp32 [C][PT] + du^T fp32 [DV][PDU]; (1, 2) dY | dO |
     // S, later u, bf16 [C or DK][PV]; (3) G bf16 [DK][PV] over dY and dO;
     // (4) q bf16 [C][PK] + per-wave x~ tiles; (5) dg fp32 [C][PG]
-    static constexpr int PH0 = C * PT * 4 + C * PDU * 4;
+    static constexpr int PH0 = C * PT * 4 + DV * PDU * 4;
     static constexpr int PH12 = 2 * C * PV * 2 + (DK > C ? DK : C) * PV * 2;
     static constexpr int PH4 = C * PK * 2 + NCBK * XW;
     static constexpr int PH5 = C * PG * 4;
@@ -267,9 +269,17 @@ struct GradCfg {
     static_assert(LDS_BYTES <= 160 * 1024, "LDS budget of one gfx950 CU");
 };
 
+// sum over the 16 lanes of a DPP row, in every lane of it (rotations within
+// the row; every lane of the wave must be active)
 __device__ __forceinline__ float sum16(float x) {
-#pragma unroll
-    for (int o = 1; o < 16; o <<= 1) x += __shfl_xor(x, o);
+    auto ror = [](float v, auto ctl) {
+        return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v),
+                                                                     decltype(ctl)::value, 0xf, 0xf, false));
+    };
+    x += ror(x, std::integral_constant<int, 0x128>{});  // row_ror:8
+    x += ror(x, std::integral_constant<int, 0x124>{});  // row_ror:4
+    x += ror(x, std::integral_constant<int, 0x122>{});  // row_ror:2
+    x += ror(x, std::integral_constant<int, 0x121>{});  // row_ror:1
     return x;
 }
 
@@ -429,8 +439,9 @@ __global__ void __launch_bounds__(512) kda_chunk_grad_kernel(ChunkGradParams prm
         if (i < C * DV / 8) {
             const int r = i / (DV / 8), j8 = (i % (DV / 8)) * 8;
             const bf16x8 v = __builtin_bit_cast(bf16x8, rdu[it]);
-            *(floatx4*)(sdu + r * PDU + j8) = floatx4{(float)v[0], (float)v[1], (float)v[2], (float)v[3]};
-            *(floatx4*)(sdu + r * PDU + j8 + 4) = floatx4{(float)v[4], (float)v[5], (float)v[6], (float)v[7]};
+            // transposed, so that dY = T^T du reads both operands k-contiguous
+#pragma unroll
+            for (int e = 0; e < 8; ++e) sdu[(j8 + e) * PDU + r] = (float)v[e];
         }
     }
     st_rows(rk, sK, PK, DK, NP_CK);
@@ -446,7 +457,7 @@ __global__ void __launch_bounds__(512) kda_chunk_grad_kernel(ChunkGradParams prm
 #pragma unroll
         for (int R = 0; R < NB; ++R) {
             floatx4 acc = {0.f, 0.f, 0.f, 0.f};
-            dY[R] = mma_block_bt<float>(acc, sTT + 16 * R * PT, PT, sdu, PDU, 16 * w, C);
+            dY[R] = mma_block<float>(acc, sTT + 16 * R * PT, PT, sdu + 16 * w * PDU, PDU, C);
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int r = 16 * R + 4 * q + i;
