@@ -995,7 +995,7 @@ int kda_recurrence_bwd_ex(const kda_shape* s, uint32_t flags, const void* q, con
 
 namespace {
 // Layout of kda_chunk_bwd's workspace (each piece rounded up to 256 bytes):
-// the forward records of every chunk, the reverse records (two per chunk),
+// the forward records of every chunk, the reverse records (one per chunk),
 // T^T, the forward scan's S and u and the reverse scan's G and du per chunk,
 // and, with one decay per token or none, per-channel fp32 ln(alpha) and an
 // fp32 beta.
@@ -1011,14 +1011,15 @@ ChunkBwdPlan chunk_bwd_plan(const kda_shape* s) {
     const int64_t rb = kda::rec_layout((int)s->dk, (int)s->dv, (int)C, 2, true).bytes;
     // sizes in doubles first: a shape whose workspace passes 2^60 bytes is refused
     const double chunks = (double)bh * (double)p.nc;
-    const double est = chunks * (3.0 * rb + C * C * 4.0 + 2.0 * s->dk * s->dv * 4 + 2.0 * C * s->dv * 2) +
+    const int64_t rrb = kda::rev_rec_bytes((int)s->dk, (int)s->dv);
+    const double est = chunks * (rb + rrb + C * C * 4.0 + 2.0 * s->dk * s->dv * 4 + 2.0 * C * s->dv * 2) +
                        (double)bh * s->L * (s->dk + 1) * 4.0;
     if (est > 1.0e18 || chunks > (double)INT_MAX) return p;
     auto up = [](int64_t x) { return (x + 255) / 256 * 256; };
     const int64_t nch = bh * p.nc;
     int64_t off = 0;
     p.recs = off; off += up(nch * rb);
-    p.rrecs = off; off += up(2 * nch * rb);
+    p.rrecs = off; off += up(nch * rrb);
     p.tt = off; off += up(nch * C * C * 4);
     p.S = off; off += up(nch * s->dk * s->dv * 4);
     p.G = off; off += up(nch * s->dk * s->dv * 4);
@@ -1155,12 +1156,13 @@ static int kda_chunk_bwd_body(const kda_shape* s, const void* q, const void* k, 
     rx.ws = ws + pl.rrecs;
     rx.S_in = dS_final;
     rx.S_out = dS0;
-    rx.L = 2 * (int64_t)nc * 64;
-    rx.ncs = 2 * nc;
+    rx.L = (int64_t)nc * 64;
+    rx.ncs = nc;
     rx.S_all = (float*)(ws + pl.G);
     rx.u_all = ws + pl.du;
-    rx.scan_shift = 1;
+    rx.scan_shift = 0;
     rx.n_store = nc;
+    rx.rev = 1;
     err = timed_launch(K_WIDE_SCAN, stream, [&] { return kda::launch_inter_wide_scan(rx, dkk, nv, stream); });
     if (err != hipSuccess) return fail(err);
     // every chunk's gradients

@@ -19,11 +19,11 @@
 // du = P^T dO + (K e^{g_n - g}) G and the one into S is
 // dJ/dS = diag(e^{g_n}) G + (Q e^g)^T dO - W^T du (W = T diag(beta) K~).
 // That recursion runs backwards over the chunks; it has the forward state
-// pass's shape, so it runs as that pass over "reverse records" (built here):
-// chunk c becomes two record steps, (W <- K e^{g_n-g}, U <- P^T dO,
-// K^T <- -W^T, decay e^{g_n}) then (W <- 0, U <- dO, K^T <- (Q e^g)^T, decay 1),
-// taken in reverse chunk order, with the state pass's scan form keeping G and
-// du per chunk.  With S (forward scan), u, G and du per chunk, every chunk's
+// pass's shape, so it runs as that pass over "reverse records" (built here),
+// one per chunk in reverse chunk order: W <- K e^{g_n-g}, U <- P^T dO,
+// K^T <- -W^T, decay e^{g_n}, and a second product of the same step,
+// K2^T <- (Q e^g)^T with U2 <- dO; the state pass's scan form keeps G and du
+// per chunk.  With S (forward scan), u, G and du per chunk, every chunk's
 // gradients are independent:
 //
 //   dY = T^T du,  dv = beta dY,  dbeta = sum_n (V - K~ S) dY + sum_c k R,
@@ -128,8 +128,7 @@ __global__ void __launch_bounds__(512) kda_rev_records_kernel(RevRecParams prm) 
     const int64_t t0 = (int64_t)c * C;
     const int n = (int)(prm.L - t0 < C ? prm.L - t0 : C);
     const char* src = (const char*)prm.recs + ((int64_t)bh * nc + c) * RL.bytes;
-    char* dA = (char*)prm.rrecs + ((int64_t)bh * 2 * nc + 2 * (nc - 1 - c)) * RL.bytes;
-    char* dB = dA + RL.bytes;
+    char* dst = (char*)prm.rrecs + ((int64_t)bh * nc + (nc - 1 - c)) * rev_rec_bytes(DK, DV);
 
     // the forward record's W (negated), K^T, Q~ and P as stored; dO by rows
     auto copy_in = [&](uint32_t goff, int loff, int bytes) {
@@ -154,14 +153,12 @@ __global__ void __launch_bounds__(512) kda_rev_records_kernel(RevRecParams prm) 
         const int j = i / C, r = i - j * C;
         sPT[j * PPT + r] = sP[wide_elem(r, j, C)];
     }
-    // step A: W <- K e^{g_n - g} (the transpose of the stored K^T),
-    //         K^T <- -W^T (the stored W is already negated)
-    // step B: W <- 0, K^T <- (Q e^g)^T
+    // W <- K e^{g_n - g} (the transpose of the stored K^T), K^T <- -W^T (the
+    // stored W is already negated), K2^T <- (Q e^g)^T in the Q~ section
     {
-        bf16* aw = (bf16*)(dA + RL.w);
-        bf16* akt = (bf16*)(dA + RL.kt);
-        bf16* bw = (bf16*)(dB + RL.w);
-        bf16* bkt = (bf16*)(dB + RL.kt);
+        bf16* aw = (bf16*)(dst + RL.w);
+        bf16* akt = (bf16*)(dst + RL.kt);
+        bf16* bkt = (bf16*)(dst + RL.qt);
         for (int pc = tid; pc < C * DK / 8; pc += NT) {
             int m, kb;
             wide_piece(pc, DK, m, kb);  // m: token, k: channel
@@ -169,7 +166,6 @@ __global__ void __launch_bounds__(512) kda_rev_records_kernel(RevRecParams prm) 
 #pragma unroll
             for (int e = 0; e < 8; ++e) v[e] = sKt[wide_elem(wide_piece_k(kb, e), m, C)];
             *(bf16x8*)(aw + pc * 8) = v;
-            *(uint4*)(bw + pc * 8) = make_uint4(0u, 0u, 0u, 0u);
         }
         for (int pc = tid; pc < DK * C / 8; pc += NT) {
             int m, kb;
@@ -184,15 +180,13 @@ __global__ void __launch_bounds__(512) kda_rev_records_kernel(RevRecParams prm) 
             *(bf16x8*)(akt + pc * 8) = va;
             *(bf16x8*)(bkt + pc * 8) = vb;
         }
-        // decays: e^{g_n} (copied), then 1
+        // the decay e^{g_n}, copied
         const float* sgam = (const float*)(src + RL.gam);
-        for (int i = tid; i < DK; i += NT) {
-            ((float*)(dA + RL.gam))[i] = sgam[i];
-            ((float*)(dB + RL.gam))[i] = 1.f;
-        }
-        // step B's U = dO in accumulator order: element (16R + 4(l/16) + i,
-        // 16vb + l%16) at ((R * DV/32 + vb/2) * 64 + l) * 8 + (vb % 2) * 4 + i
-        bf16* but = (bf16*)(dB + RL.ut);
+        for (int i = tid; i < DK; i += NT) ((float*)(dst + RL.gam))[i] = sgam[i];
+        // U2 = dO in accumulator order, after the record's own sections:
+        // element (16R + 4(l/16) + i, 16vb + l%16) at
+        // ((R * DV/32 + vb/2) * 64 + l) * 8 + (vb % 2) * 4 + i
+        bf16* but = (bf16*)(dst + RL.bytes);
         for (int t = w; t < 4 * (DV / 16); t += NT / 64) {
             const int R = t / (DV / 16), vb = t % (DV / 16);
             bf16x4 v;
@@ -202,8 +196,8 @@ __global__ void __launch_bounds__(512) kda_rev_records_kernel(RevRecParams prm) 
         }
     }
     __syncthreads();
-    // step A's U = P^T dO (MFMA), stored in accumulator order
-    bf16* aut = (bf16*)(dA + RL.ut);
+    // U = P^T dO (MFMA), stored in accumulator order
+    bf16* aut = (bf16*)(dst + RL.ut);
     for (int t = w; t < 4 * (DV / 16); t += NT / 64) {
         const int jb = t / (DV / 16), vb = t % (DV / 16);
         floatx4 acc = {0.f, 0.f, 0.f, 0.f};

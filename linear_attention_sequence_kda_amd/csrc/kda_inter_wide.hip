@@ -98,7 +98,9 @@ __device__ __forceinline__ bf16x8 pack_frag(floatx4 a, floatx4 b) {
 
 // SCAN: the scan form for the chunkwise gradients (no o; the state entering
 // a chunk and the chunk's u are written out, InterParams::S_all / u_all).
-template <class Cfg, bool SCAN = false>
+// REV (with SCAN): reverse records, whose steps add a second product
+// S += K2^T U2 (K2^T in the Q~ pieces, U2 in the P pieces).
+template <class Cfg, bool SCAN = false, bool REV = false>
 __global__ void __launch_bounds__(Cfg::NT) kda_inter_wide_kernel(InterParams prm) {
     typedef bf16 E;
     typedef Frag<E> F;
@@ -130,7 +132,8 @@ __global__ void __launch_bounds__(Cfg::NT) kda_inter_wide_kernel(InterParams prm
     const int64_t L = sr.len;
     const int DV = prm.DV;
     const RecLayout rl = rec_layout(DK, DV, C, 2, true);
-    const char* recs = (const char*)prm.ws + (int64_t)bh * prm.ncs * rl.bytes;
+    const uint32_t rstride = REV ? rev_rec_bytes(DK, DV) : rl.bytes;
+    const char* recs = (const char*)prm.ws + (int64_t)bh * prm.ncs * rstride;
     // chunks of this span that hold tokens of this head
     int64_t left = (L + C - 1) / C - prm.c0;
     const int ncs = (int)(left < 0 ? 0 : (left < prm.ncs ? left : prm.ncs));
@@ -171,7 +174,13 @@ __global__ void __launch_bounds__(Cfg::NT) kda_inter_wide_kernel(InterParams prm
             }
             // the scan form never reads Q~ or P: such pieces load the (small,
             // cached) decay piece instead of streaming their own bytes
-            if (SCAN && i >= Cfg::P_Q && (i < Cfg::P_K || (i >= Cfg::P_P && i < Cfg::P_U))) g = rl.gam;
+            if (SCAN && !REV && i >= Cfg::P_Q && (i < Cfg::P_K || (i >= Cfg::P_P && i < Cfg::P_U))) g = rl.gam;
+            // reverse records: the P pieces carry U2 (this slice's pieces of
+            // the section after the record's own), the rest the decay piece
+            if (REV && i >= Cfg::P_P && i < Cfg::P_U) {
+                const int u = i - Cfg::P_P;
+                g = u < NB * NUR ? rl.bytes + ((u / NUR) * (DV / 32) + (v0 >> 5) + u % NUR) * 1024 : rl.gam;
+            }
             pg[j] = __builtin_amdgcn_readfirstlane(g);
             pl[j] = __builtin_amdgcn_readfirstlane(i0 < Cfg::NPIECE ? (uint32_t)i0 * 1024u : 0xffffffffu);
         }
@@ -182,7 +191,7 @@ __global__ void __launch_bounds__(Cfg::NT) kda_inter_wide_kernel(InterParams prm
         };
         auto fetch = [&](DSet& st, int cs) {
             cs = __builtin_amdgcn_readfirstlane(cs < ncs ? cs : ncs - 1);
-            const __amdgpu_buffer_rsrc_t rr = make_rsrc(recs + (int64_t)cs * rl.bytes, rl.bytes);
+            const __amdgpu_buffer_rsrc_t rr = make_rsrc(recs + (int64_t)cs * rstride, rstride);
 #pragma unroll
             for (int j = 0; j < NL; ++j)
                 st.v[j] = __builtin_bit_cast(
@@ -294,10 +303,10 @@ __global__ void __launch_bounds__(Cfg::NT) kda_inter_wide_kernel(InterParams prm
         auto piece = [&](int i) -> bf16x8 { return *(const bf16x8*)(slot + i * 1024 + l * 16); };
         // U block (R, vb) in accumulator order: two blocks per piece, the
         // slot's pieces starting at column block 2 (v0 / 32)
-        auto u_init = [&](int R, int b) -> floatx4 {
+        auto u_init = [&](int R, int b, int base = Cfg::P_U) -> floatx4 {
             const int vbg = (v0 >> 4) + NVBW * w + b;  // column block of the head
             const int up = (vbg >> 1) - (v0 >> 5);
-            const uint4 q4 = *(const uint4*)(slot + (Cfg::P_U + R * NUR + up) * 1024 + l * 16);
+            const uint4 q4 = *(const uint4*)(slot + (base + R * NUR + up) * 1024 + l * 16);
             const uint32_t x = (vbg & 1) ? q4.z : q4.x, y = (vbg & 1) ? q4.w : q4.y;
             return floatx4{__uint_as_float(x << 16), __uint_as_float(x & 0xffff0000u),
                            __uint_as_float(y << 16), __uint_as_float(y & 0xffff0000u)};
@@ -413,6 +422,24 @@ __global__ void __launch_bounds__(Cfg::NT) kda_inter_wide_kernel(InterParams prm
                 for (int R = 0; R < NB; ++R) o_block(R);
             }
             s_update(0, NCB);
+            if constexpr (REV) {
+                // the step's second product, S += K2^T U2
+#pragma unroll
+                for (int R = 0; R < NB; ++R) u[R][0] = u_init(R, 0, Cfg::P_P);
+#pragma unroll
+                for (int cb = 0; cb < NCB; ++cb)
+#pragma unroll
+                    for (int kk = 0; kk < NKP; ++kk) kf[cb][kk] = piece(Cfg::P_Q + cb * NKP + kk);
+                sched_fence();
+                pack_u();
+#pragma unroll
+                for (int cb = 0; cb < NCB; ++cb) {
+                    floatx4 acc = Sacc[cb][0];
+#pragma unroll
+                    for (int kk = 0; kk < NKP; ++kk) acc = F::mma(acc, kf[cb][kk], ub[kk][0]);
+                    Sacc[cb][0] = acc;
+                }
+            }
         } else {
             // two column blocks: the reads of each group go out one step
             // ahead of the MFMAs that use them
@@ -709,11 +736,11 @@ __global__ void __launch_bounds__(Cfg::NT, 2) kda_inter_quad_kernel(InterParams 
 
 // ---- host-side dispatch -----------------------------------------------------
 
-template <int DK, int NV, int NWC, int NSET, bool SCAN = false>
+template <int DK, int NV, int NWC, int NSET, bool SCAN = false, bool REV = false>
 static hipError_t launch_wide_cfg(const InterParams& prm, hipStream_t stream) {
     typedef WideCfg<DK, NV, NWC, NSET> Cfg;
     const int total = prm.BH * prm.n_slices;
-    hipLaunchKernelGGL((kda_inter_wide_kernel<Cfg, SCAN>), dim3(total), dim3(Cfg::NT), 0, stream,
+    hipLaunchKernelGGL((kda_inter_wide_kernel<Cfg, SCAN, REV>), dim3(total), dim3(Cfg::NT), 0, stream,
                        prm);
     return hipGetLastError();
 }
@@ -759,6 +786,11 @@ hipError_t launch_inter_wide_scan(InterParams prm, int dk, int nv, hipStream_t s
         return hipErrorInvalidValue;
     prm.n_slices = prm.DV / nv;
     // (32 columns only: the 64-column scan form would spill registers)
+    if (prm.rev) {
+        if (dk == 128 && nv == 32) return launch_wide_cfg<128, 32, 2, KDA_WIDE_NSET32, true, true>(prm, stream);
+        if (dk == 64 && nv == 32) return launch_wide_cfg<64, 32, 2, KDA_WIDE_NSET32, true, true>(prm, stream);
+        return hipErrorInvalidValue;
+    }
     if (dk == 128 && nv == 32) return launch_wide_cfg<128, 32, 2, KDA_WIDE_NSET32, true>(prm, stream);
     if (dk == 64 && nv == 32) return launch_wide_cfg<64, 32, 2, KDA_WIDE_NSET32, true>(prm, stream);
     return hipErrorInvalidValue;

@@ -147,7 +147,17 @@ struct InterParams {
     void* u_all = nullptr;
     int scan_shift = 0;
     int n_store = 0;
+    // scan form over reverse records (rev_rec_bytes each): every step also
+    // adds a second product, S += K2^T U2, K2^T in the record's Q~ section
+    // (in K^T's order) and U2 in an extra section (in U's order)
+    int rev = 0;
 };
+
+// Bytes of one reverse record: the forward record's sections, then U2 (bf16
+// [C][DV] in accumulator order).
+__host__ __device__ constexpr uint32_t rev_rec_bytes(int dk, int dv) {
+    return rec_layout(dk, dv, 64, 2, true).bytes + rec_align((uint32_t)(64 * dv * 2));
+}
 
 // Device address of the calling thread's current device's static buffer of
 // kda_chunk_fwd_noalloc (KDA_NOALLOC_SCRATCH_BYTES), looked up once per device.
@@ -265,8 +275,8 @@ struct GateWiden {
 hipError_t launch_gate_widen(const GateWiden& prm, hipStream_t stream);
 
 // Records of the reverse state pass, built from the forward's wide records
-// and dJ/do: chunk c of head bh becomes entries 2 (nc - 1 - c) and
-// 2 (nc - 1 - c) + 1 of [BH][2 nc] records of the same layout.
+// and dJ/do: chunk c of head bh becomes entry nc - 1 - c of [BH][nc] records
+// of rev_rec_bytes each.
 struct RevRecParams {
     const void* recs;       // [BH][nc] forward records (wide order)
     void* rrecs;            // [BH][2 nc]
