@@ -624,6 +624,16 @@ __global__ void __launch_bounds__(512) kda_chunk_grad_kernel(ChunkGradParams prm
     bf16* xuk = (bf16*)((char*)xl + Cfg::XL);           // [C][16]: upper sums' operands
     bf16* xuq = (bf16*)((char*)xuk + Cfg::XL);
     const int ch = 16 * w + lr;
+    // Each wave builds and reads only its own operand tiles here (everything
+    // else the loop reads was written before it), so the waves need no
+    // workgroup barrier inside it: a wave's LDS accesses take effect in order
+    // once they have issued, and the fence keeps the compiler from moving them.
+    auto wave_fence = []() {
+        asm volatile("" ::: "memory");
+        __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0)
+        __builtin_amdgcn_wave_barrier();
+        asm volatile("" ::: "memory");
+    };
 #pragma unroll 1
     for (int s = 0; s < NB; ++s) {
         // Block s is "moderate" for this wave when its total decay is at least
@@ -696,7 +706,7 @@ __global__ void __launch_bounds__(512) kda_chunk_grad_kernel(ChunkGradParams prm
                 }
             }
         }
-        __syncthreads();
+        wave_fence();
         if (w < NCBK) {
             // lower sums, rows 16s..: R = decayed(dA) K, RP = decayed(dP) K (j < r)
             {
@@ -778,7 +788,7 @@ __global__ void __launch_bounds__(512) kda_chunk_grad_kernel(ChunkGradParams prm
                 for (int i = 0; i < 4; ++i) dkb[J][i] += acc[i];
             }
         }
-        __syncthreads();
+        wave_fence();
     }
 
     // ---- outputs: dq, dk; dg = q dq + k (dka - dkb) -> reverse sums; dbeta -----------
