@@ -6,7 +6,8 @@ d_k=d_v=128, all inputs bf16, fp32 state, S_final returned; one step = one
 kda_chunk_fwd over that batch.  Further legs in the same line: the Gated
 DeltaNet workload (4 x 16 heads x 4096, scalar decay), the KDA workload
 (2 x 32 heads x 8192), the KDA decode workload (256 sequences x 32 heads, fp32
-state updated in place for 64 steps), gradients, raw inputs with fused
+state updated in place for 64 steps), gradients (token by token, and in
+chunkwise form on the Gated DeltaNet and KDA workloads), raw inputs with fused
 preprocessing, and normalized linear attention.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload N]
@@ -325,12 +326,12 @@ def bench_bwd(torch, kda, gen, w, steps, warmup):
 
 def chunk_grad_flops(w):
     """Algorithmic matrix-core flops of one kda_chunk_grad_kernel launch:
-    per chunk of C = 64 tokens and head, 2 x (C^2 dv for dY = T^T du, 4 C dk dv
-    for V - K~ S, dO S^T, dY S^T and u G^T, 2 C^2 dv for dY u^T and dO u^T,
-    and 4 triangular decayed sums of C^2/2 dk each)."""
+    per chunk of C = 64 tokens and head, 2 x (C^2 dv for dY = T^T du, 3 C dk dv
+    for dO S^T, dY S^T and u G^T, 2 C^2 dv for dY u^T and dO u^T, and 4
+    triangular decayed sums of C^2/2 dk each)."""
     C = 64
     nc = -(-w.L // C)
-    per = 2 * (C * C * w.dv + 4 * C * w.dk * w.dv + 2 * C * C * w.dv + 2 * C * C * w.dk)
+    per = 2 * (C * C * w.dv + 3 * C * w.dk * w.dv + 2 * C * C * w.dv + 2 * C * C * w.dk)
     return w.B * w.H * nc * per
 
 

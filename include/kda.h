@@ -391,10 +391,10 @@ size_t kda_recurrence_bwd_workspace_bytes(const kda_shape* shape);
  *   qkv_dtype must be KDA_BF16 (q, k, v and dout bf16; KDA_ERR_DTYPE
  *            otherwise); every decay mode and gate dtype is accepted.
  *   workspace_bytes >= kda_chunk_bwd_workspace_bytes(shape): the forward's
- *            chunk records of the whole sequence, two reverse records per
- *            chunk, and fp32 copies of four states per chunk (about
- *            4.1 KiB per token and head at d_k = d_v = 128); not kept after
- *            the call's kernels end.
+ *            chunk records of the whole sequence, one reverse record per
+ *            chunk, T^T and four states per chunk (about 5.3 KiB per token
+ *            and head at d_k = d_v = 128); not kept after the call's
+ *            kernels end.
  *   Arithmetic: bf16 operands on the matrix cores with fp32 accumulation, as
  *            the forward's chunked prefill; every output is written once (no
  *            atomics), so repeated calls give the same bits.
