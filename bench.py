@@ -584,6 +584,8 @@ def main():
                     help="skip the Gated DeltaNet gradient leg (keep the KDA one)")
     ap.add_argument("--no-chunk-bwd", action="store_true",
                     help="skip the chunkwise gradient (kda_chunk_bwd) legs")
+    ap.add_argument("--no-prefill-legs", action="store_true",
+                    help="skip the prefill legs other than the headline workload's")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run one plain 256 MiB device copy (a known-size "
@@ -660,6 +662,8 @@ def main():
     legs = [("prefill_gated_deltanet", 2)]
     if not args.no_kda:
         legs += [("prefill_kda", 3), ("prefill_kda_long_context", 4)]
+    if args.no_prefill_legs:
+        legs = []
     for key, n in legs:
         if n != args.workload:
             out[key] = bench_prefill_leg(torch, kda, gen, gen.WORKLOADS[n], args.steps,

@@ -39,6 +39,13 @@ KERNEL_SOURCES = {
     "kda_inter_quad_kernel": ["kda_inter_wide.hip"],
     "kda_decode_kernel": ["kda_decode.hip"],
     "kda_bwd_kernel": ["kda_bwd.hip"],
+    # chunkwise gradients: the reverse-record builder, the gradient kernel, and
+    # the wide state pass in its scan forms (forward, reverse), which rocprofv3
+    # lists as kda_inter_wide_kernel instances (traffic --match)
+    "kda_rev_records_kernel": ["kda_chunk_bwd.hip"],
+    "kda_chunk_grad_kernel": ["kda_chunk_bwd.hip"],
+    "kda_inter_wide_scan": ["kda_inter_wide.hip"],
+    "kda_inter_wide_scan_rev": ["kda_inter_wide.hip"],
 }
 COMMON_SOURCES = ["kda_device.h", "kda_internal.h"]
 # the prefill kernels' launch shapes (spans, column slices) are set by the ABI layer
@@ -82,8 +89,8 @@ def per_dispatch_kib(pass_dir: str, counter: str, match: str, also: str = "") ->
 
 
 def traffic(fetch_dir: str, write_dir: str, kernel: str, also: str = "") -> dict:
-    """HBM bytes per dispatch of `kernel` (every dispatch whose name also
-    contains `also`: one template instance when a run launches several)."""
+    """HBM bytes per dispatch of `kernel` (every dispatch whose name contains
+    `kernel` and `also`: one template instance when a run launches several)."""
     fk = per_dispatch_kib(fetch_dir, "FETCH_SIZE", kernel, also)
     wk = per_dispatch_kib(write_dir, "WRITE_SIZE", kernel, also)
     fc = per_dispatch_kib(fetch_dir, "FETCH_SIZE", COPY_KERNEL)
@@ -165,13 +172,15 @@ def main():
     t.add_argument("--also", default="", help="a further substring of the kernel name "
                    "(one template instance, e.g. Lb1ELb1E for the KDA intra-chunk kernel "
                    "writing MFMA-order records)")
+    t.add_argument("--match", default="", help="the kernel name to look for in the counter "
+                   "files when it differs from --kernel (the scan forms of the wide state pass)")
     a = ap.parse_args()
     if a.cmd == "mfma":
         for k in a.kernel:
             for rec in mfma(a.pmc, k):
                 print(json.dumps(rec))
         return
-    rec = traffic(a.fetch, a.write, a.kernel, a.also)
+    rec = traffic(a.fetch, a.write, a.match or a.kernel, a.also)
     rec["source_sha256"] = source_digest(a.kernel)
     data = {}
     if os.path.exists(a.out):
