@@ -335,10 +335,26 @@ def chunk_grad_flops(w):
     return w.B * w.H * nc * per
 
 
+def chunk_grad_bytes(w):
+    """Algorithmic HBM bytes of one kda_chunk_grad_kernel launch: per chunk
+    of C = 64 tokens and head, every input read once (T^T fp32; du, u, dO, v,
+    q, k bf16; S and G fp32; per-channel ln alpha and beta in the gate type,
+    fp32 when widened from one decay per token) and every gradient written
+    once (fp32)."""
+    C, dk, dv = 64, w.dk, w.dv
+    nc = -(-w.L // C)
+    g = 2 if (w.gate_dtype == "bf16" and w.alpha_mode == "channel") else 4
+    reads = C * C * 4 + 4 * C * dv * 2 + 2 * C * dk * 2 + C * dk * g + C * g + 2 * dk * dv * 4
+    dla = {"channel": C * dk * 4, "head": C * 4}.get(w.alpha_mode, 0)
+    writes = 2 * C * dk * 4 + C * dv * 4 + dla + C * 4
+    return w.B * w.H * nc * (reads + writes)
+
+
 def bench_chunk_bwd(torch, kda, gen, w, steps, warmup):
     """Chunkwise gradients (kda_chunk_bwd) of one prefill workload (dJ/do
     given, dJ/dS_final zero): tokens/s, every kernel's time, and the
-    chunk-parallel gradient kernel against the bf16 matrix-core peak."""
+    chunk-parallel gradient kernel against HBM (its bound: the counters read
+    3.6 TB/s on the 2 x 32 x 8192 workload) and against bf16 MFMA."""
     log(f"chunkwise gradients, workload {w.name}: drawing inputs")
     x = gen.prefill_inputs(w, threads=16)
     d = {n: to_dev(torch, x[n], w.qkv_dtype if n in ("q", "k", "v") else w.gate_dtype)
@@ -366,17 +382,20 @@ def bench_chunk_bwd(torch, kda, gen, w, steps, warmup):
     kern = kernel_times(torch, kda, steps, step)
     per, ms = kern["kda_chunk_grad_kernel"]
     tflops = chunk_grad_flops(w) / per / (ms * 1e-3) / 1e12
+    gbs = chunk_grad_bytes(w) / per / (ms * 1e-3) / 1e9
     log(f"chunkwise gradients {w.name}: {wall * 1e3 / steps:.3f} ms/step wall; "
         + ", ".join(f"{n} {pk:g} x {m * 1e3:.1f} us" for n, (pk, m) in kern.items()))
     out = {"workload": w.name, "tokens_per_s": w.B * w.L / (wall / steps), "unit": "tokens/s",
            "ms_per_step": wall * 1e3 / steps, "workspace_bytes": wsb,
            "kernels": {n: {"launches_per_step": pk, "avg_us": m * 1e3} for n, (pk, m) in kern.items()},
-           "roofline": {"kernel": "kda_chunk_grad_kernel", "bound": "mfma", "achieved": tflops,
-                        "peak": BF16_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
-                        "frac": tflops / BF16_MFMA_PEAK_TFLOPS,
+           "roofline": {"kernel": "kda_chunk_grad_kernel", "bound": "hbm", "achieved": gbs,
+                        "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": gbs / HBM_PEAK_GBS,
                         "traffic": measured_traffic("kda_chunk_grad_kernel", w.name),
-                        "algorithmic_flops_per_launch": chunk_grad_flops(w) / per,
-                        "avg_kernel_us": ms * 1e3}}
+                        "algorithmic_bytes_per_launch": chunk_grad_bytes(w) / per,
+                        "avg_kernel_us": ms * 1e3,
+                        "mfma": {"achieved": tflops, "peak": BF16_MFMA_PEAK_TFLOPS,
+                                 "unit": "TFLOP/s", "frac": tflops / BF16_MFMA_PEAK_TFLOPS,
+                                 "algorithmic_flops_per_launch": chunk_grad_flops(w) / per}}}
     del d, do, ws
     torch.cuda.empty_cache()
     return out

@@ -78,21 +78,37 @@ def _rows(pass_dir: str) -> List[dict]:
     return rows
 
 
-def per_dispatch_kib(pass_dir: str, counter: str, match: str, also: str = "") -> List[float]:
+def per_dispatch_kib(pass_dir: str, counter: str, match: str, also: str = "",
+                     first: int = 0, last: int = -1) -> List[float]:
     """Counter value (KiB) of every dispatch whose kernel name contains `match`
-    (and `also`)."""
+    (and `also`), with a dispatch id in [first, last] (last < 0: no bound)."""
     vals: Dict[str, float] = {}
     for r in _rows(pass_dir):
+        d = int(r["Dispatch_Id"])
+        if d < first or (last >= 0 and d > last):
+            continue
         if r["Counter_Name"] == counter and match in r["Kernel_Name"] and also in r["Kernel_Name"]:
             vals[r["Dispatch_Id"]] = vals.get(r["Dispatch_Id"], 0.0) + float(r["Counter_Value"])
     return [vals[k] for k in sorted(vals, key=int)]
 
 
-def traffic(fetch_dir: str, write_dir: str, kernel: str, also: str = "") -> dict:
+def first_dispatch(pass_dir: str, match: str, also: str = "") -> int:
+    """Dispatch id of the first dispatch whose kernel name contains `match` and `also`."""
+    ids = [int(r["Dispatch_Id"]) for r in _rows(pass_dir)
+           if match in r["Kernel_Name"] and also in r["Kernel_Name"]]
+    if not ids:
+        raise ValueError(f"no dispatch of {match} {also} under {pass_dir}")
+    return min(ids)
+
+
+def traffic(fetch_dir: str, write_dir: str, kernel: str, also: str = "",
+            window=((0, -1), (0, -1))) -> dict:
     """HBM bytes per dispatch of `kernel` (every dispatch whose name contains
-    `kernel` and `also`: one template instance when a run launches several)."""
-    fk = per_dispatch_kib(fetch_dir, "FETCH_SIZE", kernel, also)
-    wk = per_dispatch_kib(write_dir, "WRITE_SIZE", kernel, also)
+    `kernel` and `also`: one template instance when a run launches several;
+    `window`: the dispatch-id ranges of the fetch and the write pass, one leg
+    of a run that launches the same instance in several legs)."""
+    fk = per_dispatch_kib(fetch_dir, "FETCH_SIZE", kernel, also, *window[0])
+    wk = per_dispatch_kib(write_dir, "WRITE_SIZE", kernel, also, *window[1])
     fc = per_dispatch_kib(fetch_dir, "FETCH_SIZE", COPY_KERNEL)
     wc = per_dispatch_kib(write_dir, "WRITE_SIZE", COPY_KERNEL)
     if not fk or not wk:
@@ -122,8 +138,9 @@ XCDS = 8          # GRBM_GUI_ACTIVE comes summed over the 8 XCDs
 
 
 def mfma(pass_dir: str, kernel: str) -> List[dict]:
-    """MFMA utilisation of one kernel's dispatches, grouped by grid size (one
-    group per workload): the MFMA pipes' busy cycles summed over all SIMDs /
+    """MFMA utilisation of one kernel's dispatches, grouped by template
+    instance and grid size (one group per workload and instance): the MFMA
+    pipes' busy cycles summed over all SIMDs /
     (the GPU's active cycles x SIMDs), and the bf16 and fp32 MFMA flops the SQ
     counted (MOPS x 512).  rocprofv3 gives one row per dispatch and counter;
     GRBM_GUI_ACTIVE is the sum of the XCDs' counts, so one XCD's active
@@ -132,22 +149,22 @@ def mfma(pass_dir: str, kernel: str) -> List[dict]:
     for r in _rows(pass_dir):
         if kernel not in r["Kernel_Name"]:
             continue
-        d = disp.setdefault(r["Dispatch_Id"], {"grid": int(r["Grid_Size"]),
+        d = disp.setdefault(r["Dispatch_Id"], {"grid": int(r["Grid_Size"]), "name": r["Kernel_Name"],
                                                 "ns": int(r["End_Timestamp"]) - int(r["Start_Timestamp"])})
         d[r["Counter_Name"]] = float(r["Counter_Value"])
-    groups: Dict[int, List[dict]] = {}
+    groups: Dict[tuple, List[dict]] = {}
     for d in disp.values():
         if "SQ_VALU_MFMA_BUSY_CYCLES" in d and d.get("GRBM_GUI_ACTIVE", 0) > 0:
-            groups.setdefault(d["grid"], []).append(d)
+            groups.setdefault((d["grid"], d["name"]), []).append(d)
     if not groups:
         raise ValueError(f"no dispatch of {kernel} with MFMA counters under {pass_dir}")
     out = []
-    for grid, ds in sorted(groups.items()):
+    for (grid, name), ds in sorted(groups.items()):
         n = len(ds)
         avg = lambda key: sum(d.get(key, 0.0) for d in ds) / n
         util = sum(d["SQ_VALU_MFMA_BUSY_CYCLES"] / (d["GRBM_GUI_ACTIVE"] / XCDS * SIMDS)
                    for d in ds) / n
-        out.append({"kernel": kernel, "grid_size": grid, "dispatches": n,
+        out.append({"kernel": kernel, "instance": name, "grid_size": grid, "dispatches": n,
                     "avg_dispatch_us": avg("ns") / 1e3,
                     "mfma_busy_cycles": avg("SQ_VALU_MFMA_BUSY_CYCLES"),
                     "gui_active_cycles_per_xcd": avg("GRBM_GUI_ACTIVE") / XCDS,
@@ -174,13 +191,22 @@ def main():
                    "writing MFMA-order records)")
     t.add_argument("--match", default="", help="the kernel name to look for in the counter "
                    "files when it differs from --kernel (the scan forms of the wide state pass)")
+    t.add_argument("--from-kernel", default="", help="count only dispatches from the first "
+                   "dispatch of this kernel-name substring on (a later leg of the run)")
+    t.add_argument("--until-kernel", default="", help="count only dispatches before the "
+                   "first dispatch of this kernel-name substring (an earlier leg)")
     a = ap.parse_args()
     if a.cmd == "mfma":
         for k in a.kernel:
             for rec in mfma(a.pmc, k):
                 print(json.dumps(rec))
         return
-    rec = traffic(a.fetch, a.write, a.match or a.kernel, a.also)
+    win = []
+    for d in (a.fetch, a.write):
+        lo = first_dispatch(d, *a.from_kernel.split("+", 1)) if a.from_kernel else 0
+        hi = first_dispatch(d, *a.until_kernel.split("+", 1)) - 1 if a.until_kernel else -1
+        win.append((lo, hi))
+    rec = traffic(a.fetch, a.write, a.match or a.kernel, a.also, tuple(win))
     rec["source_sha256"] = source_digest(a.kernel)
     data = {}
     if os.path.exists(a.out):
