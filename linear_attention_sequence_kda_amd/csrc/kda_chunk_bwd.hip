@@ -561,36 +561,20 @@ __global__ void __launch_bounds__(512) kda_chunk_grad_kernel(ChunkGradParams prm
     // would not resolve)
     st_state(rg, sGG);
     {
-        // d g_n += e^{g_n} sum_j G[c][j] S[c][j]: this thread's pieces of G
-        // against the same pieces of S (the DV/8 pieces of a row in adjacent lanes)
-        // (S read again from memory, two pieces at a time: both loads go out
-        // before the first wait)
-        const float* gS = prm.S_all + xf * DK * DV;
+        // d g_n += e^{g_n} sum_j G[c][j] S[c][j]: this thread's fp32 pieces of
+        // G against the fp32 pieces of S it loaded for the S tile (the same
+        // elements; the DV/8 pieces of a row in adjacent lanes)
 #pragma unroll
-        for (int h = 0; h < NP_KV; h += 2) {
-            floatx4 sa[2][2];
+        for (int it = 0; it < NP_KV; ++it) {
+            const int i = tid + NT * it;
+            const int r = i / (DV / 8);
+            const floatx4 a = rs[it][0], b = rs[it][1];
+            float d = a[0] * rg[it][0][0] + a[1] * rg[it][0][1] + a[2] * rg[it][0][2] +
+                      a[3] * rg[it][0][3] + b[0] * rg[it][1][0] + b[1] * rg[it][1][1] +
+                      b[2] * rg[it][1][2] + b[3] * rg[it][1][3];
 #pragma unroll
-            for (int u2 = 0; u2 < 2; ++u2) {
-                const int i = tid + NT * (h + u2 < NP_KV ? h + u2 : h);
-                const int r = i / (DV / 8), c8 = (i % (DV / 8)) * 8;
-                sa[u2][0] = *(const floatx4*)(gS + r * DV + c8);
-                sa[u2][1] = *(const floatx4*)(gS + r * DV + c8 + 4);
-            }
-#pragma unroll
-            for (int u2 = 0; u2 < 2; ++u2) {
-                const int it = h + u2;
-                if (it < NP_KV) {
-                    const int i = tid + NT * it;
-                    const int r = i / (DV / 8);
-                    const floatx4 a = sa[u2][0], b = sa[u2][1];
-                    float d = a[0] * rg[it][0][0] + a[1] * rg[it][0][1] + a[2] * rg[it][0][2] +
-                              a[3] * rg[it][0][3] + b[0] * rg[it][1][0] + b[1] * rg[it][1][1] +
-                              b[2] * rg[it][1][2] + b[3] * rg[it][1][3];
-#pragma unroll
-                    for (int o = 1; o < DV / 8; o <<= 1) d += __shfl_xor(d, o);
-                    if ((i % (DV / 8)) == 0) sEn[r] = __expf(sG[(C - 1) * PG + r]) * d;
-                }
-            }
+            for (int o = 1; o < DV / 8; o <<= 1) d += __shfl_xor(d, o);
+            if (i < DK * DV / 8 && (i % (DV / 8)) == 0) sEn[r] = __expf(sG[(C - 1) * PG + r]) * d;
         }
     }
     uint4 rq[NPR];
