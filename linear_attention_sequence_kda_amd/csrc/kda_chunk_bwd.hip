@@ -277,7 +277,7 @@ __device__ __forceinline__ float sum16(float x) {
     return x;
 }
 
-template <int DK, int DV, bool GBF>
+template <int DK, int DV, bool GBF, bool SCAL>
 __global__ void __launch_bounds__(512) kda_chunk_grad_kernel(ChunkGradParams prm) {
     typedef GradCfg<DK, DV> Cfg;
     typedef Frag<bf16> F;
@@ -406,7 +406,10 @@ __global__ void __launch_bounds__(512) kda_chunk_grad_kernel(ChunkGradParams prm
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
             const int r = 16 * p + i;
-            const float x = gate_at(prm.la, (row0 + (r < n ? r : n - 1)) * DK + (ch < DK ? ch : DK - 1));
+            // (one decay per token: every channel holds the same value, so
+            // column 0 serves them all)
+            const float x = gate_at(prm.la, (row0 + (r < n ? r : n - 1)) * DK +
+                                                (SCAL ? 0 : (ch < DK ? ch : DK - 1)));
             v[i] = (ch < DK && r < n) ? x : 0.f;
         }
 #pragma unroll
@@ -548,7 +551,10 @@ __global__ void __launch_bounds__(512) kda_chunk_grad_kernel(ChunkGradParams prm
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const int r = 16 * R + 4 * q + i, j = 16 * J + lr;
-            const float x = j < r ? (mat ? acc[i] : -acc[i]) : 0.f;
+            float x = j < r ? (mat ? acc[i] : -acc[i]) : 0.f;
+            // one decay per token: the factor e^{g_r - g_j} (<= 1 below the
+            // diagonal) goes into the tile here, in fp32
+            if constexpr (SCAL) x *= j < r ? __expf(sG[r * PG] - sG[j * PG]) : 0.f;
             dst[r * PCC + j] = (bf16)x;
             if (mat && j == r) sPd[r] = acc[i];
         }
@@ -618,114 +624,35 @@ __global__ void __launch_bounds__(512) kda_chunk_grad_kernel(ChunkGradParams prm
         __builtin_amdgcn_wave_barrier();
         asm volatile("" ::: "memory");
     };
-#pragma unroll 1
-    for (int s = 0; s < NB; ++s) {
-        // Block s is "moderate" for this wave when its total decay is at least
-        // -60 in each of the wave's 16 channels: then one anchor per sum
-        // covers the diagonal block too (its factors stay below e^60) and the
-        // whole sum runs on MFMA.  Otherwise the diagonal block is summed
-        // directly and only the blocks off it take anchored MFMA operands.
-        const float zb = w < NCBK ? sG[(16 * s + 15) * PG + ch] - (s ? sG[(16 * s - 1) * PG + ch] : 0.f)
-                                  : 0.f;
-        const bool mild = __all(zb >= -60.f);
-        // operands: lower sums of row block s anchored at a = 16s - 1 (rows
-        // j < 16s, and with a mild block also its rows), upper sums of row
-        // block s anchored at a = 16s + 15 (rows r > a, and with a mild block
-        // also the block's rows)
-        // (each lane builds 8 channels of one row per step: one 16-byte k or q
-        // piece, two of g, one of the anchor's g)
+    if constexpr (SCAL) {
+        // One decay per token (or none): D_rj = e^{g_r - g_j} is one scalar per
+        // pair, already inside the dA and dP tiles, so the three decayed sums
+        // are plain products:
+        //   R = (dA o D) K,  RP = (dP o D) K,  RU = (dA o D)^T (beta K) + (dP o D)^T Q
         if (w < NCBK) {
-            const int h8 = 16 * w + 8 * (l & 1);  // this lane's 8 channels
-            const int la = 16 * s - 1;
-            const int lrows = mild ? 16 * s + 16 : 16 * s;
-            const int KR = (lrows + 31) / 32 * 32;
-            if (lrows > 0) {
-                floatx4 a0 = {0.f, 0.f, 0.f, 0.f}, a1 = a0;
-                if (la >= 0) {
-                    a0 = *(const floatx4*)(sG + la * PG + h8);
-                    a1 = *(const floatx4*)(sG + la * PG + h8 + 4);
-                }
-                for (int t = l; t < KR * 2; t += 64) {
-                    const int j = t >> 1;
-                    bf16x8 x = {};
-                    if (j < lrows) {
-                        const bf16x8 kv = *(const bf16x8*)(sK + j * PK + h8);
-                        const floatx4 g0 = *(const floatx4*)(sG + j * PG + h8);
-                        const floatx4 g1 = *(const floatx4*)(sG + j * PG + h8 + 4);
-#pragma unroll
-                        for (int e = 0; e < 4; ++e) {
-                            x[e] = (bf16)((float)kv[e] * __expf(a0[e] - g0[e]));
-                            x[4 + e] = (bf16)((float)kv[4 + e] * __expf(a1[e] - g1[e]));
-                        }
-                    }
-                    *(bf16x8*)(xl + j * 16 + 8 * (l & 1)) = x;
-                }
-            }
-            const int ua = 16 * s + 15;
-            const int ufirst = mild ? 16 * s : ua + 1;  // first row taken
-            if (ufirst < C) {
-                const int k0 = ufirst / 32 * 32;
-                const floatx4 a0 = *(const floatx4*)(sG + ua * PG + h8);
-                const floatx4 a1 = *(const floatx4*)(sG + ua * PG + h8 + 4);
-                for (int t = l; t < (C - k0) * 2; t += 64) {
-                    const int r = k0 + (t >> 1);
-                    bf16x8 xk = {}, xq = {};
-                    if (r >= ufirst) {
-                        const float br = sBeta[r];
-                        const bf16x8 kv = *(const bf16x8*)(sK + r * PK + h8);
-                        const bf16x8 qv = *(const bf16x8*)(sQ + r * PK + h8);
-                        const floatx4 g0 = *(const floatx4*)(sG + r * PG + h8);
-                        const floatx4 g1 = *(const floatx4*)(sG + r * PG + h8 + 4);
-#pragma unroll
-                        for (int e = 0; e < 4; ++e) {
-                            const float f0 = __expf(g0[e] - a0[e]), f1 = __expf(g1[e] - a1[e]);
-                            xk[e] = (bf16)(br * (float)kv[e] * f0);
-                            xk[4 + e] = (bf16)(br * (float)kv[4 + e] * f1);
-                            xq[e] = (bf16)((float)qv[e] * f0);
-                            xq[4 + e] = (bf16)((float)qv[4 + e] * f1);
-                        }
-                    }
-                    *(bf16x8*)(xuk + r * 16 + 8 * (l & 1)) = xk;
-                    *(bf16x8*)(xuq + r * 16 + 8 * (l & 1)) = xq;
-                }
-            }
-        }
-        wave_fence();
-        if (w < NCBK) {
-            // lower sums, rows 16s..: R = decayed(dA) K, RP = decayed(dP) K (j < r)
             {
-                const int R = s, la = 16 * R - 1;
-                const int lrows = mild ? 16 * R + 16 : 16 * R;
+                // this wave's 16 channels of beta K, [C][16] (one row per lane)
+                const float br = sBeta[l];
+                const bf16x8 k0 = *(const bf16x8*)(sK + l * PK + 16 * w);
+                const bf16x8 k1 = *(const bf16x8*)(sK + l * PK + 16 * w + 8);
+                bf16x8 x0, x1;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    x0[e] = (bf16)(br * (float)k0[e]);
+                    x1[e] = (bf16)(br * (float)k1[e]);
+                }
+                *(bf16x8*)(xuk + l * 16) = x0;
+                *(bf16x8*)(xuk + l * 16 + 8) = x1;
+            }
+            wave_fence();
+#pragma unroll
+            for (int R = 0; R < NB; ++R) {
+                // columns j < r <= 16 R + 15 (the tiles are zero from the diagonal on)
+                constexpr int KS = Frag<bf16>::KS;
+                const int KR = (16 * R + 16 + KS - 1) / KS * KS;
                 floatx4 accR = {0.f, 0.f, 0.f, 0.f}, accP = accR;
-                if (lrows > 0) {
-                    const int KR = (lrows + 31) / 32 * 32;
-                    accR = mma_block_bt<bf16>(accR, sdA + 16 * R * PCC, PCC, xl, 16, 0, KR);
-                    accP = mma_block_bt<bf16>(accP, sdP + 16 * R * PCC, PCC, xl, 16, 0, KR);
-                    const float ga = la >= 0 ? sG[la * PG + ch] : 0.f;
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        const float f = __expf(sG[(16 * R + 4 * q + i) * PG + ch] - ga);
-                        accR[i] *= f;
-                        accP[i] *= f;
-                    }
-                }
-                if (!mild) {
-                    float gr[4];
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) gr[i] = sG[(16 * R + 4 * q + i) * PG + ch];
-#pragma unroll 4
-                    for (int jj = 0; jj < 16; ++jj) {
-                        const int j = 16 * R + jj;
-                        const float gj = sG[j * PG + ch], kj = (float)sK[j * PK + ch];
-#pragma unroll
-                        for (int i = 0; i < 4; ++i) {
-                            const int r = 16 * R + 4 * q + i;
-                            const float e = __expf(fminf(gr[i] - gj, 0.f)) * kj;
-                            accP[i] += (float)sdP[r * PCC + j] * e;
-                            accR[i] += (float)sdA[r * PCC + j] * e;
-                        }
-                    }
-                }
+                accR = mma_block_bt<bf16>(accR, sdA + 16 * R * PCC, PCC, sK, PK, 16 * w, KR);
+                accP = mma_block_bt<bf16>(accP, sdP + 16 * R * PCC, PCC, sK, PK, 16 * w, KR);
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
                     const int r = 16 * R + 4 * q + i;
@@ -735,44 +662,176 @@ __global__ void __launch_bounds__(512) kda_chunk_grad_kernel(ChunkGradParams prm
                     if (lr == 0) sDB[(8 + w) * C + r] = part;
                 }
             }
-            // upper sums, rows 16s..: RU = decayed^T(beta dA) K + decayed^T(dP) Q
-            {
-                const int J = s, ua = 16 * J + 15;
-                const int ufirst = mild ? 16 * J : ua + 1;
+#pragma unroll
+            for (int J = 0; J < NB; ++J) {
+                // rows r > j >= 16 J; both operands read transposed
+                constexpr int KS = Frag<bf16>::KS;
                 floatx4 acc = {0.f, 0.f, 0.f, 0.f};
-                if (ufirst < C) {
-                    const int k0 = ufirst / 32 * 32;
-                    // both operands read transposed: A[j][r] = dA[r][j], B[c][r] = x~[r][c]
-                    for (int kk = k0; kk < C; kk += 32) {
-                        acc = F::mma(acc, load_frag_tr(sdA, PCC, kk, 16 * J), load_frag_tr(xuk, 16, kk, 0));
-                        acc = F::mma(acc, load_frag_tr(sdP, PCC, kk, 16 * J), load_frag_tr(xuq, 16, kk, 0));
-                    }
-                    const float ga = sG[ua * PG + ch];
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) acc[i] *= __expf(ga - sG[(16 * J + 4 * q + i) * PG + ch]);
-                }
-                if (!mild) {
-                    float gj[4];
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) gj[i] = sG[(16 * J + 4 * q + i) * PG + ch];
-#pragma unroll 4
-                    for (int rr = 0; rr < 16; ++rr) {
-                        const int r = 16 * J + rr;
-                        const float g_r = sG[r * PG + ch];
-                        const float kr = sBeta[r] * (float)sK[r * PK + ch], qr = (float)sQ[r * PK + ch];
-#pragma unroll
-                        for (int i = 0; i < 4; ++i) {
-                            const int j = 16 * J + 4 * q + i;
-                            const float e = __expf(fminf(g_r - gj[i], 0.f));
-                            acc[i] += e * ((float)sdP[r * PCC + j] * qr + (float)sdA[r * PCC + j] * kr);
-                        }
-                    }
+                for (int kk = 16 * J / KS * KS; kk < C; kk += KS) {
+                    acc = F::mma(acc, load_frag_tr(sdA, PCC, kk, 16 * J), load_frag_tr(xuk, 16, kk, 0));
+                    acc = F::mma(acc, load_frag_tr(sdP, PCC, kk, 16 * J), load_frag_tr(sQ, PK, kk, 16 * w));
                 }
 #pragma unroll
                 for (int i = 0; i < 4; ++i) dkb[J][i] += acc[i];
             }
         }
-        wave_fence();
+    } else {
+    #pragma unroll 1
+        for (int s = 0; s < NB; ++s) {
+            // Block s is "moderate" for this wave when its total decay is at least
+            // -60 in each of the wave's 16 channels: then one anchor per sum
+            // covers the diagonal block too (its factors stay below e^60) and the
+            // whole sum runs on MFMA.  Otherwise the diagonal block is summed
+            // directly and only the blocks off it take anchored MFMA operands.
+            const float zb = w < NCBK ? sG[(16 * s + 15) * PG + ch] - (s ? sG[(16 * s - 1) * PG + ch] : 0.f)
+                                      : 0.f;
+            const bool mild = __all(zb >= -60.f);
+            // operands: lower sums of row block s anchored at a = 16s - 1 (rows
+            // j < 16s, and with a mild block also its rows), upper sums of row
+            // block s anchored at a = 16s + 15 (rows r > a, and with a mild block
+            // also the block's rows)
+            // (each lane builds 8 channels of one row per step: one 16-byte k or q
+            // piece, two of g, one of the anchor's g)
+            if (w < NCBK) {
+                const int h8 = 16 * w + 8 * (l & 1);  // this lane's 8 channels
+                const int la = 16 * s - 1;
+                const int lrows = mild ? 16 * s + 16 : 16 * s;
+                const int KR = (lrows + 31) / 32 * 32;
+                if (lrows > 0) {
+                    floatx4 a0 = {0.f, 0.f, 0.f, 0.f}, a1 = a0;
+                    if (la >= 0) {
+                        a0 = *(const floatx4*)(sG + la * PG + h8);
+                        a1 = *(const floatx4*)(sG + la * PG + h8 + 4);
+                    }
+                    for (int t = l; t < KR * 2; t += 64) {
+                        const int j = t >> 1;
+                        bf16x8 x = {};
+                        if (j < lrows) {
+                            const bf16x8 kv = *(const bf16x8*)(sK + j * PK + h8);
+                            const floatx4 g0 = *(const floatx4*)(sG + j * PG + h8);
+                            const floatx4 g1 = *(const floatx4*)(sG + j * PG + h8 + 4);
+    #pragma unroll
+                            for (int e = 0; e < 4; ++e) {
+                                x[e] = (bf16)((float)kv[e] * __expf(a0[e] - g0[e]));
+                                x[4 + e] = (bf16)((float)kv[4 + e] * __expf(a1[e] - g1[e]));
+                            }
+                        }
+                        *(bf16x8*)(xl + j * 16 + 8 * (l & 1)) = x;
+                    }
+                }
+                const int ua = 16 * s + 15;
+                const int ufirst = mild ? 16 * s : ua + 1;  // first row taken
+                if (ufirst < C) {
+                    const int k0 = ufirst / 32 * 32;
+                    const floatx4 a0 = *(const floatx4*)(sG + ua * PG + h8);
+                    const floatx4 a1 = *(const floatx4*)(sG + ua * PG + h8 + 4);
+                    for (int t = l; t < (C - k0) * 2; t += 64) {
+                        const int r = k0 + (t >> 1);
+                        bf16x8 xk = {}, xq = {};
+                        if (r >= ufirst) {
+                            const float br = sBeta[r];
+                            const bf16x8 kv = *(const bf16x8*)(sK + r * PK + h8);
+                            const bf16x8 qv = *(const bf16x8*)(sQ + r * PK + h8);
+                            const floatx4 g0 = *(const floatx4*)(sG + r * PG + h8);
+                            const floatx4 g1 = *(const floatx4*)(sG + r * PG + h8 + 4);
+    #pragma unroll
+                            for (int e = 0; e < 4; ++e) {
+                                const float f0 = __expf(g0[e] - a0[e]), f1 = __expf(g1[e] - a1[e]);
+                                xk[e] = (bf16)(br * (float)kv[e] * f0);
+                                xk[4 + e] = (bf16)(br * (float)kv[4 + e] * f1);
+                                xq[e] = (bf16)((float)qv[e] * f0);
+                                xq[4 + e] = (bf16)((float)qv[4 + e] * f1);
+                            }
+                        }
+                        *(bf16x8*)(xuk + r * 16 + 8 * (l & 1)) = xk;
+                        *(bf16x8*)(xuq + r * 16 + 8 * (l & 1)) = xq;
+                    }
+                }
+            }
+            wave_fence();
+            if (w < NCBK) {
+                // lower sums, rows 16s..: R = decayed(dA) K, RP = decayed(dP) K (j < r)
+                {
+                    const int R = s, la = 16 * R - 1;
+                    const int lrows = mild ? 16 * R + 16 : 16 * R;
+                    floatx4 accR = {0.f, 0.f, 0.f, 0.f}, accP = accR;
+                    if (lrows > 0) {
+                        const int KR = (lrows + 31) / 32 * 32;
+                        accR = mma_block_bt<bf16>(accR, sdA + 16 * R * PCC, PCC, xl, 16, 0, KR);
+                        accP = mma_block_bt<bf16>(accP, sdP + 16 * R * PCC, PCC, xl, 16, 0, KR);
+                        const float ga = la >= 0 ? sG[la * PG + ch] : 0.f;
+    #pragma unroll
+                        for (int i = 0; i < 4; ++i) {
+                            const float f = __expf(sG[(16 * R + 4 * q + i) * PG + ch] - ga);
+                            accR[i] *= f;
+                            accP[i] *= f;
+                        }
+                    }
+                    if (!mild) {
+                        float gr[4];
+    #pragma unroll
+                        for (int i = 0; i < 4; ++i) gr[i] = sG[(16 * R + 4 * q + i) * PG + ch];
+    #pragma unroll 4
+                        for (int jj = 0; jj < 16; ++jj) {
+                            const int j = 16 * R + jj;
+                            const float gj = sG[j * PG + ch], kj = (float)sK[j * PK + ch];
+    #pragma unroll
+                            for (int i = 0; i < 4; ++i) {
+                                const int r = 16 * R + 4 * q + i;
+                                const float e = __expf(fminf(gr[i] - gj, 0.f)) * kj;
+                                accP[i] += (float)sdP[r * PCC + j] * e;
+                                accR[i] += (float)sdA[r * PCC + j] * e;
+                            }
+                        }
+                    }
+    #pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const int r = 16 * R + 4 * q + i;
+                        dq[R][i] += accP[i];
+                        dka[R][i] += sBeta[r] * accR[i];
+                        const float part = sum16((float)sK[r * PK + ch] * accR[i]);
+                        if (lr == 0) sDB[(8 + w) * C + r] = part;
+                    }
+                }
+                // upper sums, rows 16s..: RU = decayed^T(beta dA) K + decayed^T(dP) Q
+                {
+                    const int J = s, ua = 16 * J + 15;
+                    const int ufirst = mild ? 16 * J : ua + 1;
+                    floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+                    if (ufirst < C) {
+                        const int k0 = ufirst / 32 * 32;
+                        // both operands read transposed: A[j][r] = dA[r][j], B[c][r] = x~[r][c]
+                        for (int kk = k0; kk < C; kk += 32) {
+                            acc = F::mma(acc, load_frag_tr(sdA, PCC, kk, 16 * J), load_frag_tr(xuk, 16, kk, 0));
+                            acc = F::mma(acc, load_frag_tr(sdP, PCC, kk, 16 * J), load_frag_tr(xuq, 16, kk, 0));
+                        }
+                        const float ga = sG[ua * PG + ch];
+    #pragma unroll
+                        for (int i = 0; i < 4; ++i) acc[i] *= __expf(ga - sG[(16 * J + 4 * q + i) * PG + ch]);
+                    }
+                    if (!mild) {
+                        float gj[4];
+    #pragma unroll
+                        for (int i = 0; i < 4; ++i) gj[i] = sG[(16 * J + 4 * q + i) * PG + ch];
+    #pragma unroll 4
+                        for (int rr = 0; rr < 16; ++rr) {
+                            const int r = 16 * J + rr;
+                            const float g_r = sG[r * PG + ch];
+                            const float kr = sBeta[r] * (float)sK[r * PK + ch], qr = (float)sQ[r * PK + ch];
+    #pragma unroll
+                            for (int i = 0; i < 4; ++i) {
+                                const int j = 16 * J + 4 * q + i;
+                                const float e = __expf(fminf(g_r - gj[i], 0.f));
+                                acc[i] += e * ((float)sdP[r * PCC + j] * qr + (float)sdA[r * PCC + j] * kr);
+                            }
+                        }
+                    }
+    #pragma unroll
+                    for (int i = 0; i < 4; ++i) dkb[J][i] += acc[i];
+                }
+            }
+            wave_fence();
+        }
     }
 
     // ---- outputs: dq, dk; dg = q dq + k (dka - dkb) -> reverse sums; dbeta -----------
@@ -851,13 +910,17 @@ __global__ void __launch_bounds__(512) kda_chunk_grad_kernel(ChunkGradParams prm
 
 hipError_t launch_chunk_grad(const ChunkGradParams& prm, int dk, int dv, hipStream_t stream) {
     if (prm.BH == 0 || prm.nc == 0) return hipSuccess;
+    // one decay per token (or none) comes widened to fp32 per channel
+    if (prm.dla_mode != 2 && prm.gate_bf16) return hipErrorInvalidValue;
     const unsigned grid = (unsigned)((int64_t)prm.BH * prm.nc);
 #define KDA_CASE(DK_, DV_)                                                                     \
     if (dk == DK_ && dv == DV_) {                                                              \
-        if (prm.gate_bf16)                                                                     \
-            hipLaunchKernelGGL((kda_chunk_grad_kernel<DK_, DV_, true>), dim3(grid), dim3(512), 0, stream, prm); \
+        if (prm.dla_mode != 2)                                                                 \
+            hipLaunchKernelGGL((kda_chunk_grad_kernel<DK_, DV_, false, true>), dim3(grid), dim3(512), 0, stream, prm); \
+        else if (prm.gate_bf16)                                                                \
+            hipLaunchKernelGGL((kda_chunk_grad_kernel<DK_, DV_, true, false>), dim3(grid), dim3(512), 0, stream, prm); \
         else                                                                                   \
-            hipLaunchKernelGGL((kda_chunk_grad_kernel<DK_, DV_, false>), dim3(grid), dim3(512), 0, stream, prm); \
+            hipLaunchKernelGGL((kda_chunk_grad_kernel<DK_, DV_, false, false>), dim3(grid), dim3(512), 0, stream, prm); \
         return hipGetLastError();                                                              \
     }
     KDA_CASE(128, 128)
