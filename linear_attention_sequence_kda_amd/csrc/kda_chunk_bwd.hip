@@ -378,8 +378,24 @@ __global__ void __launch_bounds__(512) kda_chunk_grad_kernel(ChunkGradParams prm
     };
 
     // ---- T^T, du and k; beta, g (cumulative ln alpha per channel) -------------------
+    // (loads in the order of first use: the gates, then T^T, du and k, then dO
+    // and S for the next phase; loads complete in order)
+    // gates: four threads per channel, 16 rows each
+    const int gch = tid >> 2, gp = tid & 3;
+    float gv[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+        const int r = 16 * gp + i;
+        // (one decay per token: every channel holds the same value, so
+        // column 0 serves them all)
+        const float x = gate_at(prm.la, (row0 + (r < n ? r : n - 1)) * DK +
+                                            (SCAL ? 0 : (gch < DK ? gch : DK - 1)));
+        gv[i] = (gch < DK && r < n) ? x : 0.f;
+    }
+    const float bload = gate_at(prm.beta, row0 + ((tid & (C - 1)) < n ? (tid & (C - 1)) : n - 1));
     floatx4 rtt[NP_TT];
-    uint4 rdu[NPR], rk[NPR];
+    uint4 rdu[NPR], rk[NPR], rdo[NPR];
+    floatx4 rs[NP_KV][2];
     {
         const float* gtt = prm.tt + xf * C * C;
 #pragma unroll
@@ -396,22 +412,16 @@ __global__ void __launch_bounds__(512) kda_chunk_grad_kernel(ChunkGradParams prm
             if (i < C * DV / 8) rdu[it] = *(const uint4*)(gdu + (i / (DV / 8)) * DV + (i % (DV / 8)) * 8);
         }
         ld_rows(rk, (const bf16*)prm.k + row0 * DK, DK, NP_CK);
+        ld_rows(rdo, (const bf16*)prm.dout + row0 * DV, DV, NP_CV);
+        ld_state(rs, prm.S_all + xf * DK * DV);
     }
-    if (tid < C) sBeta[tid] = tid < n ? gate_at(prm.beta, row0 + tid) : 0.f;
+    if (tid < C) sBeta[tid] = tid < n ? bload : 0.f;
     for (int i = tid; i < 3 * 8 * C; i += NT) sDB[i] = 0.f;
     {
-        // four threads per channel, 16 rows each; prefix within, offsets across
-        const int ch = tid >> 2, p = tid & 3;
-        float v[16], run = 0.f;
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-            const int r = 16 * p + i;
-            // (one decay per token: every channel holds the same value, so
-            // column 0 serves them all)
-            const float x = gate_at(prm.la, (row0 + (r < n ? r : n - 1)) * DK +
-                                                (SCAL ? 0 : (ch < DK ? ch : DK - 1)));
-            v[i] = (ch < DK && r < n) ? x : 0.f;
-        }
+        // prefix within each thread's 16 rows, offsets across its four threads
+        const int ch = gch, p = gp;
+        float* v = gv;
+        float run = 0.f;
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
             run += v[i];
@@ -444,11 +454,19 @@ __global__ void __launch_bounds__(512) kda_chunk_grad_kernel(ChunkGradParams prm
     st_rows(rk, sK, PK, DK, NP_CK);
     __syncthreads();
 
-    // ---- dY = T^T du (fp32 MFMA); dv = beta dY  (dO and S on their way) -------------
-    uint4 rdo[NPR];
-    floatx4 rs[NP_KV][2];
-    ld_rows(rdo, (const bf16*)prm.dout + row0 * DV, DV, NP_CV);
-    ld_state(rs, prm.S_all + xf * DK * DV);
+    // ---- dY = T^T du (fp32 MFMA); dv = beta dY  (dO and S arriving; u and v on their way)
+    uint4 ru[NPR], rv[NPR];
+    {
+        // u has no rows past the sequence end to drop (zero records there)
+        const bf16* gu = (const bf16*)prm.u_all + xf * C * DV;
+#pragma unroll
+        for (int it = 0; it < NP_CV; ++it) {
+            const int i = tid + NT * it;
+            ru[it] = make_uint4(0u, 0u, 0u, 0u);
+            if (i < C * DV / 8) ru[it] = *(const uint4*)(gu + (i / (DV / 8)) * DV + (i % (DV / 8)) * 8);
+        }
+    }
+    ld_rows(rv, (const bf16*)prm.v + row0 * DV, DV, NP_CV);
     floatx4 dY[NB];
     if (w < NVB) {
 #pragma unroll
@@ -473,18 +491,6 @@ __global__ void __launch_bounds__(512) kda_chunk_grad_kernel(ChunkGradParams prm
     }
     st_rows(rdo, sDO, PV, DV, NP_CV);
     st_state(rs, sS);
-    uint4 ru[NPR], rv[NPR];
-    {
-        // u has no rows past the sequence end to drop (zero records there)
-        const bf16* gu = (const bf16*)prm.u_all + xf * C * DV;
-#pragma unroll
-        for (int it = 0; it < NP_CV; ++it) {
-            const int i = tid + NT * it;
-            ru[it] = make_uint4(0u, 0u, 0u, 0u);
-            if (i < C * DV / 8) ru[it] = *(const uint4*)(gu + (i / (DV / 8)) * DV + (i % (DV / 8)) * 8);
-        }
-    }
-    ld_rows(rv, (const bf16*)prm.v + row0 * DV, DV, NP_CV);
     __syncthreads();
 
     // ---- dO S^T, dY S^T; dbeta's first term ---------------------------------------
