@@ -102,9 +102,12 @@ struct RevCfg {
     static constexpr int PDO = DV + 16, PPT = C + 16;  // bf16 pitches
     static constexpr int O_W = 0, O_KT = O_W + C * DK * 2, O_QT = O_KT + DK * C * 2;
     static constexpr int O_P = O_QT + C * DK * 2, O_DO = O_P + C * C * 2;
-    static constexpr int O_PT = O_DO + C * PDO * 2;
-    static constexpr int LDS_BYTES = O_PT + C * PPT * 2;
-    static_assert(LDS_BYTES <= 160 * 1024, "LDS budget");
+    // P^T takes the space of W and K^T once both have been transposed, so
+    // that two workgroups share a CU (at d_k = d_v = 128: 74 KiB each)
+    static constexpr int O_PT = O_W;
+    static constexpr int LDS_BYTES = O_DO + C * PDO * 2;
+    static_assert(C * PPT * 2 <= O_QT, "P^T fits over W and K^T");
+    static_assert(LDS_BYTES <= 80 * 1024 || DV > 128, "two workgroups per CU");
 };
 
 template <int DK, int DV>
@@ -148,11 +151,6 @@ __global__ void __launch_bounds__(512) kda_rev_records_kernel(RevRecParams prm) 
     }
     __syncthreads();
 
-    // P^T by rows for the product P^T dO
-    for (int i = tid; i < C * C; i += NT) {
-        const int j = i / C, r = i - j * C;
-        sPT[j * PPT + r] = sP[wide_elem(r, j, C)];
-    }
     // W <- K e^{g_n - g} (the transpose of the stored K^T), K^T <- -W^T (the
     // stored W is already negated), K2^T <- (Q e^g)^T in the Q~ section
     {
@@ -194,6 +192,12 @@ __global__ void __launch_bounds__(512) kda_rev_records_kernel(RevRecParams prm) 
             for (int i = 0; i < 4; ++i) v[i] = sDO[(16 * R + 4 * (l >> 4) + i) * PDO + 16 * vb + (l & 15)];
             *(bf16x4*)(but + ((R * (DV / 32) + vb / 2) * 64 + l) * 8 + (vb % 2) * 4) = v;
         }
+    }
+    __syncthreads();
+    // P^T by rows for the product P^T dO (over W and K^T, now read)
+    for (int i = tid; i < C * C; i += NT) {
+        const int j = i / C, r = i - j * C;
+        sPT[j * PPT + r] = sP[wide_elem(r, j, C)];
     }
     __syncthreads();
     // U = P^T dO (MFMA), stored in accumulator order
