@@ -997,8 +997,7 @@ namespace {
 // Layout of kda_chunk_bwd's workspace (each piece rounded up to 256 bytes):
 // the forward records of every chunk, the reverse records (one per chunk),
 // T^T, the forward scan's S and u and the reverse scan's G and du per chunk,
-// and, with one decay per token or none, per-channel fp32 ln(alpha) and an
-// fp32 beta.
+// and, without a decay, zero per-channel fp32 ln(alpha) and an fp32 beta.
 struct ChunkBwdPlan {
     int64_t recs = 0, rrecs = 0, tt = 0, S = 0, G = 0, u = 0, du = 0, la = 0, b = 0, total = 0;
     int64_t nc = 0;
@@ -1025,7 +1024,7 @@ ChunkBwdPlan chunk_bwd_plan(const kda_shape* s) {
     p.G = off; off += up(nch * s->dk * s->dv * 4);
     p.u = off; off += up(nch * C * s->dv * 2);
     p.du = off; off += up(nch * C * s->dv * 2);
-    if (s->alpha_mode != KDA_ALPHA_CHANNEL) {
+    if (s->alpha_mode == KDA_ALPHA_NONE) {
         p.la = off; off += up(bh * s->L * s->dk * 4);
         p.b = off; off += up(bh * s->L * 4);
     }
@@ -1084,13 +1083,14 @@ static int kda_chunk_bwd_body(const kda_shape* s, const void* q, const void* k, 
     }
     if (log_on())
         klog("kda_chunk_bwd: %d chunks of 64; workspace %lld B", nc, (long long)pl.total);
-    // per-channel gates for every decay mode
+    // per-channel gates: read as given per channel, read per token by every
+    // channel for a head gate, widened (zeros) without a decay
     const void* la = log_alpha;
     const void* bt = beta;
     int gate_bf16 = s->gate_dtype == KDA_BF16;
-    if (s->alpha_mode != KDA_ALPHA_CHANNEL) {
+    if (s->alpha_mode == KDA_ALPHA_NONE) {
         kda::GateWiden gw{};
-        gw.log_alpha = s->alpha_mode == KDA_ALPHA_HEAD ? log_alpha : nullptr;
+        gw.log_alpha = nullptr;
         gw.beta = beta;
         gw.la = (float*)(ws + pl.la);
         gw.b = (float*)(ws + pl.b);
@@ -1118,6 +1118,7 @@ static int kda_chunk_bwd_body(const kda_shape* s, const void* q, const void* k, 
     ip.gate_bf16 = gate_bf16;
     ip.wide = 1;
     ip.tt = (float*)(ws + pl.tt);
+    ip.la_head = s->alpha_mode == KDA_ALPHA_HEAD;
     err = timed_launch(K_INTRA, stream, [&] {
         return kda::launch_intra(ip, dkk, dvv, 1, KDA_ALPHA_CHANNEL, stream);
     });
@@ -1188,6 +1189,7 @@ static int kda_chunk_bwd_body(const kda_shape* s, const void* q, const void* k, 
     gp.BH = (int)bh;
     gp.gate_bf16 = gate_bf16;
     gp.dla_mode = s->alpha_mode == KDA_ALPHA_CHANNEL ? 2 : (s->alpha_mode == KDA_ALPHA_HEAD ? 1 : 0);
+    gp.la_rs = s->alpha_mode == KDA_ALPHA_HEAD ? 1 : dkk;
     err = timed_launch(K_CHUNK_GRAD, stream, [&] { return kda::launch_chunk_grad(gp, dkk, dvv, stream); });
     if (err != hipSuccess) return fail(err);
     return KDA_OK;

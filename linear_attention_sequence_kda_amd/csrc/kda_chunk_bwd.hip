@@ -390,10 +390,9 @@ __global__ void __launch_bounds__(512) kda_chunk_grad_kernel(ChunkGradParams prm
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
         const int r = 16 * gp + i;
-        // (one decay per token: every channel holds the same value, so
-        // column 0 serves them all)
-        const float x = gate_at(prm.la, (row0 + (r < n ? r : n - 1)) * DK +
-                                            (SCAL ? 0 : (gch < DK ? gch : DK - 1)));
+        // (one decay per token: the row's value serves every channel)
+        const int64_t rg = row0 + (r < n ? r : n - 1);
+        const float x = gate_at(prm.la, SCAL ? rg * prm.la_rs : rg * DK + (gch < DK ? gch : DK - 1));
         gv[i] = (gch < DK && r < n) ? x : 0.f;
     }
     const float bload = gate_at(prm.beta, row0 + ((tid & (C - 1)) < n ? (tid & (C - 1)) : n - 1));
@@ -920,12 +919,12 @@ __global__ void __launch_bounds__(512) kda_chunk_grad_kernel(ChunkGradParams prm
 
 hipError_t launch_chunk_grad(const ChunkGradParams& prm, int dk, int dv, hipStream_t stream) {
     if (prm.BH == 0 || prm.nc == 0) return hipSuccess;
-    // one decay per token (or none) comes widened to fp32 per channel
-    if (prm.dla_mode != 2 && prm.gate_bf16) return hipErrorInvalidValue;
     const unsigned grid = (unsigned)((int64_t)prm.BH * prm.nc);
 #define KDA_CASE(DK_, DV_)                                                                     \
     if (dk == DK_ && dv == DV_) {                                                              \
-        if (prm.dla_mode != 2)                                                                 \
+        if (prm.dla_mode != 2 && prm.gate_bf16)                                                \
+            hipLaunchKernelGGL((kda_chunk_grad_kernel<DK_, DV_, true, true>), dim3(grid), dim3(512), 0, stream, prm); \
+        else if (prm.dla_mode != 2)                                                            \
             hipLaunchKernelGGL((kda_chunk_grad_kernel<DK_, DV_, false, true>), dim3(grid), dim3(512), 0, stream, prm); \
         else if (prm.gate_bf16)                                                                \
             hipLaunchKernelGGL((kda_chunk_grad_kernel<DK_, DV_, true, false>), dim3(grid), dim3(512), 0, stream, prm); \

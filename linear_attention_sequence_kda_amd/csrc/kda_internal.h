@@ -115,6 +115,9 @@ struct IntraParams {
     // per-channel decay: also write T^T = ((I + A)^-1)^T of every chunk,
     // fp32 [BH][ncs][C][C] row-major (chunkwise gradients), or null
     float* tt = nullptr;
+    // per-channel decay computed from one ln(alpha) per token ([BH, L]), which
+    // every channel reads (chunkwise gradients of a head gate)
+    int la_head = 0;
 };
 
 struct InterParams {
@@ -294,7 +297,7 @@ struct ChunkGradParams {
     const void* k;
     const void* v;          // [BH, L, DV] bf16
     const void* dout;       // [BH, L, DV] bf16
-    const void* la;         // [BH, L, DK] per-channel ln(alpha), gate type
+    const void* la;         // [BH, L, DK] per-channel ln(alpha), or one per token, gate type
     const void* beta;       // [BH, L] gate type
     const float* tt;        // [BH][nc][C][C] T^T, fp32
     const float* S_all;     // [BH][nc][DK][DV] state entering each chunk, fp32
@@ -311,6 +314,7 @@ struct ChunkGradParams {
     int BH;
     int gate_bf16;
     int dla_mode;
+    int la_rs;              // elements between rows of la (DK per channel, 1 per token)
 };
 hipError_t launch_chunk_grad(const ChunkGradParams& prm, int dk, int dv, hipStream_t stream);
 

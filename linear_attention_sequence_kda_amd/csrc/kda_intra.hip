@@ -183,7 +183,9 @@ kda_intra_kernel(IntraParams prm) {
     const char* gk = (const char*)prm.k + row0 * DK * ESZ;
     const char* gv = (const char*)prm.v + row0 * DV * ESZ;
     constexpr int GSZ = GBF ? 2 : 4;
-    const char* gla = (const char*)prm.log_alpha + row0 * (KDA ? DK : 1) * GSZ;
+    // ln(alpha): [rows][DK], or one per token read by every channel (la_head)
+    const uint32_t la_rs = (KDA && !prm.la_head) ? DK : 1, la_cs = prm.la_head ? 0 : 1;
+    const char* gla = (const char*)prm.log_alpha + row0 * la_rs * GSZ;
     const char* gbeta = (const char*)prm.beta + row0 * GSZ;
     char* rec = (char*)prm.ws + ((int64_t)bh * prm.ncs + cs) * RL.bytes;
     E* rW = (E*)(rec + RL.w);
@@ -260,7 +262,7 @@ kda_intra_kernel(IntraParams prm) {
         for (int s = 0; s < 16; ++s) {
             const int r = 16 * kRc + s;
             const int rr = r < n ? r : n - 1;
-            const uint32_t el = rr * DK + kc;
+            const uint32_t el = rr * la_rs + kc * la_cs;
             la_bits[s] = GBF ? (uint32_t)ld_in(gla, el * 2, uint16_t{}) : ld_in(gla, el * 4, uint32_t{});
         }
     } else if constexpr (HEADG) {
@@ -465,7 +467,8 @@ kda_intra_kernel(IntraParams prm) {
                                         : bits_f32(ldg<uint32_t>(gq, el * 4), false);
                     float kv = ESZ == 2 ? bits_f32(ldg<uint16_t>(gk, el * 2), true)
                                         : bits_f32(ldg<uint32_t>(gk, el * 4), false);
-                    float la = bits_f32(GBF ? (uint32_t)ldg<uint16_t>(gla, el * 2) : ldg<uint32_t>(gla, el * 4), GBF);
+                    const uint32_t ea = rr * la_rs + kc * la_cs;
+                    float la = bits_f32(GBF ? (uint32_t)ldg<uint16_t>(gla, ea * 2) : ldg<uint32_t>(gla, ea * 4), GBF);
                     if (norm_qk) {
                         qv *= sQn[r];
                         kv *= sKn[r];

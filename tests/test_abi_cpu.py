@@ -377,8 +377,9 @@ def cbwd(lib, s, b, wsb=1 << 30):
 def test_chunk_bwd_workspace_size(lib):
     """Per chunk of 64 tokens and head: the forward record, a reverse record
     (the same sections and dO in one more), T^T (fp32 64 x 64), the states S
-    and G (fp32 dk x dv) and u, du (bf16 64 x dv); one decay per token (or
-    none) adds per-channel fp32 ln(alpha) and an fp32 beta per token."""
+    and G (fp32 dk x dv) and u, du (bf16 64 x dv); without a decay, zero
+    per-channel fp32 ln(alpha) and an fp32 beta per token are added (a head
+    gate is read per token by every channel)."""
     up = lambda x: (x + 255) // 256 * 256
     rec = 64 * 128 * 2 * 4 + 64 * 64 * 2 + 1024     # W, U, K^T, Q~ (bf16), P, decays
     rrec = rec + 64 * 128 * 2                        # and dO
@@ -387,7 +388,9 @@ def test_chunk_bwd_workspace_size(lib):
             2 * up(nch * 128 * 128 * 4) + 2 * up(nch * 64 * 128 * 2))
     assert lib.kda_chunk_bwd_workspace_bytes(ctypes.byref(shape())) == want
     head = shape(mode=binding.KDA_ALPHA_HEAD)
-    assert lib.kda_chunk_bwd_workspace_bytes(ctypes.byref(head)) == \
+    assert lib.kda_chunk_bwd_workspace_bytes(ctypes.byref(head)) == want
+    none = shape(mode=binding.KDA_ALPHA_NONE)
+    assert lib.kda_chunk_bwd_workspace_bytes(ctypes.byref(none)) == \
         want + up(600 * 128 * 4) + up(600 * 4)
     assert lib.kda_chunk_bwd_workspace_bytes(ctypes.byref(shape(qd=binding.KDA_F32))) == 0
     assert lib.kda_chunk_bwd_workspace_bytes(ctypes.byref(shape(L=0))) == 0
