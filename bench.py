@@ -338,13 +338,14 @@ def chunk_grad_flops(w):
 def chunk_grad_bytes(w):
     """Algorithmic HBM bytes of one kda_chunk_grad_kernel launch: per chunk
     of C = 64 tokens and head, every input read once (T^T fp32; du, u, dO, v,
-    q, k bf16; S and G fp32; per-channel ln alpha and beta in the gate type,
-    fp32 when widened from one decay per token) and every gradient written
-    once (fp32)."""
+    q, k bf16; S and G fp32; ln alpha per channel or per token, and beta, in
+    the gate type; without a decay one column of widened fp32 zeros and an
+    fp32 beta) and every gradient written once (fp32)."""
     C, dk, dv = 64, w.dk, w.dv
     nc = -(-w.L // C)
-    g = 2 if (w.gate_dtype == "bf16" and w.alpha_mode == "channel") else 4
-    reads = C * C * 4 + 4 * C * dv * 2 + 2 * C * dk * 2 + C * dk * g + C * g + 2 * dk * dv * 4
+    g = 2 if w.gate_dtype == "bf16" else 4
+    gates = {"channel": C * dk * g + C * g, "head": 2 * C * g}.get(w.alpha_mode, 2 * C * 4)
+    reads = C * C * 4 + 4 * C * dv * 2 + 2 * C * dk * 2 + gates + 2 * dk * dv * 4
     dla = {"channel": C * dk * 4, "head": C * 4}.get(w.alpha_mode, 0)
     writes = 2 * C * dk * 4 + C * dv * 4 + dla + C * 4
     return w.B * w.H * nc * (reads + writes)
