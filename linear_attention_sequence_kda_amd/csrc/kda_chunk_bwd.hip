@@ -685,72 +685,71 @@ __global__ void __launch_bounds__(512) kda_chunk_grad_kernel(ChunkGradParams prm
             }
         }
     } else {
-    #pragma unroll 1
-        for (int s = 0; s < NB; ++s) {
-            // Block s is "moderate" for this wave when its total decay is at least
-            // -60 in each of the wave's 16 channels: then one anchor per sum
-            // covers the diagonal block too (its factors stay below e^60) and the
-            // whole sum runs on MFMA.  Otherwise the diagonal block is summed
-            // directly and only the blocks off it take anchored MFMA operands.
-            const float zb = w < NCBK ? sG[(16 * s + 15) * PG + ch] - (s ? sG[(16 * s - 1) * PG + ch] : 0.f)
+        // One anchor per AB-token block: the sums of row tiles (lower) and of
+        // column tiles (upper) inside block s share one set of operand tiles.
+        constexpr int AB = 64, TPB = AB / 16;
+        static_assert(C % AB == 0 && AB % 32 == 0, "whole blocks of k steps");
+#pragma unroll
+        for (int s = 0; s < C / AB; ++s) {
+            const int b0 = AB * s;  // the block's first row
+            // Block s is "moderate" for this wave when its total decay is at
+            // least -60 in each of the wave's 16 channels: then one anchor per
+            // sum covers the block's own rows too (their factors stay below
+            // e^60) and the whole sum runs on MFMA.  Otherwise the block's own
+            // rows are summed directly and only the rows off it take anchored
+            // MFMA operands.
+            const float zb = w < NCBK ? sG[(b0 + AB - 1) * PG + ch] - (s ? sG[(b0 - 1) * PG + ch] : 0.f)
                                       : 0.f;
             const bool mild = __all(zb >= -60.f);
-            // operands: lower sums of row block s anchored at a = 16s - 1 (rows
-            // j < 16s, and with a mild block also its rows), upper sums of row
-            // block s anchored at a = 16s + 15 (rows r > a, and with a mild block
-            // also the block's rows)
+            // lower sums of the block's rows are anchored at la = b0 - 1 (rows
+            // j < b0, and with a mild block also its rows), upper sums of its
+            // columns at ua = b0 + AB - 1 (rows r > ua, and with a mild block
+            // also its rows)
+            const int la = b0 - 1, ua = b0 + AB - 1;
+            const int lrows = mild ? b0 + AB : b0;  // rows of the lower operand
+            const int ufirst = mild ? b0 : ua + 1;  // first row of the upper ones
             // (each lane builds 8 channels of one row per step: one 16-byte k or q
             // piece, two of g, one of the anchor's g)
             if (w < NCBK) {
                 const int h8 = 16 * w + 8 * (l & 1);  // this lane's 8 channels
-                const int la = 16 * s - 1;
-                const int lrows = mild ? 16 * s + 16 : 16 * s;
-                const int KR = (lrows + 31) / 32 * 32;
                 if (lrows > 0) {
                     floatx4 a0 = {0.f, 0.f, 0.f, 0.f}, a1 = a0;
                     if (la >= 0) {
                         a0 = *(const floatx4*)(sG + la * PG + h8);
                         a1 = *(const floatx4*)(sG + la * PG + h8 + 4);
                     }
-                    for (int t = l; t < KR * 2; t += 64) {
+                    for (int t = l; t < lrows * 2; t += 64) {
                         const int j = t >> 1;
-                        bf16x8 x = {};
-                        if (j < lrows) {
-                            const bf16x8 kv = *(const bf16x8*)(sK + j * PK + h8);
-                            const floatx4 g0 = *(const floatx4*)(sG + j * PG + h8);
-                            const floatx4 g1 = *(const floatx4*)(sG + j * PG + h8 + 4);
-    #pragma unroll
-                            for (int e = 0; e < 4; ++e) {
-                                x[e] = (bf16)((float)kv[e] * __expf(a0[e] - g0[e]));
-                                x[4 + e] = (bf16)((float)kv[4 + e] * __expf(a1[e] - g1[e]));
-                            }
+                        const bf16x8 kv = *(const bf16x8*)(sK + j * PK + h8);
+                        const floatx4 g0 = *(const floatx4*)(sG + j * PG + h8);
+                        const floatx4 g1 = *(const floatx4*)(sG + j * PG + h8 + 4);
+                        bf16x8 x;
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) {
+                            x[e] = (bf16)((float)kv[e] * __expf(a0[e] - g0[e]));
+                            x[4 + e] = (bf16)((float)kv[4 + e] * __expf(a1[e] - g1[e]));
                         }
                         *(bf16x8*)(xl + j * 16 + 8 * (l & 1)) = x;
                     }
                 }
-                const int ua = 16 * s + 15;
-                const int ufirst = mild ? 16 * s : ua + 1;  // first row taken
                 if (ufirst < C) {
-                    const int k0 = ufirst / 32 * 32;
                     const floatx4 a0 = *(const floatx4*)(sG + ua * PG + h8);
                     const floatx4 a1 = *(const floatx4*)(sG + ua * PG + h8 + 4);
-                    for (int t = l; t < (C - k0) * 2; t += 64) {
-                        const int r = k0 + (t >> 1);
-                        bf16x8 xk = {}, xq = {};
-                        if (r >= ufirst) {
-                            const float br = sBeta[r];
-                            const bf16x8 kv = *(const bf16x8*)(sK + r * PK + h8);
-                            const bf16x8 qv = *(const bf16x8*)(sQ + r * PK + h8);
-                            const floatx4 g0 = *(const floatx4*)(sG + r * PG + h8);
-                            const floatx4 g1 = *(const floatx4*)(sG + r * PG + h8 + 4);
-    #pragma unroll
-                            for (int e = 0; e < 4; ++e) {
-                                const float f0 = __expf(g0[e] - a0[e]), f1 = __expf(g1[e] - a1[e]);
-                                xk[e] = (bf16)(br * (float)kv[e] * f0);
-                                xk[4 + e] = (bf16)(br * (float)kv[4 + e] * f1);
-                                xq[e] = (bf16)((float)qv[e] * f0);
-                                xq[4 + e] = (bf16)((float)qv[4 + e] * f1);
-                            }
+                    for (int t = l; t < (C - ufirst) * 2; t += 64) {
+                        const int r = ufirst + (t >> 1);
+                        const float br = sBeta[r];
+                        const bf16x8 kv = *(const bf16x8*)(sK + r * PK + h8);
+                        const bf16x8 qv = *(const bf16x8*)(sQ + r * PK + h8);
+                        const floatx4 g0 = *(const floatx4*)(sG + r * PG + h8);
+                        const floatx4 g1 = *(const floatx4*)(sG + r * PG + h8 + 4);
+                        bf16x8 xk, xq;
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) {
+                            const float f0 = __expf(g0[e] - a0[e]), f1 = __expf(g1[e] - a1[e]);
+                            xk[e] = (bf16)(br * (float)kv[e] * f0);
+                            xk[4 + e] = (bf16)(br * (float)kv[4 + e] * f1);
+                            xq[e] = (bf16)((float)qv[e] * f0);
+                            xq[4 + e] = (bf16)((float)qv[4 + e] * f1);
                         }
                         *(bf16x8*)(xuk + r * 16 + 8 * (l & 1)) = xk;
                         *(bf16x8*)(xuq + r * 16 + 8 * (l & 1)) = xq;
@@ -759,17 +758,17 @@ __global__ void __launch_bounds__(512) kda_chunk_grad_kernel(ChunkGradParams prm
             }
             wave_fence();
             if (w < NCBK) {
-                // lower sums, rows 16s..: R = decayed(dA) K, RP = decayed(dP) K (j < r)
-                {
-                    const int R = s, la = 16 * R - 1;
-                    const int lrows = mild ? 16 * R + 16 : 16 * R;
+                // lower sums of the block's row tiles: R = decayed(dA) K,
+                // RP = decayed(dP) K (j < r; the tiles are zero from the
+                // diagonal on, so the operand's rows past a tile's own add zero)
+#pragma unroll
+                for (int R = TPB * s; R < TPB * (s + 1); ++R) {
                     floatx4 accR = {0.f, 0.f, 0.f, 0.f}, accP = accR;
                     if (lrows > 0) {
-                        const int KR = (lrows + 31) / 32 * 32;
-                        accR = mma_block_bt<bf16>(accR, sdA + 16 * R * PCC, PCC, xl, 16, 0, KR);
-                        accP = mma_block_bt<bf16>(accP, sdP + 16 * R * PCC, PCC, xl, 16, 0, KR);
+                        accR = mma_block_bt<bf16>(accR, sdA + 16 * R * PCC, PCC, xl, 16, 0, lrows);
+                        accP = mma_block_bt<bf16>(accP, sdP + 16 * R * PCC, PCC, xl, 16, 0, lrows);
                         const float ga = la >= 0 ? sG[la * PG + ch] : 0.f;
-    #pragma unroll
+#pragma unroll
                         for (int i = 0; i < 4; ++i) {
                             const float f = __expf(sG[(16 * R + 4 * q + i) * PG + ch] - ga);
                             accR[i] *= f;
@@ -777,14 +776,14 @@ __global__ void __launch_bounds__(512) kda_chunk_grad_kernel(ChunkGradParams prm
                         }
                     }
                     if (!mild) {
+                        // the block's own rows j < r, directly (exponents <= 0)
                         float gr[4];
-    #pragma unroll
+#pragma unroll
                         for (int i = 0; i < 4; ++i) gr[i] = sG[(16 * R + 4 * q + i) * PG + ch];
-    #pragma unroll 4
-                        for (int jj = 0; jj < 16; ++jj) {
-                            const int j = 16 * R + jj;
+#pragma unroll 4
+                        for (int j = b0; j < 16 * R + 16; ++j) {
                             const float gj = sG[j * PG + ch], kj = (float)sK[j * PK + ch];
-    #pragma unroll
+#pragma unroll
                             for (int i = 0; i < 4; ++i) {
                                 const int r = 16 * R + 4 * q + i;
                                 const float e = __expf(fminf(gr[i] - gj, 0.f)) * kj;
@@ -793,7 +792,7 @@ __global__ void __launch_bounds__(512) kda_chunk_grad_kernel(ChunkGradParams prm
                             }
                         }
                     }
-    #pragma unroll
+#pragma unroll
                     for (int i = 0; i < 4; ++i) {
                         const int r = 16 * R + 4 * q + i;
                         dq[R][i] += accP[i];
@@ -802,32 +801,30 @@ __global__ void __launch_bounds__(512) kda_chunk_grad_kernel(ChunkGradParams prm
                         if (lr == 0) sDB[(8 + w) * C + r] = part;
                     }
                 }
-                // upper sums, rows 16s..: RU = decayed^T(beta dA) K + decayed^T(dP) Q
-                {
-                    const int J = s, ua = 16 * J + 15;
-                    const int ufirst = mild ? 16 * J : ua + 1;
+                // upper sums of the block's column tiles:
+                // RU = decayed^T(beta dA) K + decayed^T(dP) Q (r > j)
+#pragma unroll
+                for (int J = TPB * s; J < TPB * (s + 1); ++J) {
                     floatx4 acc = {0.f, 0.f, 0.f, 0.f};
                     if (ufirst < C) {
-                        const int k0 = ufirst / 32 * 32;
                         // both operands read transposed: A[j][r] = dA[r][j], B[c][r] = x~[r][c]
-                        for (int kk = k0; kk < C; kk += 32) {
+                        for (int kk = ufirst; kk < C; kk += 32) {
                             acc = F::mma(acc, load_frag_tr(sdA, PCC, kk, 16 * J), load_frag_tr(xuk, 16, kk, 0));
                             acc = F::mma(acc, load_frag_tr(sdP, PCC, kk, 16 * J), load_frag_tr(xuq, 16, kk, 0));
                         }
                         const float ga = sG[ua * PG + ch];
-    #pragma unroll
+#pragma unroll
                         for (int i = 0; i < 4; ++i) acc[i] *= __expf(ga - sG[(16 * J + 4 * q + i) * PG + ch]);
                     }
                     if (!mild) {
                         float gj[4];
-    #pragma unroll
+#pragma unroll
                         for (int i = 0; i < 4; ++i) gj[i] = sG[(16 * J + 4 * q + i) * PG + ch];
-    #pragma unroll 4
-                        for (int rr = 0; rr < 16; ++rr) {
-                            const int r = 16 * J + rr;
+#pragma unroll 4
+                        for (int r = 16 * J + 1; r <= ua; ++r) {
                             const float g_r = sG[r * PG + ch];
                             const float kr = sBeta[r] * (float)sK[r * PK + ch], qr = (float)sQ[r * PK + ch];
-    #pragma unroll
+#pragma unroll
                             for (int i = 0; i < 4; ++i) {
                                 const int j = 16 * J + 4 * q + i;
                                 const float e = __expf(fminf(g_r - gj[i], 0.f));
@@ -835,7 +832,7 @@ __global__ void __launch_bounds__(512) kda_chunk_grad_kernel(ChunkGradParams prm
                             }
                         }
                     }
-    #pragma unroll
+#pragma unroll
                     for (int i = 0; i < 4; ++i) dkb[J][i] += acc[i];
                 }
             }
