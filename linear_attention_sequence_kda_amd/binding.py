@@ -166,7 +166,7 @@ def _stream(t) -> int:
 KERNELS = ("kda_intra_kernel", "kda_inter_kernel", "kda_inter_scalar_kernel",
            "kda_inter_wide_kernel", "kda_inter_quad_kernel", "kda_feature_map_kernel",
            "kda_decode_kernel", "kda_bwd_kernel", "kda_inter_wide_scan",
-           "kda_rev_records_kernel", "kda_chunk_grad_kernel", "kda_gate_widen_kernel")
+           "kda_chunk_grad_kernel", "kda_gate_widen_kernel")
 
 
 def timing_enable(on: bool = True) -> None:

@@ -68,14 +68,14 @@ struct CallScope {
 // While enabled, each kernel launch is bracketed by two events recorded on the
 // launch's stream; the pairs are kept until read or reset.
 enum KernelId { K_INTRA = 0, K_INTER, K_INTER_SCALAR, K_DECODE, K_FEATURE, K_BWD, K_INTER_WIDE,
-                K_INTER_QUAD, K_WIDE_SCAN, K_REV_REC, K_CHUNK_GRAD, K_GATE_WIDEN, K_COUNT };
+                K_INTER_QUAD, K_WIDE_SCAN, K_CHUNK_GRAD, K_GATE_WIDEN, K_COUNT };
 // (kda_inter_wide_scan is kda_inter_wide_kernel in its scan form)
 const char* const kKernelNames[K_COUNT] = {"kda_intra_kernel", "kda_inter_kernel",
                                            "kda_inter_scalar_kernel", "kda_decode_kernel",
                                            "kda_feature_map_kernel", "kda_bwd_kernel",
                                            "kda_inter_wide_kernel", "kda_inter_quad_kernel",
-                                           "kda_inter_wide_scan", "kda_rev_records_kernel",
-                                           "kda_chunk_grad_kernel", "kda_gate_widen_kernel"};
+                                           "kda_inter_wide_scan", "kda_chunk_grad_kernel",
+                                           "kda_gate_widen_kernel"};
 struct TimedLaunch {
     int kernel;
     hipEvent_t start, stop;
@@ -1119,6 +1119,9 @@ static int kda_chunk_bwd_body(const kda_shape* s, const void* q, const void* k, 
     ip.wide = 1;
     ip.tt = (float*)(ws + pl.tt);
     ip.la_head = s->alpha_mode == KDA_ALPHA_HEAD;
+    // and, from each record just written, the chunk's reverse record
+    ip.rrecs = ws + pl.rrecs;
+    ip.dout = dout;
     err = timed_launch(K_INTRA, stream, [&] {
         return kda::launch_intra(ip, dkk, dvv, 1, KDA_ALPHA_CHANNEL, stream);
     });
@@ -1141,18 +1144,8 @@ static int kda_chunk_bwd_body(const kda_shape* s, const void* q, const void* k, 
     xp.n_store = nc;
     err = timed_launch(K_WIDE_SCAN, stream, [&] { return kda::launch_inter_wide_scan(xp, dkk, nv, stream); });
     if (err != hipSuccess) return fail(err);
-    // reverse records, then the reverse scan: dJ/dS leaving every chunk and
-    // dJ/du, and dJ/dS0 at its end
-    kda::RevRecParams rp{};
-    rp.recs = ws + pl.recs;
-    rp.rrecs = ws + pl.rrecs;
-    rp.dout = dout;
-    rp.L = s->L;
-    rp.nc = nc;
-    rp.BH = (int)bh;
-    rp.DV = dvv;
-    err = timed_launch(K_REV_REC, stream, [&] { return kda::launch_rev_records(rp, dkk, stream); });
-    if (err != hipSuccess) return fail(err);
+    // the reverse scan over the reverse records: dJ/dS leaving every chunk
+    // and dJ/du, and dJ/dS0 at its end
     kda::InterParams rx = xp;
     rx.ws = ws + pl.rrecs;
     rx.S_in = dS_final;

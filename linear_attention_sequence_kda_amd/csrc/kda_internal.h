@@ -118,6 +118,11 @@ struct IntraParams {
     // per-channel decay computed from one ln(alpha) per token ([BH, L]), which
     // every channel reads (chunkwise gradients of a head gate)
     int la_head = 0;
+    // chunkwise gradients: also build each chunk's reverse record (reverse
+    // chunk order, rev_rec_bytes each) from the record just written and
+    // dJ/do ([BH, L, DV] bf16); requires the wide order, c0 = 0, ncs = all chunks
+    void* rrecs = nullptr;
+    const void* dout = nullptr;
 };
 
 struct InterParams {
@@ -276,20 +281,6 @@ struct GateWiden {
     int gate_bf16;
 };
 hipError_t launch_gate_widen(const GateWiden& prm, hipStream_t stream);
-
-// Records of the reverse state pass, built from the forward's wide records
-// and dJ/do: chunk c of head bh becomes entry nc - 1 - c of [BH][nc] records
-// of rev_rec_bytes each.
-struct RevRecParams {
-    const void* recs;       // [BH][nc] forward records (wide order)
-    void* rrecs;            // [BH][2 nc]
-    const void* dout;       // [BH, L, DV] bf16
-    int64_t L;
-    int nc;
-    int BH;
-    int DV;
-};
-hipError_t launch_rev_records(const RevRecParams& prm, int dk, hipStream_t stream);
 
 // Chunk-parallel gradients from the two scans' per-chunk states.
 struct ChunkGradParams {

@@ -50,6 +50,7 @@
 //    never above 0), reduced across the wave and added into LDS.
 #include "kda_device.h"
 #include "kda_internal.h"
+#include "kda_rev_record.h"
 
 namespace kda {
 
@@ -119,7 +120,7 @@ struct IntraCfg {
     static constexpr int MIN_WAVES = THIN ? 8 : 1;
 };
 
-template <class Cfg, bool GBF, bool WIDE>
+template <class Cfg, bool GBF, bool WIDE, bool REV = false>
 __global__ void __launch_bounds__(Cfg::NT) __attribute__((amdgpu_waves_per_eu(Cfg::MIN_WAVES)))
 kda_intra_kernel(IntraParams prm) {
     typedef typename Cfg::E E;
@@ -791,6 +792,15 @@ kda_intra_kernel(IntraParams prm) {
             st4<E>(rU + ((R * (NVB / PF) + vb / PF) * 64 + l) * 4 * PF + (vb % PF) * 4, acc);
         }
     }
+    if constexpr (REV) {
+        // the chunk's reverse record, from the record this workgroup has just
+        // written (the barrier's workgroup-scope fence makes the workgroup's
+        // global stores visible to all its threads)
+        static_assert(WIDE && RevCfg<DK, DV>::NT == NT && RevCfg<DK, DV>::LDS_BYTES <= Cfg::LDS_BYTES,
+                      "the reverse record fits this workgroup");
+        __syncthreads();
+        build_rev_record<DK, DV>(prm.ws, prm.rrecs, prm.dout, L, prm.ncs, bh, cs, smem);
+    }
 }
 
 // ---- host-side dispatch -----------------------------------------------------
@@ -803,6 +813,16 @@ static hipError_t launch_intra_cfg(const IntraParams& prm, hipStream_t stream) {
     constexpr bool CAN_WIDE = Cfg::KDA && sizeof(E) == 2;
     if (prm.wide && !CAN_WIDE) return hipErrorInvalidValue;
     if constexpr (CAN_WIDE) {
+        if (prm.wide && prm.rrecs) {
+            if (prm.c0 != 0 || !prm.dout || prm.cu) return hipErrorInvalidValue;
+            if (prm.gate_bf16)
+                hipLaunchKernelGGL((kda_intra_kernel<Cfg, true, true, true>), dim3((unsigned)grid),
+                                   dim3(Cfg::NT), 0, stream, prm);
+            else
+                hipLaunchKernelGGL((kda_intra_kernel<Cfg, false, true, true>), dim3((unsigned)grid),
+                                   dim3(Cfg::NT), 0, stream, prm);
+            return hipGetLastError();
+        }
         if (prm.wide) {
             if (prm.gate_bf16)
                 hipLaunchKernelGGL((kda_intra_kernel<Cfg, true, true>), dim3((unsigned)grid),

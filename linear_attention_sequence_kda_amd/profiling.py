@@ -32,17 +32,17 @@ COPY_KERNEL = "__amd_rocclr_copyBuffer"
 
 # sources whose change changes the kernel's memory traffic
 KERNEL_SOURCES = {
-    "kda_intra_kernel": ["kda_intra.hip"],
+    "kda_intra_kernel": ["kda_intra.hip", "kda_rev_record.h"],
     "kda_inter_kernel": ["kda_inter.hip"],
     "kda_inter_scalar_kernel": ["kda_inter_scalar.hip"],
     "kda_inter_wide_kernel": ["kda_inter_wide.hip"],
     "kda_inter_quad_kernel": ["kda_inter_wide.hip"],
     "kda_decode_kernel": ["kda_decode.hip"],
     "kda_bwd_kernel": ["kda_bwd.hip"],
-    # chunkwise gradients: the reverse-record builder, the gradient kernel, and
-    # the wide state pass in its scan forms (forward, reverse), which rocprofv3
-    # lists as kda_inter_wide_kernel instances (traffic --match)
-    "kda_rev_records_kernel": ["kda_chunk_bwd.hip"],
+    # chunkwise gradients: the gradient kernel and the wide state pass in its
+    # scan forms (forward, reverse), which rocprofv3 lists as
+    # kda_inter_wide_kernel instances (traffic --match); the reverse records
+    # are built by the intra-chunk kernel's gradient form
     "kda_chunk_grad_kernel": ["kda_chunk_bwd.hip"],
     "kda_inter_wide_scan": ["kda_inter_wide.hip"],
     "kda_inter_wide_scan_rev": ["kda_inter_wide.hip"],
