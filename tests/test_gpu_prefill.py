@@ -515,3 +515,30 @@ def test_longest_sequence_fp32():
     say(f"longest sequence: err o={e_o:.3e} S={e_s:.3e} (tol {TOL['f32']})")
     assert e_o <= TOL["f32"], f"o error {e_o}"
     assert e_s <= TOL["f32"], f"S_final error {e_s}"
+
+
+def _sweep_cases(n=20, seed=20261203):
+    """Seeded random shapes: head counts on both sides of each state-pass slice
+    width, ragged lengths, every dtype and decay mode, decay strengths from
+    almost none to strong, with and without an initial state."""
+    rng = np.random.default_rng(seed)
+    cases = []
+    for i in range(n):
+        qd, gd, mode = DTYPES[rng.integers(len(DTYPES))]
+        dk, dv = DIMS[rng.integers(len(DIMS))]
+        B = int(rng.integers(1, 4))
+        H = int(rng.integers(1, 72 // B + 1))
+        L = int(rng.integers(1, max(2, 30_000 // (B * H)) + 1))
+        L = min(L, 1500)
+        mu = float(rng.uniform(-6.0, -0.05))
+        s0 = float(rng.choice([0.0, 0.02, 0.5]))
+        cases.append((i, B, H, L, dk, dv, qd, gd, mode, mu, s0))
+    return cases
+
+
+@pytest.mark.parametrize("case", _sweep_cases(), ids=lambda c: f"sweep{c[0]}")
+def test_random_shape_sweep(case):
+    i, B, H, L, dk, dv, qd, gd, mode, mu, s0 = case
+    w = gen.custom(B=B, H=H, L=L, dk=dk, dv=dv, qkv_dtype=qd, gate_dtype=gd, alpha_mode=mode,
+                   la_mu=mu, la_sigma=0.5, s0_std=s0, seed=5000 + i)
+    run_and_compare(w, f"sweep{i} mu={mu:.2f} s0={s0}")
