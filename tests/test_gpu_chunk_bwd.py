@@ -184,3 +184,31 @@ def test_workload_full(cfg):
     w = gen.WORKLOADS[cfg]
     heads = [(0, 0), (w.B - 1, w.H - 1)]
     run_and_compare(w, f"chunk-bwd workload {cfg}", heads=heads)
+
+
+def _sweep_cases(n=12, seed=20261204):
+    """Seeded random shapes for the gradients: ragged lengths, head counts,
+    every head size, gate dtype and decay mode, decay strengths from almost
+    none to strong, with and without an initial state and a final-state
+    gradient."""
+    rng = np.random.default_rng(seed)
+    cases = []
+    for i in range(n):
+        gd, mode = GATES[rng.integers(len(GATES))]
+        dk, dv = DIMS[rng.integers(len(DIMS))]
+        B = int(rng.integers(1, 3))
+        H = int(rng.integers(1, 9))
+        L = int(rng.integers(1, min(700, 8000 // (B * H)) + 1))
+        mu = float(rng.uniform(-6.0, -0.05))
+        s0 = [None, 0.02, 0.5][int(rng.integers(3))]
+        final = bool(rng.integers(2))
+        cases.append((i, B, H, L, dk, dv, gd, mode, mu, s0, final))
+    return cases
+
+
+@pytest.mark.parametrize("case", _sweep_cases(), ids=lambda c: f"sweep{c[0]}")
+def test_random_shape_sweep(case):
+    i, B, H, L, dk, dv, gd, mode, mu, s0, final = case
+    w = gen.custom(B=B, H=H, L=L, dk=dk, dv=dv, qkv_dtype="bf16", gate_dtype=gd,
+                   alpha_mode=mode, la_mu=mu, la_sigma=0.5, s0_std=s0, seed=6000 + i)
+    run_and_compare(w, f"chunk-bwd-sweep{i} mu={mu:.2f} s0={s0}", final=final, seed=70 + i)

@@ -531,7 +531,7 @@ def _sweep_cases(n=20, seed=20261203):
         L = int(rng.integers(1, max(2, 30_000 // (B * H)) + 1))
         L = min(L, 1500)
         mu = float(rng.uniform(-6.0, -0.05))
-        s0 = float(rng.choice([0.0, 0.02, 0.5]))
+        s0 = [None, 0.02, 0.5][int(rng.integers(3))]
         cases.append((i, B, H, L, dk, dv, qd, gd, mode, mu, s0))
     return cases
 
