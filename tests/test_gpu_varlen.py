@@ -193,3 +193,30 @@ def test_varlen_prefill_then_slot_decode():
         og = np.stack([o[i] for o in outs], axis=1)  # [H, steps, dv]
         assert oracle.slab_error(og, o_ref[:, lens[i]:], 1) <= TOL["bf16"]
         assert oracle.slab_error(to_f64(pool[slots_h[i]]), S_ref, 1) <= TOL["bf16"]
+
+
+def _sweep_cases(n=10, seed=20261205):
+    """Seeded random packings: 1-40 sequences of lengths drawn from a long-tailed
+    mix (empty, single tokens, a chunk and one more, a few thousand), random
+    head counts, head sizes, dtypes and decay modes, with and without S0."""
+    rng = np.random.default_rng(seed)
+    modes = [("bf16", "bf16", "channel"), ("bf16", "f32", "head"), ("f32", "f32", "none"),
+             ("f32", "f32", "channel"), ("bf16", "bf16", "none"), ("f32", "bf16", "head")]
+    dims = [(64, 64), (128, 128), (64, 128), (128, 64)]
+    cases = []
+    for i in range(n):
+        nseq = int(rng.integers(1, 41))
+        lens = [int(x) for x in np.minimum(rng.lognormal(4.0, 1.5, nseq).astype(np.int64), 3000)]
+        lens[int(rng.integers(nseq))] = [0, 1, 65][int(rng.integers(3))]
+        qd, gd, mode = modes[i % len(modes)]
+        dk, dv = dims[rng.integers(len(dims))]
+        H = int(rng.integers(1, 9))
+        cases.append((i, lens, H, dk, dv, qd, gd, mode, bool(rng.integers(2))))
+    return cases
+
+
+@pytest.mark.parametrize("case", _sweep_cases(), ids=lambda c: f"sweep{c[0]}")
+def test_varlen_random_sweep(case):
+    i, lens, H, dk, dv, qd, gd, mode, s0 = case
+    run_varlen(lens, H=H, dk=dk, dv=dv, qd=qd, gd=gd, mode=mode, s0=s0, seed=900 + i,
+               label=f"varlen-sweep{i}")
